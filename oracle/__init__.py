@@ -1,0 +1,62 @@
+"""CPU oracle for the 4-bit-weight GEMM hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+link this package: only the test suite, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library (``gemm_bit_weight_amd``) and never imports it.
+
+Everything here is plain numpy, decoding to float64 and accumulating in
+float64.  Where the method is an encoding (the block-scaled FP4 quantizers,
+routing), the functions follow the steps in the order the pages describe
+them; where the method reaches a result with a plain definition (every GEMM,
+the LUT kernel, the VQ decode) the oracle is that definition written out with
+a float64 matmul as the contraction step.
+
+Sources (page titles as printed on the pages):
+  * "MXCode: MX-Native Codebook Quantization" -- Table 1 (block formats),
+    abstract (PreScale, MX-native operand reconstruction), Fig. 2/3 and
+    Table 4 (VQ d=4, K=256, QBlock sizes).
+  * "PRQuant: Permutation Residual Quantization for Low-Overhead Inference" --
+    §4 Eq. (1) (scaled/permuted FFN), Eq. (2) (offline weight residual),
+    §4 "Kernel design for efficient inference" (augmented MXFP4 GEMM and the
+    online tail copy).
+  * "CodeQuant: Unified Clustering and Quantization for Enhanced Outlier
+    Smoothing in Low-Precision Mixture-of-Experts" -- Fig. 1 (clustered
+    weights, LUT kernel), Fig. 4 (LUT precompute + lookup per tile).
+
+Parity status of each function is recorded in its docstring; every function
+has at least one pin in ``tests/test_oracle_*.py``.
+"""
+
+from . import formats, gemm, moe  # noqa: F401
+from .formats import (  # noqa: F401
+    E2M1_MAGNITUDES,
+    e2m1_decode,
+    e8m0_decode,
+    e4m3_decode,
+    e2m1_round_magnitude,
+    e4m3_round,
+    quantize_e8m0_b32,
+    quantize_e4m3_b16,
+    dequantize,
+    pack_nibbles,
+    unpack_nibbles,
+    bf16_bits_to_f32,
+    f32_to_bf16_bits,
+)
+from .gemm import (  # noqa: F401
+    mx_gemm,
+    residual_weight,
+    residual_tail_gemm,
+    tail_copy,
+    lut_decode,
+    lut_gemm,
+    vq_decode_codes,
+    vq_dequantize,
+)
+from .moe import (  # noqa: F401
+    moe_route,
+    moe_gateup,
+    swiglu_bf16,
+    moe_down_combine,
+)

@@ -1,0 +1,209 @@
+"""Seeded synthetic inputs for the 4-bit-weight GEMM path.
+
+This module is shared by the oracle side (tests, CPU baseline) and the HIP
+side (tests, bench).  It holds none of the method's arithmetic: it draws
+random tensors, permutes columns, and builds codebook-format weights from
+random draws.  Quantization to the block-scaled FP4 formats is never done
+here -- each side does it with its own quantizer.
+
+Every tensor is drawn from its own torch.Generator seeded from (seed, name),
+so one tensor's recipe does not shift another's.  Values are generated on the
+requested device (CPU for the oracle-sized cases, the GPU for large bench
+inputs); the oracle always works on a host copy of the very same arrays.
+
+Workload recipes (sizes follow the configurations the library is measured
+on; the distributions stand in for trained weights and calibration
+activations, which are not available):
+  * dense linear: X ~ N(0,1) rounded to bf16, W ~ N(0, 0.02^2) fp32;
+  * codebook/LUT weights: W ~ N(0, 0.02^2) with 0.5% of entries x20, one
+    16-entry fp16 codebook per (output row, 128-wide K group) from a plain
+    1-D Lloyd clustering, 4-bit indices;
+  * tail-residual down projection: X ~ N(0,1) with 1% of its channels x50,
+    rounded to bf16, W ~ N(0, 0.02^2); the outlier channels are moved to the
+    end of K by a stable partition applied to the columns of both;
+  * MoE: X ~ N(0,1) bf16, router logits ~ N(0,1) fp32, per-expert
+    W_gate, W_up, W_down ~ N(0, 0.02^2) fp32;
+  * VQ->MX MoE weights: per 64x64 QBlock a 256-entry table of 4-element
+    E2M1 keys, 8-bit indices, E8M0 prescale codes -- drawn directly in that
+    format (the codebook learning itself is offline and out of scope).
+"""
+
+import zlib
+
+import torch
+
+GATE_UP_STACK = "gate rows [0, I), up rows [I, 2I)"
+
+
+def seed_for(seed, name):
+    return (int(seed) * 1_000_003 + zlib.crc32(name.encode())) & 0x7FFF_FFFF_FFFF
+
+
+def _gen(seed, name, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_for(seed, name))
+    return g
+
+
+def normal(shape, std, seed, name, device="cpu", dtype=torch.float32):
+    g = _gen(seed, name, device)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x = x * std
+    return x.to(dtype)
+
+
+def uniform(shape, seed, name, device="cpu"):
+    g = _gen(seed, name, device)
+    return torch.rand(shape, generator=g, device=device, dtype=torch.float32)
+
+
+# ----------------------------------------------------------------------------
+# Dense linear (block-scaled FP4 weights are quantized by each side)
+# ----------------------------------------------------------------------------
+
+def dense_linear(M, N, K, seed=0, device="cpu"):
+    """X bf16 [M][K] ~ N(0,1); W fp32 [N][K] ~ N(0, 0.02^2)."""
+    x = normal((M, K), 1.0, seed, "dense.x", device).to(torch.bfloat16)
+    w = normal((N, K), 0.02, seed, "dense.w", device)
+    return dict(x=x, w=w)
+
+
+# ----------------------------------------------------------------------------
+# Tail-residual down projection
+# ----------------------------------------------------------------------------
+
+def tail_residual_problem(M, N, K, tail=256, outlier_frac=0.01, outlier_gain=50.0, seed=0,
+                          device="cpu"):
+    """Activations with injected outlier channels moved to the end of K.
+
+    Returns x bf16 [M][K] and w fp32 [N][K], both already permuted, plus the
+    permutation (new column c holds old channel perm[c]) and the outlier
+    channel ids.
+    """
+    n_out = int(outlier_frac * K)
+    assert n_out <= tail <= K
+    x = normal((M, K), 1.0, seed, "tail.x", device)
+    g = _gen(seed, "tail.channels", "cpu")
+    chans = torch.randperm(K, generator=g)[:n_out].sort().values
+    if n_out:
+        x[:, chans.to(device)] *= outlier_gain
+    x = x.to(torch.bfloat16)
+    w = normal((N, K), 0.02, seed, "tail.w", device)
+    is_out = torch.zeros(K, dtype=torch.bool)
+    is_out[chans] = True
+    perm = torch.cat([torch.nonzero(~is_out).flatten(), torch.nonzero(is_out).flatten()])
+    pd = perm.to(device)
+    return dict(x=x[:, pd].contiguous(), w=w[:, pd].contiguous(), perm=perm, outlier_channels=chans)
+
+
+# ----------------------------------------------------------------------------
+# Codebook (CodeQuant-style clustered) weights
+# ----------------------------------------------------------------------------
+
+def clustered_weight(N, K, group=128, n_centroids=16, outlier_frac=0.005, outlier_gain=20.0,
+                     iters=10, seed=0, device="cpu", rows_per_chunk=512):
+    """W ~ N(0, 0.02^2) with outliers, clustered per (row, K group) into
+    ``n_centroids`` fp16 centroids by 1-D Lloyd iterations.
+
+    Initial centroid j is the mean of the j-th equal-count slice of the
+    sorted group; each iteration assigns every value to the nearest centroid
+    (ties to the lower index) and moves each non-empty centroid to the mean of
+    its members.  Centroids are then rounded to fp16 and every value is
+    assigned to its nearest fp16 centroid.
+
+    Returns idx uint8 [N][K/2] (two 4-bit indices per byte, element 2i in
+    bits 3:0), centroids fp16 [N][K/group][n_centroids], and the fp32 weight.
+    """
+    assert K % group == 0 and group % n_centroids == 0 and n_centroids <= 16
+    w = normal((N, K), 0.02, seed, "lut.w", device)
+    mask = uniform((N, K), seed, "lut.outliers", device) < outlier_frac
+    w = torch.where(mask, w * outlier_gain, w)
+    G = K // group
+    idx_all = torch.empty((N, K), dtype=torch.uint8, device=device)
+    cent_all = torch.empty((N, G, n_centroids), dtype=torch.float16, device=device)
+    for r0 in range(0, N, rows_per_chunk):
+        r1 = min(N, r0 + rows_per_chunk)
+        v = w[r0:r1].view(r1 - r0, G, group)
+        s = v.sort(dim=-1).values
+        c = s.view(r1 - r0, G, n_centroids, group // n_centroids).mean(dim=-1)
+        prev = None
+        for _ in range(iters):
+            a = (v.unsqueeze(-1) - c.unsqueeze(-2)).abs().argmin(dim=-1)
+            if prev is not None and torch.equal(a, prev):
+                break
+            prev = a
+            oh = torch.nn.functional.one_hot(a, n_centroids).to(torch.float32)
+            cnt = oh.sum(dim=-2)
+            tot = (oh * v.unsqueeze(-1)).sum(dim=-2)
+            c = torch.where(cnt > 0, tot / cnt.clamp(min=1), c)
+        c16 = c.to(torch.float16)
+        a = (v.unsqueeze(-1) - c16.float().unsqueeze(-2)).abs().argmin(dim=-1)
+        idx_all[r0:r1] = a.view(r1 - r0, K).to(torch.uint8)
+        cent_all[r0:r1] = c16
+    packed = (idx_all[:, 0::2] & 0xF) | ((idx_all[:, 1::2] & 0xF) << 4)
+    return dict(idx=packed.contiguous(), centroids=cent_all, w=w)
+
+
+def lut_problem(M, N=4096, K=4096, group=128, seed=0, device="cpu", iters=10):
+    x = normal((M, K), 1.0, seed, "lut.x", device).to(torch.bfloat16)
+    d = clustered_weight(N, K, group=group, seed=seed, device=device, iters=iters)
+    d["x"] = x
+    return d
+
+
+# ----------------------------------------------------------------------------
+# MoE inputs
+# ----------------------------------------------------------------------------
+
+def moe_problem(T, H, I, E, seed=0, device="cpu"):
+    """X bf16 [T][H], logits fp32 [T][E], fused gate/up fp32 [E][2I][H]
+    (gate rows first), down fp32 [E][H][I]."""
+    x = normal((T, H), 1.0, seed, "moe.x", device).to(torch.bfloat16)
+    logits = normal((T, E), 1.0, seed, "moe.logits", device)
+    w_gu = torch.empty((E, 2 * I, H), dtype=torch.float32, device=device)
+    w_d = torch.empty((E, H, I), dtype=torch.float32, device=device)
+    for e in range(E):
+        w_gu[e] = normal((2 * I, H), 0.02, seed, f"moe.w_gate_up.{e}", device)
+        w_d[e] = normal((H, I), 0.02, seed, f"moe.w_down.{e}", device)
+    return dict(x=x, logits=logits, w_gate_up=w_gu, w_down=w_d)
+
+
+# Magnitude distribution used to draw E2M1 keys for synthetic VQ codebooks:
+# probabilities of the 8 magnitude codes (0, 0.5, 1, 1.5, 2, 3, 4, 6), a
+# shape typical of Gaussian weights after a per-32 power-of-two prescale.
+_E2M1_MAG_PROBS = [0.08, 0.15, 0.15, 0.14, 0.18, 0.16, 0.10, 0.04]
+
+
+def vq_weight(E, N, K, qblock=64, n_entries=256, seed=0, name="vq", device="cpu"):
+    """Codebook->MX weights drawn directly in the VQ format.
+
+    idx uint8 [E][N][K/4]; codebook 16-bit [E][N/qblock][K/qblock][256]
+    (4 E2M1 codes per entry, element i in bits 4i+3:4i); prescale E8M0 codes
+    uint8 [E][N][K/32] in {119, 120, 121} (weights of magnitude ~0.02).
+    """
+    assert N % qblock == 0 and K % qblock == 0
+    probs = torch.tensor(_E2M1_MAG_PROBS, dtype=torch.float64)
+    cdf = (probs.cumsum(0) / probs.sum()).to(torch.float32)[:-1].to(device)
+    nb = (E, N // qblock, K // qblock, n_entries, 4)
+    mag = torch.bucketize(uniform(nb, seed, f"{name}.cb.mag", device), cdf).to(torch.int32)
+    sign = (uniform(nb, seed, f"{name}.cb.sign", device) < 0.5).to(torch.int32)
+    nib = mag | (sign << 3)
+    key = nib[..., 0] | (nib[..., 1] << 4) | (nib[..., 2] << 8) | (nib[..., 3] << 12)
+    # stored as int16 bit patterns (torch has no general uint16 arithmetic)
+    codebook = torch.where(key >= 32768, key - 65536, key).to(torch.int16)
+    g = _gen(seed, f"{name}.idx", device)
+    idx = torch.randint(0, n_entries, (E, N, K // 4), generator=g, device=device, dtype=torch.uint8)
+    u = uniform((E, N, K // 32), seed, f"{name}.scale", device)
+    scales = (119 + (u >= 0.25).to(torch.uint8) + (u >= 0.75).to(torch.uint8)).to(torch.uint8)
+    return dict(idx=idx, codebook=codebook.contiguous(), scales=scales)
+
+
+def moe_vq_problem(T, H, I, E, seed=0, device="cpu"):
+    """X bf16 [T][H], logits [T][E], VQ gate/up weights (N = 2I, K = H) and
+    VQ down weights (N = H, K = I)."""
+    x = normal((T, H), 1.0, seed, "moevq.x", device).to(torch.bfloat16)
+    logits = normal((T, E), 1.0, seed, "moevq.logits", device)
+    gu = vq_weight(E, 2 * I, H, seed=seed, name="moevq.gate_up", device=device)
+    dn = vq_weight(E, H, I, seed=seed, name="moevq.down", device=device)
+    return dict(x=x, logits=logits, gate_up=gu, down=dn)

@@ -1,0 +1,170 @@
+"""Pins for the oracle's MoE routing and expert FFN stages.
+
+Routing is checked against a pure-Python full sort per token; the FFN stages
+are checked against the special cases that reduce to a dense SwiGLU FFN
+(one expert, top-1), against routing-independence when all experts are
+identical, and the SwiGLU rounding against torch's bf16 cast.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import moe as M
+
+
+def _brute_route(logits, topk):
+    T, E = logits.shape
+    ids, ws = [], []
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))[:topk]
+        mx = float(logits[t, order[0]])
+        ex = [math.exp(float(logits[t, e]) - mx) for e in order]
+        s = sum(ex)
+        ids.append(order)
+        ws.append([v / s for v in ex])
+    return np.array(ids), np.array(ws)
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 4, 1), (17, 8, 2), (64, 128, 8), (5, 16, 16)])
+def test_route_brute_force(T, E, k):
+    rng = np.random.default_rng(T + E + k)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[0, :3] = logits[0, 3] if E > 3 else logits[0, 0]        # ties
+    r = oracle.moe_route(logits, k)
+    ids, ws = _brute_route(logits, k)
+    assert np.array_equal(r["topk_ids"], ids)
+    assert np.allclose(r["topk_w"], ws, rtol=1e-14, atol=0)
+    # pair list: every (token, slot) once, sorted by (expert, token)
+    off = r["expert_offsets"]
+    assert off[0] == 0 and off[-1] == T * k and np.all(np.diff(off) >= 0)
+    pt = r["pair_token"]
+    for e in range(E):
+        seg = pt[off[e]:off[e + 1]]
+        assert np.all(np.diff(seg) > 0)
+        assert sorted(seg.tolist()) == sorted(t for t in range(T) if e in ids[t])
+    for t in range(T):
+        for j in range(k):
+            p = r["pair_pos"][t, j]
+            assert pt[p] == t and off[ids[t, j]] <= p < off[ids[t, j] + 1]
+
+
+def test_route_known_permutation():
+    E = 128
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(E)
+    logits = perm[None, :].astype(np.float32)            # logit of expert e is perm[e]
+    r = oracle.moe_route(logits, 8)
+    want = [int(np.nonzero(perm == v)[0][0]) for v in range(127, 119, -1)]
+    assert r["topk_ids"][0].tolist() == want
+    ref = np.exp(np.arange(0, -8, -1.0))
+    assert np.allclose(r["topk_w"][0], ref / ref.sum(), rtol=1e-15)
+
+
+def test_route_ties_go_to_lower_id():
+    logits = np.zeros((2, 8), np.float32)
+    logits[1, 5] = -0.0
+    r = oracle.moe_route(logits, 3)
+    assert r["topk_ids"].tolist() == [[0, 1, 2], [0, 1, 2]]
+    assert np.allclose(r["topk_w"], 1 / 3)
+
+
+def test_swiglu_bf16_rounding():
+    g = np.array([0.0, 1.0, -1.0, 20.0, -30.0, 0.5])
+    u = np.array([3.0, 2.0, 2.0, 1.5, 1.0, -7.25])
+    h = oracle.swiglu_bf16(g, u)
+    ref = g / (1 + np.exp(-g)) * u
+    want = torch.from_numpy(ref).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(h, want)
+    # double rounding guard: values just above a bf16 midpoint
+    mid = np.float64(1.0 + 2.0 ** -8)                  # exact bf16 midpoint of 1 and 1+2^-7
+    hh = M._f64_to_bf16_bits(np.array([mid, mid + 2.0 ** -40, mid - 2.0 ** -40]))
+    assert hh.tolist() == [0x3F80, 0x3F81, 0x3F80]
+
+
+def _quant_moe_weights(w_gu, w_d, fmt):
+    E = w_gu.shape[0]
+    out = dict(gu_c=[], gu_s=[], gu_t=[], d_c=[], d_s=[], d_t=[])
+    I = w_gu.shape[1] // 2
+    for e in range(E):
+        if fmt == "e8m0_b32":
+            c, s = oracle.quantize_e8m0_b32(w_gu[e])
+            out["gu_c"].append(c); out["gu_s"].append(s)
+            c, s = oracle.quantize_e8m0_b32(w_d[e])
+            out["d_c"].append(c); out["d_s"].append(s)
+        else:
+            cg, sg, tg = oracle.quantize_e4m3_b16(w_gu[e][:I])
+            cu, su, tu = oracle.quantize_e4m3_b16(w_gu[e][I:])
+            out["gu_c"].append(np.concatenate([cg, cu])); out["gu_s"].append(np.concatenate([sg, su]))
+            out["gu_t"].append([tg, tu])
+            c, s, t = oracle.quantize_e4m3_b16(w_d[e])
+            out["d_c"].append(c); out["d_s"].append(s); out["d_t"].append(t)
+    return {k: np.array(v) for k, v in out.items()}
+
+
+def _quant_act(x, fmt):
+    if fmt == "e8m0_b32":
+        c, s = oracle.quantize_e8m0_b32(x)
+        return c, s, None
+    return oracle.quantize_e4m3_b16(x)
+
+
+def _ffn(x, logits, w_gu, w_d, topk, fmt, tokens=None):
+    W = _quant_moe_weights(w_gu, w_d, fmt)
+    route = oracle.moe_route(logits, topk)
+    ac, as_, at = _quant_act(x, fmt)
+    g, u = oracle.moe_gateup(ac, as_, fmt, route, W["gu_c"], W["gu_s"], at, W["gu_t"] if len(W["gu_t"]) else None)
+    h = oracle.bf16_bits_to_f32(oracle.swiglu_bf16(g, u))
+    hc, hs, ht = _quant_act(h, fmt)
+    y = oracle.moe_down_combine(hc, hs, fmt, route, W["d_c"], W["d_s"], ht,
+                                W["d_t"] if len(W["d_t"]) else None, tokens=tokens)
+    return y, dict(W=W, route=route, g=g, u=u, h=h, hc=hc, hs=hs, ht=ht, ac=ac, as_=as_, at=at)
+
+
+@pytest.mark.parametrize("fmt", ["e8m0_b32", "e4m3_b16"])
+def test_one_expert_top1_is_dense_swiglu_ffn(fmt):
+    rng = np.random.default_rng(20)
+    T, H, I = 9, 64, 96
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    w_gu = (rng.standard_normal((1, 2 * I, H)) * 0.05).astype(np.float32)
+    w_d = (rng.standard_normal((1, H, I)) * 0.05).astype(np.float32)
+    y, st = _ffn(x, np.zeros((T, 1), np.float32), w_gu, w_d, 1, fmt)
+    W = st["W"]
+    if fmt == "e8m0_b32":
+        gu = oracle.mx_gemm(st["ac"], st["as_"], W["gu_c"][0], W["gu_s"][0])
+        g, u = gu[:, :I], gu[:, I:]
+        y_ref = oracle.mx_gemm(st["hc"], st["hs"], W["d_c"][0], W["d_s"][0])
+    else:
+        g = oracle.mx_gemm(st["ac"], st["as_"], W["gu_c"][0][:I], W["gu_s"][0][:I], fmt, st["at"], W["gu_t"][0][0])
+        u = oracle.mx_gemm(st["ac"], st["as_"], W["gu_c"][0][I:], W["gu_s"][0][I:], fmt, st["at"], W["gu_t"][0][1])
+        y_ref = oracle.mx_gemm(st["hc"], st["hs"], W["d_c"][0], W["d_s"][0], fmt, st["ht"], W["d_t"][0])
+    # one pair per token, in token order
+    assert np.array_equal(st["route"]["pair_token"], np.arange(T))
+    assert np.array_equal(st["g"], g) and np.array_equal(st["u"], u)
+    assert np.array_equal(y, y_ref)
+
+
+def test_identical_experts_make_routing_irrelevant():
+    rng = np.random.default_rng(21)
+    T, H, I, E = 12, 64, 64, 6
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    w_gu = np.repeat((rng.standard_normal((1, 2 * I, H)) * 0.05).astype(np.float32), E, axis=0)
+    w_d = np.repeat((rng.standard_normal((1, H, I)) * 0.05).astype(np.float32), E, axis=0)
+    y1, _ = _ffn(x, rng.standard_normal((T, E)).astype(np.float32), w_gu, w_d, 3, "e8m0_b32")
+    y2, _ = _ffn(x, rng.standard_normal((T, E)).astype(np.float32), w_gu, w_d, 2, "e8m0_b32")
+    assert np.allclose(y1, y2, rtol=1e-12, atol=1e-12)
+
+
+def test_token_subset_matches_full():
+    rng = np.random.default_rng(22)
+    T, H, I, E = 20, 64, 64, 4
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    w_gu = (rng.standard_normal((E, 2 * I, H)) * 0.05).astype(np.float32)
+    w_d = (rng.standard_normal((E, H, I)) * 0.05).astype(np.float32)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    y, _ = _ffn(x, logits, w_gu, w_d, 2, "e4m3_b16")
+    ys, _ = _ffn(x, logits, w_gu, w_d, 2, "e4m3_b16", tokens=[3, 0, 19])
+    assert np.array_equal(ys, y[[3, 0, 19]])
