@@ -1,0 +1,117 @@
+// Shared device codecs and host plumbing for the gfx950 kernels.
+//
+// Device codecs follow the block formats of "MXCode: MX-Native Codebook
+// Quantization", Table 1 (E2M1 elements, E8M0 and E4M3 block scales) and the
+// OCP MX element type that "PRQuant: Permutation Residual Quantization for
+// Low-Overhead Inference" cites for MXFP4 (§1).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gbw.h"
+
+namespace gbw {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------
+// E2M1
+// ---------------------------------------------------------------------------
+
+// Round a non-negative magnitude (already divided by the block scale) onto
+// the E2M1 grid {0, .5, 1, 1.5, 2, 3, 4, 6}: nearest value, ties to the even
+// code, saturating at 6.  Each comparison counts one grid step crossed; the
+// closed/open choice at each midpoint encodes ties-to-even.
+__device__ __forceinline__ uint32_t e2m1_rne(float v) {
+  return (uint32_t)(v > 0.25f) + (uint32_t)(v >= 0.75f) + (uint32_t)(v > 1.25f) +
+         (uint32_t)(v >= 1.75f) + (uint32_t)(v > 2.5f) + (uint32_t)(v >= 3.5f) +
+         (uint32_t)(v > 5.0f);
+}
+
+// E2M1 code -> float from its bit fields (1 sign, 2 exponent with bias 1, 1 mantissa).
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  float mag = (e == 0) ? 0.5f * (float)m : __uint_as_float((uint32_t)(e + 126) << 23) * (1.0f + 0.5f * (float)m);
+  return (c & 8u) ? -mag : mag;
+}
+
+// ---------------------------------------------------------------------------
+// E8M0 and E4M3 block scales
+// ---------------------------------------------------------------------------
+
+// 2^(127 - sc) as an fp32, sc in [0, 252]: the reciprocal of an E8M0 scale.
+__device__ __forceinline__ float e8m0_inv(uint32_t sc) { return __uint_as_float((254u - sc) << 23); }
+
+// E8M0 scale value 2^(sc - 127), sc in [1, 254]; sc = 0 gives 2^-127 (subnormal).
+__device__ __forceinline__ float e8m0_value(uint32_t sc) {
+  return sc == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(sc << 23);
+}
+
+// OCP MX shared-scale rule for E2M1 elements: floor(log2 amax) - 2, biased,
+// clamped at 0 (zero and subnormal blocks get code 0).
+__device__ __forceinline__ uint32_t e8m0_scale_code(float amax) {
+  const int E = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+  return (uint32_t)(E > 2 ? E - 2 : 0);
+}
+
+// Non-negative fp32 -> E4M3 ("fn") code, round to nearest even, saturating
+// at 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float s) {
+  if (!(s < 448.0f)) return 0x7Eu;
+  const uint32_t b = __float_as_uint(s);
+  const int e = (int)((b >> 23) & 0xFFu) - 127;
+  if (e < -6) {
+    // subnormal range: multiples of 2^-9; an exact power-of-two product, then RNE
+    return (uint32_t)__builtin_rintf(s * 512.0f);
+  }
+  const uint32_t m = b & 0x7FFFFFu;
+  const uint32_t r = (m + 0x7FFFFu + ((m >> 20) & 1u)) >> 20;  // 0..8, 8 carries into the exponent
+  return ((uint32_t)(e + 7) << 3) + r;
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  if (e == 0) return (float)m * 0.001953125f;  // m * 2^-9
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// ---------------------------------------------------------------------------
+// bf16
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// misc
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ v4i load16(const void* p) { return *reinterpret_cast<const v4i*>(p); }
+
+__host__ __device__ constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace gbw
+
+// ---------------------------------------------------------------------------
+// host plumbing (defined in api.hip)
+// ---------------------------------------------------------------------------
+namespace gbw {
+int fail(int status, const char* fmt, ...);
+int check_device();                       // GBW_OK on gfx950, GBW_E_UNSUPPORTED otherwise
+int check_launch(const char* what);       // maps hipGetLastError to GBW_E_LAUNCH
+int device_cu_count();
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int launch_fill_zero(float* p, int64_t n, hipStream_t st);
+}  // namespace gbw

@@ -1,0 +1,353 @@
+// Online activation quantization (E8M0-B32 and E4M3-B16 FP4), the tensor
+// amax pass, decode-to-fp32 and the offline PRQuant weight residual.
+//
+// Formats: "MXCode: MX-Native Codebook Quantization", Table 1.  Tail copy:
+// "PRQuant: Permutation Residual Quantization for Low-Overhead Inference",
+// §4 "Kernel design for efficient inference" (online copy).  Residual: same
+// page, §4 Eq. (2).
+//
+// Layout: one lane owns 8 consecutive K elements (one 16-byte bf16 load, two
+// for fp32); 4 neighbouring lanes form an E8M0 block of 32 and 2 form an E4M3
+// block of 16, so every wave-wide load is one contiguous 1 KiB (bf16) and the
+// block amax needs one or two lane swaps.  Each lane stores its 8 nibbles as
+// one 32-bit word.
+#include "common.hpp"
+
+namespace gbw {
+
+constexpr int kQuantThreads = 256;
+constexpr int kAmaxBlocks = 1024;
+
+template <typename T>
+struct In8;
+
+template <>
+struct In8<uint16_t> {  // bf16 bits
+  __device__ static void load(const uint16_t* p, float (&v)[8]) {
+    const v4i q = load16(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = (uint32_t)q[i];
+      v[2 * i] = __uint_as_float(w << 16);
+      v[2 * i + 1] = __uint_as_float(w & 0xFFFF0000u);
+    }
+  }
+};
+
+template <>
+struct In8<float> {
+  __device__ static void load(const float* p, float (&v)[8]) {
+    const v4i a = load16(p), b = load16(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = __int_as_float(a[i]);
+      v[4 + i] = __int_as_float(b[i]);
+    }
+  }
+};
+
+__device__ __forceinline__ uint32_t abs_bits(float f) { return __float_as_uint(f) & 0x7FFFFFFFu; }
+
+// max over lanes (lane ^ 1) and, if span == 4, (lane ^ 2): non-negative fp32
+// bit patterns order like unsigned integers.
+template <int SPAN>
+__device__ __forceinline__ uint32_t group_max(uint32_t a) {
+  a = max(a, (uint32_t)__shfl_xor((int)a, 1));
+  if (SPAN == 4) a = max(a, (uint32_t)__shfl_xor((int)a, 2));
+  return a;
+}
+
+// ---------------------------------------------------------------------------
+// E8M0-B32
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kQuantThreads) void k_quant_e8m0(const T* __restrict__ x, int64_t rows,
+                                                             int64_t K, int64_t tail,
+                                                             uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales) {
+  const int64_t g = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+  const int64_t total = rows * (K / 8);
+  const bool live = g < total;
+  const int64_t gg = live ? g : total - 1;  // keep the whole wave in the shuffles
+  const int64_t row = gg / (K / 8);
+  const int64_t col = (gg % (K / 8)) * 8;
+  float v[8];
+  In8<T>::load(x + row * K + col, v);
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) am = max(am, abs_bits(v[i]));
+  am = group_max<4>(am);
+  const uint32_t sc = e8m0_scale_code(__uint_as_float(am));
+  const float inv = e8m0_inv(sc);
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t c = e2m1_rne(__uint_as_float(abs_bits(v[i])) * inv) | ((__float_as_uint(v[i]) >> 28) & 8u);
+    word |= c << (4 * i);
+  }
+  if (!live) return;
+  const int64_t W = K + tail;
+  *reinterpret_cast<uint32_t*>(codes + row * (W / 2) + col / 2) = word;
+  const bool lead = (threadIdx.x & 3) == 0;
+  if (lead) scales[row * (W / 32) + col / 32] = (uint8_t)sc;
+  if (tail > 0 && col >= K - tail) {
+    const int64_t c2 = K + (col - (K - tail));
+    *reinterpret_cast<uint32_t*>(codes + row * (W / 2) + c2 / 2) = word;
+    if (lead) scales[row * (W / 32) + c2 / 32] = (uint8_t)sc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// tensor amax (deterministic two-pass: per-block partial maxima, reduced by
+// every consumer block)
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kQuantThreads) void k_amax_partial(const T* __restrict__ x, int64_t n8,
+                                                               uint32_t* __restrict__ partial) {
+  __shared__ uint32_t red[kQuantThreads / 64];
+  uint32_t am = 0;
+  for (int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * kQuantThreads) {
+    float v[8];
+    In8<T>::load(x + i * 8, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) am = max(am, abs_bits(v[j]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = am;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = 0;
+    for (int i = 0; i < kQuantThreads / 64; ++i) m = max(m, red[i]);
+    partial[blockIdx.x] = m;
+  }
+}
+
+// S_T = amax / (6 * 448) in fp32, 1 for an all-zero tensor.
+__device__ __forceinline__ float tensor_scale_from_amax(float a) { return a == 0.0f ? 1.0f : a / 2688.0f; }
+
+__device__ float block_reduce_partials(const uint32_t* __restrict__ partial, int n) {
+  __shared__ uint32_t red[kQuantThreads / 64];
+  uint32_t am = 0;
+  for (int i = threadIdx.x; i < n; i += kQuantThreads) am = max(am, partial[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = am;
+  __syncthreads();
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < kQuantThreads / 64; ++i) m = max(m, red[i]);
+  return __uint_as_float(m);
+}
+
+// ---------------------------------------------------------------------------
+// E4M3-B16 with FP32 tensor scale
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kQuantThreads) void k_quant_e4m3(const T* __restrict__ x, int64_t rows,
+                                                             int64_t K, uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales,
+                                                             float* __restrict__ tensor_scale,
+                                                             const uint32_t* __restrict__ partial,
+                                                             int n_partial) {
+  float S_T;
+  if (partial != nullptr) {
+    S_T = tensor_scale_from_amax(block_reduce_partials(partial, n_partial));
+    if (blockIdx.x == 0 && threadIdx.x == 0) tensor_scale[0] = S_T;
+  } else {
+    S_T = tensor_scale[0];
+  }
+  const int64_t g = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+  const int64_t total = rows * (K / 8);
+  const bool live = g < total;
+  const int64_t gg = live ? g : total - 1;
+  const int64_t row = gg / (K / 8);
+  const int64_t col = (gg % (K / 8)) * 8;
+  float v[8];
+  In8<T>::load(x + row * K + col, v);
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) am = max(am, abs_bits(v[i]));
+  am = group_max<2>(am);
+  const float d = 6.0f * S_T;
+  const float s = __uint_as_float(am) / d;
+  const uint32_t sc = e4m3_rne_sat(s);
+  const float den = e4m3_value(sc) * S_T;
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t mag = den > 0.0f ? e2m1_rne(__uint_as_float(abs_bits(v[i])) / den) : 0u;
+    word |= (mag | ((__float_as_uint(v[i]) >> 28) & 8u)) << (4 * i);
+  }
+  if (!live) return;
+  *reinterpret_cast<uint32_t*>(codes + row * (K / 2) + col / 2) = word;
+  if ((threadIdx.x & 1) == 0) scales[row * (K / 16) + col / 16] = (uint8_t)sc;
+}
+
+// ---------------------------------------------------------------------------
+// decode to fp32 (same decoders as the GEMM kernels) and the residual
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float decode_elem(int32_t fmt, const uint8_t* codes, const uint8_t* scales,
+                                             const uint16_t* codebook, const float* ts, int32_t ts_seg,
+                                             int64_t N, int64_t K, int64_t n, int64_t k) {
+  if (fmt == GBW_FMT_VQ4_E8M0) {
+    const uint32_t idx = codes[n * (K / 4) + k / 4];
+    const uint32_t key = codebook[((n / 64) * (K / 64) + k / 64) * 256 + idx];
+    const uint32_t c = (key >> (4 * (k & 3))) & 0xFu;
+    return e2m1_value(c) * e8m0_value(scales[n * (K / 32) + k / 32]);
+  }
+  const uint32_t c = (codes[n * (K / 2) + k / 2] >> (4 * (k & 1))) & 0xFu;
+  if (fmt == GBW_FMT_E8M0_B32) return e2m1_value(c) * e8m0_value(scales[n * (K / 32) + k / 32]);
+  const float v = e2m1_value(c) * e4m3_value(scales[n * (K / 16) + k / 16]);
+  const int64_t seg = n / (N / ts_seg);
+  return v * ts[seg];
+}
+
+__global__ void k_dequant(int32_t fmt, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                          const uint16_t* __restrict__ codebook, const float* __restrict__ ts,
+                          int32_t ts_seg, int64_t N, int64_t K, float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= N * K) return;
+  const int64_t n = i / K, k = i % K;
+  out[i] = decode_elem(fmt, codes, scales, codebook, ts, ts_seg, N, K, n, k);
+}
+
+__global__ void k_residual(const float* __restrict__ w, int64_t N, int64_t K, int64_t tail,
+                           const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                           float* __restrict__ r) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= N * tail) return;
+  const int64_t n = i / tail, k = K - tail + i % tail;
+  const float d = decode_elem(GBW_FMT_E8M0_B32, codes, scales, nullptr, nullptr, 1, N, K, n, k);
+  r[i] = w[n * K + k] - d;
+}
+
+__global__ void k_set_scalar(float* p, float v) {
+  if (threadIdx.x == 0) p[0] = v;
+}
+
+size_t ws_quantize(int64_t rows, int64_t K, int32_t fmt) {
+  (void)rows;
+  (void)K;
+  return fmt == GBW_FMT_E4M3_B16 ? (size_t)kAmaxBlocks * sizeof(uint32_t) : 0;
+}
+
+}  // namespace gbw
+
+using namespace gbw;
+
+extern "C" int mx_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t K, int32_t fmt,
+                           int64_t tail_copy, uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                           int32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  if (rows < 0 || K < 0 || tail_copy < 0) return fail(GBW_E_ARG, "mx_quantize: negative extent");
+  if (x_dtype != GBW_DTYPE_BF16 && x_dtype != GBW_DTYPE_F32) return fail(GBW_E_ARG, "mx_quantize: bad dtype");
+  if (fmt != GBW_FMT_E8M0_B32 && fmt != GBW_FMT_E4M3_B16) return fail(GBW_E_ARG, "mx_quantize: bad format");
+  const int bs = fmt == GBW_FMT_E8M0_B32 ? 32 : 16;
+  if (K % bs) return fail(GBW_E_SHAPE, "mx_quantize: K=%lld not a multiple of %d", (long long)K, bs);
+  if (tail_copy && (fmt != GBW_FMT_E8M0_B32 || tail_copy % 32 || tail_copy > K))
+    return fail(GBW_E_SHAPE, "mx_quantize: tail_copy must be a multiple of 32, <= K, E8M0 only");
+  const bool dynamic = fmt == GBW_FMT_E4M3_B16 && (flags & GBW_TS_DYNAMIC);
+  if (fmt == GBW_FMT_E4M3_B16 && !tensor_scale) return fail(GBW_E_ARG, "mx_quantize: E4M3 needs tensor_scale");
+  if (rows == 0 || K == 0) {
+    if (!dynamic) return GBW_OK;
+    int st0 = check_device();
+    if (st0) return st0;
+    // an empty tensor has amax 0, so its tensor scale is 1
+    hipLaunchKernelGGL(k_set_scalar, dim3(1), dim3(64), 0, as_stream(stream), tensor_scale, 1.0f);
+    return check_launch("mx_quantize(empty)");
+  }
+  if (!x || !codes || !scales) return fail(GBW_E_ARG, "mx_quantize: null pointer");
+  if (!aligned16(x) || !aligned16(codes)) return fail(GBW_E_ALIGN, "mx_quantize: x/codes not 16-byte aligned");
+  if (dynamic && (!ws || ws_bytes < ws_quantize(rows, K, fmt)))
+    return fail(GBW_E_WORKSPACE, "mx_quantize: dynamic tensor scale needs %zu bytes of workspace",
+                ws_quantize(rows, K, fmt));
+  int st = check_device();
+  if (st) return st;
+  hipStream_t s = as_stream(stream);
+  const int64_t total = rows * (K / 8);
+  const unsigned blocks = (unsigned)cdiv(total > 0 ? total : 1, kQuantThreads);
+  const bool bf = x_dtype == GBW_DTYPE_BF16;
+  if (fmt == GBW_FMT_E8M0_B32) {
+    if (bf)
+      hipLaunchKernelGGL(k_quant_e8m0<uint16_t>, dim3(blocks), dim3(kQuantThreads), 0, s,
+                         (const uint16_t*)x, rows, K, tail_copy, codes, scales);
+    else
+      hipLaunchKernelGGL(k_quant_e8m0<float>, dim3(blocks), dim3(kQuantThreads), 0, s, (const float*)x,
+                         rows, K, tail_copy, codes, scales);
+    return check_launch("mx_quantize(e8m0)");
+  }
+  uint32_t* partial = nullptr;
+  if (dynamic) {
+    partial = reinterpret_cast<uint32_t*>(ws);
+    if (bf)
+      hipLaunchKernelGGL(k_amax_partial<uint16_t>, dim3(kAmaxBlocks), dim3(kQuantThreads), 0, s,
+                         (const uint16_t*)x, total, partial);
+    else
+      hipLaunchKernelGGL(k_amax_partial<float>, dim3(kAmaxBlocks), dim3(kQuantThreads), 0, s,
+                         (const float*)x, total, partial);
+    if ((st = check_launch("mx_quantize(amax)"))) return st;
+  }
+  if (bf)
+    hipLaunchKernelGGL(k_quant_e4m3<uint16_t>, dim3(blocks), dim3(kQuantThreads), 0, s, (const uint16_t*)x,
+                       rows, K, codes, scales, tensor_scale, partial, kAmaxBlocks);
+  else
+    hipLaunchKernelGGL(k_quant_e4m3<float>, dim3(blocks), dim3(kQuantThreads), 0, s, (const float*)x, rows,
+                       K, codes, scales, tensor_scale, partial, kAmaxBlocks);
+  return check_launch("mx_quantize(e4m3)");
+}
+
+extern "C" int mx_dequantize(const gbw_weight* w, int32_t expert, float* out, void* stream) {
+  if (!w || !out) return fail(GBW_E_ARG, "mx_dequantize: null pointer");
+  if (w->N < 0 || w->K < 0 || expert < 0 || expert >= w->n_experts)
+    return fail(GBW_E_ARG, "mx_dequantize: bad extent or expert");
+  if (!w->codes || !w->scales) return fail(GBW_E_ARG, "mx_dequantize: null codes/scales");
+  const int64_t N = w->N, K = w->K;
+  int64_t cbytes, sbytes;
+  switch (w->fmt) {
+    case GBW_FMT_E8M0_B32:
+      if (K % 32) return fail(GBW_E_SHAPE, "mx_dequantize: K %% 32");
+      cbytes = N * K / 2;
+      sbytes = N * K / 32;
+      break;
+    case GBW_FMT_E4M3_B16:
+      if (K % 16) return fail(GBW_E_SHAPE, "mx_dequantize: K %% 16");
+      if (!w->tensor_scale || w->ts_per_expert < 1 || N % w->ts_per_expert)
+        return fail(GBW_E_ARG, "mx_dequantize: bad tensor scale");
+      cbytes = N * K / 2;
+      sbytes = N * K / 16;
+      break;
+    case GBW_FMT_VQ4_E8M0:
+      if (K % 64 || N % 64) return fail(GBW_E_SHAPE, "mx_dequantize: VQ needs N, K multiples of 64");
+      if (!w->codebook) return fail(GBW_E_ARG, "mx_dequantize: VQ needs a codebook");
+      cbytes = N * K / 4;
+      sbytes = N * K / 32;
+      break;
+    default:
+      return fail(GBW_E_ARG, "mx_dequantize: bad format");
+  }
+  if (N == 0 || K == 0) return GBW_OK;
+  int st = check_device();
+  if (st) return st;
+  const uint16_t* cb = w->codebook ? w->codebook + (int64_t)expert * (N / 64) * (K / 64) * 256 : nullptr;
+  const float* ts = w->tensor_scale ? w->tensor_scale + (int64_t)expert * w->ts_per_expert : nullptr;
+  const int64_t n = N * K;
+  hipLaunchKernelGGL(k_dequant, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, as_stream(stream), w->fmt,
+                     w->codes + expert * cbytes, w->scales + expert * sbytes, cb, ts,
+                     w->ts_per_expert > 0 ? w->ts_per_expert : 1, N, K, out);
+  return check_launch("mx_dequantize");
+}
+
+extern "C" int mx_residual(const float* w, int64_t N, int64_t K, int64_t tail, const uint8_t* codes,
+                           const uint8_t* scales, float* r, void* stream) {
+  if (N < 0 || K < 0 || tail < 0) return fail(GBW_E_ARG, "mx_residual: negative extent");
+  if (K % 32 || tail % 32 || tail > K) return fail(GBW_E_SHAPE, "mx_residual: bad K/tail");
+  if (N == 0 || tail == 0) return GBW_OK;
+  if (!w || !codes || !scales || !r) return fail(GBW_E_ARG, "mx_residual: null pointer");
+  int st = check_device();
+  if (st) return st;
+  const int64_t n = N * tail;
+  hipLaunchKernelGGL(k_residual, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, as_stream(stream), w, N, K,
+                     tail, codes, scales, r);
+  return check_launch("mx_residual");
+}

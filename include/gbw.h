@@ -1,0 +1,208 @@
+/*
+ * gbw.h -- 4-bit-weight GEMMs on AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  Every pointer argument named as a
+ * device buffer is a device address owned by the caller (in practice the
+ * data_ptr() of a torch tensor); descriptor structs are read during the call
+ * only.  Every call is asynchronous on `stream` (a hipStream_t passed as
+ * void*, NULL = the default stream); buffers must stay alive until the work
+ * on that stream completes.  No call synchronizes the device, and no compute
+ * entry point allocates device memory: where scratch is needed the caller
+ * passes a workspace sized by gbw_workspace_size().
+ *
+ * Error behaviour: arguments are validated on the host before anything is
+ * launched; a failed check returns a status code and launches nothing.  A
+ * launch failure returns GBW_E_LAUNCH.  gbw_last_error() gives a message for
+ * the last failure on the calling thread.  Nothing aborts or throws across
+ * the ABI.  Shapes with a zero extent (M = 0, T = 0, rows = 0) are no-ops.
+ *
+ * Formats (MXCode: MX-Native Codebook Quantization, Table 1):
+ *   GBW_FMT_E8M0_B32  E2M1 elements + one E8M0 scale per 32 along K (4.25 b/elt)
+ *   GBW_FMT_E4M3_B16  E2M1 elements + one E4M3 scale per 16 along K + one
+ *                     FP32 tensor scale (4.50 b/elt)
+ *   GBW_FMT_VQ4_E8M0  MXCode PreScale weights: 8-bit index per 4 consecutive K
+ *                     elements into a 256-entry table of 4xE2M1 keys per
+ *                     64x64 QBlock, plus the E8M0 per-32 prescale (abstract,
+ *                     Fig. 2, Fig. 3, Table 4 caption: d = 4, K = 256).
+ * E2M1 nibbles are packed two per byte, element 2i in bits 3:0, element 2i+1
+ * in bits 7:4, bit 3 of a nibble is the sign.  A VQ key holds element i of its
+ * 4-vector in bits 4i+3:4i.  All matrices are row-major; weights are [N][K]
+ * with K contiguous (the "K x N" weight of a linear layer stored per output
+ * column), activations [M][K].
+ */
+#ifndef GBW_H
+#define GBW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define GBW_OK 0
+#define GBW_E_ARG 1         /* null pointer, negative extent, bad enum        */
+#define GBW_E_SHAPE 2       /* K not a block multiple, tail misaligned, ...   */
+#define GBW_E_ALIGN 3       /* device pointer not 16-byte aligned             */
+#define GBW_E_UNSUPPORTED 4 /* format/dtype combination or device not gfx950  */
+#define GBW_E_WORKSPACE 5   /* workspace missing or smaller than required     */
+#define GBW_E_LAUNCH 6      /* a HIP launch failed                            */
+
+/* ---- enums -------------------------------------------------------------- */
+#define GBW_FMT_E8M0_B32 0
+#define GBW_FMT_E4M3_B16 1
+#define GBW_FMT_VQ4_E8M0 2
+
+#define GBW_DTYPE_BF16 0
+#define GBW_DTYPE_F32 1
+
+/* flags */
+#define GBW_TS_DYNAMIC 1     /* mx_quantize: compute the E4M3 tensor scale from the data */
+#define GBW_DETERMINISTIC 2  /* GEMMs: fixed summation order, bitwise repeatable          */
+
+/* moe_grouped_gemm stages */
+#define GBW_MOE_GATEUP_SWIGLU 0
+#define GBW_MOE_DOWN_COMBINE 1
+
+/* gbw_workspace_size ops */
+#define GBW_OP_QUANTIZE 0   /* d0 = rows, d1 = K                       */
+#define GBW_OP_MX_GEMM 1    /* d0 = M, d1 = N, d2 = K (+ tail)         */
+#define GBW_OP_LUT_GEMM 2   /* d0 = M, d1 = N, d2 = K                  */
+#define GBW_OP_MOE_ROUTE 3  /* d0 = T, d1 = E                          */
+#define GBW_OP_MOE_GEMM 4   /* d0 = pairs, d1 = N (output width)       */
+
+/* ---- descriptors -------------------------------------------------------- */
+
+/* A (possibly per-expert) quantized weight, each expert an [N][K] matrix. */
+typedef struct gbw_weight {
+  int32_t fmt;               /* GBW_FMT_*                                          */
+  int32_t n_experts;         /* >= 1; expert e starts at e * (per-expert size)     */
+  int64_t N, K;              /* per expert                                         */
+  const uint8_t* codes;      /* E8M0/E4M3: [E][N][K/2] nibbles; VQ: [E][N][K/4] idx */
+  const uint8_t* scales;     /* E8M0 and VQ: [E][N][K/32] E8M0; E4M3: [E][N][K/16]  */
+  const uint16_t* codebook;  /* VQ only: [E][N/64][K/64][256] keys, else NULL       */
+  const float* tensor_scale; /* E4M3 only: [E][ts_per_expert] fp32, else NULL       */
+  int32_t ts_per_expert;     /* E4M3: rows split into this many equal segments,
+                                segment s scaled by tensor_scale[e][s] (1 or 2)     */
+} gbw_weight;
+
+/* A quantized activation: [rows][K], K contiguous. */
+typedef struct gbw_act {
+  int32_t fmt;               /* GBW_FMT_E8M0_B32 or GBW_FMT_E4M3_B16               */
+  int64_t rows, K;
+  const uint8_t* codes;      /* [rows][K/2]                                        */
+  const uint8_t* scales;     /* [rows][K/32] (E8M0) or [rows][K/16] (E4M3)         */
+  const float* tensor_scale; /* E4M3: device fp32[1]; else NULL                    */
+} gbw_act;
+
+/* ---- utility ------------------------------------------------------------ */
+const char* gbw_status_string(int status);
+const char* gbw_last_error(void);
+/* Bytes of workspace an op needs for the given extents (0 = none). */
+size_t gbw_workspace_size(int32_t op, int64_t d0, int64_t d1, int64_t d2, int32_t fmt);
+
+/* ---- online activation quantization ------------------------------------
+ * mx_quantize: x [rows][K] (bf16 or fp32) -> codes [rows][(K+tail_copy)/2],
+ * scales [rows][(K+tail_copy)/bs].
+ *  E8M0-B32 (MXFP4): per block of 32, scale code = max(0, E(amax) - 2) with
+ *    E the fp32 exponent field (OCP MX floor rule), element = RNE onto E2M1,
+ *    ties to even, saturating at 6, sign kept.
+ *  E4M3-B16: S_T = amax_tensor / 2688 (1 if the tensor is zero); per block
+ *    of 16, scale = E4M3_RNE_sat(amax_blk / (6 S_T)), element =
+ *    RNE(|x| / (scale * S_T)); each step one fp32 operation.  With
+ *    GBW_TS_DYNAMIC, amax_tensor is computed from x and S_T written to
+ *    tensor_scale[0] (workspace required); otherwise S_T is read from
+ *    tensor_scale[0].
+ *  tail_copy > 0 (E8M0 only, multiple of 32, <= K) appends a copy of the
+ *    quantized last tail_copy columns with their scales: PRQuant:
+ *    Permutation Residual Quantization for Low-Overhead Inference, §4
+ *    "Kernel design for efficient inference" (online copy).
+ * Errors: GBW_E_SHAPE if K is not a multiple of the block size.
+ */
+int mx_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t K, int32_t fmt,
+                int64_t tail_copy, uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                int32_t flags, void* ws, size_t ws_bytes, void* stream);
+
+/* mx_dequantize: decode expert `expert` of w to fp32 out [N][K] through the
+ * same device decoders the GEMMs use (E8M0: e2m1*2^(s-127); E4M3:
+ * e2m1*scale*tensor_scale[segment]; VQ: QBlock table key nibble * 2^(s-127)).
+ * Used to check decoded weights bit for bit and for offline preparation. */
+int mx_dequantize(const gbw_weight* w, int32_t expert, float* out, void* stream);
+
+/* mx_residual: PRQuant §4 Eq. (2) offline weight residual,
+ * r[n][j] = w[n][K-tail+j] - deq(codes, scales)[n][K-tail+j] (fp32 RNE),
+ * for w [N][K] fp32 and its E8M0-B32 quantization; r is [N][tail]. */
+int mx_residual(const float* w, int64_t N, int64_t K, int64_t tail, const uint8_t* codes,
+                const uint8_t* scales, float* r, void* stream);
+
+/* ---- dense GEMMs ---------------------------------------------------------
+ * mx_gemm: y[M][N] fp32 = deq(a) deq(w)^T, a [M][K] and w [N][K] both
+ * E8M0-B32 (scaled MFMA, FP4 x FP4).  K must be a multiple of 32.
+ * Without GBW_DETERMINISTIC the reduction over K may be split across
+ * workgroups and combined with fp32 atomics (y is overwritten either way).
+ */
+int mx_gemm(int64_t M, const gbw_act* a, const gbw_weight* w, float* y, int32_t flags,
+            void* stream);
+
+/* residual_tail_gemm: the augmented MXFP4 GEMM of PRQuant §4 ("Offline
+ * residual augmentation", W_aug^q = Q([W, R_W]), and "Kernel design"):
+ *   y = deq(a) deq(w)^T + deq(a[:, K-tail:]) deq(r)^T
+ * a [M][K] E8M0-B32 (the tail is re-read in place, no copy), w [N][K],
+ * r [N][tail] the quantized residual.  tail % 32 == 0, tail <= K. */
+int residual_tail_gemm(int64_t M, const gbw_act* a, const gbw_weight* w, const gbw_weight* r,
+                       int64_t tail, float* y, int32_t flags, void* stream);
+
+/* lut_gemm: codebook weights (CodeQuant: Unified Clustering and Quantization
+ * for Enhanced Outlier Smoothing in Low-Precision Mixture-of-Experts,
+ * Fig. 1 stage 3-4, Fig. 4):
+ *   y[m][n] = sum_k bf16(x[m][k]) * fp16(centroids[n][k/group][idx[n][k]])
+ * x [M][K] bf16 bits, idx [N][K/2] 4-bit indices, centroids [N][K/group][16]
+ * fp16 bits, y [M][N] fp32.  group in {32, 64, 128}, K % group == 0.
+ * ws: gbw_workspace_size(GBW_OP_LUT_GEMM, M, N, K, 0) bytes (may be 0). */
+int lut_gemm(int64_t M, int64_t N, int64_t K, int32_t group, const uint16_t* x_bf16,
+             const uint8_t* idx, const uint16_t* centroids_f16, float* y, int32_t flags,
+             void* ws, size_t ws_bytes, void* stream);
+
+/* ---- MoE ------------------------------------------------------------------
+ * moe_route: logits [T][E] fp32 -> top-k experts per token (largest logit
+ * first, ties to the lower expert id), weights softmax-renormalised over the
+ * k chosen, and the pair list sorted by (expert, token):
+ *   topk_ids [T][k] i32, topk_w [T][k] f32, expert_offsets [E+1] i32,
+ *   pair_token [T*k] i32, pair_pos [T][k] i32 (index of the pair in the list).
+ * E <= 1024, 1 <= k <= min(E, 16).  ws: gbw_workspace_size(GBW_OP_MOE_ROUTE, T, E, 0, 0). */
+int moe_route(const float* logits, int64_t T, int32_t E, int32_t topk, int32_t* topk_ids,
+              float* topk_w, int32_t* expert_offsets, int32_t* pair_token, int32_t* pair_pos,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* moe_grouped_gemm: one stage of the routed expert FFN (gated MLP of PRQuant
+ * §4 Eq. (1), applied per expert as in CodeQuant Fig. 1-2):
+ *  GBW_MOE_GATEUP_SWIGLU: for each pair p=(t,e): g,u = deq(a[t]) deq(w_e)^T
+ *    with w_e the fused [2I][H] gate/up weight (gate rows first);
+ *    h = bf16(silu(g) * u).  Writes h_bf16 [P][I] if non-NULL and, for
+ *    E8M0-B32 activations, the quantized h into h_codes [P][I/2] / h_scales
+ *    [P][I/32] (the requantization is fused).  For E4M3-B16 only h_bf16 is
+ *    written; quantize it with mx_quantize(GBW_TS_DYNAMIC).
+ *  GBW_MOE_DOWN_COMBINE: y[t] = sum_j topk_w[t][j] * deq(a[pair_pos[t][j]])
+ *    deq(w_e)^T, a = quantized h in pair order, y [T][H] fp32 (overwritten).
+ * Weights: E8M0-B32, VQ4-E8M0 (decoded to MXFP4 in LDS, scaled MFMA) or
+ * E4M3-B16 (decoded exactly to bf16, bf16 MFMA).  The activation format must
+ * be E4M3-B16 for E4M3-B16 weights and E8M0-B32 otherwise.
+ * ws: gbw_workspace_size(GBW_OP_MOE_GEMM, P, N, 0, fmt) bytes. */
+typedef struct gbw_moe_out {
+  uint16_t* h_bf16;   /* GATEUP: [P][I] bf16 bits or NULL            */
+  uint8_t* h_codes;   /* GATEUP, E8M0: [P][I/2] or NULL               */
+  uint8_t* h_scales;  /* GATEUP, E8M0: [P][I/32] or NULL              */
+  float* y;           /* DOWN: [T][H]                                 */
+} gbw_moe_out;
+
+int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const int32_t* expert_offsets,
+                     const int32_t* pair_token, const int32_t* pair_pos, const float* topk_w,
+                     const gbw_act* a, const gbw_weight* w, const gbw_moe_out* out,
+                     int32_t flags, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GBW_H */

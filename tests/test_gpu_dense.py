@@ -1,0 +1,247 @@
+"""GPU parity: online quantization, decode, MXFP4 GEMM and the PRQuant
+tail-residual GEMM against the oracle.
+
+Encodings, decoded weights and residuals must match bit for bit; GEMM outputs
+must satisfy max_n |y - y_ref| <= 1e-3 * ||y_ref row||_2 (the oracle's value
+is the exact value of the quantized GEMM), and integer-valued cases must be
+bit-exact.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import assert_rows_close, banner, to_np
+
+pytestmark = pytest.mark.gpu
+
+try:
+    import gemm_bit_weight_amd as gbw
+except ImportError as e:  # collected on CPU-only hosts too; the GPU run must have the library
+    gbw = None
+    _IMPORT_ERROR = e
+
+DEV = "cuda"
+
+
+def _q8(x_t):
+    """oracle E8M0 quantization of a torch tensor (bf16 or fp32)."""
+    return oracle.quantize_e8m0_b32(x_t.float().cpu().numpy())
+
+
+def _gpu_act(codes, scales, fmt=0, ts=None):
+    return gbw.Act(fmt, torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
+                   None if ts is None else torch.tensor([ts], dtype=torch.float32, device=DEV))
+
+
+def _gpu_w(codes, scales):
+    N = codes.shape[0]
+    return gbw.Weight(gbw.FMT_E8M0_B32, N, codes.shape[1] * 2, torch.from_numpy(codes).to(DEV),
+                      torch.from_numpy(scales).to(DEV))
+
+
+def setup_module():
+    assert gbw is not None, f"HIP library missing: {_IMPORT_ERROR}"
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+
+
+# ---------------------------------------------------------------------------
+# quantizers
+# ---------------------------------------------------------------------------
+
+def _special_rows(K):
+    x = np.zeros((6, K), np.float32)
+    x[1, :] = -0.0
+    x[2, ::3] = 1e-40                    # subnormal block amax
+    x[3, :] = np.tile([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.5], K // 8)  # midpoints at scale 2^-1
+    x[3, 7::8] = 4.0
+    x[4, :] = np.tile([3e38, -1.0, 1e-30, 7.9], K // 4)
+    x[5, :] = np.linspace(-1000, 1000, K)
+    return x
+
+
+@pytest.mark.parametrize("rows,K,dtype", [(16, 512, "bf16"), (512, 512, "f32"), (13, 96, "bf16"),
+                                          (128, 9728, "bf16"), (2560, 9728, "f32"), (6, 256, "special")])
+def test_quantize_e8m0_bitexact(rows, K, dtype):
+    banner(f"quantize e8m0 {rows}x{K} {dtype}")
+    if dtype == "special":
+        x = torch.from_numpy(_special_rows(K)).to(DEV)
+    else:
+        d = synth.dense_linear(rows, 8, K, seed=1, device=DEV)
+        x = d["x"] if dtype == "bf16" else synth.normal((rows, K), 0.02, 1, "q.w", DEV)
+    a = gbw.mx_quantize(x.contiguous(), gbw.FMT_E8M0_B32)
+    c, s = _q8(x)
+    assert np.array_equal(to_np(a.scales), s)
+    assert np.array_equal(to_np(a.codes), c)
+
+
+def test_quantize_tail_copy_bitexact():
+    banner("quantize e8m0 tail copy 128x9728 tail 256")
+    p = synth.tail_residual_problem(128, 64, 9728, seed=0, device=DEV)
+    a = gbw.mx_quantize(p["x"], gbw.FMT_E8M0_B32, tail_copy=256)
+    c, s = _q8(p["x"])
+    cc, ss = oracle.tail_copy(c, s, 256)
+    assert np.array_equal(to_np(a.codes), cc)
+    assert np.array_equal(to_np(a.scales), ss)
+
+
+@pytest.mark.parametrize("rows,K,dtype,static", [(64, 2048, "bf16", False), (37, 48, "f32", False),
+                                                 (300, 768, "bf16", True), (6, 256, "special", False)])
+def test_quantize_e4m3_bitexact(rows, K, dtype, static):
+    banner(f"quantize e4m3 {rows}x{K} {dtype} static={static}")
+    if dtype == "special":
+        x = torch.from_numpy(_special_rows(K)[:, :K]).to(DEV)
+        x[4] = x[5]                                   # keep the tensor amax finite and moderate
+    elif dtype == "bf16":
+        x = synth.normal((rows, K), 1.0, 2, "q4.x", DEV).to(torch.bfloat16)
+    else:
+        x = synth.normal((rows, K), 0.02, 2, "q4.w", DEV)
+    xn = x.float().cpu().numpy()
+    if static:
+        amax = np.float32(7.5)
+        ts = torch.tensor([oracle.formats.tensor_scale_e4m3(amax)], dtype=torch.float32, device=DEV)
+        a = gbw.mx_quantize(x, gbw.FMT_E4M3_B16, tensor_scale=ts, dynamic=False)
+        c, s, st = oracle.quantize_e4m3_b16(xn, tensor_amax=amax)
+    else:
+        a = gbw.mx_quantize(x, gbw.FMT_E4M3_B16)
+        c, s, st = oracle.quantize_e4m3_b16(xn)
+    assert to_np(a.tensor_scale)[0] == st
+    assert np.array_equal(to_np(a.scales), s)
+    assert np.array_equal(to_np(a.codes), c)
+
+
+def test_quantize_e4m3_empty_tensor_scale():
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    a = gbw.mx_quantize(x, gbw.FMT_E4M3_B16)
+    assert to_np(a.tensor_scale)[0] == 1.0
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+def test_dequantize_e8m0_and_e4m3_bitexact():
+    banner("dequantize e8m0/e4m3")
+    w = synth.normal((192, 512), 0.02, 3, "dq.w", "cpu").numpy()
+    c, s = oracle.quantize_e8m0_b32(w)
+    out = gbw.mx_dequantize(_gpu_w(c, s))
+    assert np.array_equal(to_np(out).astype(np.float64), oracle.dequantize(c, s, "e8m0_b32"))
+    # E4M3 with two tensor-scale segments (gate rows, up rows)
+    cg, sg, tg = oracle.quantize_e4m3_b16(w[:96])
+    cu, su, tu = oracle.quantize_e4m3_b16(w[96:] * 3)
+    W = gbw.Weight(gbw.FMT_E4M3_B16, 192, 512, torch.from_numpy(np.concatenate([cg, cu])).to(DEV),
+                   torch.from_numpy(np.concatenate([sg, su])).to(DEV), None,
+                   torch.tensor([tg, tu], dtype=torch.float32, device=DEV), 2, 1)
+    out = to_np(gbw.mx_dequantize(W))
+    ref = np.concatenate([oracle.dequantize(cg, sg, "e4m3_b16", tg), oracle.dequantize(cu, su, "e4m3_b16", tu)])
+    assert np.array_equal(out.astype(np.float64), ref.astype(np.float32).astype(np.float64))
+
+
+def test_dequantize_vq_bitexact():
+    banner("dequantize vq")
+    v = synth.vq_weight(3, 128, 192, seed=4, device="cpu")
+    W = gbw.Weight(gbw.FMT_VQ4_E8M0, 128, 192, v["idx"].to(DEV), v["scales"].to(DEV), v["codebook"].to(DEV),
+                   None, 1, 3)
+    cb = v["codebook"].numpy().view(np.uint16)
+    for e in range(3):
+        out = to_np(gbw.mx_dequantize(W, expert=e))
+        ref = oracle.vq_dequantize(v["idx"][e].numpy(), cb[e], v["scales"][e].numpy())
+        assert np.array_equal(out.astype(np.float64), ref)
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 GEMM
+# ---------------------------------------------------------------------------
+
+def _dense_case(M, N, K, seed):
+    d = synth.dense_linear(M, N, K, seed=seed, device=DEV)
+    a = gbw.mx_quantize(d["x"], gbw.FMT_E8M0_B32)
+    wq = gbw.mx_quantize(d["w"], gbw.FMT_E8M0_B32)
+    w = gbw.weight_from_act(wq)
+    ref = oracle.mx_gemm(to_np(a.codes), to_np(a.scales), to_np(wq.codes), to_np(wq.scales))
+    return a, w, ref
+
+
+def test_mx_gemm_single_linear_16x512x512():
+    banner("mx_gemm 16x512x512 seed 0")
+    a, w, ref = _dense_case(16, 512, 512, 0)
+    y = gbw.mx_gemm(a, w)
+    assert_rows_close(to_np(y), ref, what="mx_gemm 16x512x512")
+    y1 = gbw.mx_gemm(a, w, flags=gbw.DETERMINISTIC)
+    y2 = gbw.mx_gemm(a, w, flags=gbw.DETERMINISTIC)
+    assert torch.equal(y1, y2)
+    assert_rows_close(to_np(y1), ref, what="deterministic")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (5, 20, 96), (17, 300, 160), (33, 64, 544), (100, 129, 1056),
+                                   (128, 2560, 9728), (200, 70, 256)])
+def test_mx_gemm_ragged(M, N, K):
+    banner(f"mx_gemm {M}x{N}x{K}")
+    a, w, ref = _dense_case(M, N, K, 7)
+    assert_rows_close(to_np(gbw.mx_gemm(a, w)), ref, what=f"mx_gemm {M}x{N}x{K}")
+    assert_rows_close(to_np(gbw.mx_gemm(a, w, flags=gbw.DETERMINISTIC)), ref, what="det")
+
+
+def test_mx_gemm_integer_special_case_bitexact():
+    """All scales 127: Y = int64 GEMM / 4 exactly (|Y| < 2^22)."""
+    banner("mx_gemm integer case")
+    rng = np.random.default_rng(30)
+    M, N, K = 48, 96, 1024
+    a = rng.integers(0, 16, (M, K))
+    w = rng.integers(0, 16, (N, K))
+    twice = np.array([0, 1, 2, 3, 4, 6, 8, 12])
+    ai = np.where(a & 8, -twice[a & 7], twice[a & 7]).astype(np.int64)
+    wi = np.where(w & 8, -twice[w & 7], twice[w & 7]).astype(np.int64)
+    A = _gpu_act(oracle.pack_nibbles(a), np.full((M, K // 32), 127, np.uint8))
+    W = _gpu_w(oracle.pack_nibbles(w), np.full((N, K // 32), 127, np.uint8))
+    want = (ai @ wi.T).astype(np.float64) / 4
+    assert np.abs(want).max() < 2 ** 22
+    for flags in (0, gbw.DETERMINISTIC):
+        y = to_np(gbw.mx_gemm(A, W, flags=flags)).astype(np.float64)
+        assert np.array_equal(y, want)
+
+
+# ---------------------------------------------------------------------------
+# PRQuant residual
+# ---------------------------------------------------------------------------
+
+def _tail_case(M, N, K, tail, seed=0):
+    p = synth.tail_residual_problem(M, N, K, tail=tail, seed=seed, device=DEV)
+    a = gbw.mx_quantize(p["x"], gbw.FMT_E8M0_B32)
+    wq = gbw.mx_quantize(p["w"], gbw.FMT_E8M0_B32)
+    r = gbw.mx_residual(p["w"], wq.codes, wq.scales, tail)
+    rq = gbw.mx_quantize(r, gbw.FMT_E8M0_B32)
+    return p, a, wq, r, rq
+
+
+def test_mx_residual_bitexact():
+    banner("mx_residual 256x2048 tail 256")
+    p, a, wq, r, rq = _tail_case(8, 256, 2048, 256)
+    ref = oracle.residual_weight(to_np(p["w"]), to_np(wq.codes), to_np(wq.scales), 256)
+    assert np.array_equal(to_np(r), ref)
+
+
+@pytest.mark.parametrize("M,N,K,tail", [(8, 256, 2048, 256), (13, 100, 1024, 96), (128, 2560, 9728, 256),
+                                        (64, 64, 512, 0)])
+def test_residual_tail_gemm(M, N, K, tail):
+    banner(f"residual_tail_gemm {M}x{N}x{K} tail {tail}")
+    p, a, wq, r, rq = _tail_case(M, N, K, max(tail, 96))
+    t = tail
+    w = gbw.weight_from_act(wq)
+    rw = gbw.weight_from_act(rq) if t else None
+    ref = oracle.residual_tail_gemm(to_np(a.codes), to_np(a.scales), to_np(wq.codes), to_np(wq.scales),
+                                    to_np(rq.codes)[:, :t // 2] if t else to_np(rq.codes)[:, :0],
+                                    to_np(rq.scales)[:, :t // 32] if t else to_np(rq.scales)[:, :0], t)
+    y = to_np(gbw.residual_tail_gemm(a, w, rw, t))
+    assert_rows_close(y, ref, what="residual_tail_gemm")
+    yd = to_np(gbw.residual_tail_gemm(a, w, rw, t, flags=gbw.DETERMINISTIC))
+    assert_rows_close(yd, ref, what="residual_tail_gemm det")
+    if t:
+        # the augmented GEMM is the plain GEMM over [A, A_tail] x [W, R]
+        at = gbw.mx_quantize(p["x"], gbw.FMT_E8M0_B32, tail_copy=t)
+        wcat = torch.cat([p["w"], r], dim=1).contiguous()
+        waug = gbw.weight_from_act(gbw.mx_quantize(wcat, gbw.FMT_E8M0_B32))
+        yaug = to_np(gbw.mx_gemm(at, waug, flags=gbw.DETERMINISTIC))
+        assert_rows_close(yaug, ref, what="augmented")
