@@ -79,10 +79,10 @@ _lib.mx_dequantize.argtypes = [_c.POINTER(_Weight), _i32, _vp, _vp]
 _lib.mx_residual.restype = _c.c_int
 _lib.mx_residual.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]
 _lib.mx_gemm.restype = _c.c_int
-_lib.mx_gemm.argtypes = [_i64, _c.POINTER(_Act), _c.POINTER(_Weight), _vp, _i32, _vp]
+_lib.mx_gemm.argtypes = [_i64, _c.POINTER(_Act), _c.POINTER(_Weight), _vp, _i32, _vp, _c.c_size_t, _vp]
 _lib.residual_tail_gemm.restype = _c.c_int
 _lib.residual_tail_gemm.argtypes = [_i64, _c.POINTER(_Act), _c.POINTER(_Weight), _c.POINTER(_Weight), _i64, _vp,
-                                    _i32, _vp]
+                                    _i32, _vp, _c.c_size_t, _vp]
 _lib.lut_gemm.restype = _c.c_int
 _lib.lut_gemm.argtypes = [_i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _c.c_size_t, _vp]
 _lib.moe_route.restype = _c.c_int
@@ -237,23 +237,39 @@ def weight_from_act(a: Act) -> Weight:
     return Weight(a.fmt, a.rows, a.K, a.codes, a.scales, None, a.tensor_scale, 1, 1)
 
 
-def mx_gemm(a: Act, w: Weight, M=None, out=None, flags=0, stream=None):
+def _ws(ws, nbytes, device):
+    if ws is None and nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, (ws.numel() if ws is not None else 0)
+
+
+def mx_gemm(a: Act, w: Weight, M=None, out=None, flags=0, ws=None, stream=None):
+    """y = deq(a) deq(w)^T.  ``ws=False`` runs without a workspace."""
     M = a.rows if M is None else M
     if out is None:
         out = torch.empty((M, w.N), dtype=torch.float32, device=a.codes.device)
+    if ws is False:
+        ws, wsb = None, 0
+    else:
+        ws, wsb = _ws(ws, workspace_size(OP_MX_GEMM, M, w.N, w.K), a.codes.device)
     ca, cw = a.c(), w.c()
-    _check(_lib.mx_gemm(M, _c.byref(ca), _c.byref(cw), _ptr(out), flags, _stream(stream)))
+    _check(_lib.mx_gemm(M, _c.byref(ca), _c.byref(cw), _ptr(out), flags, _ptr(ws), wsb, _stream(stream)))
     return out
 
 
-def residual_tail_gemm(a: Act, w: Weight, r: Optional[Weight], tail, M=None, out=None, flags=0, stream=None):
+def residual_tail_gemm(a: Act, w: Weight, r: Optional[Weight], tail, M=None, out=None, flags=0, ws=None,
+                       stream=None):
     M = a.rows if M is None else M
     if out is None:
         out = torch.empty((M, w.N), dtype=torch.float32, device=a.codes.device)
+    if ws is False:
+        ws, wsb = None, 0
+    else:
+        ws, wsb = _ws(ws, workspace_size(OP_MX_GEMM, M, w.N, w.K + tail), a.codes.device)
     ca, cw = a.c(), w.c()
     cr = r.c() if r is not None else None
     _check(_lib.residual_tail_gemm(M, _c.byref(ca), _c.byref(cw), _c.byref(cr) if cr is not None else None, tail,
-                                   _ptr(out), flags, _stream(stream)))
+                                   _ptr(out), flags, _ptr(ws), wsb, _stream(stream)))
     return out
 
 

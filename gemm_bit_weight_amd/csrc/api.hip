@@ -60,6 +60,30 @@ __global__ void k_fill_zero(float* __restrict__ p, int64_t n) {
   for (; i < n; i += stride) p[i] = 0.0f;
 }
 
+// Sum split-K partials [splits][mn] in split order (a fixed order, so the
+// result is bitwise repeatable), four outputs per thread.
+__global__ void k_splitk_reduce(const float* __restrict__ part, int splits, int64_t mn, float* __restrict__ y) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= mn) return;
+  if (i + 4 <= mn) {
+    v4f acc = *reinterpret_cast<const v4f*>(part + i);
+    for (int s = 1; s < splits; ++s) acc += *reinterpret_cast<const v4f*>(part + (int64_t)s * mn + i);
+    *reinterpret_cast<v4f*>(y + i) = acc;
+  } else {
+    for (int64_t j = i; j < mn; ++j) {
+      float a = part[j];
+      for (int s = 1; s < splits; ++s) a += part[(int64_t)s * mn + j];
+      y[j] = a;
+    }
+  }
+}
+
+int launch_splitk_reduce(const float* part, int splits, int64_t mn, float* y, hipStream_t st) {
+  if (mn <= 0) return GBW_OK;
+  hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)cdiv(cdiv(mn, 4), 256)), dim3(256), 0, st, part, splits, mn, y);
+  return check_launch("splitk_reduce");
+}
+
 int launch_fill_zero(float* p, int64_t n, hipStream_t st) {
   if (n <= 0) return GBW_OK;
   int64_t blocks = cdiv(n, 256);
@@ -76,6 +100,7 @@ size_t ws_quantize(int64_t rows, int64_t K, int32_t fmt);
 size_t ws_moe_route(int64_t T, int64_t E);
 size_t ws_moe_gemm(int64_t P, int64_t N, int32_t fmt);
 size_t ws_lut_gemm(int64_t M, int64_t N, int64_t K);
+size_t ws_mx_gemm(int64_t M, int64_t N, int64_t Ktot);
 }  // namespace gbw
 
 extern "C" {
@@ -98,7 +123,7 @@ const char* gbw_last_error(void) { return gbw::g_err; }
 size_t gbw_workspace_size(int32_t op, int64_t d0, int64_t d1, int64_t d2, int32_t fmt) {
   switch (op) {
     case GBW_OP_QUANTIZE: return gbw::ws_quantize(d0, d1, fmt);
-    case GBW_OP_MX_GEMM: return 0;
+    case GBW_OP_MX_GEMM: return gbw::ws_mx_gemm(d0, d1, d2);
     case GBW_OP_LUT_GEMM: return gbw::ws_lut_gemm(d0, d1, d2);
     case GBW_OP_MOE_ROUTE: return gbw::ws_moe_route(d0, d1);
     case GBW_OP_MOE_GEMM: return gbw::ws_moe_gemm(d0, d1, fmt);

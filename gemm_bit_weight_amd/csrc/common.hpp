@@ -114,4 +114,6 @@ int device_cu_count();
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 int launch_fill_zero(float* p, int64_t n, hipStream_t st);
+// y[i] = sum_s part[s][i] over s = 0..splits-1, in that order
+int launch_splitk_reduce(const float* part, int splits, int64_t mn, float* y, hipStream_t st);
 }  // namespace gbw

@@ -44,8 +44,31 @@ struct MxGemmArgs {
   int32_t total_steps, steps_per_split;
   float* y;
   int64_t ldy;
-  int32_t atomic;
+  int32_t atomic;  // 1: K is split over workgroups, partials go to `part`
+  float* part;     // [splits][M][N] fp32 workspace
 };
+
+// Fields of the segment that K step s belongs to.  Selected with uniform
+// conditionals (never a dynamic index into the argument struct, which would
+// force the arguments through memory and serialize the loads).
+struct StepSeg {
+  const uint8_t* wc;
+  const uint8_t* ws;
+  int64_t ldw, ldws, a_k0, K, k;  // k: first K element of step s within the segment
+};
+
+__device__ __forceinline__ StepSeg step_seg(const MxGemmArgs& p, int s) {
+  const bool b = s >= p.seg[0].steps;
+  StepSeg r;
+  r.wc = b ? p.seg[1].w_codes : p.seg[0].w_codes;
+  r.ws = b ? p.seg[1].w_scales : p.seg[0].w_scales;
+  r.ldw = b ? p.seg[1].ldw : p.seg[0].ldw;
+  r.ldws = b ? p.seg[1].ldws : p.seg[0].ldws;
+  r.a_k0 = b ? p.seg[1].a_k0 : p.seg[0].a_k0;
+  r.K = b ? p.seg[1].K : p.seg[0].K;
+  r.k = (int64_t)(b ? s - p.seg[0].steps : s) * 128;
+  return r;
+}
 
 __device__ __forceinline__ v8i widen(v4i x) {
   v8i r;
@@ -60,31 +83,74 @@ __device__ __forceinline__ v8i widen(v4i x) {
   return r;
 }
 
-template <int TM, int TN, int NW>
+// One workgroup: NW waves, each owning 16*TN output columns; all waves share
+// the 16*TM rows of A and one contiguous range of at most SMAX K steps (128
+// elements each).  The A range is staged once in LDS (rows padded by 16 bytes
+// so the 16 lanes of a fragment read spread over the banks); every weight load
+// of the range is issued before the first MFMA so the whole weight slice is in
+// flight at once.
+template <int TM, int TN, int NW, int SMAX>
 __global__ __launch_bounds__(64 * NW) void k_mx_gemm(const MxGemmArgs p) {
+  constexpr int ROWS = 16 * TM;
+  constexpr int LDA = SMAX * 64 + 16;             // LDS bytes per A row
+  constexpr int CHUNKS = ROWS * SMAX * 4;         // 16-byte A chunks (one E8M0 block each)
+  constexpr int PER = CHUNKS / (64 * NW);         // chunks per thread
+  static_assert(CHUNKS % (64 * NW) == 0, "A range must split evenly over the workgroup");
+  __shared__ __attribute__((aligned(16))) uint8_t sa[ROWS * LDA];
+  __shared__ uint8_t ss[ROWS * SMAX * 4];
+
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  const int64_t m0 = (int64_t)blockIdx.z * (16 * TM);
+  const int64_t m0 = (int64_t)blockIdx.z * ROWS;
   const int64_t n0 = ((int64_t)blockIdx.x * NW + wave) * (16 * TN);
-  if (n0 >= p.N) return;
-  const int s_begin = blockIdx.y * p.steps_per_split;
-  const int s_end = min(p.total_steps, s_begin + p.steps_per_split);
+  const int s0 = blockIdx.y * p.steps_per_split;
+  const int ns = min(p.total_steps - s0, p.steps_per_split);
 
-  const uint8_t* arow[TM];
-  const uint8_t* asrow[TM];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    int64_t r = m0 + 16 * i + r16;
-    r = r < p.M ? r : p.M - 1;
-    arow[i] = p.a_codes + r * p.lda;
-    asrow[i] = p.a_scales + r * p.ldas;
-  }
-  int64_t wrow[TN];
+  // --- weight slice: straight-line loads, all in flight at once -----------
+  // Steps past this split's range re-read its last step (their A is zero);
+  // blocks past the segment end re-read its last block (A is zero there too).
+  v4i bq[SMAX][TN];
+  int bsc[SMAX][TN];
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     int64_t n = n0 + 16 * j + r16;
-    wrow[j] = n < p.N ? n : p.N - 1;
+    n = n < p.N ? n : p.N - 1;
+#pragma unroll
+    for (int t = 0; t < SMAX; ++t) {
+      const StepSeg sg = step_seg(p, s0 + (t < ns ? t : ns - 1));
+      int64_t kk = sg.k + 32 * g;
+      kk = kk < sg.K ? kk : sg.K - 32;
+      bq[t][j] = load16(sg.wc + n * sg.ldw + kk / 2);
+      bsc[t][j] = sg.ws[n * sg.ldws + kk / 32];
+    }
   }
+
+  // --- activation range: batched loads, then LDS -------------------------
+  v4i av[PER];
+  uint32_t asv[PER];
+  bool ok[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int c = threadIdx.x + u * 64 * NW;
+    const int row = c / (SMAX * 4), q = c % (SMAX * 4), t = q >> 2, blk = q & 3;
+    int64_t m = m0 + row;
+    m = m < p.M ? m : p.M - 1;
+    const StepSeg sg = step_seg(p, s0 + (t < ns ? t : ns - 1));
+    int64_t kk = sg.k + 32 * blk;
+    ok[u] = t < ns && kk < sg.K;
+    kk = kk < sg.K ? kk : sg.K - 32;
+    const int64_t ka = sg.a_k0 + kk;
+    av[u] = load16(p.a_codes + m * p.lda + ka / 2);
+    asv[u] = p.a_scales[m * p.ldas + ka / 32];
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int c = threadIdx.x + u * 64 * NW;
+    const int row = c / (SMAX * 4), q = c % (SMAX * 4);
+    *reinterpret_cast<v4i*>(sa + row * LDA + q * 16) = ok[u] ? av[u] : v4i{0, 0, 0, 0};
+    ss[row * SMAX * 4 + q] = (uint8_t)(ok[u] ? asv[u] : 127u);
+  }
+  __syncthreads();
 
   v4f acc[TM][TN];
 #pragma unroll
@@ -92,31 +158,22 @@ __global__ __launch_bounds__(64 * NW) void k_mx_gemm(const MxGemmArgs p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int s = s_begin; s < s_end; ++s) {
-    const int si = s < p.seg[0].steps ? 0 : 1;
-    const MxSeg& sg = p.seg[si];
-    const int64_t kk = (int64_t)(s - (si ? p.seg[0].steps : 0)) * 128 + 32 * g;
-    const bool valid = kk < sg.K;
-    v4i af[TM], bf[TN];
-    int as[TM], bs[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int64_t ka = sg.a_k0 + kk;
-      af[i] = valid ? load16(arow[i] + ka / 2) : v4i{0, 0, 0, 0};
-      as[i] = valid ? (int)asrow[i][ka / 32] : 127;
+  for (int t = 0; t < SMAX; ++t) {
+    if (t < ns) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = 16 * i + r16;
+        const v4i af = *reinterpret_cast<const v4i*>(sa + row * LDA + t * 64 + g * 16);
+        const int as = ss[row * SMAX * 4 + t * 4 + g];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(widen(af), widen(bq[t][j]), acc[i][j], 4, 4,
+                                                                        0, as, 0, bsc[t][j]);
+      }
     }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      bf[j] = valid ? load16(sg.w_codes + wrow[j] * sg.ldw + kk / 2) : v4i{0, 0, 0, 0};
-      bs[j] = valid ? (int)sg.w_scales[wrow[j] * sg.ldws + kk / 32] : 127;
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(widen(af[i]), widen(bf[j]), acc[i][j], 4, 4,
-                                                                      0, as[i], 0, bs[j]);
   }
+  if (n0 >= p.N) return;
 
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -128,36 +185,96 @@ __global__ __launch_bounds__(64 * NW) void k_mx_gemm(const MxGemmArgs p) {
       for (int q = 0; q < 4; ++q) {
         const int64_t m = m0 + 16 * i + 4 * g + q;
         if (m >= p.M) continue;
-        float* dst = p.y + m * p.ldy + n;
-        if (p.atomic)
-          unsafeAtomicAdd(dst, acc[i][j][q]);
-        else
-          *dst = acc[i][j][q];
+        // one split: the output itself; several: this split's slab of the workspace
+        float* dst = p.atomic ? p.part + (int64_t)blockIdx.y * p.M * p.N + m * p.N + n : p.y + m * p.ldy + n;
+        *dst = acc[i][j][q];
       }
     }
 }
 
-template <int TM, int TN, int NW>
-static int launch_mx(MxGemmArgs& p, bool deterministic, hipStream_t st) {
+// Split count: enough K splits that the grid fills the CUs, but never more
+// workgroups than can be resident at once (a second partial round of
+// workgroups would double the latency of this one-pass kernel).
+template <int TM, int TN, int NW, int SMAX>
+static int pick_splits(int64_t M, int64_t N, int total_steps) {
+  const int64_t tiles = cdiv(N, 16 * TN * NW) * cdiv(M, 16 * TM);
+  constexpr int lds = 16 * TM * (SMAX * 64 + 16) + 16 * TM * SMAX * 4;
+  const int per_cu = lds > 80 * 1024 ? 1 : 2;
+  const int64_t slots = (int64_t)per_cu * device_cu_count();
+  int splits = (int)cdiv(total_steps, SMAX);
+  while ((int64_t)(splits + 1) * tiles <= slots && splits < total_steps) ++splits;
+  const int steps = (int)cdiv(total_steps, splits);
+  return (int)cdiv(total_steps, steps);
+}
+
+template <int TM, int TN, int NW, int SMAX>
+static int launch_mx(MxGemmArgs& p, int splits, hipStream_t st) {
   const int64_t n_tiles = cdiv(p.N, 16 * TN * NW);
   const int64_t m_tiles = cdiv(p.M, 16 * TM);
-  const int64_t tiles = n_tiles * m_tiles;
-  int splits = 1;
-  if (!deterministic) {
-    const int64_t want = 2 * (int64_t)device_cu_count();
-    if (tiles < want) splits = (int)cdiv(want, tiles);
-    if (splits > p.total_steps) splits = p.total_steps;
-  }
   p.steps_per_split = (int)cdiv(p.total_steps, splits);
-  splits = (int)cdiv(p.total_steps, p.steps_per_split);
   p.atomic = splits > 1;
-  if (p.atomic) {
-    int s = launch_fill_zero(p.y, p.M * p.ldy, st);
-    if (s) return s;
-  }
-  hipLaunchKernelGGL((k_mx_gemm<TM, TN, NW>), dim3((unsigned)n_tiles, (unsigned)splits, (unsigned)m_tiles),
+  hipLaunchKernelGGL((k_mx_gemm<TM, TN, NW, SMAX>), dim3((unsigned)n_tiles, (unsigned)splits, (unsigned)m_tiles),
                      dim3(64 * NW), 0, st, p);
-  return check_launch("mx_gemm");
+  int s = check_launch("mx_gemm");
+  if (s || splits == 1) return s;
+  return launch_splitk_reduce(p.part, splits, p.M * p.N, p.y, st);
+}
+
+// Serial-K variant for GBW_DETERMINISTIC: the K loop runs inside one wave, so
+// every output is summed in one fixed order.
+template <int TM, int NW>
+__global__ __launch_bounds__(64 * NW) void k_mx_gemm_serial(const MxGemmArgs p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int64_t m0 = (int64_t)blockIdx.z * (16 * TM);
+  const int64_t n0 = ((int64_t)blockIdx.x * NW + wave) * 16;
+  if (n0 >= p.N) return;
+  const uint8_t* arow[TM];
+  const uint8_t* asrow[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    int64_t r = m0 + 16 * i + r16;
+    r = r < p.M ? r : p.M - 1;
+    arow[i] = p.a_codes + r * p.lda;
+    asrow[i] = p.a_scales + r * p.ldas;
+  }
+  int64_t n = n0 + r16;
+  n = n < p.N ? n : p.N - 1;
+  v4f acc[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < p.total_steps; ++s) {
+    const StepSeg sg = step_seg(p, s);
+    const int64_t kk = sg.k + 32 * g;
+    const bool valid = kk < sg.K;
+    const v4i bf = valid ? load16(sg.wc + n * sg.ldw + kk / 2) : v4i{0, 0, 0, 0};
+    const int bs = valid ? (int)sg.ws[n * sg.ldws + kk / 32] : 127;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t ka = sg.a_k0 + kk;
+      const v4i af = valid ? load16(arow[i] + ka / 2) : v4i{0, 0, 0, 0};
+      const int as = valid ? (int)asrow[i][ka / 32] : 127;
+      acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(widen(af), widen(bf), acc[i], 4, 4, 0, as, 0, bs);
+    }
+  }
+  const int64_t nn = n0 + r16;
+  if (nn >= p.N) return;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t m = m0 + 16 * i + 4 * g + q;
+      if (m < p.M) p.y[m * p.ldy + nn] = acc[i][q];
+    }
+}
+
+template <int TM>
+static int launch_serial(MxGemmArgs& p, hipStream_t st) {
+  if (TM == 2) return launch_serial<4>(p, st);
+  p.atomic = 0;
+  hipLaunchKernelGGL((k_mx_gemm_serial<TM, 4>), dim3((unsigned)cdiv(p.N, 64), 1, (unsigned)cdiv(p.M, 16 * TM)),
+                     dim3(256), 0, st, p);
+  return check_launch("mx_gemm(serial)");
 }
 
 static int check_act(const gbw_act* a, int64_t M, const char* who) {
@@ -180,8 +297,42 @@ static int check_w(const gbw_weight* w, int64_t K, const char* who) {
   return GBW_OK;
 }
 
+template <int TM>
+static int dispatch_tm(MxGemmArgs& p, size_t ws_bytes, hipStream_t st) {
+  int splits = pick_splits<TM, 1, 4, 8>(p.M, p.N, p.total_steps);
+  const size_t slab = (size_t)p.M * p.N * sizeof(float);
+  if (splits > 1 && (!p.part || ws_bytes < (size_t)splits * slab)) {
+    // not enough workspace for the partials: the serial-K kernel needs none
+    const int fit = p.part ? (int)(ws_bytes / slab) : 0;
+    const int need = (int)cdiv(p.total_steps, 8);
+    if (fit >= need && fit >= 2)
+      splits = fit;
+    else if (need == 1)
+      splits = 1;
+    else
+      return launch_serial<TM>(p, st);
+  }
+  return launch_mx<TM, 1, 4, 8>(p, splits, st);
+}
+
+size_t ws_mx_gemm(int64_t M, int64_t N, int64_t Ktot) {
+  if (M <= 0 || N <= 0 || Ktot <= 0) return 0;
+  const int steps = (int)cdiv(Ktot, 128) + 1;  // + 1: the tail segment may start a step of its own
+  int splits;
+  if (M <= 16)
+    splits = pick_splits<1, 1, 4, 8>(M, N, steps);
+  else if (M <= 32)
+    splits = pick_splits<2, 1, 4, 8>(M, N, steps);
+  else if (M <= 64)
+    splits = pick_splits<4, 1, 4, 8>(M, N, steps);
+  else
+    splits = pick_splits<8, 1, 4, 8>(M, N, steps);
+  return splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
+}
+
 static int run_mx(int64_t M, const gbw_act* a, const gbw_weight* w, const gbw_weight* r, int64_t tail, float* y,
-                  int32_t flags, void* stream) {
+                  int32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  (void)flags;  // every path sums in a fixed order: results are bitwise repeatable
   MxGemmArgs p{};
   p.M = M;
   p.N = w->N;
@@ -197,19 +348,20 @@ static int run_mx(int64_t M, const gbw_act* a, const gbw_weight* w, const gbw_we
   p.total_steps = p.seg[0].steps + p.seg[1].steps;
   p.y = y;
   p.ldy = w->N;
-  const bool det = (flags & GBW_DETERMINISTIC) != 0;
+  p.part = reinterpret_cast<float*>(ws);
   hipStream_t st = as_stream(stream);
-  if (M <= 16) return launch_mx<1, 1, 4>(p, det, st);
-  if (M <= 32) return launch_mx<2, 1, 4>(p, det, st);
-  if (M <= 64) return launch_mx<4, 1, 4>(p, det, st);
-  return launch_mx<8, 1, 4>(p, det, st);
+  if (M <= 16) return dispatch_tm<1>(p, ws_bytes, st);
+  if (M <= 32) return dispatch_tm<2>(p, ws_bytes, st);
+  if (M <= 64) return dispatch_tm<4>(p, ws_bytes, st);
+  return dispatch_tm<8>(p, ws_bytes, st);
 }
 
 }  // namespace gbw
 
 using namespace gbw;
 
-extern "C" int mx_gemm(int64_t M, const gbw_act* a, const gbw_weight* w, float* y, int32_t flags, void* stream) {
+extern "C" int mx_gemm(int64_t M, const gbw_act* a, const gbw_weight* w, float* y, int32_t flags, void* ws,
+                       size_t ws_bytes, void* stream) {
   if (M < 0) return fail(GBW_E_ARG, "mx_gemm: negative M");
   int st;
   if ((st = check_act(a, M, "mx_gemm"))) return st;
@@ -217,11 +369,11 @@ extern "C" int mx_gemm(int64_t M, const gbw_act* a, const gbw_weight* w, float* 
   if (M == 0 || w->N == 0) return GBW_OK;
   if (!y) return fail(GBW_E_ARG, "mx_gemm: null output");
   if ((st = check_device())) return st;
-  return run_mx(M, a, w, nullptr, 0, y, flags, stream);
+  return run_mx(M, a, w, nullptr, 0, y, flags, ws, ws_bytes, stream);
 }
 
 extern "C" int residual_tail_gemm(int64_t M, const gbw_act* a, const gbw_weight* w, const gbw_weight* r,
-                                  int64_t tail, float* y, int32_t flags, void* stream) {
+                                  int64_t tail, float* y, int32_t flags, void* ws, size_t ws_bytes, void* stream) {
   if (M < 0 || tail < 0) return fail(GBW_E_ARG, "residual_tail_gemm: negative extent");
   int st;
   if ((st = check_act(a, M, "residual_tail_gemm"))) return st;
@@ -235,5 +387,5 @@ extern "C" int residual_tail_gemm(int64_t M, const gbw_act* a, const gbw_weight*
   if (M == 0 || w->N == 0) return GBW_OK;
   if (!y) return fail(GBW_E_ARG, "residual_tail_gemm: null output");
   if ((st = check_device())) return st;
-  return run_mx(M, a, w, tail > 0 ? r : nullptr, tail, y, flags, stream);
+  return run_mx(M, a, w, tail > 0 ? r : nullptr, tail, y, flags, ws, ws_bytes, stream);
 }

@@ -5,15 +5,10 @@
 namespace gbw {
 size_t ws_moe_route(int64_t, int64_t) { return 0; }
 size_t ws_moe_gemm(int64_t, int64_t, int32_t) { return 0; }
-size_t ws_lut_gemm(int64_t, int64_t, int64_t) { return 0; }
 }  // namespace gbw
 
 using namespace gbw;
 
-extern "C" int lut_gemm(int64_t, int64_t, int64_t, int32_t, const uint16_t*, const uint8_t*, const uint16_t*,
-                        float*, int32_t, void*, size_t, void*) {
-  return fail(GBW_E_UNSUPPORTED, "lut_gemm: not built");
-}
 extern "C" int moe_route(const float*, int64_t, int32_t, int32_t, int32_t*, float*, int32_t*, int32_t*, int32_t*,
                          void*, size_t, void*) {
   return fail(GBW_E_UNSUPPORTED, "moe_route: not built");

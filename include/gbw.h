@@ -67,7 +67,7 @@ extern "C" {
 
 /* gbw_workspace_size ops */
 #define GBW_OP_QUANTIZE 0   /* d0 = rows, d1 = K                       */
-#define GBW_OP_MX_GEMM 1    /* d0 = M, d1 = N, d2 = K (+ tail)         */
+#define GBW_OP_MX_GEMM 1    /* d0 = M, d1 = N, d2 = K + tail           */
 #define GBW_OP_LUT_GEMM 2   /* d0 = M, d1 = N, d2 = K                  */
 #define GBW_OP_MOE_ROUTE 3  /* d0 = T, d1 = E                          */
 #define GBW_OP_MOE_GEMM 4   /* d0 = pairs, d1 = N (output width)       */
@@ -138,12 +138,15 @@ int mx_residual(const float* w, int64_t N, int64_t K, int64_t tail, const uint8_
 
 /* ---- dense GEMMs ---------------------------------------------------------
  * mx_gemm: y[M][N] fp32 = deq(a) deq(w)^T, a [M][K] and w [N][K] both
- * E8M0-B32 (scaled MFMA, FP4 x FP4).  K must be a multiple of 32.
- * Without GBW_DETERMINISTIC the reduction over K may be split across
- * workgroups and combined with fp32 atomics (y is overwritten either way).
+ * E8M0-B32 (scaled MFMA, FP4 x FP4).  K must be a multiple of 32.  y is
+ * overwritten.  When the grid needs the reduction over K split across
+ * workgroups, the split partials go to the workspace
+ * (gbw_workspace_size(GBW_OP_MX_GEMM, M, N, K [+ tail], 0) bytes) and are
+ * summed in split order by a second kernel; with a smaller or NULL workspace
+ * a slower serial-K kernel is used.  Results are bitwise repeatable.
  */
 int mx_gemm(int64_t M, const gbw_act* a, const gbw_weight* w, float* y, int32_t flags,
-            void* stream);
+            void* ws, size_t ws_bytes, void* stream);
 
 /* residual_tail_gemm: the augmented MXFP4 GEMM of PRQuant §4 ("Offline
  * residual augmentation", W_aug^q = Q([W, R_W]), and "Kernel design"):
@@ -151,7 +154,8 @@ int mx_gemm(int64_t M, const gbw_act* a, const gbw_weight* w, float* y, int32_t 
  * a [M][K] E8M0-B32 (the tail is re-read in place, no copy), w [N][K],
  * r [N][tail] the quantized residual.  tail % 32 == 0, tail <= K. */
 int residual_tail_gemm(int64_t M, const gbw_act* a, const gbw_weight* w, const gbw_weight* r,
-                       int64_t tail, float* y, int32_t flags, void* stream);
+                       int64_t tail, float* y, int32_t flags, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /* lut_gemm: codebook weights (CodeQuant: Unified Clustering and Quantization
  * for Enhanced Outlier Smoothing in Low-Precision Mixture-of-Experts,

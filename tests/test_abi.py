@@ -51,7 +51,8 @@ def test_status_strings(gbw):
 def test_workspace_sizes(gbw):
     assert gbw.workspace_size(gbw.OP_QUANTIZE, 100, 64, 0, gbw.FMT_E8M0_B32) == 0
     assert gbw.workspace_size(gbw.OP_QUANTIZE, 100, 64, 0, gbw.FMT_E4M3_B16) > 0
-    assert gbw.workspace_size(gbw.OP_MX_GEMM, 128, 2560, 9728) == 0
+    assert gbw.workspace_size(gbw.OP_MX_GEMM, 128, 2560, 9728 + 256) > 0
+    assert gbw.workspace_size(gbw.OP_MX_GEMM, 0, 2560, 9728) == 0
 
 
 def test_validation_before_any_device_work(gbw):
@@ -82,16 +83,16 @@ def test_gemm_validation(gbw):
     L = gbw._lib
     a = gbw._Act(0, 16, 48, 0x1000, 0x2000, None)        # K = 48: not a multiple of 32
     w = gbw._Weight(0, 1, 8, 48, 0x3000, 0x4000, None, None, 1)
-    assert L.mx_gemm(16, ctypes.byref(a), ctypes.byref(w), ctypes.c_void_p(0x5000), 0, None) == 2
+    assert L.mx_gemm(16, ctypes.byref(a), ctypes.byref(w), ctypes.c_void_p(0x5000), 0, None, 0, None) == 2
     a = gbw._Act(1, 16, 64, 0x1000, 0x2000, None)        # E4M3 activation on the MXFP4 GEMM
-    assert L.mx_gemm(16, ctypes.byref(a), ctypes.byref(w), ctypes.c_void_p(0x5000), 0, None) == 4
+    assert L.mx_gemm(16, ctypes.byref(a), ctypes.byref(w), ctypes.c_void_p(0x5000), 0, None, 0, None) == 4
     a = gbw._Act(0, 16, 64, 0x1000, 0x2000, None)
     w = gbw._Weight(0, 1, 8, 96, 0x3000, 0x4000, None, None, 1)   # K mismatch
-    assert L.mx_gemm(16, ctypes.byref(a), ctypes.byref(w), ctypes.c_void_p(0x5000), 0, None) == 2
+    assert L.mx_gemm(16, ctypes.byref(a), ctypes.byref(w), ctypes.c_void_p(0x5000), 0, None, 0, None) == 2
     w = gbw._Weight(0, 1, 8, 64, 0x3000, 0x4000, None, None, 1)
-    assert L.mx_gemm(32, ctypes.byref(a), ctypes.byref(w), ctypes.c_void_p(0x5000), 0, None) == 2  # M > rows
-    assert L.mx_gemm(0, ctypes.byref(a), ctypes.byref(w), None, 0, None) == 0                   # empty
+    assert L.mx_gemm(32, ctypes.byref(a), ctypes.byref(w), ctypes.c_void_p(0x5000), 0, None, 0, None) == 2  # M > rows
+    assert L.mx_gemm(0, ctypes.byref(a), ctypes.byref(w), None, 0, None, 0, None) == 0                   # empty
     # residual tail not a multiple of 32
     r = gbw._Weight(0, 1, 8, 48, 0x3000, 0x4000, None, None, 1)
     assert L.residual_tail_gemm(16, ctypes.byref(a), ctypes.byref(w), ctypes.byref(r), 48,
-                                ctypes.c_void_p(0x5000), 0, None) == 2
+                                ctypes.c_void_p(0x5000), 0, None, 0, None) == 2
