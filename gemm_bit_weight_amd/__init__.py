@@ -306,12 +306,18 @@ def moe_route(logits, topk, out=None, ws=None, stream=None):
 
 def moe_grouped_gemm(stage, route, a: Act, w: Weight, h_bf16=None, h_codes=None, h_scales=None, y=None, flags=0,
                      ws=None, stream=None):
+    """One stage of the routed expert FFN (see include/gbw.h).
+
+    GATEUP: fills h_bf16 [P][I] and/or h_codes [P][I/2] + h_scales [P][I/32].
+    DOWN:   overwrites y [T][H].  flags=DETERMINISTIC uses a pair buffer in the
+            workspace and a fixed-order combine instead of fp32 atomics.
+    """
     T, topk = route["topk_ids"].shape
     P = T * topk
-    N_out = w.N // 2 if stage == MOE_GATEUP_SWIGLU else w.N
-    need = workspace_size(OP_MOE_GEMM, P, N_out, 0, w.fmt)
-    if ws is None and need:
-        ws = torch.empty(need, dtype=torch.uint8, device=a.codes.device)
+    need = 0
+    if stage == MOE_DOWN_COMBINE and (flags & DETERMINISTIC):
+        need = workspace_size(OP_MOE_GEMM, P, w.N, 0, w.fmt)
+    ws, wsb = _ws(ws, need, a.codes.device)
     o = _MoeOut(h_bf16.data_ptr() if h_bf16 is not None else None,
                 h_codes.data_ptr() if h_codes is not None else None,
                 h_scales.data_ptr() if h_scales is not None else None,
@@ -319,5 +325,28 @@ def moe_grouped_gemm(stage, route, a: Act, w: Weight, h_bf16=None, h_codes=None,
     ca, cw = a.c(), w.c()
     _check(_lib.moe_grouped_gemm(stage, T, topk, _ptr(route["expert_offsets"]), _ptr(route["pair_token"]),
                                  _ptr(route["pair_pos"]), _ptr(route["topk_w"]), _c.byref(ca), _c.byref(cw),
-                                 _c.byref(o), flags, _ptr(ws), ws.numel() if ws is not None else 0,
-                                 _stream(stream)))
+                                 _c.byref(o), flags, _ptr(ws), wsb, _stream(stream)))
+
+
+def moe_ffn_mx(x, route, w_gate_up: Weight, w_down: Weight, out=None, h_bf16=None, flags=0, bufs=None,
+               stream=None):
+    """The whole routed FFN on MXFP4 activations: quantize x, gate/up with the
+    fused SwiGLU + requantization, down with the weighted combine."""
+    T, H = x.shape
+    topk = route["topk_ids"].shape[1]
+    P = T * topk
+    I = w_gate_up.N // 2
+    dev = x.device
+    if bufs is None:
+        bufs = dict(xq=Act(FMT_E8M0_B32, torch.empty((T, H // 2), dtype=torch.uint8, device=dev),
+                           torch.empty((T, H // 32), dtype=torch.uint8, device=dev)),
+                    hc=torch.empty((P, I // 2), dtype=torch.uint8, device=dev),
+                    hs=torch.empty((P, I // 32), dtype=torch.uint8, device=dev))
+    xq = mx_quantize(x, FMT_E8M0_B32, out=bufs["xq"], stream=stream)
+    moe_grouped_gemm(MOE_GATEUP_SWIGLU, route, xq, w_gate_up, h_bf16=h_bf16, h_codes=bufs["hc"],
+                     h_scales=bufs["hs"], stream=stream)
+    if out is None:
+        out = torch.empty((T, w_down.N), dtype=torch.float32, device=dev)
+    moe_grouped_gemm(MOE_DOWN_COMBINE, route, Act(FMT_E8M0_B32, bufs["hc"], bufs["hs"]), w_down, y=out,
+                     flags=flags, stream=stream)
+    return out

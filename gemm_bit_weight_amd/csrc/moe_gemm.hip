@@ -1,0 +1,521 @@
+// Grouped expert GEMMs of the routed FFN on CDNA4 scaled MFMA (FP4 x FP4).
+//
+//  GATEUP: for every pair p = (token t, expert e), g and u = deq(Xq[t]) W_e^T
+//          over the fused [2I][H] gate/up weight (gate rows first), then
+//          h = bf16(silu(g) * u) and its MXFP4 (E8M0-B32) requantization --
+//          all in the epilogue, so h never exists in a wider format in HBM.
+//  DOWN:   y[t] += topk_w[t][j] * deq(Hq[p]) W_e^T for the pair p of (t, j).
+//
+// FFN form: "PRQuant: Permutation Residual Quantization for Low-Overhead
+// Inference", §4 Eq. (1) (the gated MLP, applied to each routed expert;
+// CodeQuant Fig. 1-2 show the experts of an MoE FFN).  Weight formats:
+//  * MXFP4 (E8M0-B32): codes and scales stream straight into LDS;
+//  * VQ -> MX ("MXCode: MX-Native Codebook Quantization", abstract, PreScale;
+//    Fig. 2/3 and Table 4: d = 4, 256 entries, 64x64 QBlocks): each 8-bit
+//    index is expanded through its QBlock's 256-entry table of four E2M1 codes
+//    (the table lives in LDS, 512 bytes) into an MXFP4 operand tile in LDS;
+//    the E8M0 prescales are the operand's block scales.  No wider copy of the
+//    weights exists anywhere, in HBM or on chip.
+//
+// Work decomposition: one workgroup (4 waves, 2 x 2) per 256 x 256 output
+// tile of one expert: 256 pairs (rows) x 256 weight rows.  The tile list is
+// expert-major (m tiles, then n tiles) and is recovered by every workgroup
+// from expert_offsets with a block scan; consecutive logical tiles are placed
+// on the same XCD so the experts an XCD works on stay in its L2.  K advances
+// 128 elements per stage (one scaled MFMA step), double-buffered in LDS; the
+// next stage's global loads are in flight while the current stage's 64 MFMAs
+// per wave run.  LDS rows are 80 bytes (64 of data + 16 of padding) so the 16
+// lanes reading one MFMA fragment hit distinct banks.
+//
+// For GATEUP the 256 weight rows of a tile are 128 gate rows and the 128 up
+// rows of the same intermediate columns, arranged so that each wave holds g
+// and u of the same (row, column) in its own accumulators: SwiGLU and the
+// requantization need no data exchange beyond a 16-lane max for each block
+// amax.
+#include "common.hpp"
+
+namespace gbw {
+
+constexpr int kMoeBM = 256, kMoeBN = 256, kMoeThreads = 256;
+constexpr int kRowB = 80;  // LDS bytes per operand row per stage
+constexpr int kMaxMoeExperts = 256;
+
+enum WFmt { W_MX = 0, W_VQ = 1 };
+
+struct MoeArgs {
+  int32_t stage;
+  int32_t topk, E;
+  int64_t T, P;
+  const int32_t* off;
+  const int32_t* pair_token;
+  const int32_t* pair_pos;
+  const float* topk_w;
+  const uint8_t* a_codes;  // [rows][K/2]
+  const uint8_t* a_scales; // [rows][K/32]
+  int64_t K;               // reduction length (H for GATEUP, I for DOWN)
+  const uint8_t* w_codes;  // MX: [E][N][K/2]; VQ: idx [E][N][K/4]
+  const uint8_t* w_scales; // [E][N][K/32]
+  const uint16_t* w_cb;    // VQ: [E][N/64][K/64][256]
+  int64_t N;               // weight rows per expert (2I or H)
+  int32_t n_tiles;         // output tiles along N
+  int32_t total_tiles;
+  uint16_t* h_bf16;        // GATEUP: [P][I] or null
+  uint8_t* h_codes;        // GATEUP: [P][I/2] or null
+  uint8_t* h_scales;       // GATEUP: [P][I/32] or null
+  float* y;                // DOWN: [T][H]
+  float* pairbuf;          // DOWN deterministic: [P][H] or null
+};
+
+struct TileInfo {
+  int e, mt, nt;
+  int row0, rows;  // first pair of the tile, valid rows
+};
+
+// Logical tile of this workgroup: XCD-aware remap, then (expert, m tile, n tile).
+__device__ bool find_tile(const MoeArgs& p, TileInfo& ti, int* scan) {
+  const int G = gridDim.x;
+  const int per = (G + 7) / 8;
+  const int L = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  const int tid = threadIdx.x;
+  int cnt = 0;
+  if (tid < p.E) cnt = (p.off[tid + 1] - p.off[tid] + kMoeBM - 1) / kMoeBM;
+  scan[tid] = cnt;
+  __syncthreads();
+  for (int o = 1; o < kMoeThreads; o <<= 1) {
+    const int add = tid >= o ? scan[tid - o] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  // scan[e] = m tiles of experts 0..e (inclusive)
+  const int mt_total = scan[kMoeThreads - 1];
+  const int lm = L / p.n_tiles;  // logical m tile
+  if (lm >= mt_total) return false;
+  __shared__ int s_e;
+  if (tid < p.E) {
+    const int lo = tid ? scan[tid - 1] : 0;
+    if (lm >= lo && lm < scan[tid]) s_e = tid;
+  }
+  __syncthreads();
+  ti.e = s_e;
+  ti.mt = lm - (ti.e ? scan[ti.e - 1] : 0);
+  ti.nt = L % p.n_tiles;
+  ti.row0 = p.off[ti.e] + ti.mt * kMoeBM;
+  ti.rows = min(kMoeBM, p.off[ti.e + 1] - ti.row0);
+  return true;
+}
+
+__device__ __forceinline__ v8i widen8(v4i x) {
+  v8i r;
+  r[0] = x[0];
+  r[1] = x[1];
+  r[2] = x[2];
+  r[3] = x[3];
+  r[4] = 0;
+  r[5] = 0;
+  r[6] = 0;
+  r[7] = 0;
+  return r;
+}
+
+// B-tile row j (0..255) -> weight row within the expert.
+__device__ __forceinline__ int64_t b_row(const MoeArgs& p, int nt, int j) {
+  if (p.stage == GBW_MOE_GATEUP_SWIGLU) {
+    const int64_t I = p.N / 2;
+    const int64_t i0 = (int64_t)nt * (kMoeBN / 2);
+    return j < kMoeBN / 2 ? i0 + j : I + i0 + (j - kMoeBN / 2);
+  }
+  return (int64_t)nt * kMoeBN + j;
+}
+
+template <int WF>
+__global__ __launch_bounds__(kMoeThreads) void k_moe_fp4(const MoeArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t sA[2][kMoeBM * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[2][kMoeBN * kRowB];
+  __shared__ uint32_t sAs[2][kMoeBM];
+  __shared__ uint32_t sBs[2][kMoeBN];
+  __shared__ __attribute__((aligned(16))) uint16_t sLut[WF == W_VQ ? 8 * 256 : 8];
+  __shared__ int scan[kMoeThreads];
+  __shared__ int s_tok[kMoeBM];
+  __shared__ float s_w[kMoeBM];
+
+  TileInfo ti;
+  if (!find_tile(p, ti, scan)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int64_t K = p.K;
+  const int steps = (int)(K / 128);
+
+  // per-row metadata: token (gather / combine) and routing weight
+  for (int r = tid; r < kMoeBM; r += kMoeThreads) {
+    int tok = 0;
+    float wt = 0.f;
+    if (r < ti.rows) {
+      const int pr = ti.row0 + r;
+      tok = p.pair_token[pr];
+      if (p.stage == GBW_MOE_DOWN_COMBINE)
+        for (int j = 0; j < p.topk; ++j)
+          if (p.pair_pos[(int64_t)tok * p.topk + j] == pr) wt = p.topk_w[(int64_t)tok * p.topk + j];
+    }
+    s_tok[r] = tok;
+    s_w[r] = wt;
+  }
+  __syncthreads();
+
+  // --- fixed per-thread load assignments --------------------------------
+  // A: rows ar + 64u (u = 0..3), 16-byte chunk ac of the 64-byte stage row
+  const int ar = tid >> 2, ac = tid & 3;
+  const uint8_t* arow[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = ar + 64 * u;
+    const int rr = r < ti.rows ? r : (ti.rows > 0 ? ti.rows - 1 : 0);
+    const int64_t src = p.stage == GBW_MOE_GATEUP_SWIGLU ? (int64_t)s_tok[rr] : (int64_t)(ti.row0 + rr);
+    arow[u] = p.a_codes + src * (K / 2);
+  }
+  const int64_t a_srow = p.stage == GBW_MOE_GATEUP_SWIGLU ? (int64_t)s_tok[tid < ti.rows ? tid : 0]
+                                                          : (int64_t)(ti.row0 + (tid < ti.rows ? tid : 0));
+  const uint8_t* a_scl = p.a_scales + a_srow * (K / 32);
+  // weights of expert e
+  const int64_t wN = p.N;
+  const uint8_t* wsc = p.w_scales + (int64_t)ti.e * wN * (K / 32) + b_row(p, ti.nt, tid) * (K / 32);
+  const uint8_t* wrow[4];
+  const uint8_t* vrow[2];
+  const uint16_t* cbase = nullptr;
+  int lut_bn = 0, lut_kb = 0;
+  if (WF == W_MX) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      wrow[u] = p.w_codes + (int64_t)ti.e * wN * (K / 2) + b_row(p, ti.nt, ar + 64 * u) * (K / 2);
+  } else {
+    // idx: rows (tid >> 1) + 128 v (v = 0, 1), 16-byte chunk (tid & 1) of the 32-byte stage row
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+      vrow[v] = p.w_codes + (int64_t)ti.e * wN * (K / 4) + b_row(p, ti.nt, (tid >> 1) + 128 * v) * (K / 4);
+    // LUT: thread tid loads 16 bytes of table (tid >> 5) (8 tables: 4 QBlock rows x 2 QBlock columns)
+    const int tb = tid >> 5;
+    lut_bn = tb >> 1;  // QBlock row within the tile (64 B rows each)
+    lut_kb = tb & 1;   // QBlock column within the stage
+    const int64_t qrow = b_row(p, ti.nt, lut_bn * 64) / 64;
+    cbase = p.w_cb + ((int64_t)ti.e * (wN / 64) + qrow) * (K / 64) * 256;
+  }
+
+  // prefetch registers
+  v4i pa[4], pb[4];
+  uint32_t pas, pbs;
+  v4i pl;
+  auto gload = [&](int s) {
+    const int64_t kb = (int64_t)s * 64;  // byte offset of the stage in a row of codes
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pa[u] = load16(arow[u] + kb + 16 * ac);
+    pas = *reinterpret_cast<const uint32_t*>(a_scl + (int64_t)s * 4);
+    pbs = *reinterpret_cast<const uint32_t*>(wsc + (int64_t)s * 4);
+    if (WF == W_MX) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) pb[u] = load16(wrow[u] + kb + 16 * ac);
+    } else {
+#pragma unroll
+      for (int v = 0; v < 2; ++v) pb[v] = load16(vrow[v] + (int64_t)s * 32 + 16 * (tid & 1));
+      const int64_t kq = (int64_t)s * 2 + lut_kb;  // QBlock column
+      pl = load16(cbase + kq * 256 + (tid & 31) * 8);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<v4i*>(&sA[buf][(ar + 64 * u) * kRowB + 16 * ac]) = pa[u];
+    sAs[buf][tid] = pas;
+    sBs[buf][tid] = pbs;
+    if (WF == W_MX) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) *reinterpret_cast<v4i*>(&sB[buf][(ar + 64 * u) * kRowB + 16 * ac]) = pb[u];
+    } else {
+      *reinterpret_cast<v4i*>(&sLut[(tid >> 5) * 256 + (tid & 31) * 8]) = pl;
+    }
+  };
+  // VQ: expand the 32 indices this thread holds into 64 bytes of E2M1 codes
+  auto vq_expand = [&](int buf) {
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int row = (tid >> 1) + 128 * v;
+      const int half = tid & 1;                      // which 64-element half of the stage (QBlock column)
+      const uint16_t* lut = &sLut[(((row >> 6) << 1) + half) * 256];
+      uint32_t outw[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t w = (uint32_t)pb[v][d];
+        const uint32_t k0 = lut[w & 0xFF], k1 = lut[(w >> 8) & 0xFF];
+        const uint32_t k2 = lut[(w >> 16) & 0xFF], k3 = lut[w >> 24];
+        outw[2 * d] = k0 | (k1 << 16);
+        outw[2 * d + 1] = k2 | (k3 << 16);
+      }
+      uint8_t* dst = &sB[buf][row * kRowB + 32 * half];
+      *reinterpret_cast<v4i*>(dst) = v4i{(int)outw[0], (int)outw[1], (int)outw[2], (int)outw[3]};
+      *reinterpret_cast<v4i*>(dst + 16) = v4i{(int)outw[4], (int)outw[5], (int)outw[6], (int)outw[7]};
+    }
+  };
+
+  v4f acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // B-tile rows of this wave's 8 column subtiles
+  int brow[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    brow[j] = p.stage == GBW_MOE_GATEUP_SWIGLU ? (j < 4 ? 64 * wn + 16 * j : 128 + 64 * wn + 16 * (j - 4))
+                                               : 128 * wn + 16 * j;
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  if (WF == W_VQ) {
+    vq_expand(0);
+    __syncthreads();
+  }
+
+  for (int s = 0; s < steps; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < steps) gload(s + 1);
+    // 64 MFMAs of this stage
+    v4i bf[8];
+    int bsc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = brow[j] + r16;
+      bf[j] = *reinterpret_cast<const v4i*>(&sB[buf][row * kRowB + 16 * g4]);
+      bsc[j] = (int)((sBs[buf][row] >> (8 * g4)) & 0xFFu);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 128 * wm + 16 * i + r16;
+      const v4i af = *reinterpret_cast<const v4i*>(&sA[buf][row * kRowB + 16 * g4]);
+      const int asc = (int)((sAs[buf][row] >> (8 * g4)) & 0xFFu);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(widen8(af), widen8(bf[j]), acc[i][j], 4, 4, 0,
+                                                                      asc, 0, bsc[j]);
+    }
+    if (s + 1 < steps) {
+      lstore(buf ^ 1);
+      __syncthreads();
+      if (WF == W_VQ) {
+        vq_expand(buf ^ 1);
+        __syncthreads();
+      }
+    }
+  }
+
+  // ---------------------------------------------------------------------
+  // epilogues
+  // ---------------------------------------------------------------------
+  if (p.stage == GBW_MOE_DOWN_COMBINE) {
+    const int64_t H = p.N;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 128 * wm + 16 * i + 4 * g4 + r;
+        if (m >= ti.rows) continue;
+        const float wt = s_w[m];
+        float* dst = p.pairbuf ? p.pairbuf + (int64_t)(ti.row0 + m) * H : p.y + (int64_t)s_tok[m] * H;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int64_t n = (int64_t)ti.nt * kMoeBN + 128 * wn + 16 * j + r16;
+          const float v = wt * acc[i][j][r];
+          if (p.pairbuf)
+            dst[n] = v;
+          else
+            unsafeAtomicAdd(dst + n, v);
+        }
+      }
+    return;
+  }
+
+  // GATEUP: h = bf16(silu(g) * u), then E8M0-B32 requantization of h.
+  // Wave columns: intermediate index i = nt*128 + 64*wn + 16*jj + r16, jj = 0..3
+  // (g in acc[.][jj], u in acc[.][jj+4]); E8M0 block b covers jj = 2b, 2b+1.
+  __syncthreads();  // LDS operand buffers are reused for the code tile
+  uint8_t* sH = &sA[0][0];           // [256 rows][64 bytes of codes]
+  uint8_t* sHs = &sB[0][0];          // [256 rows][4 scales]
+  const int64_t I = p.N / 2;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 128 * wm + 16 * i + 4 * g4 + r;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        float hv[2];
+        uint32_t hb[2];
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const int jj = 2 * b + t2;
+          const float gv = acc[i][jj][r], uv = acc[i][jj + 4][r];
+          const float sg = gv / (1.0f + expf(-gv));
+          hb[t2] = f32_to_bf16_rne(sg * uv);
+          hv[t2] = bf16_to_f32(hb[t2]);
+        }
+        if (p.h_bf16 && m < ti.rows) {
+          const int64_t col = (int64_t)ti.nt * 128 + 64 * wn + 32 * b + r16;
+          p.h_bf16[(int64_t)(ti.row0 + m) * I + col] = (uint16_t)hb[0];
+          p.h_bf16[(int64_t)(ti.row0 + m) * I + col + 16] = (uint16_t)hb[1];
+        }
+        // block amax over the 32 columns held by the 16 lanes of this row
+        uint32_t am = max(__float_as_uint(hv[0]) & 0x7FFFFFFFu, __float_as_uint(hv[1]) & 0x7FFFFFFFu);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) am = max(am, (uint32_t)__shfl_xor((int)am, o));
+        const uint32_t sc = e8m0_scale_code(__uint_as_float(am));
+        const float inv = e8m0_inv(sc);
+        const uint32_t c0 = e2m1_rne(fabsf(hv[0]) * inv) | ((__float_as_uint(hv[0]) >> 28) & 8u);
+        const uint32_t c1 = e2m1_rne(fabsf(hv[1]) * inv) | ((__float_as_uint(hv[1]) >> 28) & 8u);
+        // columns 2k, 2k+1 sit in lanes 2k, 2k+1: pair them into bytes
+        const uint32_t o0 = (uint32_t)__shfl_xor((int)c0, 1), o1 = (uint32_t)__shfl_xor((int)c1, 1);
+        const int cb = 64 * wn + 32 * b;  // first column of the block within the tile's 128
+        if ((r16 & 1) == 0) {
+          sH[m * 64 + (cb + r16) / 2] = (uint8_t)(c0 | (o0 << 4));
+          sH[m * 64 + (cb + 16 + r16) / 2] = (uint8_t)(c1 | (o1 << 4));
+        }
+        if (r16 == 0) sHs[m * 4 + cb / 32] = (uint8_t)sc;
+      }
+    }
+  __syncthreads();
+  if (p.h_codes) {
+    // 256 rows x 64 bytes: 4 chunks of 16 bytes per row
+    for (int c = tid; c < kMoeBM * 4; c += kMoeThreads) {
+      const int m = c >> 2, q = c & 3;
+      if (m < ti.rows)
+        *reinterpret_cast<v4i*>(p.h_codes + (int64_t)(ti.row0 + m) * (I / 2) + (int64_t)ti.nt * 64 + 16 * q) =
+            *reinterpret_cast<const v4i*>(&sH[m * 64 + 16 * q]);
+    }
+    for (int m = tid; m < kMoeBM; m += kMoeThreads)
+      if (m < ti.rows)
+        *reinterpret_cast<uint32_t*>(p.h_scales + (int64_t)(ti.row0 + m) * (I / 32) + (int64_t)ti.nt * 4) =
+            *reinterpret_cast<const uint32_t*>(&sHs[m * 4]);
+  }
+}
+
+// y[t][:] = sum_j pairbuf[pair_pos[t][j]][:] in slot order (deterministic combine)
+__global__ void k_moe_combine(const float* __restrict__ pairbuf, const int32_t* __restrict__ pair_pos, int topk,
+                              int64_t T, int64_t H, float* __restrict__ y) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= T * H) return;
+  const int64_t t = i / H, n = i % H;
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < topk; ++j) acc += *reinterpret_cast<const v4f*>(pairbuf + (int64_t)pair_pos[t * topk + j] * H + n);
+  *reinterpret_cast<v4f*>(y + i) = acc;
+}
+
+}  // namespace gbw
+
+namespace gbw {
+
+size_t ws_moe_gemm(int64_t P, int64_t N, int32_t fmt) {
+  (void)fmt;
+  // only the deterministic down/combine path uses it: a [P][N] fp32 pair buffer
+  return P > 0 && N > 0 ? (size_t)P * N * sizeof(float) : 0;
+}
+
+int launch_moe_bf16(const MoeArgs& p, const gbw_act* a, const gbw_weight* w, int grid, hipStream_t st);
+
+}  // namespace gbw
+
+using namespace gbw;
+
+extern "C" int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const int32_t* expert_offsets,
+                                const int32_t* pair_token, const int32_t* pair_pos, const float* topk_w,
+                                const gbw_act* a, const gbw_weight* w, const gbw_moe_out* out, int32_t flags,
+                                void* ws, size_t ws_bytes, void* stream) {
+  if (stage != GBW_MOE_GATEUP_SWIGLU && stage != GBW_MOE_DOWN_COMBINE)
+    return fail(GBW_E_ARG, "moe_grouped_gemm: bad stage");
+  if (T < 0 || topk < 1 || topk > 16) return fail(GBW_E_ARG, "moe_grouped_gemm: bad T/topk");
+  if (!a || !w || !out) return fail(GBW_E_ARG, "moe_grouped_gemm: null descriptor");
+  const int E = w->n_experts;
+  if (E < 1 || E > kMaxMoeExperts) return fail(GBW_E_ARG, "moe_grouped_gemm: need 1 <= experts <= %d", kMaxMoeExperts);
+  const int64_t K = w->K, N = w->N, P = T * topk;
+  if (a->K != K) return fail(GBW_E_SHAPE, "moe_grouped_gemm: activation K %lld != weight K %lld", (long long)a->K,
+                             (long long)K);
+  if (K <= 0 || K % 128) return fail(GBW_E_SHAPE, "moe_grouped_gemm: K must be a positive multiple of 128");
+  const bool fp4 = (w->fmt == GBW_FMT_E8M0_B32 || w->fmt == GBW_FMT_VQ4_E8M0) && a->fmt == GBW_FMT_E8M0_B32;
+  const bool e4m3 = w->fmt == GBW_FMT_E4M3_B16 && a->fmt == GBW_FMT_E4M3_B16;
+  if (!fp4 && !e4m3) return fail(GBW_E_UNSUPPORTED, "moe_grouped_gemm: unsupported activation/weight formats");
+  if (stage == GBW_MOE_GATEUP_SWIGLU) {
+    if (N % 256) return fail(GBW_E_SHAPE, "moe_grouped_gemm: gate/up rows (2I) must be a multiple of 256");
+    if (a->rows < T) return fail(GBW_E_SHAPE, "moe_grouped_gemm: activation has fewer rows than tokens");
+    if (fp4 && (!out->h_codes || !out->h_scales) && !out->h_bf16)
+      return fail(GBW_E_ARG, "moe_grouped_gemm: gate/up needs h_codes+h_scales or h_bf16");
+    if (fp4 && (!out->h_codes) != (!out->h_scales))
+      return fail(GBW_E_ARG, "moe_grouped_gemm: h_codes and h_scales go together");
+    if (e4m3 && !out->h_bf16) return fail(GBW_E_ARG, "moe_grouped_gemm: E4M3 gate/up writes h_bf16");
+  } else {
+    if (N % 256) return fail(GBW_E_SHAPE, "moe_grouped_gemm: down rows (H) must be a multiple of 256");
+    if (a->rows < P) return fail(GBW_E_SHAPE, "moe_grouped_gemm: activation has fewer rows than pairs");
+    if (!out->y) return fail(GBW_E_ARG, "moe_grouped_gemm: down needs y");
+  }
+  if (w->fmt == GBW_FMT_VQ4_E8M0 && !w->codebook) return fail(GBW_E_ARG, "moe_grouped_gemm: VQ needs a codebook");
+  if (e4m3 && (!w->tensor_scale || !a->tensor_scale || w->ts_per_expert < 1))
+    return fail(GBW_E_ARG, "moe_grouped_gemm: E4M3 needs tensor scales");
+  if (T == 0) return GBW_OK;
+  if (!expert_offsets || !pair_token || !pair_pos || !topk_w || !a->codes || !a->scales || !w->codes || !w->scales)
+    return fail(GBW_E_ARG, "moe_grouped_gemm: null pointer");
+  if (!aligned16(a->codes) || !aligned16(w->codes) || (w->codebook && !aligned16(w->codebook)) ||
+      (reinterpret_cast<uintptr_t>(a->scales) & 3u) || (reinterpret_cast<uintptr_t>(w->scales) & 3u))
+    return fail(GBW_E_ALIGN, "moe_grouped_gemm: codes/codebook must be 16-byte and scales 4-byte aligned");
+  const bool det = (flags & GBW_DETERMINISTIC) != 0;
+  if (stage == GBW_MOE_DOWN_COMBINE && det && (!ws || ws_bytes < ws_moe_gemm(P, N, w->fmt)))
+    return fail(GBW_E_WORKSPACE, "moe_grouped_gemm: deterministic combine needs %zu bytes of workspace",
+                ws_moe_gemm(P, N, w->fmt));
+  int st = check_device();
+  if (st) return st;
+  hipStream_t s = as_stream(stream);
+
+  MoeArgs p{};
+  p.stage = stage;
+  p.topk = topk;
+  p.E = E;
+  p.T = T;
+  p.P = P;
+  p.off = expert_offsets;
+  p.pair_token = pair_token;
+  p.pair_pos = pair_pos;
+  p.topk_w = topk_w;
+  p.a_codes = a->codes;
+  p.a_scales = a->scales;
+  p.K = K;
+  p.w_codes = w->codes;
+  p.w_scales = w->scales;
+  p.w_cb = w->codebook;
+  p.N = N;
+  p.n_tiles = (int)(stage == GBW_MOE_GATEUP_SWIGLU ? N / kMoeBN : N / kMoeBN);
+  p.h_bf16 = out->h_bf16;
+  p.h_codes = out->h_codes;
+  p.h_scales = out->h_scales;
+  p.y = out->y;
+  p.pairbuf = (stage == GBW_MOE_DOWN_COMBINE && det) ? reinterpret_cast<float*>(ws) : nullptr;
+  const int64_t m_tiles_max = cdiv(P, kMoeBM) + E;
+  int64_t grid = m_tiles_max * p.n_tiles;
+  grid = cdiv(grid, 8) * 8;
+  if (grid > INT32_MAX) return fail(GBW_E_SHAPE, "moe_grouped_gemm: problem too large");
+  p.total_tiles = (int)grid;
+  if (stage == GBW_MOE_DOWN_COMBINE && !det) {
+    if ((st = launch_fill_zero(out->y, T * N, s))) return st;
+  }
+  if (e4m3) {
+    st = launch_moe_bf16(p, a, w, (int)grid, s);
+  } else {
+    if (w->fmt == GBW_FMT_VQ4_E8M0)
+      hipLaunchKernelGGL(k_moe_fp4<W_VQ>, dim3((unsigned)grid), dim3(kMoeThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL(k_moe_fp4<W_MX>, dim3((unsigned)grid), dim3(kMoeThreads), 0, s, p);
+    st = check_launch("moe_grouped_gemm");
+  }
+  if (st) return st;
+  if (stage == GBW_MOE_DOWN_COMBINE && det) {
+    hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)cdiv(cdiv(T * N, 4), 256)), dim3(256), 0, s, p.pairbuf,
+                       pair_pos, topk, T, N, out->y);
+    st = check_launch("moe_grouped_gemm(combine)");
+  }
+  return st;
+}

@@ -1,0 +1,209 @@
+// MoE routing: top-k experts per token, softmax weights over the chosen k,
+// and the (expert, token)-sorted pair list the grouped GEMMs walk.
+//
+// The experts being routed are the quantized FFN experts of "CodeQuant:
+// Unified Clustering and Quantization for Enhanced Outlier Smoothing in
+// Low-Precision Mixture-of-Experts" (Fig. 1, Fig. 2) and the expert
+// down-projections of "PRQuant: Permutation Residual Quantization for
+// Low-Overhead Inference" (§4, §5.1).  The pages fix no routing rule; the one
+// here is: the k largest logits (ties to the lower expert id), weights
+// exp(l_j - l_max) / sum over the chosen k.
+//
+// Three kernels, no atomics on global memory, so the pair order is fixed:
+//  1. k_route_topk: one thread per token keeps a sorted top-k in registers
+//     while it scans the token's logits; a wave = a chunk of 64 tokens
+//     builds, in LDS, a 64-bit mask per expert of the chunk's tokens that
+//     chose it and writes the per-(chunk, expert) counts.
+//  2. k_route_scan: exclusive scan of the counts in (expert, chunk) order ->
+//     expert_offsets and the first pair slot of every (chunk, expert).
+//  3. k_route_scatter: a token's pair index = its chunk's slot for the
+//     expert + the number of earlier tokens of the chunk in that expert's
+//     mask (a popcount).
+#include "common.hpp"
+
+namespace gbw {
+
+constexpr int kRouteThreads = 256;  // 4 chunks of 64 tokens per workgroup
+constexpr int kMaxTopk = 16;
+constexpr int kMaxExperts = 1024;
+
+__device__ __forceinline__ int64_t n_chunks(int64_t T) { return (T + 63) / 64; }
+
+template <int K>
+__global__ __launch_bounds__(kRouteThreads) void k_route_topk(const float* __restrict__ logits, int64_t T, int E,
+                                                             int32_t* __restrict__ topk_ids,
+                                                             float* __restrict__ topk_w,
+                                                             int32_t* __restrict__ counts) {
+  __shared__ unsigned long long mask[kRouteThreads / 64][kMaxExperts];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t chunk = (int64_t)blockIdx.x * (kRouteThreads / 64) + wv;
+  const int64_t t = chunk * 64 + lane;
+  for (int e = lane; e < E; e += 64) mask[wv][e] = 0ull;
+  __syncthreads();
+
+  float v[K];
+  int id[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    v[j] = -__builtin_huge_valf();
+    id[j] = E;  // sentinel, replaced by any real expert
+  }
+  const bool live = t < T;
+  if (live) {
+    const float* row = logits + t * E;
+    for (int e = 0; e < E; ++e) {
+      float c = row[e];
+      int ci = e;
+      // insertion: a candidate moves past entries it is strictly larger than,
+      // so an equal logit never displaces an earlier (lower) expert id
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const bool gt = c > v[j] || (id[j] == E);
+        const float tv = v[j];
+        const int ti = id[j];
+        v[j] = gt ? c : tv;
+        id[j] = gt ? ci : ti;
+        c = gt ? tv : c;
+        ci = gt ? ti : ci;
+      }
+    }
+    float ex[K], sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      ex[j] = expf(v[j] - v[0]);
+      sum += ex[j];
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      topk_ids[t * K + j] = id[j];
+      topk_w[t * K + j] = ex[j] / sum;
+      atomicOr(&mask[wv][id[j]], 1ull << lane);
+    }
+  }
+  __syncthreads();
+  if (chunk < n_chunks(T))
+    for (int e = lane; e < E; e += 64) counts[chunk * E + e] = __popcll(mask[wv][e]);
+}
+
+// Single workgroup: thread e owns expert e.
+__global__ __launch_bounds__(kMaxExperts) void k_route_scan(const int32_t* __restrict__ counts, int64_t C, int E,
+                                                           int32_t* __restrict__ base,
+                                                           int32_t* __restrict__ expert_offsets) {
+  __shared__ int32_t tot[kMaxExperts];
+  const int e = threadIdx.x;
+  int32_t s = 0;
+  if (e < E)
+    for (int64_t c = 0; c < C; ++c) s += counts[c * E + e];
+  tot[e] = e < E ? s : 0;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over experts
+  for (int o = 1; o < kMaxExperts; o <<= 1) {
+    const int32_t add = e >= o ? tot[e - o] : 0;
+    __syncthreads();
+    tot[e] += add;
+    __syncthreads();
+  }
+  if (e < E) {
+    int32_t run = tot[e] - s;  // exclusive offset of expert e
+    expert_offsets[e] = run;
+    for (int64_t c = 0; c < C; ++c) {
+      base[c * E + e] = run;
+      run += counts[c * E + e];
+    }
+    if (e == E - 1) expert_offsets[E] = run;
+  }
+}
+
+template <int K>
+__global__ __launch_bounds__(kRouteThreads) void k_route_scatter(const int32_t* __restrict__ topk_ids, int64_t T,
+                                                                int E, const int32_t* __restrict__ base,
+                                                                int32_t* __restrict__ pair_token,
+                                                                int32_t* __restrict__ pair_pos) {
+  __shared__ unsigned long long mask[kRouteThreads / 64][kMaxExperts];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t chunk = (int64_t)blockIdx.x * (kRouteThreads / 64) + wv;
+  const int64_t t = chunk * 64 + lane;
+  for (int e = lane; e < E; e += 64) mask[wv][e] = 0ull;
+  __syncthreads();
+  int id[K];
+  const bool live = t < T;
+  if (live) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      id[j] = topk_ids[t * K + j];
+      atomicOr(&mask[wv][id[j]], 1ull << lane);
+    }
+  }
+  __syncthreads();
+  if (!live) return;
+  const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int32_t p = base[chunk * E + id[j]] + __popcll(mask[wv][id[j]] & below);
+    pair_token[p] = (int32_t)t;
+    pair_pos[t * K + j] = p;
+  }
+}
+
+size_t ws_moe_route(int64_t T, int64_t E) {
+  if (T <= 0 || E <= 0) return 0;
+  const int64_t C = (T + 63) / 64;
+  return (size_t)2 * C * E * sizeof(int32_t);  // counts + bases
+}
+
+template <int K>
+static int launch_route(const float* logits, int64_t T, int E, int32_t* ids, float* w, int32_t* off, int32_t* pt,
+                        int32_t* pp, int32_t* ws, hipStream_t st) {
+  const int64_t C = (T + 63) / 64;
+  int32_t* counts = ws;
+  int32_t* base = ws + C * E;
+  const unsigned blocks = (unsigned)cdiv(C, kRouteThreads / 64);
+  hipLaunchKernelGGL(k_route_topk<K>, dim3(blocks), dim3(kRouteThreads), 0, st, logits, T, E, ids, w, counts);
+  int s = check_launch("moe_route(topk)");
+  if (s) return s;
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(kMaxExperts), 0, st, counts, C, E, base, off);
+  if ((s = check_launch("moe_route(scan)"))) return s;
+  hipLaunchKernelGGL(k_route_scatter<K>, dim3(blocks), dim3(kRouteThreads), 0, st, ids, T, E, base, pt, pp);
+  return check_launch("moe_route(scatter)");
+}
+
+}  // namespace gbw
+
+using namespace gbw;
+
+extern "C" int moe_route(const float* logits, int64_t T, int32_t E, int32_t topk, int32_t* topk_ids, float* topk_w,
+                         int32_t* expert_offsets, int32_t* pair_token, int32_t* pair_pos, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (T < 0 || E <= 0 || E > kMaxExperts) return fail(GBW_E_ARG, "moe_route: need 0 < E <= %d", kMaxExperts);
+  if (topk < 1 || topk > E || topk > kMaxTopk) return fail(GBW_E_ARG, "moe_route: need 1 <= topk <= min(E, 16)");
+  if (!expert_offsets) return fail(GBW_E_ARG, "moe_route: null expert_offsets");
+  if (T > 0 && (!logits || !topk_ids || !topk_w || !pair_token || !pair_pos))
+    return fail(GBW_E_ARG, "moe_route: null pointer");
+  if ((int64_t)T * topk > INT32_MAX) return fail(GBW_E_SHAPE, "moe_route: too many pairs for int32 indices");
+  if (T > 0 && (!ws || ws_bytes < ws_moe_route(T, E)))
+    return fail(GBW_E_WORKSPACE, "moe_route: needs %zu bytes of workspace", ws_moe_route(T, E));
+  int st = check_device();
+  if (st) return st;
+  hipStream_t s = as_stream(stream);
+  if (T == 0) {
+    // no tokens: every expert offset is zero
+    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(kMaxExperts), 0, s, (const int32_t*)nullptr, (int64_t)0, E,
+                       (int32_t*)nullptr, expert_offsets);
+    return check_launch("moe_route(empty)");
+  }
+  int32_t* w32 = reinterpret_cast<int32_t*>(ws);
+  switch (topk) {
+#define GBW_ROUTE_CASE(K) \
+  case K:                 \
+    return launch_route<K>(logits, T, E, topk_ids, topk_w, expert_offsets, pair_token, pair_pos, w32, s);
+    GBW_ROUTE_CASE(1)
+    GBW_ROUTE_CASE(2)
+    GBW_ROUTE_CASE(4)
+    GBW_ROUTE_CASE(6)
+    GBW_ROUTE_CASE(8)
+    GBW_ROUTE_CASE(16)
+#undef GBW_ROUTE_CASE
+    default:
+      return fail(GBW_E_UNSUPPORTED, "moe_route: topk must be one of 1, 2, 4, 6, 8, 16");
+  }
+}

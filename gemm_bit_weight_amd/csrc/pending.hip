@@ -1,20 +1,9 @@
-// Entry points whose kernels are not built yet: they validate nothing and
-// report GBW_E_UNSUPPORTED.
+// The E4M3-B16 grouped GEMM (bf16 MFMA) is not built yet.
 #include "common.hpp"
 
 namespace gbw {
-size_t ws_moe_route(int64_t, int64_t) { return 0; }
-size_t ws_moe_gemm(int64_t, int64_t, int32_t) { return 0; }
+struct MoeArgs;
+int launch_moe_bf16(const MoeArgs&, const gbw_act*, const gbw_weight*, int, hipStream_t) {
+  return fail(GBW_E_UNSUPPORTED, "moe_grouped_gemm: E4M3-B16 path not built");
+}
 }  // namespace gbw
-
-using namespace gbw;
-
-extern "C" int moe_route(const float*, int64_t, int32_t, int32_t, int32_t*, float*, int32_t*, int32_t*, int32_t*,
-                         void*, size_t, void*) {
-  return fail(GBW_E_UNSUPPORTED, "moe_route: not built");
-}
-extern "C" int moe_grouped_gemm(int32_t, int64_t, int32_t, const int32_t*, const int32_t*, const int32_t*,
-                                const float*, const gbw_act*, const gbw_weight*, const gbw_moe_out*, int32_t,
-                                void*, size_t, void*) {
-  return fail(GBW_E_UNSUPPORTED, "moe_grouped_gemm: not built");
-}
