@@ -198,12 +198,22 @@ extern "C" int moe_route(const float* logits, int64_t T, int32_t E, int32_t topk
     return launch_route<K>(logits, T, E, topk_ids, topk_w, expert_offsets, pair_token, pair_pos, w32, s);
     GBW_ROUTE_CASE(1)
     GBW_ROUTE_CASE(2)
+    GBW_ROUTE_CASE(3)
     GBW_ROUTE_CASE(4)
+    GBW_ROUTE_CASE(5)
     GBW_ROUTE_CASE(6)
+    GBW_ROUTE_CASE(7)
     GBW_ROUTE_CASE(8)
+    GBW_ROUTE_CASE(9)
+    GBW_ROUTE_CASE(10)
+    GBW_ROUTE_CASE(11)
+    GBW_ROUTE_CASE(12)
+    GBW_ROUTE_CASE(13)
+    GBW_ROUTE_CASE(14)
+    GBW_ROUTE_CASE(15)
     GBW_ROUTE_CASE(16)
 #undef GBW_ROUTE_CASE
     default:
-      return fail(GBW_E_UNSUPPORTED, "moe_route: topk must be one of 1, 2, 4, 6, 8, 16");
+      return fail(GBW_E_UNSUPPORTED, "moe_route: topk out of range");
   }
 }
