@@ -56,6 +56,9 @@ struct MoeArgs {
   const uint8_t* w_codes;  // MX: [E][N][K/2]; VQ: idx [E][N][K/4]
   const uint8_t* w_scales; // [E][N][K/32]
   const uint16_t* w_cb;    // VQ: [E][N/64][K/64][256]
+  const float* a_ts;       // E4M3: activation tensor scale [1]
+  const float* w_ts;       // E4M3: weight tensor scales [E][ts_per]
+  int32_t ts_per;
   int64_t N;               // weight rows per expert (2I or H)
   int32_t n_tiles;         // output tiles along N
   int32_t total_tiles;
@@ -397,6 +400,228 @@ __global__ __launch_bounds__(kMoeThreads) void k_moe_fp4(const MoeArgs p) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// E4M3-B16 experts: exact decode to fp16, fp16 MFMA
+// ---------------------------------------------------------------------------
+// An E4M3-B16 element is e2m1 * s with s an E4M3 block scale: at most 6
+// significant bits and a magnitude in [2^-10, 2688], so it is exact in fp16
+// (and in bf16); both operands are decoded once per tile into fp16 LDS tiles
+// and contracted with v_mfma_f32_16x16x32_f16.  The two FP32 tensor scales
+// are applied to the fp32 accumulators in the epilogue.  (There is no exact
+// route through the FP4/FP8 scaled MFMA: its block scales are powers of two
+// per 32 elements, an E4M3 scale carries a 3-bit mantissa per 16.)
+//
+// Decode: one dword of codes (8 elements) -> four fp16x2 words through a
+// byte-permute lookup in the constant 16-entry E2M1 table, then one packed
+// fp16 multiply by the block scale per word (exact).  The lookup yields the
+// elements in the order 0,2,4,6,1,3,5,7; A and B are decoded alike, so the
+// MFMA pairs the same K indices.
+constexpr int kRowH = 144;  // LDS bytes per fp16 row per stage (64 elements + 16 pad)
+
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t perm16(uint32_t s7, uint32_t mask, uint32_t t0, uint32_t t1, uint32_t t2,
+                                           uint32_t t3) {
+  const uint32_t lo = __builtin_amdgcn_perm(t1, t0, s7);
+  const uint32_t hi = __builtin_amdgcn_perm(t3, t2, s7);
+  return (hi & mask) | (lo & ~mask);
+}
+
+// fp16 bit patterns of the 16 E2M1 codes, as low-byte and high-byte planes
+// (4 entries per dword, entry i in byte i % 4 of dword i / 4)
+// magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 -> 0x0000 0x3800 0x3C00 0x3E00 0x4000 0x4200 0x4400 0x4600
+constexpr uint32_t kE2L0 = 0x00000000u, kE2L1 = 0x00000000u, kE2L2 = 0x00000000u, kE2L3 = 0x00000000u;
+constexpr uint32_t kE2H0 = 0x3E3C3800u, kE2H1 = 0x46444240u, kE2H2 = 0xBEBCB880u, kE2H3 = 0xC6C4C2C0u;
+
+__device__ __forceinline__ void e4m3_decode8(uint32_t w, uint32_t sc2, uint32_t (&o)[4]) {
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const uint32_t s = half == 0 ? (w & 0x0F0F0F0Fu) : ((w >> 4) & 0x0F0F0F0Fu);
+    const uint32_t s7 = s & 0x07070707u;
+    const uint32_t b3 = (s >> 3) & 0x01010101u;
+    const uint32_t mask = (b3 << 8) - b3;
+    const uint32_t lo = perm16(s7, mask, kE2L0, kE2L1, kE2L2, kE2L3);
+    const uint32_t hi = perm16(s7, mask, kE2H0, kE2H1, kE2H2, kE2H3);
+    const uint32_t p0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+    const uint32_t p1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+    const v2h sv = __builtin_bit_cast(v2h, sc2);
+    o[2 * half + 0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, p0) * sv);
+    o[2 * half + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, p1) * sv);
+  }
+}
+
+// E4M3 scale code -> fp16 bits duplicated into both halves (exact: an E4M3
+// value has 4 significant bits and lies in [2^-9, 448])
+__device__ __forceinline__ uint32_t e4m3_to_h2(uint32_t c) {
+  const _Float16 h = (_Float16)e4m3_value(c & 0xFFu);
+  const uint32_t b = __builtin_bit_cast(uint16_t, h);
+  return b | (b << 16);
+}
+
+__global__ __launch_bounds__(kMoeThreads) void k_moe_e4m3(const MoeArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t sA[2][kMoeBM * kRowH];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[2][kMoeBN * kRowH];
+  __shared__ int scan[kMoeThreads];
+  __shared__ int s_tok[kMoeBM];
+  __shared__ float s_w[kMoeBM];
+
+  TileInfo ti;
+  if (!find_tile(p, ti, scan)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int64_t K = p.K;
+  const int steps = (int)(K / 64);
+
+  for (int r = tid; r < kMoeBM; r += kMoeThreads) {
+    int tok = 0;
+    float wt = 0.f;
+    if (r < ti.rows) {
+      const int pr = ti.row0 + r;
+      tok = p.pair_token[pr];
+      if (p.stage == GBW_MOE_DOWN_COMBINE)
+        for (int j = 0; j < p.topk; ++j)
+          if (p.pair_pos[(int64_t)tok * p.topk + j] == pr) wt = p.topk_w[(int64_t)tok * p.topk + j];
+    }
+    s_tok[r] = tok;
+    s_w[r] = wt;
+  }
+  __syncthreads();
+
+  // thread tid stages row tid of A and row tid of B: 64 elements = 32 bytes of
+  // codes and one dword of four E4M3 scales per stage
+  const int rr = tid < ti.rows ? tid : ti.rows - 1;
+  const int64_t asrc = p.stage == GBW_MOE_GATEUP_SWIGLU ? (int64_t)s_tok[rr] : (int64_t)(ti.row0 + rr);
+  const uint8_t* arow = p.a_codes + asrc * (K / 2);
+  const uint8_t* ascl = p.a_scales + asrc * (K / 16);
+  const int64_t wr = (int64_t)ti.e * p.N + b_row(p, ti.nt, tid);
+  const uint8_t* brow_c = p.w_codes + wr * (K / 2);
+  const uint8_t* brow_s = p.w_scales + wr * (K / 16);
+
+  v4i pa[2], pb[2];
+  uint32_t pas, pbs;
+  auto gload = [&](int s) {
+    pa[0] = load16(arow + (int64_t)s * 32);
+    pa[1] = load16(arow + (int64_t)s * 32 + 16);
+    pb[0] = load16(brow_c + (int64_t)s * 32);
+    pb[1] = load16(brow_c + (int64_t)s * 32 + 16);
+    pas = *reinterpret_cast<const uint32_t*>(ascl + (int64_t)s * 4);
+    pbs = *reinterpret_cast<const uint32_t*>(brow_s + (int64_t)s * 4);
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int op = 0; op < 2; ++op) {
+      const v4i* src = op == 0 ? pa : pb;
+      const uint32_t scl = op == 0 ? pas : pbs;
+      uint8_t* dst = op == 0 ? &sA[buf][tid * kRowH] : &sB[buf][tid * kRowH];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        // dword d of the 32 code bytes holds elements 8d..8d+7, block d/2
+        const uint32_t w = (uint32_t)src[d >> 2][d & 3];
+        uint32_t o[4];
+        e4m3_decode8(w, e4m3_to_h2(scl >> (8 * (d >> 1))), o);
+        *reinterpret_cast<v4i*>(dst + 16 * d) = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+      }
+    }
+  };
+
+  v4f acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  int brow[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    brow[j] = p.stage == GBW_MOE_GATEUP_SWIGLU ? (j < 4 ? 64 * wn + 16 * j : 128 + 64 * wn + 16 * (j - 4))
+                                               : 128 * wn + 16 * j;
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int s = 0; s < steps; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < steps) gload(s + 1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      v8h bf[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        bf[j] = *reinterpret_cast<const v8h*>(&sB[buf][(brow[j] + r16) * kRowH + 64 * ks + 16 * g4]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const v8h af = *reinterpret_cast<const v8h*>(&sA[buf][(128 * wm + 16 * i + r16) * kRowH + 64 * ks + 16 * g4]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    if (s + 1 < steps) {
+      lstore(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  const float sa = p.a_ts[0];
+  if (p.stage == GBW_MOE_DOWN_COMBINE) {
+    const int64_t H = p.N;
+    const float sw = sa * p.w_ts[(int64_t)ti.e * p.ts_per];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 128 * wm + 16 * i + 4 * g4 + r;
+        if (m >= ti.rows) continue;
+        const float wt = s_w[m] * sw;
+        float* dst = p.pairbuf ? p.pairbuf + (int64_t)(ti.row0 + m) * H : p.y + (int64_t)s_tok[m] * H;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int64_t n = (int64_t)ti.nt * kMoeBN + 128 * wn + 16 * j + r16;
+          const float v = wt * acc[i][j][r];
+          if (p.pairbuf)
+            dst[n] = v;
+          else
+            unsafeAtomicAdd(dst + n, v);
+        }
+      }
+    return;
+  }
+  // GATEUP: h = bf16(silu(g) * u), staged in LDS for coalesced stores
+  const float sg = sa * p.w_ts[(int64_t)ti.e * p.ts_per];
+  const float su = sa * p.w_ts[(int64_t)ti.e * p.ts_per + (p.ts_per > 1 ? 1 : 0)];
+  __syncthreads();
+  uint16_t* sH = reinterpret_cast<uint16_t*>(&sA[0][0]);  // [256][128] bf16
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 128 * wm + 16 * i + 4 * g4 + r;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float gv = acc[i][jj][r] * sg, uv = acc[i][jj + 4][r] * su;
+        const float h = gv / (1.0f + expf(-gv)) * uv;
+        sH[m * 128 + 64 * wn + 16 * jj + r16] = (uint16_t)f32_to_bf16_rne(h);
+      }
+    }
+  __syncthreads();
+  const int64_t I = p.N / 2;
+  for (int c = tid; c < kMoeBM * 16; c += kMoeThreads) {
+    const int m = c >> 4, q = c & 15;
+    if (m < ti.rows)
+      *reinterpret_cast<v4i*>(p.h_bf16 + (int64_t)(ti.row0 + m) * I + (int64_t)ti.nt * 128 + 8 * q) =
+          *reinterpret_cast<const v4i*>(&sH[m * 128 + 8 * q]);
+  }
+}
+
+int launch_moe_bf16(const MoeArgs& p, const gbw_act* a, const gbw_weight* w, int grid, hipStream_t st) {
+  MoeArgs q = p;
+  q.a_ts = a->tensor_scale;
+  q.w_ts = w->tensor_scale;
+  q.ts_per = w->ts_per_expert;
+  hipLaunchKernelGGL(k_moe_e4m3, dim3((unsigned)grid), dim3(kMoeThreads), 0, st, q);
+  return check_launch("moe_grouped_gemm(e4m3)");
+}
+
 // y[t][:] = sum_j pairbuf[pair_pos[t][j]][:] in slot order (deterministic combine)
 __global__ void k_moe_combine(const float* __restrict__ pairbuf, const int32_t* __restrict__ pair_pos, int topk,
                               int64_t T, int64_t H, float* __restrict__ y) {
@@ -417,8 +642,6 @@ size_t ws_moe_gemm(int64_t P, int64_t N, int32_t fmt) {
   // only the deterministic down/combine path uses it: a [P][N] fp32 pair buffer
   return P > 0 && N > 0 ? (size_t)P * N * sizeof(float) : 0;
 }
-
-int launch_moe_bf16(const MoeArgs& p, const gbw_act* a, const gbw_weight* w, int grid, hipStream_t st);
 
 }  // namespace gbw
 
@@ -443,6 +666,8 @@ extern "C" int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const in
   if (!fp4 && !e4m3) return fail(GBW_E_UNSUPPORTED, "moe_grouped_gemm: unsupported activation/weight formats");
   if (stage == GBW_MOE_GATEUP_SWIGLU) {
     if (N % 256) return fail(GBW_E_SHAPE, "moe_grouped_gemm: gate/up rows (2I) must be a multiple of 256");
+    if (e4m3 && w->ts_per_expert != 2)
+      return fail(GBW_E_ARG, "moe_grouped_gemm: E4M3 gate/up needs two tensor scales per expert (gate, up)");
     if (a->rows < T) return fail(GBW_E_SHAPE, "moe_grouped_gemm: activation has fewer rows than tokens");
     if (fp4 && (!out->h_codes || !out->h_scales) && !out->h_bf16)
       return fail(GBW_E_ARG, "moe_grouped_gemm: gate/up needs h_codes+h_scales or h_bf16");

@@ -1,14 +1,20 @@
-"""GPU parity: MoE routing and the grouped FP4 expert GEMMs (MXFP4 and
-VQ->MX weights) against the oracle, stage by stage.
+"""GPU parity: MoE routing and the grouped expert GEMMs (MXFP4, VQ->MX and
+E4M3-B16 weights) against the oracle, stage by stage.
 
-* routing: expert ids, offsets and pair lists bit-exact; weights to 1e-6.
-* gate/up: the GPU's bf16 h against bf16(silu(g)u) of the oracle's exact g, u
-  within one bf16 rounding (2^-8 relative) plus the 1e-3 row tolerance; the
-  GPU's requantized h bit-exact against the oracle's quantizer applied to the
-  GPU's own h (the two sides share data, not code).
-* down/combine: y against the oracle (fed the GPU's quantized h, which the
-  previous check proved equal to the oracle's quantization) within the 1e-3
-  row tolerance, for the atomic and the deterministic combine.
+The oracle always runs from the synthetic inputs alone (its own
+quantization of x, the weights and h); GPU outputs are compared with it and
+are never fed into it.
+* routing: expert ids, offsets and pair lists bit-exact; weights to 2e-6.
+* x and weight encodings: bit-exact.
+* gate/up: the GPU's bf16 h against the oracle's bf16(silu(g)u) within one
+  bf16 rounding step (2^-8 relative) plus the 1e-3 row tolerance (the GPU
+  accumulates g, u in fp32, the oracle exactly).
+* requantized h: every 32/16-element block whose h the two sides rounded to
+  the same bf16 values must carry the same codes and scale (bit-exact);
+  blocks whose h differs by a bf16 step may differ and are counted.
+* down/combine: y within the 1e-3 row tolerance for every token whose routed
+  h rows were requantized identically; tokens holding an explained code
+  difference are held to 2e-2 and counted.
 """
 
 import numpy as np
@@ -69,18 +75,32 @@ def test_route_ties_and_permutation():
     _check_route(logits, 8)
 
 
-def _mx_weights(w_f32):
-    """E8M0-B32 quantization of [E][N][K] weights with the library's quantizer."""
-    E, N, K = w_f32.shape
-    q = gbw.mx_quantize(w_f32.reshape(E * N, K).contiguous(), gbw.FMT_E8M0_B32)
-    return gbw.Weight(gbw.FMT_E8M0_B32, N, K, q.codes.view(E, N, K // 2), q.scales.view(E, N, K // 32),
-                      n_experts=E)
+def _bf16_ulp(v):
+    """Spacing of bf16 numbers at |v| (float64 array)."""
+    a = np.abs(v)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, 2.0 ** (e - 7), 2.0 ** -133)
 
 
-def _vq_weights(v, N, K):
-    E = v["idx"].shape[0]
-    return gbw.Weight(gbw.FMT_VQ4_E8M0, N, K, v["idx"].to(DEV), v["scales"].to(DEV), v["codebook"].to(DEV),
-                      n_experts=E)
+def _check_h(h_gpu_bits, h_ref):
+    h_gpu = oracle.bf16_bits_to_f32(h_gpu_bits).astype(np.float64)
+    err = np.abs(h_gpu - h_ref)
+    bound = _bf16_ulp(h_ref) + 1e-3 * np.linalg.norm(h_ref, axis=1, keepdims=True)
+    assert np.all(err <= bound), f"h outside tolerance: worst {np.max(err / bound):.3f}"
+
+
+def _check_requant(h_gpu_bits, h_ref_bits, codes_gpu, scales_gpu, codes_ref, scales_ref, bs):
+    """Blocks with identical h on both sides must quantize identically."""
+    P, I = h_ref_bits.shape
+    same = (h_gpu_bits.reshape(P, I // bs, bs) == h_ref_bits.reshape(P, I // bs, bs)).all(axis=2)
+    c_eq = (oracle.unpack_nibbles(codes_gpu).reshape(P, I // bs, bs) ==
+            oracle.unpack_nibbles(codes_ref).reshape(P, I // bs, bs)).all(axis=2)
+    s_eq = scales_gpu == scales_ref
+    blk_eq = c_eq & s_eq
+    assert np.all(blk_eq[same]), f"{int((~blk_eq[same]).sum())} blocks with identical h quantized differently"
+    frac = float((~blk_eq).mean())
+    assert frac < 0.05, f"too many blocks differ ({frac:.3%})"
+    return blk_eq.all(axis=1)   # rows requantized identically
 
 
 class _LazyExperts:
@@ -99,86 +119,253 @@ class _LazyExperts:
         return self._cache[e]
 
 
-def _w_codes_np(W):
-    """[E][N][K/2] E2M1 codes + [E][N][K/32] scales of a weight, as numpy."""
-    E, N, K = W.n_experts, W.N, W.K
-    scales = _LazyExperts((E, N, K // 32), lambda e: to_np(W.scales[e]))
-    if W.fmt == gbw.FMT_E8M0_B32:
-        return _LazyExperts((E, N, K // 2), lambda e: to_np(W.codes[e])), scales
-    return _LazyExperts((E, N, K // 2), lambda e: oracle.vq_decode_codes(
-        to_np(W.codes[e]), W.codebook[e].cpu().numpy().view(np.uint16))), scales
+class _Problem:
+    """One MoE FFN problem: synthetic inputs, the oracle's view of them, and
+    the GPU weight descriptors built from the same inputs."""
+
+    def __init__(self, fmt, x, logits, topk, gate_up, down, I):
+        self.fmt, self.x, self.logits, self.topk, self.I = fmt, x, logits, topk, I
+        T, H = x.shape
+        self.T, self.H = T, H
+        E = (gate_up["w"] if fmt != "vq" else gate_up["idx"]).shape[0]
+        self.E = E
+        if fmt == "vq":
+            self.Wgu = gbw.Weight(gbw.FMT_VQ4_E8M0, 2 * I, H, gate_up["idx"].to(DEV), gate_up["scales"].to(DEV),
+                                  gate_up["codebook"].to(DEV), n_experts=E)
+            self.Wd = gbw.Weight(gbw.FMT_VQ4_E8M0, H, I, down["idx"].to(DEV), down["scales"].to(DEV),
+                                 down["codebook"].to(DEV), n_experts=E)
+            gcpu = {k: v.cpu() for k, v in gate_up.items()}
+            dcpu = {k: v.cpu() for k, v in down.items()}
+            self.ref_gu = (_LazyExperts((E, 2 * I, H // 2), lambda e: oracle.vq_decode_codes(
+                gcpu["idx"][e].numpy(), gcpu["codebook"][e].numpy().view(np.uint16))),
+                _LazyExperts((E, 2 * I, H // 32), lambda e: gcpu["scales"][e].numpy()), None)
+            self.ref_d = (_LazyExperts((E, H, I // 2), lambda e: oracle.vq_decode_codes(
+                dcpu["idx"][e].numpy(), dcpu["codebook"][e].numpy().view(np.uint16))),
+                _LazyExperts((E, H, I // 32), lambda e: dcpu["scales"][e].numpy()), None)
+            return
+        wgu, wd = gate_up["w"], down["w"]          # fp32 [E][2I][H], [E][H][I] (on the GPU)
+        if fmt == "e8m0_b32":
+            q = gbw.mx_quantize(wgu.reshape(E * 2 * I, H), gbw.FMT_E8M0_B32)
+            self.Wgu = gbw.Weight(gbw.FMT_E8M0_B32, 2 * I, H, q.codes.view(E, 2 * I, H // 2),
+                                  q.scales.view(E, 2 * I, H // 32), n_experts=E)
+            q = gbw.mx_quantize(wd.reshape(E * H, I), gbw.FMT_E8M0_B32)
+            self.Wd = gbw.Weight(gbw.FMT_E8M0_B32, H, I, q.codes.view(E, H, I // 2), q.scales.view(E, H, I // 32),
+                                 n_experts=E)
+            cache = {}
+
+            def qe(which, e):
+                key = (which, e)
+                if key not in cache:
+                    w = (wgu if which == "gu" else wd)[e].cpu().numpy()
+                    cache[key] = oracle.quantize_e8m0_b32(w)
+                return cache[key]
+            self.ref_gu = (_LazyExperts((E, 2 * I, H // 2), lambda e: qe("gu", e)[0]),
+                           _LazyExperts((E, 2 * I, H // 32), lambda e: qe("gu", e)[1]), None)
+            self.ref_d = (_LazyExperts((E, H, I // 2), lambda e: qe("d", e)[0]),
+                          _LazyExperts((E, H, I // 32), lambda e: qe("d", e)[1]), None)
+            return
+        # E4M3-B16: every (expert, matrix) has its own dynamic tensor scale; gate and up separately
+        gc = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=DEV)
+        gs = torch.empty((E, 2 * I, H // 16), dtype=torch.uint8, device=DEV)
+        gt = torch.empty((E, 2), dtype=torch.float32, device=DEV)
+        dc = torch.empty((E, H, I // 2), dtype=torch.uint8, device=DEV)
+        ds = torch.empty((E, H, I // 16), dtype=torch.uint8, device=DEV)
+        dt = torch.empty((E, 1), dtype=torch.float32, device=DEV)
+        for e in range(E):
+            for half in range(2):
+                rows = slice(half * I, (half + 1) * I)
+                out = gbw.Act(gbw.FMT_E4M3_B16, gc[e, rows], gs[e, rows])
+                gbw.mx_quantize(wgu[e, rows].contiguous(), gbw.FMT_E4M3_B16, out=out, tensor_scale=gt[e, half:half + 1])
+            out = gbw.Act(gbw.FMT_E4M3_B16, dc[e], ds[e])
+            gbw.mx_quantize(wd[e].contiguous(), gbw.FMT_E4M3_B16, out=out, tensor_scale=dt[e])
+        self.Wgu = gbw.Weight(gbw.FMT_E4M3_B16, 2 * I, H, gc, gs, None, gt, 2, E)
+        self.Wd = gbw.Weight(gbw.FMT_E4M3_B16, H, I, dc, ds, None, dt, 1, E)
+        cache = {}
+
+        def q4(which, e):
+            key = (which, e)
+            if key not in cache:
+                if which == "gu":
+                    w = wgu[e].cpu().numpy()
+                    a = oracle.quantize_e4m3_b16(w[:I])
+                    b = oracle.quantize_e4m3_b16(w[I:])
+                    cache[key] = (np.concatenate([a[0], b[0]]), np.concatenate([a[1], b[1]]), [a[2], b[2]])
+                else:
+                    cache[key] = oracle.quantize_e4m3_b16(wd[e].cpu().numpy())
+            return cache[key]
+        self.ref_gu = (_LazyExperts((E, 2 * I, H // 2), lambda e: q4("gu", e)[0]),
+                       _LazyExperts((E, 2 * I, H // 16), lambda e: q4("gu", e)[1]),
+                       _LazyExperts((E, 2), lambda e: q4("gu", e)[2]))
+        self.ref_d = (_LazyExperts((E, H, I // 2), lambda e: q4("d", e)[0]),
+                      _LazyExperts((E, H, I // 16), lambda e: q4("d", e)[1]),
+                      _LazyExperts((E,), lambda e: q4("d", e)[2]))
+
+    def check_weight_encodings(self, experts):
+        if self.fmt == "vq":
+            return
+        for e in experts:
+            assert np.array_equal(to_np(self.Wgu.codes[e]), self.ref_gu[0][e])
+            assert np.array_equal(to_np(self.Wgu.scales[e]), self.ref_gu[1][e])
+            assert np.array_equal(to_np(self.Wd.codes[e]), self.ref_d[0][e])
+            assert np.array_equal(to_np(self.Wd.scales[e]), self.ref_d[1][e])
+            if self.fmt == "e4m3_b16":
+                assert np.array_equal(to_np(self.Wgu.tensor_scale[e]), np.array(self.ref_gu[2][e], np.float32))
+                assert to_np(self.Wd.tensor_scale[e])[0] == self.ref_d[2][e]
 
 
-def _run_and_check(x, logits, topk, Wgu, Wd, tokens=None, experts=None):
-    T, H = x.shape
-    I = Wgu.N // 2
-    route, ref_route = _check_route(logits, topk)
+def _run_and_check(pb, tokens=None, experts=None, h_amax=None):
+    """Run the FFN on the GPU and check it against the oracle stage by stage.
+
+    ``h_amax`` (E4M3-B16 only): quantize h with the static tensor scale
+    amax/2688 on both sides instead of the dynamic one, so the oracle needs
+    h only for the sampled pairs.
+    """
+    T, H, I, topk = pb.T, pb.H, pb.I, pb.topk
+    fmt = "e8m0_b32" if pb.fmt == "vq" else pb.fmt
+    e4 = fmt == "e4m3_b16"
+    afmt = gbw.FMT_E4M3_B16 if e4 else gbw.FMT_E8M0_B32
+    bs = 16 if e4 else 32
+    route, ref_route = _check_route(pb.logits, topk)
     P = T * topk
-    xq = gbw.mx_quantize(x, gbw.FMT_E8M0_B32)
+    # ---- GPU pipeline ----
+    xq = gbw.mx_quantize(pb.x, afmt)
     hb = torch.empty((P, I), dtype=torch.bfloat16, device=DEV)
-    hc = torch.empty((P, I // 2), dtype=torch.uint8, device=DEV)
-    hs = torch.empty((P, I // 32), dtype=torch.uint8, device=DEV)
-    gbw.moe_grouped_gemm(gbw.MOE_GATEUP_SWIGLU, route, xq, Wgu, h_bf16=hb, h_codes=hc, h_scales=hs)
+    if not e4:
+        hc = torch.empty((P, I // 2), dtype=torch.uint8, device=DEV)
+        hs = torch.empty((P, I // 32), dtype=torch.uint8, device=DEV)
+        gbw.moe_grouped_gemm(gbw.MOE_GATEUP_SWIGLU, route, xq, pb.Wgu, h_bf16=hb, h_codes=hc, h_scales=hs)
+        hq = gbw.Act(afmt, hc, hs)
+    else:
+        gbw.moe_grouped_gemm(gbw.MOE_GATEUP_SWIGLU, route, xq, pb.Wgu, h_bf16=hb)
+        if h_amax is None:
+            hq = gbw.mx_quantize(hb, afmt)
+        else:
+            st = torch.tensor([oracle.formats.tensor_scale_e4m3(np.float32(h_amax))], dtype=torch.float32,
+                              device=DEV)
+            hq = gbw.mx_quantize(hb, afmt, tensor_scale=st, dynamic=False)
     y = torch.empty((T, H), dtype=torch.float32, device=DEV)
-    hq = gbw.Act(gbw.FMT_E8M0_B32, hc, hs)
-    gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, Wd, y=y)
+    gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, pb.Wd, y=y)
     yd = torch.empty_like(y)
-    gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, Wd, y=yd, flags=gbw.DETERMINISTIC)
+    gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, pb.Wd, y=yd, flags=gbw.DETERMINISTIC)
     yd2 = torch.empty_like(y)
-    gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, Wd, y=yd2, flags=gbw.DETERMINISTIC)
+    gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, pb.Wd, y=yd2, flags=gbw.DETERMINISTIC)
     torch.cuda.synchronize()
     assert torch.equal(yd, yd2), "deterministic combine differs between runs"
 
-    # activation quantization (bit-exact)
-    ac, as_ = oracle.quantize_e8m0_b32(x.float().cpu().numpy())
+    # ---- oracle pipeline, from the synthetic inputs only ----
+    xn = pb.x.float().cpu().numpy()
+    if e4:
+        ac, as_, ats = oracle.quantize_e4m3_b16(xn)
+        assert to_np(xq.tensor_scale)[0] == ats
+    else:
+        ac, as_ = oracle.quantize_e8m0_b32(xn)
+        ats = None
     assert np.array_equal(to_np(xq.codes), ac) and np.array_equal(to_np(xq.scales), as_)
-    # gate/up + SwiGLU on the chosen pairs
     off = ref_route["expert_offsets"]
     if experts is None:
-        pairs = np.arange(P)
+        experts = list(range(pb.E))
+    pb.check_weight_encodings(experts[:4])
+    if tokens is None:
+        tokens = np.arange(T)
+    tokens = np.asarray(tokens)
+    whole = len(experts) == pb.E and len(tokens) == T
+
+    def oracle_h(pairs):
+        g, u = oracle.moe_gateup(ac, as_, fmt, ref_route, pb.ref_gu[0], pb.ref_gu[1], ats, pb.ref_gu[2],
+                                 pairs=pairs)
+        return g, u, oracle.swiglu_bf16(g, u)
+
+    def oracle_q(h_bits):
+        hf = oracle.bf16_bits_to_f32(h_bits)
+        if not e4:
+            c, s = oracle.quantize_e8m0_b32(hf)
+            return c, s, None
+        return oracle.quantize_e4m3_b16(hf, tensor_amax=h_amax)
+
+    # gate/up + SwiGLU on every pair of the chosen experts
+    pairs = np.concatenate([np.arange(off[e], off[e + 1]) for e in experts])
+    g, u, h_ref_bits = oracle_h(pairs)
+    _check_h(u16(hb)[pairs], g / (1.0 + np.exp(-g)) * u)
+
+    # requantization of h
+    if e4 and h_amax is None:
+        assert whole, "a dynamic E4M3 tensor scale needs the whole h"
+        qc, qs, qts = oracle_q(h_ref_bits)
+        same_ts = to_np(hq.tensor_scale)[0] == qts
+        if same_ts:
+            _check_requant(u16(hb), h_ref_bits, to_np(hq.codes), to_np(hq.scales), qc, qs, bs)
+        full_c, full_s, hts = qc, qs, qts
+        tp = np.arange(P)
+        row_same = ((to_np(hq.codes) == qc).all(axis=1) & (to_np(hq.scales) == qs).all(axis=1)) if same_ts \
+            else np.zeros(P, bool)
     else:
-        pairs = np.concatenate([np.arange(off[e], off[e + 1]) for e in experts])
-    gu_c, gu_s = _w_codes_np(Wgu)
-    g, u = oracle.moe_gateup(ac, as_, "e8m0_b32", ref_route, gu_c, gu_s, pairs=pairs)
-    h_ref = g / (1.0 + np.exp(-g)) * u
-    h_gpu = oracle.bf16_bits_to_f32(u16(hb)[pairs]).astype(np.float64)
-    err = np.abs(h_gpu - h_ref)
-    bound = 2.0 ** -8 * np.abs(h_ref) + 1e-3 * np.linalg.norm(h_ref, axis=1, keepdims=True)
-    assert np.all(err <= bound), f"h outside tolerance: worst {np.max(err / bound):.3f}"
-    # requantization of the GPU's h: bit-exact
-    qc, qs = oracle.quantize_e8m0_b32(h_gpu.astype(np.float32))
-    assert np.array_equal(to_np(hc)[pairs], qc) and np.array_equal(to_np(hs)[pairs], qs)
-    # down + combine from the GPU's quantized h
-    d_c, d_s = _w_codes_np(Wd)
-    y_ref = oracle.moe_down_combine(to_np(hc), to_np(hs), "e8m0_b32", ref_route, d_c, d_s, tokens=tokens)
-    sel = np.arange(T) if tokens is None else np.asarray(tokens)
-    assert_rows_close(to_np(y)[sel], y_ref, what="moe down (atomic)")
-    assert_rows_close(to_np(yd)[sel], y_ref, what="moe down (deterministic)")
+        qc, qs, qts = oracle_q(h_ref_bits)
+        if e4:
+            assert to_np(hq.tensor_scale)[0] == qts
+        _check_requant(u16(hb)[pairs], h_ref_bits, to_np(hq.codes)[pairs], to_np(hq.scales)[pairs], qc, qs, bs)
+        # the sampled tokens' pairs, requantized by the oracle from its own h
+        tp = np.sort(ref_route["pair_pos"][tokens].reshape(-1))
+        _, _, hb_t = oracle_h(tp)
+        qc_t, qs_t, hts = oracle_q(hb_t)
+        full_c = np.zeros((P, I // 2), np.uint8)
+        full_s = np.zeros((P, I // bs), np.uint8)
+        full_c[tp], full_s[tp] = qc_t, qs_t
+        row_same = np.zeros(P, bool)
+        row_same[tp] = (to_np(hq.codes)[tp] == qc_t).all(axis=1) & (to_np(hq.scales)[tp] == qs_t).all(axis=1)
+
+    # down + combine, the oracle from its own quantized h
+    y_ref = oracle.moe_down_combine(full_c, full_s, fmt, ref_route, pb.ref_d[0], pb.ref_d[1], hts,
+                                    pb.ref_d[2] if e4 else None, tokens=tokens)
+    clean = np.array([row_same[ref_route["pair_pos"][t]].all() for t in tokens])
+    for name, yy in (("atomic", y), ("deterministic", yd)):
+        yv = to_np(yy)[tokens]
+        if clean.any():
+            assert_rows_close(yv[clean], y_ref[clean], what=f"moe down ({name})")
+        if (~clean).any():
+            assert_rows_close(yv[~clean], y_ref[~clean], tol=2e-2, what=f"moe down ({name}, explained code flips)")
+    assert clean.mean() >= 0.5, f"only {clean.mean():.1%} of sampled tokens requantized identically"
+    print(f"[stats] clean tokens {clean.mean():.1%} of {len(tokens)}", flush=True)
+
+
+def _mx_problem(T, H, I, E, k, seed=1):
+    d = synth.moe_problem(T, H, I, E, seed=seed, device=DEV)
+    return _Problem("e8m0_b32", d["x"], d["logits"], k, dict(w=d["w_gate_up"]), dict(w=d["w_down"]), I)
 
 
 @pytest.mark.parametrize("T,H,I,E,k", [(300, 512, 256, 8, 2), (97, 256, 128, 5, 3), (64, 1024, 384, 16, 8)])
 def test_moe_mxfp4_small(T, H, I, E, k):
     banner(f"moe mxfp4 T={T} H={H} I={I} E={E} k={k}")
-    d = synth.moe_problem(T, H, I, E, seed=1, device=DEV)
-    Wgu = _mx_weights(d["w_gate_up"])
-    Wd = _mx_weights(d["w_down"])
-    _run_and_check(d["x"], d["logits"], k, Wgu, Wd)
+    _run_and_check(_mx_problem(T, H, I, E, k))
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [(300, 512, 256, 8, 2), (97, 256, 128, 5, 3), (64, 1024, 384, 16, 8)])
+def test_moe_e4m3_small(T, H, I, E, k):
+    banner(f"moe e4m3 T={T} H={H} I={I} E={E} k={k}")
+    d = synth.moe_problem(T, H, I, E, seed=3, device=DEV)
+    pb = _Problem("e4m3_b16", d["x"], d["logits"], k, dict(w=d["w_gate_up"]), dict(w=d["w_down"]), I)
+    _run_and_check(pb)
+    _run_and_check(pb, h_amax=1.5)
 
 
 @pytest.mark.parametrize("T,H,I,E,k", [(300, 512, 256, 8, 2), (513, 256, 384, 3, 2)])
 def test_moe_vq_small(T, H, I, E, k):
     banner(f"moe vq T={T} H={H} I={I} E={E} k={k}")
     d = synth.moe_vq_problem(T, H, I, E, seed=2, device="cpu")
-    Wgu = _vq_weights(d["gate_up"], 2 * I, H)
-    Wd = _vq_weights(d["down"], H, I)
-    _run_and_check(d["x"].to(DEV), d["logits"].to(DEV), k, Wgu, Wd)
+    _run_and_check(_Problem("vq", d["x"].to(DEV), d["logits"].to(DEV), k, d["gate_up"], d["down"], I))
 
 
 def test_moe_vq_full_size_sampled():
-    """The measured shape: T=8192, H=4096, I=1536, 128 experts, top-8; gate/up
-    checked on every pair of two experts, y on a sample of tokens."""
+    """The measured prefill shape: T=8192, H=4096, I=1536, 128 experts,
+    top-8; gate/up checked on every pair of two experts, y on sampled tokens."""
     banner("moe vq full T=8192 H=4096 I=1536 E=128 k=8")
     d = synth.moe_vq_problem(8192, 4096, 1536, 128, seed=0, device=DEV)
-    Wgu = _vq_weights(d["gate_up"], 3072, 4096)
-    Wd = _vq_weights(d["down"], 4096, 1536)
-    _run_and_check(d["x"], d["logits"], 8, Wgu, Wd, tokens=[0, 4097, 8191], experts=[0, 77])
+    _run_and_check(_Problem("vq", d["x"], d["logits"], 8, d["gate_up"], d["down"], 1536),
+                   tokens=[0, 4097, 8191], experts=[0, 77])
+
+
+def test_moe_e4m3_full_size_sampled():
+    """The E4M3-B16 shape: T=4096, H=2048, I=768, 128 experts, top-8."""
+    banner("moe e4m3 full T=4096 H=2048 I=768 E=128 k=8")
+    d = synth.moe_problem(4096, 2048, 768, 128, seed=0, device=DEV)
+    _run_and_check(_Problem("e4m3_b16", d["x"], d["logits"], 8, dict(w=d["w_gate_up"]), dict(w=d["w_down"]), 768),
+                   tokens=[1, 2048, 4095], experts=[3, 100], h_amax=2.0)
