@@ -175,9 +175,10 @@ class _Problem:
             for half in range(2):
                 rows = slice(half * I, (half + 1) * I)
                 out = gbw.Act(gbw.FMT_E4M3_B16, gc[e, rows], gs[e, rows])
-                gbw.mx_quantize(wgu[e, rows].contiguous(), gbw.FMT_E4M3_B16, out=out, tensor_scale=gt[e, half:half + 1])
+                gbw.mx_quantize(wgu[e, rows].contiguous(), gbw.FMT_E4M3_B16, out=out, tensor_scale=gt[e, half:half + 1],
+                                dynamic=True)
             out = gbw.Act(gbw.FMT_E4M3_B16, dc[e], ds[e])
-            gbw.mx_quantize(wd[e].contiguous(), gbw.FMT_E4M3_B16, out=out, tensor_scale=dt[e])
+            gbw.mx_quantize(wd[e].contiguous(), gbw.FMT_E4M3_B16, out=out, tensor_scale=dt[e], dynamic=True)
         self.Wgu = gbw.Weight(gbw.FMT_E4M3_B16, 2 * I, H, gc, gs, None, gt, 2, E)
         self.Wd = gbw.Weight(gbw.FMT_E4M3_B16, H, I, dc, ds, None, dt, 1, E)
         cache = {}
