@@ -35,6 +35,7 @@ DTYPE_BF16 = 0
 DTYPE_F32 = 1
 TS_DYNAMIC = 1
 DETERMINISTIC = 2
+FP32_COMBINE = 4
 MOE_GATEUP_SWIGLU = 0
 MOE_DOWN_COMBINE = 1
 OP_QUANTIZE = 0
@@ -309,15 +310,19 @@ def moe_grouped_gemm(stage, route, a: Act, w: Weight, h_bf16=None, h_codes=None,
     """One stage of the routed expert FFN (see include/gbw.h).
 
     GATEUP: fills h_bf16 [P][I] and/or h_codes [P][I/2] + h_scales [P][I/32].
-    DOWN:   overwrites y [T][H].  flags=DETERMINISTIC uses a pair buffer in the
-            workspace and a fixed-order combine instead of fp32 atomics.
+    DOWN:   overwrites y [T][H] through a bf16 (flags=FP32_COMBINE: fp32)
+            slot buffer in the workspace and a fixed-order combine; ws=False
+            adds into y with fp32 atomics instead (no workspace).
     """
     T, topk = route["topk_ids"].shape
     P = T * topk
     need = 0
-    if stage == MOE_DOWN_COMBINE and (flags & DETERMINISTIC):
-        need = workspace_size(OP_MOE_GEMM, P, w.N, 0, w.fmt)
-    ws, wsb = _ws(ws, need, a.codes.device)
+    if stage == MOE_DOWN_COMBINE and ws is not False:
+        need = workspace_size(OP_MOE_GEMM, P, w.N, 1 if flags & FP32_COMBINE else 0)
+    if ws is False:
+        ws, wsb = None, 0
+    else:
+        ws, wsb = _ws(ws, need, a.codes.device)
     o = _MoeOut(h_bf16.data_ptr() if h_bf16 is not None else None,
                 h_codes.data_ptr() if h_codes is not None else None,
                 h_scales.data_ptr() if h_scales is not None else None,

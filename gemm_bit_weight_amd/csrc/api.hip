@@ -98,7 +98,7 @@ int launch_fill_zero(float* p, int64_t n, hipStream_t st) {
 namespace gbw {
 size_t ws_quantize(int64_t rows, int64_t K, int32_t fmt);
 size_t ws_moe_route(int64_t T, int64_t E);
-size_t ws_moe_gemm(int64_t P, int64_t N, int32_t fmt);
+size_t ws_moe_gemm(int64_t P, int64_t N, int64_t f32);
 size_t ws_lut_gemm(int64_t M, int64_t N, int64_t K);
 size_t ws_mx_gemm(int64_t M, int64_t N, int64_t Ktot);
 }  // namespace gbw
@@ -126,7 +126,7 @@ size_t gbw_workspace_size(int32_t op, int64_t d0, int64_t d1, int64_t d2, int32_
     case GBW_OP_MX_GEMM: return gbw::ws_mx_gemm(d0, d1, d2);
     case GBW_OP_LUT_GEMM: return gbw::ws_lut_gemm(d0, d1, d2);
     case GBW_OP_MOE_ROUTE: return gbw::ws_moe_route(d0, d1);
-    case GBW_OP_MOE_GEMM: return gbw::ws_moe_gemm(d0, d1, fmt);
+    case GBW_OP_MOE_GEMM: return gbw::ws_moe_gemm(d0, d1, d2);
     default: return 0;
   }
 }

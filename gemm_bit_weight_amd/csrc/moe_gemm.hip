@@ -17,8 +17,7 @@
 //    the E8M0 prescales are the operand's block scales.  No wider copy of the
 //    weights exists anywhere, in HBM or on chip.
 //
-// Work decomposition: one workgroup (4 waves, 2 x 2) per 256 x 256 output
-// tile of one expert: 256 pairs (rows) x 256 weight rows.  The tile list is
+// Work decomposition: one workgroup per 256 x 256 output tile of one expert: 256 pairs (rows) x 256 weight rows.  The tile list is
 // expert-major (m tiles, then n tiles) and is recovered by every workgroup
 // from expert_offsets with a block scan; consecutive logical tiles are placed
 // on the same XCD so the experts an XCD works on stay in its L2.  K advances
@@ -66,7 +65,8 @@ struct MoeArgs {
   uint8_t* h_codes;        // GATEUP: [P][I/2] or null
   uint8_t* h_scales;       // GATEUP: [P][I/32] or null
   float* y;                // DOWN: [T][H]
-  float* pairbuf;          // DOWN deterministic: [P][H] or null
+  void* slots;             // DOWN: [T][topk][H] bf16 or fp32 per-pair outputs, or null (atomics into y)
+  int32_t slots_f32;       // 1: fp32 slots, 0: bf16 slots
 };
 
 struct TileInfo {
@@ -80,14 +80,15 @@ __device__ bool find_tile(const MoeArgs& p, TileInfo& ti, int* scan) {
   const int per = (G + 7) / 8;
   const int L = (blockIdx.x % 8) * per + blockIdx.x / 8;
   const int tid = threadIdx.x;
+  const bool mine = tid < kMoeThreads;  // the first 256 threads own the scan
   int cnt = 0;
   if (tid < p.E) cnt = (p.off[tid + 1] - p.off[tid] + kMoeBM - 1) / kMoeBM;
-  scan[tid] = cnt;
+  if (mine) scan[tid] = cnt;
   __syncthreads();
   for (int o = 1; o < kMoeThreads; o <<= 1) {
-    const int add = tid >= o ? scan[tid - o] : 0;
+    const int add = (mine && tid >= o) ? scan[tid - o] : 0;
     __syncthreads();
-    scan[tid] += add;
+    if (mine) scan[tid] += add;
     __syncthreads();
   }
   // scan[e] = m tiles of experts 0..e (inclusive)
@@ -106,6 +107,22 @@ __device__ bool find_tile(const MoeArgs& p, TileInfo& ti, int* scan) {
   ti.row0 = p.off[ti.e] + ti.mt * kMoeBM;
   ti.rows = min(kMoeBM, p.off[ti.e + 1] - ti.row0);
   return true;
+}
+
+// One pair's output element: into its token's slot of the slot buffer (the
+// combine kernel weights and sums the slots), or, without a slot buffer,
+// weighted straight into y with an fp32 atomic.
+__device__ __forceinline__ void store_pair_out(const MoeArgs& p, int tok, int slot, float w, int64_t n, float v) {
+  const int64_t H = p.N;
+  if (p.slots) {
+    const int64_t i = ((int64_t)tok * p.topk + slot) * H + n;
+    if (p.slots_f32)
+      reinterpret_cast<float*>(p.slots)[i] = v;
+    else
+      reinterpret_cast<uint16_t*>(p.slots)[i] = (uint16_t)f32_to_bf16_rne(v);
+  } else {
+    unsafeAtomicAdd(p.y + (int64_t)tok * H + n, w * v);
+  }
 }
 
 __device__ __forceinline__ v8i widen8(v4i x) {
@@ -131,8 +148,17 @@ __device__ __forceinline__ int64_t b_row(const MoeArgs& p, int nt, int j) {
   return (int64_t)nt * kMoeBN + j;
 }
 
+// 512 threads = 8 waves as 4 (rows) x 2 (columns); a wave owns a 64 x 128
+// block of the tile as 2 x 4 accumulators of v_mfma_scale_f32_32x32x64_f8f6f4
+// (on gfx950 the 32x32x64 shape runs at the full FP4 rate; 16x16x128 runs at
+// the FP8 rate).  Lane l of a 32x32x64 operand holds row l % 32 and the 32 K
+// elements of block l / 32 (one E8M0 block, 16 bytes); the fp32 result holds
+// column l % 32 and rows 8*(r/4) + 4*(l/32) + r%4 in register r.  Two waves
+// per SIMD let one wave's LDS reads and barriers overlap the other's MFMAs.
+constexpr int kFp4Threads = 512;
+
 template <int WF>
-__global__ __launch_bounds__(kMoeThreads) void k_moe_fp4(const MoeArgs p) {
+__global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][kMoeBM * kRowB];
   __shared__ __attribute__((aligned(16))) uint8_t sB[2][kMoeBN * kRowB];
   __shared__ uint32_t sAs[2][kMoeBM];
@@ -141,135 +167,134 @@ __global__ __launch_bounds__(kMoeThreads) void k_moe_fp4(const MoeArgs p) {
   __shared__ int scan[kMoeThreads];
   __shared__ int s_tok[kMoeBM];
   __shared__ float s_w[kMoeBM];
+  __shared__ int s_slot[kMoeBM];
 
   TileInfo ti;
   if (!find_tile(p, ti, scan)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int r16 = lane & 15, g4 = lane >> 4;
+  const int l32 = lane & 31, g2 = lane >> 5;
   const int64_t K = p.K;
   const int steps = (int)(K / 128);
 
   // per-row metadata: token (gather / combine) and routing weight
-  for (int r = tid; r < kMoeBM; r += kMoeThreads) {
-    int tok = 0;
+  for (int r = tid; r < kMoeBM; r += kFp4Threads) {
+    int tok = 0, slot = 0;
     float wt = 0.f;
     if (r < ti.rows) {
       const int pr = ti.row0 + r;
       tok = p.pair_token[pr];
       if (p.stage == GBW_MOE_DOWN_COMBINE)
         for (int j = 0; j < p.topk; ++j)
-          if (p.pair_pos[(int64_t)tok * p.topk + j] == pr) wt = p.topk_w[(int64_t)tok * p.topk + j];
+          if (p.pair_pos[(int64_t)tok * p.topk + j] == pr) {
+            wt = p.topk_w[(int64_t)tok * p.topk + j];
+            slot = j;
+          }
     }
     s_tok[r] = tok;
     s_w[r] = wt;
+    s_slot[r] = slot;
   }
   __syncthreads();
 
   // --- fixed per-thread load assignments --------------------------------
-  // A: rows ar + 64u (u = 0..3), 16-byte chunk ac of the 64-byte stage row
+  // A codes: rows ar and ar + 128, 16-byte chunk ac of the 64-byte stage row;
+  // threads 0..255 load the scale dword of A row tid, 256..511 of B row tid-256
   const int ar = tid >> 2, ac = tid & 3;
-  const uint8_t* arow[4];
+  const uint8_t* arow[2];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = ar + 64 * u;
-    const int rr = r < ti.rows ? r : (ti.rows > 0 ? ti.rows - 1 : 0);
+  for (int u = 0; u < 2; ++u) {
+    const int r = ar + 128 * u;
+    const int rr = r < ti.rows ? r : ti.rows - 1;
     const int64_t src = p.stage == GBW_MOE_GATEUP_SWIGLU ? (int64_t)s_tok[rr] : (int64_t)(ti.row0 + rr);
     arow[u] = p.a_codes + src * (K / 2);
   }
-  const int64_t a_srow = p.stage == GBW_MOE_GATEUP_SWIGLU ? (int64_t)s_tok[tid < ti.rows ? tid : 0]
-                                                          : (int64_t)(ti.row0 + (tid < ti.rows ? tid : 0));
-  const uint8_t* a_scl = p.a_scales + a_srow * (K / 32);
-  // weights of expert e
+  const int sr = tid & 255;
+  const uint8_t* scl;
+  if (tid < 256) {
+    const int rr = sr < ti.rows ? sr : ti.rows - 1;
+    const int64_t src = p.stage == GBW_MOE_GATEUP_SWIGLU ? (int64_t)s_tok[rr] : (int64_t)(ti.row0 + rr);
+    scl = p.a_scales + src * (K / 32);
+  } else {
+    scl = p.w_scales + ((int64_t)ti.e * p.N + b_row(p, ti.nt, sr)) * (K / 32);
+  }
   const int64_t wN = p.N;
-  const uint8_t* wsc = p.w_scales + (int64_t)ti.e * wN * (K / 32) + b_row(p, ti.nt, tid) * (K / 32);
-  const uint8_t* wrow[4];
-  const uint8_t* vrow[2];
+  const uint8_t* wrow[2];
+  const uint8_t* vrow = nullptr;
   const uint16_t* cbase = nullptr;
-  int lut_bn = 0, lut_kb = 0;
+  int lut_kb = 0;
   if (WF == W_MX) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      wrow[u] = p.w_codes + (int64_t)ti.e * wN * (K / 2) + b_row(p, ti.nt, ar + 64 * u) * (K / 2);
+    for (int u = 0; u < 2; ++u)
+      wrow[u] = p.w_codes + ((int64_t)ti.e * wN + b_row(p, ti.nt, ar + 128 * u)) * (K / 2);
   } else {
-    // idx: rows (tid >> 1) + 128 v (v = 0, 1), 16-byte chunk (tid & 1) of the 32-byte stage row
-#pragma unroll
-    for (int v = 0; v < 2; ++v)
-      vrow[v] = p.w_codes + (int64_t)ti.e * wN * (K / 4) + b_row(p, ti.nt, (tid >> 1) + 128 * v) * (K / 4);
-    // LUT: thread tid loads 16 bytes of table (tid >> 5) (8 tables: 4 QBlock rows x 2 QBlock columns)
-    const int tb = tid >> 5;
-    lut_bn = tb >> 1;  // QBlock row within the tile (64 B rows each)
-    lut_kb = tb & 1;   // QBlock column within the stage
-    const int64_t qrow = b_row(p, ti.nt, lut_bn * 64) / 64;
+    // idx: row tid >> 1, 16-byte chunk tid & 1 of the 32-byte stage row
+    vrow = p.w_codes + ((int64_t)ti.e * wN + b_row(p, ti.nt, tid >> 1)) * (K / 4);
+    // LUT (threads 0..255): 16 bytes of table tid >> 5 (4 QBlock rows x 2 QBlock columns)
+    const int tb = (tid & 255) >> 5;
+    lut_kb = tb & 1;
+    const int64_t qrow = b_row(p, ti.nt, (tb >> 1) * 64) / 64;
     cbase = p.w_cb + ((int64_t)ti.e * (wN / 64) + qrow) * (K / 64) * 256;
   }
 
-  // prefetch registers
-  v4i pa[4], pb[4];
-  uint32_t pas, pbs;
+  v4i pa[2], pb[2];
+  uint32_t psc;
   v4i pl;
   auto gload = [&](int s) {
-    const int64_t kb = (int64_t)s * 64;  // byte offset of the stage in a row of codes
+    const int64_t kb = (int64_t)s * 64;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) pa[u] = load16(arow[u] + kb + 16 * ac);
-    pas = *reinterpret_cast<const uint32_t*>(a_scl + (int64_t)s * 4);
-    pbs = *reinterpret_cast<const uint32_t*>(wsc + (int64_t)s * 4);
+    for (int u = 0; u < 2; ++u) pa[u] = load16(arow[u] + kb + 16 * ac);
+    psc = *reinterpret_cast<const uint32_t*>(scl + (int64_t)s * 4);
     if (WF == W_MX) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) pb[u] = load16(wrow[u] + kb + 16 * ac);
+      for (int u = 0; u < 2; ++u) pb[u] = load16(wrow[u] + kb + 16 * ac);
     } else {
-#pragma unroll
-      for (int v = 0; v < 2; ++v) pb[v] = load16(vrow[v] + (int64_t)s * 32 + 16 * (tid & 1));
-      const int64_t kq = (int64_t)s * 2 + lut_kb;  // QBlock column
-      pl = load16(cbase + kq * 256 + (tid & 31) * 8);
+      pb[0] = load16(vrow + (int64_t)s * 32 + 16 * (tid & 1));
+      if (tid < 256) pl = load16(cbase + ((int64_t)s * 2 + lut_kb) * 256 + (tid & 31) * 8);
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) *reinterpret_cast<v4i*>(&sA[buf][(ar + 64 * u) * kRowB + 16 * ac]) = pa[u];
-    sAs[buf][tid] = pas;
-    sBs[buf][tid] = pbs;
+    for (int u = 0; u < 2; ++u) *reinterpret_cast<v4i*>(&sA[buf][(ar + 128 * u) * kRowB + 16 * ac]) = pa[u];
+    if (tid < 256)
+      sAs[buf][sr] = psc;
+    else
+      sBs[buf][sr] = psc;
     if (WF == W_MX) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) *reinterpret_cast<v4i*>(&sB[buf][(ar + 64 * u) * kRowB + 16 * ac]) = pb[u];
-    } else {
+      for (int u = 0; u < 2; ++u) *reinterpret_cast<v4i*>(&sB[buf][(ar + 128 * u) * kRowB + 16 * ac]) = pb[u];
+    } else if (tid < 256) {
       *reinterpret_cast<v4i*>(&sLut[(tid >> 5) * 256 + (tid & 31) * 8]) = pl;
     }
   };
-  // VQ: expand the 32 indices this thread holds into 64 bytes of E2M1 codes
+  // VQ: expand this thread's 16 indices into 32 bytes of E2M1 codes
   auto vq_expand = [&](int buf) {
+    const int row = tid >> 1, half = tid & 1;  // half = 64-element half of the stage = QBlock column
+    const uint16_t* lut = &sLut[(((row >> 6) << 1) + half) * 256];
+    uint32_t o[8];
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      const int row = (tid >> 1) + 128 * v;
-      const int half = tid & 1;                      // which 64-element half of the stage (QBlock column)
-      const uint16_t* lut = &sLut[(((row >> 6) << 1) + half) * 256];
-      uint32_t outw[8];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t w = (uint32_t)pb[v][d];
-        const uint32_t k0 = lut[w & 0xFF], k1 = lut[(w >> 8) & 0xFF];
-        const uint32_t k2 = lut[(w >> 16) & 0xFF], k3 = lut[w >> 24];
-        outw[2 * d] = k0 | (k1 << 16);
-        outw[2 * d + 1] = k2 | (k3 << 16);
-      }
-      uint8_t* dst = &sB[buf][row * kRowB + 32 * half];
-      *reinterpret_cast<v4i*>(dst) = v4i{(int)outw[0], (int)outw[1], (int)outw[2], (int)outw[3]};
-      *reinterpret_cast<v4i*>(dst + 16) = v4i{(int)outw[4], (int)outw[5], (int)outw[6], (int)outw[7]};
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t w = (uint32_t)pb[0][d];
+      o[2 * d] = (uint32_t)lut[w & 0xFF] | ((uint32_t)lut[(w >> 8) & 0xFF] << 16);
+      o[2 * d + 1] = (uint32_t)lut[(w >> 16) & 0xFF] | ((uint32_t)lut[w >> 24] << 16);
     }
+    uint8_t* dst = &sB[buf][row * kRowB + 32 * half];
+    *reinterpret_cast<v4i*>(dst) = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+    *reinterpret_cast<v4i*>(dst + 16) = v4i{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
   };
 
-  v4f acc[8][8];
+  v16f acc[2][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
-  // B-tile rows of this wave's 8 column subtiles
-  int brow[8];
+  // B-tile rows of this wave's four 32-column subtiles
+  int brow[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    brow[j] = p.stage == GBW_MOE_GATEUP_SWIGLU ? (j < 4 ? 64 * wn + 16 * j : 128 + 64 * wn + 16 * (j - 4))
-                                               : 128 * wn + 16 * j;
+  for (int j = 0; j < 4; ++j)
+    brow[j] = p.stage == GBW_MOE_GATEUP_SWIGLU ? (j < 2 ? 64 * wn + 32 * j : 128 + 64 * wn + 32 * (j - 2))
+                                               : 128 * wn + 32 * j;
 
   gload(0);
   lstore(0);
@@ -282,24 +307,26 @@ __global__ __launch_bounds__(kMoeThreads) void k_moe_fp4(const MoeArgs p) {
   for (int s = 0; s < steps; ++s) {
     const int buf = s & 1;
     if (s + 1 < steps) gload(s + 1);
-    // 64 MFMAs of this stage
-    v4i bf[8];
-    int bsc[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = brow[j] + r16;
-      bf[j] = *reinterpret_cast<const v4i*>(&sB[buf][row * kRowB + 16 * g4]);
-      bsc[j] = (int)((sBs[buf][row] >> (8 * g4)) & 0xFFu);
-    }
+    for (int t = 0; t < 2; ++t) {  // two 64-element MFMA steps per 128-element stage
+      v4i bf[4];
+      int bsc[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = 128 * wm + 16 * i + r16;
-      const v4i af = *reinterpret_cast<const v4i*>(&sA[buf][row * kRowB + 16 * g4]);
-      const int asc = (int)((sAs[buf][row] >> (8 * g4)) & 0xFFu);
+      for (int j = 0; j < 4; ++j) {
+        const int row = brow[j] + l32;
+        bf[j] = *reinterpret_cast<const v4i*>(&sB[buf][row * kRowB + 32 * t + 16 * g2]);
+        bsc[j] = (int)((sBs[buf][row] >> (8 * (2 * t + g2))) & 0xFFu);
+      }
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(widen8(af), widen8(bf[j]), acc[i][j], 4, 4, 0,
-                                                                      asc, 0, bsc[j]);
+      for (int i = 0; i < 2; ++i) {
+        const int row = 64 * wm + 32 * i + l32;
+        const v4i af = *reinterpret_cast<const v4i*>(&sA[buf][row * kRowB + 32 * t + 16 * g2]);
+        const int asc = (int)((sAs[buf][row] >> (8 * (2 * t + g2))) & 0xFFu);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen8(af), widen8(bf[j]), acc[i][j], 4, 4, 0,
+                                                                       asc, 0, bsc[j]);
+      }
     }
     if (s + 1 < steps) {
       lstore(buf ^ 1);
@@ -312,94 +339,66 @@ __global__ __launch_bounds__(kMoeThreads) void k_moe_fp4(const MoeArgs p) {
   }
 
   // ---------------------------------------------------------------------
-  // epilogues
+  // epilogues; acc[i][j][r] is row 64*wm + 32*i + 8*(r/4) + 4*g2 + r%4 of the
+  // tile and column brow[j] + l32 of the B tile
   // ---------------------------------------------------------------------
   if (p.stage == GBW_MOE_DOWN_COMBINE) {
-    const int64_t H = p.N;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 128 * wm + 16 * i + 4 * g4 + r;
+      for (int r = 0; r < 16; ++r) {
+        const int m = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * g2 + (r & 3);
         if (m >= ti.rows) continue;
-        const float wt = s_w[m];
-        float* dst = p.pairbuf ? p.pairbuf + (int64_t)(ti.row0 + m) * H : p.y + (int64_t)s_tok[m] * H;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int64_t n = (int64_t)ti.nt * kMoeBN + 128 * wn + 16 * j + r16;
-          const float v = wt * acc[i][j][r];
-          if (p.pairbuf)
-            dst[n] = v;
-          else
-            unsafeAtomicAdd(dst + n, v);
-        }
+        for (int j = 0; j < 4; ++j)
+          store_pair_out(p, s_tok[m], s_slot[m], s_w[m], (int64_t)ti.nt * kMoeBN + brow[j] + l32, acc[i][j][r]);
       }
     return;
   }
 
-  // GATEUP: h = bf16(silu(g) * u), then E8M0-B32 requantization of h.
-  // Wave columns: intermediate index i = nt*128 + 64*wn + 16*jj + r16, jj = 0..3
-  // (g in acc[.][jj], u in acc[.][jj+4]); E8M0 block b covers jj = 2b, 2b+1.
-  __syncthreads();  // LDS operand buffers are reused for the code tile
-  uint8_t* sH = &sA[0][0];           // [256 rows][64 bytes of codes]
-  uint8_t* sHs = &sB[0][0];          // [256 rows][4 scales]
+  // GATEUP: h = bf16(silu(g) * u) for intermediate column 64*wn + 32*jj + l32
+  // of the tile (g in acc[.][jj], u in acc[.][jj+2]); the 32 columns of a
+  // subtile form one E8M0 block, so its amax is a max over the 32 lanes.
+  __syncthreads();  // operand buffers are reused for the code tile
+  uint8_t* sH = &sA[0][0];   // [256 rows][64 bytes of codes]
+  uint8_t* sHs = &sB[0][0];  // [256 rows][4 scales]
   const int64_t I = p.N / 2;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 128 * wm + 16 * i + 4 * g4 + r;
+    for (int r = 0; r < 16; ++r) {
+      const int m = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * g2 + (r & 3);
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        float hv[2];
-        uint32_t hb[2];
+      for (int jj = 0; jj < 2; ++jj) {
+        const float gv = acc[i][jj][r], uv = acc[i][jj + 2][r];
+        const uint32_t hb = f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv);
+        const float hv = bf16_to_f32(hb);
+        const int col = 64 * wn + 32 * jj + l32;  // within the tile's 128 columns
+        if (p.h_bf16 && m < ti.rows) p.h_bf16[(int64_t)(ti.row0 + m) * I + (int64_t)ti.nt * 128 + col] = (uint16_t)hb;
+        uint32_t am = __float_as_uint(hv) & 0x7FFFFFFFu;
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const int jj = 2 * b + t2;
-          const float gv = acc[i][jj][r], uv = acc[i][jj + 4][r];
-          const float sg = gv / (1.0f + expf(-gv));
-          hb[t2] = f32_to_bf16_rne(sg * uv);
-          hv[t2] = bf16_to_f32(hb[t2]);
-        }
-        if (p.h_bf16 && m < ti.rows) {
-          const int64_t col = (int64_t)ti.nt * 128 + 64 * wn + 32 * b + r16;
-          p.h_bf16[(int64_t)(ti.row0 + m) * I + col] = (uint16_t)hb[0];
-          p.h_bf16[(int64_t)(ti.row0 + m) * I + col + 16] = (uint16_t)hb[1];
-        }
-        // block amax over the 32 columns held by the 16 lanes of this row
-        uint32_t am = max(__float_as_uint(hv[0]) & 0x7FFFFFFFu, __float_as_uint(hv[1]) & 0x7FFFFFFFu);
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) am = max(am, (uint32_t)__shfl_xor((int)am, o));
+        for (int o = 1; o < 32; o <<= 1) am = max(am, (uint32_t)__shfl_xor((int)am, o));
         const uint32_t sc = e8m0_scale_code(__uint_as_float(am));
-        const float inv = e8m0_inv(sc);
-        const uint32_t c0 = e2m1_rne(fabsf(hv[0]) * inv) | ((__float_as_uint(hv[0]) >> 28) & 8u);
-        const uint32_t c1 = e2m1_rne(fabsf(hv[1]) * inv) | ((__float_as_uint(hv[1]) >> 28) & 8u);
-        // columns 2k, 2k+1 sit in lanes 2k, 2k+1: pair them into bytes
-        const uint32_t o0 = (uint32_t)__shfl_xor((int)c0, 1), o1 = (uint32_t)__shfl_xor((int)c1, 1);
-        const int cb = 64 * wn + 32 * b;  // first column of the block within the tile's 128
-        if ((r16 & 1) == 0) {
-          sH[m * 64 + (cb + r16) / 2] = (uint8_t)(c0 | (o0 << 4));
-          sH[m * 64 + (cb + 16 + r16) / 2] = (uint8_t)(c1 | (o1 << 4));
-        }
-        if (r16 == 0) sHs[m * 4 + cb / 32] = (uint8_t)sc;
+        const uint32_t c = e2m1_rne(fabsf(hv) * e8m0_inv(sc)) | ((__float_as_uint(hv) >> 28) & 8u);
+        const uint32_t partner = (uint32_t)__shfl_xor((int)c, 1);
+        if ((l32 & 1) == 0) sH[m * 64 + col / 2] = (uint8_t)(c | (partner << 4));
+        if (l32 == 0) sHs[m * 4 + col / 32] = (uint8_t)sc;
       }
     }
   __syncthreads();
   if (p.h_codes) {
-    // 256 rows x 64 bytes: 4 chunks of 16 bytes per row
-    for (int c = tid; c < kMoeBM * 4; c += kMoeThreads) {
+    for (int c = tid; c < kMoeBM * 4; c += kFp4Threads) {
       const int m = c >> 2, q = c & 3;
       if (m < ti.rows)
         *reinterpret_cast<v4i*>(p.h_codes + (int64_t)(ti.row0 + m) * (I / 2) + (int64_t)ti.nt * 64 + 16 * q) =
             *reinterpret_cast<const v4i*>(&sH[m * 64 + 16 * q]);
     }
-    for (int m = tid; m < kMoeBM; m += kMoeThreads)
+    for (int m = tid; m < kMoeBM; m += kFp4Threads)
       if (m < ti.rows)
         *reinterpret_cast<uint32_t*>(p.h_scales + (int64_t)(ti.row0 + m) * (I / 32) + (int64_t)ti.nt * 4) =
             *reinterpret_cast<const uint32_t*>(&sHs[m * 4]);
   }
 }
-
 
 // ---------------------------------------------------------------------------
 // E4M3-B16 experts: exact decode to fp16, fp16 MFMA
@@ -465,6 +464,7 @@ __global__ __launch_bounds__(kMoeThreads) void k_moe_e4m3(const MoeArgs p) {
   __shared__ int scan[kMoeThreads];
   __shared__ int s_tok[kMoeBM];
   __shared__ float s_w[kMoeBM];
+  __shared__ int s_slot[kMoeBM];
 
   TileInfo ti;
   if (!find_tile(p, ti, scan)) return;
@@ -475,17 +475,21 @@ __global__ __launch_bounds__(kMoeThreads) void k_moe_e4m3(const MoeArgs p) {
   const int steps = (int)(K / 64);
 
   for (int r = tid; r < kMoeBM; r += kMoeThreads) {
-    int tok = 0;
+    int tok = 0, slot = 0;
     float wt = 0.f;
     if (r < ti.rows) {
       const int pr = ti.row0 + r;
       tok = p.pair_token[pr];
       if (p.stage == GBW_MOE_DOWN_COMBINE)
         for (int j = 0; j < p.topk; ++j)
-          if (p.pair_pos[(int64_t)tok * p.topk + j] == pr) wt = p.topk_w[(int64_t)tok * p.topk + j];
+          if (p.pair_pos[(int64_t)tok * p.topk + j] == pr) {
+            wt = p.topk_w[(int64_t)tok * p.topk + j];
+            slot = j;
+          }
     }
     s_tok[r] = tok;
     s_w[r] = wt;
+    s_slot[r] = slot;
   }
   __syncthreads();
 
@@ -564,7 +568,6 @@ __global__ __launch_bounds__(kMoeThreads) void k_moe_e4m3(const MoeArgs p) {
 
   const float sa = p.a_ts[0];
   if (p.stage == GBW_MOE_DOWN_COMBINE) {
-    const int64_t H = p.N;
     const float sw = sa * p.w_ts[(int64_t)ti.e * p.ts_per];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -572,17 +575,10 @@ __global__ __launch_bounds__(kMoeThreads) void k_moe_e4m3(const MoeArgs p) {
       for (int r = 0; r < 4; ++r) {
         const int m = 128 * wm + 16 * i + 4 * g4 + r;
         if (m >= ti.rows) continue;
-        const float wt = s_w[m] * sw;
-        float* dst = p.pairbuf ? p.pairbuf + (int64_t)(ti.row0 + m) * H : p.y + (int64_t)s_tok[m] * H;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int64_t n = (int64_t)ti.nt * kMoeBN + 128 * wn + 16 * j + r16;
-          const float v = wt * acc[i][j][r];
-          if (p.pairbuf)
-            dst[n] = v;
-          else
-            unsafeAtomicAdd(dst + n, v);
-        }
+        for (int j = 0; j < 8; ++j)
+          store_pair_out(p, s_tok[m], s_slot[m], s_w[m], (int64_t)ti.nt * kMoeBN + 128 * wn + 16 * j + r16,
+                         sw * acc[i][j][r]);
       }
     return;
   }
@@ -622,25 +618,46 @@ int launch_moe_bf16(const MoeArgs& p, const gbw_act* a, const gbw_weight* w, int
   return check_launch("moe_grouped_gemm(e4m3)");
 }
 
-// y[t][:] = sum_j pairbuf[pair_pos[t][j]][:] in slot order (deterministic combine)
-__global__ void k_moe_combine(const float* __restrict__ pairbuf, const int32_t* __restrict__ pair_pos, int topk,
-                              int64_t T, int64_t H, float* __restrict__ y) {
-  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+// y[t][n] = sum_j topk_w[t][j] * slot[t][j][n], j = 0..topk-1 in order (a
+// fixed summation order: bitwise repeatable), eight outputs per thread.
+template <bool F32>
+__global__ void k_moe_combine(const void* __restrict__ slots, const float* __restrict__ topk_w, int topk, int64_t T,
+                              int64_t H, float* __restrict__ y) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (i >= T * H) return;
   const int64_t t = i / H, n = i % H;
-  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < topk; ++j) acc += *reinterpret_cast<const v4f*>(pairbuf + (int64_t)pair_pos[t * topk + j] * H + n);
-  *reinterpret_cast<v4f*>(y + i) = acc;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < topk; ++j) {
+    const float w = topk_w[t * topk + j];
+    const int64_t base = (t * topk + j) * H + n;
+    if (F32) {
+      const v4f a = *reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(slots) + base);
+      const v4f b = *reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(slots) + base + 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[q] += w * a[q];
+        acc[4 + q] += w * b[q];
+      }
+    } else {
+      const v4i v = load16(reinterpret_cast<const uint16_t*>(slots) + base);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += w * bf16_to_f32((uint32_t)v[q] & 0xFFFFu);
+        acc[2 * q + 1] += w * bf16_to_f32((uint32_t)v[q] >> 16);
+      }
+    }
+  }
+  *reinterpret_cast<v4f*>(y + i) = v4f{acc[0], acc[1], acc[2], acc[3]};
+  *reinterpret_cast<v4f*>(y + i + 4) = v4f{acc[4], acc[5], acc[6], acc[7]};
 }
 
 }  // namespace gbw
 
 namespace gbw {
 
-size_t ws_moe_gemm(int64_t P, int64_t N, int32_t fmt) {
-  (void)fmt;
-  // only the deterministic down/combine path uses it: a [P][N] fp32 pair buffer
-  return P > 0 && N > 0 ? (size_t)P * N * sizeof(float) : 0;
+size_t ws_moe_gemm(int64_t P, int64_t N, int64_t f32) {
+  // the down/combine stage: a [T][topk][H] slot buffer, bf16 (fp32 with GBW_FP32_COMBINE)
+  return P > 0 && N > 0 ? (size_t)P * N * (f32 ? sizeof(float) : sizeof(uint16_t)) : 0;
 }
 
 }  // namespace gbw
@@ -688,10 +705,12 @@ extern "C" int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const in
   if (!aligned16(a->codes) || !aligned16(w->codes) || (w->codebook && !aligned16(w->codebook)) ||
       (reinterpret_cast<uintptr_t>(a->scales) & 3u) || (reinterpret_cast<uintptr_t>(w->scales) & 3u))
     return fail(GBW_E_ALIGN, "moe_grouped_gemm: codes/codebook must be 16-byte and scales 4-byte aligned");
-  const bool det = (flags & GBW_DETERMINISTIC) != 0;
-  if (stage == GBW_MOE_DOWN_COMBINE && det && (!ws || ws_bytes < ws_moe_gemm(P, N, w->fmt)))
-    return fail(GBW_E_WORKSPACE, "moe_grouped_gemm: deterministic combine needs %zu bytes of workspace",
-                ws_moe_gemm(P, N, w->fmt));
+  const bool f32c = (flags & GBW_FP32_COMBINE) != 0;
+  const bool use_slots = stage == GBW_MOE_DOWN_COMBINE && ws != nullptr;
+  if (stage == GBW_MOE_DOWN_COMBINE && (flags & GBW_DETERMINISTIC) && !ws)
+    return fail(GBW_E_WORKSPACE, "moe_grouped_gemm: a deterministic combine needs the slot-buffer workspace");
+  if (use_slots && ws_bytes < ws_moe_gemm(P, N, f32c))
+    return fail(GBW_E_WORKSPACE, "moe_grouped_gemm: the combine needs %zu bytes of workspace", ws_moe_gemm(P, N, f32c));
   int st = check_device();
   if (st) return st;
   hipStream_t s = as_stream(stream);
@@ -718,28 +737,32 @@ extern "C" int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const in
   p.h_codes = out->h_codes;
   p.h_scales = out->h_scales;
   p.y = out->y;
-  p.pairbuf = (stage == GBW_MOE_DOWN_COMBINE && det) ? reinterpret_cast<float*>(ws) : nullptr;
+  p.slots = use_slots ? ws : nullptr;
+  p.slots_f32 = f32c ? 1 : 0;
   const int64_t m_tiles_max = cdiv(P, kMoeBM) + E;
   int64_t grid = m_tiles_max * p.n_tiles;
   grid = cdiv(grid, 8) * 8;
   if (grid > INT32_MAX) return fail(GBW_E_SHAPE, "moe_grouped_gemm: problem too large");
   p.total_tiles = (int)grid;
-  if (stage == GBW_MOE_DOWN_COMBINE && !det) {
+  if (stage == GBW_MOE_DOWN_COMBINE && !use_slots) {
     if ((st = launch_fill_zero(out->y, T * N, s))) return st;
   }
   if (e4m3) {
     st = launch_moe_bf16(p, a, w, (int)grid, s);
   } else {
     if (w->fmt == GBW_FMT_VQ4_E8M0)
-      hipLaunchKernelGGL(k_moe_fp4<W_VQ>, dim3((unsigned)grid), dim3(kMoeThreads), 0, s, p);
+      hipLaunchKernelGGL(k_moe_fp4<W_VQ>, dim3((unsigned)grid), dim3(kFp4Threads), 0, s, p);
     else
-      hipLaunchKernelGGL(k_moe_fp4<W_MX>, dim3((unsigned)grid), dim3(kMoeThreads), 0, s, p);
+      hipLaunchKernelGGL(k_moe_fp4<W_MX>, dim3((unsigned)grid), dim3(kFp4Threads), 0, s, p);
     st = check_launch("moe_grouped_gemm");
   }
   if (st) return st;
-  if (stage == GBW_MOE_DOWN_COMBINE && det) {
-    hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)cdiv(cdiv(T * N, 4), 256)), dim3(256), 0, s, p.pairbuf,
-                       pair_pos, topk, T, N, out->y);
+  if (use_slots) {
+    const unsigned blocks = (unsigned)cdiv(cdiv(T * N, 8), 256);
+    if (f32c)
+      hipLaunchKernelGGL(k_moe_combine<true>, dim3(blocks), dim3(256), 0, s, ws, topk_w, topk, T, N, out->y);
+    else
+      hipLaunchKernelGGL(k_moe_combine<false>, dim3(blocks), dim3(256), 0, s, ws, topk_w, topk, T, N, out->y);
     st = check_launch("moe_grouped_gemm(combine)");
   }
   return st;

@@ -85,32 +85,49 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_topk(const float* __res
     for (int e = lane; e < E; e += 64) counts[chunk * E + e] = __popcll(mask[wv][e]);
 }
 
-// Single workgroup: thread e owns expert e.
+// Single workgroup of 1024 threads: G = 1024 / E' threads per expert (E' = E
+// rounded up to a power of two) each own a contiguous run of chunks; per-run
+// sums, an exclusive scan over the runs of an expert, an inclusive scan over
+// the expert totals, then each thread writes the bases of its own chunks.
 __global__ __launch_bounds__(kMaxExperts) void k_route_scan(const int32_t* __restrict__ counts, int64_t C, int E,
                                                            int32_t* __restrict__ base,
                                                            int32_t* __restrict__ expert_offsets) {
+  __shared__ int32_t part[kMaxExperts];
   __shared__ int32_t tot[kMaxExperts];
-  const int e = threadIdx.x;
+  int Ep = 1;
+  while (Ep < E) Ep <<= 1;
+  const int G = kMaxExperts / Ep;
+  const int tid = threadIdx.x;
+  const int e = tid / G, g = tid % G;
+  const int64_t per = (C + G - 1) / G;
+  const int64_t c0 = g * per, c1 = min(C, c0 + per);
   int32_t s = 0;
   if (e < E)
-    for (int64_t c = 0; c < C; ++c) s += counts[c * E + e];
-  tot[e] = e < E ? s : 0;
+    for (int64_t c = c0; c < c1; ++c) s += counts[c * E + e];
+  part[tid] = s;
   __syncthreads();
-  // inclusive Hillis-Steele scan over experts
-  for (int o = 1; o < kMaxExperts; o <<= 1) {
-    const int32_t add = e >= o ? tot[e - o] : 0;
+  if (g == 0) {
+    int32_t t = 0;
+    for (int q = 0; q < G; ++q) t += part[e * G + q];
+    tot[e] = e < E ? t : 0;
+  }
+  if (tid >= Ep) tot[tid] = 0;
+  __syncthreads();
+  for (int o = 1; o < kMaxExperts; o <<= 1) {  // inclusive scan of the expert totals
+    const int32_t add = tid >= o ? tot[tid - o] : 0;
     __syncthreads();
-    tot[e] += add;
+    tot[tid] += add;
     __syncthreads();
   }
   if (e < E) {
-    int32_t run = tot[e] - s;  // exclusive offset of expert e
-    expert_offsets[e] = run;
-    for (int64_t c = 0; c < C; ++c) {
+    int32_t run = (e ? tot[e - 1] : 0);
+    for (int q = 0; q < g; ++q) run += part[e * G + q];
+    if (g == 0) expert_offsets[e] = e ? tot[e - 1] : 0;
+    if (e == E - 1 && g == 0) expert_offsets[E] = tot[E - 1];
+    for (int64_t c = c0; c < c1; ++c) {
       base[c * E + e] = run;
       run += counts[c * E + e];
     }
-    if (e == E - 1) expert_offsets[E] = run;
   }
 }
 

@@ -60,6 +60,7 @@ extern "C" {
 /* flags */
 #define GBW_TS_DYNAMIC 1     /* mx_quantize: compute the E4M3 tensor scale from the data */
 #define GBW_DETERMINISTIC 2  /* GEMMs: fixed summation order, bitwise repeatable          */
+#define GBW_FP32_COMBINE 4   /* moe down: keep the per-pair outputs in fp32 (default bf16) */
 
 /* moe_grouped_gemm stages */
 #define GBW_MOE_GATEUP_SWIGLU 0
@@ -70,7 +71,7 @@ extern "C" {
 #define GBW_OP_MX_GEMM 1    /* d0 = M, d1 = N, d2 = K + tail           */
 #define GBW_OP_LUT_GEMM 2   /* d0 = M, d1 = N, d2 = K                  */
 #define GBW_OP_MOE_ROUTE 3  /* d0 = T, d1 = E                          */
-#define GBW_OP_MOE_GEMM 4   /* d0 = pairs, d1 = N (output width)       */
+#define GBW_OP_MOE_GEMM 4   /* d0 = pairs, d1 = H, d2 = 1 for GBW_FP32_COMBINE */
 
 /* ---- descriptors -------------------------------------------------------- */
 
@@ -189,10 +190,16 @@ int moe_route(const float* logits, int64_t T, int32_t E, int32_t topk, int32_t* 
  *    written; quantize it with mx_quantize(GBW_TS_DYNAMIC).
  *  GBW_MOE_DOWN_COMBINE: y[t] = sum_j topk_w[t][j] * deq(a[pair_pos[t][j]])
  *    deq(w_e)^T, a = quantized h in pair order, y [T][H] fp32 (overwritten).
+ *    With a workspace, every pair's output goes once to a [T][topk][H] slot
+ *    buffer (bf16, or fp32 with GBW_FP32_COMBINE) and a second kernel sums a
+ *    token's slots in slot order: bitwise repeatable.  With ws = NULL the
+ *    outputs are added into y with fp32 atomics (no workspace, not
+ *    repeatable; GBW_DETERMINISTIC then fails with GBW_E_WORKSPACE).
  * Weights: E8M0-B32, VQ4-E8M0 (decoded to MXFP4 in LDS, scaled MFMA) or
  * E4M3-B16 (decoded exactly to bf16, bf16 MFMA).  The activation format must
  * be E4M3-B16 for E4M3-B16 weights and E8M0-B32 otherwise.
- * ws: gbw_workspace_size(GBW_OP_MOE_GEMM, P, N, 0, fmt) bytes. */
+ * ws: gbw_workspace_size(GBW_OP_MOE_GEMM, P, H, fp32_combine, 0) bytes
+ * (down stage only; the gate/up stage takes none). */
 typedef struct gbw_moe_out {
   uint16_t* h_bf16;   /* GATEUP: [P][I] bf16 bits or NULL            */
   uint8_t* h_codes;   /* GATEUP, E8M0: [P][I/2] or NULL               */

@@ -245,13 +245,15 @@ def _run_and_check(pb, tokens=None, experts=None, h_amax=None):
                               device=DEV)
             hq = gbw.mx_quantize(hb, afmt, tensor_scale=st, dynamic=False)
     y = torch.empty((T, H), dtype=torch.float32, device=DEV)
-    gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, pb.Wd, y=y)
+    gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, pb.Wd, y=y)                 # bf16 slots
+    y2 = torch.empty_like(y)
+    gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, pb.Wd, y=y2)
     yd = torch.empty_like(y)
-    gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, pb.Wd, y=yd, flags=gbw.DETERMINISTIC)
-    yd2 = torch.empty_like(y)
-    gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, pb.Wd, y=yd2, flags=gbw.DETERMINISTIC)
+    gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, pb.Wd, y=yd, flags=gbw.FP32_COMBINE)
+    ya = torch.empty_like(y)
+    gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, pb.Wd, y=ya, ws=False)      # fp32 atomics
     torch.cuda.synchronize()
-    assert torch.equal(yd, yd2), "deterministic combine differs between runs"
+    assert torch.equal(y, y2), "slot combine differs between runs"
 
     # ---- oracle pipeline, from the synthetic inputs only ----
     xn = pb.x.float().cpu().numpy()
@@ -318,7 +320,7 @@ def _run_and_check(pb, tokens=None, experts=None, h_amax=None):
     y_ref = oracle.moe_down_combine(full_c, full_s, fmt, ref_route, pb.ref_d[0], pb.ref_d[1], hts,
                                     pb.ref_d[2] if e4 else None, tokens=tokens)
     clean = np.array([row_same[ref_route["pair_pos"][t]].all() for t in tokens])
-    for name, yy in (("atomic", y), ("deterministic", yd)):
+    for name, yy in (("bf16 slots", y), ("fp32 slots", yd), ("atomic", ya)):
         yv = to_np(yy)[tokens]
         if clean.any():
             assert_rows_close(yv[clean], y_ref[clean], what=f"moe down ({name})")
