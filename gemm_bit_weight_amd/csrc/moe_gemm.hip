@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t sB[2][kMoeBN * kRowB];
   __shared__ uint32_t sAs[2][kMoeBM];
   __shared__ uint32_t sBs[2][kMoeBN];
-  __shared__ __attribute__((aligned(16))) uint16_t sLut[WF == W_VQ ? 8 * 256 : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sLut[2][WF == W_VQ ? 8 * 256 : 8];
   __shared__ int scan[kMoeThreads];
   __shared__ int s_tok[kMoeBM];
   __shared__ float s_w[kMoeBM];
@@ -237,10 +237,21 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
     cbase = p.w_cb + ((int64_t)ti.e * (wN / 64) + qrow) * (K / 64) * 256;
   }
 
+  // Software pipeline, one barrier per 128-element stage.  Iteration s:
+  //   1. store stage s+1 (loaded into registers during iteration s-1) into
+  //      LDS buffer (s+1)&1 and, for VQ, expand its indices there through the
+  //      QBlock tables of stage s+1 (stored one iteration earlier);
+  //   2. issue the global loads of stage s+2 (and the tables of stage s+3);
+  //   3. the MFMAs of stage s from buffer s&1;
+  //   4. barrier.
+  // Indices past the last stage are clamped, so the loop body has no branches
+  // (the redundant work at the end hits L2 and a spare buffer).
   v4i pa[2], pb[2];
   uint32_t psc;
   v4i pl;
+  const int last = steps - 1;
   auto gload = [&](int s) {
+    s = s < last ? s : last;
     const int64_t kb = (int64_t)s * 64;
 #pragma unroll
     for (int u = 0; u < 2; ++u) pa[u] = load16(arow[u] + kb + 16 * ac);
@@ -250,10 +261,13 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
       for (int u = 0; u < 2; ++u) pb[u] = load16(wrow[u] + kb + 16 * ac);
     } else {
       pb[0] = load16(vrow + (int64_t)s * 32 + 16 * (tid & 1));
-      if (tid < 256) pl = load16(cbase + ((int64_t)s * 2 + lut_kb) * 256 + (tid & 31) * 8);
+      const int sl = s + 1 < last ? s + 1 : last;  // tables run one stage ahead
+      pl = load16(cbase + ((int64_t)sl * 2 + lut_kb) * 256 + (tid & 31) * 8);
     }
   };
-  auto lstore = [&](int buf) {
+  // stage k's registers -> LDS buffer k&1 (tables of stage k+1 -> table buffer (k+1)&1)
+  auto lstore = [&](int k) {
+    const int buf = k & 1;
 #pragma unroll
     for (int u = 0; u < 2; ++u) *reinterpret_cast<v4i*>(&sA[buf][(ar + 128 * u) * kRowB + 16 * ac]) = pa[u];
     if (tid < 256)
@@ -264,13 +278,14 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) *reinterpret_cast<v4i*>(&sB[buf][(ar + 128 * u) * kRowB + 16 * ac]) = pb[u];
     } else if (tid < 256) {
-      *reinterpret_cast<v4i*>(&sLut[(tid >> 5) * 256 + (tid & 31) * 8]) = pl;
+      *reinterpret_cast<v4i*>(&sLut[buf ^ 1][(tid >> 5) * 256 + (tid & 31) * 8]) = pl;
     }
   };
-  // VQ: expand this thread's 16 indices into 32 bytes of E2M1 codes
-  auto vq_expand = [&](int buf) {
+  // VQ: expand this thread's 16 indices of stage k into 32 bytes of E2M1 codes
+  auto vq_expand = [&](int k) {
+    const int buf = k & 1;
     const int row = tid >> 1, half = tid & 1;  // half = 64-element half of the stage = QBlock column
-    const uint16_t* lut = &sLut[(((row >> 6) << 1) + half) * 256];
+    const uint16_t* lut = &sLut[buf][(((row >> 6) << 1) + half) * 256];
     uint32_t o[8];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -295,18 +310,27 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
   for (int j = 0; j < 4; ++j)
     brow[j] = p.stage == GBW_MOE_GATEUP_SWIGLU ? (j < 2 ? 64 * wn + 32 * j : 128 + 64 * wn + 32 * (j - 2))
                                                : 128 * wn + 32 * j;
+  // 32-row bands of this wave that hold pairs (the last tile of an expert is
+  // usually partly empty: its waves skip the empty bands' MFMAs)
+  const bool band0 = 64 * wm < ti.rows, band1 = 64 * wm + 32 < ti.rows;
 
+  // prologue: stage 0 (and the tables of stages 0 and 1) in LDS, stage 1 in registers
+  if (WF == W_VQ && tid < 256) {
+    const v4i t0 = load16(cbase + (int64_t)lut_kb * 256 + (tid & 31) * 8);
+    *reinterpret_cast<v4i*>(&sLut[0][(tid >> 5) * 256 + (tid & 31) * 8]) = t0;
+  }
   gload(0);
   lstore(0);
   __syncthreads();
-  if (WF == W_VQ) {
-    vq_expand(0);
-    __syncthreads();
-  }
+  if (WF == W_VQ) vq_expand(0);
+  gload(1);
+  __syncthreads();
 
   for (int s = 0; s < steps; ++s) {
     const int buf = s & 1;
-    if (s + 1 < steps) gload(s + 1);
+    lstore(s + 1);
+    if (WF == W_VQ) vq_expand(s + 1);
+    gload(s + 2);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {  // two 64-element MFMA steps per 128-element stage
       v4i bf[4];
@@ -319,6 +343,7 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
+        if (i == 0 ? !band0 : !band1) continue;
         const int row = 64 * wm + 32 * i + l32;
         const v4i af = *reinterpret_cast<const v4i*>(&sA[buf][row * kRowB + 32 * t + 16 * g2]);
         const int asc = (int)((sAs[buf][row] >> (8 * (2 * t + g2))) & 0xFFu);
@@ -328,14 +353,7 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
                                                                        asc, 0, bsc[j]);
       }
     }
-    if (s + 1 < steps) {
-      lstore(buf ^ 1);
-      __syncthreads();
-      if (WF == W_VQ) {
-        vq_expand(buf ^ 1);
-        __syncthreads();
-      }
-    }
+    __syncthreads();
   }
 
   // ---------------------------------------------------------------------
@@ -343,16 +361,57 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
   // tile and column brow[j] + l32 of the B tile
   // ---------------------------------------------------------------------
   if (p.stage == GBW_MOE_DOWN_COMBINE) {
+    if (!p.slots) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * g2 + (r & 3);
-        if (m >= ti.rows) continue;
+        for (int r = 0; r < 16; ++r) {
+          const int m = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * g2 + (r & 3);
+          if (m >= ti.rows) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          store_pair_out(p, s_tok[m], s_slot[m], s_w[m], (int64_t)ti.nt * kMoeBN + brow[j] + l32, acc[i][j][r]);
+          for (int j = 0; j < 4; ++j)
+            store_pair_out(p, s_tok[m], s_slot[m], s_w[m], (int64_t)ti.nt * kMoeBN + brow[j] + l32, acc[i][j][r]);
+        }
+      return;
+    }
+    // slot buffer: each wave stages its 64 x 128 block in LDS, 16 rows at a
+    // time (8 KiB at most: waves 0-3 in the freed A buffers, 4-7 in the B
+    // buffers), then writes whole 16-byte pieces of the output rows
+    const int esz = p.slots_f32 ? 4 : 2;
+    uint8_t* stg = (wave < 4 ? &sA[0][0] : &sB[0][0]) + (wave & 3) * (16 * 128 * 4);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int r = 8 * h; r < 8 * h + 8; ++r) {
+          const int mr = 8 * ((r >> 2) & 1) + 4 * g2 + (r & 3);  // row within the 16-row half
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int c = 32 * j + l32;
+            if (esz == 4)
+              reinterpret_cast<float*>(stg)[mr * 128 + c] = acc[i][j][r];
+            else
+              reinterpret_cast<uint16_t*>(stg)[mr * 128 + c] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+        const int pieces = 128 * esz / 16;  // 16-byte pieces per row
+        for (int q = lane; q < 16 * pieces; q += 64) {
+          const int mr = q / pieces, pc = q % pieces;
+          const int m = 64 * wm + 32 * i + 16 * h + mr;
+          if (m < ti.rows) {
+            const int64_t col0 = (int64_t)ti.nt * kMoeBN + 128 * wn;
+            uint8_t* dst = reinterpret_cast<uint8_t*>(p.slots) +
+                           (((int64_t)s_tok[m] * p.topk + s_slot[m]) * p.N + col0) * esz + pc * 16;
+            *reinterpret_cast<v4i*>(dst) = *reinterpret_cast<const v4i*>(stg + mr * 128 * esz + pc * 16);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
       }
+    }
     return;
   }
 
