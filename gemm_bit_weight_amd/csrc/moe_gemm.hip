@@ -75,7 +75,7 @@ struct TileInfo {
 };
 
 // Logical tile of this workgroup: XCD-aware remap, then (expert, m tile, n tile).
-__device__ bool find_tile(const MoeArgs& p, TileInfo& ti, int* scan) {
+__device__ __forceinline__ bool find_tile(const MoeArgs& p, TileInfo& ti, int* scan) {
   const int G = gridDim.x;
   const int per = (G + 7) / 8;
   const int L = (blockIdx.x % 8) * per + blockIdx.x / 8;
@@ -146,6 +146,70 @@ __device__ __forceinline__ int64_t b_row(const MoeArgs& p, int nt, int j) {
     return j < kMoeBN / 2 ? i0 + j : I + i0 + (j - kMoeBN / 2);
   }
   return (int64_t)nt * kMoeBN + j;
+}
+
+// DOWN epilogue shared by the expert kernels (8 waves of 64 x 128, 32x32
+// accumulators): acc[i][j][r] is row 64*wm + 32*i + 8*(r/4) + 4*(lane/32) +
+// r%4 of the tile and column brow[j] + lane%32 of the B tile; `scale`
+// multiplies every output (the tensor scales of E4M3-B16, 1 otherwise).
+// With a slot buffer each wave stages its block in LDS, 16 rows at a time
+// (8 KiB at most; waves 0-3 in stgA, 4-7 in stgB, both free after the main
+// loop's last barrier), then writes whole 16-byte pieces of output rows.
+__device__ __forceinline__ void down_epilogue(const MoeArgs& p, const TileInfo& ti, const v16f (&acc)[2][4],
+                                              const int (&brow)[4], int wave, int lane, float scale, uint8_t* stgA,
+                                              uint8_t* stgB, const int* s_tok, const int* s_slot, const float* s_w) {
+  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, g2 = lane >> 5;
+  if (!p.slots) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * g2 + (r & 3);
+        if (m >= ti.rows) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          store_pair_out(p, s_tok[m], s_slot[m], s_w[m], (int64_t)ti.nt * kMoeBN + brow[j] + l32,
+                         scale * acc[i][j][r]);
+      }
+    return;
+  }
+  const int esz = p.slots_f32 ? 4 : 2;
+  uint8_t* stg = (wave < 4 ? stgA : stgB) + (wave & 3) * (16 * 128 * 4);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const int r = 8 * h + rr;
+        const int mr = 8 * ((r >> 2) & 1) + 4 * g2 + (r & 3);  // row within the 16-row half
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = 32 * j + l32;
+          const float v = scale * acc[i][j][r];
+          if (esz == 4)
+            reinterpret_cast<float*>(stg)[mr * 128 + c] = v;
+          else
+            reinterpret_cast<uint16_t*>(stg)[mr * 128 + c] = (uint16_t)f32_to_bf16_rne(v);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+      __builtin_amdgcn_wave_barrier();
+      const int pieces = 128 * esz / 16;  // 16-byte pieces per row
+      for (int q = lane; q < 16 * pieces; q += 64) {
+        const int mr = q / pieces, pc = q % pieces;
+        const int m = 64 * wm + 32 * i + 16 * h + mr;
+        if (m < ti.rows) {
+          const int64_t col0 = (int64_t)ti.nt * kMoeBN + 128 * wn;
+          uint8_t* dst = reinterpret_cast<uint8_t*>(p.slots) +
+                         (((int64_t)s_tok[m] * p.topk + s_slot[m]) * p.N + col0) * esz + pc * 16;
+          *reinterpret_cast<v4i*>(dst) = *reinterpret_cast<const v4i*>(stg + mr * 128 * esz + pc * 16);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
 }
 
 // 512 threads = 8 waves as 4 (rows) x 2 (columns); a wave owns a 64 x 128
@@ -361,57 +425,7 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
   // tile and column brow[j] + l32 of the B tile
   // ---------------------------------------------------------------------
   if (p.stage == GBW_MOE_DOWN_COMBINE) {
-    if (!p.slots) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * g2 + (r & 3);
-          if (m >= ti.rows) continue;
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            store_pair_out(p, s_tok[m], s_slot[m], s_w[m], (int64_t)ti.nt * kMoeBN + brow[j] + l32, acc[i][j][r]);
-        }
-      return;
-    }
-    // slot buffer: each wave stages its 64 x 128 block in LDS, 16 rows at a
-    // time (8 KiB at most: waves 0-3 in the freed A buffers, 4-7 in the B
-    // buffers), then writes whole 16-byte pieces of the output rows
-    const int esz = p.slots_f32 ? 4 : 2;
-    uint8_t* stg = (wave < 4 ? &sA[0][0] : &sB[0][0]) + (wave & 3) * (16 * 128 * 4);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int r = 8 * h; r < 8 * h + 8; ++r) {
-          const int mr = 8 * ((r >> 2) & 1) + 4 * g2 + (r & 3);  // row within the 16-row half
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int c = 32 * j + l32;
-            if (esz == 4)
-              reinterpret_cast<float*>(stg)[mr * 128 + c] = acc[i][j][r];
-            else
-              reinterpret_cast<uint16_t*>(stg)[mr * 128 + c] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
-          }
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-        __builtin_amdgcn_wave_barrier();
-        const int pieces = 128 * esz / 16;  // 16-byte pieces per row
-        for (int q = lane; q < 16 * pieces; q += 64) {
-          const int mr = q / pieces, pc = q % pieces;
-          const int m = 64 * wm + 32 * i + 16 * h + mr;
-          if (m < ti.rows) {
-            const int64_t col0 = (int64_t)ti.nt * kMoeBN + 128 * wn;
-            uint8_t* dst = reinterpret_cast<uint8_t*>(p.slots) +
-                           (((int64_t)s_tok[m] * p.topk + s_slot[m]) * p.N + col0) * esz + pc * 16;
-            *reinterpret_cast<v4i*>(dst) = *reinterpret_cast<const v4i*>(stg + mr * 128 * esz + pc * 16);
-          }
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
-      }
-    }
+    down_epilogue(p, ti, acc, brow, wave, lane, 1.0f, &sA[0][0], &sB[0][0], s_tok, s_slot, s_w);
     return;
   }
 
@@ -517,7 +531,13 @@ __device__ __forceinline__ uint32_t e4m3_to_h2(uint32_t c) {
   return b | (b << 16);
 }
 
-__global__ __launch_bounds__(kMoeThreads) void k_moe_e4m3(const MoeArgs p) {
+// 8 waves (4 x 2) of 64 x 128 as in k_moe_fp4, v_mfma_f32_32x32x16_f16
+// (lane l: row l % 32, K elements [8*(l/32), 8*(l/32)+8) of the 16-element
+// step; on gfx950 the 32x32 shape runs at about twice the 16x16 rate).  Stage
+// = 64 K elements: threads 0..255 decode row tid of A, 256..511 row tid-256 of
+// B, into fp16 LDS rows of 128 bytes + 16 of padding.  Same single-barrier
+// pipeline: stage s+1 is decoded into LDS before the MFMAs of stage s.
+__global__ __launch_bounds__(kFp4Threads) void k_moe_e4m3(const MoeArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][kMoeBM * kRowH];
   __shared__ __attribute__((aligned(16))) uint8_t sB[2][kMoeBN * kRowH];
   __shared__ int scan[kMoeThreads];
@@ -529,11 +549,11 @@ __global__ __launch_bounds__(kMoeThreads) void k_moe_e4m3(const MoeArgs p) {
   if (!find_tile(p, ti, scan)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int r16 = lane & 15, g4 = lane >> 4;
+  const int l32 = lane & 31, g2 = lane >> 5;
   const int64_t K = p.K;
   const int steps = (int)(K / 64);
 
-  for (int r = tid; r < kMoeBM; r += kMoeThreads) {
+  for (int r = tid; r < kMoeBM; r += kFp4Threads) {
     int tok = 0, slot = 0;
     float wt = 0.f;
     if (r < ti.rows) {
@@ -552,115 +572,105 @@ __global__ __launch_bounds__(kMoeThreads) void k_moe_e4m3(const MoeArgs p) {
   }
   __syncthreads();
 
-  // thread tid stages row tid of A and row tid of B: 64 elements = 32 bytes of
-  // codes and one dword of four E4M3 scales per stage
-  const int rr = tid < ti.rows ? tid : ti.rows - 1;
-  const int64_t asrc = p.stage == GBW_MOE_GATEUP_SWIGLU ? (int64_t)s_tok[rr] : (int64_t)(ti.row0 + rr);
-  const uint8_t* arow = p.a_codes + asrc * (K / 2);
-  const uint8_t* ascl = p.a_scales + asrc * (K / 16);
-  const int64_t wr = (int64_t)ti.e * p.N + b_row(p, ti.nt, tid);
-  const uint8_t* brow_c = p.w_codes + wr * (K / 2);
-  const uint8_t* brow_s = p.w_scales + wr * (K / 16);
+  // thread tid stages one row: A row tid (tid < 256) or B row tid - 256
+  const int row = tid & 255;
+  const uint8_t* rc;
+  const uint8_t* rs;
+  if (tid < 256) {
+    const int rr = row < ti.rows ? row : ti.rows - 1;
+    const int64_t src = p.stage == GBW_MOE_GATEUP_SWIGLU ? (int64_t)s_tok[rr] : (int64_t)(ti.row0 + rr);
+    rc = p.a_codes + src * (K / 2);
+    rs = p.a_scales + src * (K / 16);
+  } else {
+    const int64_t wr = (int64_t)ti.e * p.N + b_row(p, ti.nt, row);
+    rc = p.w_codes + wr * (K / 2);
+    rs = p.w_scales + wr * (K / 16);
+  }
+  uint8_t* const dst0 = tid < 256 ? &sA[0][row * kRowH] : &sB[0][row * kRowH];
+  uint8_t* const dst1 = tid < 256 ? &sA[1][row * kRowH] : &sB[1][row * kRowH];
 
-  v4i pa[2], pb[2];
-  uint32_t pas, pbs;
+  v4i pc[2];
+  uint32_t ps;
+  const int last = steps - 1;
   auto gload = [&](int s) {
-    pa[0] = load16(arow + (int64_t)s * 32);
-    pa[1] = load16(arow + (int64_t)s * 32 + 16);
-    pb[0] = load16(brow_c + (int64_t)s * 32);
-    pb[1] = load16(brow_c + (int64_t)s * 32 + 16);
-    pas = *reinterpret_cast<const uint32_t*>(ascl + (int64_t)s * 4);
-    pbs = *reinterpret_cast<const uint32_t*>(brow_s + (int64_t)s * 4);
+    s = s < last ? s : last;
+    pc[0] = load16(rc + (int64_t)s * 32);
+    pc[1] = load16(rc + (int64_t)s * 32 + 16);
+    ps = *reinterpret_cast<const uint32_t*>(rs + (int64_t)s * 4);
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int k) {
+    uint8_t* dst = (k & 1) ? dst1 : dst0;
 #pragma unroll
-    for (int op = 0; op < 2; ++op) {
-      const v4i* src = op == 0 ? pa : pb;
-      const uint32_t scl = op == 0 ? pas : pbs;
-      uint8_t* dst = op == 0 ? &sA[buf][tid * kRowH] : &sB[buf][tid * kRowH];
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        // dword d of the 32 code bytes holds elements 8d..8d+7, block d/2
-        const uint32_t w = (uint32_t)src[d >> 2][d & 3];
-        uint32_t o[4];
-        e4m3_decode8(w, e4m3_to_h2(scl >> (8 * (d >> 1))), o);
-        *reinterpret_cast<v4i*>(dst + 16 * d) = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-      }
+    for (int d = 0; d < 8; ++d) {
+      // dword d of the 32 code bytes holds elements 8d..8d+7, scale block d/2
+      uint32_t o[4];
+      e4m3_decode8((uint32_t)pc[d >> 2][d & 3], e4m3_to_h2(ps >> (8 * (d >> 1))), o);
+      *reinterpret_cast<v4i*>(dst + 16 * d) = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
     }
   };
 
-  v4f acc[8][8];
+  v16f acc[2][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  int brow[8];
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+  int brow[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    brow[j] = p.stage == GBW_MOE_GATEUP_SWIGLU ? (j < 4 ? 64 * wn + 16 * j : 128 + 64 * wn + 16 * (j - 4))
-                                               : 128 * wn + 16 * j;
+  for (int j = 0; j < 4; ++j)
+    brow[j] = p.stage == GBW_MOE_GATEUP_SWIGLU ? (j < 2 ? 64 * wn + 32 * j : 128 + 64 * wn + 32 * (j - 2))
+                                               : 128 * wn + 32 * j;
+  const bool band0 = 64 * wm < ti.rows, band1 = 64 * wm + 32 < ti.rows;
 
   gload(0);
   lstore(0);
+  gload(1);
   __syncthreads();
   for (int s = 0; s < steps; ++s) {
     const int buf = s & 1;
-    if (s + 1 < steps) gload(s + 1);
+    lstore(s + 1);
+    gload(s + 2);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      v8h bf[8];
+    for (int ks = 0; ks < 4; ++ks) {  // four 16-element MFMA steps per 64-element stage
+      v8h bf[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        bf[j] = *reinterpret_cast<const v8h*>(&sB[buf][(brow[j] + r16) * kRowH + 64 * ks + 16 * g4]);
+      for (int j = 0; j < 4; ++j)
+        bf[j] = *reinterpret_cast<const v8h*>(&sB[buf][(brow[j] + l32) * kRowH + 32 * ks + 16 * g2]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const v8h af = *reinterpret_cast<const v8h*>(&sA[buf][(128 * wm + 16 * i + r16) * kRowH + 64 * ks + 16 * g4]);
+      for (int i = 0; i < 2; ++i) {
+        if (i == 0 ? !band0 : !band1) continue;
+        const v8h af = *reinterpret_cast<const v8h*>(&sA[buf][(64 * wm + 32 * i + l32) * kRowH + 32 * ks + 16 * g2]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[j], acc[i][j], 0, 0, 0);
       }
     }
-    if (s + 1 < steps) {
-      lstore(buf ^ 1);
-      __syncthreads();
-    }
+    __syncthreads();
   }
 
   const float sa = p.a_ts[0];
   if (p.stage == GBW_MOE_DOWN_COMBINE) {
-    const float sw = sa * p.w_ts[(int64_t)ti.e * p.ts_per];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 128 * wm + 16 * i + 4 * g4 + r;
-        if (m >= ti.rows) continue;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          store_pair_out(p, s_tok[m], s_slot[m], s_w[m], (int64_t)ti.nt * kMoeBN + 128 * wn + 16 * j + r16,
-                         sw * acc[i][j][r]);
-      }
+    down_epilogue(p, ti, acc, brow, wave, lane, sa * p.w_ts[(int64_t)ti.e * p.ts_per], &sA[0][0], &sB[0][0], s_tok,
+                  s_slot, s_w);
     return;
   }
-  // GATEUP: h = bf16(silu(g) * u), staged in LDS for coalesced stores
+  // GATEUP: h = bf16(silu(g) * u), staged in LDS (the A buffers) for coalesced stores
   const float sg = sa * p.w_ts[(int64_t)ti.e * p.ts_per];
   const float su = sa * p.w_ts[(int64_t)ti.e * p.ts_per + (p.ts_per > 1 ? 1 : 0)];
-  __syncthreads();
-  uint16_t* sH = reinterpret_cast<uint16_t*>(&sA[0][0]);  // [256][128] bf16
+  uint16_t* sH = reinterpret_cast<uint16_t*>(&sA[0][0]);  // [256][128] bf16 = 64 KiB
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 128 * wm + 16 * i + 4 * g4 + r;
+    for (int r = 0; r < 16; ++r) {
+      const int m = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * g2 + (r & 3);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float gv = acc[i][jj][r] * sg, uv = acc[i][jj + 4][r] * su;
+      for (int jj = 0; jj < 2; ++jj) {
+        const float gv = acc[i][jj][r] * sg, uv = acc[i][jj + 2][r] * su;
         const float h = gv / (1.0f + expf(-gv)) * uv;
-        sH[m * 128 + 64 * wn + 16 * jj + r16] = (uint16_t)f32_to_bf16_rne(h);
+        sH[m * 128 + 64 * wn + 32 * jj + l32] = (uint16_t)f32_to_bf16_rne(h);
       }
     }
   __syncthreads();
   const int64_t I = p.N / 2;
-  for (int c = tid; c < kMoeBM * 16; c += kMoeThreads) {
+  for (int c = tid; c < kMoeBM * 16; c += kFp4Threads) {
     const int m = c >> 4, q = c & 15;
     if (m < ti.rows)
       *reinterpret_cast<v4i*>(p.h_bf16 + (int64_t)(ti.row0 + m) * I + (int64_t)ti.nt * 128 + 8 * q) =
@@ -673,7 +683,7 @@ int launch_moe_bf16(const MoeArgs& p, const gbw_act* a, const gbw_weight* w, int
   q.a_ts = a->tensor_scale;
   q.w_ts = w->tensor_scale;
   q.ts_per = w->ts_per_expert;
-  hipLaunchKernelGGL(k_moe_e4m3, dim3((unsigned)grid), dim3(kMoeThreads), 0, st, q);
+  hipLaunchKernelGGL(k_moe_e4m3, dim3((unsigned)grid), dim3(kFp4Threads), 0, st, q);
   return check_launch("moe_grouped_gemm(e4m3)");
 }
 
