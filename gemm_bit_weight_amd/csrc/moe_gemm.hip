@@ -74,11 +74,24 @@ struct TileInfo {
   int row0, rows;  // first pair of the tile, valid rows
 };
 
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
+// 32-row bands (0, 1 or 2) of wave row wm (rows 64*wm .. 64*wm+63) that hold
+// pairs; the value is the same in every lane, and is made a scalar so that a
+// branch on it is a scalar branch
+__device__ __forceinline__ int band_count(int rows, int wm) {
+  const int r = rows - 64 * wm;
+  return __builtin_amdgcn_readfirstlane(r >= 64 ? 2 : (r > 32 ? 2 : (r > 0 ? 1 : 0)));
+}
+
 // Logical tile of this workgroup: XCD-aware remap, then (expert, m tile, n tile).
+// Workgroup b runs on XCD b % 8; the tiles that exist (known only here, from
+// expert_offsets) are split into 8 equal runs of consecutive logical tiles, one
+// per XCD, so every XCD gets the same share and its experts stay in its L2.
 __device__ __forceinline__ bool find_tile(const MoeArgs& p, TileInfo& ti, int* scan) {
-  const int G = gridDim.x;
-  const int per = (G + 7) / 8;
-  const int L = (blockIdx.x % 8) * per + blockIdx.x / 8;
   const int tid = threadIdx.x;
   const bool mine = tid < kMoeThreads;  // the first 256 threads own the scan
   int cnt = 0;
@@ -93,8 +106,12 @@ __device__ __forceinline__ bool find_tile(const MoeArgs& p, TileInfo& ti, int* s
   }
   // scan[e] = m tiles of experts 0..e (inclusive)
   const int mt_total = scan[kMoeThreads - 1];
+  const int valid = mt_total * p.n_tiles;
+  const int per = (valid + 7) / 8;
+  const int k = blockIdx.x / 8;
+  const int L = (blockIdx.x % 8) * per + k;
+  if (k >= per || L >= valid) return false;
   const int lm = L / p.n_tiles;  // logical m tile
-  if (lm >= mt_total) return false;
   __shared__ int s_e;
   if (tid < p.E) {
     const int lo = tid ? scan[tid - 1] : 0;
@@ -314,7 +331,7 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
   uint32_t psc;
   v4i pl;
   const int last = steps - 1;
-  auto gload = [&](int s) {
+  auto gload = [&](int s) __attribute__((always_inline)) {
     s = s < last ? s : last;
     const int64_t kb = (int64_t)s * 64;
 #pragma unroll
@@ -330,7 +347,7 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
     }
   };
   // stage k's registers -> LDS buffer k&1 (tables of stage k+1 -> table buffer (k+1)&1)
-  auto lstore = [&](int k) {
+  auto lstore = [&](int k) __attribute__((always_inline)) {
     const int buf = k & 1;
 #pragma unroll
     for (int u = 0; u < 2; ++u) *reinterpret_cast<v4i*>(&sA[buf][(ar + 128 * u) * kRowB + 16 * ac]) = pa[u];
@@ -346,7 +363,7 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
     }
   };
   // VQ: expand this thread's 16 indices of stage k into 32 bytes of E2M1 codes
-  auto vq_expand = [&](int k) {
+  auto vq_expand = [&](int k) __attribute__((always_inline)) {
     const int buf = k & 1;
     const int row = tid >> 1, half = tid & 1;  // half = 64-element half of the stage = QBlock column
     const uint16_t* lut = &sLut[buf][(((row >> 6) << 1) + half) * 256];
@@ -374,9 +391,10 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
   for (int j = 0; j < 4; ++j)
     brow[j] = p.stage == GBW_MOE_GATEUP_SWIGLU ? (j < 2 ? 64 * wn + 32 * j : 128 + 64 * wn + 32 * (j - 2))
                                                : 128 * wn + 32 * j;
-  // 32-row bands of this wave that hold pairs (the last tile of an expert is
-  // usually partly empty: its waves skip the empty bands' MFMAs)
-  const bool band0 = 64 * wm < ti.rows, band1 = 64 * wm + 32 < ti.rows;
+  // number of this wave's 32-row bands that hold pairs (the last tile of an
+  // expert is usually partly empty); the K loop is instantiated per count, so
+  // the MFMA sequence carries no branch and the empty bands cost nothing
+  const int nband = band_count(ti.rows, wm);
 
   // prologue: stage 0 (and the tables of stages 0 and 1) in LDS, stage 1 in registers
   if (WF == W_VQ && tid < 256) {
@@ -390,15 +408,14 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
   gload(1);
   __syncthreads();
 
-  for (int s = 0; s < steps; ++s) {
-    const int buf = s & 1;
-    lstore(s + 1);
-    if (WF == W_VQ) vq_expand(s + 1);
-    gload(s + 2);
+  // MFMAs of one stage from LDS buffer buf: all fragments of a 64-element
+  // step are read first, then the NB x 4 MFMAs
+  auto mma = [&](int buf, auto nb) __attribute__((always_inline)) {
+    constexpr int NB = decltype(nb)::value;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {  // two 64-element MFMA steps per 128-element stage
-      v4i bf[4];
-      int bsc[4];
+      v4i bf[4], af[2];
+      int bsc[4], asc[2];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int row = brow[j] + l32;
@@ -406,19 +423,34 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
         bsc[j] = (int)((sBs[buf][row] >> (8 * (2 * t + g2))) & 0xFFu);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if (i == 0 ? !band0 : !band1) continue;
+      for (int i = 0; i < NB; ++i) {
         const int row = 64 * wm + 32 * i + l32;
-        const v4i af = *reinterpret_cast<const v4i*>(&sA[buf][row * kRowB + 32 * t + 16 * g2]);
-        const int asc = (int)((sAs[buf][row] >> (8 * (2 * t + g2))) & 0xFFu);
+        af[i] = *reinterpret_cast<const v4i*>(&sA[buf][row * kRowB + 32 * t + 16 * g2]);
+        asc[i] = (int)((sAs[buf][row] >> (8 * (2 * t + g2))) & 0xFFu);
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen8(af), widen8(bf[j]), acc[i][j], 4, 4, 0,
-                                                                       asc, 0, bsc[j]);
-      }
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen8(af[i]), widen8(bf[j]), acc[i][j], 4, 4,
+                                                                       0, asc[i], 0, bsc[j]);
     }
-    __syncthreads();
-  }
+  };
+  auto kloop = [&](auto nb) __attribute__((always_inline)) {
+    for (int s = 0; s < steps; ++s) {
+      lstore(s + 1);
+      if (WF == W_VQ) vq_expand(s + 1);
+      gload(s + 2);
+      mma(s & 1, nb);
+      __syncthreads();
+    }
+  };
+  if (nband == 2)
+    kloop(IntC<2>{});
+  else if (nband == 1)
+    kloop(IntC<1>{});
+  else
+    kloop(IntC<0>{});
 
   // ---------------------------------------------------------------------
   // epilogues; acc[i][j][r] is row 64*wm + 32*i + 8*(r/4) + 4*g2 + r%4 of the
@@ -586,20 +618,20 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_e4m3(const MoeArgs p) {
     rc = p.w_codes + wr * (K / 2);
     rs = p.w_scales + wr * (K / 16);
   }
+  // LDS row of this thread in buffer 0; buffer 1 is kMoeBM * kRowH bytes further
   uint8_t* const dst0 = tid < 256 ? &sA[0][row * kRowH] : &sB[0][row * kRowH];
-  uint8_t* const dst1 = tid < 256 ? &sA[1][row * kRowH] : &sB[1][row * kRowH];
 
   v4i pc[2];
   uint32_t ps;
   const int last = steps - 1;
-  auto gload = [&](int s) {
+  auto gload = [&](int s) __attribute__((always_inline)) {
     s = s < last ? s : last;
     pc[0] = load16(rc + (int64_t)s * 32);
     pc[1] = load16(rc + (int64_t)s * 32 + 16);
     ps = *reinterpret_cast<const uint32_t*>(rs + (int64_t)s * 4);
   };
-  auto lstore = [&](int k) {
-    uint8_t* dst = (k & 1) ? dst1 : dst0;
+  auto lstore = [&](int k) __attribute__((always_inline)) {
+    uint8_t* dst = dst0 + (k & 1) * (kMoeBM * kRowH);
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       // dword d of the 32 code bytes holds elements 8d..8d+7, scale block d/2
@@ -619,32 +651,43 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_e4m3(const MoeArgs p) {
   for (int j = 0; j < 4; ++j)
     brow[j] = p.stage == GBW_MOE_GATEUP_SWIGLU ? (j < 2 ? 64 * wn + 32 * j : 128 + 64 * wn + 32 * (j - 2))
                                                : 128 * wn + 32 * j;
-  const bool band0 = 64 * wm < ti.rows, band1 = 64 * wm + 32 < ti.rows;
+  const int nband = band_count(ti.rows, wm);
 
   gload(0);
   lstore(0);
   gload(1);
   __syncthreads();
-  for (int s = 0; s < steps; ++s) {
-    const int buf = s & 1;
-    lstore(s + 1);
-    gload(s + 2);
+  auto mma = [&](int buf, auto nb) __attribute__((always_inline)) {
+    constexpr int NB = decltype(nb)::value;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {  // four 16-element MFMA steps per 64-element stage
-      v8h bf[4];
+      v8h bf[4], af[2];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         bf[j] = *reinterpret_cast<const v8h*>(&sB[buf][(brow[j] + l32) * kRowH + 32 * ks + 16 * g2]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if (i == 0 ? !band0 : !band1) continue;
-        const v8h af = *reinterpret_cast<const v8h*>(&sA[buf][(64 * wm + 32 * i + l32) * kRowH + 32 * ks + 16 * g2]);
+      for (int i = 0; i < NB; ++i)
+        af[i] = *reinterpret_cast<const v8h*>(&sA[buf][(64 * wm + 32 * i + l32) * kRowH + 32 * ks + 16 * g2]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[j], acc[i][j], 0, 0, 0);
-      }
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-    __syncthreads();
-  }
+  };
+  auto kloop = [&](auto nb) __attribute__((always_inline)) {
+    for (int s = 0; s < steps; ++s) {
+      lstore(s + 1);
+      gload(s + 2);
+      mma(s & 1, nb);
+      __syncthreads();
+    }
+  };
+  if (nband == 2)
+    kloop(IntC<2>{});
+  else if (nband == 1)
+    kloop(IntC<1>{});
+  else
+    kloop(IntC<0>{});
 
   const float sa = p.a_ts[0];
   if (p.stage == GBW_MOE_DOWN_COMBINE) {
