@@ -93,6 +93,59 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 (a in the low half), round to nearest even, in one
+// v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, v2bf));
+}
+
+// silu(g) * u = g / (1 + e^-g) * u from the hardware exp2 and reciprocal
+// (a few fp32 ulp; the result is rounded to bf16 next)
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
+// eight bf16 (four dwords, element 2i in the low half of dword i) -> eight
+// E2M1 codes (element 2i in the low nibble of byte i) of x / scale, round to
+// nearest even, saturating at 6, sign kept (v_cvt_scalef32_pk_fp4_f32 divides
+// by `scale`; every scale here is a power of two, so the quotient is exact).
+// The bf16 are widened to fp32 first (exact): the bf16-source form of the
+// instruction is not used.
+__device__ __forceinline__ uint32_t e2m1x8_from_bf16(v4i w, float scale) {
+#define GBW_CVT_PAIR(c, d) \
+  __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, __uint_as_float((uint32_t)w[d] << 16), \
+                                           __uint_as_float((uint32_t)w[d] & 0xFFFF0000u), scale, d)
+  uint32_t c = 0;
+  c = GBW_CVT_PAIR(c, 0);
+  c = GBW_CVT_PAIR(c, 1);
+  c = GBW_CVT_PAIR(c, 2);
+  c = GBW_CVT_PAIR(c, 3);
+#undef GBW_CVT_PAIR
+  return c;
+}
+
+// largest |x| of eight bf16 (as above), as the bf16 magnitude bits
+__device__ __forceinline__ uint32_t bf16x8_absmax_bits(v4i w) {
+  typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+  const v2u16 a = __builtin_bit_cast(v2u16, (uint32_t)w[0] & 0x7FFF7FFFu);
+  const v2u16 b = __builtin_bit_cast(v2u16, (uint32_t)w[1] & 0x7FFF7FFFu);
+  const v2u16 c = __builtin_bit_cast(v2u16, (uint32_t)w[2] & 0x7FFF7FFFu);
+  const v2u16 d = __builtin_bit_cast(v2u16, (uint32_t)w[3] & 0x7FFF7FFFu);
+  const v2u16 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+  return max((uint32_t)m[0], (uint32_t)m[1]);
+}
+
+// max over the four lanes of a quad (lanes 4k..4k+3), by two DPP quad permutes
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));  // lanes ^ 1
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));  // lanes ^ 2
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // misc
 // ---------------------------------------------------------------------------

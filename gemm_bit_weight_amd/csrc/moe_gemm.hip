@@ -229,6 +229,36 @@ __device__ __forceinline__ void down_epilogue(const MoeArgs& p, const TileInfo& 
   }
 }
 
+// GATEUP h tile (256 rows x 128 intermediate columns of bf16, staged in LDS
+// with rows of kHRow elements) -> h codes and E8M0 scales (and h in bf16 when
+// asked for).  Thread t handles groups t, t + 512, ... of 8 consecutive
+// elements: group g is row g / 16, columns 8 * (g % 16) ..; the four groups of
+// a 32-element block sit in one quad of lanes.  E8M0 rule as in the MX
+// quantizer: scale code = biased exponent of the block amax - 2, floored at 0.
+constexpr int kHRow = 136;  // 128 + 8 bf16: rows 4 apart fall in different banks
+
+__device__ __forceinline__ void h_tile_store(const MoeArgs& p, const TileInfo& ti, const uint16_t* sHb, int tid) {
+  const int64_t I = p.N / 2;
+#pragma unroll 2
+  for (int k = 0; k < kMoeBM * 16 / 512; ++k) {
+    const int g = tid + 512 * k;
+    const int m = g >> 4, q = g & 15;
+    const v4i w = *reinterpret_cast<const v4i*>(&sHb[m * kHRow + 8 * q]);
+    const uint32_t am = quad_max_u32(bf16x8_absmax_bits(w));
+    const uint32_t E = am >> 7;  // biased exponent field of the bf16 amax
+    const uint32_t sc = E > 2 ? E - 2 : 0;
+    const uint32_t codes = e2m1x8_from_bf16(w, e8m0_value(sc));
+    if (m < ti.rows) {
+      const int64_t row = ti.row0 + m;
+      if (p.h_codes) {
+        *reinterpret_cast<uint32_t*>(p.h_codes + row * (I / 2) + (int64_t)ti.nt * 64 + 4 * q) = codes;
+        if ((q & 3) == 0) p.h_scales[row * (I / 32) + (int64_t)ti.nt * 4 + (q >> 2)] = (uint8_t)sc;
+      }
+      if (p.h_bf16) *reinterpret_cast<v4i*>(p.h_bf16 + row * I + (int64_t)ti.nt * 128 + 8 * q) = w;
+    }
+  }
+}
+
 // 512 threads = 8 waves as 4 (rows) x 2 (columns); a wave owns a 64 x 128
 // block of the tile as 2 x 4 accumulators of v_mfma_scale_f32_32x32x64_f8f6f4
 // (on gfx950 the 32x32x64 shape runs at the full FP4 rate; 16x16x128 runs at
@@ -240,8 +270,10 @@ constexpr int kFp4Threads = 512;
 
 template <int WF>
 __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][kMoeBM * kRowB];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][kMoeBN * kRowB];
+  static_assert(kMoeBM == kMoeBN, "A and B operand tiles share one LDS array");
+  __shared__ __attribute__((aligned(16))) uint8_t sOp[2][2][kMoeBM * kRowB];  // [A, B][stage buffer]
+  uint8_t(&sA)[2][kMoeBM * kRowB] = sOp[0];
+  uint8_t(&sB)[2][kMoeBN * kRowB] = sOp[1];
   __shared__ uint32_t sAs[2][kMoeBM];
   __shared__ uint32_t sBs[2][kMoeBN];
   __shared__ __attribute__((aligned(16))) uint16_t sLut[2][WF == W_VQ ? 8 * 256 : 8];
@@ -461,48 +493,26 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
     return;
   }
 
-  // GATEUP: h = bf16(silu(g) * u) for intermediate column 64*wn + 32*jj + l32
-  // of the tile (g in acc[.][jj], u in acc[.][jj+2]); the 32 columns of a
-  // subtile form one E8M0 block, so its amax is a max over the 32 lanes.
-  __syncthreads();  // operand buffers are reused for the code tile
-  uint8_t* sH = &sA[0][0];   // [256 rows][64 bytes of codes]
-  uint8_t* sHs = &sB[0][0];  // [256 rows][4 scales]
-  const int64_t I = p.N / 2;
+  // GATEUP, in two passes over an LDS copy of the h tile:
+  //  1. h = bf16(silu(g) * u) for intermediate column 64*wn + 32*jj + l32 of
+  //     the tile (g in acc[.][jj], u in acc[.][jj+2]) -> LDS, row-major;
+  //  2. every thread takes 8 consecutive h of a row: the four threads of one
+  //     32-column E8M0 block (a quad) share their amax over DPP, then encode
+  //     and store whole dwords of codes (and h itself when asked for).
+  __syncthreads();  // operand buffers are reused for the h tile
+  static_assert(kMoeBM * kHRow * 2 <= (int)sizeof(sOp), "h tile fits the operand buffers");
+  uint16_t* const sHb = reinterpret_cast<uint16_t*>(&sOp[0][0][0]);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * g2 + (r & 3);
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const float gv = acc[i][jj][r], uv = acc[i][jj + 2][r];
-        const uint32_t hb = f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * uv);
-        const float hv = bf16_to_f32(hb);
-        const int col = 64 * wn + 32 * jj + l32;  // within the tile's 128 columns
-        if (p.h_bf16 && m < ti.rows) p.h_bf16[(int64_t)(ti.row0 + m) * I + (int64_t)ti.nt * 128 + col] = (uint16_t)hb;
-        uint32_t am = __float_as_uint(hv) & 0x7FFFFFFFu;
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) am = max(am, (uint32_t)__shfl_xor((int)am, o));
-        const uint32_t sc = e8m0_scale_code(__uint_as_float(am));
-        const uint32_t c = e2m1_rne(fabsf(hv) * e8m0_inv(sc)) | ((__float_as_uint(hv) >> 28) & 8u);
-        const uint32_t partner = (uint32_t)__shfl_xor((int)c, 1);
-        if ((l32 & 1) == 0) sH[m * 64 + col / 2] = (uint8_t)(c | (partner << 4));
-        if (l32 == 0) sHs[m * 4 + col / 32] = (uint8_t)sc;
-      }
+      const uint32_t hp = cvt_pk_bf16(silu_mul(acc[i][0][r], acc[i][2][r]), silu_mul(acc[i][1][r], acc[i][3][r]));
+      sHb[m * kHRow + 64 * wn + l32] = (uint16_t)hp;
+      sHb[m * kHRow + 64 * wn + 32 + l32] = (uint16_t)(hp >> 16);
     }
   __syncthreads();
-  if (p.h_codes) {
-    for (int c = tid; c < kMoeBM * 4; c += kFp4Threads) {
-      const int m = c >> 2, q = c & 3;
-      if (m < ti.rows)
-        *reinterpret_cast<v4i*>(p.h_codes + (int64_t)(ti.row0 + m) * (I / 2) + (int64_t)ti.nt * 64 + 16 * q) =
-            *reinterpret_cast<const v4i*>(&sH[m * 64 + 16 * q]);
-    }
-    for (int m = tid; m < kMoeBM; m += kFp4Threads)
-      if (m < ti.rows)
-        *reinterpret_cast<uint32_t*>(p.h_scales + (int64_t)(ti.row0 + m) * (I / 32) + (int64_t)ti.nt * 4) =
-            *reinterpret_cast<const uint32_t*>(&sHs[m * 4]);
-  }
+  h_tile_store(p, ti, sHb, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -698,18 +708,17 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_e4m3(const MoeArgs p) {
   // GATEUP: h = bf16(silu(g) * u), staged in LDS (the A buffers) for coalesced stores
   const float sg = sa * p.w_ts[(int64_t)ti.e * p.ts_per];
   const float su = sa * p.w_ts[(int64_t)ti.e * p.ts_per + (p.ts_per > 1 ? 1 : 0)];
-  uint16_t* sH = reinterpret_cast<uint16_t*>(&sA[0][0]);  // [256][128] bf16 = 64 KiB
+  static_assert(kMoeBM * kHRow * 2 <= (int)sizeof(sA), "h tile fits the A buffers");
+  uint16_t* sH = reinterpret_cast<uint16_t*>(&sA[0][0]);  // [256][kHRow] bf16
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * g2 + (r & 3);
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const float gv = acc[i][jj][r] * sg, uv = acc[i][jj + 2][r] * su;
-        const float h = gv / (1.0f + expf(-gv)) * uv;
-        sH[m * 128 + 64 * wn + 32 * jj + l32] = (uint16_t)f32_to_bf16_rne(h);
-      }
+      const uint32_t hp = cvt_pk_bf16(silu_mul(acc[i][0][r] * sg, acc[i][2][r] * su),
+                                      silu_mul(acc[i][1][r] * sg, acc[i][3][r] * su));
+      sH[m * kHRow + 64 * wn + l32] = (uint16_t)hp;
+      sH[m * kHRow + 64 * wn + 32 + l32] = (uint16_t)(hp >> 16);
     }
   __syncthreads();
   const int64_t I = p.N / 2;
@@ -717,7 +726,7 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_e4m3(const MoeArgs p) {
     const int m = c >> 4, q = c & 15;
     if (m < ti.rows)
       *reinterpret_cast<v4i*>(p.h_bf16 + (int64_t)(ti.row0 + m) * I + (int64_t)ti.nt * 128 + 8 * q) =
-          *reinterpret_cast<const v4i*>(&sH[m * 128 + 8 * q]);
+          *reinterpret_cast<const v4i*>(&sH[m * kHRow + 8 * q]);
   }
 }
 
