@@ -1,10 +1,13 @@
-// Grouped expert GEMMs of the routed FFN on CDNA4 scaled MFMA (FP4 x FP4).
+// Grouped expert GEMMs of the routed FFN on CDNA4 matrix cores.
 //
 //  GATEUP: for every pair p = (token t, expert e), g and u = deq(Xq[t]) W_e^T
 //          over the fused [2I][H] gate/up weight (gate rows first), then
-//          h = bf16(silu(g) * u) and its MXFP4 (E8M0-B32) requantization --
-//          all in the epilogue, so h never exists in a wider format in HBM.
-//  DOWN:   y[t] += topk_w[t][j] * deq(Hq[p]) W_e^T for the pair p of (t, j).
+//          h = bf16(silu(g) * u) and (FP4 path) its MXFP4 (E8M0-B32)
+//          requantization -- all in the epilogue, so h never exists in a
+//          wider format in HBM.
+//  DOWN:   o_p = deq(Hq[p]) W_e^T for every pair, written once to row p of a
+//          pair-major slot buffer; a combine kernel forms
+//          y[t] = sum_j topk_w[t][j] * o_{pair_pos[t][j]} in slot order.
 //
 // FFN form: "PRQuant: Permutation Residual Quantization for Low-Overhead
 // Inference", §4 Eq. (1) (the gated MLP, applied to each routed expert;
@@ -15,28 +18,29 @@
 //    index is expanded through its QBlock's 256-entry table of four E2M1 codes
 //    (the table lives in LDS, 512 bytes) into an MXFP4 operand tile in LDS;
 //    the E8M0 prescales are the operand's block scales.  No wider copy of the
-//    weights exists anywhere, in HBM or on chip.
+//    weights exists anywhere, in HBM or on chip;
+//  * E4M3-B16 + FP32 tensor scale: exact decode to fp16 tiles, fp16 MFMA.
 //
-// Work decomposition: one workgroup per 256 x 256 output tile of one expert: 256 pairs (rows) x 256 weight rows.  The tile list is
+// Work decomposition: one workgroup per output tile of one expert (256 pairs
+// x 128 weight rows for FP4, 256 x 256 for E4M3).  The tile list is
 // expert-major (m tiles, then n tiles) and is recovered by every workgroup
 // from expert_offsets with a block scan; consecutive logical tiles are placed
 // on the same XCD so the experts an XCD works on stay in its L2.  K advances
-// 128 elements per stage (one scaled MFMA step), double-buffered in LDS; the
-// next stage's global loads are in flight while the current stage's 64 MFMAs
-// per wave run.  LDS rows are 80 bytes (64 of data + 16 of padding) so the 16
-// lanes reading one MFMA fragment hit distinct banks.
+// one stage at a time, double-buffered in LDS; the next stage's global loads
+// are in flight while the current stage's MFMAs run.  LDS operand rows carry
+// 16 bytes of padding so the 16 lanes reading one MFMA fragment hit distinct
+// banks.
 //
-// For GATEUP the 256 weight rows of a tile are 128 gate rows and the 128 up
-// rows of the same intermediate columns, arranged so that each wave holds g
-// and u of the same (row, column) in its own accumulators: SwiGLU and the
-// requantization need no data exchange beyond a 16-lane max for each block
-// amax.
+// For GATEUP the weight rows of a tile are gate rows and the up rows of the
+// same intermediate columns, arranged so that each wave holds g and u of the
+// same (row, column) in its own accumulators.
 #include "common.hpp"
 
 namespace gbw {
 
-constexpr int kMoeBM = 256, kMoeBN = 256, kMoeThreads = 256;
-constexpr int kRowB = 80;  // LDS bytes per operand row per stage
+constexpr int kMoeBM = 256;       // pairs (A rows) per tile
+constexpr int kMoeThreads = 256;  // threads that run the tile-list scan (every kernel has at least this many)
+constexpr int kRowB = 80;         // LDS bytes per FP4 operand row per stage (64 of data + 16 of padding)
 constexpr int kMaxMoeExperts = 256;
 
 enum WFmt { W_MX = 0, W_VQ = 1 };
@@ -65,7 +69,7 @@ struct MoeArgs {
   uint8_t* h_codes;        // GATEUP: [P][I/2] or null
   uint8_t* h_scales;       // GATEUP: [P][I/32] or null
   float* y;                // DOWN: [T][H]
-  void* slots;             // DOWN: [T][topk][H] bf16 or fp32 per-pair outputs, or null (atomics into y)
+  void* slots;             // DOWN: [P][H] bf16 or fp32 per-pair outputs (pair-major), or null (atomics into y)
   int32_t slots_f32;       // 1: fp32 slots, 0: bf16 slots
 };
 
@@ -126,20 +130,10 @@ __device__ __forceinline__ bool find_tile(const MoeArgs& p, TileInfo& ti, int* s
   return true;
 }
 
-// One pair's output element: into its token's slot of the slot buffer (the
-// combine kernel weights and sums the slots), or, without a slot buffer,
-// weighted straight into y with an fp32 atomic.
-__device__ __forceinline__ void store_pair_out(const MoeArgs& p, int tok, int slot, float w, int64_t n, float v) {
-  const int64_t H = p.N;
-  if (p.slots) {
-    const int64_t i = ((int64_t)tok * p.topk + slot) * H + n;
-    if (p.slots_f32)
-      reinterpret_cast<float*>(p.slots)[i] = v;
-    else
-      reinterpret_cast<uint16_t*>(p.slots)[i] = (uint16_t)f32_to_bf16_rne(v);
-  } else {
-    unsafeAtomicAdd(p.y + (int64_t)tok * H + n, w * v);
-  }
+// One pair's output element on the atomic path (no slot buffer): weighted
+// straight into y[token] with an fp32 atomic.
+__device__ __forceinline__ void atomic_pair_out(const MoeArgs& p, int tok, float w, int64_t n, float v) {
+  unsafeAtomicAdd(p.y + (int64_t)tok * p.N + n, w * v);
 }
 
 __device__ __forceinline__ v8i widen8(v4i x) {
@@ -155,27 +149,33 @@ __device__ __forceinline__ v8i widen8(v4i x) {
   return r;
 }
 
-// B-tile row j (0..255) -> weight row within the expert.
+// Weight row within the expert of row j (0 .. BN-1) of B tile nt.  GATEUP
+// tiles hold BN/2 gate rows and the BN/2 up rows of the same intermediate
+// columns (gate rows first in the fused [2I][H] weight).
+template <int BN>
 __device__ __forceinline__ int64_t b_row(const MoeArgs& p, int nt, int j) {
   if (p.stage == GBW_MOE_GATEUP_SWIGLU) {
     const int64_t I = p.N / 2;
-    const int64_t i0 = (int64_t)nt * (kMoeBN / 2);
-    return j < kMoeBN / 2 ? i0 + j : I + i0 + (j - kMoeBN / 2);
+    const int64_t i0 = (int64_t)nt * (BN / 2);
+    return j < BN / 2 ? i0 + j : I + i0 + (j - BN / 2);
   }
-  return (int64_t)nt * kMoeBN + j;
+  return (int64_t)nt * BN + j;
 }
 
-// DOWN epilogue shared by the expert kernels (8 waves of 64 x 128, 32x32
+// DOWN epilogue shared by the expert kernels (waves of 64 x 128, 32x32
 // accumulators): acc[i][j][r] is row 64*wm + 32*i + 8*(r/4) + 4*(lane/32) +
-// r%4 of the tile and column brow[j] + lane%32 of the B tile; `scale`
-// multiplies every output (the tensor scales of E4M3-B16, 1 otherwise).
-// With a slot buffer each wave stages its block in LDS, 16 rows at a time
-// (8 KiB at most; waves 0-3 in stgA, 4-7 in stgB, both free after the main
-// loop's last barrier), then writes whole 16-byte pieces of output rows.
-__device__ __forceinline__ void down_epilogue(const MoeArgs& p, const TileInfo& ti, const v16f (&acc)[2][4],
-                                              const int (&brow)[4], int wave, int lane, float scale, uint8_t* stgA,
-                                              uint8_t* stgB, const int* s_tok, const int* s_slot, const float* s_w) {
-  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, g2 = lane >> 5;
+// r%4 of the tile and column 128*wn + 32*j + lane%32 of the BN-column tile;
+// `scale` multiplies every output (the tensor scales of E4M3-B16, 1
+// otherwise).  With a slot buffer (pair-major [P][H]: the output row of pair
+// p is row p) each wave stages its block in LDS, 16 rows at a time (8 KiB at
+// most, at stg + 8 KiB * its wave index; the operand buffers are free after
+// the K loop's last barrier), then writes whole 16-byte pieces of rows.
+template <int BN>
+__device__ __forceinline__ void down_epilogue(const MoeArgs& p, const TileInfo& ti, const v16f (&acc)[2][4], int wm,
+                                              int wn, int lane, float scale, uint8_t* stg, const int* s_tok,
+                                              const float* s_w) {
+  const int l32 = lane & 31, g2 = lane >> 5;
+  const int64_t col0 = (int64_t)ti.nt * BN + 128 * wn;
   if (!p.slots) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -184,14 +184,12 @@ __device__ __forceinline__ void down_epilogue(const MoeArgs& p, const TileInfo& 
         const int m = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * g2 + (r & 3);
         if (m >= ti.rows) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          store_pair_out(p, s_tok[m], s_slot[m], s_w[m], (int64_t)ti.nt * kMoeBN + brow[j] + l32,
-                         scale * acc[i][j][r]);
+        for (int j = 0; j < 4; ++j) atomic_pair_out(p, s_tok[m], s_w[m], col0 + 32 * j + l32, scale * acc[i][j][r]);
       }
     return;
   }
   const int esz = p.slots_f32 ? 4 : 2;
-  uint8_t* stg = (wave < 4 ? stgA : stgB) + (wave & 3) * (16 * 128 * 4);
+  uint8_t* const st = stg + (wm * (BN / 128) + wn) * (16 * 128 * 4);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -201,13 +199,17 @@ __device__ __forceinline__ void down_epilogue(const MoeArgs& p, const TileInfo& 
         const int r = 8 * h + rr;
         const int mr = 8 * ((r >> 2) & 1) + 4 * g2 + (r & 3);  // row within the 16-row half
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 4; j += 2) {
           const int c = 32 * j + l32;
-          const float v = scale * acc[i][j][r];
-          if (esz == 4)
-            reinterpret_cast<float*>(stg)[mr * 128 + c] = v;
-          else
-            reinterpret_cast<uint16_t*>(stg)[mr * 128 + c] = (uint16_t)f32_to_bf16_rne(v);
+          const float v0 = scale * acc[i][j][r], v1 = scale * acc[i][j + 1][r];
+          if (esz == 4) {
+            reinterpret_cast<float*>(st)[mr * 128 + c] = v0;
+            reinterpret_cast<float*>(st)[mr * 128 + c + 32] = v1;
+          } else {
+            const uint32_t hp = cvt_pk_bf16(v0, v1);
+            reinterpret_cast<uint16_t*>(st)[mr * 128 + c] = (uint16_t)hp;
+            reinterpret_cast<uint16_t*>(st)[mr * 128 + c + 32] = (uint16_t)(hp >> 16);
+          }
         }
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
@@ -217,10 +219,8 @@ __device__ __forceinline__ void down_epilogue(const MoeArgs& p, const TileInfo& 
         const int mr = q / pieces, pc = q % pieces;
         const int m = 64 * wm + 32 * i + 16 * h + mr;
         if (m < ti.rows) {
-          const int64_t col0 = (int64_t)ti.nt * kMoeBN + 128 * wn;
-          uint8_t* dst = reinterpret_cast<uint8_t*>(p.slots) +
-                         (((int64_t)s_tok[m] * p.topk + s_slot[m]) * p.N + col0) * esz + pc * 16;
-          *reinterpret_cast<v4i*>(dst) = *reinterpret_cast<const v4i*>(stg + mr * 128 * esz + pc * 16);
+          uint8_t* dst = reinterpret_cast<uint8_t*>(p.slots) + ((int64_t)(ti.row0 + m) * p.N + col0) * esz + pc * 16;
+          *reinterpret_cast<v4i*>(dst) = *reinterpret_cast<const v4i*>(st + mr * 128 * esz + pc * 16);
         }
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -229,21 +229,33 @@ __device__ __forceinline__ void down_epilogue(const MoeArgs& p, const TileInfo& 
   }
 }
 
-// GATEUP h tile (256 rows x 128 intermediate columns of bf16, staged in LDS
-// with rows of kHRow elements) -> h codes and E8M0 scales (and h in bf16 when
-// asked for).  Thread t handles groups t, t + 512, ... of 8 consecutive
-// elements: group g is row g / 16, columns 8 * (g % 16) ..; the four groups of
-// a 32-element block sit in one quad of lanes.  E8M0 rule as in the MX
-// quantizer: scale code = biased exponent of the block amax - 2, floored at 0.
-constexpr int kHRow = 136;  // 128 + 8 bf16: rows 4 apart fall in different banks
+// FP4 experts.  A workgroup of 2*BN threads = BN/32 waves computes a tile of
+// 256 pairs x BN weight rows (BN = 256: 8 waves as 4 x 2, one workgroup per
+// CU; BN = 128: 4 waves as 4 x 1, two workgroups per CU, so one workgroup's
+// prologue, barriers and epilogue overlap the other's MFMAs).  A wave owns a
+// 64 x 128 block as 2 x 4 accumulators of v_mfma_scale_f32_32x32x64_f8f6f4 (on
+// gfx950 the 32x32x64 shape runs at the full FP4 rate; 16x16x128 at the FP8
+// rate).  Lane l of a 32x32x64 operand holds row l % 32 and the 32 K elements
+// of block l / 32 (one E8M0 block, 16 bytes); the fp32 result holds column
+// l % 32 and rows 8*(r/4) + 4*(l/32) + r%4 in register r.
+constexpr int fp4_threads(int BN) { return 2 * BN; }
 
+// GATEUP h tile (256 rows x BN/2 intermediate columns of bf16, staged in LDS
+// with rows of BN/2 + 8 elements, so rows 4 apart fall in different banks) ->
+// h codes and E8M0 scales (and h in bf16 when asked for).  Thread t handles
+// groups t, t + 2BN, ... of 8 consecutive elements: group g is row g / (BN/16),
+// columns 8 * (g % (BN/16)) ..; the four groups of a 32-element block sit in
+// one quad of lanes.  E8M0 rule as in the MX quantizer: scale code = biased
+// exponent of the block amax - 2, floored at 0.
+template <int BN>
 __device__ __forceinline__ void h_tile_store(const MoeArgs& p, const TileInfo& ti, const uint16_t* sHb, int tid) {
+  constexpr int HR = BN / 2 + 8, GPR = BN / 16, NT = fp4_threads(BN);
   const int64_t I = p.N / 2;
 #pragma unroll 2
-  for (int k = 0; k < kMoeBM * 16 / 512; ++k) {
-    const int g = tid + 512 * k;
-    const int m = g >> 4, q = g & 15;
-    const v4i w = *reinterpret_cast<const v4i*>(&sHb[m * kHRow + 8 * q]);
+  for (int k = 0; k < kMoeBM * GPR / NT; ++k) {
+    const int g = tid + NT * k;
+    const int m = g / GPR, q = g % GPR;
+    const v4i w = *reinterpret_cast<const v4i*>(&sHb[m * HR + 8 * q]);
     const uint32_t am = quad_max_u32(bf16x8_absmax_bits(w));
     const uint32_t E = am >> 7;  // biased exponent field of the bf16 amax
     const uint32_t sc = E > 2 ? E - 2 : 0;
@@ -251,87 +263,82 @@ __device__ __forceinline__ void h_tile_store(const MoeArgs& p, const TileInfo& t
     if (m < ti.rows) {
       const int64_t row = ti.row0 + m;
       if (p.h_codes) {
-        *reinterpret_cast<uint32_t*>(p.h_codes + row * (I / 2) + (int64_t)ti.nt * 64 + 4 * q) = codes;
-        if ((q & 3) == 0) p.h_scales[row * (I / 32) + (int64_t)ti.nt * 4 + (q >> 2)] = (uint8_t)sc;
+        *reinterpret_cast<uint32_t*>(p.h_codes + row * (I / 2) + (int64_t)ti.nt * (BN / 4) + 4 * q) = codes;
+        if ((q & 3) == 0) p.h_scales[row * (I / 32) + (int64_t)ti.nt * (BN / 64) + (q >> 2)] = (uint8_t)sc;
       }
-      if (p.h_bf16) *reinterpret_cast<v4i*>(p.h_bf16 + row * I + (int64_t)ti.nt * 128 + 8 * q) = w;
+      if (p.h_bf16) *reinterpret_cast<v4i*>(p.h_bf16 + row * I + (int64_t)ti.nt * (BN / 2) + 8 * q) = w;
     }
   }
 }
 
-// 512 threads = 8 waves as 4 (rows) x 2 (columns); a wave owns a 64 x 128
-// block of the tile as 2 x 4 accumulators of v_mfma_scale_f32_32x32x64_f8f6f4
-// (on gfx950 the 32x32x64 shape runs at the full FP4 rate; 16x16x128 runs at
-// the FP8 rate).  Lane l of a 32x32x64 operand holds row l % 32 and the 32 K
-// elements of block l / 32 (one E8M0 block, 16 bytes); the fp32 result holds
-// column l % 32 and rows 8*(r/4) + 4*(l/32) + r%4 in register r.  Two waves
-// per SIMD let one wave's LDS reads and barriers overlap the other's MFMAs.
-constexpr int kFp4Threads = 512;
-
-template <int WF>
-__global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
-  static_assert(kMoeBM == kMoeBN, "A and B operand tiles share one LDS array");
-  __shared__ __attribute__((aligned(16))) uint8_t sOp[2][2][kMoeBM * kRowB];  // [A, B][stage buffer]
-  uint8_t(&sA)[2][kMoeBM * kRowB] = sOp[0];
-  uint8_t(&sB)[2][kMoeBN * kRowB] = sOp[1];
+template <int WF, int BN>
+__global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p) {
+  constexpr int NT = fp4_threads(BN), WN = BN / 128;    // threads, wave columns
+  constexpr int kABuf = kMoeBM * kRowB, kBBuf = BN * kRowB;  // bytes per stage buffer
+  constexpr int NA = kMoeBM * 4 / NT;                   // 16-byte A chunks per thread per stage
+  constexpr int NLUT = BN / 32;                         // QBlock tables per stage (2 per 64 weight rows)
+  constexpr int SB = BN > 256 ? BN : 256;               // B scale slots (>= BN; the extra ones are never read)
+  __shared__ __attribute__((aligned(16))) uint8_t sOp[2 * kABuf + 2 * kBBuf];
   __shared__ uint32_t sAs[2][kMoeBM];
-  __shared__ uint32_t sBs[2][kMoeBN];
-  __shared__ __attribute__((aligned(16))) uint16_t sLut[2][WF == W_VQ ? 8 * 256 : 8];
+  __shared__ uint32_t sBs[2][SB];
+  __shared__ __attribute__((aligned(16))) uint16_t sLut[2][WF == W_VQ ? NLUT * 256 : 4];
   __shared__ int scan[kMoeThreads];
   __shared__ int s_tok[kMoeBM];
   __shared__ float s_w[kMoeBM];
-  __shared__ int s_slot[kMoeBM];
+  uint8_t* const sA0 = sOp;              // A buffer b at sA0 + b * kABuf
+  uint8_t* const sB0 = sOp + 2 * kABuf;  // B buffer b at sB0 + b * kBBuf
 
   TileInfo ti;
   if (!find_tile(p, ti, scan)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, g2 = lane >> 5;
   const int64_t K = p.K;
   const int steps = (int)(K / 128);
+  const bool gate = p.stage == GBW_MOE_GATEUP_SWIGLU;
 
-  // per-row metadata: token (gather / combine) and routing weight
-  for (int r = tid; r < kMoeBM; r += kFp4Threads) {
-    int tok = 0, slot = 0;
+  // per-row metadata: the token of each pair (the A row of the gate/up
+  // gather) and, for the atomic down path only, its routing weight
+  for (int r = tid; r < kMoeBM; r += NT) {
+    int tok = 0;
     float wt = 0.f;
     if (r < ti.rows) {
       const int pr = ti.row0 + r;
       tok = p.pair_token[pr];
-      if (p.stage == GBW_MOE_DOWN_COMBINE)
+      if (!gate && !p.slots)
         for (int j = 0; j < p.topk; ++j)
-          if (p.pair_pos[(int64_t)tok * p.topk + j] == pr) {
-            wt = p.topk_w[(int64_t)tok * p.topk + j];
-            slot = j;
-          }
+          if (p.pair_pos[(int64_t)tok * p.topk + j] == pr) wt = p.topk_w[(int64_t)tok * p.topk + j];
     }
     s_tok[r] = tok;
     s_w[r] = wt;
-    s_slot[r] = slot;
   }
   __syncthreads();
 
   // --- fixed per-thread load assignments --------------------------------
-  // A codes: rows ar and ar + 128, 16-byte chunk ac of the 64-byte stage row;
-  // threads 0..255 load the scale dword of A row tid, 256..511 of B row tid-256
+  // A codes: rows ar + (NT/4)u, 16-byte chunk ac of the 64-byte stage row.
+  // Scales: with 512 threads, thread t loads the dword of A row t (t < 256) or
+  // of B row t - 256; with 256 threads, of A row t and of B row t % BN.
   const int ar = tid >> 2, ac = tid & 3;
-  const uint8_t* arow[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int r = ar + 128 * u;
-    const int rr = r < ti.rows ? r : ti.rows - 1;
-    const int64_t src = p.stage == GBW_MOE_GATEUP_SWIGLU ? (int64_t)s_tok[rr] : (int64_t)(ti.row0 + rr);
-    arow[u] = p.a_codes + src * (K / 2);
-  }
-  const int sr = tid & 255;
-  const uint8_t* scl;
-  if (tid < 256) {
-    const int rr = sr < ti.rows ? sr : ti.rows - 1;
-    const int64_t src = p.stage == GBW_MOE_GATEUP_SWIGLU ? (int64_t)s_tok[rr] : (int64_t)(ti.row0 + rr);
-    scl = p.a_scales + src * (K / 32);
-  } else {
-    scl = p.w_scales + ((int64_t)ti.e * p.N + b_row(p, ti.nt, sr)) * (K / 32);
-  }
   const int64_t wN = p.N;
+  auto a_src = [&](int r) __attribute__((always_inline)) {
+    const int rr = r < ti.rows ? r : ti.rows - 1;
+    return gate ? (int64_t)s_tok[rr] : (int64_t)(ti.row0 + rr);
+  };
+  const uint8_t* arow[NA];
+#pragma unroll
+  for (int u = 0; u < NA; ++u) arow[u] = p.a_codes + a_src(ar + (NT / 4) * u) * (K / 2);
+  const uint8_t* scl0;  // A scales (or, with 512 threads, B scales for t >= 256)
+  const uint8_t* scl1;  // B scales (256 threads only)
+  if (NT == 512) {
+    scl0 = tid < 256 ? p.a_scales + a_src(tid) * (K / 32)
+                     : p.w_scales + ((int64_t)ti.e * wN + b_row<BN>(p, ti.nt, tid - 256)) * (K / 32);
+    scl1 = scl0;
+  } else {
+    scl0 = p.a_scales + a_src(tid) * (K / 32);
+    scl1 = p.w_scales + ((int64_t)ti.e * wN + b_row<BN>(p, ti.nt, tid % BN)) * (K / 32);
+  }
+  uint32_t* const sdst0 = (NT == 512 && tid >= 256) ? &sBs[0][tid - 256] : &sAs[0][tid];  // buffer 1: + SB or 256
   const uint8_t* wrow[2];
   const uint8_t* vrow = nullptr;
   const uint16_t* cbase = nullptr;
@@ -339,14 +346,14 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
   if (WF == W_MX) {
 #pragma unroll
     for (int u = 0; u < 2; ++u)
-      wrow[u] = p.w_codes + ((int64_t)ti.e * wN + b_row(p, ti.nt, ar + 128 * u)) * (K / 2);
+      wrow[u] = p.w_codes + ((int64_t)ti.e * wN + b_row<BN>(p, ti.nt, ar + (NT / 4) * u)) * (K / 2);
   } else {
     // idx: row tid >> 1, 16-byte chunk tid & 1 of the 32-byte stage row
-    vrow = p.w_codes + ((int64_t)ti.e * wN + b_row(p, ti.nt, tid >> 1)) * (K / 4);
-    // LUT (threads 0..255): 16 bytes of table tid >> 5 (4 QBlock rows x 2 QBlock columns)
-    const int tb = (tid & 255) >> 5;
+    vrow = p.w_codes + ((int64_t)ti.e * wN + b_row<BN>(p, ti.nt, tid >> 1)) * (K / 4);
+    // LUT: 8 bytes of table tid >> 6 (BN/64 QBlock rows x 2 QBlock columns)
+    const int tb = tid >> 6;
     lut_kb = tb & 1;
-    const int64_t qrow = b_row(p, ti.nt, (tb >> 1) * 64) / 64;
+    const int64_t qrow = b_row<BN>(p, ti.nt, (tb >> 1) * 64) / 64;
     cbase = p.w_cb + ((int64_t)ti.e * (wN / 64) + qrow) * (K / 64) * 256;
   }
 
@@ -359,39 +366,44 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
   //   4. barrier.
   // Indices past the last stage are clamped, so the loop body has no branches
   // (the redundant work at the end hits L2 and a spare buffer).
-  v4i pa[2], pb[2];
-  uint32_t psc;
-  v4i pl;
+  v4i pa[NA], pb[2];
+  uint32_t ps0, ps1;
+  uint2 pl;
   const int last = steps - 1;
   auto gload = [&](int s) __attribute__((always_inline)) {
     s = s < last ? s : last;
     const int64_t kb = (int64_t)s * 64;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) pa[u] = load16(arow[u] + kb + 16 * ac);
-    psc = *reinterpret_cast<const uint32_t*>(scl + (int64_t)s * 4);
+    for (int u = 0; u < NA; ++u) pa[u] = load16(arow[u] + kb + 16 * ac);
+    ps0 = *reinterpret_cast<const uint32_t*>(scl0 + (int64_t)s * 4);
+    if (NT != 512) ps1 = *reinterpret_cast<const uint32_t*>(scl1 + (int64_t)s * 4);
     if (WF == W_MX) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) pb[u] = load16(wrow[u] + kb + 16 * ac);
     } else {
       pb[0] = load16(vrow + (int64_t)s * 32 + 16 * (tid & 1));
       const int sl = s + 1 < last ? s + 1 : last;  // tables run one stage ahead
-      pl = load16(cbase + ((int64_t)sl * 2 + lut_kb) * 256 + (tid & 31) * 8);
+      pl = *reinterpret_cast<const uint2*>(cbase + ((int64_t)sl * 2 + lut_kb) * 256 + (tid & 63) * 4);
     }
   };
   // stage k's registers -> LDS buffer k&1 (tables of stage k+1 -> table buffer (k+1)&1)
   auto lstore = [&](int k) __attribute__((always_inline)) {
     const int buf = k & 1;
+    uint8_t* const a = sA0 + buf * kABuf;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) *reinterpret_cast<v4i*>(&sA[buf][(ar + 128 * u) * kRowB + 16 * ac]) = pa[u];
-    if (tid < 256)
-      sAs[buf][sr] = psc;
-    else
-      sBs[buf][sr] = psc;
+    for (int u = 0; u < NA; ++u) *reinterpret_cast<v4i*>(a + (ar + (NT / 4) * u) * kRowB + 16 * ac) = pa[u];
+    if (NT == 512) {
+      sdst0[buf * (tid >= 256 ? SB : kMoeBM)] = ps0;
+    } else {
+      sAs[buf][tid] = ps0;
+      sBs[buf][tid] = ps1;
+    }
     if (WF == W_MX) {
+      uint8_t* const b = sB0 + buf * kBBuf;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) *reinterpret_cast<v4i*>(&sB[buf][(ar + 128 * u) * kRowB + 16 * ac]) = pb[u];
-    } else if (tid < 256) {
-      *reinterpret_cast<v4i*>(&sLut[buf ^ 1][(tid >> 5) * 256 + (tid & 31) * 8]) = pl;
+      for (int u = 0; u < 2; ++u) *reinterpret_cast<v4i*>(b + (ar + (NT / 4) * u) * kRowB + 16 * ac) = pb[u];
+    } else {
+      *reinterpret_cast<uint2*>(&sLut[buf ^ 1][(tid >> 6) * 256 + (tid & 63) * 4]) = pl;
     }
   };
   // VQ: expand this thread's 16 indices of stage k into 32 bytes of E2M1 codes
@@ -406,7 +418,7 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
       o[2 * d] = (uint32_t)lut[w & 0xFF] | ((uint32_t)lut[(w >> 8) & 0xFF] << 16);
       o[2 * d + 1] = (uint32_t)lut[(w >> 16) & 0xFF] | ((uint32_t)lut[w >> 24] << 16);
     }
-    uint8_t* dst = &sB[buf][row * kRowB + 32 * half];
+    uint8_t* dst = sB0 + buf * kBBuf + row * kRowB + 32 * half;
     *reinterpret_cast<v4i*>(dst) = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
     *reinterpret_cast<v4i*>(dst + 16) = v4i{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
   };
@@ -417,21 +429,22 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
-  // B-tile rows of this wave's four 32-column subtiles
+  // B-tile rows of this wave's four 32-row subtiles (GATEUP: j = 0, 1 gate,
+  // j = 2, 3 the up rows of the same intermediate columns 64*wn + 32*(j%2) ..)
   int brow[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    brow[j] = p.stage == GBW_MOE_GATEUP_SWIGLU ? (j < 2 ? 64 * wn + 32 * j : 128 + 64 * wn + 32 * (j - 2))
-                                               : 128 * wn + 32 * j;
+    brow[j] = gate ? (j < 2 ? 64 * wn + 32 * j : BN / 2 + 64 * wn + 32 * (j - 2)) : 128 * wn + 32 * j;
+
   // number of this wave's 32-row bands that hold pairs (the last tile of an
   // expert is usually partly empty); the K loop is instantiated per count, so
   // the MFMA sequence carries no branch and the empty bands cost nothing
   const int nband = band_count(ti.rows, wm);
 
   // prologue: stage 0 (and the tables of stages 0 and 1) in LDS, stage 1 in registers
-  if (WF == W_VQ && tid < 256) {
-    const v4i t0 = load16(cbase + (int64_t)lut_kb * 256 + (tid & 31) * 8);
-    *reinterpret_cast<v4i*>(&sLut[0][(tid >> 5) * 256 + (tid & 31) * 8]) = t0;
+  if (WF == W_VQ) {
+    const uint2 t0 = *reinterpret_cast<const uint2*>(cbase + (int64_t)lut_kb * 256 + (tid & 63) * 4);
+    *reinterpret_cast<uint2*>(&sLut[0][(tid >> 6) * 256 + (tid & 63) * 4]) = t0;
   }
   gload(0);
   lstore(0);
@@ -444,6 +457,8 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
   // step are read first, then the NB x 4 MFMAs
   auto mma = [&](int buf, auto nb) __attribute__((always_inline)) {
     constexpr int NB = decltype(nb)::value;
+    const uint8_t* const a = sA0 + buf * kABuf;
+    const uint8_t* const b = sB0 + buf * kBBuf;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {  // two 64-element MFMA steps per 128-element stage
       v4i bf[4], af[2];
@@ -451,13 +466,13 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int row = brow[j] + l32;
-        bf[j] = *reinterpret_cast<const v4i*>(&sB[buf][row * kRowB + 32 * t + 16 * g2]);
+        bf[j] = *reinterpret_cast<const v4i*>(b + row * kRowB + 32 * t + 16 * g2);
         bsc[j] = (int)((sBs[buf][row] >> (8 * (2 * t + g2))) & 0xFFu);
       }
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         const int row = 64 * wm + 32 * i + l32;
-        af[i] = *reinterpret_cast<const v4i*>(&sA[buf][row * kRowB + 32 * t + 16 * g2]);
+        af[i] = *reinterpret_cast<const v4i*>(a + row * kRowB + 32 * t + 16 * g2);
         asc[i] = (int)((sAs[buf][row] >> (8 * (2 * t + g2))) & 0xFFu);
       }
 #pragma unroll
@@ -485,34 +500,51 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
     kloop(IntC<0>{});
 
   // ---------------------------------------------------------------------
-  // epilogues; acc[i][j][r] is row 64*wm + 32*i + 8*(r/4) + 4*g2 + r%4 of the
-  // tile and column brow[j] + l32 of the B tile
+  // epilogues; acc[i][j][r] is row 64*wm + 32*i + 8*(r/4) + 4*g2 + r%4 of
+  // the tile and row brow[j] + l32 of the B tile.  The last barrier of the
+  // K loop has freed the operand buffers.
   // ---------------------------------------------------------------------
-  if (p.stage == GBW_MOE_DOWN_COMBINE) {
-    down_epilogue(p, ti, acc, brow, wave, lane, 1.0f, &sA[0][0], &sB[0][0], s_tok, s_slot, s_w);
+  if (!gate) {
+    static_assert(fp4_threads(BN) / 64 * 8192 <= 2 * kABuf + 2 * kBBuf, "down staging fits the operand buffers");
+    down_epilogue<BN>(p, ti, acc, wm, wn, lane, 1.0f, sA0, s_tok, s_w);
     return;
   }
 
   // GATEUP, in two passes over an LDS copy of the h tile:
   //  1. h = bf16(silu(g) * u) for intermediate column 64*wn + 32*jj + l32 of
   //     the tile (g in acc[.][jj], u in acc[.][jj+2]) -> LDS, row-major;
-  //  2. every thread takes 8 consecutive h of a row: the four threads of one
-  //     32-column E8M0 block (a quad) share their amax over DPP, then encode
-  //     and store whole dwords of codes (and h itself when asked for).
-  __syncthreads();  // operand buffers are reused for the h tile
-  static_assert(kMoeBM * kHRow * 2 <= (int)sizeof(sOp), "h tile fits the operand buffers");
-  uint16_t* const sHb = reinterpret_cast<uint16_t*>(&sOp[0][0][0]);
+  //  2. h_tile_store: every thread takes 8 consecutive h of a row, the four
+  //     threads of one 32-column E8M0 block (a quad) share their amax over
+  //     DPP, then encode and store whole dwords of codes.
+  constexpr int HR = BN / 2 + 8;
+  static_assert(kMoeBM * HR * 2 <= (int)sizeof(sOp), "h tile fits the operand buffers");
+  uint16_t* const sHb = reinterpret_cast<uint16_t*>(sA0);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * g2 + (r & 3);
       const uint32_t hp = cvt_pk_bf16(silu_mul(acc[i][0][r], acc[i][2][r]), silu_mul(acc[i][1][r], acc[i][3][r]));
-      sHb[m * kHRow + 64 * wn + l32] = (uint16_t)hp;
-      sHb[m * kHRow + 64 * wn + 32 + l32] = (uint16_t)(hp >> 16);
+      sHb[m * HR + 64 * wn + l32] = (uint16_t)hp;
+      sHb[m * HR + 64 * wn + 32 + l32] = (uint16_t)(hp >> 16);
     }
   __syncthreads();
-  h_tile_store(p, ti, sHb, tid);
+  h_tile_store<BN>(p, ti, sHb, tid);
+}
+
+template <int WF>
+int launch_moe_fp4(const MoeArgs& p, int bn, hipStream_t st) {
+  MoeArgs q = p;
+  q.n_tiles = (int)(p.N / bn);
+  int64_t grid = (cdiv(p.P, kMoeBM) + p.E) * q.n_tiles;
+  grid = cdiv(grid, 8) * 8;
+  if (grid > INT32_MAX) return fail(GBW_E_SHAPE, "moe_grouped_gemm: problem too large");
+  q.total_tiles = (int)grid;
+  if (bn == 256)
+    hipLaunchKernelGGL((k_moe_fp4<WF, 256>), dim3((unsigned)grid), dim3(fp4_threads(256)), 0, st, q);
+  else
+    hipLaunchKernelGGL((k_moe_fp4<WF, 128>), dim3((unsigned)grid), dim3(fp4_threads(128)), 0, st, q);
+  return check_launch("moe_grouped_gemm");
 }
 
 // ---------------------------------------------------------------------------
@@ -521,7 +553,7 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
 // An E4M3-B16 element is e2m1 * s with s an E4M3 block scale: at most 6
 // significant bits and a magnitude in [2^-10, 2688], so it is exact in fp16
 // (and in bf16); both operands are decoded once per tile into fp16 LDS tiles
-// and contracted with v_mfma_f32_16x16x32_f16.  The two FP32 tensor scales
+// and contracted with v_mfma_f32_32x32x16_f16.  The two FP32 tensor scales
 // are applied to the fp32 accumulators in the epilogue.  (There is no exact
 // route through the FP4/FP8 scaled MFMA: its block scales are powers of two
 // per 32 elements, an E4M3 scale carries a 3-bit mantissa per 16.)
@@ -532,6 +564,8 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_fp4(const MoeArgs p) {
 // elements in the order 0,2,4,6,1,3,5,7; A and B are decoded alike, so the
 // MFMA pairs the same K indices.
 constexpr int kRowH = 144;  // LDS bytes per fp16 row per stage (64 elements + 16 pad)
+constexpr int kE4Threads = 512, kE4BN = 256;
+constexpr int kHRow8 = 136;  // bf16 per staged h row (128 + 8): rows 4 apart fall in different banks
 
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
@@ -573,19 +607,19 @@ __device__ __forceinline__ uint32_t e4m3_to_h2(uint32_t c) {
   return b | (b << 16);
 }
 
-// 8 waves (4 x 2) of 64 x 128 as in k_moe_fp4, v_mfma_f32_32x32x16_f16
-// (lane l: row l % 32, K elements [8*(l/32), 8*(l/32)+8) of the 16-element
-// step; on gfx950 the 32x32 shape runs at about twice the 16x16 rate).  Stage
-// = 64 K elements: threads 0..255 decode row tid of A, 256..511 row tid-256 of
-// B, into fp16 LDS rows of 128 bytes + 16 of padding.  Same single-barrier
-// pipeline: stage s+1 is decoded into LDS before the MFMAs of stage s.
-__global__ __launch_bounds__(kFp4Threads) void k_moe_e4m3(const MoeArgs p) {
+// 512 threads = 8 waves (4 x 2) of 64 x 128 over a 256 x 256 tile,
+// v_mfma_f32_32x32x16_f16 (lane l: row l % 32, K elements [8*(l/32),
+// 8*(l/32)+8) of the 16-element step; on gfx950 the 32x32 shape runs at about
+// twice the 16x16 rate).  Stage = 64 K elements: threads 0..255 decode row tid
+// of A, 256..511 row tid-256 of B, into fp16 LDS rows of 128 bytes + 16 of
+// padding.  Same single-barrier pipeline as the FP4 kernel: stage s+1 is
+// decoded into LDS before the MFMAs of stage s.
+__global__ __launch_bounds__(kE4Threads) void k_moe_e4m3(const MoeArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][kMoeBM * kRowH];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][kMoeBN * kRowH];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[2][kE4BN * kRowH];
   __shared__ int scan[kMoeThreads];
   __shared__ int s_tok[kMoeBM];
   __shared__ float s_w[kMoeBM];
-  __shared__ int s_slot[kMoeBM];
 
   TileInfo ti;
   if (!find_tile(p, ti, scan)) return;
@@ -595,22 +629,20 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_e4m3(const MoeArgs p) {
   const int64_t K = p.K;
   const int steps = (int)(K / 64);
 
-  for (int r = tid; r < kMoeBM; r += kFp4Threads) {
-    int tok = 0, slot = 0;
+  // per-row metadata: the token of each pair and, for the atomic down path
+  // only, its routing weight
+  for (int r = tid; r < kMoeBM; r += kE4Threads) {
+    int tok = 0;
     float wt = 0.f;
     if (r < ti.rows) {
       const int pr = ti.row0 + r;
       tok = p.pair_token[pr];
-      if (p.stage == GBW_MOE_DOWN_COMBINE)
+      if (p.stage == GBW_MOE_DOWN_COMBINE && !p.slots)
         for (int j = 0; j < p.topk; ++j)
-          if (p.pair_pos[(int64_t)tok * p.topk + j] == pr) {
-            wt = p.topk_w[(int64_t)tok * p.topk + j];
-            slot = j;
-          }
+          if (p.pair_pos[(int64_t)tok * p.topk + j] == pr) wt = p.topk_w[(int64_t)tok * p.topk + j];
     }
     s_tok[r] = tok;
     s_w[r] = wt;
-    s_slot[r] = slot;
   }
   __syncthreads();
 
@@ -624,7 +656,7 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_e4m3(const MoeArgs p) {
     rc = p.a_codes + src * (K / 2);
     rs = p.a_scales + src * (K / 16);
   } else {
-    const int64_t wr = (int64_t)ti.e * p.N + b_row(p, ti.nt, row);
+    const int64_t wr = (int64_t)ti.e * p.N + b_row<kE4BN>(p, ti.nt, row);
     rc = p.w_codes + wr * (K / 2);
     rs = p.w_scales + wr * (K / 16);
   }
@@ -701,15 +733,14 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_e4m3(const MoeArgs p) {
 
   const float sa = p.a_ts[0];
   if (p.stage == GBW_MOE_DOWN_COMBINE) {
-    down_epilogue(p, ti, acc, brow, wave, lane, sa * p.w_ts[(int64_t)ti.e * p.ts_per], &sA[0][0], &sB[0][0], s_tok,
-                  s_slot, s_w);
+    down_epilogue<kE4BN>(p, ti, acc, wm, wn, lane, sa * p.w_ts[(int64_t)ti.e * p.ts_per], &sA[0][0], s_tok, s_w);
     return;
   }
   // GATEUP: h = bf16(silu(g) * u), staged in LDS (the A buffers) for coalesced stores
   const float sg = sa * p.w_ts[(int64_t)ti.e * p.ts_per];
   const float su = sa * p.w_ts[(int64_t)ti.e * p.ts_per + (p.ts_per > 1 ? 1 : 0)];
-  static_assert(kMoeBM * kHRow * 2 <= (int)sizeof(sA), "h tile fits the A buffers");
-  uint16_t* sH = reinterpret_cast<uint16_t*>(&sA[0][0]);  // [256][kHRow] bf16
+  static_assert(kMoeBM * kHRow8 * 2 <= (int)sizeof(sA), "h tile fits the A buffers");
+  uint16_t* sH = reinterpret_cast<uint16_t*>(&sA[0][0]);  // [256][kHRow8] bf16
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -717,16 +748,16 @@ __global__ __launch_bounds__(kFp4Threads) void k_moe_e4m3(const MoeArgs p) {
       const int m = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * g2 + (r & 3);
       const uint32_t hp = cvt_pk_bf16(silu_mul(acc[i][0][r] * sg, acc[i][2][r] * su),
                                       silu_mul(acc[i][1][r] * sg, acc[i][3][r] * su));
-      sH[m * kHRow + 64 * wn + l32] = (uint16_t)hp;
-      sH[m * kHRow + 64 * wn + 32 + l32] = (uint16_t)(hp >> 16);
+      sH[m * kHRow8 + 64 * wn + l32] = (uint16_t)hp;
+      sH[m * kHRow8 + 64 * wn + 32 + l32] = (uint16_t)(hp >> 16);
     }
   __syncthreads();
   const int64_t I = p.N / 2;
-  for (int c = tid; c < kMoeBM * 16; c += kFp4Threads) {
+  for (int c = tid; c < kMoeBM * 16; c += kE4Threads) {
     const int m = c >> 4, q = c & 15;
     if (m < ti.rows)
       *reinterpret_cast<v4i*>(p.h_bf16 + (int64_t)(ti.row0 + m) * I + (int64_t)ti.nt * 128 + 8 * q) =
-          *reinterpret_cast<const v4i*>(&sH[m * kHRow + 8 * q]);
+          *reinterpret_cast<const v4i*>(&sH[m * kHRow8 + 8 * q]);
   }
 }
 
@@ -735,22 +766,24 @@ int launch_moe_bf16(const MoeArgs& p, const gbw_act* a, const gbw_weight* w, int
   q.a_ts = a->tensor_scale;
   q.w_ts = w->tensor_scale;
   q.ts_per = w->ts_per_expert;
-  hipLaunchKernelGGL(k_moe_e4m3, dim3((unsigned)grid), dim3(kFp4Threads), 0, st, q);
+  hipLaunchKernelGGL(k_moe_e4m3, dim3((unsigned)grid), dim3(kE4Threads), 0, st, q);
   return check_launch("moe_grouped_gemm(e4m3)");
 }
 
-// y[t][n] = sum_j topk_w[t][j] * slot[t][j][n], j = 0..topk-1 in order (a
-// fixed summation order: bitwise repeatable), eight outputs per thread.
+// y[t][n] = sum_j topk_w[t][j] * slots[pair_pos[t][j]][n], j = 0..topk-1 in
+// order (a fixed summation order: bitwise repeatable), eight outputs per
+// thread; the slot rows of a token are gathered whole-row by the pair index.
 template <bool F32>
-__global__ void k_moe_combine(const void* __restrict__ slots, const float* __restrict__ topk_w, int topk, int64_t T,
-                              int64_t H, float* __restrict__ y) {
+__global__ void k_moe_combine(const void* __restrict__ slots, const float* __restrict__ topk_w,
+                              const int32_t* __restrict__ pair_pos, int topk, int64_t T, int64_t H,
+                              float* __restrict__ y) {
   const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (i >= T * H) return;
   const int64_t t = i / H, n = i % H;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < topk; ++j) {
     const float w = topk_w[t * topk + j];
-    const int64_t base = (t * topk + j) * H + n;
+    const int64_t base = (int64_t)pair_pos[t * topk + j] * H + n;
     if (F32) {
       const v4f a = *reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(slots) + base);
       const v4f b = *reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(slots) + base + 4);
@@ -777,7 +810,7 @@ __global__ void k_moe_combine(const void* __restrict__ slots, const float* __res
 namespace gbw {
 
 size_t ws_moe_gemm(int64_t P, int64_t N, int64_t f32) {
-  // the down/combine stage: a [T][topk][H] slot buffer, bf16 (fp32 with GBW_FP32_COMBINE)
+  // the down/combine stage: a pair-major [P][H] slot buffer, bf16 (fp32 with GBW_FP32_COMBINE)
   return P > 0 && N > 0 ? (size_t)P * N * (f32 ? sizeof(float) : sizeof(uint16_t)) : 0;
 }
 
@@ -853,37 +886,39 @@ extern "C" int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const in
   p.w_scales = w->scales;
   p.w_cb = w->codebook;
   p.N = N;
-  p.n_tiles = (int)(stage == GBW_MOE_GATEUP_SWIGLU ? N / kMoeBN : N / kMoeBN);
   p.h_bf16 = out->h_bf16;
   p.h_codes = out->h_codes;
   p.h_scales = out->h_scales;
   p.y = out->y;
   p.slots = use_slots ? ws : nullptr;
   p.slots_f32 = f32c ? 1 : 0;
-  const int64_t m_tiles_max = cdiv(P, kMoeBM) + E;
-  int64_t grid = m_tiles_max * p.n_tiles;
-  grid = cdiv(grid, 8) * 8;
-  if (grid > INT32_MAX) return fail(GBW_E_SHAPE, "moe_grouped_gemm: problem too large");
-  p.total_tiles = (int)grid;
+  // every kernel below writes through these: refuse to launch without them
+  if (stage == GBW_MOE_DOWN_COMBINE ? (!p.y || (use_slots && !p.slots)) : (!p.h_codes && !p.h_bf16))
+    return fail(GBW_E_ARG, "moe_grouped_gemm: no output buffer");
   if (stage == GBW_MOE_DOWN_COMBINE && !use_slots) {
     if ((st = launch_fill_zero(out->y, T * N, s))) return st;
   }
   if (e4m3) {
+    p.n_tiles = (int)(N / kE4BN);
+    int64_t grid = (cdiv(P, kMoeBM) + E) * p.n_tiles;
+    grid = cdiv(grid, 8) * 8;
+    if (grid > INT32_MAX) return fail(GBW_E_SHAPE, "moe_grouped_gemm: problem too large");
+    p.total_tiles = (int)grid;
     st = launch_moe_bf16(p, a, w, (int)grid, s);
   } else {
-    if (w->fmt == GBW_FMT_VQ4_E8M0)
-      hipLaunchKernelGGL(k_moe_fp4<W_VQ>, dim3((unsigned)grid), dim3(kFp4Threads), 0, s, p);
-    else
-      hipLaunchKernelGGL(k_moe_fp4<W_MX>, dim3((unsigned)grid), dim3(kFp4Threads), 0, s, p);
-    st = check_launch("moe_grouped_gemm");
+    // gate/up: 256-row weight tiles (each expanded weight tile meets the most
+    // pairs); down (short K): 128-row tiles, two workgroups per CU
+    const int bn = stage == GBW_MOE_GATEUP_SWIGLU ? 256 : 128;
+    st = w->fmt == GBW_FMT_VQ4_E8M0 ? launch_moe_fp4<W_VQ>(p, bn, s) : launch_moe_fp4<W_MX>(p, bn, s);
   }
   if (st) return st;
   if (use_slots) {
     const unsigned blocks = (unsigned)cdiv(cdiv(T * N, 8), 256);
     if (f32c)
-      hipLaunchKernelGGL(k_moe_combine<true>, dim3(blocks), dim3(256), 0, s, ws, topk_w, topk, T, N, out->y);
+      hipLaunchKernelGGL(k_moe_combine<true>, dim3(blocks), dim3(256), 0, s, ws, topk_w, pair_pos, topk, T, N, out->y);
     else
-      hipLaunchKernelGGL(k_moe_combine<false>, dim3(blocks), dim3(256), 0, s, ws, topk_w, topk, T, N, out->y);
+      hipLaunchKernelGGL(k_moe_combine<false>, dim3(blocks), dim3(256), 0, s, ws, topk_w, pair_pos, topk, T, N,
+                         out->y);
     st = check_launch("moe_grouped_gemm(combine)");
   }
   return st;

@@ -190,13 +190,14 @@ int moe_route(const float* logits, int64_t T, int32_t E, int32_t topk, int32_t* 
  *    written; quantize it with mx_quantize(GBW_TS_DYNAMIC).
  *  GBW_MOE_DOWN_COMBINE: y[t] = sum_j topk_w[t][j] * deq(a[pair_pos[t][j]])
  *    deq(w_e)^T, a = quantized h in pair order, y [T][H] fp32 (overwritten).
- *    With a workspace, every pair's output goes once to a [T][topk][H] slot
- *    buffer (bf16, or fp32 with GBW_FP32_COMBINE) and a second kernel sums a
- *    token's slots in slot order: bitwise repeatable.  With ws = NULL the
+ *    With a workspace, every pair's output goes once to row p of a [P][H]
+ *    slot buffer (bf16, or fp32 with GBW_FP32_COMBINE) and a second kernel
+ *    sums a token's rows pair_pos[t][0..topk-1] in slot order: bitwise
+ *    repeatable.  With ws = NULL the
  *    outputs are added into y with fp32 atomics (no workspace, not
  *    repeatable; GBW_DETERMINISTIC then fails with GBW_E_WORKSPACE).
  * Weights: E8M0-B32, VQ4-E8M0 (decoded to MXFP4 in LDS, scaled MFMA) or
- * E4M3-B16 (decoded exactly to bf16, bf16 MFMA).  The activation format must
+ * E4M3-B16 (decoded exactly to fp16, fp16 MFMA).  The activation format must
  * be E4M3-B16 for E4M3-B16 weights and E8M0-B32 otherwise.
  * ws: gbw_workspace_size(GBW_OP_MOE_GEMM, P, H, fp32_combine, 0) bytes
  * (down stage only; the gate/up stage takes none). */
