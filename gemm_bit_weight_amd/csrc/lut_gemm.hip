@@ -182,6 +182,96 @@ __global__ __launch_bounds__(64 * NW) void k_lut_gemm(const LutArgs p) {
     }
 }
 
+// Decode shape (M <= 16): one workgroup per 16 output rows n over the whole
+// of K, so a call is one kernel with no partial sums in HBM.  Wave w takes
+// the 128-element chunks w, w + NW, ...; a lane (r16 = n, q) holds elements
+// [32q, 32q + 32) of a chunk as above.  Every weight load of a batch of CB
+// chunks is issued before the first is used, so a CU has all its weight
+// bytes in flight at once.  The x rows of the wave's chunks (M x 128 each)
+// are converted once, by the wave that uses them, into its own LDS slice
+// (fp16, decode order); rows >= M of that slice are never written and feed
+// only output rows that are never stored.  The NW per-wave 16 x 16 partial
+// products are summed in LDS in wave order (a fixed order: repeatable).
+template <int NW, int CB>
+__global__ __launch_bounds__(64 * NW) void k_lut_gemv(const LutArgs p) {
+  constexpr int XROW = 128 * 2 + 16;  // LDS bytes per x row in a chunk slot (16-byte pad)
+  __shared__ __attribute__((aligned(16))) uint8_t xs[NW][CB][16 * XROW];
+  __shared__ float red[NW][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t n = n0 + r16 < p.N ? n0 + r16 : p.N - 1;
+  const int chunks = (int)(p.K / 128);
+  const int64_t G = p.K / p.group;
+  const int M = (int)p.M;
+  const uint8_t* wr = p.idx + n * (p.K / 2);
+  const uint16_t* cr = p.cent + n * G * 16;
+
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int cb0 = wave; cb0 < chunks; cb0 += NW * CB) {
+    v4i iq[CB], ca[CB], cc[CB];
+#pragma unroll
+    for (int b = 0; b < CB; ++b) {
+      const int c0 = cb0 + NW * b;
+      const int c = c0 < chunks ? c0 : chunks - 1;  // clamped: redundant loads hit L2
+      const int64_t k = (int64_t)c * 128 + 32 * q;  // this lane's first element
+      iq[b] = load16(wr + k / 2);
+      const uint16_t* t = cr + (k / p.group) * 16;
+      ca[b] = load16(t);
+      cc[b] = load16(t + 8);
+    }
+    // x: M rows x 128 of each chunk, 16 pieces of 8 per row -> fp16 in the
+    // order 0,2,4,6,1,3,5,7 into this wave's slot
+#pragma unroll
+    for (int b = 0; b < CB; ++b) {
+      const int c0 = cb0 + NW * b;
+      const int c = c0 < chunks ? c0 : chunks - 1;
+      for (int u = lane; u < M * 16; u += 64) {
+        const int m = u >> 4, j = u & 15;
+        const v4i v = load16(p.x + (int64_t)m * p.K + (int64_t)c * 128 + 8 * j);
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f[2 * e] = bf16_to_f32((uint32_t)v[e] & 0xFFFFu);
+          f[2 * e + 1] = bf16_to_f32((uint32_t)v[e] >> 16);
+        }
+        const v8h h = v8h{(_Float16)f[0], (_Float16)f[2], (_Float16)f[4], (_Float16)f[6],
+                          (_Float16)f[1], (_Float16)f[3], (_Float16)f[5], (_Float16)f[7]};
+        *reinterpret_cast<v8h*>(&xs[wave][b][m * XROW + 16 * j]) = h;
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < CB; ++b) {
+      if (cb0 + NW * b >= chunks) break;
+      uint32_t L[4], H[4];
+      split_table(ca[b], cc[b], L, H);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        uint32_t o[4];
+        decode8((uint32_t)iq[b][s], L, H, o);
+        const v8h bfrag = __builtin_bit_cast(v8h, v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]});
+        const v8h afrag = *reinterpret_cast<const v8h*>(&xs[wave][b][r16 * XROW + (32 * q + 8 * s) * 2]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(afrag, bfrag, acc, 0, 0, 0);
+      }
+    }
+  }
+  // acc[r]: x row 4q + r, output row n0 + r16
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[wave][(4 * q + r) * 16 + r16] = acc[r];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 256; i += 64 * NW) {
+    const int m = i >> 4, c = i & 15;
+    if (m < M && n0 + c < p.N) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v += red[w][i];
+      p.y[(int64_t)m * p.N + n0 + c] = v;
+    }
+  }
+}
+
+constexpr int kGemvNW = 16, kGemvCB = 2;
+
 // splits of K: enough workgroups for every CU, at most one resident round
 static int lut_splits(int64_t M, int64_t N, int64_t K, int nw, int kr_max) {
   const int64_t tiles = cdiv(N, 16 * nw) * cdiv(M, 64);
@@ -197,7 +287,7 @@ constexpr int kLutNW = 8;
 constexpr int kLutKR = 4;
 
 size_t ws_lut_gemm(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K <= 0 || K % 128) return 0;
+  if (M <= 16 || N <= 0 || K <= 0 || K % 128) return 0;  // M <= 16: one kernel, no partials
   const int splits = lut_splits(M, N, K, kLutNW, kLutKR);
   return splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
 }
@@ -243,6 +333,11 @@ extern "C" int lut_gemm(int64_t M, int64_t N, int64_t K, int32_t group, const ui
   p.cent = centroids_f16;
   p.y = y;
   p.part = reinterpret_cast<float*>(ws);
+  hipStream_t s = as_stream(stream);
+  if (M <= 16) {
+    hipLaunchKernelGGL((k_lut_gemv<kGemvNW, kGemvCB>), dim3((unsigned)cdiv(N, 16)), dim3(64 * kGemvNW), 0, s, p);
+    return check_launch("lut_gemm");
+  }
   int splits = lut_splits(M, N, K, kLutNW, kLutKR);
   const int need = (int)cdiv(K / 128, kLutKR);
   if (splits > 1 && (!ws || ws_bytes < (size_t)splits * M * N * sizeof(float))) {
@@ -254,8 +349,6 @@ extern "C" int lut_gemm(int64_t M, int64_t N, int64_t K, int32_t group, const ui
     else
       return fail(GBW_E_WORKSPACE, "lut_gemm: needs %zu bytes of workspace", ws_lut_gemm(M, N, K));
   }
-  hipStream_t s = as_stream(stream);
-  if (M <= 16) return launch_lut<1>(p, splits, s);
   if (M <= 32) return launch_lut<2>(p, splits, s);
   return launch_lut<4>(p, splits, s);
 }
