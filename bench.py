@@ -50,7 +50,20 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only copy BYTES between two device buffers 3 times (scale for the HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(torch, nbytes):
+    """A plain device copy of known size: what FETCH_SIZE / WRITE_SIZE read for
+    it converts those counters into bytes for the other kernels."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "calls": 3}), flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -114,16 +127,19 @@ def moe_vq_prefill(gbw, synth, torch, steps, warmup):
                 flops_dn=flops_dn, weight_bytes=weight_bytes, data=d, route=route, T=T, H=H, I=I, E=E, K=K)
 
 
+CPU_SAMPLE_EXPERTS = 32   # about 10-15 s of oracle work on the host cores
+
+
 def cpu_baseline(oracle, synth, torch, np, res):
     """The oracle on a bounded sample of the headline workload: every pair
-    routed to experts 0 and 1 through gate/up, SwiGLU, requantization and the
-    down GEMM (float64 numpy on the host)."""
+    routed to the first CPU_SAMPLE_EXPERTS experts through gate/up, SwiGLU,
+    requantization and the down GEMM (float64 numpy on the host)."""
     import threadpoolctl
     d = res["data"]
     T, H, I = res["T"], res["H"], res["I"]
     route = {k: v.cpu().numpy() for k, v in res["route"].items()}
     off = route["expert_offsets"]
-    experts = [0, 1]
+    experts = list(range(CPU_SAMPLE_EXPERTS))
     pairs = np.concatenate([np.arange(off[e], off[e + 1]) for e in experts])
     x = d["x"].float().cpu().numpy()
     gcpu = {k: v[experts].cpu() for k, v in d["gate_up"].items()}
@@ -147,7 +163,7 @@ def cpu_baseline(oracle, synth, torch, np, res):
     flops = 2.0 * len(pairs) * 3 * I * H
     threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"all {len(pairs)} pairs routed to experts 0 and 1 of the headline batch "
+            "sample": f"all {len(pairs)} pairs routed to experts 0-{experts[-1]} of the headline batch "
                       f"(quantize x, gate/up, SwiGLU, requantize, down; no combine), {secs:.1f} s"}
 
 
@@ -294,6 +310,9 @@ def main():
     import gemm_bit_weight_amd as gbw
     import synth
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration)
+        return
 
     log("headline: VQ->MX MoE prefill T=8192 H=4096 I=1536 E=128 top-8")
     res = moe_vq_prefill(gbw, synth, torch, args.steps, args.warmup)

@@ -91,7 +91,7 @@ __device__ __forceinline__ int band_count(int rows, int wm) {
   return __builtin_amdgcn_readfirstlane(r >= 64 ? 2 : (r > 32 ? 2 : (r > 0 ? 1 : 0)));
 }
 
-// Logical tile of this workgroup: XCD-aware remap, then (expert, m tile, n tile).
+// Logical tile of this workgroup: XCD-aware remap, then (expert, n tile, m tile).
 // Workgroup b runs on XCD b % 8; the tiles that exist (known only here, from
 // expert_offsets) are split into 8 equal runs of consecutive logical tiles, one
 // per XCD, so every XCD gets the same share and its experts stay in its L2.
@@ -123,8 +123,13 @@ __device__ __forceinline__ bool find_tile(const MoeArgs& p, TileInfo& ti, int* s
   }
   __syncthreads();
   ti.e = s_e;
-  ti.mt = lm - (ti.e ? scan[ti.e - 1] : 0);
-  ti.nt = L % p.n_tiles;
+  // within the expert, m tiles vary fastest: the workgroups that run at the
+  // same time on an XCD share each weight tile, which then comes from L2
+  const int first = ti.e ? scan[ti.e - 1] : 0;
+  const int mts = scan[ti.e] - first;
+  const int local = L - first * p.n_tiles;
+  ti.mt = local % mts;
+  ti.nt = local / mts;
   ti.row0 = p.off[ti.e] + ti.mt * kMoeBM;
   ti.rows = min(kMoeBM, p.off[ti.e + 1] - ti.row0);
   return true;
