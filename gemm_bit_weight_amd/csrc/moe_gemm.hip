@@ -71,6 +71,7 @@ struct MoeArgs {
   float* y;                // DOWN: [T][H]
   void* slots;             // DOWN: [P][H] bf16 or fp32 per-pair outputs (pair-major), or null (atomics into y)
   int32_t slots_f32;       // 1: fp32 slots, 0: bf16 slots
+  int32_t scales16;        // 1: K % 512 == 0 and both scale arrays 16-byte aligned
 };
 
 struct TileInfo {
@@ -372,7 +373,11 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
   // Indices past the last stage are clamped, so the loop body has no branches
   // (the redundant work at the end hits L2 and a spare buffer).
   v4i pa[NA], pb[2];
-  uint32_t ps0, ps1;
+  uint32_t ps0 = 0, ps1 = 0;
+  // with p.scales16 (256-wide tiles only: the 128-wide kernel has no
+  // registers to spare): the scale dwords of stage groups of four, by group parity
+  constexpr bool S16 = BN == 256;
+  v4i s4a0 = v4i{0, 0, 0, 0}, s4a1 = s4a0, s4b0 = s4a0, s4b1 = s4a0;
   uint2 pl;
   const int last = steps - 1;
   auto gload = [&](int s) __attribute__((always_inline)) {
@@ -380,8 +385,23 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
     const int64_t kb = (int64_t)s * 64;
 #pragma unroll
     for (int u = 0; u < NA; ++u) pa[u] = load16(arow[u] + kb + 16 * ac);
-    ps0 = *reinterpret_cast<const uint32_t*>(scl0 + (int64_t)s * 4);
-    if (NT != 512) ps1 = *reinterpret_cast<const uint32_t*>(scl1 + (int64_t)s * 4);
+    if (S16 && p.scales16) {
+      // one 16-byte load per row covers the scale dwords of stages s .. s+3
+      if ((s & 3) == 0) {
+        const v4i a4 = load16(scl0 + (int64_t)s * 4);
+        const v4i b4 = NT != 512 ? load16(scl1 + (int64_t)s * 4) : a4;
+        if ((s >> 2) & 1) {
+          s4a1 = a4;
+          s4b1 = b4;
+        } else {
+          s4a0 = a4;
+          s4b0 = b4;
+        }
+      }
+    } else {
+      ps0 = *reinterpret_cast<const uint32_t*>(scl0 + (int64_t)s * 4);
+      if (NT != 512) ps1 = *reinterpret_cast<const uint32_t*>(scl1 + (int64_t)s * 4);
+    }
     if (WF == W_MX) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) pb[u] = load16(wrow[u] + kb + 16 * ac);
@@ -395,6 +415,14 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
   auto lstore = [&](int k) __attribute__((always_inline)) {
     const int buf = k & 1;
     uint8_t* const a = sA0 + buf * kABuf;
+    if (S16 && p.scales16) {
+      const int kk = k < last ? k : last;
+      const bool odd = (kk >> 2) & 1;
+      const v4i a4 = odd ? s4a1 : s4a0, b4 = odd ? s4b1 : s4b0;
+      const int e = kk & 3;
+      ps0 = (uint32_t)(e == 0 ? a4[0] : e == 1 ? a4[1] : e == 2 ? a4[2] : a4[3]);
+      ps1 = (uint32_t)(e == 0 ? b4[0] : e == 1 ? b4[1] : e == 2 ? b4[2] : b4[3]);
+    }
 #pragma unroll
     for (int u = 0; u < NA; ++u) *reinterpret_cast<v4i*>(a + (ar + (NT / 4) * u) * kRowB + 16 * ac) = pa[u];
     if (NT == 512) {
@@ -897,6 +925,10 @@ extern "C" int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const in
   p.y = out->y;
   p.slots = use_slots ? ws : nullptr;
   p.slots_f32 = f32c ? 1 : 0;
+  p.scales16 = (K % 512 == 0 && !(reinterpret_cast<uintptr_t>(a->scales) & 15u) &&
+                !(reinterpret_cast<uintptr_t>(w->scales) & 15u))
+                   ? 1
+                   : 0;
   // every kernel below writes through these: refuse to launch without them
   if (stage == GBW_MOE_DOWN_COMBINE ? (!p.y || (use_slots && !p.slots)) : (!p.h_codes && !p.h_bf16))
     return fail(GBW_E_ARG, "moe_grouped_gemm: no output buffer");
