@@ -85,6 +85,87 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_topk(const float* __res
     for (int e = lane; e < E; e += 64) counts[chunk * E + e] = __popcll(mask[wv][e]);
 }
 
+// Same outputs for E <= 256 with 16 lanes per token: a workgroup of 1024
+// threads is one chunk of 64 tokens; lane s of a token's group holds logits
+// s, s + 16, ... (coalesced loads), and each of the k rounds takes the
+// largest (value, then lowest expert id) not yet taken, by a lane-local scan
+// and a 16-lane reduction over DPP row permutes.
+template <int CTRL>
+__device__ __forceinline__ void best_step(float& v, int& e) {
+  const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+  const int oe = __builtin_amdgcn_mov_dpp(e, CTRL, 0xF, 0xF, true);
+  const bool take = ov > v || (ov == v && oe < e);
+  v = take ? ov : v;
+  e = take ? oe : e;
+}
+
+// lanes ^1, ^2 (quad permutes), then the mirrors within 8 and 16 lanes:
+// after the four steps every lane of the 16-lane row holds the row's best
+__device__ __forceinline__ void row16_best(float& v, int& e) {
+  best_step<0xB1>(v, e);
+  best_step<0x4E>(v, e);
+  best_step<0x141>(v, e);
+  best_step<0x140>(v, e);
+}
+
+template <int K>
+__global__ __launch_bounds__(1024) void k_route_topk16(const float* __restrict__ logits, int64_t T, int E,
+                                                       int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+                                                       int32_t* __restrict__ counts) {
+  __shared__ unsigned long long mask[256];
+  const int tid = threadIdx.x;
+  const int64_t chunk = blockIdx.x;
+  const int tl = tid >> 4, sl = tid & 15;  // token of the chunk, lane of its group
+  const int64_t t = chunk * 64 + tl;
+  if (tid < E) mask[tid] = 0ull;
+  __syncthreads();
+  const bool live = t < T;
+  const float* row = logits + (live ? t : 0) * E;
+  float v[16];
+  uint32_t open = 0;  // bit i: entry i (expert sl + 16 i) exists and is not taken
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = sl + 16 * i;
+    const bool ok = live && e < E;
+    v[i] = ok ? row[e] : 0.f;
+    open |= (uint32_t)ok << i;
+  }
+  int ids[K];
+  float vals[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    float bv = -__builtin_huge_valf();
+    int be = 1 << 30;  // no entry: loses every comparison against a real one
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bool take = ((open >> i) & 1u) && (be == (1 << 30) || v[i] > bv);
+      bv = take ? v[i] : bv;
+      be = take ? sl + 16 * i : be;
+    }
+    row16_best(bv, be);
+    ids[j] = be;
+    vals[j] = bv;
+    if ((be & 15) == sl) open &= ~(1u << (be >> 4));
+  }
+  if (live) {
+    float ex[K], sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      ex[j] = expf(vals[j] - vals[0]);
+      sum += ex[j];
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      if (j == sl) {
+        topk_ids[t * K + j] = ids[j];
+        topk_w[t * K + j] = ex[j] / sum;
+        atomicOr(&mask[ids[j]], 1ull << tl);
+      }
+  }
+  __syncthreads();
+  if (tid < E) counts[chunk * E + tid] = __popcll(mask[tid]);
+}
+
 // Single workgroup of 1024 threads: G = 1024 / E' threads per expert (E' = E
 // rounded up to a power of two) each own a contiguous run of chunks; per-run
 // sums, an exclusive scan over the runs of an expert, an inclusive scan over
@@ -175,7 +256,10 @@ static int launch_route(const float* logits, int64_t T, int E, int32_t* ids, flo
   int32_t* counts = ws;
   int32_t* base = ws + C * E;
   const unsigned blocks = (unsigned)cdiv(C, kRouteThreads / 64);
-  hipLaunchKernelGGL(k_route_topk<K>, dim3(blocks), dim3(kRouteThreads), 0, st, logits, T, E, ids, w, counts);
+  if (E <= 256)
+    hipLaunchKernelGGL(k_route_topk16<K>, dim3((unsigned)C), dim3(1024), 0, st, logits, T, E, ids, w, counts);
+  else
+    hipLaunchKernelGGL(k_route_topk<K>, dim3(blocks), dim3(kRouteThreads), 0, st, logits, T, E, ids, w, counts);
   int s = check_launch("moe_route(topk)");
   if (s) return s;
   hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(kMaxExperts), 0, st, counts, C, E, base, off);
