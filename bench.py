@@ -37,6 +37,11 @@ METRIC = "quantized GEMM TFLOP/s (prefill) + weight GB/s (decode) at 1 GPU"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MXFP4_PEAK_TFLOPS = 10100.0    # dense MFMA, fp4 / fp6
 F16_PEAK_TFLOPS = 2500.0       # dense MFMA, fp16 / bf16
+# HBM bytes per gate/up launch of the headline workload: rocprofv3 FETCH_SIZE and
+# WRITE_SIZE of k_moe_fp4<VQ,256>, scaled by a 1 GiB copy (factors 2.0 and 1.0);
+# profiles/k_moe_fp4_vq_prefill_T8192_H4096_I1536_E128_top8.md.  Must be
+# measured again (or set to None) whenever that kernel changes.
+GATEUP_HBM_BYTES = 434111 * 2 * 1024 + 62968.4 * 1024
 
 
 def log(msg):
@@ -339,7 +344,8 @@ def main():
                    "activations": "E8M0-B32 FP4, quantized online", "routed_flops": res["flops"]},
         "roofline": {"kernel": "k_moe_fp4<VQ> gate/up (fused SwiGLU + requantization)", "bound": "mfma",
                      "achieved": gu_tflops, "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": gu_tflops / MXFP4_PEAK_TFLOPS, "traffic": None,
+                     "frac": gu_tflops / MXFP4_PEAK_TFLOPS, "traffic": GATEUP_HBM_BYTES,
+                     "traffic_unit": "bytes per launch (HBM, calibrated counters)",
                      "flops_per_launch": res["flops_gu"], "avg_launch_ms": res["gu_ms"]},
         "stages_ms": {"gate_up": res["gu_ms"], "down_combine": res["dn_ms"],
                       "route_quant_other": res["ms_step"] - res["gu_ms"] - res["dn_ms"]},
