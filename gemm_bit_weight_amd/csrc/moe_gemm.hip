@@ -305,11 +305,12 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
   const bool gate = p.stage == GBW_MOE_GATEUP_SWIGLU;
 
   // per-row metadata: the token of each pair (the A row of the gate/up
-  // gather) and, for the atomic down path only, its routing weight
+  // gather) and, for the atomic down path only, its routing weight (the
+  // down stage with a slot buffer needs neither)
   for (int r = tid; r < kMoeBM; r += NT) {
     int tok = 0;
     float wt = 0.f;
-    if (r < ti.rows) {
+    if (r < ti.rows && (gate || !p.slots)) {
       const int pr = ti.row0 + r;
       tok = p.pair_token[pr];
       if (!gate && !p.slots)
