@@ -109,46 +109,62 @@ __global__ __launch_bounds__(64 * NW) void k_mx_gemm(const MxGemmArgs p) {
   // --- weight slice: straight-line loads, all in flight at once -----------
   // Steps past this split's range re-read its last step (their A is zero);
   // blocks past the segment end re-read its last block (A is zero there too).
+  // The row pointers of both K segments are formed once; a step only picks
+  // one of them (a uniform choice) and adds its K offset.
+  const bool two = p.seg[1].steps > 0;
   v4i bq[SMAX][TN];
   int bsc[SMAX][TN];
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     int64_t n = n0 + 16 * j + r16;
     n = n < p.N ? n : p.N - 1;
+    const uint8_t* wc0 = p.seg[0].w_codes + n * p.seg[0].ldw;
+    const uint8_t* ws0 = p.seg[0].w_scales + n * p.seg[0].ldws;
+    const uint8_t* wc1 = two ? p.seg[1].w_codes + n * p.seg[1].ldw : wc0;
+    const uint8_t* ws1 = two ? p.seg[1].w_scales + n * p.seg[1].ldws : ws0;
 #pragma unroll
     for (int t = 0; t < SMAX; ++t) {
-      const StepSeg sg = step_seg(p, s0 + (t < ns ? t : ns - 1));
-      int64_t kk = sg.k + 32 * g;
-      kk = kk < sg.K ? kk : sg.K - 32;
-      bq[t][j] = load16(sg.wc + n * sg.ldw + kk / 2);
-      bsc[t][j] = sg.ws[n * sg.ldws + kk / 32];
+      const int s = s0 + (t < ns ? t : ns - 1);
+      const bool b = s >= p.seg[0].steps;
+      const int64_t K = b ? p.seg[1].K : p.seg[0].K;
+      int64_t kk = (int64_t)(b ? s - p.seg[0].steps : s) * 128 + 32 * g;
+      kk = kk < K ? kk : K - 32;
+      bq[t][j] = load16((b ? wc1 : wc0) + kk / 2);
+      bsc[t][j] = (b ? ws1 : ws0)[kk / 32];
     }
   }
 
   // --- activation range: batched loads, then LDS -------------------------
+  // 16-byte chunk c of the range is row c / (4 SMAX), step (c / 4) % SMAX,
+  // block c % 4; a thread's chunks c = tid + 64 NW u all share one (step,
+  // block), so its K offset is computed once.
+  constexpr int RPU = 64 * NW / (SMAX * 4);  // rows between a thread's consecutive chunks
+  static_assert((64 * NW) % (SMAX * 4) == 0, "a thread's chunks must share their step");
+  const int row0 = (int)threadIdx.x / (SMAX * 4), tq = (int)threadIdx.x % (SMAX * 4);
+  const int ta = tq >> 2, blk = tq & 3;
+  const int sta = s0 + (ta < ns ? ta : ns - 1);
+  const bool ba = sta >= p.seg[0].steps;
+  const int64_t Ka = ba ? p.seg[1].K : p.seg[0].K;
+  int64_t kka = (int64_t)(ba ? sta - p.seg[0].steps : sta) * 128 + 32 * blk;
+  const bool okk = ta < ns && kka < Ka;
+  kka = kka < Ka ? kka : Ka - 32;
+  const int64_t ka = (ba ? p.seg[1].a_k0 : p.seg[0].a_k0) + kka;
+  const uint8_t* acol = p.a_codes + ka / 2;
+  const uint8_t* ascol = p.a_scales + ka / 32;
   v4i av[PER];
   uint32_t asv[PER];
-  bool ok[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
-    const int c = threadIdx.x + u * 64 * NW;
-    const int row = c / (SMAX * 4), q = c % (SMAX * 4), t = q >> 2, blk = q & 3;
-    int64_t m = m0 + row;
+    int64_t m = m0 + row0 + RPU * u;
     m = m < p.M ? m : p.M - 1;
-    const StepSeg sg = step_seg(p, s0 + (t < ns ? t : ns - 1));
-    int64_t kk = sg.k + 32 * blk;
-    ok[u] = t < ns && kk < sg.K;
-    kk = kk < sg.K ? kk : sg.K - 32;
-    const int64_t ka = sg.a_k0 + kk;
-    av[u] = load16(p.a_codes + m * p.lda + ka / 2);
-    asv[u] = p.a_scales[m * p.ldas + ka / 32];
+    av[u] = load16(acol + m * p.lda);
+    asv[u] = ascol[m * p.ldas];
   }
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
-    const int c = threadIdx.x + u * 64 * NW;
-    const int row = c / (SMAX * 4), q = c % (SMAX * 4);
-    *reinterpret_cast<v4i*>(sa + row * LDA + q * 16) = ok[u] ? av[u] : v4i{0, 0, 0, 0};
-    ss[row * SMAX * 4 + q] = (uint8_t)(ok[u] ? asv[u] : 127u);
+    const int row = row0 + RPU * u;
+    *reinterpret_cast<v4i*>(sa + row * LDA + tq * 16) = okk ? av[u] : v4i{0, 0, 0, 0};
+    ss[row * SMAX * 4 + tq] = (uint8_t)(okk ? asv[u] : 127u);
   }
   __syncthreads();
 
@@ -297,14 +313,18 @@ static int check_w(const gbw_weight* w, int64_t K, const char* who) {
   return GBW_OK;
 }
 
-template <int TM>
+// K steps (of 128) per workgroup at most: 16 for long K (fewer split-K
+// partials), 8 otherwise (a workgroup loads all SMAX steps' registers)
+constexpr int mx_smax(int64_t steps) { return steps >= 48 ? 16 : 8; }
+
+template <int TM, int SMAX>
 static int dispatch_tm(MxGemmArgs& p, size_t ws_bytes, hipStream_t st) {
-  int splits = pick_splits<TM, 1, 4, 8>(p.M, p.N, p.total_steps);
+  int splits = pick_splits<TM, 1, 4, SMAX>(p.M, p.N, p.total_steps);
   const size_t slab = (size_t)p.M * p.N * sizeof(float);
   if (splits > 1 && (!p.part || ws_bytes < (size_t)splits * slab)) {
     // not enough workspace for the partials: the serial-K kernel needs none
     const int fit = p.part ? (int)(ws_bytes / slab) : 0;
-    const int need = (int)cdiv(p.total_steps, 8);
+    const int need = (int)cdiv(p.total_steps, SMAX);
     if (fit >= need && fit >= 2)
       splits = fit;
     else if (need == 1)
@@ -312,21 +332,23 @@ static int dispatch_tm(MxGemmArgs& p, size_t ws_bytes, hipStream_t st) {
     else
       return launch_serial<TM>(p, st);
   }
-  return launch_mx<TM, 1, 4, 8>(p, splits, st);
+  return launch_mx<TM, 1, 4, SMAX>(p, splits, st);
+}
+
+template <int SMAX>
+static int ws_splits(int64_t M, int64_t N, int steps) {
+  if (M <= 16) return pick_splits<1, 1, 4, SMAX>(M, N, steps);
+  if (M <= 32) return pick_splits<2, 1, 4, SMAX>(M, N, steps);
+  return pick_splits<4, 1, 4, SMAX>(M, N, steps);
 }
 
 size_t ws_mx_gemm(int64_t M, int64_t N, int64_t Ktot) {
   if (M <= 0 || N <= 0 || Ktot <= 0) return 0;
   const int steps = (int)cdiv(Ktot, 128) + 1;  // + 1: the tail segment may start a step of its own
-  int splits;
-  if (M <= 16)
-    splits = pick_splits<1, 1, 4, 8>(M, N, steps);
-  else if (M <= 32)
-    splits = pick_splits<2, 1, 4, 8>(M, N, steps);
-  else if (M <= 64)
-    splits = pick_splits<4, 1, 4, 8>(M, N, steps);
-  else
-    splits = pick_splits<8, 1, 4, 8>(M, N, steps);
+  // the largest split count either K-range choice can make for these steps
+  int splits = ws_splits<8>(M, N, steps);
+  const int s16 = ws_splits<16>(M, N, steps);
+  splits = splits > s16 ? splits : s16;
   return splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
 }
 
@@ -350,10 +372,16 @@ static int run_mx(int64_t M, const gbw_act* a, const gbw_weight* w, const gbw_we
   p.ldy = w->N;
   p.part = reinterpret_cast<float*>(ws);
   hipStream_t st = as_stream(stream);
-  if (M <= 16) return dispatch_tm<1>(p, ws_bytes, st);
-  if (M <= 32) return dispatch_tm<2>(p, ws_bytes, st);
-  if (M <= 64) return dispatch_tm<4>(p, ws_bytes, st);
-  return dispatch_tm<8>(p, ws_bytes, st);
+  // rows per workgroup: up to 64 (more rows are more workgroups along M: a
+  // 128-row tile leaves too few workgroups once K is split into 16-step ranges)
+  if (mx_smax(p.total_steps) == 16) {
+    if (M <= 16) return dispatch_tm<1, 16>(p, ws_bytes, st);
+    if (M <= 32) return dispatch_tm<2, 16>(p, ws_bytes, st);
+    return dispatch_tm<4, 16>(p, ws_bytes, st);
+  }
+  if (M <= 16) return dispatch_tm<1, 8>(p, ws_bytes, st);
+  if (M <= 32) return dispatch_tm<2, 8>(p, ws_bytes, st);
+  return dispatch_tm<4, 8>(p, ws_bytes, st);
 }
 
 }  // namespace gbw
