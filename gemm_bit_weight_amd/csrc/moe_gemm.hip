@@ -592,45 +592,23 @@ int launch_moe_fp4(const MoeArgs& p, int bn, hipStream_t st) {
 // route through the FP4/FP8 scaled MFMA: its block scales are powers of two
 // per 32 elements, an E4M3 scale carries a 3-bit mantissa per 16.)
 //
-// Decode: one dword of codes (8 elements) -> four fp16x2 words through a
-// byte-permute lookup in the constant 16-entry E2M1 table, then one packed
-// fp16 multiply by the block scale per word (exact).  The lookup yields the
-// elements in the order 0,2,4,6,1,3,5,7; A and B are decoded alike, so the
-// MFMA pairs the same K indices.
+// Decode: one dword of codes (8 elements, element 2i in the low nibble of
+// byte i) -> four fp16x2 words in element order: v_cvt_scalef32_pk_f16_fp4
+// with scale 1 gives the two E2M1 values of a byte exactly (the instruction
+// applies only the exponent of its fp32 scale, so the E4M3 block scale cannot
+// go there), then one packed fp16 multiply by the block scale (exact).
 constexpr int kRowH = 144;  // LDS bytes per fp16 row per stage (64 elements + 16 pad)
 constexpr int kE4Threads = 512, kE4BN = 256;
 constexpr int kHRow8 = 136;  // bf16 per staged h row (128 + 8): rows 4 apart fall in different banks
 
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t perm16(uint32_t s7, uint32_t mask, uint32_t t0, uint32_t t1, uint32_t t2,
-                                           uint32_t t3) {
-  const uint32_t lo = __builtin_amdgcn_perm(t1, t0, s7);
-  const uint32_t hi = __builtin_amdgcn_perm(t3, t2, s7);
-  return (hi & mask) | (lo & ~mask);
-}
-
-// fp16 bit patterns of the 16 E2M1 codes, as low-byte and high-byte planes
-// (4 entries per dword, entry i in byte i % 4 of dword i / 4)
-// magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 -> 0x0000 0x3800 0x3C00 0x3E00 0x4000 0x4200 0x4400 0x4600
-constexpr uint32_t kE2L0 = 0x00000000u, kE2L1 = 0x00000000u, kE2L2 = 0x00000000u, kE2L3 = 0x00000000u;
-constexpr uint32_t kE2H0 = 0x3E3C3800u, kE2H1 = 0x46444240u, kE2H2 = 0xBEBCB880u, kE2H3 = 0xC6C4C2C0u;
-
 __device__ __forceinline__ void e4m3_decode8(uint32_t w, uint32_t sc2, uint32_t (&o)[4]) {
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const uint32_t s = half == 0 ? (w & 0x0F0F0F0Fu) : ((w >> 4) & 0x0F0F0F0Fu);
-    const uint32_t s7 = s & 0x07070707u;
-    const uint32_t b3 = (s >> 3) & 0x01010101u;
-    const uint32_t mask = (b3 << 8) - b3;
-    const uint32_t lo = perm16(s7, mask, kE2L0, kE2L1, kE2L2, kE2L3);
-    const uint32_t hi = perm16(s7, mask, kE2H0, kE2H1, kE2H2, kE2H3);
-    const uint32_t p0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
-    const uint32_t p1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
-    const v2h sv = __builtin_bit_cast(v2h, sc2);
-    o[2 * half + 0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, p0) * sv);
-    o[2 * half + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, p1) * sv);
-  }
+  const v2h sv = __builtin_bit_cast(v2h, sc2);
+  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sv);
+  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sv);
+  o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sv);
+  o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sv);
 }
 
 // E4M3 scale code -> fp16 bits duplicated into both halves (exact: an E4M3
