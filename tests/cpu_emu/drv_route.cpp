@@ -1,0 +1,40 @@
+// CPU check of moe_route: bounds (ASan) and results against a sort-based reference.
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <stdarg.h>
+#include <random>
+#include <numeric>
+#include "gbw.h"
+thread_local emu_idx threadIdx, blockIdx, blockDim, gridDim;
+thread_local std::barrier<>* emu_bar;
+thread_local emu_wave emu_w;
+std::mutex emu_atomic_mu;
+namespace gbw {
+size_t ws_moe_route(int64_t T, int64_t E);
+int fail(int status, const char* fmt, ...) {
+  va_list ap; va_start(ap, fmt); fprintf(stderr, "fail: "); vfprintf(stderr, fmt, ap); fprintf(stderr, "\n"); va_end(ap);
+  return status;
+}
+int check_device() { return 0; }
+int check_launch(const char*) { return 0; }
+int device_cu_count() { return 256; }
+}
+int main(int argc, char** argv) {
+  const int64_t T = atoll(argv[1]); const int E = atoi(argv[2]), K = atoi(argv[3]); const int ties = argc > 4;
+  std::mt19937 g(3); std::normal_distribution<float> nd;
+  float* l = (float*)malloc(T * E * 4);
+  for (int64_t i = 0; i < T * E; ++i) l[i] = ties ? (float)(g() % 3) : nd(g);
+  int32_t* ids = (int32_t*)malloc(T * K * 4); float* w = (float*)malloc(T * K * 4);
+  int32_t* off = (int32_t*)malloc((E + 1) * 4); int32_t* pt = (int32_t*)malloc(T * K * 4); int32_t* pp = (int32_t*)malloc(T * K * 4);
+  size_t wsb = gbw::ws_moe_route(T, E); void* ws = malloc(wsb);
+  int st = moe_route(l, T, E, K, ids, w, off, pt, pp, ws, wsb, nullptr);
+  long bad = 0;
+  for (int64_t t = 0; t < T; ++t) {
+    std::vector<int> o(E); std::iota(o.begin(), o.end(), 0);
+    std::stable_sort(o.begin(), o.end(), [&](int a, int b) { return l[t * E + a] > l[t * E + b]; });
+    for (int j = 0; j < K; ++j) bad += ids[t * K + j] != o[j];
+  }
+  printf("route T=%lld E=%d K=%d status %d mismatched ids %ld off[E]=%d\n", (long long)T, E, K, st, bad, off[E]);
+  return 0;
+}
