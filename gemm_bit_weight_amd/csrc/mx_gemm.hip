@@ -10,18 +10,21 @@
 // time in place (identical to the appended copy when the tail starts on a
 // 32-element block boundary), so no copy is made.
 //
-// Contraction: v_mfma_scale_f32_16x16x128_f8f6f4 with both operands FP4 (E2M1)
-// and one E8M0 scale per lane.  A lane (row r = lane % 16, group g = lane / 16)
-// holds 32 consecutive K elements -- exactly one E8M0 block -- as 16 bytes, and
-// that block's scale.  A and W use the same lane -> K mapping, so each lane's
-// products pair the same K indices and the scale applies to its own block.
-// The 16x16 fp32 result lives as lane l, register i = row 4*(l/16)+i, column l%16.
-//
-// Decode-shaped problems (M <= 128, N in the thousands) are bound by the weight
-// stream from HBM: each wave streams its own 16*TN weight rows with 16-byte
-// loads, the M side is covered in registers (TM tiles of 16 rows) and the K
-// range is split across workgroups when the (N, M) tiles alone cannot fill
-// 256 CUs; the split partial sums are combined with fp32 atomics.
+// Two kernels, both on the scaled FP4 MFMA with one E8M0 scale per lane (a
+// lane holds 32 consecutive K elements -- exactly one E8M0 block -- as 16
+// bytes, and that block's scale; activation and weight use the same lane -> K
+// mapping, so each lane's products pair the same K indices):
+//  * k_mx_gemm (up to 16 rows, or K not a multiple of 128):
+//    v_mfma_scale_f32_16x16x128_f8f6f4; lane (row r = lane % 16, group
+//    g = lane / 16); the 16x16 fp32 result is lane l, register i = row
+//    4*(l/16)+i, column l%16.  Each wave streams its own 16*TN weight rows.
+//  * k_mx_gemm32 (17+ rows with 128-aligned K segments): the 32x32x64 shape,
+//    which runs at twice the 16x16x128 rate; the weight slice is read once
+//    for all rows of the M tile (up to 128).
+// Decode-shaped problems (M <= 128, N in the thousands) stream the weights
+// from HBM once; the K range is split across workgroups when the (N, M) tiles
+// alone cannot fill 256 CUs, each split writes its own fp32 partial slab and
+// k_splitk_reduce sums the slabs in split order (bitwise repeatable).
 #include "common.hpp"
 
 namespace gbw {
@@ -208,6 +211,169 @@ __global__ __launch_bounds__(64 * NW) void k_mx_gemm(const MxGemmArgs p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// 32x32x64 path for 17..128 rows per tile with 128-aligned K segments
+// ---------------------------------------------------------------------------
+//
+// v_mfma_scale_f32_32x32x64_f8f6f4 (the full FP4 rate on gfx950; 16x16x128
+// runs at the FP8 rate).  Operand lane l holds row l % 32 and one 32-element
+// E8M0 block (16 bytes) of K; the fp32 result holds column l % 32 and rows
+// 8*(r/4) + 4*(l/32) + r%4 in register r.  Within a 128-element K step, MFMA h
+// (0, 1) gives lane half j block 2h + j, for the activation and the weight
+// alike, with that block's own scale.
+//
+// A workgroup (4 waves) owns 64 output columns, all 32*TM rows of its M tile
+// and a range of at most SMAX K steps: waves 0/1 take columns 0-31/32-63 over
+// the first half of the steps, waves 2/3 the same columns over the second
+// half (their sums meet in LDS at the end, in a fixed order).  The weight
+// slice is read once from HBM straight into registers; the activation range
+// goes HBM/L2 -> LDS by direct-to-LDS loads (no registers), issued before the
+// weight loads so the barrier only waits for them, and the MFMAs consume the
+// weight steps in arrival order.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+// s_waitcnt operand that waits until at most n vector memory operations of
+// this wave are outstanding (vmcnt in bits 3:0 and 15:14; expcnt, lgkmcnt
+// left at their maxima, i.e. not waited for)
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// 16-byte slot of logical block `blk` in LDS row `rr` (0..15) of a 1 KB
+// activation block: rows are 64 bytes, so 8 (or 16) consecutive rows read by
+// one ds_read_b128 pass land in distinct banks
+__device__ __forceinline__ int a_slot(int rr, int blk) { return blk ^ (((rr >> 2) & 3) ^ (rr & 2)); }
+
+template <int TM, int SMAX>
+__global__ __launch_bounds__(256) void k_mx_gemm32(const MxGemmArgs p) {
+  constexpr int ROWS = 32 * TM;
+  constexpr int RB = ROWS / 16;              // 1 KB activation blocks (16 rows x 64 bytes) per step
+  constexpr int SR = ROWS > 64 ? ROWS : 64;  // scale dwords per step (a 4-byte direct load fills 64)
+  constexpr int HALF = SMAX / 2;             // K steps per wave at most
+  static_assert(SMAX % 2 == 0 && TM >= 1 && TM <= 4, "tile");
+  static_assert(3 * HALF <= 63, "weight loads must fit the vmcnt counter");
+  __shared__ __attribute__((aligned(16))) uint8_t sa[SMAX * RB * 1024];
+  __shared__ __attribute__((aligned(16))) uint32_t ssc[SMAX * SR];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cg = wave & 1, kh = wave >> 1;
+  const int c = lane & 31, j = lane >> 5;
+  const int64_t m0 = (int64_t)blockIdx.z * ROWS;
+  const int64_t n0 = (int64_t)blockIdx.x * 64 + cg * 32;
+  const int s0 = blockIdx.y * p.steps_per_split;
+  const int ns = min(p.total_steps - s0, p.steps_per_split);  // >= 1
+  const int h0 = (ns + 1) >> 1;
+  const int tb = kh ? h0 : 0;         // this wave's first step within the range
+  const int cnt = kh ? ns - h0 : h0;  // and its step count (0 when ns = 1, kh = 1)
+  const int steps0 = p.seg[0].steps;
+  // first A column of range step t (segment 1 starts at its own A column)
+  auto a_col = [&](int t) __attribute__((always_inline)) {
+    const int s = s0 + t;
+    return s >= steps0 ? p.seg[1].a_k0 + (int64_t)(s - steps0) * 128 : (int64_t)s * 128;
+  };
+
+  // --- activation range -> LDS (direct loads; rows past M re-read row M-1) --
+  {
+    const int rr = lane >> 2;
+    const int blk = (lane & 3) ^ (((rr >> 2) & 3) ^ (rr & 2));  // inverse of a_slot for this lane's slot
+    for (int b = wave; b < ns * RB; b += 4) {
+      const int t = b / RB, rb = b - t * RB;
+      int64_t m = m0 + rb * 16 + rr;
+      m = m < p.M ? m : p.M - 1;
+      __builtin_amdgcn_global_load_lds((glb_void*)(p.a_codes + m * p.lda + (a_col(t) + 32 * blk) / 2),
+                                       (lds_void*)(sa + b * 1024), 16, 0, 0);
+    }
+    for (int b = wave; b < ns * (SR / 64); b += 4) {
+      const int t = b / (SR / 64), hb = b - t * (SR / 64);
+      int64_t m = m0 + hb * 64 + lane;
+      m = m < p.M ? m : p.M - 1;
+      __builtin_amdgcn_global_load_lds((glb_void*)(p.a_scales + m * p.ldas + a_col(t) / 32),
+                                       (lds_void*)(ssc + t * SR + hb * 64), 4, 0, 0);
+    }
+  }
+  __asm__ volatile("" ::: "memory");
+
+  // --- this wave's weight steps -> registers (3 loads per step, all in flight)
+  // Steps past the wave's count re-read its last step (never used).
+  int64_t n = n0 + c;
+  n = n < p.N ? n : p.N - 1;
+  const bool two = p.seg[1].steps > 0;
+  const uint8_t* wc0 = p.seg[0].w_codes + n * p.seg[0].ldw;
+  const uint8_t* ws0 = p.seg[0].w_scales + n * p.seg[0].ldws;
+  const uint8_t* wc1 = two ? p.seg[1].w_codes + n * p.seg[1].ldw : wc0;
+  const uint8_t* ws1 = two ? p.seg[1].w_scales + n * p.seg[1].ldws : ws0;
+  const int last = tb + cnt - 1 > 0 ? tb + cnt - 1 : 0;
+  v4i bq[HALF][2];
+  uint32_t bs[HALF];
+#pragma unroll
+  for (int t = 0; t < HALF; ++t) {
+    const int s = s0 + min(tb + t, last);
+    const bool sb = s >= steps0;
+    const int64_t kb = (int64_t)(sb ? s - steps0 : s) * 64;  // byte offset of the step in the code row
+    const uint8_t* wc = (sb ? wc1 : wc0) + kb + 16 * j;
+    bq[t][0] = load16(wc);       // block j
+    bq[t][1] = load16(wc + 32);  // block 2 + j
+    bs[t] = *reinterpret_cast<const uint32_t*>((sb ? ws1 : ws0) + kb / 16);  // the step's 4 scales
+  }
+  __asm__ volatile("" ::: "memory");
+  // the direct loads were issued before the 3*HALF weight loads: once at most
+  // that many are outstanding, this wave's LDS data has landed
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * HALF));
+  // a bare barrier between two compiler memory barriers (no memory access
+  // moves across it): __syncthreads()' fences would also wait for the weight
+  // loads still in flight
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+
+  v16f acc[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) acc[i] = v16f{};
+#pragma unroll
+  for (int t = 0; t < HALF; ++t) {
+    if (t < cnt) {
+      const int tt = tb + t;
+      const int bsc0 = (int)((bs[t] >> (8 * j)) & 0xFFu), bsc1 = (int)((bs[t] >> (8 * (2 + j))) & 0xFFu);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int R = 32 * i + c, rr = R & 15;
+        const uint8_t* row = sa + (tt * RB + (R >> 4)) * 1024 + rr * 64;
+        const v4i a0 = *reinterpret_cast<const v4i*>(row + 16 * a_slot(rr, j));
+        const v4i a1 = *reinterpret_cast<const v4i*>(row + 16 * a_slot(rr, 2 + j));
+        const uint32_t asw = ssc[tt * SR + R];
+        const int asc0 = (int)((asw >> (8 * j)) & 0xFFu), asc1 = (int)((asw >> (8 * (2 + j))) & 0xFFu);
+        acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(a0), widen(bq[t][0]), acc[i], 4, 4, 0, asc0,
+                                                                  0, bsc0);
+        acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(a1), widen(bq[t][1]), acc[i], 4, 4, 0, asc1,
+                                                                  0, bsc1);
+      }
+    }
+  }
+
+  // --- second-half sums join the first half's through LDS ----------------
+  __syncthreads();  // every wave is done reading the activation range
+  float* red = reinterpret_cast<float*>(sa);  // [2 column groups][TM * 16][64 lanes]
+  if (kh) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) red[((cg * TM + i) * 16 + v) * 64 + lane] = acc[i][v];
+  }
+  __syncthreads();
+  if (kh) return;
+  const int64_t nn = n0 + c;
+  if (nn >= p.N) return;
+  float* out = p.atomic ? p.part + (int64_t)blockIdx.y * p.M * p.N : p.y;
+  const int64_t ld = p.atomic ? p.N : p.ldy;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t m = m0 + 32 * i + 8 * (v >> 2) + 4 * j + (v & 3);
+      if (m < p.M) out[m * ld + nn] = acc[i][v] + red[((cg * TM + i) * 16 + v) * 64 + lane];
+    }
+}
+
 // Split count: enough K splits that the grid fills the CUs, but never more
 // workgroups than can be resident at once (a second partial round of
 // workgroups would double the latency of this one-pass kernel).
@@ -342,15 +508,67 @@ static int ws_splits(int64_t M, int64_t N, int steps) {
   return pick_splits<4, 1, 4, SMAX>(M, N, steps);
 }
 
+// 32x32x64 path: K steps per workgroup at most, and its split count
+constexpr int kMx32Smax = 16;
+
+template <int TM>
+static int pick_splits32(int64_t M, int64_t N, int total_steps) {
+  const int64_t tiles = cdiv(N, 64) * cdiv(M, 32 * TM);
+  constexpr int lds = kMx32Smax * 2 * TM * 1024 + kMx32Smax * (32 * TM > 64 ? 32 * TM : 64) * 4;
+  const int per_cu = lds > 80 * 1024 ? 1 : 2;
+  const int64_t slots = (int64_t)per_cu * device_cu_count();
+  int splits = (int)cdiv(total_steps, kMx32Smax);
+  while ((int64_t)(splits + 1) * tiles <= slots && splits < total_steps) ++splits;
+  const int steps = (int)cdiv(total_steps, splits);
+  return (int)cdiv(total_steps, steps);
+}
+
+static int ws_splits32(int64_t M, int64_t N, int steps) {
+  if (M <= 32) return pick_splits32<1>(M, N, steps);
+  if (M <= 64) return pick_splits32<2>(M, N, steps);
+  return pick_splits32<4>(M, N, steps);
+}
+
 size_t ws_mx_gemm(int64_t M, int64_t N, int64_t Ktot) {
   if (M <= 0 || N <= 0 || Ktot <= 0) return 0;
   const int steps = (int)cdiv(Ktot, 128) + 1;  // + 1: the tail segment may start a step of its own
-  // the largest split count either K-range choice can make for these steps
+  // the largest split count any kernel choice can make for these steps
   int splits = ws_splits<8>(M, N, steps);
   const int s16 = ws_splits<16>(M, N, steps);
   splits = splits > s16 ? splits : s16;
+  if (M > 16) {
+    const int s32 = ws_splits32(M, N, steps);
+    splits = splits > s32 ? splits : s32;
+  }
   return splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
 }
+
+template <int TM>
+static int dispatch32(MxGemmArgs& p, size_t ws_bytes, hipStream_t st) {
+  int splits = pick_splits32<TM>(p.M, p.N, p.total_steps);
+  const size_t slab = (size_t)p.M * p.N * sizeof(float);
+  if (splits > 1 && (!p.part || ws_bytes < (size_t)splits * slab)) {
+    const int fit = p.part ? (int)(ws_bytes / slab) : 0;
+    const int need = (int)cdiv(p.total_steps, kMx32Smax);
+    if (fit >= need && fit >= 2)
+      splits = fit;
+    else if (need == 1)
+      splits = 1;
+    else
+      return launch_serial<4>(p, st);
+  }
+  const int64_t n_tiles = cdiv(p.N, 64), m_tiles = cdiv(p.M, 32 * TM);
+  p.steps_per_split = (int)cdiv(p.total_steps, splits);
+  splits = (int)cdiv(p.total_steps, p.steps_per_split);
+  p.atomic = splits > 1;
+  hipLaunchKernelGGL((k_mx_gemm32<TM, kMx32Smax>), dim3((unsigned)n_tiles, (unsigned)splits, (unsigned)m_tiles),
+                     dim3(256), 0, st, p);
+  int s = check_launch("mx_gemm");
+  if (s || splits == 1) return s;
+  return launch_splitk_reduce(p.part, splits, p.M * p.N, p.y, st);
+}
+
+static bool aligned4(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 3u) == 0; }
 
 static int run_mx(int64_t M, const gbw_act* a, const gbw_weight* w, const gbw_weight* r, int64_t tail, float* y,
                   int32_t flags, void* ws, size_t ws_bytes, void* stream) {
@@ -372,6 +590,15 @@ static int run_mx(int64_t M, const gbw_act* a, const gbw_weight* w, const gbw_we
   p.ldy = w->N;
   p.part = reinterpret_cast<float*>(ws);
   hipStream_t st = as_stream(stream);
+  // 17+ rows with every K segment a whole number of 128-element steps (and
+  // dword-aligned scale rows): the 32x32x64 kernel
+  const bool k128 = a->K % 128 == 0 && w->K % 128 == 0 && (!r || tail % 128 == 0) && aligned4(a->scales) &&
+                    aligned4(w->scales) && (!r || aligned4(r->scales));
+  if (M > 16 && k128) {
+    if (M <= 32) return dispatch32<1>(p, ws_bytes, st);
+    if (M <= 64) return dispatch32<2>(p, ws_bytes, st);
+    return dispatch32<4>(p, ws_bytes, st);
+  }
   // rows per workgroup: up to 64 (more rows are more workgroups along M: a
   // 128-row tile leaves too few workgroups once K is split into 16-step ranges)
   if (mx_smax(p.total_steps) == 16) {

@@ -91,6 +91,10 @@ inline emu_v2h emu_cvt_f16_fp4(uint32_t w, float s, int sel) {
 #define __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, sel) emu_cvt_f16_fp4((w), (s), (sel))
 #define __builtin_amdgcn_perm(a, b, s) ((uint32_t)(a) ^ (uint32_t)(b) ^ (uint32_t)(s))
 #define __builtin_amdgcn_s_waitcnt(x) ((void)0)
+#define __builtin_amdgcn_s_barrier() __syncthreads()
+// direct-to-LDS load: lane l of the wave writes `size` bytes at dst + off + l * size
+#define __builtin_amdgcn_global_load_lds(src, dst, size, off, aux) \
+  memcpy((char*)(void*)(dst) + (off) + (threadIdx.x & 63) * (size), (const void*)(src), (size))
 #define __builtin_amdgcn_wave_barrier() ((void)0)
 #define __builtin_amdgcn_sched_barrier(x) ((void)0)
 #define __builtin_amdgcn_s_setprio(x) ((void)0)

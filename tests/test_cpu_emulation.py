@@ -67,7 +67,8 @@ def test_lut_gemm_in_bounds(build_dir, M, N, K, group):
 
 
 @pytest.mark.parametrize("M,N,K,tail", [(16, 512, 512, 0), (1, 40, 96, 0), (130, 72, 640, 64), (33, 40, 2048, 32),
-                                        (128, 64, 9728, 256)])
+                                        (128, 64, 9728, 256), (130, 72, 640, 128), (40, 100, 1024, 0),
+                                        (200, 70, 512, 0), (64, 33, 256, 128), (17, 64, 128, 0)])
 def test_mx_gemm_in_bounds(build_dir, M, N, K, tail):
     exe = _build(build_dir, "mx_gemm.hip", "drv_mx.cpp", "emu_mx")
     out = _run(exe, M, N, K, tail)

@@ -177,7 +177,8 @@ def test_mx_gemm_single_linear_16x512x512():
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (5, 20, 96), (17, 300, 160), (33, 64, 544), (100, 129, 1056),
-                                   (128, 2560, 9728), (200, 70, 256)])
+                                   (128, 2560, 9728), (200, 70, 256), (17, 64, 128), (40, 130, 640),
+                                   (96, 64, 4096), (129, 100, 1280)])
 def test_mx_gemm_ragged(M, N, K):
     banner(f"mx_gemm {M}x{N}x{K}")
     a, w, ref = _dense_case(M, N, K, 7)
@@ -227,7 +228,7 @@ def test_mx_residual_bitexact():
 
 
 @pytest.mark.parametrize("M,N,K,tail", [(8, 256, 2048, 256), (13, 100, 1024, 96), (128, 2560, 9728, 256),
-                                        (64, 64, 512, 0)])
+                                        (64, 64, 512, 0), (33, 200, 1024, 128), (70, 96, 2048, 256)])
 def test_residual_tail_gemm(M, N, K, tail):
     banner(f"residual_tail_gemm {M}x{N}x{K} tail {tail}")
     p, a, wq, r, rq = _tail_case(M, N, K, max(tail, 96))
