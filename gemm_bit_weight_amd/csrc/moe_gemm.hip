@@ -376,9 +376,13 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
   v4i pa[NA], pb[2];
   uint32_t ps0 = 0, ps1 = 0;
   // with p.scales16 (256-wide tiles only: the 128-wide kernel has no
-  // registers to spare): the scale dwords of stage groups of four, by group parity
+  // registers to spare): the scale dwords of a group of four stages.  The
+  // next group's load goes to fixed registers (s4n*) and is copied to the
+  // current ones (s4c*) when its first stage is stored, one iteration later:
+  // choosing the destination at load time would need the loaded value at
+  // once and stall on every load still in flight.
   constexpr bool S16 = BN == 256;
-  v4i s4a0 = v4i{0, 0, 0, 0}, s4a1 = s4a0, s4b0 = s4a0, s4b1 = s4a0;
+  v4i s4ca = v4i{0, 0, 0, 0}, s4cb = s4ca, s4na = s4ca, s4nb = s4ca;
   uint2 pl;
   const int last = steps - 1;
   auto gload = [&](int s) __attribute__((always_inline)) {
@@ -389,15 +393,8 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
     if (S16 && p.scales16) {
       // one 16-byte load per row covers the scale dwords of stages s .. s+3
       if ((s & 3) == 0) {
-        const v4i a4 = load16(scl0 + (int64_t)s * 4);
-        const v4i b4 = NT != 512 ? load16(scl1 + (int64_t)s * 4) : a4;
-        if ((s >> 2) & 1) {
-          s4a1 = a4;
-          s4b1 = b4;
-        } else {
-          s4a0 = a4;
-          s4b0 = b4;
-        }
+        s4na = load16(scl0 + (int64_t)s * 4);
+        if (NT != 512) s4nb = load16(scl1 + (int64_t)s * 4);
       }
     } else {
       ps0 = *reinterpret_cast<const uint32_t*>(scl0 + (int64_t)s * 4);
@@ -418,8 +415,11 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
     uint8_t* const a = sA0 + buf * kABuf;
     if (S16 && p.scales16) {
       const int kk = k < last ? k : last;
-      const bool odd = (kk >> 2) & 1;
-      const v4i a4 = odd ? s4a1 : s4a0, b4 = odd ? s4b1 : s4b0;
+      if ((kk & 3) == 0) {
+        s4ca = s4na;
+        s4cb = NT != 512 ? s4nb : s4na;
+      }
+      const v4i a4 = s4ca, b4 = s4cb;
       const int e = kk & 3;
       ps0 = (uint32_t)(e == 0 ? a4[0] : e == 1 ? a4[1] : e == 2 ? a4[2] : a4[3]);
       ps1 = (uint32_t)(e == 0 ? b4[0] : e == 1 ? b4[1] : e == 2 ? b4[2] : b4[3]);
