@@ -170,21 +170,41 @@ __global__ __launch_bounds__(1024) void k_route_topk16(const float* __restrict__
 // rounded up to a power of two) each own a contiguous run of chunks; per-run
 // sums, an exclusive scan over the runs of an expert, an inclusive scan over
 // the expert totals, then each thread writes the bases of its own chunks.
+// STAGE: the whole [C][E] count table (at most kScanLds entries) is first
+// copied to LDS by coalesced loads that are all in flight together, so the
+// per-thread runs read LDS instead of walking global memory one load at a time.
+constexpr int kScanLds = 16384;  // 64 KiB of counts
+template <bool STAGE>
 __global__ __launch_bounds__(kMaxExperts) void k_route_scan(const int32_t* __restrict__ counts, int64_t C, int E,
                                                            int32_t* __restrict__ base,
                                                            int32_t* __restrict__ expert_offsets) {
   __shared__ int32_t part[kMaxExperts];
   __shared__ int32_t tot[kMaxExperts];
+  __shared__ int32_t stg[STAGE ? kScanLds : 1];
+  const int tid = threadIdx.x;
+  if (STAGE) {
+    const int n = (int)(C * E);  // <= kScanLds
+    constexpr int U = kScanLds / kMaxExperts;
+    int32_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = u * kMaxExperts + tid;
+      v[u] = i < n ? counts[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) stg[u * kMaxExperts + tid] = v[u];
+    __syncthreads();
+  }
+  const int32_t* const cnt = STAGE ? stg : counts;
   int Ep = 1;
   while (Ep < E) Ep <<= 1;
   const int G = kMaxExperts / Ep;
-  const int tid = threadIdx.x;
   const int e = tid / G, g = tid % G;
   const int64_t per = (C + G - 1) / G;
   const int64_t c0 = g * per, c1 = min(C, c0 + per);
   int32_t s = 0;
   if (e < E)
-    for (int64_t c = c0; c < c1; ++c) s += counts[c * E + e];
+    for (int64_t c = c0; c < c1; ++c) s += cnt[c * E + e];
   part[tid] = s;
   __syncthreads();
   if (g == 0) {
@@ -207,7 +227,7 @@ __global__ __launch_bounds__(kMaxExperts) void k_route_scan(const int32_t* __res
     if (e == E - 1 && g == 0) expert_offsets[E] = tot[E - 1];
     for (int64_t c = c0; c < c1; ++c) {
       base[c * E + e] = run;
-      run += counts[c * E + e];
+      run += cnt[c * E + e];
     }
   }
 }
@@ -262,7 +282,10 @@ static int launch_route(const float* logits, int64_t T, int E, int32_t* ids, flo
     hipLaunchKernelGGL(k_route_topk<K>, dim3(blocks), dim3(kRouteThreads), 0, st, logits, T, E, ids, w, counts);
   int s = check_launch("moe_route(topk)");
   if (s) return s;
-  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(kMaxExperts), 0, st, counts, C, E, base, off);
+  if (C * E <= kScanLds)
+    hipLaunchKernelGGL(k_route_scan<true>, dim3(1), dim3(kMaxExperts), 0, st, counts, C, E, base, off);
+  else
+    hipLaunchKernelGGL(k_route_scan<false>, dim3(1), dim3(kMaxExperts), 0, st, counts, C, E, base, off);
   if ((s = check_launch("moe_route(scan)"))) return s;
   hipLaunchKernelGGL(k_route_scatter<K>, dim3(blocks), dim3(kRouteThreads), 0, st, ids, T, E, base, pt, pp);
   return check_launch("moe_route(scatter)");
@@ -288,7 +311,7 @@ extern "C" int moe_route(const float* logits, int64_t T, int32_t E, int32_t topk
   hipStream_t s = as_stream(stream);
   if (T == 0) {
     // no tokens: every expert offset is zero
-    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(kMaxExperts), 0, s, (const int32_t*)nullptr, (int64_t)0, E,
+    hipLaunchKernelGGL(k_route_scan<false>, dim3(1), dim3(kMaxExperts), 0, s, (const int32_t*)nullptr, (int64_t)0, E,
                        (int32_t*)nullptr, expert_offsets);
     return check_launch("moe_route(empty)");
   }

@@ -16,7 +16,7 @@
 namespace gbw {
 
 constexpr int kQuantThreads = 256;
-constexpr int kAmaxBlocks = 1024;
+constexpr int kAmaxBlocks = 256;  // amax partials; every E4M3 quantizer block reduces all of them
 
 template <typename T>
 struct In8;
@@ -48,6 +48,22 @@ struct In8<float> {
 
 __device__ __forceinline__ uint32_t abs_bits(float f) { return __float_as_uint(f) & 0x7FFFFFFFu; }
 
+// Row and first column of 8-element unit u of a [rows][K] tensor.  The unit
+// count fits 32 bits in every tensor below 2^35 elements, where a 32-bit
+// division (a dozen VALU operations) replaces the 64-bit one.
+template <bool WIDE>
+__device__ __forceinline__ void unit_pos(int64_t u, int64_t K, int64_t& row, int64_t& col) {
+  if (WIDE) {
+    row = u / (K / 8);
+    col = (u % (K / 8)) * 8;
+  } else {
+    const uint32_t kg = (uint32_t)(K / 8), uu = (uint32_t)u;
+    const uint32_t r = uu / kg;
+    row = r;
+    col = (int64_t)(uu - r * kg) * 8;
+  }
+}
+
 // max over lanes (lane ^ 1) and, if span == 4, (lane ^ 2): non-negative fp32
 // bit patterns order like unsigned integers.
 template <int SPAN>
@@ -60,7 +76,7 @@ __device__ __forceinline__ uint32_t group_max(uint32_t a) {
 // ---------------------------------------------------------------------------
 // E8M0-B32
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool WIDE>
 __global__ __launch_bounds__(kQuantThreads) void k_quant_e8m0(const T* __restrict__ x, int64_t rows,
                                                              int64_t K, int64_t tail,
                                                              uint8_t* __restrict__ codes,
@@ -69,8 +85,8 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_e8m0(const T* __restric
   const int64_t total = rows * (K / 8);
   const bool live = g < total;
   const int64_t gg = live ? g : total - 1;  // keep the whole wave in the shuffles
-  const int64_t row = gg / (K / 8);
-  const int64_t col = (gg % (K / 8)) * 8;
+  int64_t row, col;
+  unit_pos<WIDE>(gg, K, row, col);
   float v[8];
   In8<T>::load(x + row * K + col, v);
   uint32_t am = 0;
@@ -105,13 +121,20 @@ template <typename T>
 __global__ __launch_bounds__(kQuantThreads) void k_amax_partial(const T* __restrict__ x, int64_t n8,
                                                                uint32_t* __restrict__ partial) {
   __shared__ uint32_t red[kQuantThreads / 64];
+  // four 8-element units per thread in flight at a time
   uint32_t am = 0;
-  for (int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; i < n8;
-       i += (int64_t)gridDim.x * kQuantThreads) {
-    float v[8];
-    In8<T>::load(x + i * 8, v);
+  const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+  for (int64_t i0 = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; i0 < n8; i0 += 4 * stride) {
+    float v[4][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) am = max(am, abs_bits(v[j]));
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * stride;
+      In8<T>::load(x + (i < n8 ? i : i0) * 8, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) am = max(am, abs_bits(v[u][j]));
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, o));
@@ -144,7 +167,7 @@ __device__ float block_reduce_partials(const uint32_t* __restrict__ partial, int
 // ---------------------------------------------------------------------------
 // E4M3-B16 with FP32 tensor scale
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool WIDE>
 __global__ __launch_bounds__(kQuantThreads) void k_quant_e4m3(const T* __restrict__ x, int64_t rows,
                                                              int64_t K, uint8_t* __restrict__ codes,
                                                              uint8_t* __restrict__ scales,
@@ -162,8 +185,8 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_e4m3(const T* __restric
   const int64_t total = rows * (K / 8);
   const bool live = g < total;
   const int64_t gg = live ? g : total - 1;
-  const int64_t row = gg / (K / 8);
-  const int64_t col = (gg % (K / 8)) * 8;
+  int64_t row, col;
+  unit_pos<WIDE>(gg, K, row, col);
   float v[8];
   In8<T>::load(x + row * K + col, v);
   uint32_t am = 0;
@@ -268,13 +291,17 @@ extern "C" int mx_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t
   const int64_t total = rows * (K / 8);
   const unsigned blocks = (unsigned)cdiv(total > 0 ? total : 1, kQuantThreads);
   const bool bf = x_dtype == GBW_DTYPE_BF16;
+  const bool wide = total > (int64_t)UINT32_MAX;
   if (fmt == GBW_FMT_E8M0_B32) {
-    if (bf)
-      hipLaunchKernelGGL(k_quant_e8m0<uint16_t>, dim3(blocks), dim3(kQuantThreads), 0, s,
-                         (const uint16_t*)x, rows, K, tail_copy, codes, scales);
-    else
-      hipLaunchKernelGGL(k_quant_e8m0<float>, dim3(blocks), dim3(kQuantThreads), 0, s, (const float*)x,
-                         rows, K, tail_copy, codes, scales);
+#define GBW_Q8(T, W) \
+  hipLaunchKernelGGL((k_quant_e8m0<T, W>), dim3(blocks), dim3(kQuantThreads), 0, s, (const T*)x, rows, K, tail_copy, \
+                     codes, scales)
+    if (bf) {
+      if (wide) GBW_Q8(uint16_t, true); else GBW_Q8(uint16_t, false);
+    } else {
+      if (wide) GBW_Q8(float, true); else GBW_Q8(float, false);
+    }
+#undef GBW_Q8
     return check_launch("mx_quantize(e8m0)");
   }
   uint32_t* partial = nullptr;
@@ -288,12 +315,15 @@ extern "C" int mx_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t
                          (const float*)x, total, partial);
     if ((st = check_launch("mx_quantize(amax)"))) return st;
   }
-  if (bf)
-    hipLaunchKernelGGL(k_quant_e4m3<uint16_t>, dim3(blocks), dim3(kQuantThreads), 0, s, (const uint16_t*)x,
-                       rows, K, codes, scales, tensor_scale, partial, kAmaxBlocks);
-  else
-    hipLaunchKernelGGL(k_quant_e4m3<float>, dim3(blocks), dim3(kQuantThreads), 0, s, (const float*)x, rows,
-                       K, codes, scales, tensor_scale, partial, kAmaxBlocks);
+#define GBW_Q4(T, W)                                                                                           \
+  hipLaunchKernelGGL((k_quant_e4m3<T, W>), dim3(blocks), dim3(kQuantThreads), 0, s, (const T*)x, rows, K, codes, \
+                     scales, tensor_scale, partial, kAmaxBlocks)
+  if (bf) {
+    if (wide) GBW_Q4(uint16_t, true); else GBW_Q4(uint16_t, false);
+  } else {
+    if (wide) GBW_Q4(float, true); else GBW_Q4(float, false);
+  }
+#undef GBW_Q4
   return check_launch("mx_quantize(e4m3)");
 }
 
