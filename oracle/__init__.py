@@ -38,6 +38,9 @@ from .formats import (  # noqa: F401
     e4m3_round,
     quantize_e8m0_b32,
     quantize_e4m3_b16,
+    ue5m3_decode,
+    ue5m3_round,
+    quantize_e5m3_b16,
     dequantize,
     pack_nibbles,
     unpack_nibbles,

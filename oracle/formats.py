@@ -8,6 +8,9 @@ Formats, as "MXCode: MX-Native Codebook Quantization", Table 1 lists them:
   * E4M3-B16-FP4: E2M1 elements, one E4M3 scale per 16 elements, smallest
     scale 2^-9, largest 448, an optional FP32 tensor scale, 4.50 bits per
     element.
+  * E5M3-B16-FP4: E2M1 elements, one UE5M3 scale per 16 elements, smallest
+    scale 2^-17, largest 114688, an optional FP32 tensor scale, 4.50 bits per
+    element.
 The E2M1 value set {0, 0.5, 1, 1.5, 2, 3, 4, 6} is the OCP MX element type
 that the PRQuant page cites for MXFP4 (§1, "block-wise duality").
 
@@ -27,6 +30,12 @@ Readings taken where the pages leave a step open (all listed in the design doc):
     tensor), block scale code = E4M3 round-to-nearest-even of
     amax_blk / (6*S_T) saturating at 448, element = RNE(|x| / (sd*S_T)),
     every step an fp32 operation in that order.
+  * UE5M3: unsigned, 5 exponent bits with bias 15 (the bias that makes the
+    smallest subnormal (1/8)*2^-14 the 2^-17 of Table 1) and 3 mantissa bits;
+    the all-ones code 0xFF is reserved (not finite), so the largest finite
+    code 0xFE = 1.75*2^16 = 114688, the Table 1 maximum.
+  * E5M3-B16: the E4M3-B16 steps with UE5M3 block scales and
+    S_T = amax / (6*114688).
 """
 
 import numpy as np
@@ -66,6 +75,19 @@ def e4m3_decode(codes):
     return np.where((c & 0x80) != 0, -mag, mag)
 
 
+def ue5m3_decode(codes):
+    """UE5M3 byte -> float64 (unsigned; 5 exponent bits, bias 15; 3 mantissa bits).
+
+    Exponent field 0: (m/8) * 2^-14 (subnormal); otherwise (1 + m/8) * 2^(e-15).
+    0xFF is reserved and decodes to NaN.
+    """
+    c = np.asarray(codes).astype(np.int64)
+    e = (c >> 3) & 0x1F
+    m = c & 7
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -14, (1.0 + m / 8.0) * np.ldexp(1.0, e - 15))
+    return np.where(c == 0xFF, np.nan, mag)
+
+
 # ----------------------------------------------------------------------------
 # Round-to-nearest-even onto a finite grid
 # ----------------------------------------------------------------------------
@@ -102,6 +124,14 @@ _E4M3_POS_GRID = e4m3_decode(np.arange(0, 127))          # codes 0x00..0x7E, inc
 def e4m3_round(s):
     """Non-negative fp32 s -> unsigned E4M3 code, RNE, saturating at 448 (0x7E)."""
     return _round_to_grid(np.asarray(s, dtype=np.float64), _E4M3_POS_GRID)
+
+
+_UE5M3_GRID = ue5m3_decode(np.arange(0, 255))           # codes 0x00..0xFE, increasing
+
+
+def ue5m3_round(s):
+    """Non-negative fp32 s -> UE5M3 code, RNE, saturating at 114688 (0xFE)."""
+    return _round_to_grid(np.asarray(s, dtype=np.float64), _UE5M3_GRID)
 
 
 # ----------------------------------------------------------------------------
@@ -219,26 +249,77 @@ def quantize_e4m3_b16(x, tensor_amax=None):
 
 
 # ----------------------------------------------------------------------------
+# E5M3-B16-FP4 quantizer with FP32 tensor scale
+# ----------------------------------------------------------------------------
+
+UE5M3_MAX = np.float32(114688.0)
+
+
+def tensor_scale_e5m3(amax):
+    """S_T = amax / (6 * 114688) in fp32; 1.0 for an all-zero tensor."""
+    a = np.float32(amax)
+    if a == 0:
+        return np.float32(1.0)
+    return np.float32(a / np.float32(688128.0))
+
+
+def quantize_e5m3_b16(x, tensor_amax=None):
+    """x [rows][K] fp32 -> (codes [rows][K/2], scales uint8 [rows][K/16], S_T fp32).
+
+    The E4M3-B16 steps with UE5M3 block scales (MXCode Table 1, E5M3-B16-FP4
+    row), every step an fp32 operation, in this order:
+      S_T = A / 688128; d = 6 * S_T; s = amax_blk / d; sc = UE5M3_RNE_sat(s);
+      sd = decode(sc); den = sd * S_T; code = sign(x) | RNE_sat(|x| / den)
+    and a block with sd == 0 (or den == 0) encodes as signed zeros.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    rows, K = x.shape
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    A = np.float32(np.max(np.abs(x))) if tensor_amax is None else np.float32(tensor_amax)
+    if x.size == 0:
+        A = np.float32(0.0)
+    S_T = tensor_scale_e5m3(A)
+    blk = x.reshape(rows, K // 16, 16)
+    amax = np.max(np.abs(blk), axis=2).astype(np.float32) if x.size else np.zeros((rows, K // 16), np.float32)
+    d = np.float32(E2M1_MAX * S_T)
+    s = (amax / d).astype(np.float32)
+    sc = ue5m3_round(s)
+    sd = ue5m3_decode(sc).astype(np.float32)
+    den = (sd * S_T).astype(np.float32)
+    ok = den > 0
+    safe = np.where(ok, den, np.float32(1.0)).astype(np.float32)
+    q = (np.abs(blk) / safe[..., None]).astype(np.float32)
+    mag = e2m1_round_magnitude(q)
+    mag = np.where(ok[..., None], mag, 0)
+    sign = np.signbit(blk).astype(np.int64)
+    codes = (mag | (sign << 3)).reshape(rows, K)
+    return pack_nibbles(codes), sc.astype(np.uint8), np.float32(S_T)
+
+
+# ----------------------------------------------------------------------------
 # Dequantization
 # ----------------------------------------------------------------------------
 
 FMT_E8M0_B32 = "e8m0_b32"
 FMT_E4M3_B16 = "e4m3_b16"
+FMT_E5M3_B16 = "e5m3_b16"
+TENSOR_SCALED = (FMT_E4M3_B16, FMT_E5M3_B16)   # formats with an FP32 tensor scale
 
 
 def dequantize(codes, scales, fmt, tensor_scale=None):
     """Packed codes [rows][K/2] + block scales -> float64 [rows][K].
 
-    E8M0-B32: e2m1 * 2^(sc-127).  E4M3-B16: e2m1 * decode(sc) * S_T (S_T
-    defaults to 1, so the product of the two left factors is returned).
+    E8M0-B32: e2m1 * 2^(sc-127).  E4M3-B16 / E5M3-B16: e2m1 * decode(sc) * S_T
+    (S_T defaults to 1, so the product of the two left factors is returned).
     """
     el = e2m1_decode(unpack_nibbles(codes))
     rows, K = el.shape
     if fmt == FMT_E8M0_B32:
         s = e8m0_decode(scales)
         return (el.reshape(rows, K // 32, 32) * s[..., None]).reshape(rows, K)
-    if fmt == FMT_E4M3_B16:
-        s = e4m3_decode(scales)
+    if fmt in TENSOR_SCALED:
+        s = e4m3_decode(scales) if fmt == FMT_E4M3_B16 else ue5m3_decode(scales)
         out = (el.reshape(rows, K // 16, 16) * s[..., None]).reshape(rows, K)
         if tensor_scale is not None:
             out = out * np.float64(np.float32(tensor_scale))

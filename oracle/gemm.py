@@ -17,6 +17,7 @@ import numpy as np
 
 from .formats import (
     FMT_E4M3_B16,
+    TENSOR_SCALED,
     FMT_E8M0_B32,
     bf16_bits_to_f32,
     dequantize,
@@ -28,13 +29,13 @@ from .formats import (
 def mx_gemm(a_codes, a_scales, w_codes, w_scales, fmt=FMT_E8M0_B32, a_ts=None, w_ts=None):
     """Y[m][n] = sum_k deq(A)[m][k] * deq(W)[n][k] in float64.
 
-    For E4M3-B16 the tensor scales are applied once to the exact sum:
+    For E4M3-B16 and E5M3-B16 the tensor scales are applied once to the exact sum:
     Y = S_Ta * S_Tw * sum_k (e2m1*sd)_a (e2m1*sd)_w.
     """
     a = dequantize(a_codes, a_scales, fmt)
     w = dequantize(w_codes, w_scales, fmt)
     y = a @ w.T
-    if fmt == FMT_E4M3_B16:
+    if fmt in TENSOR_SCALED:
         sa = 1.0 if a_ts is None else float(np.float32(a_ts))
         sw = 1.0 if w_ts is None else float(np.float32(w_ts))
         y = y * sa * sw

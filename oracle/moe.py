@@ -21,6 +21,7 @@ import numpy as np
 
 from .formats import (
     FMT_E4M3_B16,
+    TENSOR_SCALED,
     bf16_bits_to_f32,
     dequantize,
     f32_to_bf16_bits,
@@ -82,7 +83,7 @@ def moe_gateup(a_codes, a_scales, fmt, route, wgu_codes, wgu_scales, a_ts=None, 
         a = dequantize(a_codes[toks], a_scales[toks], fmt)
         w = dequantize(wgu_codes[e], wgu_scales[e], fmt)
         out = a @ w.T
-        if fmt == FMT_E4M3_B16:
+        if fmt in TENSOR_SCALED:
             sa = float(np.float32(a_ts))
             out[:, :I] *= sa * float(np.float32(wgu_ts[e][0]))
             out[:, I:] *= sa * float(np.float32(wgu_ts[e][1]))
@@ -152,7 +153,7 @@ def moe_down_combine(h_codes, h_scales, fmt, route, wd_codes, wd_scales, h_ts=No
         j = np.argmax(ids[t] == e, axis=1)          # the slot that chose e
         a = dequantize(h_codes[p], h_scales[p], fmt)
         out = a @ dequantize(wd_codes[e], wd_scales[e], fmt).T
-        if fmt == FMT_E4M3_B16:
+        if fmt in TENSOR_SCALED:
             out = out * (float(np.float32(h_ts)) * float(np.float32(wd_ts[e])))
         np.add.at(y, row_of[t], w[t, j][:, None] * out)
     return y

@@ -64,6 +64,26 @@ def test_e4m3_extremes_table1_and_torch_decode():
     assert np.array_equal(ref[~both_nan], dec[~both_nan])
 
 
+def test_ue5m3_extremes_table1_and_fp16_bit_layout():
+    """UE5M3 has fp16's exponent field (5 bits, bias 15) and the top 3 of its
+    mantissa bits: for exponent fields 0..30 a code c is numpy's float16 with
+    bits c << 7; exponent field 31 (infinite/NaN in fp16) continues the
+    binade scale by one more factor of two.  Table 1: smallest scale 2^-17,
+    largest 114688."""
+    f = GOLD["formats"]["E5M3-B16-FP4"]
+    dec = oracle.ue5m3_decode(np.arange(256))
+    low = np.arange(0, 248)
+    ref = (low.astype(np.uint16) << 7).view(np.float16).astype(np.float64)
+    assert np.array_equal(dec[low], ref)
+    top = np.arange(248, 255)
+    assert np.array_equal(dec[top], 2.0 * dec[top - 8])
+    pos = dec[1:255]
+    assert pos.min() == 2.0 ** f["min_scale_log2"]
+    assert pos.max() == f["max_scale"]
+    assert np.all(np.diff(dec[:255]) > 0)
+    assert np.isnan(dec[255])
+
+
 # ---------------------------------------------------------------------------
 # E2M1 round-to-nearest-even
 # ---------------------------------------------------------------------------
@@ -188,6 +208,8 @@ def test_bpe_table1():
     assert (c.nbytes + s.nbytes) * 8 / x.size == GOLD["formats"]["E8M0-B32-FP4"]["bpe"]
     c, s, _ = oracle.quantize_e4m3_b16(x)
     assert (c.nbytes + s.nbytes) * 8 / x.size == GOLD["formats"]["E4M3-B16-FP4"]["bpe"]
+    c, s, _ = oracle.quantize_e5m3_b16(x)
+    assert (c.nbytes + s.nbytes) * 8 / x.size == GOLD["formats"]["E5M3-B16-FP4"]["bpe"]
 
 
 # ---------------------------------------------------------------------------
@@ -262,6 +284,85 @@ def test_e4m3_b16_zero_tensor():
     assert st == 1.0 and np.all(scales == 0) and np.all(codes == 0)
 
 
+# ---------------------------------------------------------------------------
+# UE5M3 rounding and the E5M3-B16 quantizer
+# ---------------------------------------------------------------------------
+
+def _nearest_code_brute(s, grid):
+    """Brute force: the grid index nearest to s, ties to the even index,
+    values above the grid saturating to its last point."""
+    out = []
+    for v in s:
+        if v >= grid[-1]:
+            out.append(len(grid) - 1)
+            continue
+        d = np.abs(grid - v)
+        best = np.flatnonzero(d == d.min())
+        out.append(int(best[0]) if len(best) == 1 else int(best[best % 2 == 0][0]))
+    return np.array(out)
+
+
+def test_ue5m3_rne_brute_force():
+    rng = np.random.default_rng(12)
+    grid = oracle.ue5m3_decode(np.arange(255))
+    s = np.concatenate([
+        np.exp2(rng.uniform(-20, 17.2, 4000)),
+        grid,                                                   # every grid point
+        (grid[:-1] + grid[1:]) / 2,                             # every midpoint (ties)
+        [0.0, 2.0 ** -18, 3 * 2.0 ** -19, 114688.0, 118784.0, 1e30],
+    ]).astype(np.float32)
+    assert np.array_equal(oracle.ue5m3_round(s), _nearest_code_brute(s.astype(np.float64), grid))
+    assert list(oracle.ue5m3_round(np.float32([114688.0, 118784.0, 3e38]))) == [0xFE, 0xFE, 0xFE]
+
+
+def test_e5m3_b16_tensor_amax_element_maps_to_top_codes():
+    """S_T = amax/(6*114688): the largest element's block gets scale code 0xFE
+    (114688) and the element encodes to magnitude code 7 (6)."""
+    rng = np.random.default_rng(13)
+    for trial in range(50):
+        x = (rng.standard_normal((4, 64)) * np.exp(rng.uniform(-30, 30))).astype(np.float32)
+        codes, scales, st = oracle.quantize_e5m3_b16(x)
+        r, c = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+        assert scales[r, c // 16] == 0xFE
+        assert (oracle.unpack_nibbles(codes)[r, c] & 7) == 7
+        assert st == np.float32(np.float32(np.abs(x).max()) / np.float32(688128.0))
+
+
+def test_e5m3_b16_elements_and_scales_are_nearest_grid_points():
+    rng = np.random.default_rng(14)
+    x = (rng.standard_normal((16, 128)) * np.exp(rng.uniform(-8, 8, (16, 8)).repeat(16, 1))).astype(np.float32)
+    codes, scales, st = oracle.quantize_e5m3_b16(x)
+    # block scales: brute-force nearest UE5M3 grid point of amax / (6 S_T)
+    amax = np.abs(x.reshape(16, 8, 16)).max(-1).astype(np.float32)
+    sv = (amax / np.float32(np.float32(6.0) * st)).astype(np.float32)
+    grid = oracle.ue5m3_decode(np.arange(255))
+    assert np.array_equal(scales.reshape(-1), _nearest_code_brute(sv.reshape(-1).astype(np.float64), grid))
+    # elements: nearest E2M1 magnitude of |x| / (sd S_T)
+    sd = oracle.ue5m3_decode(scales).astype(np.float32)
+    den = (sd * st).astype(np.float32).repeat(16, axis=1)
+    q = (np.abs(x) / den).astype(np.float32).astype(np.float64)
+    el = oracle.e2m1_decode(oracle.unpack_nibbles(codes))
+    e2 = np.array(GOLD["e2m1_values"]["magnitudes"])
+    assert np.all(np.abs(q - np.abs(el)) == np.abs(q[..., None] - e2).min(axis=-1))
+    assert np.array_equal(np.signbit(el), np.signbit(x))
+
+
+def test_e5m3_b16_decoded_values_exact_in_bf16_not_fp16():
+    """e2m1 * sd (UE5M3) has at most 6 significant bits and spans
+    [2^-18, 6*114688]: exact in bf16; beyond fp16's largest finite value."""
+    el = oracle.e2m1_decode(np.arange(16))
+    sd = oracle.ue5m3_decode(np.arange(0, 255))
+    prod = (el[:, None] * sd[None, :]).astype(np.float32)
+    bf = torch.from_numpy(prod).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(bf, prod)
+    assert np.abs(prod).max() == 6 * 114688.0 > 65504.0
+
+
+def test_e5m3_b16_zero_tensor():
+    codes, scales, st = oracle.quantize_e5m3_b16(np.zeros((2, 32), np.float32))
+    assert st == 1.0 and np.all(scales == 0) and np.all(codes == 0)
+
+
 def test_bf16_helpers():
     x = np.array([1.0, 1.00390625, 1.005859375, -2.5, 3.0e38], np.float32)
     b = oracle.f32_to_bf16_bits(x)
@@ -270,14 +371,15 @@ def test_bf16_helpers():
     assert np.array_equal(oracle.bf16_bits_to_f32(b), torch.from_numpy(x).to(torch.bfloat16).float().numpy())
 
 
-@pytest.mark.parametrize("fmt", ["e8m0_b32", "e4m3_b16"])
+@pytest.mark.parametrize("fmt", ["e8m0_b32", "e4m3_b16", "e5m3_b16"])
 def test_dequantize_shapes(fmt):
     x = np.random.default_rng(6).standard_normal((3, 64)).astype(np.float32)
     if fmt == "e8m0_b32":
         c, s = oracle.quantize_e8m0_b32(x)
         d = oracle.dequantize(c, s, fmt)
     else:
-        c, s, st = oracle.quantize_e4m3_b16(x)
+        q = oracle.quantize_e4m3_b16 if fmt == "e4m3_b16" else oracle.quantize_e5m3_b16
+        c, s, st = q(x)
         d = oracle.dequantize(c, s, fmt, st)
     assert d.shape == x.shape
     assert np.max(np.abs(d - x)) < 0.5 * np.max(np.abs(x))

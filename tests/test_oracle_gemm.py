@@ -100,15 +100,17 @@ def test_mx_gemm_k_permutation_and_transpose():
     assert np.array_equal(oracle.mx_gemm(wc, ws, ac, as_), y.T)
 
 
-def test_mx_gemm_e4m3_tensor_scales():
+@pytest.mark.parametrize("fmt", ["e4m3_b16", "e5m3_b16"])
+def test_mx_gemm_tensor_scaled_formats(fmt):
     rng = np.random.default_rng(9)
     x = rng.standard_normal((5, 64)).astype(np.float32)
     w = (rng.standard_normal((7, 64)) * 0.02).astype(np.float32)
-    ac, as_, ats = oracle.quantize_e4m3_b16(x)
-    wc, ws, wts = oracle.quantize_e4m3_b16(w)
-    y = oracle.mx_gemm(ac, as_, wc, ws, "e4m3_b16", ats, wts)
-    a = oracle.dequantize(ac, as_, "e4m3_b16", ats)
-    b = oracle.dequantize(wc, ws, "e4m3_b16", wts)
+    q = oracle.quantize_e4m3_b16 if fmt == "e4m3_b16" else oracle.quantize_e5m3_b16
+    ac, as_, ats = q(x)
+    wc, ws, wts = q(w)
+    y = oracle.mx_gemm(ac, as_, wc, ws, fmt, ats, wts)
+    a = oracle.dequantize(ac, as_, fmt, ats)
+    b = oracle.dequantize(wc, ws, fmt, wts)
     # brute force over exact rationals
     for m in range(5):
         for n in range(7):

@@ -96,11 +96,12 @@ def _quant_moe_weights(w_gu, w_d, fmt):
             c, s = oracle.quantize_e8m0_b32(w_d[e])
             out["d_c"].append(c); out["d_s"].append(s)
         else:
-            cg, sg, tg = oracle.quantize_e4m3_b16(w_gu[e][:I])
-            cu, su, tu = oracle.quantize_e4m3_b16(w_gu[e][I:])
+            q = oracle.quantize_e4m3_b16 if fmt == "e4m3_b16" else oracle.quantize_e5m3_b16
+            cg, sg, tg = q(w_gu[e][:I])
+            cu, su, tu = q(w_gu[e][I:])
             out["gu_c"].append(np.concatenate([cg, cu])); out["gu_s"].append(np.concatenate([sg, su]))
             out["gu_t"].append([tg, tu])
-            c, s, t = oracle.quantize_e4m3_b16(w_d[e])
+            c, s, t = q(w_d[e])
             out["d_c"].append(c); out["d_s"].append(s); out["d_t"].append(t)
     return {k: np.array(v) for k, v in out.items()}
 
@@ -109,7 +110,7 @@ def _quant_act(x, fmt):
     if fmt == "e8m0_b32":
         c, s = oracle.quantize_e8m0_b32(x)
         return c, s, None
-    return oracle.quantize_e4m3_b16(x)
+    return (oracle.quantize_e4m3_b16 if fmt == "e4m3_b16" else oracle.quantize_e5m3_b16)(x)
 
 
 def _ffn(x, logits, w_gu, w_d, topk, fmt, tokens=None):
@@ -124,7 +125,7 @@ def _ffn(x, logits, w_gu, w_d, topk, fmt, tokens=None):
     return y, dict(W=W, route=route, g=g, u=u, h=h, hc=hc, hs=hs, ht=ht, ac=ac, as_=as_, at=at)
 
 
-@pytest.mark.parametrize("fmt", ["e8m0_b32", "e4m3_b16"])
+@pytest.mark.parametrize("fmt", ["e8m0_b32", "e4m3_b16", "e5m3_b16"])
 def test_one_expert_top1_is_dense_swiglu_ffn(fmt):
     rng = np.random.default_rng(20)
     T, H, I = 9, 64, 96
