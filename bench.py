@@ -258,7 +258,10 @@ def dense_small(gbw, synth, torch):
     return {"M": 16, "N": 512, "K": 512, "us_per_call": _graph_time(torch, fn, 50)}
 
 
-def moe_e4m3(gbw, synth, torch, steps=5):
+def moe_e4m3(gbw, synth, torch, steps=5, fmt=None):
+    """The tensor-scaled MoE workload (E4M3-B16 by default; E5M3-B16 with
+    fmt=gbw.FMT_E5M3_B16, decoded to bf16 instead of fp16)."""
+    fmt = gbw.FMT_E4M3_B16 if fmt is None else fmt
     T, H, I, E, K = 4096, 2048, 768, 128, 8
     d = synth.moe_problem(T, H, I, E, seed=0, device="cuda")
     dev = "cuda"
@@ -271,22 +274,22 @@ def moe_e4m3(gbw, synth, torch, steps=5):
     for e in range(E):
         for half in range(2):
             rows = slice(half * I, (half + 1) * I)
-            gbw.mx_quantize(d["w_gate_up"][e, rows].contiguous(), gbw.FMT_E4M3_B16,
-                            out=gbw.Act(1, gc[e, rows], gs[e, rows]), tensor_scale=gt[e, half:half + 1], dynamic=True)
-        gbw.mx_quantize(d["w_down"][e].contiguous(), gbw.FMT_E4M3_B16, out=gbw.Act(1, dc[e], ds[e]),
+            gbw.mx_quantize(d["w_gate_up"][e, rows].contiguous(), fmt,
+                            out=gbw.Act(fmt, gc[e, rows], gs[e, rows]), tensor_scale=gt[e, half:half + 1], dynamic=True)
+        gbw.mx_quantize(d["w_down"][e].contiguous(), fmt, out=gbw.Act(fmt, dc[e], ds[e]),
                         tensor_scale=dt[e], dynamic=True)
     del d["w_gate_up"], d["w_down"]
-    Wgu = gbw.Weight(gbw.FMT_E4M3_B16, 2 * I, H, gc, gs, None, gt, 2, E)
-    Wd = gbw.Weight(gbw.FMT_E4M3_B16, H, I, dc, ds, None, dt, 1, E)
+    Wgu = gbw.Weight(fmt, 2 * I, H, gc, gs, None, gt, 2, E)
+    Wd = gbw.Weight(fmt, H, I, dc, ds, None, dt, 1, E)
     P = T * K
     hb = torch.empty((P, I), dtype=torch.bfloat16, device=dev)
     y = torch.empty((T, H), dtype=torch.float32, device=dev)
 
     def step():
         route = gbw.moe_route(d["logits"], K)
-        xq = gbw.mx_quantize(d["x"], gbw.FMT_E4M3_B16)
+        xq = gbw.mx_quantize(d["x"], fmt)
         gbw.moe_grouped_gemm(gbw.MOE_GATEUP_SWIGLU, route, xq, Wgu, h_bf16=hb)
-        hq = gbw.mx_quantize(hb, gbw.FMT_E4M3_B16)
+        hq = gbw.mx_quantize(hb, fmt)
         gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, Wd, y=y)
     step()
     torch.cuda.synchronize()
@@ -299,7 +302,8 @@ def moe_e4m3(gbw, synth, torch, steps=5):
     ms = e0.elapsed_time(e1) / steps
     flops = 2.0 * P * 3 * H * I
     return {"T": T, "hidden": H, "intermediate": I, "experts": E, "topk": K, "ms_per_step": ms,
-            "TFLOP_s": flops / ms / 1e9, "frac_f16_mfma": flops / ms / 1e9 / F16_PEAK_TFLOPS,
+            "TFLOP_s": flops / ms / 1e9,
+            ("frac_bf16_mfma" if fmt == gbw.FMT_E5M3_B16 else "frac_f16_mfma"): flops / ms / 1e9 / F16_PEAK_TFLOPS,
             "frac_mxfp4_mfma": flops / ms / 1e9 / MXFP4_PEAK_TFLOPS}
 
 
@@ -364,7 +368,9 @@ def main():
                          "residual_tail_gemm": tail_decode(gbw, synth, torch)}
         torch.cuda.empty_cache()
         log("extra: E4M3-B16 MoE, 16x512x512 linear")
-        out["extra"] = {"moe_e4m3_b16": moe_e4m3(gbw, synth, torch), "mx_gemm_16x512x512": dense_small(gbw, synth, torch)}
+        out["extra"] = {"moe_e4m3_b16": moe_e4m3(gbw, synth, torch),
+                        "moe_e5m3_b16": moe_e4m3(gbw, synth, torch, fmt=gbw.FMT_E5M3_B16),
+                        "mx_gemm_16x512x512": dense_small(gbw, synth, torch)}
     print(json.dumps(out), flush=True)
 
 

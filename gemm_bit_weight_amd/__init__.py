@@ -31,6 +31,7 @@ STATUS_NAMES = {0: "GBW_OK", 1: "GBW_E_ARG", 2: "GBW_E_SHAPE", 3: "GBW_E_ALIGN",
 FMT_E8M0_B32 = 0
 FMT_E4M3_B16 = 1
 FMT_VQ4_E8M0 = 2
+FMT_E5M3_B16 = 3
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
 TS_DYNAMIC = 1
@@ -185,8 +186,8 @@ def mx_quantize(x, fmt=FMT_E8M0_B32, tail_copy=0, tensor_scale=None, dynamic=Non
                 stream=None):
     """Quantize x [rows][K] (bf16 or fp32, on the GPU) -> Act.
 
-    E4M3-B16: the tensor scale is computed from x unless ``tensor_scale`` (a
-    1-element fp32 device tensor) is given.
+    E4M3-B16 / E5M3-B16: the tensor scale is computed from x unless
+    ``tensor_scale`` (a 1-element fp32 device tensor) is given.
     """
     assert x.dim() == 2 and x.is_contiguous()
     rows, K = x.shape
@@ -201,7 +202,7 @@ def mx_quantize(x, fmt=FMT_E8M0_B32, tail_copy=0, tensor_scale=None, dynamic=Non
         codes, scales = out.codes, out.scales
     flags = 0
     ts = None
-    if fmt == FMT_E4M3_B16:
+    if fmt in (FMT_E4M3_B16, FMT_E5M3_B16):
         if dynamic is None:
             dynamic = tensor_scale is None
         if dynamic:
@@ -234,7 +235,7 @@ def mx_residual(w_f32, codes, scales, tail, out=None, stream=None):
 
 
 def weight_from_act(a: Act) -> Weight:
-    """View a quantized [N][K] matrix (E8M0-B32 or E4M3-B16) as a one-expert weight."""
+    """View a quantized [N][K] matrix (E8M0-B32, E4M3-B16 or E5M3-B16) as a one-expert weight."""
     return Weight(a.fmt, a.rows, a.K, a.codes, a.scales, None, a.tensor_scale, 1, 1)
 
 

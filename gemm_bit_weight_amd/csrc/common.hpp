@@ -82,6 +82,28 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   return __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
+// Non-negative fp32 -> UE5M3 code (5 exponent bits with bias 15, 3 mantissa
+// bits, no sign), round to nearest even, saturating at 114688 (0xFE; the
+// all-ones code is reserved).
+__device__ __forceinline__ uint32_t ue5m3_rne_sat(float s) {
+  if (!(s < 114688.0f)) return 0xFEu;
+  const uint32_t b = __float_as_uint(s);
+  const int e = (int)((b >> 23) & 0xFFu) - 127;
+  if (e < -14) {
+    // subnormal range: multiples of 2^-17; an exact power-of-two product, then RNE
+    return (uint32_t)__builtin_rintf(s * 131072.0f);
+  }
+  const uint32_t m = b & 0x7FFFFFu;
+  const uint32_t r = (m + 0x7FFFFu + ((m >> 20) & 1u)) >> 20;  // 0..8, 8 carries into the exponent
+  return ((uint32_t)(e + 15) << 3) + r;
+}
+
+__device__ __forceinline__ float ue5m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 0x1Fu, m = c & 7u;
+  if (e == 0) return (float)m * 7.62939453125e-06f;  // m * 2^-17
+  return __uint_as_float(((e + 112u) << 23) | (m << 20));
+}
+
 // ---------------------------------------------------------------------------
 // bf16
 // ---------------------------------------------------------------------------

@@ -34,6 +34,8 @@
 // For GATEUP the weight rows of a tile are gate rows and the up rows of the
 // same intermediate columns, arranged so that each wave holds g and u of the
 // same (row, column) in its own accumulators.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace gbw {
@@ -611,6 +613,22 @@ __device__ __forceinline__ void e4m3_decode8(uint32_t w, uint32_t sc2, uint32_t 
   o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sv);
 }
 
+// E5M3-B16: the four code bytes of a dword -> four bf16x2 words in element
+// order.  v_cvt_scalef32_pk_f32_fp4 at scale 1 gives the two E2M1 values of a
+// byte exactly; times the UE5M3 block scale in fp32 (exact: at most 6
+// significant bits) and one v_cvt_pk_bf16_f32 (exact for the same reason).
+// fp16 cannot hold these products (they reach 6 * 114688).
+__device__ __forceinline__ void e5m3_decode8(uint32_t w, float sd, uint32_t (&o)[4]) {
+  const v2f a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const v2f b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const v2f c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const v2f d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  o[0] = cvt_pk_bf16(a[0] * sd, a[1] * sd);
+  o[1] = cvt_pk_bf16(b[0] * sd, b[1] * sd);
+  o[2] = cvt_pk_bf16(c[0] * sd, c[1] * sd);
+  o[3] = cvt_pk_bf16(d[0] * sd, d[1] * sd);
+}
+
 // E4M3 scale code -> fp16 bits duplicated into both halves (exact: an E4M3
 // value has 4 significant bits and lies in [2^-9, 448])
 __device__ __forceinline__ uint32_t e4m3_to_h2(uint32_t c) {
@@ -625,7 +643,9 @@ __device__ __forceinline__ uint32_t e4m3_to_h2(uint32_t c) {
 // twice the 16x16 rate).  Stage = 64 K elements: threads 0..255 decode row tid
 // of A, 256..511 row tid-256 of B, into fp16 LDS rows of 128 bytes + 16 of
 // padding.  Same single-barrier pipeline as the FP4 kernel: stage s+1 is
-// decoded into LDS before the MFMAs of stage s.
+// decoded into LDS before the MFMAs of stage s.  E5 = true: E5M3-B16 operands,
+// decoded to bf16 and contracted with v_mfma_f32_32x32x16_bf16 (same layout).
+template <bool E5>
 __global__ __launch_bounds__(kE4Threads) void k_moe_e4m3(const MoeArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][kMoeBM * kRowH];
   __shared__ __attribute__((aligned(16))) uint8_t sB[2][kE4BN * kRowH];
@@ -690,7 +710,10 @@ __global__ __launch_bounds__(kE4Threads) void k_moe_e4m3(const MoeArgs p) {
     for (int d = 0; d < 8; ++d) {
       // dword d of the 32 code bytes holds elements 8d..8d+7, scale block d/2
       uint32_t o[4];
-      e4m3_decode8((uint32_t)pc[d >> 2][d & 3], e4m3_to_h2(ps >> (8 * (d >> 1))), o);
+      if constexpr (E5)
+        e5m3_decode8((uint32_t)pc[d >> 2][d & 3], ue5m3_value((ps >> (8 * (d >> 1))) & 0xFFu), o);
+      else
+        e4m3_decode8((uint32_t)pc[d >> 2][d & 3], e4m3_to_h2(ps >> (8 * (d >> 1))), o);
       *reinterpret_cast<v4i*>(dst + 16 * d) = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
     }
   };
@@ -715,17 +738,23 @@ __global__ __launch_bounds__(kE4Threads) void k_moe_e4m3(const MoeArgs p) {
     constexpr int NB = decltype(nb)::value;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {  // four 16-element MFMA steps per 64-element stage
-      v8h bf[4], af[2];
+      typedef typename std::conditional<E5, v8bf, v8h>::type frag;
+      frag bf[4], af[2];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        bf[j] = *reinterpret_cast<const v8h*>(&sB[buf][(brow[j] + l32) * kRowH + 32 * ks + 16 * g2]);
+        bf[j] = *reinterpret_cast<const frag*>(&sB[buf][(brow[j] + l32) * kRowH + 32 * ks + 16 * g2]);
 #pragma unroll
       for (int i = 0; i < NB; ++i)
-        af[i] = *reinterpret_cast<const v8h*>(&sA[buf][(64 * wm + 32 * i + l32) * kRowH + 32 * ks + 16 * g2]);
+        af[i] = *reinterpret_cast<const frag*>(&sA[buf][(64 * wm + 32 * i + l32) * kRowH + 32 * ks + 16 * g2]);
 #pragma unroll
       for (int i = 0; i < NB; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (E5)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
     }
   };
   auto kloop = [&](auto nb) __attribute__((always_inline)) {
@@ -778,8 +807,11 @@ int launch_moe_bf16(const MoeArgs& p, const gbw_act* a, const gbw_weight* w, int
   q.a_ts = a->tensor_scale;
   q.w_ts = w->tensor_scale;
   q.ts_per = w->ts_per_expert;
-  hipLaunchKernelGGL(k_moe_e4m3, dim3((unsigned)grid), dim3(kE4Threads), 0, st, q);
-  return check_launch("moe_grouped_gemm(e4m3)");
+  if (w->fmt == GBW_FMT_E5M3_B16)
+    hipLaunchKernelGGL(k_moe_e4m3<true>, dim3((unsigned)grid), dim3(kE4Threads), 0, st, q);
+  else
+    hipLaunchKernelGGL(k_moe_e4m3<false>, dim3((unsigned)grid), dim3(kE4Threads), 0, st, q);
+  return check_launch("moe_grouped_gemm(e4m3/e5m3)");
 }
 
 // y[t][n] = sum_j topk_w[t][j] * slots[pair_pos[t][j]][n], j = 0..topk-1 in
@@ -845,18 +877,19 @@ extern "C" int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const in
                              (long long)K);
   if (K <= 0 || K % 128) return fail(GBW_E_SHAPE, "moe_grouped_gemm: K must be a positive multiple of 128");
   const bool fp4 = (w->fmt == GBW_FMT_E8M0_B32 || w->fmt == GBW_FMT_VQ4_E8M0) && a->fmt == GBW_FMT_E8M0_B32;
-  const bool e4m3 = w->fmt == GBW_FMT_E4M3_B16 && a->fmt == GBW_FMT_E4M3_B16;
+  // E4M3-B16 or E5M3-B16 (tensor-scaled, decoded exactly to fp16 / bf16)
+  const bool e4m3 = (w->fmt == GBW_FMT_E4M3_B16 || w->fmt == GBW_FMT_E5M3_B16) && a->fmt == w->fmt;
   if (!fp4 && !e4m3) return fail(GBW_E_UNSUPPORTED, "moe_grouped_gemm: unsupported activation/weight formats");
   if (stage == GBW_MOE_GATEUP_SWIGLU) {
     if (N % 256) return fail(GBW_E_SHAPE, "moe_grouped_gemm: gate/up rows (2I) must be a multiple of 256");
     if (e4m3 && w->ts_per_expert != 2)
-      return fail(GBW_E_ARG, "moe_grouped_gemm: E4M3 gate/up needs two tensor scales per expert (gate, up)");
+      return fail(GBW_E_ARG, "moe_grouped_gemm: E4M3/E5M3 gate/up needs two tensor scales per expert (gate, up)");
     if (a->rows < T) return fail(GBW_E_SHAPE, "moe_grouped_gemm: activation has fewer rows than tokens");
     if (fp4 && (!out->h_codes || !out->h_scales) && !out->h_bf16)
       return fail(GBW_E_ARG, "moe_grouped_gemm: gate/up needs h_codes+h_scales or h_bf16");
     if (fp4 && (!out->h_codes) != (!out->h_scales))
       return fail(GBW_E_ARG, "moe_grouped_gemm: h_codes and h_scales go together");
-    if (e4m3 && !out->h_bf16) return fail(GBW_E_ARG, "moe_grouped_gemm: E4M3 gate/up writes h_bf16");
+    if (e4m3 && !out->h_bf16) return fail(GBW_E_ARG, "moe_grouped_gemm: E4M3/E5M3 gate/up writes h_bf16");
   } else {
     if (N % 256) return fail(GBW_E_SHAPE, "moe_grouped_gemm: down rows (H) must be a multiple of 256");
     if (a->rows < P) return fail(GBW_E_SHAPE, "moe_grouped_gemm: activation has fewer rows than pairs");
@@ -864,7 +897,7 @@ extern "C" int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const in
   }
   if (w->fmt == GBW_FMT_VQ4_E8M0 && !w->codebook) return fail(GBW_E_ARG, "moe_grouped_gemm: VQ needs a codebook");
   if (e4m3 && (!w->tensor_scale || !a->tensor_scale || w->ts_per_expert < 1))
-    return fail(GBW_E_ARG, "moe_grouped_gemm: E4M3 needs tensor scales");
+    return fail(GBW_E_ARG, "moe_grouped_gemm: E4M3/E5M3 needs tensor scales");
   if (T == 0) return GBW_OK;
   if (!expert_offsets || !pair_token || !pair_pos || !topk_w || !a->codes || !a->scales || !w->codes || !w->scales)
     return fail(GBW_E_ARG, "moe_grouped_gemm: null pointer");

@@ -147,8 +147,12 @@ __global__ __launch_bounds__(kQuantThreads) void k_amax_partial(const T* __restr
   }
 }
 
-// S_T = amax / (6 * 448) in fp32, 1 for an all-zero tensor.
-__device__ __forceinline__ float tensor_scale_from_amax(float a) { return a == 0.0f ? 1.0f : a / 2688.0f; }
+// S_T = amax / (6 * 448) (E4M3 scales) or amax / (6 * 114688) (UE5M3 scales)
+// in fp32, 1 for an all-zero tensor.
+template <bool E5>
+__device__ __forceinline__ float tensor_scale_from_amax(float a) {
+  return a == 0.0f ? 1.0f : a / (E5 ? 688128.0f : 2688.0f);
+}
 
 __device__ float block_reduce_partials(const uint32_t* __restrict__ partial, int n) {
   __shared__ uint32_t red[kQuantThreads / 64];
@@ -165,9 +169,9 @@ __device__ float block_reduce_partials(const uint32_t* __restrict__ partial, int
 }
 
 // ---------------------------------------------------------------------------
-// E4M3-B16 with FP32 tensor scale
+// E4M3-B16 and E5M3-B16 (E5 = true: UE5M3 block scales) with FP32 tensor scale
 // ---------------------------------------------------------------------------
-template <typename T, bool WIDE>
+template <typename T, bool WIDE, bool E5>
 __global__ __launch_bounds__(kQuantThreads) void k_quant_e4m3(const T* __restrict__ x, int64_t rows,
                                                              int64_t K, uint8_t* __restrict__ codes,
                                                              uint8_t* __restrict__ scales,
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_e4m3(const T* __restric
                                                              int n_partial) {
   float S_T;
   if (partial != nullptr) {
-    S_T = tensor_scale_from_amax(block_reduce_partials(partial, n_partial));
+    S_T = tensor_scale_from_amax<E5>(block_reduce_partials(partial, n_partial));
     if (blockIdx.x == 0 && threadIdx.x == 0) tensor_scale[0] = S_T;
   } else {
     S_T = tensor_scale[0];
@@ -195,8 +199,8 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_e4m3(const T* __restric
   am = group_max<2>(am);
   const float d = 6.0f * S_T;
   const float s = __uint_as_float(am) / d;
-  const uint32_t sc = e4m3_rne_sat(s);
-  const float den = e4m3_value(sc) * S_T;
+  const uint32_t sc = E5 ? ue5m3_rne_sat(s) : e4m3_rne_sat(s);
+  const float den = (E5 ? ue5m3_value(sc) : e4m3_value(sc)) * S_T;
   uint32_t word = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -222,7 +226,8 @@ __device__ __forceinline__ float decode_elem(int32_t fmt, const uint8_t* codes, 
   }
   const uint32_t c = (codes[n * (K / 2) + k / 2] >> (4 * (k & 1))) & 0xFu;
   if (fmt == GBW_FMT_E8M0_B32) return e2m1_value(c) * e8m0_value(scales[n * (K / 32) + k / 32]);
-  const float v = e2m1_value(c) * e4m3_value(scales[n * (K / 16) + k / 16]);
+  const uint32_t sc = scales[n * (K / 16) + k / 16];
+  const float v = e2m1_value(c) * (fmt == GBW_FMT_E5M3_B16 ? ue5m3_value(sc) : e4m3_value(sc));
   const int64_t seg = n / (N / ts_seg);
   return v * ts[seg];
 }
@@ -253,7 +258,7 @@ __global__ void k_set_scalar(float* p, float v) {
 size_t ws_quantize(int64_t rows, int64_t K, int32_t fmt) {
   (void)rows;
   (void)K;
-  return fmt == GBW_FMT_E4M3_B16 ? (size_t)kAmaxBlocks * sizeof(uint32_t) : 0;
+  return fmt == GBW_FMT_E4M3_B16 || fmt == GBW_FMT_E5M3_B16 ? (size_t)kAmaxBlocks * sizeof(uint32_t) : 0;
 }
 
 }  // namespace gbw
@@ -265,13 +270,15 @@ extern "C" int mx_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t
                            int32_t flags, void* ws, size_t ws_bytes, void* stream) {
   if (rows < 0 || K < 0 || tail_copy < 0) return fail(GBW_E_ARG, "mx_quantize: negative extent");
   if (x_dtype != GBW_DTYPE_BF16 && x_dtype != GBW_DTYPE_F32) return fail(GBW_E_ARG, "mx_quantize: bad dtype");
-  if (fmt != GBW_FMT_E8M0_B32 && fmt != GBW_FMT_E4M3_B16) return fail(GBW_E_ARG, "mx_quantize: bad format");
+  if (fmt != GBW_FMT_E8M0_B32 && fmt != GBW_FMT_E4M3_B16 && fmt != GBW_FMT_E5M3_B16)
+    return fail(GBW_E_ARG, "mx_quantize: bad format");
+  const bool tscaled = fmt != GBW_FMT_E8M0_B32;  // E4M3-B16 or E5M3-B16: FP32 tensor scale
   const int bs = fmt == GBW_FMT_E8M0_B32 ? 32 : 16;
   if (K % bs) return fail(GBW_E_SHAPE, "mx_quantize: K=%lld not a multiple of %d", (long long)K, bs);
   if (tail_copy && (fmt != GBW_FMT_E8M0_B32 || tail_copy % 32 || tail_copy > K))
     return fail(GBW_E_SHAPE, "mx_quantize: tail_copy must be a multiple of 32, <= K, E8M0 only");
-  const bool dynamic = fmt == GBW_FMT_E4M3_B16 && (flags & GBW_TS_DYNAMIC);
-  if (fmt == GBW_FMT_E4M3_B16 && !tensor_scale) return fail(GBW_E_ARG, "mx_quantize: E4M3 needs tensor_scale");
+  const bool dynamic = tscaled && (flags & GBW_TS_DYNAMIC);
+  if (tscaled && !tensor_scale) return fail(GBW_E_ARG, "mx_quantize: E4M3/E5M3 needs tensor_scale");
   if (rows == 0 || K == 0) {
     if (!dynamic) return GBW_OK;
     int st0 = check_device();
@@ -315,16 +322,23 @@ extern "C" int mx_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t
                          (const float*)x, total, partial);
     if ((st = check_launch("mx_quantize(amax)"))) return st;
   }
-#define GBW_Q4(T, W)                                                                                           \
-  hipLaunchKernelGGL((k_quant_e4m3<T, W>), dim3(blocks), dim3(kQuantThreads), 0, s, (const T*)x, rows, K, codes, \
+#define GBW_Q4(T, W, E5)                                                                                          \
+  hipLaunchKernelGGL((k_quant_e4m3<T, W, E5>), dim3(blocks), dim3(kQuantThreads), 0, s, (const T*)x, rows, K, codes, \
                      scales, tensor_scale, partial, kAmaxBlocks)
-  if (bf) {
-    if (wide) GBW_Q4(uint16_t, true); else GBW_Q4(uint16_t, false);
-  } else {
-    if (wide) GBW_Q4(float, true); else GBW_Q4(float, false);
+#define GBW_Q4F(E5)                                                   \
+  if (bf) {                                                           \
+    if (wide) GBW_Q4(uint16_t, true, E5); else GBW_Q4(uint16_t, false, E5); \
+  } else {                                                            \
+    if (wide) GBW_Q4(float, true, E5); else GBW_Q4(float, false, E5);       \
   }
+  if (fmt == GBW_FMT_E5M3_B16) {
+    GBW_Q4F(true)
+  } else {
+    GBW_Q4F(false)
+  }
+#undef GBW_Q4F
 #undef GBW_Q4
-  return check_launch("mx_quantize(e4m3)");
+  return check_launch("mx_quantize(e4m3/e5m3)");
 }
 
 extern "C" int mx_dequantize(const gbw_weight* w, int32_t expert, float* out, void* stream) {
@@ -341,6 +355,7 @@ extern "C" int mx_dequantize(const gbw_weight* w, int32_t expert, float* out, vo
       sbytes = N * K / 32;
       break;
     case GBW_FMT_E4M3_B16:
+    case GBW_FMT_E5M3_B16:
       if (K % 16) return fail(GBW_E_SHAPE, "mx_dequantize: K %% 16");
       if (!w->tensor_scale || w->ts_per_expert < 1 || N % w->ts_per_expert)
         return fail(GBW_E_ARG, "mx_dequantize: bad tensor scale");

@@ -20,6 +20,10 @@
  *   GBW_FMT_E8M0_B32  E2M1 elements + one E8M0 scale per 32 along K (4.25 b/elt)
  *   GBW_FMT_E4M3_B16  E2M1 elements + one E4M3 scale per 16 along K + one
  *                     FP32 tensor scale (4.50 b/elt)
+ *   GBW_FMT_E5M3_B16  E2M1 elements + one UE5M3 scale per 16 along K + one
+ *                     FP32 tensor scale (4.50 b/elt).  UE5M3: unsigned, 5
+ *                     exponent bits (bias 15), 3 mantissa bits; scales from
+ *                     2^-17 to 114688 (code 0xFE), code 0xFF reserved.
  *   GBW_FMT_VQ4_E8M0  MXCode PreScale weights: 8-bit index per 4 consecutive K
  *                     elements into a 256-entry table of 4xE2M1 keys per
  *                     64x64 QBlock, plus the E8M0 per-32 prescale (abstract,
@@ -53,12 +57,13 @@ extern "C" {
 #define GBW_FMT_E8M0_B32 0
 #define GBW_FMT_E4M3_B16 1
 #define GBW_FMT_VQ4_E8M0 2
+#define GBW_FMT_E5M3_B16 3
 
 #define GBW_DTYPE_BF16 0
 #define GBW_DTYPE_F32 1
 
 /* flags */
-#define GBW_TS_DYNAMIC 1     /* mx_quantize: compute the E4M3 tensor scale from the data */
+#define GBW_TS_DYNAMIC 1     /* mx_quantize: compute the E4M3/E5M3 tensor scale from the data */
 #define GBW_DETERMINISTIC 2  /* GEMMs: fixed summation order, bitwise repeatable          */
 #define GBW_FP32_COMBINE 4   /* moe down: keep the per-pair outputs in fp32 (default bf16) */
 
@@ -80,21 +85,21 @@ typedef struct gbw_weight {
   int32_t fmt;               /* GBW_FMT_*                                          */
   int32_t n_experts;         /* >= 1; expert e starts at e * (per-expert size)     */
   int64_t N, K;              /* per expert                                         */
-  const uint8_t* codes;      /* E8M0/E4M3: [E][N][K/2] nibbles; VQ: [E][N][K/4] idx */
-  const uint8_t* scales;     /* E8M0 and VQ: [E][N][K/32] E8M0; E4M3: [E][N][K/16]  */
+  const uint8_t* codes;      /* E8M0/E4M3/E5M3: [E][N][K/2] nibbles; VQ: [E][N][K/4] idx */
+  const uint8_t* scales;     /* E8M0 and VQ: [E][N][K/32] E8M0; E4M3/E5M3: [E][N][K/16] */
   const uint16_t* codebook;  /* VQ only: [E][N/64][K/64][256] keys, else NULL       */
-  const float* tensor_scale; /* E4M3 only: [E][ts_per_expert] fp32, else NULL       */
-  int32_t ts_per_expert;     /* E4M3: rows split into this many equal segments,
+  const float* tensor_scale; /* E4M3/E5M3 only: [E][ts_per_expert] fp32, else NULL  */
+  int32_t ts_per_expert;     /* E4M3/E5M3: rows split into this many equal segments,
                                 segment s scaled by tensor_scale[e][s] (1 or 2)     */
 } gbw_weight;
 
 /* A quantized activation: [rows][K], K contiguous. */
 typedef struct gbw_act {
-  int32_t fmt;               /* GBW_FMT_E8M0_B32 or GBW_FMT_E4M3_B16               */
+  int32_t fmt;               /* GBW_FMT_E8M0_B32, GBW_FMT_E4M3_B16 or GBW_FMT_E5M3_B16 */
   int64_t rows, K;
   const uint8_t* codes;      /* [rows][K/2]                                        */
-  const uint8_t* scales;     /* [rows][K/32] (E8M0) or [rows][K/16] (E4M3)         */
-  const float* tensor_scale; /* E4M3: device fp32[1]; else NULL                    */
+  const uint8_t* scales;     /* [rows][K/32] (E8M0) or [rows][K/16] (E4M3, E5M3)   */
+  const float* tensor_scale; /* E4M3/E5M3: device fp32[1]; else NULL               */
 } gbw_act;
 
 /* ---- utility ------------------------------------------------------------ */
@@ -115,6 +120,9 @@ size_t gbw_workspace_size(int32_t op, int64_t d0, int64_t d1, int64_t d2, int32_
  *    GBW_TS_DYNAMIC, amax_tensor is computed from x and S_T written to
  *    tensor_scale[0] (workspace required); otherwise S_T is read from
  *    tensor_scale[0].
+ *  E5M3-B16 (MXCode Table 1, E5M3-B16-FP4 row): the E4M3-B16 steps with
+ *    UE5M3 block scales, S_T = amax_tensor / 688128 (= 6 * 114688) and
+ *    scale = UE5M3_RNE_sat(amax_blk / (6 S_T)) saturating at 114688.
  *  tail_copy > 0 (E8M0 only, multiple of 32, <= K) appends a copy of the
  *    quantized last tail_copy columns with their scales: PRQuant:
  *    Permutation Residual Quantization for Low-Overhead Inference, §4
@@ -126,7 +134,7 @@ int mx_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t K, int32_t
                 int32_t flags, void* ws, size_t ws_bytes, void* stream);
 
 /* mx_dequantize: decode expert `expert` of w to fp32 out [N][K] through the
- * same device decoders the GEMMs use (E8M0: e2m1*2^(s-127); E4M3:
+ * same device decoders the GEMMs use (E8M0: e2m1*2^(s-127); E4M3 and E5M3:
  * e2m1*scale*tensor_scale[segment]; VQ: QBlock table key nibble * 2^(s-127)).
  * Used to check decoded weights bit for bit and for offline preparation. */
 int mx_dequantize(const gbw_weight* w, int32_t expert, float* out, void* stream);
@@ -186,8 +194,8 @@ int moe_route(const float* logits, int64_t T, int32_t E, int32_t topk, int32_t* 
  *    with w_e the fused [2I][H] gate/up weight (gate rows first);
  *    h = bf16(silu(g) * u).  Writes h_bf16 [P][I] if non-NULL and, for
  *    E8M0-B32 activations, the quantized h into h_codes [P][I/2] / h_scales
- *    [P][I/32] (the requantization is fused).  For E4M3-B16 only h_bf16 is
- *    written; quantize it with mx_quantize(GBW_TS_DYNAMIC).
+ *    [P][I/32] (the requantization is fused).  For E4M3-B16 and E5M3-B16
+ *    only h_bf16 is written; quantize it with mx_quantize(GBW_TS_DYNAMIC).
  *  GBW_MOE_DOWN_COMBINE: y[t] = sum_j topk_w[t][j] * deq(a[pair_pos[t][j]])
  *    deq(w_e)^T, a = quantized h in pair order, y [T][H] fp32 (overwritten).
  *    With a workspace, every pair's output goes once to row p of a [P][H]
@@ -196,9 +204,11 @@ int moe_route(const float* logits, int64_t T, int32_t E, int32_t topk, int32_t* 
  *    repeatable.  With ws = NULL the
  *    outputs are added into y with fp32 atomics (no workspace, not
  *    repeatable; GBW_DETERMINISTIC then fails with GBW_E_WORKSPACE).
- * Weights: E8M0-B32, VQ4-E8M0 (decoded to MXFP4 in LDS, scaled MFMA) or
- * E4M3-B16 (decoded exactly to fp16, fp16 MFMA).  The activation format must
- * be E4M3-B16 for E4M3-B16 weights and E8M0-B32 otherwise.
+ * Weights: E8M0-B32, VQ4-E8M0 (decoded to MXFP4 in LDS, scaled MFMA),
+ * E4M3-B16 (decoded exactly to fp16, fp16 MFMA) or E5M3-B16 (decoded exactly
+ * to bf16 -- the products reach 6 * 114688, past fp16's range -- bf16 MFMA).
+ * The activation format must equal the weight format for E4M3-B16 and
+ * E5M3-B16 weights and be E8M0-B32 otherwise.
  * ws: gbw_workspace_size(GBW_OP_MOE_GEMM, P, H, fp32_combine, 0) bytes
  * (down stage only; the gate/up stage takes none). */
 typedef struct gbw_moe_out {

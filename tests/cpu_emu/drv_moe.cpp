@@ -31,7 +31,7 @@ template <class T> T* buf(size_t n, std::mt19937& g) {
 }
 int main(int argc, char** argv) {
   const int T = atoi(argv[1]), H = atoi(argv[2]), I = atoi(argv[3]), E = atoi(argv[4]), k = atoi(argv[5]);
-  const int fmt = atoi(argv[6]);  // 0 MX, 2 VQ, 1 E4M3
+  const int fmt = atoi(argv[6]);  // 0 MX, 2 VQ, 1 E4M3, 3 E5M3
   const int P = T * k;
   std::mt19937 g(1234);
   // routing: k distinct experts per token
@@ -54,7 +54,7 @@ int main(int argc, char** argv) {
   for (int e = 0; e < E; ++e) off[e + 1] += off[e];
   for (int p = 0; p < P; ++p) { ptok[p] = pairs[p].second / k; ppos[pairs[p].second] = p; }
   for (int i = 0; i < P; ++i) tw[i] = 1.0f / k;
-  const bool e4 = fmt == 1;
+  const bool e4 = fmt == 1 || fmt == 3;  // tensor-scaled formats
   const int sdiv = e4 ? 16 : 32;
   // gate/up
   gbw_weight wg{}, wd{};
@@ -68,7 +68,7 @@ int main(int argc, char** argv) {
     if (e4) { float* ts = (float*)malloc(E * 2 * 4); for (int i = 0; i < 2 * E; ++i) ts[i] = 1.f; w->tensor_scale = ts; w->ts_per_expert = w == &wg ? 2 : 1; }
   }
   float* ats = (float*)malloc(4); *ats = 1.f;
-  gbw_act ax{}; ax.fmt = e4 ? 1 : 0; ax.rows = T; ax.K = H;
+  gbw_act ax{}; ax.fmt = e4 ? fmt : 0; ax.rows = T; ax.K = H;
   ax.codes = buf<uint8_t>((size_t)T * H / 2, g); ax.scales = buf<uint8_t>((size_t)T * H / sdiv, g);
   ax.tensor_scale = e4 ? ats : nullptr;
   gbw_moe_out o{};
@@ -79,7 +79,7 @@ int main(int argc, char** argv) {
   int st = moe_grouped_gemm(0, T, k, off, ptok, ppos, tw, &ax, &wg, &o, 0, nullptr, 0, nullptr);
   printf("gateup status %d\n", st);
   // down: activation = h
-  gbw_act ah{}; ah.fmt = e4 ? 1 : 0; ah.rows = P; ah.K = I;
+  gbw_act ah{}; ah.fmt = e4 ? fmt : 0; ah.rows = P; ah.K = I;
   uint8_t* hcodes = e4 ? buf<uint8_t>((size_t)P * I / 2, g) : hc;
   uint8_t* hsc = e4 ? buf<uint8_t>((size_t)P * I / 16, g) : hs;
   ah.codes = hcodes; ah.scales = hsc; ah.tensor_scale = e4 ? ats : nullptr;

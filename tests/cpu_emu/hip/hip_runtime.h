@@ -89,6 +89,14 @@ inline emu_v2h emu_cvt_f16_fp4(uint32_t w, float s, int sel) {
   return emu_v2h{(_Float16)lo, (_Float16)hi};
 }
 #define __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, sel) emu_cvt_f16_fp4((w), (s), (sel))
+typedef float emu_v2f __attribute__((ext_vector_type(2)));
+inline emu_v2f emu_cvt_f32_fp4(uint32_t w, float s, int sel) {
+  static const float m[8] = {0, .5f, 1, 1.5f, 2, 3, 4, 6};
+  const uint32_t b = (w >> (8 * sel)) & 255;
+  return emu_v2f{((b & 8) ? -m[b & 7] : m[b & 7]) * s, ((b & 128) ? -m[(b >> 4) & 7] : m[(b >> 4) & 7]) * s};
+}
+#define __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, sel) emu_cvt_f32_fp4((w), (s), (sel))
+#define __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, ...) ((void)(a), (void)(b), (c))
 #define __builtin_amdgcn_perm(a, b, s) ((uint32_t)(a) ^ (uint32_t)(b) ^ (uint32_t)(s))
 #define __builtin_amdgcn_s_waitcnt(x) ((void)0)
 #define __builtin_amdgcn_s_barrier() __syncthreads()

@@ -45,7 +45,7 @@ def _run(exe, *args, timeout=300):
     return r.stdout
 
 
-@pytest.mark.parametrize("fmt", [0, 2, 1], ids=["mxfp4", "vq", "e4m3"])
+@pytest.mark.parametrize("fmt", [0, 2, 1, 3], ids=["mxfp4", "vq", "e4m3", "e5m3"])
 def test_moe_grouped_gemm_in_bounds(build_dir, fmt):
     exe = _build(build_dir, "moe_gemm.hip", "drv_moe.cpp", "emu_moe")
     out = _run(exe, 300, 512, 256, 8, 2, fmt)

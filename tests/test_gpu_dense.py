@@ -87,34 +87,47 @@ def test_quantize_tail_copy_bitexact():
     assert np.array_equal(to_np(a.scales), ss)
 
 
+_TS_FORMATS = {"e4m3": (gbw.FMT_E4M3_B16, oracle.quantize_e4m3_b16, oracle.formats.tensor_scale_e4m3),
+               "e5m3": (gbw.FMT_E5M3_B16, oracle.quantize_e5m3_b16, oracle.formats.tensor_scale_e5m3)}
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m3"])
 @pytest.mark.parametrize("rows,K,dtype,static", [(64, 2048, "bf16", False), (37, 48, "f32", False),
-                                                 (300, 768, "bf16", True), (6, 256, "special", False)])
-def test_quantize_e4m3_bitexact(rows, K, dtype, static):
-    banner(f"quantize e4m3 {rows}x{K} {dtype} static={static}")
+                                                 (300, 768, "bf16", True), (6, 256, "special", False),
+                                                 (40, 512, "wide", False)])
+def test_quantize_e4m3_bitexact(rows, K, dtype, static, fmt):
+    banner(f"quantize {fmt} {rows}x{K} {dtype} static={static}")
+    gfmt, oq, ots = _TS_FORMATS[fmt]
     if dtype == "special":
         x = torch.from_numpy(_special_rows(K)[:, :K]).to(DEV)
         x[4] = x[5]                                   # keep the tensor amax finite and moderate
     elif dtype == "bf16":
         x = synth.normal((rows, K), 1.0, 2, "q4.x", DEV).to(torch.bfloat16)
+    elif dtype == "wide":
+        # 16-element blocks spread over 2^-40 .. 2^20: subnormal, normal and top block scales
+        g = synth.normal((rows, K), 1.0, 5, "q4.wide", DEV)
+        e = torch.arange(rows * K // 16, device=DEV).reshape(rows, K // 16) % 61 - 40
+        x = (g * torch.exp2(e.float()).repeat_interleave(16, dim=1)).contiguous()
     else:
         x = synth.normal((rows, K), 0.02, 2, "q4.w", DEV)
     xn = x.float().cpu().numpy()
     if static:
         amax = np.float32(7.5)
-        ts = torch.tensor([oracle.formats.tensor_scale_e4m3(amax)], dtype=torch.float32, device=DEV)
-        a = gbw.mx_quantize(x, gbw.FMT_E4M3_B16, tensor_scale=ts, dynamic=False)
-        c, s, st = oracle.quantize_e4m3_b16(xn, tensor_amax=amax)
+        ts = torch.tensor([ots(amax)], dtype=torch.float32, device=DEV)
+        a = gbw.mx_quantize(x, gfmt, tensor_scale=ts, dynamic=False)
+        c, s, st = oq(xn, tensor_amax=amax)
     else:
-        a = gbw.mx_quantize(x, gbw.FMT_E4M3_B16)
-        c, s, st = oracle.quantize_e4m3_b16(xn)
+        a = gbw.mx_quantize(x, gfmt)
+        c, s, st = oq(xn)
     assert to_np(a.tensor_scale)[0] == st
     assert np.array_equal(to_np(a.scales), s)
     assert np.array_equal(to_np(a.codes), c)
 
 
-def test_quantize_e4m3_empty_tensor_scale():
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m3"])
+def test_quantize_e4m3_empty_tensor_scale(fmt):
     x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
-    a = gbw.mx_quantize(x, gbw.FMT_E4M3_B16)
+    a = gbw.mx_quantize(x, _TS_FORMATS[fmt][0])
     assert to_np(a.tensor_scale)[0] == 1.0
 
 
@@ -137,6 +150,17 @@ def test_dequantize_e8m0_and_e4m3_bitexact():
     out = to_np(gbw.mx_dequantize(W))
     ref = np.concatenate([oracle.dequantize(cg, sg, "e4m3_b16", tg), oracle.dequantize(cu, su, "e4m3_b16", tu)])
     assert np.array_equal(out.astype(np.float64), ref.astype(np.float32).astype(np.float64))
+    # E5M3 likewise, with a spread of block magnitudes that reaches subnormal and top UE5M3 scales
+    w5 = w * np.exp2(np.arange(192 * 32).reshape(192, 32) % 50 - 30).repeat(16, axis=1)
+    cg, sg, tg = oracle.quantize_e5m3_b16(w5[:96].astype(np.float32))
+    cu, su, tu = oracle.quantize_e5m3_b16(w5[96:].astype(np.float32))
+    W = gbw.Weight(gbw.FMT_E5M3_B16, 192, 512, torch.from_numpy(np.concatenate([cg, cu])).to(DEV),
+                   torch.from_numpy(np.concatenate([sg, su])).to(DEV), None,
+                   torch.tensor([tg, tu], dtype=torch.float32, device=DEV), 2, 1)
+    out = to_np(gbw.mx_dequantize(W))
+    ref = np.concatenate([oracle.dequantize(cg, sg, "e5m3_b16", tg), oracle.dequantize(cu, su, "e5m3_b16", tu)])
+    assert np.array_equal(out.astype(np.float64), ref.astype(np.float32).astype(np.float64))
+    assert (np.concatenate([sg, su]) < 8).any() and (np.concatenate([sg, su]) == 0xFE).any()
 
 
 def test_dequantize_vq_bitexact():

@@ -164,7 +164,9 @@ class _Problem:
             self.ref_d = (_LazyExperts((E, H, I // 2), lambda e: qe("d", e)[0]),
                           _LazyExperts((E, H, I // 32), lambda e: qe("d", e)[1]), None)
             return
-        # E4M3-B16: every (expert, matrix) has its own dynamic tensor scale; gate and up separately
+        # E4M3-B16 / E5M3-B16: every (expert, matrix) has its own dynamic tensor scale; gate and up separately
+        gfmt = gbw.FMT_E4M3_B16 if fmt == "e4m3_b16" else gbw.FMT_E5M3_B16
+        oq = oracle.quantize_e4m3_b16 if fmt == "e4m3_b16" else oracle.quantize_e5m3_b16
         gc = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=DEV)
         gs = torch.empty((E, 2 * I, H // 16), dtype=torch.uint8, device=DEV)
         gt = torch.empty((E, 2), dtype=torch.float32, device=DEV)
@@ -174,13 +176,13 @@ class _Problem:
         for e in range(E):
             for half in range(2):
                 rows = slice(half * I, (half + 1) * I)
-                out = gbw.Act(gbw.FMT_E4M3_B16, gc[e, rows], gs[e, rows])
-                gbw.mx_quantize(wgu[e, rows].contiguous(), gbw.FMT_E4M3_B16, out=out, tensor_scale=gt[e, half:half + 1],
+                out = gbw.Act(gfmt, gc[e, rows], gs[e, rows])
+                gbw.mx_quantize(wgu[e, rows].contiguous(), gfmt, out=out, tensor_scale=gt[e, half:half + 1],
                                 dynamic=True)
-            out = gbw.Act(gbw.FMT_E4M3_B16, dc[e], ds[e])
-            gbw.mx_quantize(wd[e].contiguous(), gbw.FMT_E4M3_B16, out=out, tensor_scale=dt[e], dynamic=True)
-        self.Wgu = gbw.Weight(gbw.FMT_E4M3_B16, 2 * I, H, gc, gs, None, gt, 2, E)
-        self.Wd = gbw.Weight(gbw.FMT_E4M3_B16, H, I, dc, ds, None, dt, 1, E)
+            out = gbw.Act(gfmt, dc[e], ds[e])
+            gbw.mx_quantize(wd[e].contiguous(), gfmt, out=out, tensor_scale=dt[e], dynamic=True)
+        self.Wgu = gbw.Weight(gfmt, 2 * I, H, gc, gs, None, gt, 2, E)
+        self.Wd = gbw.Weight(gfmt, H, I, dc, ds, None, dt, 1, E)
         cache = {}
 
         def q4(which, e):
@@ -188,11 +190,11 @@ class _Problem:
             if key not in cache:
                 if which == "gu":
                     w = wgu[e].cpu().numpy()
-                    a = oracle.quantize_e4m3_b16(w[:I])
-                    b = oracle.quantize_e4m3_b16(w[I:])
+                    a = oq(w[:I])
+                    b = oq(w[I:])
                     cache[key] = (np.concatenate([a[0], b[0]]), np.concatenate([a[1], b[1]]), [a[2], b[2]])
                 else:
-                    cache[key] = oracle.quantize_e4m3_b16(wd[e].cpu().numpy())
+                    cache[key] = oq(wd[e].cpu().numpy())
             return cache[key]
         self.ref_gu = (_LazyExperts((E, 2 * I, H // 2), lambda e: q4("gu", e)[0]),
                        _LazyExperts((E, 2 * I, H // 16), lambda e: q4("gu", e)[1]),
@@ -209,7 +211,7 @@ class _Problem:
             assert np.array_equal(to_np(self.Wgu.scales[e]), self.ref_gu[1][e])
             assert np.array_equal(to_np(self.Wd.codes[e]), self.ref_d[0][e])
             assert np.array_equal(to_np(self.Wd.scales[e]), self.ref_d[1][e])
-            if self.fmt == "e4m3_b16":
+            if self.fmt in ("e4m3_b16", "e5m3_b16"):
                 assert np.array_equal(to_np(self.Wgu.tensor_scale[e]), np.array(self.ref_gu[2][e], np.float32))
                 assert to_np(self.Wd.tensor_scale[e])[0] == self.ref_d[2][e]
 
@@ -223,8 +225,11 @@ def _run_and_check(pb, tokens=None, experts=None, h_amax=None):
     """
     T, H, I, topk = pb.T, pb.H, pb.I, pb.topk
     fmt = "e8m0_b32" if pb.fmt == "vq" else pb.fmt
-    e4 = fmt == "e4m3_b16"
-    afmt = gbw.FMT_E4M3_B16 if e4 else gbw.FMT_E8M0_B32
+    e4 = fmt in ("e4m3_b16", "e5m3_b16")          # tensor-scaled formats: h quantized by mx_quantize
+    e5 = fmt == "e5m3_b16"
+    afmt = (gbw.FMT_E5M3_B16 if e5 else gbw.FMT_E4M3_B16) if e4 else gbw.FMT_E8M0_B32
+    oq = oracle.quantize_e5m3_b16 if e5 else oracle.quantize_e4m3_b16
+    ots = oracle.formats.tensor_scale_e5m3 if e5 else oracle.formats.tensor_scale_e4m3
     bs = 16 if e4 else 32
     route, ref_route = _check_route(pb.logits, topk)
     P = T * topk
@@ -241,8 +246,7 @@ def _run_and_check(pb, tokens=None, experts=None, h_amax=None):
         if h_amax is None:
             hq = gbw.mx_quantize(hb, afmt)
         else:
-            st = torch.tensor([oracle.formats.tensor_scale_e4m3(np.float32(h_amax))], dtype=torch.float32,
-                              device=DEV)
+            st = torch.tensor([ots(np.float32(h_amax))], dtype=torch.float32, device=DEV)
             hq = gbw.mx_quantize(hb, afmt, tensor_scale=st, dynamic=False)
     y = torch.empty((T, H), dtype=torch.float32, device=DEV)
     gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, pb.Wd, y=y)                 # bf16 slots
@@ -258,7 +262,7 @@ def _run_and_check(pb, tokens=None, experts=None, h_amax=None):
     # ---- oracle pipeline, from the synthetic inputs only ----
     xn = pb.x.float().cpu().numpy()
     if e4:
-        ac, as_, ats = oracle.quantize_e4m3_b16(xn)
+        ac, as_, ats = oq(xn)
         assert to_np(xq.tensor_scale)[0] == ats
     else:
         ac, as_ = oracle.quantize_e8m0_b32(xn)
@@ -283,7 +287,7 @@ def _run_and_check(pb, tokens=None, experts=None, h_amax=None):
         if not e4:
             c, s = oracle.quantize_e8m0_b32(hf)
             return c, s, None
-        return oracle.quantize_e4m3_b16(hf, tensor_amax=h_amax)
+        return oq(hf, tensor_amax=h_amax)
 
     # gate/up + SwiGLU on every pair of the chosen experts
     pairs = np.concatenate([np.arange(off[e], off[e + 1]) for e in experts])
@@ -364,6 +368,23 @@ def test_moe_vq_full_size_sampled():
     d = synth.moe_vq_problem(8192, 4096, 1536, 128, seed=0, device=DEV)
     _run_and_check(_Problem("vq", d["x"], d["logits"], 8, d["gate_up"], d["down"], 1536),
                    tokens=[0, 4097, 8191], experts=[0, 77])
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [(300, 512, 256, 8, 2), (64, 1024, 384, 16, 8)])
+def test_moe_e5m3_small(T, H, I, E, k):
+    banner(f"moe e5m3 T={T} H={H} I={I} E={E} k={k}")
+    d = synth.moe_problem(T, H, I, E, seed=4, device=DEV)
+    pb = _Problem("e5m3_b16", d["x"], d["logits"], k, dict(w=d["w_gate_up"]), dict(w=d["w_down"]), I)
+    _run_and_check(pb)
+    _run_and_check(pb, h_amax=1.5)
+
+
+def test_moe_e5m3_full_size_sampled():
+    """E5M3-B16 at the E4M3-B16 shape: T=4096, H=2048, I=768, 128 experts, top-8."""
+    banner("moe e5m3 full T=4096 H=2048 I=768 E=128 k=8")
+    d = synth.moe_problem(4096, 2048, 768, 128, seed=0, device=DEV)
+    _run_and_check(_Problem("e5m3_b16", d["x"], d["logits"], 8, dict(w=d["w_gate_up"]), dict(w=d["w_down"]), 768),
+                   tokens=[1, 2048, 4095], experts=[3, 100], h_amax=2.0)
 
 
 def test_moe_e4m3_full_size_sampled():
