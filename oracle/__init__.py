@@ -28,7 +28,7 @@ Parity status of each function is recorded in its docstring; every function
 has at least one pin in ``tests/test_oracle_*.py``.
 """
 
-from . import formats, gemm, moe  # noqa: F401
+from . import formats, gemm, moe, rotation  # noqa: F401
 from .formats import (  # noqa: F401
     E2M1_MAGNITUDES,
     e2m1_decode,
@@ -57,6 +57,7 @@ from .gemm import (  # noqa: F401
     vq_decode_codes,
     vq_dequantize,
 )
+from .rotation import fwht32_fp32  # noqa: F401
 from .moe import (  # noqa: F401
     moe_route,
     moe_gateup,
