@@ -245,6 +245,25 @@ def tail_decode(gbw, synth, torch):
             "TFLOP_s": flops / us / 1e6, "replicas": R}
 
 
+def quantize_rate(gbw, synth, torch):
+    """Online activation quantization (E8M0-B32) at the headline activation
+    shape, plain and with the block Hadamard rotation, over four distinct
+    64 MB inputs so every call reads its input from HBM."""
+    rows, K = 8192, 4096
+    xs = [synth.normal((rows, K), 1.0, 40 + r, "bench.q.x", "cuda").to(torch.bfloat16) for r in range(4)]
+    out = gbw.Act(gbw.FMT_E8M0_B32, torch.empty((rows, K // 2), dtype=torch.uint8, device="cuda"),
+                  torch.empty((rows, K // 32), dtype=torch.uint8, device="cuda"))
+    nbytes = rows * K * 2 + rows * K // 2 + rows * K // 32
+    res = {"rows": rows, "K": K, "dtype": "bf16", "bytes_per_call": nbytes}
+    for name, rot in (("plain", False), ("block_hadamard", True)):
+        def fn(rot=rot):
+            for x in xs:
+                gbw.mx_quantize(x, gbw.FMT_E8M0_B32, out=out, rotate=rot)
+        us = _graph_time(torch, fn, len(xs))
+        res[name] = {"us_per_call": us, "GB_s": nbytes / us / 1e3, "frac_hbm": nbytes / us / 1e3 / HBM_PEAK_GBS}
+    return res
+
+
 def dense_small(gbw, synth, torch):
     d = synth.dense_linear(16, 512, 512, seed=0, device="cuda")
     a = gbw.mx_quantize(d["x"], gbw.FMT_E8M0_B32)
@@ -370,7 +389,8 @@ def main():
         log("extra: E4M3-B16 MoE, 16x512x512 linear")
         out["extra"] = {"moe_e4m3_b16": moe_e4m3(gbw, synth, torch),
                         "moe_e5m3_b16": moe_e4m3(gbw, synth, torch, fmt=gbw.FMT_E5M3_B16),
-                        "mx_gemm_16x512x512": dense_small(gbw, synth, torch)}
+                        "mx_gemm_16x512x512": dense_small(gbw, synth, torch),
+                        "quantize_e8m0_8192x4096": quantize_rate(gbw, synth, torch)}
     print(json.dumps(out), flush=True)
 
 

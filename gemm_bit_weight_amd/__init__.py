@@ -37,6 +37,7 @@ DTYPE_F32 = 1
 TS_DYNAMIC = 1
 DETERMINISTIC = 2
 FP32_COMBINE = 4
+ROTATE_H32 = 8
 MOE_GATEUP_SWIGLU = 0
 MOE_DOWN_COMBINE = 1
 OP_QUANTIZE = 0
@@ -183,11 +184,12 @@ def _dev(t):
 # ---------------------------------------------------------------------------
 
 def mx_quantize(x, fmt=FMT_E8M0_B32, tail_copy=0, tensor_scale=None, dynamic=None, out=None, ws=None,
-                stream=None):
+                stream=None, rotate=False):
     """Quantize x [rows][K] (bf16 or fp32, on the GPU) -> Act.
 
     E4M3-B16 / E5M3-B16: the tensor scale is computed from x unless
     ``tensor_scale`` (a 1-element fp32 device tensor) is given.
+    ``rotate`` (E8M0-B32): block Hadamard rotation of every 32-block first.
     """
     assert x.dim() == 2 and x.is_contiguous()
     rows, K = x.shape
@@ -200,7 +202,7 @@ def mx_quantize(x, fmt=FMT_E8M0_B32, tail_copy=0, tensor_scale=None, dynamic=Non
         scales = torch.empty((rows, W // bs), dtype=torch.uint8, device=dev)
     else:
         codes, scales = out.codes, out.scales
-    flags = 0
+    flags = ROTATE_H32 if rotate else 0
     ts = None
     if fmt in (FMT_E4M3_B16, FMT_E5M3_B16):
         if dynamic is None:

@@ -76,7 +76,35 @@ __device__ __forceinline__ uint32_t group_max(uint32_t a) {
 // ---------------------------------------------------------------------------
 // E8M0-B32
 // ---------------------------------------------------------------------------
-template <typename T, bool WIDE>
+// Normalized order-32 Walsh-Hadamard transform of the 32-block a quad of
+// lanes holds (lane 4k+q: elements 8q..8q+7 of the block): stages of span 1,
+// 2, 4 inside the lane, 8 and 16 across lanes q^1 and q^2, each pair (a, b)
+// -> (a + b, a - b) in fp32, then one multiply by fp32(1/sqrt(32)).
+__device__ __forceinline__ void fwht32_quad(float (&v)[8]) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+  const int q = threadIdx.x & 3;
+#pragma unroll
+  for (int m = 1; m <= 2; m <<= 1) {
+    const bool upper = (q & m) != 0;  // this lane holds the (i + h) side of each pair
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float o = __shfl_xor(v[i], m);
+      v[i] = upper ? o - v[i] : v[i] + o;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] *= 0x1.6a09e6p-3f;  // fp32(1/sqrt(32))
+}
+
+template <typename T, bool WIDE, bool ROT>
 __global__ __launch_bounds__(kQuantThreads) void k_quant_e8m0(const T* __restrict__ x, int64_t rows,
                                                              int64_t K, int64_t tail,
                                                              uint8_t* __restrict__ codes,
@@ -89,6 +117,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_e8m0(const T* __restric
   unit_pos<WIDE>(gg, K, row, col);
   float v[8];
   In8<T>::load(x + row * K + col, v);
+  if (ROT) fwht32_quad(v);
   uint32_t am = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) am = max(am, abs_bits(v[i]));
@@ -273,6 +302,8 @@ extern "C" int mx_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t
   if (fmt != GBW_FMT_E8M0_B32 && fmt != GBW_FMT_E4M3_B16 && fmt != GBW_FMT_E5M3_B16)
     return fail(GBW_E_ARG, "mx_quantize: bad format");
   const bool tscaled = fmt != GBW_FMT_E8M0_B32;  // E4M3-B16 or E5M3-B16: FP32 tensor scale
+  if ((flags & GBW_ROTATE_H32) && fmt != GBW_FMT_E8M0_B32)
+    return fail(GBW_E_UNSUPPORTED, "mx_quantize: the block rotation is for E8M0-B32 (32-element blocks)");
   const int bs = fmt == GBW_FMT_E8M0_B32 ? 32 : 16;
   if (K % bs) return fail(GBW_E_SHAPE, "mx_quantize: K=%lld not a multiple of %d", (long long)K, bs);
   if (tail_copy && (fmt != GBW_FMT_E8M0_B32 || tail_copy % 32 || tail_copy > K))
@@ -300,14 +331,21 @@ extern "C" int mx_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t
   const bool bf = x_dtype == GBW_DTYPE_BF16;
   const bool wide = total > (int64_t)UINT32_MAX;
   if (fmt == GBW_FMT_E8M0_B32) {
-#define GBW_Q8(T, W) \
-  hipLaunchKernelGGL((k_quant_e8m0<T, W>), dim3(blocks), dim3(kQuantThreads), 0, s, (const T*)x, rows, K, tail_copy, \
-                     codes, scales)
-    if (bf) {
-      if (wide) GBW_Q8(uint16_t, true); else GBW_Q8(uint16_t, false);
+#define GBW_Q8(T, W, R)                                                                                       \
+  hipLaunchKernelGGL((k_quant_e8m0<T, W, R>), dim3(blocks), dim3(kQuantThreads), 0, s, (const T*)x, rows, K, \
+                     tail_copy, codes, scales)
+#define GBW_Q8F(R)                                                              \
+  if (bf) {                                                                     \
+    if (wide) GBW_Q8(uint16_t, true, R); else GBW_Q8(uint16_t, false, R);       \
+  } else {                                                                      \
+    if (wide) GBW_Q8(float, true, R); else GBW_Q8(float, false, R);             \
+  }
+    if (flags & GBW_ROTATE_H32) {
+      GBW_Q8F(true)
     } else {
-      if (wide) GBW_Q8(float, true); else GBW_Q8(float, false);
+      GBW_Q8F(false)
     }
+#undef GBW_Q8F
 #undef GBW_Q8
     return check_launch("mx_quantize(e8m0)");
   }

@@ -66,6 +66,7 @@ extern "C" {
 #define GBW_TS_DYNAMIC 1     /* mx_quantize: compute the E4M3/E5M3 tensor scale from the data */
 #define GBW_DETERMINISTIC 2  /* GEMMs: fixed summation order, bitwise repeatable          */
 #define GBW_FP32_COMBINE 4   /* moe down: keep the per-pair outputs in fp32 (default bf16) */
+#define GBW_ROTATE_H32 8     /* mx_quantize, E8M0-B32: rotate every 32-block (block Hadamard) */
 
 /* moe_grouped_gemm stages */
 #define GBW_MOE_GATEUP_SWIGLU 0
@@ -123,6 +124,14 @@ size_t gbw_workspace_size(int32_t op, int64_t d0, int64_t d1, int64_t d2, int32_
  *  E5M3-B16 (MXCode Table 1, E5M3-B16-FP4 row): the E4M3-B16 steps with
  *    UE5M3 block scales, S_T = amax_tensor / 688128 (= 6 * 114688) and
  *    scale = UE5M3_RNE_sat(amax_blk / (6 S_T)) saturating at 114688.
+ *  GBW_ROTATE_H32 (E8M0-B32 only): each 32-element block is first multiplied
+ *    by the normalized order-32 Sylvester-Hadamard matrix (H[i][j] =
+ *    (-1)^popcount(i&j) / sqrt(32), symmetric and orthonormal) -- the online
+ *    Hadamard of CodeQuant Table 2 ("had") applied within the MXFP4 blocks as
+ *    PRQuant §2 ("Rotation and block-aware FP4 quantization") describes.
+ *    Weights quantized with the same flag give X W^T = (X H)(W H)^T.  Computed
+ *    in fp32 by the fast transform (stages of span 1, 2, 4, 8, 16, each
+ *    (a, b) -> (a + b, a - b)), then one multiply by fp32(1/sqrt(32)).
  *  tail_copy > 0 (E8M0 only, multiple of 32, <= K) appends a copy of the
  *    quantized last tail_copy columns with their scales: PRQuant:
  *    Permutation Residual Quantization for Low-Overhead Inference, §4

@@ -87,6 +87,59 @@ def test_quantize_tail_copy_bitexact():
     assert np.array_equal(to_np(a.scales), ss)
 
 
+@pytest.mark.parametrize("rows,K,kind", [(13, 96, "bf16"), (128, 9728, "outliers"), (2560, 9728, "f32"),
+                                        (40, 512, "wide")])
+def test_quantize_e8m0_block_hadamard_bitexact(rows, K, kind):
+    """mx_quantize(rotate=True): the oracle rotates each 32-block in fp32 in
+    the same butterfly order, then quantizes; codes and scales bit for bit."""
+    banner(f"quantize e8m0 block-hadamard {rows}x{K} {kind}")
+    if kind == "bf16":
+        x = synth.normal((rows, K), 1.0, 6, "h.x", DEV).to(torch.bfloat16)
+    elif kind == "outliers":
+        x = synth.tail_residual_problem(rows, 64, K, seed=0, device=DEV)["x"]
+    elif kind == "f32":
+        x = synth.normal((rows, K), 0.02, 6, "h.w", DEV)
+    else:
+        g = synth.normal((rows, K), 1.0, 7, "h.wide", DEV)
+        e = torch.arange(rows * K // 32, device=DEV).reshape(rows, K // 32) % 41 - 20
+        x = (g * torch.exp2(e.float()).repeat_interleave(32, dim=1)).contiguous()
+    a = gbw.mx_quantize(x.contiguous(), gbw.FMT_E8M0_B32, rotate=True)
+    c, s = oracle.quantize_e8m0_b32(oracle.fwht32_fp32(x.float().cpu().numpy()))
+    assert np.array_equal(to_np(a.scales), s)
+    assert np.array_equal(to_np(a.codes), c)
+    if kind == "outliers":
+        at = gbw.mx_quantize(x, gbw.FMT_E8M0_B32, rotate=True, tail_copy=256)
+        cc, ss = oracle.tail_copy(c, s, 256)
+        assert np.array_equal(to_np(at.codes), cc) and np.array_equal(to_np(at.scales), ss)
+
+
+def test_block_hadamard_gemm_parity_and_error():
+    """Q(XH) Q(WH)^T through mx_gemm against the oracle's GEMM of the oracle's
+    rotated quantization; with outlier channels it is closer to X W^T than
+    the plain MXFP4 GEMM (the reason for the rotation)."""
+    banner("mx_gemm block-hadamard 128x2560x9728")
+    p = synth.tail_residual_problem(128, 2560, 9728, seed=0, device=DEV)
+    x, w = p["x"], p["w"]
+    a = gbw.mx_quantize(x, gbw.FMT_E8M0_B32, rotate=True)
+    wq = gbw.mx_quantize(w, gbw.FMT_E8M0_B32, rotate=True)
+    y = to_np(gbw.mx_gemm(a, gbw.weight_from_act(wq))).astype(np.float64)
+    ref = oracle.mx_gemm(to_np(a.codes), to_np(a.scales), to_np(wq.codes), to_np(wq.scales))
+    assert_rows_close(y, ref, what="rotated mx_gemm")
+    y_plain = to_np(gbw.mx_gemm(gbw.mx_quantize(x, gbw.FMT_E8M0_B32),
+                                gbw.weight_from_act(gbw.mx_quantize(w, gbw.FMT_E8M0_B32)))).astype(np.float64)
+    exact = x.double().cpu().numpy() @ w.double().cpu().numpy().T
+    e_rot = np.linalg.norm(y - exact) / np.linalg.norm(exact)
+    e_plain = np.linalg.norm(y_plain - exact) / np.linalg.norm(exact)
+    print(f"[stats] y-NRMSE rotated {e_rot:.4f} plain {e_plain:.4f}", flush=True)
+    assert e_rot < e_plain
+
+
+def test_block_hadamard_rejects_16_element_blocks():
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(gbw.GbwError):
+        gbw.mx_quantize(x, gbw.FMT_E4M3_B16, rotate=True)
+
+
 _TS_FORMATS = {"e4m3": (gbw.FMT_E4M3_B16, oracle.quantize_e4m3_b16, oracle.formats.tensor_scale_e4m3),
                "e5m3": (gbw.FMT_E5M3_B16, oracle.quantize_e5m3_b16, oracle.formats.tensor_scale_e5m3)}
 
