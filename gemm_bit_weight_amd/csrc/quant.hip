@@ -104,41 +104,55 @@ __device__ __forceinline__ void fwht32_quad(float (&v)[8]) {
   for (int i = 0; i < 8; ++i) v[i] *= 0x1.6a09e6p-3f;  // fp32(1/sqrt(32))
 }
 
+// Four 8-element units per thread (all four loads in flight before any
+// arithmetic); the units of one load instruction are 64 consecutive units of
+// the row-major tensor (1 KiB contiguous), and a lane quad always holds one
+// whole 32-element block.
+constexpr int kQ8Units = 4;
+
 template <typename T, bool WIDE, bool ROT>
 __global__ __launch_bounds__(kQuantThreads) void k_quant_e8m0(const T* __restrict__ x, int64_t rows,
                                                              int64_t K, int64_t tail,
                                                              uint8_t* __restrict__ codes,
                                                              uint8_t* __restrict__ scales) {
-  const int64_t g = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
   const int64_t total = rows * (K / 8);
-  const bool live = g < total;
-  const int64_t gg = live ? g : total - 1;  // keep the whole wave in the shuffles
-  int64_t row, col;
-  unit_pos<WIDE>(gg, K, row, col);
-  float v[8];
-  In8<T>::load(x + row * K + col, v);
-  if (ROT) fwht32_quad(v);
-  uint32_t am = 0;
+  const int64_t g0 = (int64_t)blockIdx.x * (kQuantThreads * kQ8Units) + threadIdx.x;
+  float v[kQ8Units][8];
+  int64_t row[kQ8Units], col[kQ8Units];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) am = max(am, abs_bits(v[i]));
-  am = group_max<4>(am);
-  const uint32_t sc = e8m0_scale_code(__uint_as_float(am));
-  const float inv = e8m0_inv(sc);
-  uint32_t word = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t c = e2m1_rne(__uint_as_float(abs_bits(v[i])) * inv) | ((__float_as_uint(v[i]) >> 28) & 8u);
-    word |= c << (4 * i);
+  for (int u = 0; u < kQ8Units; ++u) {
+    const int64_t g = g0 + (int64_t)u * kQuantThreads;
+    const int64_t gg = g < total ? g : total - 1;  // keep the whole wave in the shuffles
+    unit_pos<WIDE>(gg, K, row[u], col[u]);
+    In8<T>::load(x + row[u] * K + col[u], v[u]);
   }
-  if (!live) return;
   const int64_t W = K + tail;
-  *reinterpret_cast<uint32_t*>(codes + row * (W / 2) + col / 2) = word;
   const bool lead = (threadIdx.x & 3) == 0;
-  if (lead) scales[row * (W / 32) + col / 32] = (uint8_t)sc;
-  if (tail > 0 && col >= K - tail) {
-    const int64_t c2 = K + (col - (K - tail));
-    *reinterpret_cast<uint32_t*>(codes + row * (W / 2) + c2 / 2) = word;
-    if (lead) scales[row * (W / 32) + c2 / 32] = (uint8_t)sc;
+#pragma unroll
+  for (int u = 0; u < kQ8Units; ++u) {
+    if (ROT) fwht32_quad(v[u]);
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = max(am, abs_bits(v[u][i]));
+    am = group_max<4>(am);
+    const uint32_t sc = e8m0_scale_code(__uint_as_float(am));
+    // v_cvt_scalef32_pk_fp4_f32: x / 2^(sc-127) (exact: a power of two, also
+    // for the subnormal 2^-127), RNE onto E2M1, saturating at 6, sign kept --
+    // the rounding rule above, one instruction per two elements
+    const float scale = e8m0_value(sc);
+    uint32_t word = 0;
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[u][0], v[u][1], scale, 0);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[u][2], v[u][3], scale, 1);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[u][4], v[u][5], scale, 2);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[u][6], v[u][7], scale, 3);
+    if (g0 + (int64_t)u * kQuantThreads >= total) continue;
+    *reinterpret_cast<uint32_t*>(codes + row[u] * (W / 2) + col[u] / 2) = word;
+    if (lead) scales[row[u] * (W / 32) + col[u] / 32] = (uint8_t)sc;
+    if (tail > 0 && col[u] >= K - tail) {
+      const int64_t c2 = K + (col[u] - (K - tail));
+      *reinterpret_cast<uint32_t*>(codes + row[u] * (W / 2) + c2 / 2) = word;
+      if (lead) scales[row[u] * (W / 32) + c2 / 32] = (uint8_t)sc;
+    }
   }
 }
 
@@ -328,11 +342,12 @@ extern "C" int mx_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t
   hipStream_t s = as_stream(stream);
   const int64_t total = rows * (K / 8);
   const unsigned blocks = (unsigned)cdiv(total > 0 ? total : 1, kQuantThreads);
+  const unsigned blocks8 = (unsigned)cdiv(total > 0 ? total : 1, kQuantThreads * kQ8Units);
   const bool bf = x_dtype == GBW_DTYPE_BF16;
   const bool wide = total > (int64_t)UINT32_MAX;
   if (fmt == GBW_FMT_E8M0_B32) {
 #define GBW_Q8(T, W, R)                                                                                       \
-  hipLaunchKernelGGL((k_quant_e8m0<T, W, R>), dim3(blocks), dim3(kQuantThreads), 0, s, (const T*)x, rows, K, \
+  hipLaunchKernelGGL((k_quant_e8m0<T, W, R>), dim3(blocks8), dim3(kQuantThreads), 0, s, (const T*)x, rows, K, \
                      tail_copy, codes, scales)
 #define GBW_Q8F(R)                                                              \
   if (bf) {                                                                     \
