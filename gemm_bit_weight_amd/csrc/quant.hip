@@ -244,12 +244,17 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_e4m3(const T* __restric
   const float s = __uint_as_float(am) / d;
   const uint32_t sc = E5 ? ue5m3_rne_sat(s) : e4m3_rne_sat(s);
   const float den = (E5 ? ue5m3_value(sc) : e4m3_value(sc)) * S_T;
-  uint32_t word = 0;
+  // element = RNE onto E2M1 of the fp32 quotient x / den (sign kept; a block
+  // whose scale decodes to 0 encodes signed zeros): the division in fp32,
+  // then v_cvt_scalef32_pk_fp4_f32 at scale 1 for the rounding
+  float q[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t mag = den > 0.0f ? e2m1_rne(__uint_as_float(abs_bits(v[i])) / den) : 0u;
-    word |= (mag | ((__float_as_uint(v[i]) >> 28) & 8u)) << (4 * i);
-  }
+  for (int i = 0; i < 8; ++i) q[i] = den > 0.0f ? v[i] / den : v[i] * 0.0f;
+  uint32_t word = 0;
+  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q[0], q[1], 1.0f, 0);
+  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q[2], q[3], 1.0f, 1);
+  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q[4], q[5], 1.0f, 2);
+  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q[6], q[7], 1.0f, 3);
   if (!live) return;
   *reinterpret_cast<uint32_t*>(codes + row * (K / 2) + col / 2) = word;
   if ((threadIdx.x & 1) == 0) scales[row * (K / 16) + col / 16] = (uint8_t)sc;
