@@ -63,4 +63,5 @@ from .moe import (  # noqa: F401
     moe_gateup,
     swiglu_bf16,
     moe_down_combine,
+    moe_down_combine_residual,
 )

@@ -21,6 +21,7 @@ import numpy as np
 
 from .formats import (
     FMT_E4M3_B16,
+    FMT_E8M0_B32,
     TENSOR_SCALED,
     bf16_bits_to_f32,
     dequantize,
@@ -161,3 +162,21 @@ def moe_down_combine(h_codes, h_scales, fmt, route, wd_codes, wd_scales, h_ts=No
 
 def bf16_to_f64(bits):
     return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def moe_down_combine_residual(h_codes, h_scales, route, wd_codes, wd_scales, r_codes, r_scales, tail,
+                              tokens=None):
+    """PRQuant on the expert down-projections (E8M0-B32 / MXFP4):
+
+    Y[t] = sum_j w[t][j] * (deq(Hq_p) deq(W_down,e)^T + deq(Hq_p[:, I-tail:]) deq(R_e)^T)
+
+    with R_e = W_down,e[:, I-tail:] - deq(Q(W_down,e))[:, I-tail:] quantized
+    (PRQuant §4 Eq. (2) per expert; the augmented GEMM of §4 "Kernel design"
+    over I + tail).  h_codes [P][I/2]; r_codes [E][H][tail/2].
+    """
+    y = moe_down_combine(h_codes, h_scales, FMT_E8M0_B32, route, wd_codes, wd_scales, tokens=tokens)
+    if tail:
+        I = h_codes.shape[1] * 2
+        y = y + moe_down_combine(h_codes[:, (I - tail) // 2:], h_scales[:, (I - tail) // 32:], FMT_E8M0_B32, route,
+                                 r_codes, r_scales, tokens=tokens)
+    return y

@@ -169,3 +169,63 @@ def test_token_subset_matches_full():
     y, _ = _ffn(x, logits, w_gu, w_d, 2, "e4m3_b16")
     ys, _ = _ffn(x, logits, w_gu, w_d, 2, "e4m3_b16", tokens=[3, 0, 19])
     assert np.array_equal(ys, y[[3, 0, 19]])
+
+
+# ---------------------------------------------------------------------------
+# PRQuant tail residual on the expert down-projections
+# ---------------------------------------------------------------------------
+
+def _residual_problem(seed, T=10, H=64, I=128, E=3, topk=2, tail=64, on_grid=False):
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((T * topk, I)).astype(np.float32)
+    w_d = (rng.standard_normal((E, H, I)) * 0.05).astype(np.float32)
+    if on_grid:   # weights that MXFP4 represents exactly: R = 0
+        w_d = np.stack([oracle.dequantize(*oracle.quantize_e8m0_b32(w_d[e]), "e8m0_b32").astype(np.float32)
+                        for e in range(E)])
+    route = oracle.moe_route(rng.standard_normal((T, E)).astype(np.float32), topk)
+    hc, hs = oracle.quantize_e8m0_b32(h)
+    wc, ws, rc, rs = [], [], [], []
+    for e in range(E):
+        c, s = oracle.quantize_e8m0_b32(w_d[e])
+        r = oracle.residual_weight(w_d[e], c, s, tail)
+        r_c, r_s = oracle.quantize_e8m0_b32(r)
+        wc.append(c); ws.append(s); rc.append(r_c); rs.append(r_s)
+    return hc, hs, route, np.array(wc), np.array(ws), np.array(rc), np.array(rs), w_d, h
+
+
+def test_residual_down_is_the_augmented_gemm():
+    """Y with the residual term equals the plain down GEMM over [H, H_tail] x
+    [W, R] (the online tail copy of the activation, the concatenated weight)."""
+    hc, hs, route, wc, ws, rc, rs, _, _ = _residual_problem(40)
+    y = oracle.moe_down_combine_residual(hc, hs, route, wc, ws, rc, rs, 64)
+    ac, as_ = oracle.tail_copy(hc, hs, 64)
+    y_aug = oracle.moe_down_combine(ac, as_, "e8m0_b32", route, np.concatenate([wc, rc], axis=2),
+                                    np.concatenate([ws, rs], axis=2))
+    assert np.allclose(y, y_aug, rtol=1e-12, atol=1e-12 * np.abs(y).max())
+
+
+def test_residual_down_special_cases():
+    hc, hs, route, wc, ws, rc, rs, _, _ = _residual_problem(41)
+    plain = oracle.moe_down_combine(hc, hs, "e8m0_b32", route, wc, ws)
+    assert np.array_equal(oracle.moe_down_combine_residual(hc, hs, route, wc, ws, rc[..., :0], rs[..., :0], 0), plain)
+    # weights already on the MXFP4 grid: the residual quantizes to zero codes and changes nothing
+    hc, hs, route, wc, ws, rc, rs, _, _ = _residual_problem(42, on_grid=True)
+    assert np.all((oracle.unpack_nibbles(rc) & 7) == 0)
+    plain = oracle.moe_down_combine(hc, hs, "e8m0_b32", route, wc, ws)
+    assert np.array_equal(oracle.moe_down_combine_residual(hc, hs, route, wc, ws, rc, rs, 64), plain)
+
+
+def test_residual_down_reduces_weight_error():
+    """Sanity for the method: the residual term moves the output toward the
+    unquantized weights (same quantized activations on both sides)."""
+    hc, hs, route, wc, ws, rc, rs, w_d, _ = _residual_problem(43, tail=64)
+    hd = oracle.dequantize(hc, hs, "e8m0_b32")
+    exact = np.zeros((10, 64))
+    for e in range(3):
+        p = np.arange(route["expert_offsets"][e], route["expert_offsets"][e + 1])
+        t = route["pair_token"][p]
+        j = np.argmax(route["topk_ids"][t] == e, axis=1)
+        np.add.at(exact, t, route["topk_w"][t, j][:, None] * (hd[p] @ w_d[e].astype(np.float64).T))
+    plain = oracle.moe_down_combine(hc, hs, "e8m0_b32", route, wc, ws)
+    res = oracle.moe_down_combine_residual(hc, hs, route, wc, ws, rc, rs, 64)
+    assert np.linalg.norm(res - exact) < np.linalg.norm(plain - exact)
