@@ -245,6 +245,54 @@ def tail_decode(gbw, synth, torch):
             "TFLOP_s": flops / us / 1e6, "replicas": R}
 
 
+def moe_mxfp4_prquant(gbw, synth, torch, steps=5, tail=128):
+    """MXFP4 experts at the E4M3-B16 workload's shape (T=4096, H=2048, I=768,
+    128 experts, top-8), plain and with PRQuant's tail residual on the
+    down-projections (gate/up appends the tail copy of h; the down stage runs
+    over I + tail against [W_down | R]).  Overhead of the residual in %."""
+    T, H, I, E, K = 4096, 2048, 768, 128, 8
+    d = synth.moe_problem(T, H, I, E, seed=0, device="cuda")
+    q = gbw.mx_quantize(d["w_gate_up"].reshape(E * 2 * I, H), gbw.FMT_E8M0_B32)
+    Wgu = gbw.Weight(gbw.FMT_E8M0_B32, 2 * I, H, q.codes.view(E, 2 * I, H // 2), q.scales.view(E, 2 * I, H // 32),
+                     n_experts=E)
+    wd = d["w_down"]
+    qc = torch.empty((E, H, (I + tail) // 2), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((E, H, (I + tail) // 32), dtype=torch.uint8, device="cuda")
+    for e in range(E):
+        wq = gbw.mx_quantize(wd[e].contiguous(), gbw.FMT_E8M0_B32)
+        rq = gbw.mx_quantize(gbw.mx_residual(wd[e].contiguous(), wq.codes, wq.scales, tail), gbw.FMT_E8M0_B32)
+        qc[e] = torch.cat([wq.codes, rq.codes], dim=1)
+        qs[e] = torch.cat([wq.scales, rq.scales], dim=1)
+    Wd = {0: gbw.Weight(gbw.FMT_E8M0_B32, H, I, qc[:, :, :I // 2].contiguous(), qs[:, :, :I // 32].contiguous(),
+                        n_experts=E),
+          tail: gbw.Weight(gbw.FMT_E8M0_B32, H, I + tail, qc, qs, n_experts=E)}
+    del d["w_gate_up"], d["w_down"]
+    P = T * K
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    res = {"T": T, "hidden": H, "intermediate": I, "experts": E, "topk": K, "tail": tail}
+    for tl in (0, tail):
+        hc = torch.empty((P, (I + tl) // 2), dtype=torch.uint8, device="cuda")
+        hs = torch.empty((P, (I + tl) // 32), dtype=torch.uint8, device="cuda")
+
+        def step(tl=tl, hc=hc, hs=hs):
+            route = gbw.moe_route(d["logits"], K)
+            xq = gbw.mx_quantize(d["x"], gbw.FMT_E8M0_B32)
+            gbw.moe_grouped_gemm(gbw.MOE_GATEUP_SWIGLU, route, xq, Wgu, h_codes=hc, h_scales=hs, h_tail=tl)
+            gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, gbw.Act(gbw.FMT_E8M0_B32, hc, hs), Wd[tl], y=y)
+        step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        res["ms_per_step_tail%d" % tl] = e0.elapsed_time(e1) / steps
+    res["overhead_pct"] = 100.0 * (res["ms_per_step_tail%d" % tail] / res["ms_per_step_tail0"] - 1.0)
+    res["added_down_flop_pct"] = 100.0 * tail / I
+    return res
+
+
 def quantize_rate(gbw, synth, torch):
     """Online activation quantization (E8M0-B32) at the headline activation
     shape, plain and with the block Hadamard rotation, over four distinct
@@ -390,7 +438,8 @@ def main():
         out["extra"] = {"moe_e4m3_b16": moe_e4m3(gbw, synth, torch),
                         "moe_e5m3_b16": moe_e4m3(gbw, synth, torch, fmt=gbw.FMT_E5M3_B16),
                         "mx_gemm_16x512x512": dense_small(gbw, synth, torch),
-                        "quantize_e8m0_8192x4096": quantize_rate(gbw, synth, torch)}
+                        "quantize_e8m0_8192x4096": quantize_rate(gbw, synth, torch),
+                        "moe_mxfp4_prquant_down": moe_mxfp4_prquant(gbw, synth, torch)}
     print(json.dumps(out), flush=True)
 
 

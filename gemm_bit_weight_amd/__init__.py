@@ -66,7 +66,7 @@ class _Act(_c.Structure):
 
 
 class _MoeOut(_c.Structure):
-    _fields_ = [("h_bf16", _vp), ("h_codes", _vp), ("h_scales", _vp), ("y", _vp)]
+    _fields_ = [("h_bf16", _vp), ("h_codes", _vp), ("h_scales", _vp), ("y", _vp), ("h_tail", _c.c_int64)]
 
 
 _lib.gbw_status_string.restype = _c.c_char_p
@@ -309,10 +309,12 @@ def moe_route(logits, topk, out=None, ws=None, stream=None):
 
 
 def moe_grouped_gemm(stage, route, a: Act, w: Weight, h_bf16=None, h_codes=None, h_scales=None, y=None, flags=0,
-                     ws=None, stream=None):
+                     ws=None, stream=None, h_tail=0):
     """One stage of the routed expert FFN (see include/gbw.h).
 
-    GATEUP: fills h_bf16 [P][I] and/or h_codes [P][I/2] + h_scales [P][I/32].
+    GATEUP: fills h_bf16 [P][I] and/or h_codes [P][(I+h_tail)/2] + h_scales
+            [P][(I+h_tail)/32] (h_tail > 0: the quantized last h_tail columns
+            are appended again, PRQuant's online tail copy).
     DOWN:   overwrites y [T][H] through a bf16 (flags=FP32_COMBINE: fp32)
             slot buffer in the workspace and a fixed-order combine; ws=False
             adds into y with fp32 atomics instead (no workspace).
@@ -329,7 +331,7 @@ def moe_grouped_gemm(stage, route, a: Act, w: Weight, h_bf16=None, h_codes=None,
     o = _MoeOut(h_bf16.data_ptr() if h_bf16 is not None else None,
                 h_codes.data_ptr() if h_codes is not None else None,
                 h_scales.data_ptr() if h_scales is not None else None,
-                y.data_ptr() if y is not None else None)
+                y.data_ptr() if y is not None else None, h_tail)
     ca, cw = a.c(), w.c()
     _check(_lib.moe_grouped_gemm(stage, T, topk, _ptr(route["expert_offsets"]), _ptr(route["pair_token"]),
                                  _ptr(route["pair_pos"]), _ptr(route["topk_w"]), _c.byref(ca), _c.byref(cw),

@@ -68,8 +68,9 @@ struct MoeArgs {
   int32_t n_tiles;         // output tiles along N
   int32_t total_tiles;
   uint16_t* h_bf16;        // GATEUP: [P][I] or null
-  uint8_t* h_codes;        // GATEUP: [P][I/2] or null
-  uint8_t* h_scales;       // GATEUP: [P][I/32] or null
+  uint8_t* h_codes;        // GATEUP: [P][(I+h_tail)/2] or null
+  uint8_t* h_scales;       // GATEUP: [P][(I+h_tail)/32] or null
+  int32_t h_tail;          // GATEUP: columns I-h_tail..I-1 also stored at I..I+h_tail-1
   float* y;                // DOWN: [T][H]
   void* slots;             // DOWN: [P][H] bf16 or fp32 per-pair outputs (pair-major), or null (atomics into y)
   int32_t slots_f32;       // 1: fp32 slots, 0: bf16 slots
@@ -258,7 +259,7 @@ constexpr int fp4_threads(int BN) { return 2 * BN; }
 template <int BN>
 __device__ __forceinline__ void h_tile_store(const MoeArgs& p, const TileInfo& ti, const uint16_t* sHb, int tid) {
   constexpr int HR = BN / 2 + 8, GPR = BN / 16, NT = fp4_threads(BN);
-  const int64_t I = p.N / 2;
+  const int64_t I = p.N / 2, W = I + p.h_tail;  // W: code columns per h row
 #pragma unroll 2
   for (int k = 0; k < kMoeBM * GPR / NT; ++k) {
     const int g = tid + NT * k;
@@ -271,8 +272,14 @@ __device__ __forceinline__ void h_tile_store(const MoeArgs& p, const TileInfo& t
     if (m < ti.rows) {
       const int64_t row = ti.row0 + m;
       if (p.h_codes) {
-        *reinterpret_cast<uint32_t*>(p.h_codes + row * (I / 2) + (int64_t)ti.nt * (BN / 4) + 4 * q) = codes;
-        if ((q & 3) == 0) p.h_scales[row * (I / 32) + (int64_t)ti.nt * (BN / 64) + (q >> 2)] = (uint8_t)sc;
+        const int64_t c = (int64_t)ti.nt * (BN / 2) + 8 * q;  // first h column of these 8
+        *reinterpret_cast<uint32_t*>(p.h_codes + row * (W / 2) + c / 2) = codes;
+        if ((q & 3) == 0) p.h_scales[row * (W / 32) + c / 32] = (uint8_t)sc;
+        if (c >= I - p.h_tail) {  // PRQuant online tail copy
+          const int64_t c2 = c + p.h_tail;
+          *reinterpret_cast<uint32_t*>(p.h_codes + row * (W / 2) + c2 / 2) = codes;
+          if ((q & 3) == 0) p.h_scales[row * (W / 32) + c2 / 32] = (uint8_t)sc;
+        }
       }
       if (p.h_bf16) *reinterpret_cast<v4i*>(p.h_bf16 + row * I + (int64_t)ti.nt * (BN / 2) + 8 * q) = w;
     }
@@ -890,6 +897,8 @@ extern "C" int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const in
     if (fp4 && (!out->h_codes) != (!out->h_scales))
       return fail(GBW_E_ARG, "moe_grouped_gemm: h_codes and h_scales go together");
     if (e4m3 && !out->h_bf16) return fail(GBW_E_ARG, "moe_grouped_gemm: E4M3/E5M3 gate/up writes h_bf16");
+    if (out->h_tail < 0 || out->h_tail % 32 || out->h_tail > N / 2 || (out->h_tail && (e4m3 || !out->h_codes)))
+      return fail(GBW_E_SHAPE, "moe_grouped_gemm: h_tail must be a multiple of 32, <= I, with E8M0 h codes");
   } else {
     if (N % 256) return fail(GBW_E_SHAPE, "moe_grouped_gemm: down rows (H) must be a multiple of 256");
     if (a->rows < P) return fail(GBW_E_SHAPE, "moe_grouped_gemm: activation has fewer rows than pairs");
@@ -934,6 +943,7 @@ extern "C" int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const in
   p.h_bf16 = out->h_bf16;
   p.h_codes = out->h_codes;
   p.h_scales = out->h_scales;
+  p.h_tail = stage == GBW_MOE_GATEUP_SWIGLU ? (int32_t)out->h_tail : 0;
   p.y = out->y;
   p.slots = use_slots ? ws : nullptr;
   p.slots_f32 = f32c ? 1 : 0;

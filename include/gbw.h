@@ -222,9 +222,16 @@ int moe_route(const float* logits, int64_t T, int32_t E, int32_t topk, int32_t* 
  * (down stage only; the gate/up stage takes none). */
 typedef struct gbw_moe_out {
   uint16_t* h_bf16;   /* GATEUP: [P][I] bf16 bits or NULL            */
-  uint8_t* h_codes;   /* GATEUP, E8M0: [P][I/2] or NULL               */
-  uint8_t* h_scales;  /* GATEUP, E8M0: [P][I/32] or NULL              */
+  uint8_t* h_codes;   /* GATEUP, E8M0: [P][(I+h_tail)/2] or NULL      */
+  uint8_t* h_scales;  /* GATEUP, E8M0: [P][(I+h_tail)/32] or NULL     */
   float* y;           /* DOWN: [T][H]                                 */
+  int64_t h_tail;     /* GATEUP, E8M0: append a copy of the quantized
+                         last h_tail columns of h with their scales
+                         (PRQuant §4 online tail copy; multiple of 32,
+                         <= I; 0 = none).  A down stage over I + h_tail
+                         with weights [W_down | R] (R the quantized
+                         residual of the last h_tail columns, PRQuant §4
+                         Eq. (2)) is then PRQuant's augmented GEMM.      */
 } gbw_moe_out;
 
 int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const int32_t* expert_offsets,

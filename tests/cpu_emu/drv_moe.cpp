@@ -1,6 +1,6 @@
 // CPU emulation driver for moe_grouped_gemm (test infrastructure): every
 // buffer is its own exact-size heap block, so AddressSanitizer reports any
-// out-of-bounds access; usage: drv_moe T H I E topk fmt [h_bf16].
+// out-of-bounds access; usage: drv_moe T H I E topk fmt [h_bf16 [h_tail]].
 #include <hip/hip_runtime.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -32,6 +32,8 @@ template <class T> T* buf(size_t n, std::mt19937& g) {
 int main(int argc, char** argv) {
   const int T = atoi(argv[1]), H = atoi(argv[2]), I = atoi(argv[3]), E = atoi(argv[4]), k = atoi(argv[5]);
   const int fmt = atoi(argv[6]);  // 0 MX, 2 VQ, 1 E4M3, 3 E5M3
+  const int tail = argc > 8 ? atoi(argv[8]) : 0;  // E8M0 h: PRQuant tail copy, down over I + tail
+  const int Ih = I + tail;                        // h code columns
   const int P = T * k;
   std::mt19937 g(1234);
   // routing: k distinct experts per token
@@ -59,7 +61,7 @@ int main(int argc, char** argv) {
   // gate/up
   gbw_weight wg{}, wd{};
   wg.fmt = fmt; wg.n_experts = E; wg.N = 2 * I; wg.K = H;
-  wd.fmt = fmt; wd.n_experts = E; wd.N = H; wd.K = I;
+  wd.fmt = fmt; wd.n_experts = E; wd.N = H; wd.K = Ih;
   for (gbw_weight* w : {&wg, &wd}) {
     const size_t NK = (size_t)E * w->N * w->K;
     w->codes = fmt == 2 ? buf<uint8_t>(NK / 4, g) : buf<uint8_t>(NK / 2, g);
@@ -72,14 +74,15 @@ int main(int argc, char** argv) {
   ax.codes = buf<uint8_t>((size_t)T * H / 2, g); ax.scales = buf<uint8_t>((size_t)T * H / sdiv, g);
   ax.tensor_scale = e4 ? ats : nullptr;
   gbw_moe_out o{};
-  uint8_t* hc = buf<uint8_t>((size_t)P * I / 2, g);
-  uint8_t* hs = buf<uint8_t>((size_t)P * I / 32, g);
+  uint8_t* hc = buf<uint8_t>((size_t)P * Ih / 2, g);
+  uint8_t* hs = buf<uint8_t>((size_t)P * Ih / 32, g);
+  o.h_tail = tail;
   uint16_t* hb = buf<uint16_t>((size_t)P * I, g);
   if (e4) o.h_bf16 = hb; else { o.h_codes = hc; o.h_scales = hs; o.h_bf16 = (argc > 7) ? hb : nullptr; }
   int st = moe_grouped_gemm(0, T, k, off, ptok, ppos, tw, &ax, &wg, &o, 0, nullptr, 0, nullptr);
   printf("gateup status %d\n", st);
   // down: activation = h
-  gbw_act ah{}; ah.fmt = e4 ? fmt : 0; ah.rows = P; ah.K = I;
+  gbw_act ah{}; ah.fmt = e4 ? fmt : 0; ah.rows = P; ah.K = Ih;
   uint8_t* hcodes = e4 ? buf<uint8_t>((size_t)P * I / 2, g) : hc;
   uint8_t* hsc = e4 ? buf<uint8_t>((size_t)P * I / 16, g) : hs;
   ah.codes = hcodes; ah.scales = hsc; ah.tensor_scale = e4 ? ats : nullptr;

@@ -52,6 +52,14 @@ def test_moe_grouped_gemm_in_bounds(build_dir, fmt):
     assert "gateup status 0" in out and all(f"down mode {m} status 0" in out for m in range(3)), out
 
 
+def test_moe_prquant_tail_copy_in_bounds(build_dir):
+    """MXFP4 gate/up writing h with a 128-column tail copy (I + 128 code
+    columns), then the down stage over I + 128."""
+    exe = _build(build_dir, "moe_gemm.hip", "drv_moe.cpp", "emu_moe")
+    out = _run(exe, 300, 512, 256, 8, 2, 0, 1, 128)
+    assert "gateup status 0" in out and all(f"down mode {m} status 0" in out for m in range(3)), out
+
+
 @pytest.mark.parametrize("T,E,K,ties", [(37, 16, 4, 0), (300, 128, 8, 0), (70, 32, 8, 1), (50, 300, 5, 0)])
 def test_moe_route_in_bounds_and_exact(build_dir, T, E, K, ties):
     exe = _build(build_dir, "moe_route.hip", "drv_route.cpp", "emu_route")

@@ -393,3 +393,78 @@ def test_moe_e4m3_full_size_sampled():
     d = synth.moe_problem(4096, 2048, 768, 128, seed=0, device=DEV)
     _run_and_check(_Problem("e4m3_b16", d["x"], d["logits"], 8, dict(w=d["w_gate_up"]), dict(w=d["w_down"]), 768),
                    tokens=[1, 2048, 4095], experts=[3, 100], h_amax=2.0)
+
+
+def _prquant_weights(wd, tail):
+    """Per expert: E8M0 down weight, its tail residual (mx_residual) quantized,
+    and the augmented [W | R] rows the down stage reads over I + tail."""
+    E, H, I = wd.shape
+    qc = torch.empty((E, H, (I + tail) // 2), dtype=torch.uint8, device=DEV)
+    qs = torch.empty((E, H, (I + tail) // 32), dtype=torch.uint8, device=DEV)
+    plain_c = torch.empty((E, H, I // 2), dtype=torch.uint8, device=DEV)
+    plain_s = torch.empty((E, H, I // 32), dtype=torch.uint8, device=DEV)
+    for e in range(E):
+        wq = gbw.mx_quantize(wd[e].contiguous(), gbw.FMT_E8M0_B32)
+        r = gbw.mx_residual(wd[e].contiguous(), wq.codes, wq.scales, tail)
+        rq = gbw.mx_quantize(r, gbw.FMT_E8M0_B32)
+        qc[e] = torch.cat([wq.codes, rq.codes], dim=1)
+        qs[e] = torch.cat([wq.scales, rq.scales], dim=1)
+        plain_c[e], plain_s[e] = wq.codes, wq.scales
+    return (gbw.Weight(gbw.FMT_E8M0_B32, H, I + tail, qc, qs, n_experts=E),
+            gbw.Weight(gbw.FMT_E8M0_B32, H, I, plain_c, plain_s, n_experts=E))
+
+
+@pytest.mark.parametrize("T,H,I,E,k,tail", [(300, 512, 256, 8, 2, 128), (64, 1024, 384, 16, 8, 128),
+                                            (97, 256, 640, 5, 3, 256)])
+def test_moe_prquant_down_residual(T, H, I, E, k, tail):
+    """PRQuant on the expert down-projections: the gate/up stage appends the
+    tail copy of the quantized h, the down stage runs over I + tail with
+    [W_down | R] rows; checked against the oracle's residual formula."""
+    banner(f"moe prquant T={T} H={H} I={I} E={E} k={k} tail={tail}")
+    d = synth.moe_problem(T, H, I, E, seed=6, device=DEV)
+    route, ref_route = _check_route(d["logits"], k)
+    P = T * k
+    wgu = d["w_gate_up"]
+    q = gbw.mx_quantize(wgu.reshape(E * 2 * I, H), gbw.FMT_E8M0_B32)
+    Wgu = gbw.Weight(gbw.FMT_E8M0_B32, 2 * I, H, q.codes.view(E, 2 * I, H // 2), q.scales.view(E, 2 * I, H // 32),
+                     n_experts=E)
+    Waug, Wplain = _prquant_weights(d["w_down"], tail)
+    xq = gbw.mx_quantize(d["x"], gbw.FMT_E8M0_B32)
+    hc = torch.empty((P, I // 2), dtype=torch.uint8, device=DEV)
+    hs = torch.empty((P, I // 32), dtype=torch.uint8, device=DEV)
+    gbw.moe_grouped_gemm(gbw.MOE_GATEUP_SWIGLU, route, xq, Wgu, h_codes=hc, h_scales=hs)
+    hca = torch.empty((P, (I + tail) // 2), dtype=torch.uint8, device=DEV)
+    hsa = torch.empty((P, (I + tail) // 32), dtype=torch.uint8, device=DEV)
+    gbw.moe_grouped_gemm(gbw.MOE_GATEUP_SWIGLU, route, xq, Wgu, h_codes=hca, h_scales=hsa, h_tail=tail)
+    # the appended columns are the online tail copy of the same quantized h
+    cc, ss = oracle.tail_copy(to_np(hc), to_np(hs), tail)
+    assert np.array_equal(to_np(hca), cc) and np.array_equal(to_np(hsa), ss)
+    y = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, gbw.Act(gbw.FMT_E8M0_B32, hca, hsa), Waug, y=y)
+    # oracle weights from the fp32 down weights: Q(W), R = W_tail - Q(W)_tail, Q(R)
+    wd = d["w_down"].cpu().numpy()
+    wc, ws, rc, rs = [], [], [], []
+    for e in range(E):
+        c, s = oracle.quantize_e8m0_b32(wd[e])
+        rq_c, rq_s = oracle.quantize_e8m0_b32(oracle.residual_weight(wd[e], c, s, tail))
+        wc.append(c); ws.append(s); rc.append(rq_c); rs.append(rq_s)
+    wc, ws, rc, rs = (np.array(v) for v in (wc, ws, rc, rs))
+    assert np.array_equal(to_np(Waug.codes), np.concatenate([wc, rc], axis=2))
+    assert np.array_equal(to_np(Waug.scales), np.concatenate([ws, rs], axis=2))
+    y_ref = oracle.moe_down_combine_residual(to_np(hc), to_np(hs), ref_route, wc, ws, rc, rs, tail)
+    assert_rows_close(to_np(y), y_ref, what="moe down with the tail residual")
+    # the residual moves the output toward the unquantized down weights
+    y_plain = torch.empty_like(y)
+    gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, gbw.Act(gbw.FMT_E8M0_B32, hc, hs), Wplain, y=y_plain)
+    hd = oracle.dequantize(to_np(hc), to_np(hs), "e8m0_b32")
+    exact = np.zeros((T, H))
+    off, pt = ref_route["expert_offsets"], ref_route["pair_token"]
+    for e in range(E):
+        p = np.arange(off[e], off[e + 1])
+        t = pt[p]
+        j = np.argmax(ref_route["topk_ids"][t] == e, axis=1)
+        np.add.at(exact, t, ref_route["topk_w"][t, j][:, None] * (hd[p] @ wd[e].astype(np.float64).T))
+    e_res = np.linalg.norm(to_np(y) - exact) / np.linalg.norm(exact)
+    e_plain = np.linalg.norm(to_np(y_plain) - exact) / np.linalg.norm(exact)
+    print(f"[stats] down-weight error with residual {e_res:.4f}, plain {e_plain:.4f}", flush=True)
+    assert e_res < e_plain
