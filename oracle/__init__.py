@@ -14,8 +14,9 @@ a float64 matmul as the contraction step.
 
 Sources (page titles as printed on the pages):
   * "MXCode: MX-Native Codebook Quantization" -- Table 1 (block formats),
-    abstract (PreScale, MX-native operand reconstruction), Fig. 2/3 and
-    Table 4 (VQ d=4, K=256, QBlock sizes).
+    abstract (PreScale, PostScale, PreScale+, MX-native operand
+    reconstruction), Fig. 2/3 and Table 4 (VQ d=4, K=256, QBlock sizes,
+    scale VQ Ks=256, ds=8), Table 2 (bits per element of each method).
   * "PRQuant: Permutation Residual Quantization for Low-Overhead Inference" --
     §4 Eq. (1) (scaled/permuted FFN), Eq. (2) (offline weight residual),
     §4 "Kernel design for efficient inference" (augmented MXFP4 GEMM and the
@@ -56,6 +57,9 @@ from .gemm import (  # noqa: F401
     lut_gemm,
     vq_decode_codes,
     vq_dequantize,
+    postscale_block_scales,
+    prescale_plus_block_scales,
+    mxcode_bpe,
 )
 from .rotation import fwht32_fp32  # noqa: F401
 from .moe import (  # noqa: F401

@@ -1,4 +1,5 @@
-"""GEMM references: MX GEMM, tail-residual GEMM, LUT GEMM, VQ decode.
+"""GEMM references: MX GEMM, tail-residual GEMM, LUT GEMM, VQ decode (MXCode
+PreScale, PostScale and PreScale+ block scales).
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
 
@@ -137,3 +138,65 @@ def vq_dequantize(idx, codebook, scales, qblock=64):
     E8M0-B32 prescale."""
     codes = vq_decode_codes(idx, codebook, qblock)
     return dequantize(codes, scales, FMT_E8M0_B32)
+
+
+# ----------------------------------------------------------------------------
+# MXCode PostScale and PreScale+: where the block scales come from
+# ----------------------------------------------------------------------------
+# The E2M1 code stream is the PreScale one in both (vq_decode_codes); only the
+# E8M0 block scale of each 32-element block along K is stored differently.
+
+def postscale_block_scales(qscales, K, qblock=64):
+    """MXCode PostScale (abstract: the learned codebook itself is quantized
+    to MXFP4).  Reading: the QBlock's codebook is one MXFP4 tensor with one
+    E8M0 scale, so every 32-block of weights in QBlock (n // qblock,
+    k // qblock) has that scale.
+
+    qscales [N/qblock][K/qblock] uint8 -> E8M0 block scales [N][K/32].
+    """
+    qs = np.asarray(qscales, dtype=np.uint8)
+    N = qs.shape[0] * qblock
+    assert qs.shape[1] * qblock == K and K % 32 == 0
+    rows = np.arange(N) // qblock
+    cols = (np.arange(K // 32) * 32) // qblock
+    return qs[rows[:, None], cols[None, :]]
+
+
+def prescale_plus_block_scales(sidx, scale_codebook, ds=8):
+    """MXCode PreScale+ (abstract: the PreScale scales are compressed by VQ;
+    Table 4 caption: Ks = 256 entries, ds = 8).  Reading: the block scales of
+    one row are cut along K into vectors of ds consecutive scales; vector j of
+    row n is entry sidx[n][j] of the matrix's scale codebook.
+
+    sidx [N][K/(32 ds)] uint8, scale_codebook [Ks][ds] E8M0 codes
+    -> E8M0 block scales [N][K/32].
+    """
+    si = np.asarray(sidx).astype(np.int64)
+    scb = np.asarray(scale_codebook, dtype=np.uint8)
+    assert scb.shape[1] == ds
+    return scb[si].reshape(si.shape[0], si.shape[1] * ds)
+
+
+def mxcode_bpe(method, block, qblock, N, K, d=4, n_entries=256, ks=256, ds=8, scale_bits=8):
+    """Stored bits per weight element as MXCode Table 2 counts them: VQ
+    indices, FP4 codebooks and scales (Table 1: the FP32 tensor scale of the
+    16-element formats is not counted).
+
+    method: "native" (plain block-scaled FP4), "prescale" (per-block scales
+    kept), "postscale" (one scale per QBlock codebook), "prescale_plus"
+    (block scales vector-quantized, one Ks x ds scale codebook per matrix).
+    block: elements per scale block (32 for E8M0-B32, 16 for E4M3-B16).
+    """
+    if method == "native":
+        return 4.0 + scale_bits / block
+    idx = np.log2(n_entries) / d                      # one index per d weights
+    fp4_codebook = n_entries * d * 4 / qblock ** 2     # one table per QBlock
+    if method == "prescale":
+        return idx + fp4_codebook + scale_bits / block
+    if method == "postscale":
+        return idx + fp4_codebook + scale_bits / qblock ** 2
+    if method == "prescale_plus":
+        scale_idx = np.log2(ks) / (ds * block)         # one index per ds scales
+        scale_codebook = ks * ds * scale_bits / (N * K)
+        return idx + fp4_codebook + scale_idx + scale_codebook
+    raise ValueError(method)

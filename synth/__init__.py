@@ -23,9 +23,12 @@ activations, which are not available):
     end of K by a stable partition applied to the columns of both;
   * MoE: X ~ N(0,1) bf16, router logits ~ N(0,1) fp32, per-expert
     W_gate, W_up, W_down ~ N(0, 0.02^2) fp32;
-  * VQ->MX MoE weights: per 64x64 QBlock a 256-entry table of 4-element
-    E2M1 keys, 8-bit indices, E8M0 prescale codes -- drawn directly in that
-    format (the codebook learning itself is offline and out of scope).
+  * VQ->MX MoE weights: per QBlock (64x64 unless stated) a 256-entry table
+    of 4-element E2M1 keys, 8-bit indices, and E8M0 scales stored per 32
+    along K (PreScale), per QBlock table (PostScale) or as 8-vectors of
+    scales quantized against a 256-entry table per matrix (PreScale+) --
+    drawn directly in that format (codebook learning is offline and out of
+    scope).
 """
 
 import zlib
@@ -175,12 +178,24 @@ def moe_problem(T, H, I, E, seed=0, device="cpu"):
 _E2M1_MAG_PROBS = [0.08, 0.15, 0.15, 0.14, 0.18, 0.16, 0.10, 0.04]
 
 
-def vq_weight(E, N, K, qblock=64, n_entries=256, seed=0, name="vq", device="cpu"):
+def _scale_codes(shape, seed, name, device):
+    """E8M0 codes in {119, 120, 121} (weights of magnitude ~0.02), 1:2:1."""
+    u = uniform(shape, seed, name, device)
+    return (119 + (u >= 0.25).to(torch.uint8) + (u >= 0.75).to(torch.uint8)).to(torch.uint8)
+
+
+def vq_weight(E, N, K, qblock=64, n_entries=256, seed=0, name="vq", device="cpu", scales="prescale"):
     """Codebook->MX weights drawn directly in the VQ format.
 
     idx uint8 [E][N][K/4]; codebook 16-bit [E][N/qblock][K/qblock][256]
-    (4 E2M1 codes per entry, element i in bits 4i+3:4i); prescale E8M0 codes
-    uint8 [E][N][K/32] in {119, 120, 121} (weights of magnitude ~0.02).
+    (4 E2M1 codes per entry, element i in bits 4i+3:4i); and the scales, by
+    ``scales``:
+      "prescale":      E8M0 codes uint8 [E][N][K/32];
+      "postscale":     one E8M0 code per QBlock table, uint8 [E][N/qblock][K/qblock];
+      "prescale_plus": 8-bit scale-vector indices uint8 [E][N][K/256] into a
+                       per-matrix table ``scale_codebook`` uint8 [E][256][8] of
+                       E8M0 codes (8 consecutive block scales along K each).
+    Every E8M0 code is drawn from {119, 120, 121}.
     """
     assert N % qblock == 0 and K % qblock == 0
     probs = torch.tensor(_E2M1_MAG_PROBS, dtype=torch.float64)
@@ -194,16 +209,26 @@ def vq_weight(E, N, K, qblock=64, n_entries=256, seed=0, name="vq", device="cpu"
     codebook = torch.where(key >= 32768, key - 65536, key).to(torch.int16)
     g = _gen(seed, f"{name}.idx", device)
     idx = torch.randint(0, n_entries, (E, N, K // 4), generator=g, device=device, dtype=torch.uint8)
-    u = uniform((E, N, K // 32), seed, f"{name}.scale", device)
-    scales = (119 + (u >= 0.25).to(torch.uint8) + (u >= 0.75).to(torch.uint8)).to(torch.uint8)
-    return dict(idx=idx, codebook=codebook.contiguous(), scales=scales)
+    out = dict(idx=idx, codebook=codebook.contiguous())
+    if scales == "prescale":
+        out["scales"] = _scale_codes((E, N, K // 32), seed, f"{name}.scale", device)
+    elif scales == "postscale":
+        out["scales"] = _scale_codes((E, N // qblock, K // qblock), seed, f"{name}.qscale", device)
+    elif scales == "prescale_plus":
+        assert K % 256 == 0
+        g = _gen(seed, f"{name}.sidx", device)
+        out["scales"] = torch.randint(0, 256, (E, N, K // 256), generator=g, device=device, dtype=torch.uint8)
+        out["scale_codebook"] = _scale_codes((E, 256, 8), seed, f"{name}.scb", device)
+    else:
+        raise ValueError(scales)
+    return out
 
 
-def moe_vq_problem(T, H, I, E, seed=0, device="cpu"):
+def moe_vq_problem(T, H, I, E, seed=0, device="cpu", scales="prescale", qblock=64):
     """X bf16 [T][H], logits [T][E], VQ gate/up weights (N = 2I, K = H) and
-    VQ down weights (N = H, K = I)."""
+    VQ down weights (N = H, K = I); ``scales`` and ``qblock`` as in vq_weight."""
     x = normal((T, H), 1.0, seed, "moevq.x", device).to(torch.bfloat16)
     logits = normal((T, E), 1.0, seed, "moevq.logits", device)
-    gu = vq_weight(E, 2 * I, H, seed=seed, name="moevq.gate_up", device=device)
-    dn = vq_weight(E, H, I, seed=seed, name="moevq.down", device=device)
+    gu = vq_weight(E, 2 * I, H, qblock=qblock, seed=seed, name="moevq.gate_up", device=device, scales=scales)
+    dn = vq_weight(E, H, I, qblock=qblock, seed=seed, name="moevq.down", device=device, scales=scales)
     return dict(x=x, logits=logits, gate_up=gu, down=dn)
