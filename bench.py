@@ -75,14 +75,22 @@ def copy_calibration(torch, nbytes):
 # headline: VQ->MX MoE prefill
 # ---------------------------------------------------------------------------
 
-def moe_vq_prefill(gbw, synth, torch, steps, warmup):
+VQ_SCALE_FMT = {"prescale": "FMT_VQ4_E8M0", "postscale": "FMT_VQ4_POST", "prescale_plus": "FMT_VQ4_PLUS"}
+
+
+def moe_vq_prefill(gbw, synth, torch, steps, warmup, scales="prescale"):
+    """The VQ->MX MoE FFN; ``scales`` picks the MXCode block-scale layout
+    (PreScale for the headline, PostScale / PreScale+ as extra lines)."""
     T, H, I, E, K = 8192, 4096, 1536, 128, 8
     dev = "cuda"
-    d = synth.moe_vq_problem(T, H, I, E, seed=0, device=dev)
-    Wgu = gbw.Weight(gbw.FMT_VQ4_E8M0, 2 * I, H, d["gate_up"]["idx"], d["gate_up"]["scales"],
-                     d["gate_up"]["codebook"], n_experts=E)
-    Wd = gbw.Weight(gbw.FMT_VQ4_E8M0, H, I, d["down"]["idx"], d["down"]["scales"], d["down"]["codebook"],
-                    n_experts=E)
+    d = synth.moe_vq_problem(T, H, I, E, seed=0, device=dev, scales=scales)
+    fmt = getattr(gbw, VQ_SCALE_FMT[scales])
+
+    def weight(v, N, Kd):
+        return gbw.Weight(fmt, N, Kd, v["idx"], v["scales"], v["codebook"], n_experts=E,
+                          scale_codebook=v.get("scale_codebook"))
+    Wgu = weight(d["gate_up"], 2 * I, H)
+    Wd = weight(d["down"], H, I)
     P = T * K
     route = dict(topk_ids=torch.empty((T, K), dtype=torch.int32, device=dev),
                  topk_w=torch.empty((T, K), dtype=torch.float32, device=dev),
@@ -127,12 +135,28 @@ def moe_vq_prefill(gbw, synth, torch, steps, warmup):
     flops_gu = 2.0 * P * (2 * I) * H
     flops_dn = 2.0 * P * H * I
     weight_bytes = sum(t.numel() * t.element_size() for t in
-                       (Wgu.codes, Wgu.scales, Wgu.codebook, Wd.codes, Wd.scales, Wd.codebook))
+                       (Wgu.codes, Wgu.scales, Wgu.codebook, Wd.codes, Wd.scales, Wd.codebook)
+                       + tuple(w.scale_codebook for w in (Wgu, Wd) if w.scale_codebook is not None))
     return dict(ms_step=ms_step, gu_ms=gu_ms, dn_ms=dn_ms, flops=flops_gu + flops_dn, flops_gu=flops_gu,
                 flops_dn=flops_dn, weight_bytes=weight_bytes, data=d, route=route, T=T, H=H, I=I, E=E, K=K)
 
 
 CPU_SAMPLE_EXPERTS = 32   # about 10-15 s of oracle work on the host cores
+
+
+def moe_vq_scale_layouts(gbw, synth, torch, steps=5, warmup=2):
+    """The headline FFN with MXCode PostScale and PreScale+ weight scales:
+    same shapes and kernels, fewer stored scale bytes."""
+    out = {}
+    for scales in ("postscale", "prescale_plus"):
+        r = moe_vq_prefill(gbw, synth, torch, steps, warmup, scales=scales)
+        n_w = 3 * r["E"] * r["H"] * r["I"]
+        out[scales] = {"ms_per_step": r["ms_step"], "gate_up_ms": r["gu_ms"], "down_combine_ms": r["dn_ms"],
+                       "tflops": r["flops"] / (r["ms_step"] * 1e-3) / 1e12,
+                       "weight_bytes": r["weight_bytes"], "bits_per_weight": 8.0 * r["weight_bytes"] / n_w}
+        r.clear()
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(oracle, synth, torch, np, res):
@@ -439,7 +463,8 @@ def main():
                         "moe_e5m3_b16": moe_e4m3(gbw, synth, torch, fmt=gbw.FMT_E5M3_B16),
                         "mx_gemm_16x512x512": dense_small(gbw, synth, torch),
                         "quantize_e8m0_8192x4096": quantize_rate(gbw, synth, torch),
-                        "moe_mxfp4_prquant_down": moe_mxfp4_prquant(gbw, synth, torch)}
+                        "moe_mxfp4_prquant_down": moe_mxfp4_prquant(gbw, synth, torch),
+                        "moe_vq_scale_layouts": moe_vq_scale_layouts(gbw, synth, torch)}
     print(json.dumps(out), flush=True)
 
 

@@ -32,6 +32,8 @@ FMT_E8M0_B32 = 0
 FMT_E4M3_B16 = 1
 FMT_VQ4_E8M0 = 2
 FMT_E5M3_B16 = 3
+FMT_VQ4_POST = 4
+FMT_VQ4_PLUS = 5
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
 TS_DYNAMIC = 1
@@ -57,7 +59,8 @@ _i64 = _c.c_int64
 
 class _Weight(_c.Structure):
     _fields_ = [("fmt", _i32), ("n_experts", _i32), ("N", _i64), ("K", _i64), ("codes", _vp), ("scales", _vp),
-                ("codebook", _vp), ("tensor_scale", _vp), ("ts_per_expert", _i32)]
+                ("codebook", _vp), ("tensor_scale", _vp), ("ts_per_expert", _i32), ("qblock", _i32),
+                ("scale_codebook", _vp)]
 
 
 class _Act(_c.Structure):
@@ -167,12 +170,15 @@ class Weight:
     tensor_scale: Optional[torch.Tensor] = None
     ts_per_expert: int = 1
     n_experts: int = 1
+    qblock: int = 0                                # VQ formats: QBlock edge (0 = 64)
+    scale_codebook: Optional[torch.Tensor] = None  # FMT_VQ4_PLUS: [E][256][8] E8M0 codes
 
     def c(self):
         return _Weight(self.fmt, self.n_experts, self.N, self.K, self.codes.data_ptr(), self.scales.data_ptr(),
                        self.codebook.data_ptr() if self.codebook is not None else None,
                        self.tensor_scale.data_ptr() if self.tensor_scale is not None else None,
-                       self.ts_per_expert)
+                       self.ts_per_expert, self.qblock,
+                       self.scale_codebook.data_ptr() if self.scale_codebook is not None else None)
 
 
 def _dev(t):

@@ -14,11 +14,14 @@
 // CodeQuant Fig. 1-2 show the experts of an MoE FFN).  Weight formats:
 //  * MXFP4 (E8M0-B32): codes and scales stream straight into LDS;
 //  * VQ -> MX ("MXCode: MX-Native Codebook Quantization", abstract, PreScale;
-//    Fig. 2/3 and Table 4: d = 4, 256 entries, 64x64 QBlocks): each 8-bit
-//    index is expanded through its QBlock's 256-entry table of four E2M1 codes
-//    (the table lives in LDS, 512 bytes) into an MXFP4 operand tile in LDS;
-//    the E8M0 prescales are the operand's block scales.  No wider copy of the
-//    weights exists anywhere, in HBM or on chip;
+//    Fig. 2/3 and Table 4: d = 4, 256 entries, QBlocks of 64, 128 or 256):
+//    each 8-bit index is expanded through its QBlock's 256-entry table of four
+//    E2M1 codes (the table lives in LDS, 512 bytes) into an MXFP4 operand tile
+//    in LDS; the E8M0 prescales are the operand's block scales.  PostScale
+//    keeps one scale per QBlock table, PreScale+ an 8-bit index per 8 scales
+//    along K into a 256 x 8 table per expert (held in LDS, 2 KiB): both are
+//    turned into the same per-stage scale dwords when a stage is stored.  No
+//    wider copy of the weights exists anywhere, in HBM or on chip;
 //  * E4M3-B16 + FP32 tensor scale: exact decode to fp16 tiles, fp16 MFMA.
 //
 // Work decomposition: one workgroup per output tile of one expert (256 pairs
@@ -44,8 +47,12 @@ constexpr int kMoeBM = 256;       // pairs (A rows) per tile
 constexpr int kMoeThreads = 256;  // threads that run the tile-list scan (every kernel has at least this many)
 constexpr int kRowB = 80;         // LDS bytes per FP4 operand row per stage (64 of data + 16 of padding)
 constexpr int kMaxMoeExperts = 256;
+constexpr int kXsMaxK = 8192;     // PostScale / PreScale+: longest K whose tile scale bytes are staged in LDS
 
-enum WFmt { W_MX = 0, W_VQ = 1 };
+// weight formats of the FP4 kernel: MXFP4, and VQ -> MX with the block
+// scales stored per 32 along K (PreScale), per QBlock table (PostScale) or
+// as table-coded 8-vectors (PreScale+)
+enum WFmt { W_MX = 0, W_VQ = 1, W_VQ_POST = 2, W_VQ_PLUS = 3 };
 
 struct MoeArgs {
   int32_t stage;
@@ -59,8 +66,10 @@ struct MoeArgs {
   const uint8_t* a_scales; // [rows][K/32]
   int64_t K;               // reduction length (H for GATEUP, I for DOWN)
   const uint8_t* w_codes;  // MX: [E][N][K/2]; VQ: idx [E][N][K/4]
-  const uint8_t* w_scales; // [E][N][K/32]
-  const uint16_t* w_cb;    // VQ: [E][N/64][K/64][256]
+  const uint8_t* w_scales; // [E][N][K/32]; PostScale [E][N/qb][K/qb]; PreScale+ [E][N][K/256]
+  const uint16_t* w_cb;    // VQ: [E][N/qb][K/qb][256]
+  const uint8_t* w_scb;    // PreScale+: [E][256][8] E8M0 codes
+  int32_t qsh;             // VQ: log2 of the QBlock edge (6, 7 or 8)
   const float* a_ts;       // E4M3: activation tensor scale [1]
   const float* w_ts;       // E4M3: weight tensor scales [E][ts_per]
   int32_t ts_per;
@@ -293,10 +302,18 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
   constexpr int NA = kMoeBM * 4 / NT;                   // 16-byte A chunks per thread per stage
   constexpr int NLUT = BN / 32;                         // QBlock tables per stage (2 per 64 weight rows)
   constexpr int SB = BN > 256 ? BN : 256;               // B scale slots (>= BN; the extra ones are never read)
+  constexpr bool VQ = WF != W_MX;
+  constexpr bool XS = WF == W_VQ_POST || WF == W_VQ_PLUS;  // B scales not stored per 32 along K
   __shared__ __attribute__((aligned(16))) uint8_t sOp[2 * kABuf + 2 * kBBuf];
   __shared__ uint32_t sAs[2][kMoeBM];
   __shared__ uint32_t sBs[2][SB];
-  __shared__ __attribute__((aligned(16))) uint16_t sLut[2][WF == W_VQ ? NLUT * 256 : 4];
+  __shared__ __attribute__((aligned(16))) uint16_t sLut[2][VQ ? NLUT * 256 : 4];
+  __shared__ uint32_t sScb[WF == W_VQ_PLUS ? 512 : 1];  // PreScale+: the expert's 256 x 8 scale table
+  // PostScale / PreScale+: the tile's stored B-scale bytes, staged once per
+  // tile -- PostScale: the K/qb codes of the QBlock row of each 64-row band
+  // at band * nq; PreScale+: the K/256 indices of tile row j at j * nq
+  constexpr int XSB = WF == W_VQ_PLUS ? BN * (kXsMaxK / 256) : WF == W_VQ_POST ? (BN / 64) * (kXsMaxK / 64) : 4;
+  __shared__ __attribute__((aligned(4))) uint8_t sXs[XSB];
   __shared__ int scan[kMoeThreads];
   __shared__ int s_tok[kMoeBM];
   __shared__ float s_w[kMoeBM];
@@ -329,6 +346,39 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
     s_tok[r] = tok;
     s_w[r] = wt;
   }
+  // bytes per staged PostScale band / PreScale+ row
+  const int nq = WF == W_VQ_PLUS ? (int)(p.K / 256) : WF == W_VQ_POST ? (int)(p.K >> p.qsh) : 0;
+  if (WF == W_VQ_PLUS) {
+    const uint32_t* scb = reinterpret_cast<const uint32_t*>(p.w_scb) + (int64_t)ti.e * 512;
+    for (int i = tid; i < 512; i += NT) sScb[i] = scb[i];
+    // the tile's rows are two runs of BN/2 consecutive weight rows (gate and
+    // up halves, or the two halves of a down tile): (BN/2) * nq contiguous,
+    // 4-byte aligned bytes each; nq <= 32 makes at most 4 dwords per thread
+    const int run_dw = (BN / 2) * nq / 4;
+    uint32_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + u * NT;
+      if (i < 2 * run_dw) {
+        const int run = i >= run_dw ? 1 : 0;
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(
+            p.w_scales + ((int64_t)ti.e * p.N + b_row<BN>(p, ti.nt, run * (BN / 2))) * nq);
+        v[u] = src[i - run * run_dw];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + u * NT;
+      if (i < 2 * run_dw) reinterpret_cast<uint32_t*>(sXs)[i] = v[u];
+    }
+  } else if (WF == W_VQ_POST) {
+    // (BN/64) * nq <= NT bytes: one per thread
+    if (tid < (BN / 64) * nq) {
+      const int band = tid / nq;
+      const int64_t qrow = b_row<BN>(p, ti.nt, band * 64) >> p.qsh;
+      sXs[tid] = p.w_scales[((int64_t)ti.e * (p.N >> p.qsh) + qrow) * nq + (tid - band * nq)];
+    }
+  }
   __syncthreads();
 
   // --- fixed per-thread load assignments --------------------------------
@@ -344,16 +394,35 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
   const uint8_t* arow[NA];
 #pragma unroll
   for (int u = 0; u < NA; ++u) arow[u] = p.a_codes + a_src(ar + (NT / 4) * u) * (K / 2);
+  // PostScale / PreScale+ (XS) B scales come from LDS (sXs), not from a
+  // per-32 stream: the B-scale waves of the 512-thread kernel then load the
+  // scale row of A row t - 256 instead (unused, keeps one load sequence)
   const uint8_t* scl0;  // A scales (or, with 512 threads, B scales for t >= 256)
   const uint8_t* scl1;  // B scales (256 threads only)
   if (NT == 512) {
-    scl0 = tid < 256 ? p.a_scales + a_src(tid) * (K / 32)
-                     : p.w_scales + ((int64_t)ti.e * wN + b_row<BN>(p, ti.nt, tid - 256)) * (K / 32);
+    scl0 = tid < 256 || XS ? p.a_scales + a_src(tid & 255) * (K / 32)
+                           : p.w_scales + ((int64_t)ti.e * wN + b_row<BN>(p, ti.nt, tid - 256)) * (K / 32);
     scl1 = scl0;
   } else {
     scl0 = p.a_scales + a_src(tid) * (K / 32);
     scl1 = p.w_scales + ((int64_t)ti.e * wN + b_row<BN>(p, ti.nt, tid % BN)) * (K / 32);
   }
+  // XS: whether this thread makes B scales (all threads with 256, t >= 256
+  // with 512 -- whole waves either way), and for which tile row
+  const bool xs_thr = XS && (NT != 512 || wave >= 4);
+  const int xs_row = NT == 512 ? (tid & 255) : tid % BN;
+  // the four E8M0 block scales of stage s of that row, as one dword
+  auto xs_scales = [&](int s) __attribute__((always_inline)) {
+    if (WF == W_VQ_PLUS) {
+      const uint32_t si = sXs[xs_row * nq + (s >> 1)];  // 8 scales = 2 stages per index
+      return sScb[(si << 1) | (uint32_t)(s & 1)];
+    }
+    // PostScale: the codes of the QBlocks holding the stage's two 64-wide
+    // halves (the same one for QBlocks of 128 or 256)
+    const uint8_t* const q = sXs + (xs_row >> 6) * nq;
+    const uint32_t c0 = q[(s * 128) >> p.qsh], c1 = q[(s * 128 + 64) >> p.qsh];
+    return c0 * 0x0101u | c1 * 0x01010000u;
+  };
   uint32_t* const sdst0 = (NT == 512 && tid >= 256) ? &sBs[0][tid - 256] : &sAs[0][tid];  // buffer 1: + SB or 256
   const uint8_t* wrow[2];
   const uint8_t* vrow = nullptr;
@@ -366,12 +435,19 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
   } else {
     // idx: row tid >> 1, 16-byte chunk tid & 1 of the 32-byte stage row
     vrow = p.w_codes + ((int64_t)ti.e * wN + b_row<BN>(p, ti.nt, tid >> 1)) * (K / 4);
-    // LUT: 8 bytes of table tid >> 6 (BN/64 QBlock rows x 2 QBlock columns)
-    const int tb = tid >> 6;
+    // LUT: 8 bytes of table slot tid >> 6 (BN/64 row bands of 64 x 2 halves
+    // of the stage); a slot holds the table of the QBlock its 64 x 64 weight
+    // block lies in (with QBlocks of 128 or 256 several slots hold one table)
+    const int tb = wave;  // (a scalar: the table offsets below are scalar arithmetic)
     lut_kb = tb & 1;
-    const int64_t qrow = b_row<BN>(p, ti.nt, (tb >> 1) * 64) / 64;
-    cbase = p.w_cb + ((int64_t)ti.e * (wN / 64) + qrow) * (K / 64) * 256;
+    const int64_t qrow = b_row<BN>(p, ti.nt, (tb >> 1) * 64) >> p.qsh;
+    cbase = p.w_cb + ((int64_t)ti.e * (wN >> p.qsh) + qrow) * (K >> p.qsh) * 256 + (tid & 63) * 4;
   }
+  // element offset of the table of slot half `kb` of stage s within the
+  // slot's QBlock row (K <= 2^30, so 32 bits hold it)
+  auto lut_off = [&](int s, int kb) __attribute__((always_inline)) {
+    return (uint32_t)(((s * 128 + kb * 64) >> p.qsh) << 8);
+  };
 
   // Software pipeline, one barrier per 128-element stage.  Iteration s:
   //   1. store stage s+1 (loaded into registers during iteration s-1) into
@@ -393,6 +469,7 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
   constexpr bool S16 = BN == 256;
   v4i s4ca = v4i{0, 0, 0, 0}, s4cb = s4ca, s4na = s4ca, s4nb = s4ca;
   uint2 pl;
+  uint32_t pq = 0;  // XS: the B-scale dword of the stage gload last prepared
   const int last = steps - 1;
   auto gload = [&](int s) __attribute__((always_inline)) {
     s = s < last ? s : last;
@@ -407,15 +484,16 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
       }
     } else {
       ps0 = *reinterpret_cast<const uint32_t*>(scl0 + (int64_t)s * 4);
-      if (NT != 512) ps1 = *reinterpret_cast<const uint32_t*>(scl1 + (int64_t)s * 4);
+      if (NT != 512 && !XS) ps1 = *reinterpret_cast<const uint32_t*>(scl1 + (int64_t)s * 4);
     }
+    if (XS && xs_thr) pq = xs_scales(s);
     if (WF == W_MX) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) pb[u] = load16(wrow[u] + kb + 16 * ac);
     } else {
       pb[0] = load16(vrow + (int64_t)s * 32 + 16 * (tid & 1));
       const int sl = s + 1 < last ? s + 1 : last;  // tables run one stage ahead
-      pl = *reinterpret_cast<const uint2*>(cbase + ((int64_t)sl * 2 + lut_kb) * 256 + (tid & 63) * 4);
+      pl = *reinterpret_cast<const uint2*>(cbase + lut_off(sl, lut_kb));
     }
   };
   // stage k's registers -> LDS buffer k&1 (tables of stage k+1 -> table buffer (k+1)&1)
@@ -432,6 +510,12 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
       const int e = kk & 3;
       ps0 = (uint32_t)(e == 0 ? a4[0] : e == 1 ? a4[1] : e == 2 ? a4[2] : a4[3]);
       ps1 = (uint32_t)(e == 0 ? b4[0] : e == 1 ? b4[1] : e == 2 ? b4[2] : b4[3]);
+    }
+    if (XS) {
+      if (NT == 512)
+        ps0 = xs_thr ? pq : ps0;
+      else
+        ps1 = pq;
     }
 #pragma unroll
     for (int u = 0; u < NA; ++u) *reinterpret_cast<v4i*>(a + (ar + (NT / 4) * u) * kRowB + 16 * ac) = pa[u];
@@ -485,14 +569,14 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
   const int nband = band_count(ti.rows, wm);
 
   // prologue: stage 0 (and the tables of stages 0 and 1) in LDS, stage 1 in registers
-  if (WF == W_VQ) {
-    const uint2 t0 = *reinterpret_cast<const uint2*>(cbase + (int64_t)lut_kb * 256 + (tid & 63) * 4);
+  if (VQ) {
+    const uint2 t0 = *reinterpret_cast<const uint2*>(cbase + lut_off(0, lut_kb));
     *reinterpret_cast<uint2*>(&sLut[0][(tid >> 6) * 256 + (tid & 63) * 4]) = t0;
   }
   gload(0);
   lstore(0);
   __syncthreads();
-  if (WF == W_VQ) vq_expand(0);
+  if (VQ) vq_expand(0);
   gload(1);
   __syncthreads();
 
@@ -529,7 +613,7 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
   auto kloop = [&](auto nb) __attribute__((always_inline)) {
     for (int s = 0; s < steps; ++s) {
       lstore(s + 1);
-      if (WF == W_VQ) vq_expand(s + 1);
+      if (VQ) vq_expand(s + 1);
       gload(s + 2);
       mma(s & 1, nb);
       __syncthreads();
@@ -882,8 +966,10 @@ extern "C" int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const in
   const int64_t K = w->K, N = w->N, P = T * topk;
   if (a->K != K) return fail(GBW_E_SHAPE, "moe_grouped_gemm: activation K %lld != weight K %lld", (long long)a->K,
                              (long long)K);
-  if (K <= 0 || K % 128) return fail(GBW_E_SHAPE, "moe_grouped_gemm: K must be a positive multiple of 128");
-  const bool fp4 = (w->fmt == GBW_FMT_E8M0_B32 || w->fmt == GBW_FMT_VQ4_E8M0) && a->fmt == GBW_FMT_E8M0_B32;
+  if (K <= 0 || K % 128 || K > (int64_t(1) << 30))
+    return fail(GBW_E_SHAPE, "moe_grouped_gemm: K must be a positive multiple of 128, at most 2^30");
+  const bool vq = w->fmt == GBW_FMT_VQ4_E8M0 || w->fmt == GBW_FMT_VQ4_POST || w->fmt == GBW_FMT_VQ4_PLUS;
+  const bool fp4 = (w->fmt == GBW_FMT_E8M0_B32 || vq) && a->fmt == GBW_FMT_E8M0_B32;
   // E4M3-B16 or E5M3-B16 (tensor-scaled, decoded exactly to fp16 / bf16)
   const bool e4m3 = (w->fmt == GBW_FMT_E4M3_B16 || w->fmt == GBW_FMT_E5M3_B16) && a->fmt == w->fmt;
   if (!fp4 && !e4m3) return fail(GBW_E_UNSUPPORTED, "moe_grouped_gemm: unsupported activation/weight formats");
@@ -904,7 +990,20 @@ extern "C" int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const in
     if (a->rows < P) return fail(GBW_E_SHAPE, "moe_grouped_gemm: activation has fewer rows than pairs");
     if (!out->y) return fail(GBW_E_ARG, "moe_grouped_gemm: down needs y");
   }
-  if (w->fmt == GBW_FMT_VQ4_E8M0 && !w->codebook) return fail(GBW_E_ARG, "moe_grouped_gemm: VQ needs a codebook");
+  const int qb = vq && w->qblock ? w->qblock : 64;
+  if (vq) {
+    if (!w->codebook) return fail(GBW_E_ARG, "moe_grouped_gemm: VQ needs a codebook");
+    if (qb != 64 && qb != 128 && qb != 256) return fail(GBW_E_ARG, "moe_grouped_gemm: QBlock edge must be 64, 128 or 256");
+    if (N % qb || K % qb) return fail(GBW_E_SHAPE, "moe_grouped_gemm: N and K must be multiples of the QBlock edge");
+    if (w->fmt != GBW_FMT_VQ4_E8M0 && K > kXsMaxK)
+      return fail(GBW_E_SHAPE, "moe_grouped_gemm: PostScale / PreScale+ weights need K <= %d", kXsMaxK);
+    if (w->fmt == GBW_FMT_VQ4_PLUS) {
+      if (K % 256) return fail(GBW_E_SHAPE, "moe_grouped_gemm: PreScale+ needs K %% 256 == 0 (8 scales per index)");
+      if (!w->scale_codebook) return fail(GBW_E_ARG, "moe_grouped_gemm: PreScale+ needs a scale codebook");
+      if (reinterpret_cast<uintptr_t>(w->scale_codebook) & 3u)
+        return fail(GBW_E_ALIGN, "moe_grouped_gemm: the scale codebook must be 4-byte aligned");
+    }
+  }
   if (e4m3 && (!w->tensor_scale || !a->tensor_scale || w->ts_per_expert < 1))
     return fail(GBW_E_ARG, "moe_grouped_gemm: E4M3/E5M3 needs tensor scales");
   if (T == 0) return GBW_OK;
@@ -939,6 +1038,8 @@ extern "C" int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const in
   p.w_codes = w->codes;
   p.w_scales = w->scales;
   p.w_cb = w->codebook;
+  p.w_scb = w->fmt == GBW_FMT_VQ4_PLUS ? w->scale_codebook : nullptr;
+  p.qsh = qb == 256 ? 8 : qb == 128 ? 7 : 6;
   p.N = N;
   p.h_bf16 = out->h_bf16;
   p.h_codes = out->h_codes;
@@ -947,8 +1048,10 @@ extern "C" int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const in
   p.y = out->y;
   p.slots = use_slots ? ws : nullptr;
   p.slots_f32 = f32c ? 1 : 0;
+  // (PostScale / PreScale+ weight scales are staged in LDS whatever this says)
+  const bool w_row_scales = w->fmt != GBW_FMT_VQ4_POST && w->fmt != GBW_FMT_VQ4_PLUS;
   p.scales16 = (K % 512 == 0 && !(reinterpret_cast<uintptr_t>(a->scales) & 15u) &&
-                !(reinterpret_cast<uintptr_t>(w->scales) & 15u))
+                (!w_row_scales || !(reinterpret_cast<uintptr_t>(w->scales) & 15u)))
                    ? 1
                    : 0;
   // every kernel below writes through these: refuse to launch without them
@@ -968,7 +1071,12 @@ extern "C" int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const in
     // gate/up: 256-row weight tiles (each expanded weight tile meets the most
     // pairs); down (short K): 128-row tiles, two workgroups per CU
     const int bn = stage == GBW_MOE_GATEUP_SWIGLU ? 256 : 128;
-    st = w->fmt == GBW_FMT_VQ4_E8M0 ? launch_moe_fp4<W_VQ>(p, bn, s) : launch_moe_fp4<W_MX>(p, bn, s);
+    switch (w->fmt) {
+      case GBW_FMT_VQ4_E8M0: st = launch_moe_fp4<W_VQ>(p, bn, s); break;
+      case GBW_FMT_VQ4_POST: st = launch_moe_fp4<W_VQ_POST>(p, bn, s); break;
+      case GBW_FMT_VQ4_PLUS: st = launch_moe_fp4<W_VQ_PLUS>(p, bn, s); break;
+      default: st = launch_moe_fp4<W_MX>(p, bn, s); break;
+    }
   }
   if (st) return st;
   if (use_slots) {

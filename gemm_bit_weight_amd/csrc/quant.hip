@@ -263,14 +263,28 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_e4m3(const T* __restric
 // ---------------------------------------------------------------------------
 // decode to fp32 (same decoders as the GEMM kernels) and the residual
 // ---------------------------------------------------------------------------
+// One decoded weight element.  VQ formats (qsh = log2 of the QBlock edge):
+// the E2M1 code is nibble k%4 of the QBlock table entry the index selects;
+// the E8M0 scale is stored per 32 along K (PreScale), per QBlock (PostScale)
+// or is element (k/32)%8 of the scale-table entry of the row's index for
+// elements 256*(k/256) .. (PreScale+).
 __device__ __forceinline__ float decode_elem(int32_t fmt, const uint8_t* codes, const uint8_t* scales,
-                                             const uint16_t* codebook, const float* ts, int32_t ts_seg,
-                                             int64_t N, int64_t K, int64_t n, int64_t k) {
-  if (fmt == GBW_FMT_VQ4_E8M0) {
+                                             const uint16_t* codebook, const uint8_t* scb, int32_t qsh,
+                                             const float* ts, int32_t ts_seg, int64_t N, int64_t K, int64_t n,
+                                             int64_t k) {
+  if (fmt == GBW_FMT_VQ4_E8M0 || fmt == GBW_FMT_VQ4_POST || fmt == GBW_FMT_VQ4_PLUS) {
     const uint32_t idx = codes[n * (K / 4) + k / 4];
-    const uint32_t key = codebook[((n / 64) * (K / 64) + k / 64) * 256 + idx];
+    const int64_t qblk = (n >> qsh) * (K >> qsh) + (k >> qsh);
+    const uint32_t key = codebook[qblk * 256 + idx];
     const uint32_t c = (key >> (4 * (k & 3))) & 0xFu;
-    return e2m1_value(c) * e8m0_value(scales[n * (K / 32) + k / 32]);
+    uint32_t sc;
+    if (fmt == GBW_FMT_VQ4_POST)
+      sc = scales[qblk];
+    else if (fmt == GBW_FMT_VQ4_PLUS)
+      sc = scb[(uint32_t)scales[n * (K / 256) + k / 256] * 8 + (k / 32) % 8];
+    else
+      sc = scales[n * (K / 32) + k / 32];
+    return e2m1_value(c) * e8m0_value(sc);
   }
   const uint32_t c = (codes[n * (K / 2) + k / 2] >> (4 * (k & 1))) & 0xFu;
   if (fmt == GBW_FMT_E8M0_B32) return e2m1_value(c) * e8m0_value(scales[n * (K / 32) + k / 32]);
@@ -281,12 +295,13 @@ __device__ __forceinline__ float decode_elem(int32_t fmt, const uint8_t* codes, 
 }
 
 __global__ void k_dequant(int32_t fmt, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-                          const uint16_t* __restrict__ codebook, const float* __restrict__ ts,
-                          int32_t ts_seg, int64_t N, int64_t K, float* __restrict__ out) {
+                          const uint16_t* __restrict__ codebook, const uint8_t* __restrict__ scb, int32_t qsh,
+                          const float* __restrict__ ts, int32_t ts_seg, int64_t N, int64_t K,
+                          float* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= N * K) return;
   const int64_t n = i / K, k = i % K;
-  out[i] = decode_elem(fmt, codes, scales, codebook, ts, ts_seg, N, K, n, k);
+  out[i] = decode_elem(fmt, codes, scales, codebook, scb, qsh, ts, ts_seg, N, K, n, k);
 }
 
 __global__ void k_residual(const float* __restrict__ w, int64_t N, int64_t K, int64_t tail,
@@ -295,7 +310,7 @@ __global__ void k_residual(const float* __restrict__ w, int64_t N, int64_t K, in
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= N * tail) return;
   const int64_t n = i / tail, k = K - tail + i % tail;
-  const float d = decode_elem(GBW_FMT_E8M0_B32, codes, scales, nullptr, nullptr, 1, N, K, n, k);
+  const float d = decode_elem(GBW_FMT_E8M0_B32, codes, scales, nullptr, nullptr, 6, nullptr, 1, N, K, n, k);
   r[i] = w[n * K + k] - d;
 }
 
@@ -405,6 +420,8 @@ extern "C" int mx_dequantize(const gbw_weight* w, int32_t expert, float* out, vo
     return fail(GBW_E_ARG, "mx_dequantize: bad extent or expert");
   if (!w->codes || !w->scales) return fail(GBW_E_ARG, "mx_dequantize: null codes/scales");
   const int64_t N = w->N, K = w->K;
+  const int qb = w->qblock ? w->qblock : 64;
+  const int qsh = qb == 256 ? 8 : qb == 128 ? 7 : 6;
   int64_t cbytes, sbytes;
   switch (w->fmt) {
     case GBW_FMT_E8M0_B32:
@@ -421,10 +438,15 @@ extern "C" int mx_dequantize(const gbw_weight* w, int32_t expert, float* out, vo
       sbytes = N * K / 16;
       break;
     case GBW_FMT_VQ4_E8M0:
-      if (K % 64 || N % 64) return fail(GBW_E_SHAPE, "mx_dequantize: VQ needs N, K multiples of 64");
+    case GBW_FMT_VQ4_POST:
+    case GBW_FMT_VQ4_PLUS:
+      if (qb != 64 && qb != 128 && qb != 256) return fail(GBW_E_ARG, "mx_dequantize: QBlock edge must be 64, 128 or 256");
+      if (K % qb || N % qb) return fail(GBW_E_SHAPE, "mx_dequantize: VQ needs N, K multiples of the QBlock edge");
       if (!w->codebook) return fail(GBW_E_ARG, "mx_dequantize: VQ needs a codebook");
       cbytes = N * K / 4;
-      sbytes = N * K / 32;
+      sbytes = w->fmt == GBW_FMT_VQ4_E8M0 ? N * K / 32 : w->fmt == GBW_FMT_VQ4_POST ? (N / qb) * (K / qb) : N * K / 256;
+      if (w->fmt == GBW_FMT_VQ4_PLUS && (K % 256 || !w->scale_codebook))
+        return fail(w->scale_codebook ? GBW_E_SHAPE : GBW_E_ARG, "mx_dequantize: PreScale+ needs K %% 256 == 0 and a scale codebook");
       break;
     default:
       return fail(GBW_E_ARG, "mx_dequantize: bad format");
@@ -432,11 +454,13 @@ extern "C" int mx_dequantize(const gbw_weight* w, int32_t expert, float* out, vo
   if (N == 0 || K == 0) return GBW_OK;
   int st = check_device();
   if (st) return st;
-  const uint16_t* cb = w->codebook ? w->codebook + (int64_t)expert * (N / 64) * (K / 64) * 256 : nullptr;
+  const bool vq = w->fmt == GBW_FMT_VQ4_E8M0 || w->fmt == GBW_FMT_VQ4_POST || w->fmt == GBW_FMT_VQ4_PLUS;
+  const uint16_t* cb = vq ? w->codebook + (int64_t)expert * (N / qb) * (K / qb) * 256 : nullptr;
+  const uint8_t* scb = w->fmt == GBW_FMT_VQ4_PLUS ? w->scale_codebook + (int64_t)expert * 2048 : nullptr;
   const float* ts = w->tensor_scale ? w->tensor_scale + (int64_t)expert * w->ts_per_expert : nullptr;
   const int64_t n = N * K;
   hipLaunchKernelGGL(k_dequant, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, as_stream(stream), w->fmt,
-                     w->codes + expert * cbytes, w->scales + expert * sbytes, cb, ts,
+                     w->codes + expert * cbytes, w->scales + expert * sbytes, cb, scb, qsh, ts,
                      w->ts_per_expert > 0 ? w->ts_per_expert : 1, N, K, out);
   return check_launch("mx_dequantize");
 }

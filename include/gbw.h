@@ -26,8 +26,18 @@
  *                     2^-17 to 114688 (code 0xFE), code 0xFF reserved.
  *   GBW_FMT_VQ4_E8M0  MXCode PreScale weights: 8-bit index per 4 consecutive K
  *                     elements into a 256-entry table of 4xE2M1 keys per
- *                     64x64 QBlock, plus the E8M0 per-32 prescale (abstract,
- *                     Fig. 2, Fig. 3, Table 4 caption: d = 4, K = 256).
+ *                     QBlock (qblock x qblock, 64 by default), plus the E8M0
+ *                     per-32 prescale (abstract, Fig. 2, Fig. 3, Table 4
+ *                     caption: d = 4, K = 256).
+ *   GBW_FMT_VQ4_POST  MXCode PostScale: the same indices and tables, the
+ *                     table of each QBlock quantized to MXFP4 with one E8M0
+ *                     scale, which every 32-block of that QBlock's weights
+ *                     carries (abstract; layout read from Table 2's BPE).
+ *   GBW_FMT_VQ4_PLUS  MXCode PreScale+: the same indices and tables; the
+ *                     per-32 E8M0 scales of a row are taken 8 at a time along
+ *                     K and each 8-vector is stored as an 8-bit index into a
+ *                     256-entry table of 8 E8M0 codes per matrix (abstract;
+ *                     Table 4 caption: Ks = 256, ds = 8).
  * E2M1 nibbles are packed two per byte, element 2i in bits 3:0, element 2i+1
  * in bits 7:4, bit 3 of a nibble is the sign.  A VQ key holds element i of its
  * 4-vector in bits 4i+3:4i.  All matrices are row-major; weights are [N][K]
@@ -58,6 +68,8 @@ extern "C" {
 #define GBW_FMT_E4M3_B16 1
 #define GBW_FMT_VQ4_E8M0 2
 #define GBW_FMT_E5M3_B16 3
+#define GBW_FMT_VQ4_POST 4
+#define GBW_FMT_VQ4_PLUS 5
 
 #define GBW_DTYPE_BF16 0
 #define GBW_DTYPE_F32 1
@@ -86,12 +98,18 @@ typedef struct gbw_weight {
   int32_t fmt;               /* GBW_FMT_*                                          */
   int32_t n_experts;         /* >= 1; expert e starts at e * (per-expert size)     */
   int64_t N, K;              /* per expert                                         */
-  const uint8_t* codes;      /* E8M0/E4M3/E5M3: [E][N][K/2] nibbles; VQ: [E][N][K/4] idx */
-  const uint8_t* scales;     /* E8M0 and VQ: [E][N][K/32] E8M0; E4M3/E5M3: [E][N][K/16] */
-  const uint16_t* codebook;  /* VQ only: [E][N/64][K/64][256] keys, else NULL       */
+  const uint8_t* codes;      /* E8M0/E4M3/E5M3: [E][N][K/2] nibbles; VQ*: [E][N][K/4] idx */
+  const uint8_t* scales;     /* E8M0, VQ4_E8M0: [E][N][K/32] E8M0; E4M3/E5M3: [E][N][K/16];
+                                VQ4_POST: [E][N/qb][K/qb] E8M0, one per QBlock table;
+                                VQ4_PLUS: [E][N][K/256] scale-vector indices         */
+  const uint16_t* codebook;  /* VQ*: [E][N/qb][K/qb][256] keys, else NULL           */
   const float* tensor_scale; /* E4M3/E5M3 only: [E][ts_per_expert] fp32, else NULL  */
   int32_t ts_per_expert;     /* E4M3/E5M3: rows split into this many equal segments,
                                 segment s scaled by tensor_scale[e][s] (1 or 2)     */
+  int32_t qblock;            /* VQ*: QBlock edge qb (64, 128 or 256; 0 means 64)    */
+  const uint8_t* scale_codebook; /* VQ4_PLUS: [E][256][8] E8M0 codes, 4-byte
+                                aligned: block scales 8i .. 8i+7 of row n of
+                                expert e are entry scales[e][n][i]; else NULL  */
 } gbw_weight;
 
 /* A quantized activation: [rows][K], K contiguous. */
@@ -144,7 +162,8 @@ int mx_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t K, int32_t
 
 /* mx_dequantize: decode expert `expert` of w to fp32 out [N][K] through the
  * same device decoders the GEMMs use (E8M0: e2m1*2^(s-127); E4M3 and E5M3:
- * e2m1*scale*tensor_scale[segment]; VQ: QBlock table key nibble * 2^(s-127)).
+ * e2m1*scale*tensor_scale[segment]; VQ*: QBlock table key nibble * 2^(s-127)
+ * with s the stored, per-QBlock or table-decoded E8M0 scale).
  * Used to check decoded weights bit for bit and for offline preparation. */
 int mx_dequantize(const gbw_weight* w, int32_t expert, float* out, void* stream);
 
@@ -213,7 +232,9 @@ int moe_route(const float* logits, int64_t T, int32_t E, int32_t topk, int32_t* 
  *    repeatable.  With ws = NULL the
  *    outputs are added into y with fp32 atomics (no workspace, not
  *    repeatable; GBW_DETERMINISTIC then fails with GBW_E_WORKSPACE).
- * Weights: E8M0-B32, VQ4-E8M0 (decoded to MXFP4 in LDS, scaled MFMA),
+ * Weights: E8M0-B32, VQ4-E8M0 / VQ4_POST / VQ4_PLUS (decoded to MXFP4 in
+ * LDS, scaled MFMA; N and K multiples of the QBlock edge; VQ4_POST and
+ * VQ4_PLUS need K <= 8192, VQ4_PLUS also K % 256 == 0),
  * E4M3-B16 (decoded exactly to fp16, fp16 MFMA) or E5M3-B16 (decoded exactly
  * to bf16 -- the products reach 6 * 114688, past fp16's range -- bf16 MFMA).
  * The activation format must equal the weight format for E4M3-B16 and

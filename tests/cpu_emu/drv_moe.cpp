@@ -1,6 +1,6 @@
 // CPU emulation driver for moe_grouped_gemm (test infrastructure): every
 // buffer is its own exact-size heap block, so AddressSanitizer reports any
-// out-of-bounds access; usage: drv_moe T H I E topk fmt [h_bf16 [h_tail]].
+// out-of-bounds access; usage: drv_moe T H I E topk fmt [h_bf16 [h_tail [qblock]]].
 #include <hip/hip_runtime.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -31,7 +31,8 @@ template <class T> T* buf(size_t n, std::mt19937& g) {
 }
 int main(int argc, char** argv) {
   const int T = atoi(argv[1]), H = atoi(argv[2]), I = atoi(argv[3]), E = atoi(argv[4]), k = atoi(argv[5]);
-  const int fmt = atoi(argv[6]);  // 0 MX, 2 VQ, 1 E4M3, 3 E5M3
+  const int fmt = atoi(argv[6]);  // 0 MX, 2 VQ, 1 E4M3, 3 E5M3, 4 VQ PostScale, 5 VQ PreScale+
+  const int qb = argc > 9 ? atoi(argv[9]) : 64;   // VQ QBlock edge
   const int tail = argc > 8 ? atoi(argv[8]) : 0;  // E8M0 h: PRQuant tail copy, down over I + tail
   const int Ih = I + tail;                        // h code columns
   const int P = T * k;
@@ -62,11 +63,15 @@ int main(int argc, char** argv) {
   gbw_weight wg{}, wd{};
   wg.fmt = fmt; wg.n_experts = E; wg.N = 2 * I; wg.K = H;
   wd.fmt = fmt; wd.n_experts = E; wd.N = H; wd.K = Ih;
+  const bool vq = fmt == 2 || fmt == 4 || fmt == 5;
   for (gbw_weight* w : {&wg, &wd}) {
     const size_t NK = (size_t)E * w->N * w->K;
-    w->codes = fmt == 2 ? buf<uint8_t>(NK / 4, g) : buf<uint8_t>(NK / 2, g);
-    w->scales = buf<uint8_t>(NK / sdiv, g);
-    if (fmt == 2) w->codebook = buf<uint16_t>((size_t)E * (w->N / 64) * (w->K / 64) * 256, g);
+    w->codes = vq ? buf<uint8_t>(NK / 4, g) : buf<uint8_t>(NK / 2, g);
+    const size_t nsc = fmt == 4 ? (size_t)E * (w->N / qb) * (w->K / qb) : fmt == 5 ? NK / 256 : NK / sdiv;
+    w->scales = buf<uint8_t>(nsc, g);
+    if (vq) w->codebook = buf<uint16_t>((size_t)E * (w->N / qb) * (w->K / qb) * 256, g);
+    if (vq) w->qblock = qb;
+    if (fmt == 5) w->scale_codebook = buf<uint8_t>((size_t)E * 2048, g);
     if (e4) { float* ts = (float*)malloc(E * 2 * 4); for (int i = 0; i < 2 * E; ++i) ts[i] = 1.f; w->tensor_scale = ts; w->ts_per_expert = w == &wg ? 2 : 1; }
   }
   float* ats = (float*)malloc(4); *ats = 1.f;

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth
-from parity import assert_rows_close, banner, to_np
+from parity import assert_rows_close, banner, to_np, vq_ref_block_scales
 
 pytestmark = pytest.mark.gpu
 
@@ -225,6 +225,28 @@ def test_dequantize_vq_bitexact():
     for e in range(3):
         out = to_np(gbw.mx_dequantize(W, expert=e))
         ref = oracle.vq_dequantize(v["idx"][e].numpy(), cb[e], v["scales"][e].numpy())
+        assert np.array_equal(out.astype(np.float64), ref)
+
+
+_VQ_FMT = {"prescale": gbw.FMT_VQ4_E8M0, "postscale": gbw.FMT_VQ4_POST, "prescale_plus": gbw.FMT_VQ4_PLUS}
+
+
+@pytest.mark.parametrize("scales,qblock,N,K", [("postscale", 64, 128, 192), ("postscale", 128, 256, 384),
+                                               ("postscale", 256, 256, 512), ("prescale_plus", 64, 128, 512),
+                                               ("prescale_plus", 256, 256, 768), ("prescale", 128, 384, 256)])
+def test_dequantize_vq_scale_layouts_bitexact(scales, qblock, N, K):
+    """MXCode PostScale / PreScale+ block scales and QBlocks of 64-256: the
+    device decode equals the oracle's, expert by expert."""
+    banner(f"dequantize vq {scales} qblock={qblock} N={N} K={K}")
+    E = 3
+    v = synth.vq_weight(E, N, K, qblock=qblock, seed=5, device="cpu", scales=scales)
+    W = gbw.Weight(_VQ_FMT[scales], N, K, v["idx"].to(DEV), v["scales"].to(DEV), v["codebook"].to(DEV),
+                   None, 1, E, qblock=qblock,
+                   scale_codebook=v["scale_codebook"].to(DEV) if "scale_codebook" in v else None)
+    cb = v["codebook"].numpy().view(np.uint16)
+    for e in range(E):
+        out = to_np(gbw.mx_dequantize(W, expert=e))
+        ref = oracle.vq_dequantize(v["idx"][e].numpy(), cb[e], vq_ref_block_scales(v, e, scales, K, qblock), qblock)
         assert np.array_equal(out.astype(np.float64), ref)
 
 

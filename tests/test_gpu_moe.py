@@ -23,7 +23,7 @@ import torch
 
 import oracle
 import synth
-from parity import assert_rows_close, banner, to_np, u16
+from parity import assert_rows_close, banner, to_np, u16, vq_ref_block_scales
 
 pytestmark = pytest.mark.gpu
 
@@ -123,25 +123,33 @@ class _Problem:
     """One MoE FFN problem: synthetic inputs, the oracle's view of them, and
     the GPU weight descriptors built from the same inputs."""
 
-    def __init__(self, fmt, x, logits, topk, gate_up, down, I):
+    # VQ weights by scale layout (MXCode PreScale, PostScale, PreScale+)
+    VQ = {"vq": ("prescale", gbw.FMT_VQ4_E8M0), "vq_post": ("postscale", gbw.FMT_VQ4_POST),
+          "vq_plus": ("prescale_plus", gbw.FMT_VQ4_PLUS)}
+
+    def __init__(self, fmt, x, logits, topk, gate_up, down, I, qblock=64):
         self.fmt, self.x, self.logits, self.topk, self.I = fmt, x, logits, topk, I
         T, H = x.shape
         self.T, self.H = T, H
-        E = (gate_up["w"] if fmt != "vq" else gate_up["idx"]).shape[0]
+        E = (gate_up["w"] if fmt not in self.VQ else gate_up["idx"]).shape[0]
         self.E = E
-        if fmt == "vq":
-            self.Wgu = gbw.Weight(gbw.FMT_VQ4_E8M0, 2 * I, H, gate_up["idx"].to(DEV), gate_up["scales"].to(DEV),
-                                  gate_up["codebook"].to(DEV), n_experts=E)
-            self.Wd = gbw.Weight(gbw.FMT_VQ4_E8M0, H, I, down["idx"].to(DEV), down["scales"].to(DEV),
-                                 down["codebook"].to(DEV), n_experts=E)
+        if fmt in self.VQ:
+            mode, gfmt = self.VQ[fmt]
+
+            def weight(v, N, K):
+                return gbw.Weight(gfmt, N, K, v["idx"].to(DEV), v["scales"].to(DEV), v["codebook"].to(DEV),
+                                  n_experts=E, qblock=qblock,
+                                  scale_codebook=v["scale_codebook"].to(DEV) if "scale_codebook" in v else None)
+            self.Wgu = weight(gate_up, 2 * I, H)
+            self.Wd = weight(down, H, I)
             gcpu = {k: v.cpu() for k, v in gate_up.items()}
             dcpu = {k: v.cpu() for k, v in down.items()}
             self.ref_gu = (_LazyExperts((E, 2 * I, H // 2), lambda e: oracle.vq_decode_codes(
-                gcpu["idx"][e].numpy(), gcpu["codebook"][e].numpy().view(np.uint16))),
-                _LazyExperts((E, 2 * I, H // 32), lambda e: gcpu["scales"][e].numpy()), None)
+                gcpu["idx"][e].numpy(), gcpu["codebook"][e].numpy().view(np.uint16), qblock)),
+                _LazyExperts((E, 2 * I, H // 32), lambda e: vq_ref_block_scales(gcpu, e, mode, H, qblock)), None)
             self.ref_d = (_LazyExperts((E, H, I // 2), lambda e: oracle.vq_decode_codes(
-                dcpu["idx"][e].numpy(), dcpu["codebook"][e].numpy().view(np.uint16))),
-                _LazyExperts((E, H, I // 32), lambda e: dcpu["scales"][e].numpy()), None)
+                dcpu["idx"][e].numpy(), dcpu["codebook"][e].numpy().view(np.uint16), qblock)),
+                _LazyExperts((E, H, I // 32), lambda e: vq_ref_block_scales(dcpu, e, mode, I, qblock)), None)
             return
         wgu, wd = gate_up["w"], down["w"]          # fp32 [E][2I][H], [E][H][I] (on the GPU)
         if fmt == "e8m0_b32":
@@ -204,7 +212,7 @@ class _Problem:
                       _LazyExperts((E,), lambda e: q4("d", e)[2]))
 
     def check_weight_encodings(self, experts):
-        if self.fmt == "vq":
+        if self.fmt in self.VQ:
             return
         for e in experts:
             assert np.array_equal(to_np(self.Wgu.codes[e]), self.ref_gu[0][e])
@@ -224,7 +232,7 @@ def _run_and_check(pb, tokens=None, experts=None, h_amax=None):
     h only for the sampled pairs.
     """
     T, H, I, topk = pb.T, pb.H, pb.I, pb.topk
-    fmt = "e8m0_b32" if pb.fmt == "vq" else pb.fmt
+    fmt = "e8m0_b32" if pb.fmt in _Problem.VQ else pb.fmt
     e4 = fmt in ("e4m3_b16", "e5m3_b16")          # tensor-scaled formats: h quantized by mx_quantize
     e5 = fmt == "e5m3_b16"
     afmt = (gbw.FMT_E5M3_B16 if e5 else gbw.FMT_E4M3_B16) if e4 else gbw.FMT_E8M0_B32
@@ -359,6 +367,30 @@ def test_moe_vq_small(T, H, I, E, k):
     banner(f"moe vq T={T} H={H} I={I} E={E} k={k}")
     d = synth.moe_vq_problem(T, H, I, E, seed=2, device="cpu")
     _run_and_check(_Problem("vq", d["x"].to(DEV), d["logits"].to(DEV), k, d["gate_up"], d["down"], I))
+
+
+@pytest.mark.parametrize("fmt,qblock,T,H,I,E,k", [("vq_post", 64, 300, 512, 256, 8, 2),
+                                                  ("vq_plus", 64, 300, 512, 256, 8, 2),
+                                                  ("vq_post", 128, 200, 768, 384, 6, 3),
+                                                  ("vq_plus", 256, 260, 1024, 512, 5, 2),
+                                                  ("vq", 128, 150, 512, 256, 4, 2)])
+def test_moe_vq_scale_layouts_small(fmt, qblock, T, H, I, E, k):
+    """MXCode PostScale and PreScale+ experts, and QBlocks above 64."""
+    banner(f"moe {fmt} qblock={qblock} T={T} H={H} I={I} E={E} k={k}")
+    mode = _Problem.VQ[fmt][0]
+    d = synth.moe_vq_problem(T, H, I, E, seed=3, device="cpu", scales=mode, qblock=qblock)
+    _run_and_check(_Problem(fmt, d["x"].to(DEV), d["logits"].to(DEV), k, d["gate_up"], d["down"], I, qblock))
+
+
+@pytest.mark.parametrize("fmt", ["vq_post", "vq_plus"])
+def test_moe_vq_scale_layouts_full_size_sampled(fmt):
+    """The VQ->MX FFN shape (8192 tokens, H 4096, I 1536, 128 experts, top-8)
+    with PostScale / PreScale+ scales; sampled experts and tokens."""
+    banner(f"moe {fmt} full T=8192 H=4096 I=1536 E=128 k=8")
+    mode = _Problem.VQ[fmt][0]
+    d = synth.moe_vq_problem(8192, 4096, 1536, 128, seed=0, device=DEV, scales=mode)
+    _run_and_check(_Problem(fmt, d["x"], d["logits"], 8, d["gate_up"], d["down"], 1536),
+                   tokens=[0, 2049, 4097, 8191], experts=[0, 77, 127])
 
 
 def test_moe_vq_full_size_sampled():
