@@ -96,3 +96,30 @@ def test_gemm_validation(gbw):
     r = gbw._Weight(0, 1, 8, 48, 0x3000, 0x4000, None, None, 1)
     assert L.residual_tail_gemm(16, ctypes.byref(a), ctypes.byref(w), ctypes.byref(r), 48,
                                 ctypes.c_void_p(0x5000), 0, None, 0, None) == 2
+
+
+def test_descriptor_layouts_match_the_header(gbw, tmp_path):
+    """The ctypes descriptors have the C structs' field offsets and sizes
+    (compiled from include/gbw.h by the host C compiler)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    structs = {"gbw_weight": gbw._Weight, "gbw_act": gbw._Act, "gbw_moe_out": gbw._MoeOut}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "gbw.h"', 'int main(void) {']
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ['  return 0;', '}']
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)

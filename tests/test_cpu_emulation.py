@@ -56,9 +56,9 @@ def test_moe_grouped_gemm_in_bounds(build_dir, fmt):
                          ids=["postscale-q64", "postscale-q128", "prescale_plus-q64", "prescale_plus-q256"])
 def test_moe_vq_scale_layouts_in_bounds(build_dir, fmt, qblock):
     """VQ weights with PostScale / PreScale+ scales and larger QBlocks:
-    gate/up (2I = 512 rows, K = 512) and down (K = I = 256)."""
+    gate/up (2I = 512 rows, K = 512) and down (K = I = 256), 4 experts."""
     exe = _build(build_dir, "moe_gemm.hip", "drv_moe.cpp", "emu_moe")
-    out = _run(exe, 300, 512, 256, 8, 2, fmt, 0, 0, qblock)
+    out = _run(exe, 120, 512, 256, 4, 2, fmt, 0, 0, qblock)
     assert "gateup status 0" in out and all(f"down mode {m} status 0" in out for m in range(3)), out
 
 
