@@ -146,19 +146,20 @@ def vq_dequantize(idx, codebook, scales, qblock=64):
 # The E2M1 code stream is the PreScale one in both (vq_decode_codes); only the
 # E8M0 block scale of each 32-element block along K is stored differently.
 
-def postscale_block_scales(qscales, K, qblock=64):
+def postscale_block_scales(qscales, K, qblock=64, block=32):
     """MXCode PostScale (abstract: the learned codebook itself is quantized
-    to MXFP4).  Reading: the QBlock's codebook is one MXFP4 tensor with one
-    E8M0 scale, so every 32-block of weights in QBlock (n // qblock,
-    k // qblock) has that scale.
+    to MXFP4).  Reading: the QBlock's codebook is one block-scaled FP4
+    tensor with one scale, so every block of weights in QBlock
+    (n // qblock, k // qblock) has that scale.
 
-    qscales [N/qblock][K/qblock] uint8 -> E8M0 block scales [N][K/32].
+    qscales [N/qblock][K/qblock] uint8 -> block scale codes [N][K/block]
+    (block 32 for E8M0-B32, 16 for E4M3-B16 and E5M3-B16).
     """
     qs = np.asarray(qscales, dtype=np.uint8)
     N = qs.shape[0] * qblock
-    assert qs.shape[1] * qblock == K and K % 32 == 0
+    assert qs.shape[1] * qblock == K and K % block == 0
     rows = np.arange(N) // qblock
-    cols = (np.arange(K // 32) * 32) // qblock
+    cols = (np.arange(K // block) * block) // qblock
     return qs[rows[:, None], cols[None, :]]
 
 
@@ -168,8 +169,9 @@ def prescale_plus_block_scales(sidx, scale_codebook, ds=8):
     one row are cut along K into vectors of ds consecutive scales; vector j of
     row n is entry sidx[n][j] of the matrix's scale codebook.
 
-    sidx [N][K/(32 ds)] uint8, scale_codebook [Ks][ds] E8M0 codes
-    -> E8M0 block scales [N][K/32].
+    sidx [N][K/(block ds)] uint8, scale_codebook [Ks][ds] scale codes
+    -> block scale codes [N][K/block] (block 32 for E8M0-B32, 16 for
+    E4M3-B16 and E5M3-B16).
     """
     si = np.asarray(sidx).astype(np.int64)
     scb = np.asarray(scale_codebook, dtype=np.uint8)

@@ -178,24 +178,38 @@ def moe_problem(T, H, I, E, seed=0, device="cpu"):
 _E2M1_MAG_PROBS = [0.08, 0.15, 0.15, 0.14, 0.18, 0.16, 0.10, 0.04]
 
 
-def _scale_codes(shape, seed, name, device):
-    """E8M0 codes in {119, 120, 121} (weights of magnitude ~0.02), 1:2:1."""
+def _scale_codes(shape, seed, name, device, scale_fmt="e8m0"):
+    """Block scale codes.  E8M0: {119, 120, 121} (weights of magnitude
+    ~0.02), 1:2:1.  E4M3 / UE5M3 (beside an FP32 tensor scale that maps the
+    largest block to the top of the scale range): uniform over the codes of
+    the upper three binades, 64 .. 448 (E4M3 0x68-0x7E) and 16384 .. 114688
+    (UE5M3 0xE8-0xFE)."""
     u = uniform(shape, seed, name, device)
-    return (119 + (u >= 0.25).to(torch.uint8) + (u >= 0.75).to(torch.uint8)).to(torch.uint8)
+    if scale_fmt == "e8m0":
+        return (119 + (u >= 0.25).to(torch.uint8) + (u >= 0.75).to(torch.uint8)).to(torch.uint8)
+    lo = {"e4m3": 0x68, "e5m3": 0xE8}[scale_fmt]
+    return (lo + torch.clamp((u * 23).to(torch.int32), max=22)).to(torch.uint8)
 
 
-def vq_weight(E, N, K, qblock=64, n_entries=256, seed=0, name="vq", device="cpu", scales="prescale"):
+# FP32 tensor scales of the synthetic 16-element-block VQ weights: about
+# amax / (6 * top scale) for N(0, 0.02^2) weights (amax ~ 0.1)
+VQ_TENSOR_SCALE = {"e4m3": 0.1 / 2688.0, "e5m3": 0.1 / 688128.0}
+
+
+def vq_weight(E, N, K, qblock=64, n_entries=256, seed=0, name="vq", device="cpu", scales="prescale",
+              scale_fmt="e8m0", ts_segments=1):
     """Codebook->MX weights drawn directly in the VQ format.
 
     idx uint8 [E][N][K/4]; codebook 16-bit [E][N/qblock][K/qblock][256]
     (4 E2M1 codes per entry, element i in bits 4i+3:4i); and the scales, by
-    ``scales``:
-      "prescale":      E8M0 codes uint8 [E][N][K/32];
-      "postscale":     one E8M0 code per QBlock table, uint8 [E][N/qblock][K/qblock];
-      "prescale_plus": 8-bit scale-vector indices uint8 [E][N][K/256] into a
+    ``scales``, with block b = 32 for scale_fmt "e8m0", 16 for "e4m3" and
+    "e5m3":
+      "prescale":      scale codes uint8 [E][N][K/b];
+      "postscale":     one scale code per QBlock table, uint8 [E][N/qblock][K/qblock];
+      "prescale_plus": 8-bit scale-vector indices uint8 [E][N][K/(8 b)] into a
                        per-matrix table ``scale_codebook`` uint8 [E][256][8] of
-                       E8M0 codes (8 consecutive block scales along K each).
-    Every E8M0 code is drawn from {119, 120, 121}.
+                       scale codes (8 consecutive block scales along K each).
+    "e4m3" / "e5m3" also give ``tensor_scale`` fp32 [E][ts_segments].
     """
     assert N % qblock == 0 and K % qblock == 0
     probs = torch.tensor(_E2M1_MAG_PROBS, dtype=torch.float64)
@@ -210,25 +224,33 @@ def vq_weight(E, N, K, qblock=64, n_entries=256, seed=0, name="vq", device="cpu"
     g = _gen(seed, f"{name}.idx", device)
     idx = torch.randint(0, n_entries, (E, N, K // 4), generator=g, device=device, dtype=torch.uint8)
     out = dict(idx=idx, codebook=codebook.contiguous())
+    b = 32 if scale_fmt == "e8m0" else 16
     if scales == "prescale":
-        out["scales"] = _scale_codes((E, N, K // 32), seed, f"{name}.scale", device)
+        out["scales"] = _scale_codes((E, N, K // b), seed, f"{name}.scale", device, scale_fmt)
     elif scales == "postscale":
-        out["scales"] = _scale_codes((E, N // qblock, K // qblock), seed, f"{name}.qscale", device)
+        out["scales"] = _scale_codes((E, N // qblock, K // qblock), seed, f"{name}.qscale", device, scale_fmt)
     elif scales == "prescale_plus":
-        assert K % 256 == 0
+        assert K % (8 * b) == 0
         g = _gen(seed, f"{name}.sidx", device)
-        out["scales"] = torch.randint(0, 256, (E, N, K // 256), generator=g, device=device, dtype=torch.uint8)
-        out["scale_codebook"] = _scale_codes((E, 256, 8), seed, f"{name}.scb", device)
+        out["scales"] = torch.randint(0, 256, (E, N, K // (8 * b)), generator=g, device=device, dtype=torch.uint8)
+        out["scale_codebook"] = _scale_codes((E, 256, 8), seed, f"{name}.scb", device, scale_fmt)
     else:
         raise ValueError(scales)
+    if scale_fmt != "e8m0":
+        u = uniform((E, ts_segments), seed, f"{name}.ts", device)
+        out["tensor_scale"] = (VQ_TENSOR_SCALE[scale_fmt] * (0.75 + 0.5 * u)).to(torch.float32)
     return out
 
 
-def moe_vq_problem(T, H, I, E, seed=0, device="cpu", scales="prescale", qblock=64):
-    """X bf16 [T][H], logits [T][E], VQ gate/up weights (N = 2I, K = H) and
-    VQ down weights (N = H, K = I); ``scales`` and ``qblock`` as in vq_weight."""
+def moe_vq_problem(T, H, I, E, seed=0, device="cpu", scales="prescale", qblock=64, scale_fmt="e8m0"):
+    """X bf16 [T][H], logits [T][E], VQ gate/up weights (N = 2I, K = H; with
+    16-element blocks, tensor scales per gate and up half) and VQ down
+    weights (N = H, K = I); ``scales``, ``qblock``, ``scale_fmt`` as in
+    vq_weight."""
     x = normal((T, H), 1.0, seed, "moevq.x", device).to(torch.bfloat16)
     logits = normal((T, E), 1.0, seed, "moevq.logits", device)
-    gu = vq_weight(E, 2 * I, H, qblock=qblock, seed=seed, name="moevq.gate_up", device=device, scales=scales)
-    dn = vq_weight(E, H, I, qblock=qblock, seed=seed, name="moevq.down", device=device, scales=scales)
+    gu = vq_weight(E, 2 * I, H, qblock=qblock, seed=seed, name="moevq.gate_up", device=device, scales=scales,
+                   scale_fmt=scale_fmt, ts_segments=2)
+    dn = vq_weight(E, H, I, qblock=qblock, seed=seed, name="moevq.down", device=device, scales=scales,
+                   scale_fmt=scale_fmt)
     return dict(x=x, logits=logits, gate_up=gu, down=dn)

@@ -6,8 +6,9 @@
   along K per 8-bit index into a 256-entry scale codebook per matrix for
   PreScale+), reproduces all eight printed values, and the nearby
   alternative readings do not.
-* Lossless round trips: weights built directly in MXFP4 so that the
-  compression loses nothing (at most 256 distinct 4-vectors per QBlock, one
+* Lossless round trips: weights built directly in a block-scaled FP4
+  format (E8M0-B32, E4M3-B16 or E5M3-B16) so that the compression loses
+  nothing (at most 256 distinct 4-vectors per QBlock, one
   scale per QBlock, at most 256 distinct scale vectors per matrix) are
   encoded here by a brute-force dictionary encoder written from the
   definitions; the oracle's decode must give back the original codes and
@@ -20,7 +21,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle.formats import FMT_E8M0_B32
+from oracle.formats import FMT_E4M3_B16, FMT_E5M3_B16, FMT_E8M0_B32
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "mxcode_bpe.json")))
 
@@ -92,23 +93,29 @@ def _mx_codes_with_few_vectors(rng, N, K, qblock, pool):
     return out
 
 
+# (format, block, scale codes drawn from [lo, hi)): the three block-scaled formats
+_SCALE_FMTS = [(FMT_E8M0_B32, 32, 110, 135), (FMT_E4M3_B16, 16, 0x30, 0x7F), (FMT_E5M3_B16, 16, 0x60, 0xFF)]
+
+
+@pytest.mark.parametrize("fmt,block,lo,hi", _SCALE_FMTS, ids=["e8m0", "e4m3", "e5m3"])
 @pytest.mark.parametrize("N,K,qblock", [(128, 192, 64), (128, 256, 128), (256, 512, 256)])
-def test_postscale_lossless_round_trip(N, K, qblock):
-    rng = np.random.default_rng(N + K + qblock)
+def test_postscale_lossless_round_trip(N, K, qblock, fmt, block, lo, hi):
+    rng = np.random.default_rng(N + K + qblock + block)
     nib = _mx_codes_with_few_vectors(rng, N, K, qblock, pool=200)
-    qscales = rng.integers(110, 135, size=(N // qblock, K // qblock), dtype=np.uint8)
-    # the MXFP4 weight: every 32-block of a QBlock carries that QBlock's scale
-    scales = np.zeros((N, K // 32), np.uint8)
+    qscales = rng.integers(lo, hi, size=(N // qblock, K // qblock), dtype=np.uint8)
+    # the block-scaled weight: every block of a QBlock carries that QBlock's scale
+    scales = np.zeros((N, K // block), np.uint8)
     for n in range(N):
-        for b in range(K // 32):
-            scales[n, b] = qscales[n // qblock, (32 * b) // qblock]
+        for b in range(K // block):
+            scales[n, b] = qscales[n // qblock, (block * b) // qblock]
     idx, cb = _encode_vq(nib, qblock)
     codes = oracle.vq_decode_codes(idx, cb, qblock)
     assert np.array_equal(codes, oracle.pack_nibbles(nib))
-    got = oracle.postscale_block_scales(qscales, K, qblock)
+    got = oracle.postscale_block_scales(qscales, K, qblock, block)
     assert got.dtype == np.uint8 and np.array_equal(got, scales)
-    w = oracle.dequantize(codes, got, FMT_E8M0_B32)
-    assert np.array_equal(w, oracle.dequantize(oracle.pack_nibbles(nib), scales, FMT_E8M0_B32))
+    ts = None if fmt == FMT_E8M0_B32 else 3.0e-5
+    w = oracle.dequantize(codes, got, fmt, ts)
+    assert np.array_equal(w, oracle.dequantize(oracle.pack_nibbles(nib), scales, fmt, ts))
 
 
 def _encode_scale_vq(scales, ds):
@@ -129,20 +136,21 @@ def _encode_scale_vq(scales, ds):
     return sidx, scb
 
 
+@pytest.mark.parametrize("fmt,block,lo,hi", _SCALE_FMTS, ids=["e8m0", "e4m3", "e5m3"])
 @pytest.mark.parametrize("N,K,pool", [(64, 256, 5), (96, 1024, 256), (128, 768, 40)])
-def test_prescale_plus_lossless_round_trip(N, K, pool):
-    rng = np.random.default_rng(7 * N + K)
+def test_prescale_plus_lossless_round_trip(N, K, pool, fmt, block, lo, hi):
+    rng = np.random.default_rng(7 * N + K + block)
     ds = 8
-    vecs = rng.integers(100, 140, size=(pool, ds), dtype=np.uint8)
-    pick = rng.integers(0, pool, size=(N, K // (32 * ds)))
-    scales = vecs[pick].reshape(N, K // 32)
+    vecs = rng.integers(lo, hi, size=(pool, ds), dtype=np.uint8)
+    pick = rng.integers(0, pool, size=(N, K // (block * ds)))
+    scales = vecs[pick].reshape(N, K // block)
     sidx, scb = _encode_scale_vq(scales, ds)
     got = oracle.prescale_plus_block_scales(sidx, scb, ds)
     assert got.dtype == np.uint8 and np.array_equal(got, scales)
     nib = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
     codes = oracle.pack_nibbles(nib)
-    assert np.array_equal(oracle.dequantize(codes, got, FMT_E8M0_B32),
-                          oracle.dequantize(codes, scales, FMT_E8M0_B32))
+    ts = None if fmt == FMT_E8M0_B32 else 3.0e-5
+    assert np.array_equal(oracle.dequantize(codes, got, fmt, ts), oracle.dequantize(codes, scales, fmt, ts))
 
 
 def test_prescale_plus_vector_order_along_k():
