@@ -34,6 +34,12 @@ FMT_VQ4_E8M0 = 2
 FMT_E5M3_B16 = 3
 FMT_VQ4_POST = 4
 FMT_VQ4_PLUS = 5
+FMT_VQ4_E4M3 = 6
+FMT_VQ4_E4M3_POST = 7
+FMT_VQ4_E4M3_PLUS = 8
+FMT_VQ4_E5M3 = 9
+FMT_VQ4_E5M3_POST = 10
+FMT_VQ4_E5M3_PLUS = 11
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
 TS_DYNAMIC = 1

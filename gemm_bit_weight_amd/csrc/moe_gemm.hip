@@ -736,10 +736,27 @@ __device__ __forceinline__ uint32_t e4m3_to_h2(uint32_t c) {
 // padding.  Same single-barrier pipeline as the FP4 kernel: stage s+1 is
 // decoded into LDS before the MFMAs of stage s.  E5 = true: E5M3-B16 operands,
 // decoded to bf16 and contracted with v_mfma_f32_32x32x16_bf16 (same layout).
-template <bool E5>
+//
+// WL: the weight codes.  W16_NIB: packed E2M1 nibbles with a scale per 16.
+// VQ ("MXCode: MX-Native Codebook Quantization", abstract; Table 2's E4M3-B16
+// columns): 8-bit indices into the QBlock's 256-entry table of four E2M1
+// codes, with the block scales per 16 along K (W16_VQ, PreScale), one per
+// QBlock table (W16_VQ_POST, PostScale) or 8 at a time coded against a
+// 256 x 8 table per expert (W16_VQ_PLUS, PreScale+).  A B-row thread expands
+// its 16 indices of a stage through the tables of its 64-row band (in LDS,
+// loaded one stage ahead) into the 32 code bytes the decode takes.  Every
+// thread issues the same loads each stage (A threads' table load and B
+// threads' second code load are spare), so the waits stay those of the
+// plain kernel.
+enum W16 { W16_NIB = 0, W16_VQ = 1, W16_VQ_POST = 2, W16_VQ_PLUS = 3 };
+
+template <bool E5, int WL>
 __global__ __launch_bounds__(kE4Threads) void k_moe_e4m3(const MoeArgs p) {
+  constexpr bool VQ = WL != W16_NIB;
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][kMoeBM * kRowH];
   __shared__ __attribute__((aligned(16))) uint8_t sB[2][kE4BN * kRowH];
+  __shared__ __attribute__((aligned(16))) uint16_t sLut[2][VQ ? 4 * 256 : 4];  // 4 bands of 64 B rows
+  __shared__ uint32_t sScb[WL == W16_VQ_PLUS ? 512 : 1];                      // PreScale+: 256 x 8 scale codes
   __shared__ int scan[kMoeThreads];
   __shared__ int s_tok[kMoeBM];
   __shared__ float s_w[kMoeBM];
@@ -767,44 +784,102 @@ __global__ __launch_bounds__(kE4Threads) void k_moe_e4m3(const MoeArgs p) {
     s_tok[r] = tok;
     s_w[r] = wt;
   }
+  if (WL == W16_VQ_PLUS) {
+    const uint32_t* scb = reinterpret_cast<const uint32_t*>(p.w_scb) + (int64_t)ti.e * 512;
+    for (int i = tid; i < 512; i += kE4Threads) sScb[i] = scb[i];
+  }
   __syncthreads();
 
   // thread tid stages one row: A row tid (tid < 256) or B row tid - 256
   const int row = tid & 255;
+  const bool is_b = VQ && __builtin_amdgcn_readfirstlane(tid >> 6) >= 4;  // (whole waves)
   const uint8_t* rc;
   const uint8_t* rs;
+  const uint16_t* cbase = nullptr;  // VQ: this thread's 8 bytes of its band's table, stage 0
   if (tid < 256) {
     const int rr = row < ti.rows ? row : ti.rows - 1;
     const int64_t src = p.stage == GBW_MOE_GATEUP_SWIGLU ? (int64_t)s_tok[rr] : (int64_t)(ti.row0 + rr);
     rc = p.a_codes + src * (K / 2);
     rs = p.a_scales + src * (K / 16);
   } else {
-    const int64_t wr = (int64_t)ti.e * p.N + b_row<kE4BN>(p, ti.nt, row);
-    rc = p.w_codes + wr * (K / 2);
-    rs = p.w_scales + wr * (K / 16);
+    const int64_t n = b_row<kE4BN>(p, ti.nt, row);
+    const int64_t wr = (int64_t)ti.e * p.N + n;
+    rc = p.w_codes + wr * (VQ ? K / 4 : K / 2);
+    if (WL == W16_VQ_POST)
+      rs = p.w_scales + ((int64_t)ti.e * (p.N >> p.qsh) + (n >> p.qsh)) * (K >> p.qsh);
+    else if (WL == W16_VQ_PLUS)
+      rs = p.w_scales + wr * (K / 128);
+    else
+      rs = p.w_scales + wr * (K / 16);
+  }
+  if (VQ) {
+    // table loads: B thread t - 256 fetches 8 bytes of band (t - 256) / 64;
+    // A threads fetch the same bytes (spare loads of valid memory)
+    const int band = (row >> 6), bl = row & 63;
+    const int64_t qrow = b_row<kE4BN>(p, ti.nt, band * 64) >> p.qsh;
+    cbase = p.w_cb + ((int64_t)ti.e * (p.N >> p.qsh) + qrow) * (K >> p.qsh) * 256 + bl * 4;
   }
   // LDS row of this thread in buffer 0; buffer 1 is kMoeBM * kRowH bytes further
   uint8_t* const dst0 = tid < 256 ? &sA[0][row * kRowH] : &sB[0][row * kRowH];
 
   v4i pc[2];
   uint32_t ps;
+  uint2 pl;
   const int last = steps - 1;
+  // table element offset of stage s (64 K per stage) within the band's QBlock row
+  auto lut_off = [&](int s) __attribute__((always_inline)) { return (uint32_t)(((s * 64) >> p.qsh) << 8); };
   auto gload = [&](int s) __attribute__((always_inline)) {
     s = s < last ? s : last;
-    pc[0] = load16(rc + (int64_t)s * 32);
-    pc[1] = load16(rc + (int64_t)s * 32 + 16);
-    ps = *reinterpret_cast<const uint32_t*>(rs + (int64_t)s * 4);
+    if (!VQ) {
+      pc[0] = load16(rc + (int64_t)s * 32);
+      pc[1] = load16(rc + (int64_t)s * 32 + 16);
+      ps = *reinterpret_cast<const uint32_t*>(rs + (int64_t)s * 4);
+    } else {
+      // A rows: 32 code bytes and 4 scale codes.  B rows: 16 indices (the
+      // second load repeats them) and the stage's scale codes (PostScale:
+      // the QBlock's code; PreScale+: the index of the 8-scale vector
+      // covering stages 2(s/2), 2(s/2)+1)
+      const int64_t c0 = is_b ? (int64_t)s * 16 : (int64_t)s * 32;
+      pc[0] = load16(rc + c0);
+      pc[1] = load16(rc + c0 + (is_b ? 0 : 16));
+      if (is_b && WL == W16_VQ_POST)
+        ps = rs[(s * 64) >> p.qsh];
+      else if (is_b && WL == W16_VQ_PLUS)
+        ps = rs[s >> 1];
+      else
+        ps = *reinterpret_cast<const uint32_t*>(rs + (int64_t)s * 4);
+      const int sl = s + 1 < last ? s + 1 : last;  // tables run one stage ahead
+      pl = *reinterpret_cast<const uint2*>(cbase + lut_off(sl));
+    }
   };
   auto lstore = [&](int k) __attribute__((always_inline)) {
     uint8_t* dst = dst0 + (k & 1) * (kMoeBM * kRowH);
+    uint32_t cw[8];  // the 32 code bytes of this row's stage
+    uint32_t sc = ps;  // its four block-scale codes
+#pragma unroll
+    for (int d = 0; d < 8; ++d) cw[d] = (uint32_t)pc[d >> 2][d & 3];
+    if (VQ && is_b) {
+      // store the next stage's table; expand this stage's 16 indices
+      const int kk = k < last ? k : last;
+      *reinterpret_cast<uint2*>(&sLut[(k + 1) & 1][(row >> 6) * 256 + (row & 63) * 4]) = pl;
+      const uint16_t* lut = &sLut[k & 1][(row >> 6) * 256];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w = (uint32_t)pc[0][q];
+        cw[2 * q] = (uint32_t)lut[w & 0xFF] | ((uint32_t)lut[(w >> 8) & 0xFF] << 16);
+        cw[2 * q + 1] = (uint32_t)lut[(w >> 16) & 0xFF] | ((uint32_t)lut[w >> 24] << 16);
+      }
+      if (WL == W16_VQ_POST) sc = (ps & 0xFFu) * 0x01010101u;
+      if (WL == W16_VQ_PLUS) sc = sScb[((ps & 0xFFu) << 1) | (uint32_t)(kk & 1)];
+    }
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       // dword d of the 32 code bytes holds elements 8d..8d+7, scale block d/2
       uint32_t o[4];
       if constexpr (E5)
-        e5m3_decode8((uint32_t)pc[d >> 2][d & 3], ue5m3_value((ps >> (8 * (d >> 1))) & 0xFFu), o);
+        e5m3_decode8(cw[d], ue5m3_value((sc >> (8 * (d >> 1))) & 0xFFu), o);
       else
-        e4m3_decode8((uint32_t)pc[d >> 2][d & 3], e4m3_to_h2(ps >> (8 * (d >> 1))), o);
+        e4m3_decode8(cw[d], e4m3_to_h2(sc >> (8 * (d >> 1))), o);
       *reinterpret_cast<v4i*>(dst + 16 * d) = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
     }
   };
@@ -821,6 +896,12 @@ __global__ __launch_bounds__(kE4Threads) void k_moe_e4m3(const MoeArgs p) {
                                                : 128 * wn + 32 * j;
   const int nband = band_count(ti.rows, wm);
 
+  if (VQ) {
+    // the tables of stage 0
+    const uint2 t0 = *reinterpret_cast<const uint2*>(cbase);
+    if (is_b) *reinterpret_cast<uint2*>(&sLut[0][(row >> 6) * 256 + (row & 63) * 4]) = t0;
+    __syncthreads();
+  }
   gload(0);
   lstore(0);
   gload(1);
@@ -893,15 +974,34 @@ __global__ __launch_bounds__(kE4Threads) void k_moe_e4m3(const MoeArgs p) {
   }
 }
 
+template <bool E5>
+static void launch_moe_b16(const MoeArgs& q, int wl, int grid, hipStream_t st) {
+  switch (wl) {
+    case W16_VQ: hipLaunchKernelGGL((k_moe_e4m3<E5, W16_VQ>), dim3((unsigned)grid), dim3(kE4Threads), 0, st, q); break;
+    case W16_VQ_POST:
+      hipLaunchKernelGGL((k_moe_e4m3<E5, W16_VQ_POST>), dim3((unsigned)grid), dim3(kE4Threads), 0, st, q);
+      break;
+    case W16_VQ_PLUS:
+      hipLaunchKernelGGL((k_moe_e4m3<E5, W16_VQ_PLUS>), dim3((unsigned)grid), dim3(kE4Threads), 0, st, q);
+      break;
+    default: hipLaunchKernelGGL((k_moe_e4m3<E5, W16_NIB>), dim3((unsigned)grid), dim3(kE4Threads), 0, st, q); break;
+  }
+}
+
 int launch_moe_bf16(const MoeArgs& p, const gbw_act* a, const gbw_weight* w, int grid, hipStream_t st) {
   MoeArgs q = p;
   q.a_ts = a->tensor_scale;
   q.w_ts = w->tensor_scale;
   q.ts_per = w->ts_per_expert;
-  if (w->fmt == GBW_FMT_E5M3_B16)
-    hipLaunchKernelGGL(k_moe_e4m3<true>, dim3((unsigned)grid), dim3(kE4Threads), 0, st, q);
+  const int f = w->fmt;
+  const int wl = (f == GBW_FMT_VQ4_E4M3 || f == GBW_FMT_VQ4_E5M3)             ? W16_VQ
+                 : (f == GBW_FMT_VQ4_E4M3_POST || f == GBW_FMT_VQ4_E5M3_POST) ? W16_VQ_POST
+                 : (f == GBW_FMT_VQ4_E4M3_PLUS || f == GBW_FMT_VQ4_E5M3_PLUS) ? W16_VQ_PLUS
+                                                                                : W16_NIB;
+  if (a->fmt == GBW_FMT_E5M3_B16)
+    launch_moe_b16<true>(q, wl, grid, st);
   else
-    hipLaunchKernelGGL(k_moe_e4m3<false>, dim3((unsigned)grid), dim3(kE4Threads), 0, st, q);
+    launch_moe_b16<false>(q, wl, grid, st);
   return check_launch("moe_grouped_gemm(e4m3/e5m3)");
 }
 
@@ -968,10 +1068,16 @@ extern "C" int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const in
                              (long long)K);
   if (K <= 0 || K % 128 || K > (int64_t(1) << 30))
     return fail(GBW_E_SHAPE, "moe_grouped_gemm: K must be a positive multiple of 128, at most 2^30");
-  const bool vq = w->fmt == GBW_FMT_VQ4_E8M0 || w->fmt == GBW_FMT_VQ4_POST || w->fmt == GBW_FMT_VQ4_PLUS;
-  const bool fp4 = (w->fmt == GBW_FMT_E8M0_B32 || vq) && a->fmt == GBW_FMT_E8M0_B32;
-  // E4M3-B16 or E5M3-B16 (tensor-scaled, decoded exactly to fp16 / bf16)
-  const bool e4m3 = (w->fmt == GBW_FMT_E4M3_B16 || w->fmt == GBW_FMT_E5M3_B16) && a->fmt == w->fmt;
+  const int wf = w->fmt;
+  const bool vq32 = wf == GBW_FMT_VQ4_E8M0 || wf == GBW_FMT_VQ4_POST || wf == GBW_FMT_VQ4_PLUS;
+  const bool vq16e4 = wf == GBW_FMT_VQ4_E4M3 || wf == GBW_FMT_VQ4_E4M3_POST || wf == GBW_FMT_VQ4_E4M3_PLUS;
+  const bool vq16e5 = wf == GBW_FMT_VQ4_E5M3 || wf == GBW_FMT_VQ4_E5M3_POST || wf == GBW_FMT_VQ4_E5M3_PLUS;
+  const bool vq = vq32 || vq16e4 || vq16e5;
+  const bool vq_plus = wf == GBW_FMT_VQ4_PLUS || wf == GBW_FMT_VQ4_E4M3_PLUS || wf == GBW_FMT_VQ4_E5M3_PLUS;
+  const bool fp4 = (wf == GBW_FMT_E8M0_B32 || vq32) && a->fmt == GBW_FMT_E8M0_B32;
+  // E4M3-B16 or E5M3-B16 (tensor-scaled, decoded exactly to fp16 / bf16), packed or VQ codes
+  const bool e4m3 = ((wf == GBW_FMT_E4M3_B16 || vq16e4) && a->fmt == GBW_FMT_E4M3_B16) ||
+                    ((wf == GBW_FMT_E5M3_B16 || vq16e5) && a->fmt == GBW_FMT_E5M3_B16);
   if (!fp4 && !e4m3) return fail(GBW_E_UNSUPPORTED, "moe_grouped_gemm: unsupported activation/weight formats");
   if (stage == GBW_MOE_GATEUP_SWIGLU) {
     if (N % 256) return fail(GBW_E_SHAPE, "moe_grouped_gemm: gate/up rows (2I) must be a multiple of 256");
@@ -995,10 +1101,11 @@ extern "C" int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const in
     if (!w->codebook) return fail(GBW_E_ARG, "moe_grouped_gemm: VQ needs a codebook");
     if (qb != 64 && qb != 128 && qb != 256) return fail(GBW_E_ARG, "moe_grouped_gemm: QBlock edge must be 64, 128 or 256");
     if (N % qb || K % qb) return fail(GBW_E_SHAPE, "moe_grouped_gemm: N and K must be multiples of the QBlock edge");
-    if (w->fmt != GBW_FMT_VQ4_E8M0 && K > kXsMaxK)
+    if ((wf == GBW_FMT_VQ4_POST || wf == GBW_FMT_VQ4_PLUS) && K > kXsMaxK)
       return fail(GBW_E_SHAPE, "moe_grouped_gemm: PostScale / PreScale+ weights need K <= %d", kXsMaxK);
-    if (w->fmt == GBW_FMT_VQ4_PLUS) {
-      if (K % 256) return fail(GBW_E_SHAPE, "moe_grouped_gemm: PreScale+ needs K %% 256 == 0 (8 scales per index)");
+    if (vq_plus) {
+      if (K % (vq32 ? 256 : 128))
+        return fail(GBW_E_SHAPE, "moe_grouped_gemm: PreScale+ needs K a multiple of 8 scale blocks");
       if (!w->scale_codebook) return fail(GBW_E_ARG, "moe_grouped_gemm: PreScale+ needs a scale codebook");
       if (reinterpret_cast<uintptr_t>(w->scale_codebook) & 3u)
         return fail(GBW_E_ALIGN, "moe_grouped_gemm: the scale codebook must be 4-byte aligned");
@@ -1038,7 +1145,7 @@ extern "C" int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const in
   p.w_codes = w->codes;
   p.w_scales = w->scales;
   p.w_cb = w->codebook;
-  p.w_scb = w->fmt == GBW_FMT_VQ4_PLUS ? w->scale_codebook : nullptr;
+  p.w_scb = vq_plus ? w->scale_codebook : nullptr;
   p.qsh = qb == 256 ? 8 : qb == 128 ? 7 : 6;
   p.N = N;
   p.h_bf16 = out->h_bf16;

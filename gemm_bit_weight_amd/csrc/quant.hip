@@ -272,6 +272,23 @@ __device__ __forceinline__ float decode_elem(int32_t fmt, const uint8_t* codes, 
                                              const uint16_t* codebook, const uint8_t* scb, int32_t qsh,
                                              const float* ts, int32_t ts_seg, int64_t N, int64_t K, int64_t n,
                                              int64_t k) {
+  if (fmt >= GBW_FMT_VQ4_E4M3 && fmt <= GBW_FMT_VQ4_E5M3_PLUS) {
+    // 16-element blocks: E4M3 (formats 6-8) or UE5M3 (9-11) scales, FP32 tensor scale
+    const int lay = (fmt - GBW_FMT_VQ4_E4M3) % 3;  // 0 PreScale, 1 PostScale, 2 PreScale+
+    const bool e5 = fmt >= GBW_FMT_VQ4_E5M3;
+    const uint32_t idx = codes[n * (K / 4) + k / 4];
+    const int64_t qblk = (n >> qsh) * (K >> qsh) + (k >> qsh);
+    const uint32_t c = (codebook[qblk * 256 + idx] >> (4 * (k & 3))) & 0xFu;
+    uint32_t sc;
+    if (lay == 1)
+      sc = scales[qblk];
+    else if (lay == 2)
+      sc = scb[(uint32_t)scales[n * (K / 128) + k / 128] * 8 + (k / 16) % 8];
+    else
+      sc = scales[n * (K / 16) + k / 16];
+    const float v = e2m1_value(c) * (e5 ? ue5m3_value(sc) : e4m3_value(sc));
+    return v * ts[n / (N / ts_seg)];
+  }
   if (fmt == GBW_FMT_VQ4_E8M0 || fmt == GBW_FMT_VQ4_POST || fmt == GBW_FMT_VQ4_PLUS) {
     const uint32_t idx = codes[n * (K / 4) + k / 4];
     const int64_t qblk = (n >> qsh) * (K >> qsh) + (k >> qsh);
@@ -440,23 +457,38 @@ extern "C" int mx_dequantize(const gbw_weight* w, int32_t expert, float* out, vo
     case GBW_FMT_VQ4_E8M0:
     case GBW_FMT_VQ4_POST:
     case GBW_FMT_VQ4_PLUS:
+    case GBW_FMT_VQ4_E4M3:
+    case GBW_FMT_VQ4_E4M3_POST:
+    case GBW_FMT_VQ4_E4M3_PLUS:
+    case GBW_FMT_VQ4_E5M3:
+    case GBW_FMT_VQ4_E5M3_POST:
+    case GBW_FMT_VQ4_E5M3_PLUS: {
       if (qb != 64 && qb != 128 && qb != 256) return fail(GBW_E_ARG, "mx_dequantize: QBlock edge must be 64, 128 or 256");
       if (K % qb || N % qb) return fail(GBW_E_SHAPE, "mx_dequantize: VQ needs N, K multiples of the QBlock edge");
       if (!w->codebook) return fail(GBW_E_ARG, "mx_dequantize: VQ needs a codebook");
+      const bool b16 = w->fmt >= GBW_FMT_VQ4_E4M3;
+      const int lay = b16 ? (w->fmt - GBW_FMT_VQ4_E4M3) % 3 : w->fmt == GBW_FMT_VQ4_POST ? 1 : w->fmt == GBW_FMT_VQ4_PLUS ? 2 : 0;
+      const int bs = b16 ? 16 : 32;
       cbytes = N * K / 4;
-      sbytes = w->fmt == GBW_FMT_VQ4_E8M0 ? N * K / 32 : w->fmt == GBW_FMT_VQ4_POST ? (N / qb) * (K / qb) : N * K / 256;
-      if (w->fmt == GBW_FMT_VQ4_PLUS && (K % 256 || !w->scale_codebook))
-        return fail(w->scale_codebook ? GBW_E_SHAPE : GBW_E_ARG, "mx_dequantize: PreScale+ needs K %% 256 == 0 and a scale codebook");
+      sbytes = lay == 0 ? N * K / bs : lay == 1 ? (N / qb) * (K / qb) : N * K / (8 * bs);
+      if (lay == 2 && (K % (8 * bs) || !w->scale_codebook))
+        return fail(w->scale_codebook ? GBW_E_SHAPE : GBW_E_ARG,
+                    "mx_dequantize: PreScale+ needs K a multiple of 8 scale blocks and a scale codebook");
+      if (b16 && (!w->tensor_scale || w->ts_per_expert < 1 || N % w->ts_per_expert))
+        return fail(GBW_E_ARG, "mx_dequantize: bad tensor scale");
       break;
+    }
     default:
       return fail(GBW_E_ARG, "mx_dequantize: bad format");
   }
   if (N == 0 || K == 0) return GBW_OK;
   int st = check_device();
   if (st) return st;
-  const bool vq = w->fmt == GBW_FMT_VQ4_E8M0 || w->fmt == GBW_FMT_VQ4_POST || w->fmt == GBW_FMT_VQ4_PLUS;
+  const bool vq = w->fmt == GBW_FMT_VQ4_E8M0 || w->fmt == GBW_FMT_VQ4_POST || w->fmt == GBW_FMT_VQ4_PLUS ||
+                  (w->fmt >= GBW_FMT_VQ4_E4M3 && w->fmt <= GBW_FMT_VQ4_E5M3_PLUS);
+  const bool plus = w->fmt == GBW_FMT_VQ4_PLUS || w->fmt == GBW_FMT_VQ4_E4M3_PLUS || w->fmt == GBW_FMT_VQ4_E5M3_PLUS;
   const uint16_t* cb = vq ? w->codebook + (int64_t)expert * (N / qb) * (K / qb) * 256 : nullptr;
-  const uint8_t* scb = w->fmt == GBW_FMT_VQ4_PLUS ? w->scale_codebook + (int64_t)expert * 2048 : nullptr;
+  const uint8_t* scb = plus ? w->scale_codebook + (int64_t)expert * 2048 : nullptr;
   const float* ts = w->tensor_scale ? w->tensor_scale + (int64_t)expert * w->ts_per_expert : nullptr;
   const int64_t n = N * K;
   hipLaunchKernelGGL(k_dequant, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, as_stream(stream), w->fmt,

@@ -38,6 +38,12 @@
  *                     K and each 8-vector is stored as an 8-bit index into a
  *                     256-entry table of 8 E8M0 codes per matrix (abstract;
  *                     Table 4 caption: Ks = 256, ds = 8).
+ *   GBW_FMT_VQ4_E4M3[_POST|_PLUS], GBW_FMT_VQ4_E5M3[_POST|_PLUS]: the same
+ *                     three VQ layouts with E4M3 (UE5M3) block scales per 16
+ *                     along K and FP32 tensor scales, as in E4M3-B16
+ *                     (E5M3-B16) (Table 2's E4M3-B16-FP4 columns, Table 4):
+ *                     PreScale scales [E][N][K/16], PostScale one per QBlock
+ *                     table, PreScale+ indices [E][N][K/128] (8 scales of 16).
  * E2M1 nibbles are packed two per byte, element 2i in bits 3:0, element 2i+1
  * in bits 7:4, bit 3 of a nibble is the sign.  A VQ key holds element i of its
  * 4-vector in bits 4i+3:4i.  All matrices are row-major; weights are [N][K]
@@ -70,6 +76,12 @@ extern "C" {
 #define GBW_FMT_E5M3_B16 3
 #define GBW_FMT_VQ4_POST 4
 #define GBW_FMT_VQ4_PLUS 5
+#define GBW_FMT_VQ4_E4M3 6
+#define GBW_FMT_VQ4_E4M3_POST 7
+#define GBW_FMT_VQ4_E4M3_PLUS 8
+#define GBW_FMT_VQ4_E5M3 9
+#define GBW_FMT_VQ4_E5M3_POST 10
+#define GBW_FMT_VQ4_E5M3_PLUS 11
 
 #define GBW_DTYPE_BF16 0
 #define GBW_DTYPE_F32 1
@@ -99,15 +111,17 @@ typedef struct gbw_weight {
   int32_t n_experts;         /* >= 1; expert e starts at e * (per-expert size)     */
   int64_t N, K;              /* per expert                                         */
   const uint8_t* codes;      /* E8M0/E4M3/E5M3: [E][N][K/2] nibbles; VQ*: [E][N][K/4] idx */
-  const uint8_t* scales;     /* E8M0, VQ4_E8M0: [E][N][K/32] E8M0; E4M3/E5M3: [E][N][K/16];
-                                VQ4_POST: [E][N/qb][K/qb] E8M0, one per QBlock table;
-                                VQ4_PLUS: [E][N][K/256] scale-vector indices         */
+  const uint8_t* scales;     /* E8M0, VQ4_E8M0: [E][N][K/32] E8M0; E4M3/E5M3, VQ4_E4M3,
+                                VQ4_E5M3: [E][N][K/16];
+                                *_POST: [E][N/qb][K/qb], one per QBlock table;
+                                VQ4_PLUS: [E][N][K/256], VQ4_E4M3_PLUS and
+                                VQ4_E5M3_PLUS: [E][N][K/128] scale-vector indices  */
   const uint16_t* codebook;  /* VQ*: [E][N/qb][K/qb][256] keys, else NULL           */
-  const float* tensor_scale; /* E4M3/E5M3 only: [E][ts_per_expert] fp32, else NULL  */
+  const float* tensor_scale; /* E4M3/E5M3 and their VQ forms: [E][ts_per_expert] fp32 */
   int32_t ts_per_expert;     /* E4M3/E5M3: rows split into this many equal segments,
                                 segment s scaled by tensor_scale[e][s] (1 or 2)     */
   int32_t qblock;            /* VQ*: QBlock edge qb (64, 128 or 256; 0 means 64)    */
-  const uint8_t* scale_codebook; /* VQ4_PLUS: [E][256][8] E8M0 codes, 4-byte
+  const uint8_t* scale_codebook; /* *_PLUS: [E][256][8] scale codes, 4-byte
                                 aligned: block scales 8i .. 8i+7 of row n of
                                 expert e are entry scales[e][n][i]; else NULL  */
 } gbw_weight;
@@ -234,11 +248,13 @@ int moe_route(const float* logits, int64_t T, int32_t E, int32_t topk, int32_t* 
  *    repeatable; GBW_DETERMINISTIC then fails with GBW_E_WORKSPACE).
  * Weights: E8M0-B32, VQ4-E8M0 / VQ4_POST / VQ4_PLUS (decoded to MXFP4 in
  * LDS, scaled MFMA; N and K multiples of the QBlock edge; VQ4_POST and
- * VQ4_PLUS need K <= 8192, VQ4_PLUS also K % 256 == 0),
+ * VQ4_PLUS need K <= 8192, VQ4_PLUS also K % 256 == 0), the VQ4_E4M3* and
+ * VQ4_E5M3* forms (expanded and decoded like E4M3-B16 / E5M3-B16; *_PLUS
+ * needs K % 128 == 0),
  * E4M3-B16 (decoded exactly to fp16, fp16 MFMA) or E5M3-B16 (decoded exactly
  * to bf16 -- the products reach 6 * 114688, past fp16's range -- bf16 MFMA).
- * The activation format must equal the weight format for E4M3-B16 and
- * E5M3-B16 weights and be E8M0-B32 otherwise.
+ * The activation format is E4M3-B16 for E4M3-B16 and VQ4_E4M3* weights,
+ * E5M3-B16 for E5M3-B16 and VQ4_E5M3* weights, E8M0-B32 otherwise.
  * ws: gbw_workspace_size(GBW_OP_MOE_GEMM, P, H, fp32_combine, 0) bytes
  * (down stage only; the gate/up stage takes none). */
 typedef struct gbw_moe_out {

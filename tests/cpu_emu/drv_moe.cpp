@@ -31,7 +31,7 @@ template <class T> T* buf(size_t n, std::mt19937& g) {
 }
 int main(int argc, char** argv) {
   const int T = atoi(argv[1]), H = atoi(argv[2]), I = atoi(argv[3]), E = atoi(argv[4]), k = atoi(argv[5]);
-  const int fmt = atoi(argv[6]);  // 0 MX, 2 VQ, 1 E4M3, 3 E5M3, 4 VQ PostScale, 5 VQ PreScale+
+  const int fmt = atoi(argv[6]);  // gbw.h GBW_FMT_* (0 .. 11)
   const int qb = argc > 9 ? atoi(argv[9]) : 64;   // VQ QBlock edge
   const int tail = argc > 8 ? atoi(argv[8]) : 0;  // E8M0 h: PRQuant tail copy, down over I + tail
   const int Ih = I + tail;                        // h code columns
@@ -57,25 +57,27 @@ int main(int argc, char** argv) {
   for (int e = 0; e < E; ++e) off[e + 1] += off[e];
   for (int p = 0; p < P; ++p) { ptok[p] = pairs[p].second / k; ppos[pairs[p].second] = p; }
   for (int i = 0; i < P; ++i) tw[i] = 1.0f / k;
-  const bool e4 = fmt == 1 || fmt == 3;  // tensor-scaled formats
+  const bool e4 = fmt == 1 || fmt == 3 || fmt >= 6;  // tensor-scaled formats
+  const int afmt = (fmt == 3 || fmt >= 9) ? 3 : e4 ? 1 : 0;  // activation format
   const int sdiv = e4 ? 16 : 32;
+  const int lay = fmt == 4 ? 1 : fmt == 5 ? 2 : fmt >= 6 ? (fmt - 6) % 3 : 0;  // VQ scales: block / QBlock / table
   // gate/up
   gbw_weight wg{}, wd{};
   wg.fmt = fmt; wg.n_experts = E; wg.N = 2 * I; wg.K = H;
   wd.fmt = fmt; wd.n_experts = E; wd.N = H; wd.K = Ih;
-  const bool vq = fmt == 2 || fmt == 4 || fmt == 5;
+  const bool vq = fmt == 2 || fmt == 4 || fmt == 5 || fmt >= 6;
   for (gbw_weight* w : {&wg, &wd}) {
     const size_t NK = (size_t)E * w->N * w->K;
     w->codes = vq ? buf<uint8_t>(NK / 4, g) : buf<uint8_t>(NK / 2, g);
-    const size_t nsc = fmt == 4 ? (size_t)E * (w->N / qb) * (w->K / qb) : fmt == 5 ? NK / 256 : NK / sdiv;
+    const size_t nsc = lay == 1 ? (size_t)E * (w->N / qb) * (w->K / qb) : lay == 2 ? NK / (8 * sdiv) : NK / sdiv;
     w->scales = buf<uint8_t>(nsc, g);
     if (vq) w->codebook = buf<uint16_t>((size_t)E * (w->N / qb) * (w->K / qb) * 256, g);
     if (vq) w->qblock = qb;
-    if (fmt == 5) w->scale_codebook = buf<uint8_t>((size_t)E * 2048, g);
+    if (lay == 2) w->scale_codebook = buf<uint8_t>((size_t)E * 2048, g);
     if (e4) { float* ts = (float*)malloc(E * 2 * 4); for (int i = 0; i < 2 * E; ++i) ts[i] = 1.f; w->tensor_scale = ts; w->ts_per_expert = w == &wg ? 2 : 1; }
   }
   float* ats = (float*)malloc(4); *ats = 1.f;
-  gbw_act ax{}; ax.fmt = e4 ? fmt : 0; ax.rows = T; ax.K = H;
+  gbw_act ax{}; ax.fmt = afmt; ax.rows = T; ax.K = H;
   ax.codes = buf<uint8_t>((size_t)T * H / 2, g); ax.scales = buf<uint8_t>((size_t)T * H / sdiv, g);
   ax.tensor_scale = e4 ? ats : nullptr;
   gbw_moe_out o{};
@@ -87,7 +89,7 @@ int main(int argc, char** argv) {
   int st = moe_grouped_gemm(0, T, k, off, ptok, ppos, tw, &ax, &wg, &o, 0, nullptr, 0, nullptr);
   printf("gateup status %d\n", st);
   // down: activation = h
-  gbw_act ah{}; ah.fmt = e4 ? fmt : 0; ah.rows = P; ah.K = Ih;
+  gbw_act ah{}; ah.fmt = afmt; ah.rows = P; ah.K = Ih;
   uint8_t* hcodes = e4 ? buf<uint8_t>((size_t)P * I / 2, g) : hc;
   uint8_t* hsc = e4 ? buf<uint8_t>((size_t)P * I / 16, g) : hs;
   ah.codes = hcodes; ah.scales = hsc; ah.tensor_scale = e4 ? ats : nullptr;

@@ -41,13 +41,13 @@ def banner(msg):
     print(f"[case] {msg}", flush=True)
 
 
-def vq_ref_block_scales(v, e, scales, K, qblock=64):
-    """The oracle's per-32 E8M0 block scales [N][K/32] of expert e of a
+def vq_ref_block_scales(v, e, scales, K, qblock=64, block=32):
+    """The oracle's block scale codes [N][K/block] of expert e of a
     synth.vq_weight dict, for its scale layout ``scales``."""
     import oracle
     sc = v["scales"][e].cpu().numpy()
     if scales == "prescale":
         return sc
     if scales == "postscale":
-        return oracle.postscale_block_scales(sc, K, qblock)
+        return oracle.postscale_block_scales(sc, K, qblock, block)
     return oracle.prescale_plus_block_scales(sc, v["scale_codebook"][e].cpu().numpy())

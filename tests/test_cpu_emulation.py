@@ -52,11 +52,14 @@ def test_moe_grouped_gemm_in_bounds(build_dir, fmt):
     assert "gateup status 0" in out and all(f"down mode {m} status 0" in out for m in range(3)), out
 
 
-@pytest.mark.parametrize("fmt,qblock", [(4, 64), (4, 128), (5, 64), (5, 256)],
-                         ids=["postscale-q64", "postscale-q128", "prescale_plus-q64", "prescale_plus-q256"])
+@pytest.mark.parametrize("fmt,qblock", [(4, 64), (4, 128), (5, 64), (5, 256), (6, 128), (7, 64), (8, 64), (11, 256)],
+                         ids=["postscale-q64", "postscale-q128", "prescale_plus-q64", "prescale_plus-q256",
+                              "e4m3-prescale-q128", "e4m3-postscale-q64", "e4m3-prescale_plus-q64",
+                              "e5m3-prescale_plus-q256"])
 def test_moe_vq_scale_layouts_in_bounds(build_dir, fmt, qblock):
-    """VQ weights with PostScale / PreScale+ scales and larger QBlocks:
-    gate/up (2I = 512 rows, K = 512) and down (K = I = 256), 4 experts."""
+    """VQ weights (E8M0-B32, E4M3-B16 and E5M3-B16 scales) with PreScale /
+    PostScale / PreScale+ scales and larger QBlocks: gate/up (2I = 512 rows,
+    K = 512) and down (K = I = 256), 4 experts."""
     exe = _build(build_dir, "moe_gemm.hip", "drv_moe.cpp", "emu_moe")
     out = _run(exe, 120, 512, 256, 4, 2, fmt, 0, 0, qblock)
     assert "gateup status 0" in out and all(f"down mode {m} status 0" in out for m in range(3)), out

@@ -250,6 +250,37 @@ def test_dequantize_vq_scale_layouts_bitexact(scales, qblock, N, K):
         assert np.array_equal(out.astype(np.float64), ref)
 
 
+_VQ16_FMT = {("e4m3", "prescale"): gbw.FMT_VQ4_E4M3, ("e4m3", "postscale"): gbw.FMT_VQ4_E4M3_POST,
+             ("e4m3", "prescale_plus"): gbw.FMT_VQ4_E4M3_PLUS, ("e5m3", "prescale"): gbw.FMT_VQ4_E5M3,
+             ("e5m3", "postscale"): gbw.FMT_VQ4_E5M3_POST, ("e5m3", "prescale_plus"): gbw.FMT_VQ4_E5M3_PLUS}
+
+
+@pytest.mark.parametrize("scale_fmt", ["e4m3", "e5m3"])
+@pytest.mark.parametrize("scales,qblock,N,K", [("prescale", 64, 128, 192), ("postscale", 128, 256, 384),
+                                               ("prescale_plus", 64, 128, 384), ("prescale_plus", 256, 256, 512)])
+def test_dequantize_vq_b16_bitexact(scale_fmt, scales, qblock, N, K):
+    """VQ codes with E4M3 / UE5M3 block scales per 16 (PreScale, PostScale,
+    PreScale+) and two tensor-scale row segments: the device decode equals
+    the oracle's, expert by expert."""
+    banner(f"dequantize vq {scale_fmt} {scales} qblock={qblock} N={N} K={K}")
+    E = 2
+    v = synth.vq_weight(E, N, K, qblock=qblock, seed=6, device="cpu", scales=scales, scale_fmt=scale_fmt,
+                        ts_segments=2)
+    W = gbw.Weight(_VQ16_FMT[(scale_fmt, scales)], N, K, v["idx"].to(DEV), v["scales"].to(DEV),
+                   v["codebook"].to(DEV), v["tensor_scale"].to(DEV), 2, E, qblock=qblock,
+                   scale_codebook=v["scale_codebook"].to(DEV) if "scale_codebook" in v else None)
+    cb = v["codebook"].numpy().view(np.uint16)
+    ofmt = "e4m3_b16" if scale_fmt == "e4m3" else "e5m3_b16"
+    for e in range(E):
+        out = to_np(gbw.mx_dequantize(W, expert=e))
+        codes = oracle.vq_decode_codes(v["idx"][e].numpy(), cb[e], qblock)
+        sc = vq_ref_block_scales(v, e, scales, K, qblock, 16)
+        ts = v["tensor_scale"][e].numpy()
+        ref = np.concatenate([oracle.dequantize(codes[:N // 2], sc[:N // 2], ofmt, ts[0]),
+                              oracle.dequantize(codes[N // 2:], sc[N // 2:], ofmt, ts[1])])
+        assert np.array_equal(out.astype(np.float64), ref.astype(np.float32).astype(np.float64))
+
+
 # ---------------------------------------------------------------------------
 # MXFP4 GEMM
 # ---------------------------------------------------------------------------

@@ -123,33 +123,45 @@ class _Problem:
     """One MoE FFN problem: synthetic inputs, the oracle's view of them, and
     the GPU weight descriptors built from the same inputs."""
 
-    # VQ weights by scale layout (MXCode PreScale, PostScale, PreScale+)
-    VQ = {"vq": ("prescale", gbw.FMT_VQ4_E8M0), "vq_post": ("postscale", gbw.FMT_VQ4_POST),
-          "vq_plus": ("prescale_plus", gbw.FMT_VQ4_PLUS)}
+    # VQ weights by scale layout (MXCode PreScale, PostScale, PreScale+) and
+    # scale format: (layout, library format, the oracle's format name)
+    VQ = {"vq": ("prescale", gbw.FMT_VQ4_E8M0, "e8m0_b32"), "vq_post": ("postscale", gbw.FMT_VQ4_POST, "e8m0_b32"),
+          "vq_plus": ("prescale_plus", gbw.FMT_VQ4_PLUS, "e8m0_b32"),
+          "vq_e4m3": ("prescale", gbw.FMT_VQ4_E4M3, "e4m3_b16"),
+          "vq_e4m3_post": ("postscale", gbw.FMT_VQ4_E4M3_POST, "e4m3_b16"),
+          "vq_e4m3_plus": ("prescale_plus", gbw.FMT_VQ4_E4M3_PLUS, "e4m3_b16"),
+          "vq_e5m3": ("prescale", gbw.FMT_VQ4_E5M3, "e5m3_b16"),
+          "vq_e5m3_post": ("postscale", gbw.FMT_VQ4_E5M3_POST, "e5m3_b16"),
+          "vq_e5m3_plus": ("prescale_plus", gbw.FMT_VQ4_E5M3_PLUS, "e5m3_b16")}
 
     def __init__(self, fmt, x, logits, topk, gate_up, down, I, qblock=64):
         self.fmt, self.x, self.logits, self.topk, self.I = fmt, x, logits, topk, I
+        self.ofmt = self.VQ[fmt][2] if fmt in self.VQ else fmt   # the activation / oracle format
         T, H = x.shape
         self.T, self.H = T, H
         E = (gate_up["w"] if fmt not in self.VQ else gate_up["idx"]).shape[0]
         self.E = E
         if fmt in self.VQ:
-            mode, gfmt = self.VQ[fmt]
+            mode, gfmt, ofmt = self.VQ[fmt]
+            b16 = ofmt != "e8m0_b32"
+            bs = 16 if b16 else 32
 
-            def weight(v, N, K):
+            def weight(v, N, K, nts):
                 return gbw.Weight(gfmt, N, K, v["idx"].to(DEV), v["scales"].to(DEV), v["codebook"].to(DEV),
-                                  n_experts=E, qblock=qblock,
+                                  v["tensor_scale"].to(DEV) if b16 else None, nts, E, qblock=qblock,
                                   scale_codebook=v["scale_codebook"].to(DEV) if "scale_codebook" in v else None)
-            self.Wgu = weight(gate_up, 2 * I, H)
-            self.Wd = weight(down, H, I)
+            self.Wgu = weight(gate_up, 2 * I, H, 2)
+            self.Wd = weight(down, H, I, 1)
             gcpu = {k: v.cpu() for k, v in gate_up.items()}
             dcpu = {k: v.cpu() for k, v in down.items()}
             self.ref_gu = (_LazyExperts((E, 2 * I, H // 2), lambda e: oracle.vq_decode_codes(
                 gcpu["idx"][e].numpy(), gcpu["codebook"][e].numpy().view(np.uint16), qblock)),
-                _LazyExperts((E, 2 * I, H // 32), lambda e: vq_ref_block_scales(gcpu, e, mode, H, qblock)), None)
+                _LazyExperts((E, 2 * I, H // bs), lambda e: vq_ref_block_scales(gcpu, e, mode, H, qblock, bs)),
+                _LazyExperts((E, 2), lambda e: list(gcpu["tensor_scale"][e].numpy())) if b16 else None)
             self.ref_d = (_LazyExperts((E, H, I // 2), lambda e: oracle.vq_decode_codes(
                 dcpu["idx"][e].numpy(), dcpu["codebook"][e].numpy().view(np.uint16), qblock)),
-                _LazyExperts((E, H, I // 32), lambda e: vq_ref_block_scales(dcpu, e, mode, I, qblock)), None)
+                _LazyExperts((E, H, I // bs), lambda e: vq_ref_block_scales(dcpu, e, mode, I, qblock, bs)),
+                _LazyExperts((E,), lambda e: dcpu["tensor_scale"][e].numpy()[0]) if b16 else None)
             return
         wgu, wd = gate_up["w"], down["w"]          # fp32 [E][2I][H], [E][H][I] (on the GPU)
         if fmt == "e8m0_b32":
@@ -232,7 +244,7 @@ def _run_and_check(pb, tokens=None, experts=None, h_amax=None):
     h only for the sampled pairs.
     """
     T, H, I, topk = pb.T, pb.H, pb.I, pb.topk
-    fmt = "e8m0_b32" if pb.fmt in _Problem.VQ else pb.fmt
+    fmt = pb.ofmt
     e4 = fmt in ("e4m3_b16", "e5m3_b16")          # tensor-scaled formats: h quantized by mx_quantize
     e5 = fmt == "e5m3_b16"
     afmt = (gbw.FMT_E5M3_B16 if e5 else gbw.FMT_E4M3_B16) if e4 else gbw.FMT_E8M0_B32
@@ -391,6 +403,34 @@ def test_moe_vq_scale_layouts_full_size_sampled(fmt):
     d = synth.moe_vq_problem(8192, 4096, 1536, 128, seed=0, device=DEV, scales=mode)
     _run_and_check(_Problem(fmt, d["x"], d["logits"], 8, d["gate_up"], d["down"], 1536),
                    tokens=[0, 2049, 4097, 8191], experts=[0, 77, 127])
+
+
+@pytest.mark.parametrize("fmt,qblock,T,H,I,E,k", [("vq_e4m3", 64, 300, 512, 256, 8, 2),
+                                                  ("vq_e4m3_post", 64, 300, 512, 256, 8, 2),
+                                                  ("vq_e4m3_plus", 128, 200, 768, 384, 6, 3),
+                                                  ("vq_e5m3", 128, 260, 512, 256, 5, 2),
+                                                  ("vq_e5m3_post", 256, 150, 1024, 512, 4, 2),
+                                                  ("vq_e5m3_plus", 64, 300, 512, 256, 8, 2)])
+def test_moe_vq_b16_small(fmt, qblock, T, H, I, E, k):
+    """VQ experts with 16-element E4M3 / UE5M3 block scales (PreScale,
+    PostScale, PreScale+) on the fp16 / bf16 MFMA kernel."""
+    banner(f"moe {fmt} qblock={qblock} T={T} H={H} I={I} E={E} k={k}")
+    mode = _Problem.VQ[fmt][0]
+    sf = "e4m3" if "e4m3" in fmt else "e5m3"
+    d = synth.moe_vq_problem(T, H, I, E, seed=4, device="cpu", scales=mode, qblock=qblock, scale_fmt=sf)
+    _run_and_check(_Problem(fmt, d["x"].to(DEV), d["logits"].to(DEV), k, d["gate_up"], d["down"], I, qblock))
+
+
+@pytest.mark.parametrize("fmt", ["vq_e4m3_post", "vq_e4m3_plus"])
+def test_moe_vq_b16_e4m3_shape_sampled(fmt):
+    """The E4M3-B16 MoE shape (4096 tokens, H 2048, I 768, 128 experts,
+    top-8) with VQ weights; every pair of three experts, sampled tokens (h is
+    quantized with a static tensor scale on both sides)."""
+    banner(f"moe {fmt} T=4096 H=2048 I=768 E=128 k=8")
+    mode = _Problem.VQ[fmt][0]
+    d = synth.moe_vq_problem(4096, 2048, 768, 128, seed=0, device=DEV, scales=mode, scale_fmt="e4m3")
+    _run_and_check(_Problem(fmt, d["x"], d["logits"], 8, d["gate_up"], d["down"], 768),
+                   tokens=[0, 1, 2049, 4095], experts=[0, 64, 127], h_amax=4.0)
 
 
 def test_moe_vq_full_size_sampled():
