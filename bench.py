@@ -398,6 +398,50 @@ def moe_e4m3(gbw, synth, torch, steps=5, fmt=None):
             "frac_mxfp4_mfma": flops / ms / 1e9 / MXFP4_PEAK_TFLOPS}
 
 
+def moe_vq_b16(gbw, synth, torch, steps=5):
+    """The E4M3-B16 MoE workload with VQ weights (MXCode PreScale, PostScale,
+    PreScale+ with E4M3 block scales per 16): activations E4M3-B16 online."""
+    T, H, I, E, K = 4096, 2048, 768, 128, 8
+    fmts = {"prescale": gbw.FMT_VQ4_E4M3, "postscale": gbw.FMT_VQ4_E4M3_POST,
+            "prescale_plus": gbw.FMT_VQ4_E4M3_PLUS}
+    out = {"T": T, "hidden": H, "intermediate": I, "experts": E, "topk": K}
+    for scales, fmt in fmts.items():
+        d = synth.moe_vq_problem(T, H, I, E, seed=0, device="cuda", scales=scales, scale_fmt="e4m3")
+
+        def weight(v, N, Kd, nts):
+            return gbw.Weight(fmt, N, Kd, v["idx"], v["scales"], v["codebook"], v["tensor_scale"], nts, E,
+                              scale_codebook=v.get("scale_codebook"))
+        Wgu, Wd = weight(d["gate_up"], 2 * I, H, 2), weight(d["down"], H, I, 1)
+        P = T * K
+        hb = torch.empty((P, I), dtype=torch.bfloat16, device="cuda")
+        y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+
+        def step():
+            route = gbw.moe_route(d["logits"], K)
+            xq = gbw.mx_quantize(d["x"], gbw.FMT_E4M3_B16)
+            gbw.moe_grouped_gemm(gbw.MOE_GATEUP_SWIGLU, route, xq, Wgu, h_bf16=hb)
+            hq = gbw.mx_quantize(hb, gbw.FMT_E4M3_B16)
+            gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, Wd, y=y)
+        step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        flops = 2.0 * P * 3 * H * I
+        wbytes = sum(t.numel() * t.element_size() for w in (Wgu, Wd)
+                     for t in (w.codes, w.scales, w.codebook, w.scale_codebook) if t is not None)
+        out[scales] = {"ms_per_step": ms, "TFLOP_s": flops / ms / 1e9,
+                       "frac_f16_mfma": flops / ms / 1e9 / F16_PEAK_TFLOPS,
+                       "bits_per_weight": 8.0 * wbytes / (3 * E * H * I)}
+        del d, Wgu, Wd
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -464,7 +508,8 @@ def main():
                         "mx_gemm_16x512x512": dense_small(gbw, synth, torch),
                         "quantize_e8m0_8192x4096": quantize_rate(gbw, synth, torch),
                         "moe_mxfp4_prquant_down": moe_mxfp4_prquant(gbw, synth, torch),
-                        "moe_vq_scale_layouts": moe_vq_scale_layouts(gbw, synth, torch)}
+                        "moe_vq_scale_layouts": moe_vq_scale_layouts(gbw, synth, torch),
+                        "moe_vq_e4m3_b16": moe_vq_b16(gbw, synth, torch)}
     print(json.dumps(out), flush=True)
 
 
