@@ -1084,17 +1084,18 @@ extern "C" int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const in
     if (e4m3 && w->ts_per_expert != 2)
       return fail(GBW_E_ARG, "moe_grouped_gemm: E4M3/E5M3 gate/up needs two tensor scales per expert (gate, up)");
     if (a->rows < T) return fail(GBW_E_SHAPE, "moe_grouped_gemm: activation has fewer rows than tokens");
-    if (fp4 && (!out->h_codes || !out->h_scales) && !out->h_bf16)
+    // (with T = 0 nothing is written, and the outputs may be NULL)
+    if (T > 0 && fp4 && (!out->h_codes || !out->h_scales) && !out->h_bf16)
       return fail(GBW_E_ARG, "moe_grouped_gemm: gate/up needs h_codes+h_scales or h_bf16");
     if (fp4 && (!out->h_codes) != (!out->h_scales))
       return fail(GBW_E_ARG, "moe_grouped_gemm: h_codes and h_scales go together");
-    if (e4m3 && !out->h_bf16) return fail(GBW_E_ARG, "moe_grouped_gemm: E4M3/E5M3 gate/up writes h_bf16");
+    if (T > 0 && e4m3 && !out->h_bf16) return fail(GBW_E_ARG, "moe_grouped_gemm: E4M3/E5M3 gate/up writes h_bf16");
     if (out->h_tail < 0 || out->h_tail % 32 || out->h_tail > N / 2 || (out->h_tail && (e4m3 || !out->h_codes)))
       return fail(GBW_E_SHAPE, "moe_grouped_gemm: h_tail must be a multiple of 32, <= I, with E8M0 h codes");
   } else {
     if (N % 256) return fail(GBW_E_SHAPE, "moe_grouped_gemm: down rows (H) must be a multiple of 256");
     if (a->rows < P) return fail(GBW_E_SHAPE, "moe_grouped_gemm: activation has fewer rows than pairs");
-    if (!out->y) return fail(GBW_E_ARG, "moe_grouped_gemm: down needs y");
+    if (T > 0 && !out->y) return fail(GBW_E_ARG, "moe_grouped_gemm: down needs y");
   }
   const int qb = vq && w->qblock ? w->qblock : 64;
   if (vq) {

@@ -98,6 +98,39 @@ def test_gemm_validation(gbw):
                                 ctypes.c_void_p(0x5000), 0, None, 0, None) == 2
 
 
+def test_moe_validation(gbw):
+    """moe_grouped_gemm: format pairs, QBlock edges and the scale-table
+    requirements are checked on the host; T = 0 is a no-op (NULL outputs
+    allowed) that never touches the device."""
+    L = gbw._lib
+    off = ctypes.c_void_p(0x1000)
+    ptr = ctypes.c_void_p(0x2000)
+
+    def call(stage, T, a, w, out):
+        return L.moe_grouped_gemm(stage, T, 2, off, ptr, ptr, ptr, ctypes.byref(a), ctypes.byref(w),
+                                  ctypes.byref(out), 0, None, 0, None)
+    H, I, E = 256, 128, 4
+    a = gbw._Act(0, 8, H, 0x3000, 0x4000, None)
+    out = gbw._MoeOut(None, None, None, None, 0)
+    w = gbw._Weight(gbw.FMT_VQ4_E8M0, E, 2 * I, H, 0x5000, 0x6000, 0x7000, None, 1, 0, None)
+    assert call(0, 0, a, w, out) == 0                              # no tokens, no outputs: OK
+    assert call(0, 4, a, w, out) == 1                              # tokens but no h buffers
+    w.qblock = 96
+    assert call(0, 0, a, w, out) == 1                              # QBlock edge not 64/128/256
+    w.qblock = 256
+    assert call(0, 0, a, w, out) == 0                              # N = 256, K = 256: fine
+    w = gbw._Weight(gbw.FMT_VQ4_PLUS, E, 2 * I, H, 0x5000, 0x6000, 0x7000, None, 1, 0, None)
+    assert call(0, 0, a, w, out) == 1                              # PreScale+ without a scale table
+    w.scale_codebook = 0x8001
+    assert call(0, 0, a, w, out) == 3                              # scale table not 4-byte aligned
+    w = gbw._Weight(gbw.FMT_VQ4_E4M3, E, 2 * I, H, 0x5000, 0x6000, 0x7000, 0x9000, 2, 0, None)
+    assert call(0, 0, a, w, out) == 4                              # E4M3 VQ weights need E4M3 activations
+    a16 = gbw._Act(gbw.FMT_E4M3_B16, 8, H, 0x3000, 0x4000, 0xA000)
+    assert call(0, 0, a16, w, out) == 0
+    a16.fmt = gbw.FMT_E5M3_B16
+    assert call(0, 0, a16, w, out) == 4                            # scale formats must agree
+
+
 def test_descriptor_layouts_match_the_header(gbw, tmp_path):
     """The ctypes descriptors have the C structs' field offsets and sizes
     (compiled from include/gbw.h by the host C compiler)."""

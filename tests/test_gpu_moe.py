@@ -433,6 +433,45 @@ def test_moe_vq_b16_e4m3_shape_sampled(fmt):
                    tokens=[0, 1, 2049, 4095], experts=[0, 64, 127], h_amax=4.0)
 
 
+@pytest.mark.parametrize("fmt", ["e8m0_b32", "e4m3_b16", "vq", "vq_e5m3_plus"])
+@pytest.mark.parametrize("T,E,k", [(1, 4, 1), (3, 64, 2), (5, 1, 1), (40, 200, 3)])
+def test_moe_edge_shapes(fmt, T, E, k):
+    """One token, one expert, top-1, and most experts without a pair (every
+    kernel then walks tiles of empty and one-row experts)."""
+    banner(f"moe edge {fmt} T={T} E={E} k={k}")
+    H, I = 256, 128
+    if fmt.startswith("vq"):
+        mode = _Problem.VQ[fmt][0]
+        sf = "e8m0" if fmt == "vq" else "e5m3"
+        d = synth.moe_vq_problem(T, H, I, E, seed=5, device="cpu", scales=mode, scale_fmt=sf)
+        pb = _Problem(fmt, d["x"].to(DEV), d["logits"].to(DEV), k, d["gate_up"], d["down"], I)
+    else:
+        d = synth.moe_problem(T, H, I, E, seed=5, device=DEV)
+        pb = _Problem(fmt, d["x"], d["logits"], k, dict(w=d["w_gate_up"]), dict(w=d["w_down"]), I)
+    _run_and_check(pb)
+
+
+def test_moe_no_tokens():
+    """T = 0: routing zeroes the expert offsets, both GEMM stages return OK
+    and write nothing."""
+    banner("moe T=0")
+    E, H, I = 8, 256, 128
+    logits = torch.empty((0, E), dtype=torch.float32, device=DEV)
+    route = gbw.moe_route(logits, 2)
+    torch.cuda.synchronize()
+    assert to_np(route["expert_offsets"]).tolist() == [0] * (E + 1)
+    d = synth.moe_problem(1, H, I, E, seed=6, device=DEV)
+    pb = _Problem("e8m0_b32", d["x"], d["logits"], 2, dict(w=d["w_gate_up"]), dict(w=d["w_down"]), I)
+    xq = gbw.Act(gbw.FMT_E8M0_B32, torch.empty((0, H // 2), dtype=torch.uint8, device=DEV),
+                 torch.empty((0, H // 32), dtype=torch.uint8, device=DEV))
+    hc = torch.empty((0, I // 2), dtype=torch.uint8, device=DEV)
+    hs = torch.empty((0, I // 32), dtype=torch.uint8, device=DEV)
+    gbw.moe_grouped_gemm(gbw.MOE_GATEUP_SWIGLU, route, xq, pb.Wgu, h_codes=hc, h_scales=hs)
+    y = torch.full((0, H), 7.0, dtype=torch.float32, device=DEV)
+    gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, gbw.Act(gbw.FMT_E8M0_B32, hc, hs), pb.Wd, y=y)
+    torch.cuda.synchronize()
+
+
 def test_moe_vq_full_size_sampled():
     """The measured prefill shape: T=8192, H=4096, I=1536, 128 experts,
     top-8; gate/up checked on every pair of two experts, y on sampled tokens."""
