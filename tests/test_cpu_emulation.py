@@ -48,7 +48,7 @@ def _run(exe, *args, timeout=300):
 @pytest.mark.parametrize("fmt", [0, 2, 1, 3], ids=["mxfp4", "vq", "e4m3", "e5m3"])
 def test_moe_grouped_gemm_in_bounds(build_dir, fmt):
     exe = _build(build_dir, "moe_gemm.hip", "drv_moe.cpp", "emu_moe")
-    out = _run(exe, 300, 512, 256, 8, 2, fmt)
+    out = _run(exe, 200, 512, 256, 6, 2, fmt)
     assert "gateup status 0" in out and all(f"down mode {m} status 0" in out for m in range(3)), out
 
 
@@ -59,9 +59,9 @@ def test_moe_grouped_gemm_in_bounds(build_dir, fmt):
 def test_moe_vq_scale_layouts_in_bounds(build_dir, fmt, qblock):
     """VQ weights (E8M0-B32, E4M3-B16 and E5M3-B16 scales) with PreScale /
     PostScale / PreScale+ scales and larger QBlocks: gate/up (2I = 512 rows,
-    K = 512) and down (K = I = 256), 4 experts."""
+    K = 512) and down (K = I = 256), 3 experts."""
     exe = _build(build_dir, "moe_gemm.hip", "drv_moe.cpp", "emu_moe")
-    out = _run(exe, 120, 512, 256, 4, 2, fmt, 0, 0, qblock)
+    out = _run(exe, 90, 512, 256, 3, 2, fmt, 0, 0, qblock)
     assert "gateup status 0" in out and all(f"down mode {m} status 0" in out for m in range(3)), out
 
 
@@ -69,7 +69,7 @@ def test_moe_prquant_tail_copy_in_bounds(build_dir):
     """MXFP4 gate/up writing h with a 128-column tail copy (I + 128 code
     columns), then the down stage over I + 128."""
     exe = _build(build_dir, "moe_gemm.hip", "drv_moe.cpp", "emu_moe")
-    out = _run(exe, 300, 512, 256, 8, 2, 0, 1, 128)
+    out = _run(exe, 200, 512, 256, 6, 2, 0, 1, 128)
     assert "gateup status 0" in out and all(f"down mode {m} status 0" in out for m in range(3)), out
 
 
