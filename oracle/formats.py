@@ -18,7 +18,7 @@ Packing (the pages are silent; this is the reading used everywhere here):
 byte i of a row holds element 2i in bits 3:0 and element 2i+1 in bits 7:4;
 bit 3 of a nibble is the sign.
 
-Readings taken where the pages leave a step open (all listed in the design doc):
+Readings taken where the pages leave a step open:
   * E8M0 scale rule: the OCP floor rule, scale exponent = floor(log2 amax)
     - 2 (2 = emax of E2M1), written as the biased code max(0, E(amax) - 2)
     where E(.) is the fp32 biased exponent field; a zero or subnormal block

@@ -6,7 +6,7 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
 The FFN form is the gated MLP of PRQuant §4 Eq. (1):
 MLP(X) = (X W_up^T * sigma(X W_gate^T)) W_down^T, applied per routed expert
 (CodeQuant Fig. 1 / Fig. 2 place the quantized weights in the MoE FFN
-experts).  Readings taken here (listed in the design doc):
+experts).  Readings taken here, where the pages leave a step open:
   * routing selects the top-k logits of a token, ties to the lower expert id,
     and weights the k chosen experts by a softmax renormalised over them;
   * the gated activation is silu(g) * u (sigma(z) * z with the logistic
