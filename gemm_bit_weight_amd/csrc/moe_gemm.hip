@@ -823,10 +823,12 @@ __global__ __launch_bounds__(kE4Threads) void k_moe_e4m3(const MoeArgs p) {
   }
   // LDS row of this thread in buffer 0; buffer 1 is kMoeBM * kRowH bytes further
   uint8_t* const dst0 = tid < 256 ? &sA[0][row * kRowH] : &sB[0][row * kRowH];
-  // A rows past the tile's pairs are neither loaded nor decoded: their LDS
-  // rows feed only output rows that are never stored (3 % of the E4M3-B16
-  // gate/up time, spent in the last, partly filled tile of each expert)
-  const bool a_live = tid >= 256 || row < ti.rows;
+  // packed codes: A rows past the tile's pairs are neither loaded nor
+  // decoded, their LDS rows feed only output rows that are never stored (3 %
+  // of the E4M3-B16 gate/up time, spent in the last, partly filled tile of
+  // each expert; with VQ weights the same branch costs 8-10 %, so those keep
+  // every row)
+  const bool a_live = VQ || tid >= 256 || row < ti.rows;
 
   v4i pc[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
   uint32_t ps;
