@@ -228,36 +228,44 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_e4m3(const T* __restric
   } else {
     S_T = tensor_scale[0];
   }
-  const int64_t g = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+  // kQ8Units 8-element units per thread, as in the E8M0 quantizer (the
+  // tensor-amax reduction above is paid once per 1024 units)
   const int64_t total = rows * (K / 8);
-  const bool live = g < total;
-  const int64_t gg = live ? g : total - 1;
-  int64_t row, col;
-  unit_pos<WIDE>(gg, K, row, col);
-  float v[8];
-  In8<T>::load(x + row * K + col, v);
-  uint32_t am = 0;
+  const int64_t g0 = (int64_t)blockIdx.x * (kQuantThreads * kQ8Units) + threadIdx.x;
+  float v[kQ8Units][8];
+  int64_t row[kQ8Units], col[kQ8Units];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) am = max(am, abs_bits(v[i]));
-  am = group_max<2>(am);
+  for (int u = 0; u < kQ8Units; ++u) {
+    const int64_t g = g0 + (int64_t)u * kQuantThreads;
+    const int64_t gg = g < total ? g : total - 1;  // keep the whole wave in the shuffles
+    unit_pos<WIDE>(gg, K, row[u], col[u]);
+    In8<T>::load(x + row[u] * K + col[u], v[u]);
+  }
   const float d = 6.0f * S_T;
-  const float s = __uint_as_float(am) / d;
-  const uint32_t sc = E5 ? ue5m3_rne_sat(s) : e4m3_rne_sat(s);
-  const float den = (E5 ? ue5m3_value(sc) : e4m3_value(sc)) * S_T;
-  // element = RNE onto E2M1 of the fp32 quotient x / den (sign kept; a block
-  // whose scale decodes to 0 encodes signed zeros): the division in fp32,
-  // then v_cvt_scalef32_pk_fp4_f32 at scale 1 for the rounding
-  float q[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = den > 0.0f ? v[i] / den : v[i] * 0.0f;
-  uint32_t word = 0;
-  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q[0], q[1], 1.0f, 0);
-  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q[2], q[3], 1.0f, 1);
-  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q[4], q[5], 1.0f, 2);
-  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q[6], q[7], 1.0f, 3);
-  if (!live) return;
-  *reinterpret_cast<uint32_t*>(codes + row * (K / 2) + col / 2) = word;
-  if ((threadIdx.x & 1) == 0) scales[row * (K / 16) + col / 16] = (uint8_t)sc;
+  for (int u = 0; u < kQ8Units; ++u) {
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = max(am, abs_bits(v[u][i]));
+    am = group_max<2>(am);
+    const float s = __uint_as_float(am) / d;
+    const uint32_t sc = E5 ? ue5m3_rne_sat(s) : e4m3_rne_sat(s);
+    const float den = (E5 ? ue5m3_value(sc) : e4m3_value(sc)) * S_T;
+    // element = RNE onto E2M1 of the fp32 quotient x / den (sign kept; a block
+    // whose scale decodes to 0 encodes signed zeros): the division in fp32,
+    // then v_cvt_scalef32_pk_fp4_f32 at scale 1 for the rounding
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = den > 0.0f ? v[u][i] / den : v[u][i] * 0.0f;
+    uint32_t word = 0;
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q[0], q[1], 1.0f, 0);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q[2], q[3], 1.0f, 1);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q[4], q[5], 1.0f, 2);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q[6], q[7], 1.0f, 3);
+    if (g0 + (int64_t)u * kQuantThreads >= total) continue;
+    *reinterpret_cast<uint32_t*>(codes + row[u] * (K / 2) + col[u] / 2) = word;
+    if ((threadIdx.x & 1) == 0) scales[row[u] * (K / 16) + col[u] / 16] = (uint8_t)sc;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -378,7 +386,6 @@ extern "C" int mx_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t
   if (st) return st;
   hipStream_t s = as_stream(stream);
   const int64_t total = rows * (K / 8);
-  const unsigned blocks = (unsigned)cdiv(total > 0 ? total : 1, kQuantThreads);
   const unsigned blocks8 = (unsigned)cdiv(total > 0 ? total : 1, kQuantThreads * kQ8Units);
   const bool bf = x_dtype == GBW_DTYPE_BF16;
   const bool wide = total > (int64_t)UINT32_MAX;
@@ -413,7 +420,7 @@ extern "C" int mx_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t
     if ((st = check_launch("mx_quantize(amax)"))) return st;
   }
 #define GBW_Q4(T, W, E5)                                                                                          \
-  hipLaunchKernelGGL((k_quant_e4m3<T, W, E5>), dim3(blocks), dim3(kQuantThreads), 0, s, (const T*)x, rows, K, codes, \
+  hipLaunchKernelGGL((k_quant_e4m3<T, W, E5>), dim3(blocks8), dim3(kQuantThreads), 0, s, (const T*)x, rows, K, codes, \
                      scales, tensor_scale, partial, kAmaxBlocks)
 #define GBW_Q4F(E5)                                                   \
   if (bf) {                                                           \
