@@ -249,7 +249,8 @@ __device__ __forceinline__ void down_epilogue(const MoeArgs& p, const TileInfo& 
 
 // FP4 experts.  A workgroup of 2*BN threads = BN/32 waves computes a tile of
 // 256 pairs x BN weight rows (BN = 256, launched for both stages: 8 waves as
-// 4 x 2, one workgroup per CU; BN = 128, built but not launched: 4 waves as
+// 4 x 2, one workgroup per CU; BN = 128, kept in the template but not
+// instantiated: 4 waves as
 // 4 x 1, two workgroups per CU, so one workgroup's prologue, barriers and
 // epilogue overlap the other's MFMAs).  A wave owns a
 // 64 x 128 block as 2 x 4 accumulators of v_mfma_scale_f32_32x32x64_f8f6f4 (on
@@ -666,7 +667,7 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
 
 template <int WF>
 int launch_moe_fp4(const MoeArgs& p, hipStream_t st) {
-  constexpr int bn = 256;  // (the kernel also builds 128-row tiles, two workgroups per CU: 4 % slower for the down stage)
+  constexpr int bn = 256;  // (128-row tiles, two workgroups per CU, were 4 % slower for the down stage)
   MoeArgs q = p;
   q.n_tiles = (int)(p.N / bn);
   int64_t grid = (cdiv(p.P, kMoeBM) + p.E) * q.n_tiles;
