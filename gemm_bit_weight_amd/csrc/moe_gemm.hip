@@ -250,9 +250,8 @@ __device__ __forceinline__ void down_epilogue(const MoeArgs& p, const TileInfo& 
 // FP4 experts.  A workgroup of 2*BN threads = BN/32 waves computes a tile of
 // 256 pairs x BN weight rows (BN = 256, launched for both stages: 8 waves as
 // 4 x 2, one workgroup per CU; BN = 128, kept in the template but not
-// instantiated: 4 waves as
-// 4 x 1, two workgroups per CU, so one workgroup's prologue, barriers and
-// epilogue overlap the other's MFMAs).  A wave owns a
+// instantiated: 4 waves as 4 x 1, two workgroups per CU, so one workgroup's
+// prologue, barriers and epilogue overlap the other's MFMAs).  A wave owns a
 // 64 x 128 block as 2 x 4 accumulators of v_mfma_scale_f32_32x32x64_f8f6f4 (on
 // gfx950 the 32x32x64 shape runs at the full FP4 rate; 16x16x128 at the FP8
 // rate).  Lane l of a 32x32x64 operand holds row l % 32 and the 32 K elements
