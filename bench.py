@@ -41,7 +41,7 @@ F16_PEAK_TFLOPS = 2500.0       # dense MFMA, fp16 / bf16
 # WRITE_SIZE of k_moe_fp4<VQ,256>, scaled by a 1 GiB copy (factors 2.0 and 1.0);
 # profiles/k_moe_fp4_vq_prefill_T8192_H4096_I1536_E128_top8.md.  Must be
 # measured again (or set to None) whenever that kernel changes.
-GATEUP_HBM_BYTES = 429362.9 * 2 * 1024 + 65460.6 * 1024   # FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (calibrated KiB per launch)
+GATEUP_HBM_BYTES = 431005.2 * 2 * 1024 + 62916.5 * 1024   # FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (calibrated KiB per launch)
 
 
 def log(msg):
