@@ -6,14 +6,16 @@
 // Low-Precision Mixture-of-Experts" (Fig. 1, Fig. 2) and the expert
 // down-projections of "PRQuant: Permutation Residual Quantization for
 // Low-Overhead Inference" (§4, §5.1).  The pages fix no routing rule; the one
-// here is: the k largest logits (ties to the lower expert id), weights
-// exp(l_j - l_max) / sum over the chosen k.
+// here is: the k largest logits (ties to the lower expert id; -0 ties +0,
+// NaN ranks below every number), weights exp(l_j - l_max) / sum over the
+// chosen k.
 //
 // Three kernels, no atomics on global memory, so the pair order is fixed:
 //  1. k_route_topk: one thread per token keeps a sorted top-k in registers
-//     while it scans the token's logits; a wave = a chunk of 64 tokens
-//     builds, in LDS, a 64-bit mask per expert of the chunk's tokens that
-//     chose it and writes the per-(chunk, expert) counts.
+//     while it scans the token's logits (k_route_topk16, for E <= 256: 16
+//     lanes per token); a chunk of 64 tokens builds, in LDS, a 64-bit mask
+//     per expert of the chunk's tokens that chose it and writes the
+//     per-(chunk, expert) counts.
 //  2. k_route_scan: exclusive scan of the counts in (expert, chunk) order ->
 //     expert_offsets and the first pair slot of every (chunk, expert).
 //  3. k_route_scatter: a token's pair index = its chunk's slot for the
@@ -29,6 +31,26 @@ constexpr int kMaxExperts = 1024;
 
 __device__ __forceinline__ int64_t n_chunks(int64_t T) { return (T + 63) / 64; }
 
+// Every (logit, expert) as one 64-bit key that orders exactly as the routing
+// rule does: the logit's bits made order-preserving as an unsigned integer in
+// the high word (-0 counted as +0, so the two zeros tie; NaN below every
+// number, where a stable sort of the negated logits puts it), 0xFFFF - expert
+// in the low word (a tie goes to the lower id); 0 is "no entry".  Keys are
+// distinct, so a top-k over keys needs no tie rule of its own.
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+  uint32_t u = __float_as_uint(v);
+  u = u == 0x80000000u ? 0u : u;
+  const bool nan = (u & 0x7FFFFFFFu) > 0x7F800000u;
+  uint32_t s = (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // -inf -> 0x007FFFFF, +inf -> 0xFF800000
+  s = nan ? 1u : s;
+  return ((uint64_t)s << 32) | (uint32_t)(0xFFFF - e);
+}
+
+__device__ __forceinline__ float route_key_value(uint64_t k) {
+  const uint32_t s = (uint32_t)(k >> 32);
+  return __uint_as_float((s & 0x80000000u) ? (s & 0x7FFFFFFFu) : ~s);  // (s = 1, NaN: a NaN)
+}
+
 template <int K>
 __global__ __launch_bounds__(kRouteThreads) void k_route_topk(const float* __restrict__ logits, int64_t T, int E,
                                                              int32_t* __restrict__ topk_ids,
@@ -41,31 +63,29 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_topk(const float* __res
   for (int e = lane; e < E; e += 64) mask[wv][e] = 0ull;
   __syncthreads();
 
-  float v[K];
-  int id[K];
+  uint64_t kk[K];  // descending route keys, 0 = empty
 #pragma unroll
-  for (int j = 0; j < K; ++j) {
-    v[j] = -__builtin_huge_valf();
-    id[j] = E;  // sentinel, replaced by any real expert
-  }
+  for (int j = 0; j < K; ++j) kk[j] = 0ull;
   const bool live = t < T;
   if (live) {
     const float* row = logits + t * E;
     for (int e = 0; e < E; ++e) {
-      float c = row[e];
-      int ci = e;
-      // insertion: a candidate moves past entries it is strictly larger than,
-      // so an equal logit never displaces an earlier (lower) expert id
+      // insertion: the candidate moves past every smaller key
+      uint64_t c = route_key(row[e], e);
 #pragma unroll
       for (int j = 0; j < K; ++j) {
-        const bool gt = c > v[j] || (id[j] == E);
-        const float tv = v[j];
-        const int ti = id[j];
-        v[j] = gt ? c : tv;
-        id[j] = gt ? ci : ti;
-        c = gt ? tv : c;
-        ci = gt ? ti : ci;
+        const uint64_t tk = kk[j];
+        const bool gt = c > tk;
+        kk[j] = gt ? c : tk;
+        c = gt ? tk : c;
       }
+    }
+    float v[K];
+    int id[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      v[j] = route_key_value(kk[j]);
+      id[j] = 0xFFFF - (int)(kk[j] & 0xFFFFu);
     }
     float ex[K], sum = 0.f;
 #pragma unroll
@@ -86,29 +106,29 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_topk(const float* __res
 }
 
 // Same outputs for E <= 256 with 16 lanes per token: a workgroup of 1024
-// threads is one chunk of 64 tokens; lane s of a token's group holds logits
-// s, s + 16, ... (coalesced loads), and each of the k rounds takes the
-// largest (value, then lowest expert id) not yet taken, by a lane-local scan
-// and a 16-lane reduction over DPP row permutes.
+// threads is one chunk of 64 tokens; lane s of a token's group holds the
+// logits of experts s, s + 16, ... (NV of them: 8 for E <= 128, else 16;
+// coalesced loads), as route_key keys.  Round j takes the largest key below
+// round j-1's: a lane-local pass over NV keys, then a 16-lane maximum over
+// DPP row permutes -- no branches and nothing to remove from the lists.
 template <int CTRL>
-__device__ __forceinline__ void best_step(float& v, int& e) {
-  const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
-  const int oe = __builtin_amdgcn_mov_dpp(e, CTRL, 0xF, 0xF, true);
-  const bool take = ov > v || (ov == v && oe < e);
-  v = take ? ov : v;
-  e = take ? oe : e;
+__device__ __forceinline__ uint64_t max_step(uint64_t k) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)k, CTRL, 0xF, 0xF, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(k >> 32), CTRL, 0xF, 0xF, true);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > k ? o : k;
 }
 
 // lanes ^1, ^2 (quad permutes), then the mirrors within 8 and 16 lanes:
-// after the four steps every lane of the 16-lane row holds the row's best
-__device__ __forceinline__ void row16_best(float& v, int& e) {
-  best_step<0xB1>(v, e);
-  best_step<0x4E>(v, e);
-  best_step<0x141>(v, e);
-  best_step<0x140>(v, e);
+// after the four steps every lane of the 16-lane row holds the row's maximum
+__device__ __forceinline__ uint64_t row16_max(uint64_t k) {
+  k = max_step<0xB1>(k);
+  k = max_step<0x4E>(k);
+  k = max_step<0x141>(k);
+  return max_step<0x140>(k);
 }
 
-template <int K>
+template <int K, int NV>
 __global__ __launch_bounds__(1024) void k_route_topk16(const float* __restrict__ logits, int64_t T, int E,
                                                        int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
                                                        int32_t* __restrict__ counts) {
@@ -121,31 +141,33 @@ __global__ __launch_bounds__(1024) void k_route_topk16(const float* __restrict__
   __syncthreads();
   const bool live = t < T;
   const float* row = logits + (live ? t : 0) * E;
-  float v[16];
-  uint32_t open = 0;  // bit i: entry i (expert sl + 16 i) exists and is not taken
+  float v[NV];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int e = sl + 16 * i;
-    const bool ok = live && e < E;
-    v[i] = ok ? row[e] : 0.f;
-    open |= (uint32_t)ok << i;
+    v[i] = live && e < E ? row[e] : 0.f;
+  }
+  uint64_t key[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = sl + 16 * i;
+    key[i] = live && e < E ? route_key(v[i], e) : 0ull;
   }
   int ids[K];
   float vals[K];
+  uint64_t bound = ~0ull;
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    float bv = -__builtin_huge_valf();
-    int be = 1 << 30;  // no entry: loses every comparison against a real one
+    uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const bool take = ((open >> i) & 1u) && (be == (1 << 30) || v[i] > bv);
-      bv = take ? v[i] : bv;
-      be = take ? sl + 16 * i : be;
+    for (int i = 0; i < NV; ++i) {
+      const uint64_t c = key[i] < bound ? key[i] : 0ull;
+      best = c > best ? c : best;
     }
-    row16_best(bv, be);
-    ids[j] = be;
-    vals[j] = bv;
-    if ((be & 15) == sl) open &= ~(1u << (be >> 4));
+    best = row16_max(best);
+    bound = best;
+    ids[j] = 0xFFFF - (int)(best & 0xFFFFu);
+    vals[j] = route_key_value(best);
   }
   if (live) {
     float ex[K], sum = 0.f;
@@ -276,8 +298,10 @@ static int launch_route(const float* logits, int64_t T, int E, int32_t* ids, flo
   int32_t* counts = ws;
   int32_t* base = ws + C * E;
   const unsigned blocks = (unsigned)cdiv(C, kRouteThreads / 64);
-  if (E <= 256)
-    hipLaunchKernelGGL(k_route_topk16<K>, dim3((unsigned)C), dim3(1024), 0, st, logits, T, E, ids, w, counts);
+  if (E <= 128)
+    hipLaunchKernelGGL((k_route_topk16<K, 8>), dim3((unsigned)C), dim3(1024), 0, st, logits, T, E, ids, w, counts);
+  else if (E <= 256)
+    hipLaunchKernelGGL((k_route_topk16<K, 16>), dim3((unsigned)C), dim3(1024), 0, st, logits, T, E, ids, w, counts);
   else
     hipLaunchKernelGGL(k_route_topk<K>, dim3(blocks), dim3(kRouteThreads), 0, st, logits, T, E, ids, w, counts);
   int s = check_launch("moe_route(topk)");

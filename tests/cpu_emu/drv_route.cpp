@@ -21,10 +21,12 @@ int check_launch(const char*) { return 0; }
 int device_cu_count() { return 256; }
 }
 int main(int argc, char** argv) {
-  const int64_t T = atoll(argv[1]); const int E = atoi(argv[2]), K = atoi(argv[3]); const int ties = argc > 4;
+  const int64_t T = atoll(argv[1]); const int E = atoi(argv[2]), K = atoi(argv[3]);
+  const std::string mode = argc > 4 ? argv[4] : "";  // "ties": values 0, 1, 2; "special": +-0, +-1, +-inf, NaN
   std::mt19937 g(3); std::normal_distribution<float> nd;
+  const float sp[8] = {0.f, -0.f, 1.f, -1.f, INFINITY, -INFINITY, NAN, -NAN};
   float* l = (float*)malloc(T * E * 4);
-  for (int64_t i = 0; i < T * E; ++i) l[i] = ties ? (float)(g() % 3) : nd(g);
+  for (int64_t i = 0; i < T * E; ++i) l[i] = mode == "ties" ? (float)(g() % 3) : mode == "special" ? sp[g() % 8] : nd(g);
   int32_t* ids = (int32_t*)malloc(T * K * 4); float* w = (float*)malloc(T * K * 4);
   int32_t* off = (int32_t*)malloc((E + 1) * 4); int32_t* pt = (int32_t*)malloc(T * K * 4); int32_t* pp = (int32_t*)malloc(T * K * 4);
   size_t wsb = gbw::ws_moe_route(T, E); void* ws = malloc(wsb);
@@ -32,7 +34,13 @@ int main(int argc, char** argv) {
   long bad = 0;
   for (int64_t t = 0; t < T; ++t) {
     std::vector<int> o(E); std::iota(o.begin(), o.end(), 0);
-    std::stable_sort(o.begin(), o.end(), [&](int a, int b) { return l[t * E + a] > l[t * E + b]; });
+    // descending, NaN after every number, equal values (and the two zeros) in id order
+    std::stable_sort(o.begin(), o.end(), [&](int a, int b) {
+      const float x = l[t * E + a], y = l[t * E + b];
+      if (std::isnan(x)) return false;
+      if (std::isnan(y)) return true;
+      return x > y;
+    });
     for (int j = 0; j < K; ++j) bad += ids[t * K + j] != o[j];
   }
   printf("route T=%lld E=%d K=%d status %d mismatched ids %ld off[E]=%d\n", (long long)T, E, K, st, bad, off[E]);

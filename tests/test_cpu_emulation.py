@@ -73,10 +73,15 @@ def test_moe_prquant_tail_copy_in_bounds(build_dir):
     assert "gateup status 0" in out and all(f"down mode {m} status 0" in out for m in range(3)), out
 
 
-@pytest.mark.parametrize("T,E,K,ties", [(37, 16, 4, 0), (300, 128, 8, 0), (70, 32, 8, 1), (50, 300, 5, 0)])
-def test_moe_route_in_bounds_and_exact(build_dir, T, E, K, ties):
+@pytest.mark.parametrize("T,E,K,mode", [(37, 16, 4, ""), (300, 128, 8, ""), (70, 32, 8, "ties"), (50, 300, 5, ""),
+                                        (90, 128, 8, "special"), (40, 200, 6, "special"), (30, 300, 8, "special")])
+def test_moe_route_in_bounds_and_exact(build_dir, T, E, K, mode):
+    """Ids against a stable sort (descending; -0 ties +0; NaN after every
+    number): 'ties' draws from {0, 1, 2}, 'special' from {+-0, +-1, +-inf,
+    NaN}; E = 128, 200 and 300 run the 8- and 16-entry lane-group kernels
+    and the one-thread-per-token kernel."""
     exe = _build(build_dir, "moe_route.hip", "drv_route.cpp", "emu_route")
-    out = _run(exe, T, E, K, *(["ties"] if ties else []))
+    out = _run(exe, T, E, K, *([mode] if mode else []))
     assert "status 0 mismatched ids 0" in out, out
 
 

@@ -75,6 +75,23 @@ def test_route_ties_and_permutation():
     _check_route(logits, 8)
 
 
+@pytest.mark.parametrize("E,k", [(128, 8), (200, 6), (300, 8)])
+def test_route_special_values(E, k):
+    """Logits drawn from {+-0, +-1, +-inf, NaN}: -0 ties +0 and NaN ranks
+    below every number, as in the oracle's stable sort of the negated logits
+    (E = 128 and 200 run the lane-group kernel, 300 the per-token one)."""
+    banner(f"route special values E={E} k={k}")
+    vals = np.array([0.0, -0.0, 1.0, -1.0, np.inf, -np.inf, np.nan, -np.nan], dtype=np.float32)
+    rng = np.random.default_rng(E * 31 + k)
+    logits = torch.from_numpy(vals[rng.integers(0, 8, size=(300, E))]).to(DEV)
+    r = gbw.moe_route(logits, k)
+    ref = oracle.moe_route(to_np(logits), k)
+    g = _route_np(r)
+    for key in ("topk_ids", "expert_offsets", "pair_token", "pair_pos"):
+        assert np.array_equal(g[key], ref[key]), key
+    assert np.allclose(g["topk_w"], ref["topk_w"], rtol=2e-6, atol=1e-7, equal_nan=True)
+
+
 def _bf16_ulp(v):
     """Spacing of bf16 numbers at |v| (float64 array)."""
     a = np.abs(v)

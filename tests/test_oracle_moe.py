@@ -72,6 +72,15 @@ def test_route_ties_go_to_lower_id():
     assert np.allclose(r["topk_w"], 1 / 3)
 
 
+def test_route_special_values_order():
+    """Infinities order as numbers, -0 ties +0 (lower id first) and NaN
+    ranks after every number (lower id first among NaNs): the order written
+    out by hand for one row."""
+    with np.errstate(invalid="ignore"):
+        r = oracle.moe_route(np.array([[np.nan, -0.0, 0.0, 1.0, -np.inf, np.inf, 1.0, np.nan]], np.float32), 8)
+    assert r["topk_ids"][0].tolist() == [5, 3, 6, 1, 2, 4, 0, 7]
+
+
 def test_swiglu_bf16_rounding():
     g = np.array([0.0, 1.0, -1.0, 20.0, -30.0, 0.5])
     u = np.array([3.0, 2.0, 2.0, 1.5, 1.0, -7.25])
