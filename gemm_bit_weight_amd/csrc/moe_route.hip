@@ -21,6 +21,7 @@
 //  3. k_route_scatter: a token's pair index = its chunk's slot for the
 //     expert + the number of earlier tokens of the chunk in that expert's
 //     mask (a popcount).
+// With at most kScanLds counts, 2 and 3 are one kernel, k_route_scan_scatter.
 #include "common.hpp"
 
 namespace gbw {
@@ -188,36 +189,20 @@ __global__ __launch_bounds__(1024) void k_route_topk16(const float* __restrict__
   if (tid < E) counts[chunk * E + tid] = __popcll(mask[tid]);
 }
 
-// Single workgroup of 1024 threads: G = 1024 / E' threads per expert (E' = E
-// rounded up to a power of two) each own a contiguous run of chunks; per-run
-// sums, an exclusive scan over the runs of an expert, an inclusive scan over
-// the expert totals, then each thread writes the bases of its own chunks.
-// STAGE: the whole [C][E] count table (at most kScanLds entries) is first
-// copied to LDS by coalesced loads that are all in flight together, so the
-// per-thread runs read LDS instead of walking global memory one load at a time.
+// Single workgroup of 1024 threads (count tables larger than kScanLds; smaller
+// ones go through k_route_scan_scatter): G = 1024 / E' threads per expert (E'
+// = E rounded up to a power of two) each own a contiguous run of chunks;
+// per-run sums, an exclusive scan over the runs of an expert, an inclusive
+// scan over the expert totals, then each thread writes the bases of its own
+// chunks.
 constexpr int kScanLds = 16384;  // 64 KiB of counts
-template <bool STAGE>
 __global__ __launch_bounds__(kMaxExperts) void k_route_scan(const int32_t* __restrict__ counts, int64_t C, int E,
                                                            int32_t* __restrict__ base,
                                                            int32_t* __restrict__ expert_offsets) {
   __shared__ int32_t part[kMaxExperts];
   __shared__ int32_t tot[kMaxExperts];
-  __shared__ int32_t stg[STAGE ? kScanLds : 1];
   const int tid = threadIdx.x;
-  if (STAGE) {
-    const int n = (int)(C * E);  // <= kScanLds
-    constexpr int U = kScanLds / kMaxExperts;
-    int32_t v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = u * kMaxExperts + tid;
-      v[u] = i < n ? counts[i] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) stg[u * kMaxExperts + tid] = v[u];
-    __syncthreads();
-  }
-  const int32_t* const cnt = STAGE ? stg : counts;
+  const int32_t* const cnt = counts;
   int Ep = 1;
   while (Ep < E) Ep <<= 1;
   const int G = kMaxExperts / Ep;
@@ -285,6 +270,87 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_scatter(const int32_t* 
   }
 }
 
+// Scan and scatter in one kernel when the [C][E] count table fits in LDS
+// (C * E <= kScanLds): every workgroup (4 chunks, one wave each) copies the
+// whole table with all loads in flight, forms for each expert the total over
+// all chunks and the sum over the chunks before each of its own, scans the
+// totals over the experts (expert_offsets, written by workgroup 0), and
+// places its tokens' pairs as k_route_scatter does.  Same bases as the
+// separate scan, without its single-workgroup pass and kernel boundary.
+template <int K>
+__global__ __launch_bounds__(kRouteThreads) void k_route_scan_scatter(const int32_t* __restrict__ counts,
+                                                                     const int32_t* __restrict__ topk_ids, int64_t T,
+                                                                     int E, int32_t* __restrict__ expert_offsets,
+                                                                     int32_t* __restrict__ pair_token,
+                                                                     int32_t* __restrict__ pair_pos) {
+  constexpr int NW = kRouteThreads / 64;  // chunks per workgroup
+  __shared__ int32_t stg[kScanLds];
+  __shared__ unsigned long long mask[NW][kMaxExperts];
+  __shared__ int32_t base[NW][kMaxExperts];  // expert_offsets[e] + pairs of e in earlier chunks
+  __shared__ int32_t run[kRouteThreads];       // per-thread sums of the expert totals, then their scan
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t C = n_chunks(T);
+  const int64_t c0 = (int64_t)blockIdx.x * NW;  // first chunk of this workgroup
+  const int64_t chunk = c0 + wv;
+  const int64_t t = chunk * 64 + lane;
+  const int n = (int)(C * E);
+#pragma unroll 16
+  for (int i = tid; i < n; i += kRouteThreads) stg[i] = counts[i];
+  for (int e = lane; e < E; e += 64) mask[wv][e] = 0ull;
+  __syncthreads();
+  int id[K];
+  const bool live = t < T;
+  if (live) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      id[j] = topk_ids[t * K + j];
+      atomicOr(&mask[wv][id[j]], 1ull << lane);
+    }
+  }
+  // experts are dealt to threads in runs of EPT consecutive ids; each thread
+  // keeps, per expert of its run, the prefix over this workgroup's chunks in
+  // base[w][e] and the total; the run sums are then scanned across threads
+  const int EPT = (E + kRouteThreads - 1) / kRouteThreads;
+  const int e0 = tid * EPT, e1 = min(E, e0 + EPT);
+  int32_t rsum = 0;
+  for (int e = e0; e < e1; ++e) {
+    int32_t acc = 0;
+    for (int64_t c = 0; c < C; ++c) {
+      const int64_t w = c - c0;
+      if (w >= 0 && w < NW) base[w][e] = acc;
+      acc += stg[c * E + e];
+    }
+    rsum += acc;
+    stg[e] = acc;  // the total, over row 0 (only this thread reads column e)
+  }
+  run[tid] = rsum;
+  __syncthreads();
+  for (int o = 1; o < kRouteThreads; o <<= 1) {  // inclusive scan of the run sums
+    const int32_t add = tid >= o ? run[tid - o] : 0;
+    __syncthreads();
+    run[tid] += add;
+    __syncthreads();
+  }
+  int32_t off = tid ? run[tid - 1] : 0;
+  for (int e = e0; e < e1; ++e) {
+    const int32_t tot = stg[e];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) base[w][e] += off;
+    if (blockIdx.x == 0) expert_offsets[e] = off;
+    off += tot;
+  }
+  if (blockIdx.x == 0 && tid == kRouteThreads - 1) expert_offsets[E] = run[tid];
+  __syncthreads();
+  if (!live) return;
+  const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int32_t p = base[wv][id[j]] + __popcll(mask[wv][id[j]] & below);
+    pair_token[p] = (int32_t)t;
+    pair_pos[t * K + j] = p;
+  }
+}
+
 size_t ws_moe_route(int64_t T, int64_t E) {
   if (T <= 0 || E <= 0) return 0;
   const int64_t C = (T + 63) / 64;
@@ -306,10 +372,12 @@ static int launch_route(const float* logits, int64_t T, int E, int32_t* ids, flo
     hipLaunchKernelGGL(k_route_topk<K>, dim3(blocks), dim3(kRouteThreads), 0, st, logits, T, E, ids, w, counts);
   int s = check_launch("moe_route(topk)");
   if (s) return s;
-  if (C * E <= kScanLds)
-    hipLaunchKernelGGL(k_route_scan<true>, dim3(1), dim3(kMaxExperts), 0, st, counts, C, E, base, off);
-  else
-    hipLaunchKernelGGL(k_route_scan<false>, dim3(1), dim3(kMaxExperts), 0, st, counts, C, E, base, off);
+  if (C * E <= kScanLds) {
+    hipLaunchKernelGGL(k_route_scan_scatter<K>, dim3(blocks), dim3(kRouteThreads), 0, st, counts, ids, T, E, off, pt,
+                       pp);
+    return check_launch("moe_route(scan + scatter)");
+  }
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(kMaxExperts), 0, st, counts, C, E, base, off);
   if ((s = check_launch("moe_route(scan)"))) return s;
   hipLaunchKernelGGL(k_route_scatter<K>, dim3(blocks), dim3(kRouteThreads), 0, st, ids, T, E, base, pt, pp);
   return check_launch("moe_route(scatter)");
@@ -335,7 +403,7 @@ extern "C" int moe_route(const float* logits, int64_t T, int32_t E, int32_t topk
   hipStream_t s = as_stream(stream);
   if (T == 0) {
     // no tokens: every expert offset is zero
-    hipLaunchKernelGGL(k_route_scan<false>, dim3(1), dim3(kMaxExperts), 0, s, (const int32_t*)nullptr, (int64_t)0, E,
+    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(kMaxExperts), 0, s, (const int32_t*)nullptr, (int64_t)0, E,
                        (int32_t*)nullptr, expert_offsets);
     return check_launch("moe_route(empty)");
   }

@@ -43,6 +43,20 @@ int main(int argc, char** argv) {
     });
     for (int j = 0; j < K; ++j) bad += ids[t * K + j] != o[j];
   }
-  printf("route T=%lld E=%d K=%d status %d mismatched ids %ld off[E]=%d\n", (long long)T, E, K, st, bad, off[E]);
+  // pair list: (expert, token) order; offsets = exclusive prefix of the counts
+  long badp = 0;
+  std::vector<long> cnt(E + 1, 0);
+  for (int64_t i = 0; i < T * K; ++i) cnt[ids[i] + 1]++;
+  for (int e = 0; e < E; ++e) cnt[e + 1] += cnt[e];
+  for (int e = 0; e <= E; ++e) badp += off[e] != cnt[e];
+  std::vector<long> fill(cnt.begin(), cnt.end() - 1);
+  for (int64_t t = 0; t < T; ++t)
+    for (int j = 0; j < K; ++j) {
+      const long p = fill[ids[t * K + j]]++;  // tokens ascend within an expert
+      badp += pp[t * K + j] != p;
+      badp += pt[p] != t;
+    }
+  printf("route T=%lld E=%d K=%d status %d mismatched ids %ld mismatched pairs %ld off[E]=%d\n", (long long)T, E, K,
+         st, bad, badp, off[E]);
   return 0;
 }

@@ -58,7 +58,7 @@ def _check_route(logits, topk):
 
 
 @pytest.mark.parametrize("T,E,k", [(1, 4, 1), (37, 16, 4), (200, 64, 6), (4096, 128, 8), (8192, 128, 8),
-                                   (130, 1000, 16)])
+                                   (130, 1000, 16), (20000, 128, 8), (1100, 1000, 8)])
 def test_route(T, E, k):
     banner(f"route T={T} E={E} k={k}")
     logits = synth.normal((T, E), 1.0, T + E, "route.l", DEV)
