@@ -313,10 +313,24 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_scan_scatter(const int3
   const int EPT = (E + kRouteThreads - 1) / kRouteThreads;
   const int e0 = tid * EPT, e1 = min(E, e0 + EPT);
   int32_t rsum = 0;
+  const int Ci = (int)C;
+  const int w0 = (int)c0;
   for (int e = e0; e < e1; ++e) {
     int32_t acc = 0;
-    for (int64_t c = 0; c < C; ++c) {
-      const int64_t w = c - c0;
+    int c = 0;
+    for (; c + 8 <= Ci; c += 8) {  // eight LDS reads in flight per step
+      int32_t v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = stg[(c + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int w = c + i - w0;
+        if (w >= 0 && w < NW) base[w][e] = acc;
+        acc += v[i];
+      }
+    }
+    for (; c < Ci; ++c) {
+      const int w = c - w0;
       if (w >= 0 && w < NW) base[w][e] = acc;
       acc += stg[c * E + e];
     }
