@@ -75,7 +75,8 @@ def test_moe_prquant_tail_copy_in_bounds(build_dir):
 
 @pytest.mark.parametrize("T,E,K,mode", [(37, 16, 4, ""), (300, 128, 8, ""), (70, 32, 8, "ties"), (50, 300, 5, ""),
                                         (90, 128, 8, "special"), (40, 200, 6, "special"), (30, 300, 8, "special"),
-                                        (1100, 1000, 8, ""), (700, 16, 4, "")])
+                                        (1100, 1000, 8, ""), (700, 16, 4, ""),
+                                        (100, 7, 2, "")])
 def test_moe_route_in_bounds_and_exact(build_dir, T, E, K, mode):
     """Ids against a stable sort (descending; -0 ties +0; NaN after every
     number): 'ties' draws from {0, 1, 2}, 'special' from {+-0, +-1, +-inf,
@@ -85,7 +86,8 @@ def test_moe_route_in_bounds_and_exact(build_dir, T, E, K, mode):
     entries (chunks of 64 tokens x experts) take the fused scan + scatter
     kernel (700 tokens: 11 chunks, more than one eight-chunk step of its
     per-expert pass); 1100 tokens x 1000 experts (18000) the separate scan
-    and scatter."""
+    and scatter; 7 experts leave a count table that is not a whole number of
+    16-byte pieces."""
     exe = _build(build_dir, "moe_route.hip", "drv_route.cpp", "emu_route")
     out = _run(exe, T, E, K, *([mode] if mode else []))
     assert "status 0 mismatched ids 0 mismatched pairs 0" in out, out
