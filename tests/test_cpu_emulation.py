@@ -86,8 +86,7 @@ def test_moe_route_in_bounds_and_exact(build_dir, T, E, K, mode):
     entries (chunks of 64 tokens x experts) take the fused scan + scatter
     kernel (700 tokens: 11 chunks, more than one eight-chunk step of its
     per-expert pass); 1100 tokens x 1000 experts (18000) the separate scan
-    and scatter; 7 experts leave a count table that is not a whole number of
-    16-byte pieces."""
+    and scatter; 7 experts: an odd expert count (14 counts)."""
     exe = _build(build_dir, "moe_route.hip", "drv_route.cpp", "emu_route")
     out = _run(exe, T, E, K, *([mode] if mode else []))
     assert "status 0 mismatched ids 0 mismatched pairs 0" in out, out
