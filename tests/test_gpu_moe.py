@@ -85,7 +85,8 @@ def test_route_special_values(E, k):
     rng = np.random.default_rng(E * 31 + k)
     logits = torch.from_numpy(vals[rng.integers(0, 8, size=(300, E))]).to(DEV)
     r = gbw.moe_route(logits, k)
-    ref = oracle.moe_route(to_np(logits), k)
+    with np.errstate(invalid="ignore"):  # inf - inf in the weights of tokens led by +inf
+        ref = oracle.moe_route(to_np(logits), k)
     g = _route_np(r)
     for key in ("topk_ids", "expert_offsets", "pair_token", "pair_pos"):
         assert np.array_equal(g[key], ref[key]), key
