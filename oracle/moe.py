@@ -98,7 +98,8 @@ def swiglu_bf16(g, u):
     float64 and rounded once to bf16.  Returns bf16 bit patterns."""
     g = np.asarray(g, dtype=np.float64)
     u = np.asarray(u, dtype=np.float64)
-    h = g / (1.0 + np.exp(-g)) * u
+    with np.errstate(over="ignore"):             # e^-g = inf for g < -709: h = -0 * u
+        h = g / (1.0 + np.exp(-g)) * u
     # float64 -> bf16 RNE: go through float32 only when that is exact enough
     return _f64_to_bf16_bits(h)
 

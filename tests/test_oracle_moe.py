@@ -238,3 +238,203 @@ def test_residual_down_reduces_weight_error():
     plain = oracle.moe_down_combine(hc, hs, "e8m0_b32", route, wc, ws)
     res = oracle.moe_down_combine_residual(hc, hs, route, wc, ws, rc, rs, 64)
     assert np.linalg.norm(res - exact) < np.linalg.norm(plain - exact)
+
+
+# ---------------------------------------------------------------------------
+# Distinct experts: the grouped stages against scalar loops over the pairs
+# ---------------------------------------------------------------------------
+#
+# The gated MLP of the PRQuant page (§4 Eq. (1)) applied to each routed
+# expert: for token t and its j-th chosen expert e,
+#   g = a_t . W_gate,e rows, u = a_t . W_up,e rows, h = bf16(silu(g) * u),
+#   y_t = sum_j w_tj * deq(hq_(t,j)) . W_down,e rows.
+# The loops below walk tokens and slots (not the pair list), decode every
+# element from the format's closed form with a local table (the E2M1 value set
+# of the golden file; E8M0 2^(s-127); E4M3 (1 + m/8) 2^(e-7), (m/8) 2^-6) and
+# sum products one at a time in float64.  Every expert's weights are drawn
+# independently, so an oracle that contracts a pair with the wrong expert's
+# weight, or shifts a segment by one expert, disagrees with them.
+
+import json
+import os
+
+_GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "mx_formats.json")))
+_E2M1 = _GOLD["e2m1_values"]["magnitudes"]
+
+
+def _nib(packed_row, k):
+    b = int(packed_row[k // 2])
+    return (b >> 4) & 15 if k & 1 else b & 15
+
+
+def _e2m1(c):
+    return -_E2M1[c & 7] if c & 8 else _E2M1[c & 7]
+
+
+def _scale(code, fmt):
+    c = int(code)
+    if fmt == "e8m0_b32":
+        return math.ldexp(1.0, c - 127)
+    e, m = (c >> 3) & 15, c & 7
+    return (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * math.ldexp(1.0, e - 7)
+
+
+def _elem(codes, scales, r, k, fmt):
+    bs = 32 if fmt == "e8m0_b32" else 16
+    return _e2m1(_nib(codes[r], k)) * _scale(scales[r][k // bs], fmt)
+
+
+def _dot(ac, as_, ar, wc, ws, wr, K, fmt):
+    s = 0.0
+    for k in range(K):
+        s += _elem(ac, as_, ar, k, fmt) * _elem(wc, ws, wr, k, fmt)
+    return s
+
+
+def _bf16(v):
+    """float64 -> nearest bf16 value (ties to even); below bf16's normal
+    range (2^-126) the spacing is that of its subnormals, 2^-133."""
+    if v == 0.0:
+        return v
+    if abs(v) < 2.0 ** -126:
+        return math.ldexp(round(math.ldexp(v, 133)), -133)   # round(): ties to even on floats
+    m, e = math.frexp(v)                 # v = m 2^e, 0.5 <= |m| < 1
+    return math.ldexp(round(m * 256.0), e - 8)
+
+
+def _rand_codes(rng, shape):
+    return rng.integers(0, 256, size=shape, dtype=np.uint8)
+
+
+def _rand_scales(rng, shape, fmt):
+    if fmt == "e8m0_b32":
+        return rng.integers(118, 131, size=shape).astype(np.uint8)
+    return rng.integers(0x28, 0x48, size=shape).astype(np.uint8)      # E4M3 codes around 1
+
+
+def _distinct_problem(fmt, seed, T=7, H=64, I=32, E=3, k=2):
+    rng = np.random.default_rng(seed)
+    bs = 32 if fmt == "e8m0_b32" else 16
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    route = oracle.moe_route(logits, k)
+    d = dict(route=route, T=T, H=H, I=I, E=E, k=k, bs=bs,
+             ac=_rand_codes(rng, (T, H // 2)), as_=_rand_scales(rng, (T, H // bs), fmt),
+             gc=_rand_codes(rng, (E, 2 * I, H // 2)), gs=_rand_scales(rng, (E, 2 * I, H // bs), fmt),
+             hc=_rand_codes(rng, (T * k, I // 2)), hs=_rand_scales(rng, (T * k, I // bs), fmt),
+             dc=_rand_codes(rng, (E, H, I // 2)), ds=_rand_scales(rng, (E, H, I // bs), fmt))
+    if fmt != "e8m0_b32":
+        d.update(a_ts=np.float32(0.375), g_ts=np.array([[0.5 + e, 1.25 * (e + 1)] for e in range(E)], np.float32),
+                 h_ts=np.float32(1.5), d_ts=np.array([2.0 ** -e + 0.25 for e in range(E)], np.float32))
+    return d
+
+
+def _loop_gateup(d, fmt):
+    """g, u [P][I] in pair order, from token/slot loops."""
+    r = d["route"]
+    I, H = d["I"], d["H"]
+    P = d["T"] * d["k"]
+    g = np.zeros((P, I))
+    u = np.zeros((P, I))
+    for t in range(d["T"]):
+        for j in range(d["k"]):
+            e = int(r["topk_ids"][t, j])
+            p = int(r["pair_pos"][t, j])
+            for i in range(I):
+                gv = _dot(d["ac"], d["as_"], t, d["gc"][e], d["gs"][e], i, H, fmt)
+                uv = _dot(d["ac"], d["as_"], t, d["gc"][e], d["gs"][e], I + i, H, fmt)
+                if fmt != "e8m0_b32":
+                    gv *= float(d["a_ts"]) * float(d["g_ts"][e][0])
+                    uv *= float(d["a_ts"]) * float(d["g_ts"][e][1])
+                g[p, i], u[p, i] = gv, uv
+    return g, u
+
+
+def _loop_down(d, fmt, hc, hs, dc, ds, I):
+    """y [T][H]: for each token, its slots in order, weighted by topk_w."""
+    r = d["route"]
+    y = np.zeros((d["T"], d["H"]))
+    for t in range(d["T"]):
+        for j in range(d["k"]):
+            e = int(r["topk_ids"][t, j])
+            p = int(r["pair_pos"][t, j])
+            w = float(r["topk_w"][t, j])
+            for n in range(d["H"]):
+                o = _dot(hc, hs, p, dc[e], ds[e], n, I, fmt)
+                if fmt != "e8m0_b32":
+                    o *= float(d["h_ts"]) * float(d["d_ts"][e])
+                y[t, n] += w * o
+    return y
+
+
+@pytest.mark.parametrize("fmt", ["e8m0_b32", "e4m3_b16"])
+def test_gateup_distinct_experts_scalar_loop(fmt):
+    d = _distinct_problem(fmt, 50)
+    assert len(set(d["route"]["topk_ids"].reshape(-1).tolist())) == d["E"]   # every expert owns pairs
+    g_ref, u_ref = _loop_gateup(d, fmt)
+    g, u = oracle.moe_gateup(d["ac"], d["as_"], fmt, d["route"], d["gc"], d["gs"], d.get("a_ts"), d.get("g_ts"))
+    # every product has <= 12 significant bits and the sums span far fewer than
+    # 53 bits: both sides hold the exact value
+    assert np.array_equal(g, g_ref) and np.array_equal(u, u_ref)
+    # a subset of pairs, in a scrambled order
+    pairs = np.array([5, 0, 13, 2])
+    gs, us = oracle.moe_gateup(d["ac"], d["as_"], fmt, d["route"], d["gc"], d["gs"], d.get("a_ts"), d.get("g_ts"),
+                               pairs=pairs)
+    assert np.array_equal(gs, g_ref[pairs]) and np.array_equal(us, u_ref[pairs])
+    # the loop tells experts apart: with experts 0 and 1 swapped it disagrees
+    sw = dict(d, gc=d["gc"][[1, 0, 2]], gs=d["gs"][[1, 0, 2]])
+    if fmt != "e8m0_b32":
+        sw["g_ts"] = d["g_ts"][[1, 0, 2]]
+    g_sw, _ = _loop_gateup(sw, fmt)
+    assert not np.array_equal(g_sw, g)
+
+
+def test_swiglu_of_gateup_scalar_loop():
+    """h = bf16(silu(g) u) element by element against a scalar frexp/round."""
+    d = _distinct_problem("e8m0_b32", 51)
+    g, u = oracle.moe_gateup(d["ac"], d["as_"], "e8m0_b32", d["route"], d["gc"], d["gs"])
+    h = oracle.bf16_bits_to_f32(oracle.swiglu_bf16(g, u)).astype(np.float64)
+    for p in range(g.shape[0]):
+        for i in range(g.shape[1]):
+            z = g[p, i]
+            # z e^z / (1 + e^z) where e^-z would overflow (the result is then far below bf16's range)
+            s = z / (1.0 + math.exp(-z)) if z > -700.0 else z * math.exp(z) / (1.0 + math.exp(z))
+            assert h[p, i] == _bf16(s * u[p, i])
+
+
+@pytest.mark.parametrize("fmt", ["e8m0_b32", "e4m3_b16"])
+def test_down_combine_distinct_experts_scalar_loop(fmt):
+    d = _distinct_problem(fmt, 52)
+    y_ref = _loop_down(d, fmt, d["hc"], d["hs"], d["dc"], d["ds"], d["I"])
+    y = oracle.moe_down_combine(d["hc"], d["hs"], fmt, d["route"], d["dc"], d["ds"], d.get("h_ts"), d.get("d_ts"))
+    # per-pair outputs are exact; the weighted sums of k terms round in a
+    # different order
+    assert np.allclose(y, y_ref, rtol=1e-13, atol=1e-13 * np.abs(y_ref).max())
+    toks = [6, 1, 3]
+    ys = oracle.moe_down_combine(d["hc"], d["hs"], fmt, d["route"], d["dc"], d["ds"], d.get("h_ts"),
+                                 d.get("d_ts"), tokens=toks)
+    assert np.allclose(ys, y_ref[toks], rtol=1e-13, atol=1e-13 * np.abs(y_ref).max())
+    # a mistaken oracle -- the pairs of expert 1 contracted with expert 2's
+    # down weight -- fails this comparison
+    bad = d["dc"].copy()
+    bad[1] = d["dc"][2]
+    bad_s = d["ds"].copy()
+    bad_s[1] = d["ds"][2]
+    y_bad = oracle.moe_down_combine(d["hc"], d["hs"], fmt, d["route"], bad, bad_s, d.get("h_ts"), d.get("d_ts"))
+    assert not np.allclose(y_bad, y_ref, rtol=1e-6, atol=1e-6 * np.abs(y_ref).max())
+
+
+def test_down_combine_residual_distinct_experts_scalar_loop():
+    """PRQuant residual on the down projections: the loop over I + tail with
+    the activation's last `tail` columns read a second time against R_e."""
+    fmt, tail = "e8m0_b32", 32
+    d = _distinct_problem(fmt, 53, I=64)
+    rng = np.random.default_rng(54)
+    rc = _rand_codes(rng, (d["E"], d["H"], tail // 2))
+    rs = _rand_scales(rng, (d["E"], d["H"], tail // 32), fmt)
+    I = d["I"]
+    hc_aug = np.concatenate([d["hc"], d["hc"][:, (I - tail) // 2:]], axis=1)
+    hs_aug = np.concatenate([d["hs"], d["hs"][:, (I - tail) // 32:]], axis=1)
+    y_ref = _loop_down(d, fmt, hc_aug, hs_aug, np.concatenate([d["dc"], rc], axis=2),
+                       np.concatenate([d["ds"], rs], axis=2), I + tail)
+    y = oracle.moe_down_combine_residual(d["hc"], d["hs"], d["route"], d["dc"], d["ds"], rc, rs, tail)
+    assert np.allclose(y, y_ref, rtol=1e-13, atol=1e-13 * np.abs(y_ref).max())
