@@ -5,8 +5,18 @@ link this package: only the test suite, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
 library (``gemm_bit_weight_amd``) and never imports it.
 
-Everything here is plain numpy, decoding to float64 and accumulating in
-float64.  Where the method is an encoding (the block-scaled FP4 quantizers,
+Two implementations of the same definitions:
+  * ``oracle.native`` -- plain C++17 (``oracle/native/oracle.cpp``): every
+    operand decoded to double from its format's closed form, every output
+    one term-by-term Neumaier-compensated sum, std::thread over outputs.  The
+    GPU parity tests and the bench's CPU baseline use it for the
+    contractions.
+  * this package's numpy modules, the cross-check: each C++ function is
+    held bit for bit (or to the last ulp where the summation order differs)
+    to its numpy twin, and both are pinned by the same closed forms, brute
+    force and special cases.
+
+The numpy side decodes to float64 and accumulates in float64.  Where the method is an encoding (the block-scaled FP4 quantizers,
 routing), the functions follow the steps in the order the pages describe
 them; where the method reaches a result with a plain definition (every GEMM,
 the LUT kernel, the VQ decode) the oracle is that definition written out with

@@ -258,6 +258,11 @@ def test_residual_down_reduces_weight_error():
 import json
 import os
 
+import oracle.native
+
+# both oracles (numpy, C++) are held to the same loops
+IMPLS = pytest.mark.parametrize("impl", [oracle, oracle.native], ids=["numpy", "cpp"])
+
 _GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "mx_formats.json")))
 _E2M1 = _GOLD["e2m1_values"]["magnitudes"]
 
@@ -366,19 +371,20 @@ def _loop_down(d, fmt, hc, hs, dc, ds, I):
     return y
 
 
+@IMPLS
 @pytest.mark.parametrize("fmt", ["e8m0_b32", "e4m3_b16"])
-def test_gateup_distinct_experts_scalar_loop(fmt):
+def test_gateup_distinct_experts_scalar_loop(fmt, impl):
     d = _distinct_problem(fmt, 50)
     assert len(set(d["route"]["topk_ids"].reshape(-1).tolist())) == d["E"]   # every expert owns pairs
     g_ref, u_ref = _loop_gateup(d, fmt)
-    g, u = oracle.moe_gateup(d["ac"], d["as_"], fmt, d["route"], d["gc"], d["gs"], d.get("a_ts"), d.get("g_ts"))
+    g, u = impl.moe_gateup(d["ac"], d["as_"], fmt, d["route"], d["gc"], d["gs"], d.get("a_ts"), d.get("g_ts"))
     # every product has <= 12 significant bits and the sums span far fewer than
     # 53 bits: both sides hold the exact value
     assert np.array_equal(g, g_ref) and np.array_equal(u, u_ref)
     # a subset of pairs, in a scrambled order
     pairs = np.array([5, 0, 13, 2])
-    gs, us = oracle.moe_gateup(d["ac"], d["as_"], fmt, d["route"], d["gc"], d["gs"], d.get("a_ts"), d.get("g_ts"),
-                               pairs=pairs)
+    gs, us = impl.moe_gateup(d["ac"], d["as_"], fmt, d["route"], d["gc"], d["gs"], d.get("a_ts"), d.get("g_ts"),
+                             pairs=pairs)
     assert np.array_equal(gs, g_ref[pairs]) and np.array_equal(us, u_ref[pairs])
     # the loop tells experts apart: with experts 0 and 1 swapped it disagrees
     sw = dict(d, gc=d["gc"][[1, 0, 2]], gs=d["gs"][[1, 0, 2]])
@@ -388,11 +394,12 @@ def test_gateup_distinct_experts_scalar_loop(fmt):
     assert not np.array_equal(g_sw, g)
 
 
-def test_swiglu_of_gateup_scalar_loop():
+@IMPLS
+def test_swiglu_of_gateup_scalar_loop(impl):
     """h = bf16(silu(g) u) element by element against a scalar frexp/round."""
     d = _distinct_problem("e8m0_b32", 51)
-    g, u = oracle.moe_gateup(d["ac"], d["as_"], "e8m0_b32", d["route"], d["gc"], d["gs"])
-    h = oracle.bf16_bits_to_f32(oracle.swiglu_bf16(g, u)).astype(np.float64)
+    g, u = impl.moe_gateup(d["ac"], d["as_"], "e8m0_b32", d["route"], d["gc"], d["gs"])
+    h = oracle.bf16_bits_to_f32(impl.swiglu_bf16(g, u)).astype(np.float64)
     for p in range(g.shape[0]):
         for i in range(g.shape[1]):
             z = g[p, i]
@@ -401,17 +408,18 @@ def test_swiglu_of_gateup_scalar_loop():
             assert h[p, i] == _bf16(s * u[p, i])
 
 
+@IMPLS
 @pytest.mark.parametrize("fmt", ["e8m0_b32", "e4m3_b16"])
-def test_down_combine_distinct_experts_scalar_loop(fmt):
+def test_down_combine_distinct_experts_scalar_loop(fmt, impl):
     d = _distinct_problem(fmt, 52)
     y_ref = _loop_down(d, fmt, d["hc"], d["hs"], d["dc"], d["ds"], d["I"])
-    y = oracle.moe_down_combine(d["hc"], d["hs"], fmt, d["route"], d["dc"], d["ds"], d.get("h_ts"), d.get("d_ts"))
+    y = impl.moe_down_combine(d["hc"], d["hs"], fmt, d["route"], d["dc"], d["ds"], d.get("h_ts"), d.get("d_ts"))
     # per-pair outputs are exact; the weighted sums of k terms round in a
     # different order
     assert np.allclose(y, y_ref, rtol=1e-13, atol=1e-13 * np.abs(y_ref).max())
     toks = [6, 1, 3]
-    ys = oracle.moe_down_combine(d["hc"], d["hs"], fmt, d["route"], d["dc"], d["ds"], d.get("h_ts"),
-                                 d.get("d_ts"), tokens=toks)
+    ys = impl.moe_down_combine(d["hc"], d["hs"], fmt, d["route"], d["dc"], d["ds"], d.get("h_ts"),
+                               d.get("d_ts"), tokens=toks)
     assert np.allclose(ys, y_ref[toks], rtol=1e-13, atol=1e-13 * np.abs(y_ref).max())
     # a mistaken oracle -- the pairs of expert 1 contracted with expert 2's
     # down weight -- fails this comparison
@@ -419,11 +427,12 @@ def test_down_combine_distinct_experts_scalar_loop(fmt):
     bad[1] = d["dc"][2]
     bad_s = d["ds"].copy()
     bad_s[1] = d["ds"][2]
-    y_bad = oracle.moe_down_combine(d["hc"], d["hs"], fmt, d["route"], bad, bad_s, d.get("h_ts"), d.get("d_ts"))
+    y_bad = impl.moe_down_combine(d["hc"], d["hs"], fmt, d["route"], bad, bad_s, d.get("h_ts"), d.get("d_ts"))
     assert not np.allclose(y_bad, y_ref, rtol=1e-6, atol=1e-6 * np.abs(y_ref).max())
 
 
-def test_down_combine_residual_distinct_experts_scalar_loop():
+@IMPLS
+def test_down_combine_residual_distinct_experts_scalar_loop(impl):
     """PRQuant residual on the down projections: the loop over I + tail with
     the activation's last `tail` columns read a second time against R_e."""
     fmt, tail = "e8m0_b32", 32
@@ -436,5 +445,5 @@ def test_down_combine_residual_distinct_experts_scalar_loop():
     hs_aug = np.concatenate([d["hs"], d["hs"][:, (I - tail) // 32:]], axis=1)
     y_ref = _loop_down(d, fmt, hc_aug, hs_aug, np.concatenate([d["dc"], rc], axis=2),
                        np.concatenate([d["ds"], rs], axis=2), I + tail)
-    y = oracle.moe_down_combine_residual(d["hc"], d["hs"], d["route"], d["dc"], d["ds"], rc, rs, tail)
+    y = impl.moe_down_combine_residual(d["hc"], d["hs"], d["route"], d["dc"], d["ds"], rc, rs, tail)
     assert np.allclose(y, y_ref, rtol=1e-13, atol=1e-13 * np.abs(y_ref).max())
