@@ -290,13 +290,19 @@ def residual_tail_gemm(a: Act, w: Weight, r: Optional[Weight], tail, M=None, out
 
 
 def lut_gemm(x_bf16, idx, centroids_f16, group=128, out=None, ws=None, flags=0, stream=None):
+    """y = bf16(x) fp16(C[idx])^T.  ``ws``: a workspace whose first bytes
+    (the tile arrival counters) are zero before its first use; every call
+    leaves them zero, so one zeroed workspace serves any number of calls.
+    ``ws=False`` runs without one (one workgroup per tile over all of K)."""
     M, K = x_bf16.shape
     N = idx.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x_bf16.device)
     need = workspace_size(OP_LUT_GEMM, M, N, K)
-    if ws is None and need:
-        ws = torch.empty(need, dtype=torch.uint8, device=x_bf16.device)
+    if ws is False:
+        ws = None
+    elif ws is None and need:
+        ws = torch.zeros(need, dtype=torch.uint8, device=x_bf16.device)
     _check(_lib.lut_gemm(M, N, K, group, _ptr(x_bf16), _ptr(idx), _ptr(centroids_f16), _ptr(out), flags, _ptr(ws),
                          ws.numel() if ws is not None else 0, _stream(stream)))
     return out

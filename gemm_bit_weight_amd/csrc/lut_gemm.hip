@@ -11,19 +11,22 @@
 // the 16-entry table of its own (row, group) in eight VGPRs, split into a
 // low-byte plane and a high-byte plane, and looks up four indices at once
 // with byte permutes (v_perm_b32) -- no LDS traffic and no bank conflicts for
-// the lookups.  The decoded fp16 weights feed fp16 MFMA (16x16x32) directly;
-// fp32 accumulation.
+// the lookups.  The decoded fp16 weights feed fp16 MFMA directly; fp32
+// accumulation.
 //
-// Data path per wave: 16 output rows n; per K group of 128 a lane (n, q)
-// holds elements [32q, 32q + 32) of that group: one 16-byte index load, its
-// table (two 16-byte loads), four MFMA steps of 8 elements.  Inside each
-// 8-element step the decode yields the elements in the order 0,2,4,6,1,3,5,7
-// (even nibbles, then odd); x is staged in LDS as fp16 in the same order, so
-// both MFMA operands pair the same K indices.
+// Activations: bf16 has fp32's exponent range, fp16 a much narrower one, so
+// x is not converted to fp16 as it is.  Each 128-element chunk of an x row is
+// multiplied by a power of two 2^s chosen from the chunk's largest magnitude
+// (that magnitude lands in [2^14, 2^15), far from fp16's 65504), converted to
+// fp16, contracted, and the chunk's fp32 partial sum is multiplied by 2^-s
+// before it joins the row's sum.  Both multiplies are exact; every bf16 value
+// within 2^31 of its chunk's largest is exact in fp16 after the scaling (a
+// smaller one contributes less than 2^-31 of that chunk's largest product,
+// and is rounded).  So any finite bf16 input works, 1e30 and 2^-30 alike.
 //
-// x (bf16) is converted to fp16 once per workgroup while it is staged; values
-// with |x| < 2^-17 lose low bits in fp16's subnormal range (a relative error
-// far below the output tolerance), every other bf16 value is exact in fp16.
+// Decode order: inside each 8-element piece the decode yields the elements
+// in the order 0,2,4,6,1,3,5,7 (even nibbles, then odd); x is staged in LDS as
+// fp16 in the same order, so both MFMA operands pair the same K indices.
 #include "common.hpp"
 
 namespace gbw {
@@ -64,6 +67,40 @@ __device__ __forceinline__ void split_table(const v4i a, const v4i b, uint32_t (
   }
 }
 
+// max over the 16 lanes of a DPP row (lanes 16r .. 16r + 15)
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));   // quad_perm: lane ^ 1
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));   // quad_perm: lane ^ 2
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, true));  // row_ror:4
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true));  // row_ror:8
+  return v;
+}
+
+// Power-of-two prescale exponent of an x chunk from the bf16 magnitude bits
+// of its largest element: 2^s puts that element in [2^14, 2^15); zero and
+// bf16-subnormal chunks take the largest exponent used, 126 (every value
+// stays below 2); clamped to [-126, 126] so 2^s and 2^-s are normal fp32.
+__device__ __forceinline__ int chunk_prescale(uint32_t amax_bits) {
+  const int e = (int)(amax_bits >> 7);  // biased exponent field (255: inf / NaN)
+  int s = e == 0 ? 126 : 141 - e;       // 14 - (e - 127)
+  return s < -126 ? -126 : (s > 126 ? 126 : s);
+}
+__device__ __forceinline__ float pow2f(int s) { return __uint_as_float((uint32_t)(s + 127) << 23); }
+
+// Eight bf16 (four dwords, element 2i in the low half of dword i), times
+// 2^s, to fp16 in the decode order 0,2,4,6,1,3,5,7.
+__device__ __forceinline__ v4i x8_to_f16(v4i v, float scale) {
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = bf16_to_f32((uint32_t)v[e] & 0xFFFFu) * scale;
+    f[2 * e + 1] = bf16_to_f32((uint32_t)v[e] >> 16) * scale;
+  }
+  const v8h h = v8h{(_Float16)f[0], (_Float16)f[2], (_Float16)f[4], (_Float16)f[6],
+                    (_Float16)f[1], (_Float16)f[3], (_Float16)f[5], (_Float16)f[7]};
+  return __builtin_bit_cast(v4i, h);
+}
+
 struct LutArgs {
   int64_t M, N, K;
   int32_t group;
@@ -71,131 +108,30 @@ struct LutArgs {
   const uint8_t* idx;    // [N][K/2]
   const uint16_t* cent;  // [N][K/group][16] fp16
   float* y;              // [M][N]
-  float* part;           // [splits][M][N]
+  float* part;           // [splits][M][N] fp32 partial tiles (splits > 1)
+  uint32_t* counters;    // one arrival counter per output tile (splits > 1), zero between calls
   int32_t chunks_per_split;  // 128-element chunks of K per workgroup
-  int32_t split;
+  int32_t splits;
 };
 
-// Workgroup: NW waves x 16 rows of W each; 16*TM rows of x; KR chunks of 128
-// along K (one split).
-template <int TM, int NW, int KR>
-__global__ __launch_bounds__(64 * NW) void k_lut_gemm(const LutArgs p) {
-  constexpr int XR = 16 * TM;
-  constexpr int LDX = KR * 128 * 2 + 16;  // LDS bytes per x row (16-byte pad)
-  __shared__ __attribute__((aligned(16))) uint8_t xs[XR * LDX];
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r16 = lane & 15, q = lane >> 4;
-  const int64_t n0 = ((int64_t)blockIdx.x * NW + wave) * 16;
-  const int64_t m0 = (int64_t)blockIdx.z * XR;
-  const int c0 = blockIdx.y * p.chunks_per_split;
-  const int nc = min((int)(p.K / 128) - c0, p.chunks_per_split);
-  const int64_t G = p.K / p.group;
-
-  // --- weight slice: all loads issued up front --------------------------
-  int64_t n = n0 + r16;
-  n = n < p.N ? n : p.N - 1;
-  v4i iq[KR], ca[KR], cb[KR];
-#pragma unroll
-  for (int c = 0; c < KR; ++c) {
-    const int cc = c0 + (c < nc ? c : nc - 1);
-    const int64_t k = (int64_t)cc * 128 + 32 * q;  // this lane's first element
-    iq[c] = load16(p.idx + n * (p.K / 2) + k / 2);
-    const uint16_t* t = p.cent + (n * G + k / p.group) * 16;
-    ca[c] = load16(t);
-    cb[c] = load16(t + 8);
-  }
-
-  // --- x range -> LDS as fp16, 8-element chunks in order 0,2,4,6,1,3,5,7 --
-  // all global loads first (one round trip), then convert and store
-  constexpr int XCH = XR * KR * 16;  // 8-element chunks
-  constexpr int PER = XCH / (64 * NW);
-  static_assert(XCH % (64 * NW) == 0, "x range must split evenly over the workgroup");
-  v4i xv[PER];
-  bool xok[PER];
-#pragma unroll
-  for (int t = 0; t < PER; ++t) {
-    const int u = threadIdx.x + t * 64 * NW;
-    const int row = u / (KR * 16), j = u % (KR * 16);
-    int64_t m = m0 + row;
-    xok[t] = m < p.M && j / 16 < nc;
-    m = m < p.M ? m : p.M - 1;
-    const int jj = j / 16 < nc ? j : j % 16;  // stay inside this split's range
-    xv[t] = load16(p.x + m * p.K + (int64_t)c0 * 128 + jj * 8);
-  }
-#pragma unroll
-  for (int t = 0; t < PER; ++t) {
-    const int u = threadIdx.x + t * 64 * NW;
-    const int row = u / (KR * 16), j = u % (KR * 16);
-    uint32_t o[4] = {0u, 0u, 0u, 0u};
-    if (xok[t]) {
-      const v4i v = xv[t];
-      float f[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f[2 * e] = bf16_to_f32((uint32_t)v[e] & 0xFFFFu);
-        f[2 * e + 1] = bf16_to_f32((uint32_t)v[e] >> 16);
-      }
-      const int ord[8] = {0, 2, 4, 6, 1, 3, 5, 7};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const _Float16 h0 = (_Float16)f[ord[2 * e]], h1 = (_Float16)f[ord[2 * e + 1]];
-        o[e] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-      }
-    }
-    *reinterpret_cast<v4i*>(xs + row * LDX + j * 16) = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-  }
-  __syncthreads();
-
-  v4f acc[TM];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-  for (int c = 0; c < KR; ++c) {
-    if (c < nc) {
-      uint32_t L[4], H[4];
-      split_table(ca[c], cb[c], L, H);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        uint32_t o[4];
-        decode8((uint32_t)iq[c][s], L, H, o);
-        const v8h bfrag = __builtin_bit_cast(v8h, v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]});
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const v4i xa = *reinterpret_cast<const v4i*>(xs + (16 * i + r16) * LDX + (c * 128 + 32 * q + 8 * s) * 2);
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, xa), bfrag, acc[i], 0, 0, 0);
-        }
-      }
-    }
-  }
-
-  const int64_t nn = n0 + r16;
-  if (nn >= p.N) return;
-  float* out = p.split ? p.part + (int64_t)blockIdx.y * p.M * p.N : p.y;
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t m = m0 + 16 * i + 4 * q + r;
-      if (m < p.M) out[m * p.N + nn] = acc[i][r];
-    }
-}
-
-// Decode shape (M <= 16): one workgroup per 16 output rows n over the whole
-// of K, so a call is one kernel with no partial sums in HBM.  Wave w takes
-// the 128-element chunks w, w + NW, ...; a lane (r16 = n, q) holds elements
-// [32q, 32q + 32) of a chunk as above.  Every weight load of a batch of CB
-// chunks is issued before the first is used, so a CU has all its weight
-// bytes in flight at once.  The x rows of the wave's chunks (M x 128 each)
-// are converted once, by the wave that uses them, into its own LDS slice
-// (fp16, decode order); rows >= M of that slice are never written and feed
-// only output rows that are never stored.  The NW per-wave 16 x 16 partial
-// products are summed in LDS in wave order (a fixed order: repeatable).
+// ---------------------------------------------------------------------------
+// M <= 16: one workgroup per 16 output rows n over the whole of K
+// ---------------------------------------------------------------------------
+// Wave w takes the 128-element chunks w, w + NW, ...; a lane (r16 = n, q)
+// holds elements [32q, 32q + 32) of a chunk and feeds them to four
+// v_mfma_f32_16x16x32_f16 steps.  Every weight load of a batch of CB chunks is
+// issued before the first is used, so a CU has all its weight bytes in flight
+// at once.  The x rows of the wave's chunks (M x 128 each) are converted once,
+// by the wave that uses them, into its own LDS slice (16 lanes per row, the
+// chunk's prescale from a 16-lane maximum); rows >= M of that slice are never
+// written and feed only output rows that are never stored.  The NW per-wave
+// 16 x 16 partial products are summed in LDS in wave order (a fixed order:
+// repeatable).
 template <int NW, int CB>
 __global__ __launch_bounds__(64 * NW) void k_lut_gemv(const LutArgs p) {
   constexpr int XROW = 128 * 2 + 16;  // LDS bytes per x row in a chunk slot (16-byte pad)
   __shared__ __attribute__((aligned(16))) uint8_t xs[NW][CB][16 * XROW];
+  __shared__ __attribute__((aligned(16))) float invs[NW][CB][16];
   __shared__ float red[NW][256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
@@ -204,6 +140,7 @@ __global__ __launch_bounds__(64 * NW) void k_lut_gemv(const LutArgs p) {
   const int chunks = (int)(p.K / 128);
   const int64_t G = p.K / p.group;
   const int M = (int)p.M;
+  const int xrounds = (M * 16 + 63) / 64;  // rounds of 64 pieces (16 lanes per row)
   const uint8_t* wr = p.idx + n * (p.K / 2);
   const uint16_t* cr = p.cent + n * G * 16;
 
@@ -220,24 +157,22 @@ __global__ __launch_bounds__(64 * NW) void k_lut_gemv(const LutArgs p) {
       ca[b] = load16(t);
       cc[b] = load16(t + 8);
     }
-    // x: M rows x 128 of each chunk, 16 pieces of 8 per row -> fp16 in the
-    // order 0,2,4,6,1,3,5,7 into this wave's slot
+    // x: M rows x 128 of each chunk, 16 pieces of 8 per row -> prescaled fp16
+    // in the order 0,2,4,6,1,3,5,7 into this wave's slot
 #pragma unroll
     for (int b = 0; b < CB; ++b) {
       const int c0 = cb0 + NW * b;
       const int c = c0 < chunks ? c0 : chunks - 1;
-      for (int u = lane; u < M * 16; u += 64) {
+      for (int t = 0; t < xrounds; ++t) {
+        const int u = lane + 64 * t;
         const int m = u >> 4, j = u & 15;
-        const v4i v = load16(p.x + (int64_t)m * p.K + (int64_t)c * 128 + 8 * j);
-        float f[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          f[2 * e] = bf16_to_f32((uint32_t)v[e] & 0xFFFFu);
-          f[2 * e + 1] = bf16_to_f32((uint32_t)v[e] >> 16);
+        const bool ok = m < M;  // the same for all 16 lanes of a DPP row
+        const v4i v = ok ? load16(p.x + (int64_t)m * p.K + (int64_t)c * 128 + 8 * j) : v4i{0, 0, 0, 0};
+        const int s = chunk_prescale(row16_max_u32(bf16x8_absmax_bits(v)));
+        if (ok) {
+          *reinterpret_cast<v4i*>(&xs[wave][b][m * XROW + 16 * j]) = x8_to_f16(v, pow2f(s));
+          if (j == 0) invs[wave][b][m] = pow2f(-s);
         }
-        const v8h h = v8h{(_Float16)f[0], (_Float16)f[2], (_Float16)f[4], (_Float16)f[6],
-                          (_Float16)f[1], (_Float16)f[3], (_Float16)f[5], (_Float16)f[7]};
-        *reinterpret_cast<v8h*>(&xs[wave][b][m * XROW + 16 * j]) = h;
       }
     }
 #pragma unroll
@@ -245,14 +180,19 @@ __global__ __launch_bounds__(64 * NW) void k_lut_gemv(const LutArgs p) {
       if (cb0 + NW * b >= chunks) break;
       uint32_t L[4], H[4];
       split_table(ca[b], cc[b], L, H);
+      v4f part = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         uint32_t o[4];
         decode8((uint32_t)iq[b][s], L, H, o);
         const v8h bfrag = __builtin_bit_cast(v8h, v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]});
         const v8h afrag = *reinterpret_cast<const v8h*>(&xs[wave][b][r16 * XROW + (32 * q + 8 * s) * 2]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(afrag, bfrag, acc, 0, 0, 0);
+        part = __builtin_amdgcn_mfma_f32_16x16x32_f16(afrag, bfrag, part, 0, 0, 0);
       }
+      // part[r]: x row 4q + r; undo that row's prescale for this chunk
+      const v4f inv = *reinterpret_cast<const v4f*>(&invs[wave][b][4 * q]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] += part[r] * inv[r];
     }
   }
   // acc[r]: x row 4q + r, output row n0 + r16
@@ -270,38 +210,192 @@ __global__ __launch_bounds__(64 * NW) void k_lut_gemv(const LutArgs p) {
   }
 }
 
-constexpr int kGemvNW = 16, kGemvCB = 2;
+// ---------------------------------------------------------------------------
+// M > 16: 64 output columns x 32*MT rows of x per workgroup, K split S ways
+// ---------------------------------------------------------------------------
+// Eight waves: two blocks of 32 output columns (n) x four K groups.  The
+// workgroup owns one range of the K chunks (split blockIdx.y of S); K group
+// g takes its chunks g, g + 4, ... .  Per round of four chunks (one per K
+// group) the two waves of a K group convert that chunk's x rows into the
+// group's LDS slot (prescaled fp16, 16 lanes per row), barrier; then each
+// wave contracts its 32 columns: v_mfma_f32_32x32x16_f16, lane l holding
+// column (or x row) l % 32 and, in step s, elements 64(l/32) + 8s .. + 7 of
+// the chunk for A and B alike, eight steps per chunk into a zeroed
+// accumulator that joins the running sum through the rows' inverse
+// prescales; barrier.  The four K groups' sums meet in LDS in group order.
+// With S > 1 every workgroup writes its tile to a partial slab; the last of
+// the tile's S workgroups to arrive (an atomic counter per tile) adds the
+// slabs in split order -- a fixed order whatever the arrival order, so the
+// result is bitwise repeatable -- writes y and resets the counter.  The
+// partial tiles of one call are written and read back within it, mostly
+// from L2.
+template <int MT>
+__global__ __launch_bounds__(512) void k_lut_gemm(const LutArgs p) {
+  constexpr int XR = 32 * MT;          // x rows per tile
+  constexpr int XROW = 128 * 2 + 16;   // LDS bytes per x row of a chunk slot
+  constexpr int XSB = 4 * XR * XROW;   // the four slots
+  constexpr int REDB = 8 * MT * 16 * 64 * 4;  // per-wave partial sums
+  __shared__ __attribute__((aligned(16))) uint8_t smem[XSB > REDB ? XSB : REDB];
+  __shared__ __attribute__((aligned(16))) float invs[4][XR];
+  __shared__ int s_last;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nb = wave & 1, kg = wave >> 1;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int64_t ntile0 = (int64_t)blockIdx.x * 64;
+  const int64_t n0 = ntile0 + 32 * nb;
+  const int64_t m0 = (int64_t)blockIdx.z * XR;
+  const int chunks = (int)(p.K / 128);
+  const int cs0 = blockIdx.y * p.chunks_per_split;
+  const int nc = min(chunks - cs0, p.chunks_per_split);  // >= 1: the host makes no empty split
+  const int rounds = (nc + 3) / 4;
+  const int64_t G = p.K / p.group;
+  const int64_t n = n0 + l32 < p.N ? n0 + l32 : p.N - 1;
+  uint8_t* const xs = smem + kg * XR * XROW;
 
-// splits of K: enough workgroups for every CU, at most one resident round
-static int lut_splits(int64_t M, int64_t N, int64_t K, int nw, int kr_max) {
-  const int64_t tiles = cdiv(N, 16 * nw) * cdiv(M, 64);
-  const int chunks = (int)(K / 128);
-  int splits = (int)cdiv(chunks, kr_max);
-  const int64_t slots = 2 * (int64_t)device_cu_count();
-  while ((int64_t)(splits + 1) * tiles <= slots && splits < chunks) ++splits;
-  const int per = (int)cdiv(chunks, splits);
-  return (int)cdiv(chunks, per);
+  v16f acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = v16f{};
+
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int cl = 4 * rd + kg;  // chunk of the range for this K group
+    const bool has = cl < nc;    // the same for both waves of the group
+    const int c = cs0 + (has ? cl : nc - 1);
+    // weights of this wave's chunk: the lane's 64 indices, its table(s)
+    const uint8_t* ir = p.idx + n * (p.K / 2) + (int64_t)c * 64 + 32 * h;
+    const v4i iq0 = load16(ir), iq1 = load16(ir + 16);
+    const int64_t g0 = ((int64_t)c * 128 + 64 * h) / p.group;  // table of elements 64h .. 64h + 31
+    const int64_t g1 = ((int64_t)c * 128 + 64 * h + 32) / p.group;
+    const uint16_t* t0 = p.cent + (n * G + g0) * 16;
+    const uint16_t* t1 = p.cent + (n * G + g1) * 16;
+    const v4i ta0 = load16(t0), tb0 = load16(t0 + 8);
+    const v4i ta1 = load16(t1), tb1 = load16(t1 + 8);  // the same table unless group == 32
+    // x: XR rows x 16 pieces of this K group's chunk over its 128 lanes
+    constexpr int XP = XR * 16 / 128;  // pieces per lane
+    v4i xv[XP];
+#pragma unroll
+    for (int t = 0; t < XP; ++t) {
+      const int u = nb * 64 + lane + 128 * t;
+      const int64_t m = m0 + (u >> 4);
+      xv[t] = m < p.M ? load16(p.x + m * p.K + (int64_t)c * 128 + 8 * (u & 15)) : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int t = 0; t < XP; ++t) {
+      const int u = nb * 64 + lane + 128 * t;
+      const int r = u >> 4, j = u & 15;
+      const int s = chunk_prescale(row16_max_u32(bf16x8_absmax_bits(xv[t])));
+      *reinterpret_cast<v4i*>(xs + r * XROW + 16 * j) = x8_to_f16(xv[t], pow2f(s));
+      if (j == 0) invs[kg][r] = pow2f(-s);
+    }
+    __syncthreads();
+    if (has) {
+      uint32_t L0[4], H0[4], L1[4], H1[4];
+      split_table(ta0, tb0, L0, H0);
+      split_table(ta1, tb1, L1, H1);
+      const uint32_t wd[8] = {(uint32_t)iq0[0], (uint32_t)iq0[1], (uint32_t)iq0[2], (uint32_t)iq0[3],
+                              (uint32_t)iq1[0], (uint32_t)iq1[1], (uint32_t)iq1[2], (uint32_t)iq1[3]};
+      v8h bf[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        uint32_t o[4];
+        if (s < 4)
+          decode8(wd[s], L0, H0, o);
+        else
+          decode8(wd[s], L1, H1, o);
+        bf[s] = __builtin_bit_cast(v8h, v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]});
+      }
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        v16f part = v16f{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const v8h af = *reinterpret_cast<const v8h*>(xs + (32 * i + l32) * XROW + (64 * h + 8 * s) * 2);
+          part = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[s], part, 0, 0, 0);
+        }
+        // part[r]: x row 32i + 8(r/4) + 4h + r%4
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v4f inv = *reinterpret_cast<const v4f*>(&invs[kg][32 * i + 8 * q + 4 * h]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][4 * q + r] += part[4 * q + r] * inv[r];
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // the four K groups' sums, in group order
+  float* red = reinterpret_cast<float*>(smem);  // [wave][MT][16][64]
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[((wave * MT + i) * 16 + r) * 64 + lane] = acc[i][r];
+  __syncthreads();
+  constexpr int OUTS = 2 * MT * 16 * 64;  // outputs of the tile (2 column blocks)
+  constexpr int PER = OUTS / 512;
+  float v[PER];
+  int64_t om[PER], on[PER];
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    const int o = (int)threadIdx.x + 512 * t;
+    const int ob = o / (MT * 1024), rem = o % (MT * 1024);  // column block, then (i, r, lane)
+    const int i = rem / 1024, r = (rem / 64) % 16, l = rem % 64;
+    float sum = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) sum += red[(((2 * g + ob) * MT + i) * 16 + r) * 64 + l];
+    v[t] = sum;
+    om[t] = m0 + 32 * i + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+    on[t] = ntile0 + 32 * ob + (l & 31);
+  }
+  if (p.splits == 1) {
+#pragma unroll
+    for (int t = 0; t < PER; ++t)
+      if (om[t] < p.M && on[t] < p.N) p.y[om[t] * p.N + on[t]] = v[t];
+    return;
+  }
+  const int64_t MN = p.M * p.N;
+#pragma unroll
+  for (int t = 0; t < PER; ++t)
+    if (om[t] < p.M && on[t] < p.N) p.part[(int64_t)blockIdx.y * MN + om[t] * p.N + on[t]] = v[t];
+  __threadfence();  // this thread's partial tile is visible device-wide before the arrival below
+  __syncthreads();
+  uint32_t* const cnt = p.counters + (int64_t)blockIdx.z * gridDim.x + blockIdx.x;
+  if (threadIdx.x == 0) s_last = atomicAdd(cnt, 1u) == (uint32_t)(p.splits - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();  // the other splits' tiles, published before their arrivals, are visible now
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    if (om[t] >= p.M || on[t] >= p.N) continue;
+    const int64_t off = om[t] * p.N + on[t];
+    float sum = 0.f;
+    for (int sp = 0; sp < p.splits; ++sp) sum += sp == (int)blockIdx.y ? v[t] : p.part[(int64_t)sp * MN + off];
+    p.y[off] = sum;
+  }
+  if (threadIdx.x == 0) *cnt = 0u;  // ready for the next call
 }
 
-constexpr int kLutNW = 8;
-constexpr int kLutKR = 4;
+constexpr int kGemvNW = 16, kGemvCB = 2;
+
+// K splits for the M > 16 kernel: about one workgroup per CU over all tiles,
+// each K group with at least one chunk when K allows it
+static int lut_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = cdiv(N, 64) * cdiv(M, 64);
+  const int chunks = (int)(K / 128);
+  const int most = chunks / 4 > 1 ? chunks / 4 : 1;
+  int64_t s = cdiv(device_cu_count(), tiles);
+  s = s < 1 ? 1 : (s > most ? most : s);
+  const int per = (int)cdiv(chunks, s);
+  return (int)cdiv(chunks, per);  // no empty split
+}
+
+static size_t lut_counter_bytes(int64_t M, int64_t N) {
+  return (size_t)cdiv(cdiv(N, 64) * cdiv(M, 64) * 4, 256) * 256;
+}
 
 size_t ws_lut_gemm(int64_t M, int64_t N, int64_t K) {
   if (M <= 16 || N <= 0 || K <= 0 || K % 128) return 0;  // M <= 16: one kernel, no partials
-  const int splits = lut_splits(M, N, K, kLutNW, kLutKR);
-  return splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
-}
-
-template <int TM>
-static int launch_lut(LutArgs& p, int splits, hipStream_t st) {
-  p.chunks_per_split = (int)cdiv(p.K / 128, splits);
-  p.split = splits > 1;
-  hipLaunchKernelGGL((k_lut_gemm<TM, kLutNW, kLutKR>),
-                     dim3((unsigned)cdiv(p.N, 16 * kLutNW), (unsigned)splits, (unsigned)cdiv(p.M, 16 * TM)),
-                     dim3(64 * kLutNW), 0, st, p);
-  int s = check_launch("lut_gemm");
-  if (s || splits == 1) return s;
-  return launch_splitk_reduce(p.part, splits, p.M * p.N, p.y, st);
+  const int splits = lut_splits(M, N, K);
+  return splits > 1 ? lut_counter_bytes(M, N) + (size_t)splits * M * N * sizeof(float) : 0;
 }
 
 }  // namespace gbw
@@ -311,7 +405,7 @@ using namespace gbw;
 extern "C" int lut_gemm(int64_t M, int64_t N, int64_t K, int32_t group, const uint16_t* x_bf16, const uint8_t* idx,
                         const uint16_t* centroids_f16, float* y, int32_t flags, void* ws, size_t ws_bytes,
                         void* stream) {
-  (void)flags;
+  (void)flags;  // every path sums in a fixed order: results are bitwise repeatable
   if (M < 0 || N < 0 || K < 0) return fail(GBW_E_ARG, "lut_gemm: negative extent");
   if (group != 32 && group != 64 && group != 128)
     return fail(GBW_E_SHAPE, "lut_gemm: group must be 32, 64 or 128");
@@ -321,6 +415,8 @@ extern "C" int lut_gemm(int64_t M, int64_t N, int64_t K, int32_t group, const ui
   if (!x_bf16 || !idx || !centroids_f16 || !y) return fail(GBW_E_ARG, "lut_gemm: null pointer");
   if (!aligned16(x_bf16) || !aligned16(idx) || !aligned16(centroids_f16))
     return fail(GBW_E_ALIGN, "lut_gemm: x/idx/centroids not 16-byte aligned");
+  if (M > 16 && (int64_t)cdiv(N, 64) * cdiv(M, 64) > 0x7FFFFFFF)
+    return fail(GBW_E_SHAPE, "lut_gemm: too many output tiles");
   int st = check_device();
   if (st) return st;
   LutArgs p{};
@@ -332,23 +428,26 @@ extern "C" int lut_gemm(int64_t M, int64_t N, int64_t K, int32_t group, const ui
   p.idx = idx;
   p.cent = centroids_f16;
   p.y = y;
-  p.part = reinterpret_cast<float*>(ws);
   hipStream_t s = as_stream(stream);
   if (M <= 16) {
     hipLaunchKernelGGL((k_lut_gemv<kGemvNW, kGemvCB>), dim3((unsigned)cdiv(N, 16)), dim3(64 * kGemvNW), 0, s, p);
     return check_launch("lut_gemm");
   }
-  int splits = lut_splits(M, N, K, kLutNW, kLutKR);
-  const int need = (int)cdiv(K / 128, kLutKR);
-  if (splits > 1 && (!ws || ws_bytes < (size_t)splits * M * N * sizeof(float))) {
-    const int fit = ws ? (int)(ws_bytes / ((size_t)M * N * sizeof(float))) : 0;
-    if (fit >= need && fit >= 2)
-      splits = fit;
-    else if (need == 1)
-      splits = 1;
-    else
-      return fail(GBW_E_WORKSPACE, "lut_gemm: needs %zu bytes of workspace", ws_lut_gemm(M, N, K));
+  const int chunks = (int)(K / 128);
+  int splits = lut_splits(M, N, K);
+  // too little workspace for the partial tiles: one workgroup per tile over
+  // all of K (no workspace; slower, same results up to the summation order)
+  if (splits > 1 && (!ws || ws_bytes < ws_lut_gemm(M, N, K) || ((uintptr_t)ws & 15u))) splits = 1;
+  p.chunks_per_split = (int)cdiv(chunks, splits);
+  p.splits = splits;
+  if (splits > 1) {
+    p.counters = reinterpret_cast<uint32_t*>(ws);
+    p.part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + lut_counter_bytes(M, N));
   }
-  if (M <= 32) return launch_lut<2>(p, splits, s);
-  return launch_lut<4>(p, splits, s);
+  const dim3 grid((unsigned)cdiv(N, 64), (unsigned)splits, (unsigned)cdiv(M, M <= 32 ? 32 : 64));
+  if (M <= 32)
+    hipLaunchKernelGGL((k_lut_gemm<1>), grid, dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_lut_gemm<2>), grid, dim3(512), 0, s, p);
+  return check_launch("lut_gemm");
 }

@@ -1110,6 +1110,8 @@ extern "C" int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const in
       return fail(GBW_E_SHAPE, "moe_grouped_gemm: h_tail must be a multiple of 32, <= I, with E8M0 h codes");
   } else {
     if (N % 256) return fail(GBW_E_SHAPE, "moe_grouped_gemm: down rows (H) must be a multiple of 256");
+    if (e4m3 && w->ts_per_expert != 1)
+      return fail(GBW_E_ARG, "moe_grouped_gemm: E4M3/E5M3 down weights take one tensor scale per expert");
     if (a->rows < P) return fail(GBW_E_SHAPE, "moe_grouped_gemm: activation has fewer rows than pairs");
     if (T > 0 && !out->y) return fail(GBW_E_ARG, "moe_grouped_gemm: down needs y");
   }

@@ -119,7 +119,9 @@ typedef struct gbw_weight {
   const uint16_t* codebook;  /* VQ*: [E][N/qb][K/qb][256] keys, else NULL           */
   const float* tensor_scale; /* E4M3/E5M3 and their VQ forms: [E][ts_per_expert] fp32 */
   int32_t ts_per_expert;     /* E4M3/E5M3: rows split into this many equal segments,
-                                segment s scaled by tensor_scale[e][s] (1 or 2)     */
+                                segment s scaled by tensor_scale[e][s] (1 or 2;
+                                moe_grouped_gemm: 2 for the gate/up stage -- gate
+                                rows, up rows -- and 1 for the down stage)         */
   int32_t qblock;            /* VQ*: QBlock edge qb (64, 128 or 256; 0 means 64)    */
   const uint8_t* scale_codebook; /* *_PLUS: [E][256][8] scale codes, 4-byte
                                 aligned: block scales 8i .. 8i+7 of row n of
@@ -189,8 +191,12 @@ int mx_residual(const float* w, int64_t N, int64_t K, int64_t tail, const uint8_
 
 /* ---- dense GEMMs ---------------------------------------------------------
  * mx_gemm: y[M][N] fp32 = deq(a) deq(w)^T, a [M][K] and w [N][K] both
- * E8M0-B32 (scaled MFMA, FP4 x FP4).  K must be a multiple of 32.  y is
- * overwritten.  When the grid needs the reduction over K split across
+ * E8M0-B32 (scaled MFMA, FP4 x FP4): the W4A4 linear layer Y = X W of
+ * PRQuant: Permutation Residual Quantization for Low-Overhead Inference,
+ * §4 Eq. (1) (with the permutation and scaling already folded into the
+ * operands), on the E8M0-B32-FP4 format of MXCode: MX-Native Codebook
+ * Quantization, Table 1; deq() decodes each element as e2m1 * 2^(scale-127).
+ * K must be a multiple of 32.  y is overwritten.  When the grid needs the reduction over K split across
  * workgroups, the split partials go to the workspace
  * (gbw_workspace_size(GBW_OP_MX_GEMM, M, N, K [+ tail], 0) bytes) and are
  * summed in split order by a second kernel; with a smaller or NULL workspace
@@ -213,16 +219,33 @@ int residual_tail_gemm(int64_t M, const gbw_act* a, const gbw_weight* w, const g
  * Fig. 1 stage 3-4, Fig. 4):
  *   y[m][n] = sum_k bf16(x[m][k]) * fp16(centroids[n][k/group][idx[n][k]])
  * x [M][K] bf16 bits, idx [N][K/2] 4-bit indices, centroids [N][K/group][16]
- * fp16 bits, y [M][N] fp32.  group in {32, 64, 128}, K % group == 0.
- * ws: gbw_workspace_size(GBW_OP_LUT_GEMM, M, N, K, 0) bytes (may be 0). */
+ * fp16 bits, y [M][N] fp32 (overwritten).  group in {32, 64, 128},
+ * K % 128 == 0.  Any finite bf16 x: each 128-element chunk of an x row is
+ * scaled by a power of two into fp16's range for the fp16 matrix cores and
+ * the chunk's partial sum is scaled back (both exact).
+ * ws: gbw_workspace_size(GBW_OP_LUT_GEMM, M, N, K, 0) bytes (0 for M <= 16),
+ * 16-byte aligned.  For M > 16 the reduction over K is split across
+ * workgroups: each writes a partial tile into ws and the last of a tile's
+ * workgroups to arrive (a counter per output tile at the start of ws) sums
+ * them in a fixed order, so results are bitwise repeatable.  Those counters
+ * must be zero before the first call with a workspace and every completed
+ * call leaves them zero: zero the workspace once, then reuse it.  Calls that
+ * share a workspace must not overlap in time.  With a smaller or NULL
+ * workspace one workgroup covers all of K per tile (slower, no workspace). */
 int lut_gemm(int64_t M, int64_t N, int64_t K, int32_t group, const uint16_t* x_bf16,
              const uint8_t* idx, const uint16_t* centroids_f16, float* y, int32_t flags,
              void* ws, size_t ws_bytes, void* stream);
 
 /* ---- MoE ------------------------------------------------------------------
- * moe_route: logits [T][E] fp32 -> top-k experts per token (largest logit
- * first, ties to the lower expert id), weights softmax-renormalised over the
- * k chosen, and the pair list sorted by (expert, token):
+ * moe_route: the router of the mixture-of-experts FFNs whose experts the
+ * pages quantize (CodeQuant Fig. 1-2: clustered weights in the MoE experts;
+ * PRQuant §4 applies to the routed experts' down projections).  The pages do
+ * not spell the router out; this is the top-k softmax routing their MoE
+ * models use, read as: logits [T][E] fp32 -> top-k experts per token
+ * (largest logit first, ties to the lower expert id; -0 ties +0, NaN ranks
+ * after every number), weights exp(l_j - l_max) normalised over the k chosen
+ * (a reading: the softmax is taken over the chosen k), and the pair list
+ * sorted by (expert, token):
  *   topk_ids [T][k] i32, topk_w [T][k] f32, expert_offsets [E+1] i32,
  *   pair_token [T*k] i32, pair_pos [T][k] i32 (index of the pair in the list).
  * E <= 1024, 1 <= k <= min(E, 16).  ws: gbw_workspace_size(GBW_OP_MOE_ROUTE, T, E, 0, 0). */

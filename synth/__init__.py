@@ -72,6 +72,25 @@ def dense_linear(M, N, K, seed=0, device="cpu"):
     return dict(x=x, w=w)
 
 
+def random_codes(rows, K, seed, name, device="cpu"):
+    """Packed E2M1 codes [rows][K/2]: every byte uniform over 0 .. 255."""
+    g = _gen(seed, name, device)
+    return torch.randint(0, 256, (rows, K // 2), generator=g, device=device, dtype=torch.uint8)
+
+
+def paired_scale_codes(M, N, K, seed, name, device="cpu", block=32):
+    """E8M0 block scale codes over 1 .. 253 for an [M][K] activation and an
+    [N][K] weight: per K block a base b drawn from 1 .. 119, activation codes
+    b + (0 .. 7) and weight codes 254 - b - (0 .. 7), so a low activation scale
+    meets a high weight scale in every block and each product of two scales
+    stays within 2^-7 .. 2^7."""
+    nb = K // block
+    base = 1 + (uniform((nb,), seed, f"{name}.base", device) * 119).to(torch.int32).clamp(max=118)
+    da = (uniform((M, 1), seed, f"{name}.da", device) * 8).to(torch.int32).clamp(max=7)
+    dw = (uniform((N, 1), seed, f"{name}.dw", device) * 8).to(torch.int32).clamp(max=7)
+    return (base[None, :] + da).to(torch.uint8), (254 - base[None, :] - dw).to(torch.uint8)
+
+
 # ----------------------------------------------------------------------------
 # Tail-residual down projection
 # ----------------------------------------------------------------------------
@@ -178,13 +197,16 @@ def moe_problem(T, H, I, E, seed=0, device="cpu"):
 _E2M1_MAG_PROBS = [0.08, 0.15, 0.15, 0.14, 0.18, 0.16, 0.10, 0.04]
 
 
-def _scale_codes(shape, seed, name, device, scale_fmt="e8m0"):
+def _scale_codes(shape, seed, name, device, scale_fmt="e8m0", e8m0_range=None):
     """Block scale codes.  E8M0: {119, 120, 121} (weights of magnitude
-    ~0.02), 1:2:1.  E4M3 / UE5M3 (beside an FP32 tensor scale that maps the
-    largest block to the top of the scale range): uniform over the codes of
-    the upper three binades, 64 .. 448 (E4M3 0x68-0x7E) and 16384 .. 114688
-    (UE5M3 0xE8-0xFE)."""
+    ~0.02), 1:2:1, or uniform over e8m0_range = (lo, hi) inclusive.  E4M3 /
+    UE5M3 (beside an FP32 tensor scale that maps the largest block to the top
+    of the scale range): uniform over the codes of the upper three binades,
+    64 .. 448 (E4M3 0x68-0x7E) and 16384 .. 114688 (UE5M3 0xE8-0xFE)."""
     u = uniform(shape, seed, name, device)
+    if scale_fmt == "e8m0" and e8m0_range is not None:
+        lo, hi = e8m0_range
+        return (lo + torch.clamp((u * (hi - lo + 1)).to(torch.int32), max=hi - lo)).to(torch.uint8)
     if scale_fmt == "e8m0":
         return (119 + (u >= 0.25).to(torch.uint8) + (u >= 0.75).to(torch.uint8)).to(torch.uint8)
     lo = {"e4m3": 0x68, "e5m3": 0xE8}[scale_fmt]
@@ -197,7 +219,7 @@ VQ_TENSOR_SCALE = {"e4m3": 0.1 / 2688.0, "e5m3": 0.1 / 688128.0}
 
 
 def vq_weight(E, N, K, qblock=64, n_entries=256, seed=0, name="vq", device="cpu", scales="prescale",
-              scale_fmt="e8m0", ts_segments=1):
+              scale_fmt="e8m0", ts_segments=1, e8m0_range=None):
     """Codebook->MX weights drawn directly in the VQ format.
 
     idx uint8 [E][N][K/4]; codebook 16-bit [E][N/qblock][K/qblock][256]
@@ -210,6 +232,8 @@ def vq_weight(E, N, K, qblock=64, n_entries=256, seed=0, name="vq", device="cpu"
                        per-matrix table ``scale_codebook`` uint8 [E][256][8] of
                        scale codes (8 consecutive block scales along K each).
     "e4m3" / "e5m3" also give ``tensor_scale`` fp32 [E][ts_segments].
+    ``e8m0_range`` = (lo, hi): E8M0 scale codes uniform over lo .. hi instead
+    of the {119, 120, 121} of N(0, 0.02^2) weights.
     """
     assert N % qblock == 0 and K % qblock == 0
     probs = torch.tensor(_E2M1_MAG_PROBS, dtype=torch.float64)
@@ -226,14 +250,15 @@ def vq_weight(E, N, K, qblock=64, n_entries=256, seed=0, name="vq", device="cpu"
     out = dict(idx=idx, codebook=codebook.contiguous())
     b = 32 if scale_fmt == "e8m0" else 16
     if scales == "prescale":
-        out["scales"] = _scale_codes((E, N, K // b), seed, f"{name}.scale", device, scale_fmt)
+        out["scales"] = _scale_codes((E, N, K // b), seed, f"{name}.scale", device, scale_fmt, e8m0_range)
     elif scales == "postscale":
-        out["scales"] = _scale_codes((E, N // qblock, K // qblock), seed, f"{name}.qscale", device, scale_fmt)
+        out["scales"] = _scale_codes((E, N // qblock, K // qblock), seed, f"{name}.qscale", device, scale_fmt,
+                                     e8m0_range)
     elif scales == "prescale_plus":
         assert K % (8 * b) == 0
         g = _gen(seed, f"{name}.sidx", device)
         out["scales"] = torch.randint(0, 256, (E, N, K // (8 * b)), generator=g, device=device, dtype=torch.uint8)
-        out["scale_codebook"] = _scale_codes((E, 256, 8), seed, f"{name}.scb", device, scale_fmt)
+        out["scale_codebook"] = _scale_codes((E, 256, 8), seed, f"{name}.scb", device, scale_fmt, e8m0_range)
     else:
         raise ValueError(scales)
     if scale_fmt != "e8m0":
@@ -242,15 +267,18 @@ def vq_weight(E, N, K, qblock=64, n_entries=256, seed=0, name="vq", device="cpu"
     return out
 
 
-def moe_vq_problem(T, H, I, E, seed=0, device="cpu", scales="prescale", qblock=64, scale_fmt="e8m0"):
-    """X bf16 [T][H], logits [T][E], VQ gate/up weights (N = 2I, K = H; with
-    16-element blocks, tensor scales per gate and up half) and VQ down
+def moe_vq_problem(T, H, I, E, seed=0, device="cpu", scales="prescale", qblock=64, scale_fmt="e8m0",
+                   x_log2=0, gate_up_e8m0_range=None):
+    """X bf16 [T][H] (times 2^x_log2), logits [T][E], VQ gate/up weights
+    (N = 2I, K = H; with 16-element blocks, tensor scales per gate and up
+    half; E8M0 scale codes over gate_up_e8m0_range if given) and VQ down
     weights (N = H, K = I); ``scales``, ``qblock``, ``scale_fmt`` as in
     vq_weight."""
-    x = normal((T, H), 1.0, seed, "moevq.x", device).to(torch.bfloat16)
+    x = normal((T, H), 1.0, seed, "moevq.x", device)
+    x = (x * 2.0 ** x_log2 if x_log2 else x).to(torch.bfloat16)
     logits = normal((T, E), 1.0, seed, "moevq.logits", device)
     gu = vq_weight(E, 2 * I, H, qblock=qblock, seed=seed, name="moevq.gate_up", device=device, scales=scales,
-                   scale_fmt=scale_fmt, ts_segments=2)
+                   scale_fmt=scale_fmt, ts_segments=2, e8m0_range=gate_up_e8m0_range)
     dn = vq_weight(E, H, I, qblock=qblock, seed=seed, name="moevq.down", device=device, scales=scales,
                    scale_fmt=scale_fmt)
     return dict(x=x, logits=logits, gate_up=gu, down=dn)

@@ -1,4 +1,7 @@
-// CPU bounds check of lut_gemm (every buffer an exact-size heap block).
+// CPU bounds check of lut_gemm (every buffer an exact-size heap block): the
+// call with the full workspace twice (the arrival counters must be back at
+// zero after each call), then with a workspace one byte short (the no-split
+// path).
 #include <hip/hip_runtime.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -33,9 +36,22 @@ int main(int argc, char** argv) {
   uint8_t* idx = mk(N * K / 2);
   uint16_t* cent = (uint16_t*)mk(N * (K / group) * 16 * 2);
   float* y = (float*)mk(M * N * 4);
-  size_t wsb = gbw::ws_lut_gemm(M, N, K);
-  void* ws = wsb ? malloc(wsb) : nullptr;
-  int st = lut_gemm(M, N, K, group, x, idx, cent, y, 0, ws, wsb, nullptr);
-  printf("lut M=%lld N=%lld K=%lld g=%d ws=%zu status %d\n", (long long)M, (long long)N, (long long)K, group, wsb, st);
+  const size_t wsb = gbw::ws_lut_gemm(M, N, K);
+  uint8_t* ws = wsb ? (uint8_t*)calloc(wsb, 1) : nullptr;
+  for (int rep = 0; rep < 2; ++rep) {
+    int st = lut_gemm(M, N, K, group, x, idx, cent, y, 0, ws, wsb, nullptr);
+    size_t nonzero = 0;
+    // the counters sit at the front of the workspace, one dword per tile
+    const size_t tiles = (size_t)((N + 63) / 64) * ((M + 63) / 64);
+    for (size_t i = 0; wsb && i < tiles; ++i) nonzero += ((uint32_t*)ws)[i] != 0;
+    printf("lut M=%lld N=%lld K=%lld g=%d ws=%zu status %d counters left %zu\n", (long long)M, (long long)N,
+           (long long)K, group, wsb, st, nonzero);
+  }
+  if (wsb) {
+    uint8_t* shortws = (uint8_t*)calloc(wsb - 1, 1);
+    int st = lut_gemm(M, N, K, group, x, idx, cent, y, 0, shortws, wsb - 1, nullptr);
+    printf("short workspace status %d\n", st);
+    free(shortws);
+  }
   return 0;
 }

@@ -20,6 +20,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 #include <memory>
+#include <atomic>
 
 #define __global__
 #define __device__
@@ -52,6 +53,8 @@ extern std::mutex emu_atomic_mu;
 inline void unsafeAtomicAdd(float* p, float v) { std::lock_guard<std::mutex> g(emu_atomic_mu); *p += v; }
 inline unsigned long long atomicOr(unsigned long long* p, unsigned long long v) { std::lock_guard<std::mutex> g(emu_atomic_mu); auto o = *p; *p |= v; return o; }
 template <class T> inline T __shfl_xor(T v, int) { return v; }
+inline unsigned atomicAdd(unsigned* p, unsigned v) { std::lock_guard<std::mutex> g(emu_atomic_mu); auto o = *p; *p += v; return o; }
+inline void __threadfence() { std::atomic_thread_fence(std::memory_order_seq_cst); }
 
 #define __builtin_amdgcn_readfirstlane(x) (x)
 // DPP: the 64 lanes of a wave exchange through a per-wave array (all lanes
@@ -63,6 +66,7 @@ inline int emu_dpp_src(int lane, int ctrl) {
   if (ctrl <= 0xFF) return (lane & ~3) | ((ctrl >> (2 * (lane & 3))) & 3);     // quad_perm
   if (ctrl == 0x140) return row | (15 - r);                                      // row_mirror
   if (ctrl == 0x141) return row | ((r & 8) | (7 - (r & 7)));                     // row_half_mirror
+  if (ctrl > 0x120 && ctrl <= 0x12F) return row | ((r - (ctrl - 0x120)) & 15);   // row_ror:n
   fprintf(stderr, "emu: unsupported dpp ctrl %x\n", ctrl); abort();
 }
 inline int emu_dpp(int v, int ctrl) {

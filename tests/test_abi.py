@@ -129,6 +129,15 @@ def test_moe_validation(gbw):
     assert call(0, 0, a16, w, out) == 0
     a16.fmt = gbw.FMT_E5M3_B16
     assert call(0, 0, a16, w, out) == 4                            # scale formats must agree
+    # E4M3-B16 down weights: one tensor scale per expert (two segments would
+    # give the lower output rows the wrong scale)
+    a16.fmt = gbw.FMT_E4M3_B16
+    wd = gbw._Weight(gbw.FMT_E4M3_B16, E, H, I, 0x5000, 0x6000, None, 0x9000, 2, 0, None)
+    a16.K = I
+    a16.rows = 16
+    assert call(1, 0, a16, wd, out) == 1
+    wd.ts_per_expert = 1
+    assert call(1, 0, a16, wd, out) == 0
 
 
 def test_descriptor_layouts_match_the_header(gbw, tmp_path):

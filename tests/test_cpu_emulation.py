@@ -92,11 +92,16 @@ def test_moe_route_in_bounds_and_exact(build_dir, T, E, K, mode):
     assert "status 0 mismatched ids 0 mismatched pairs 0" in out, out
 
 
-@pytest.mark.parametrize("M,N,K,group", [(1, 40, 384, 32), (5, 256, 1024, 128), (17, 40, 384, 32), (64, 128, 2048, 128)])
+@pytest.mark.parametrize("M,N,K,group", [(1, 40, 384, 32), (5, 256, 1024, 128), (17, 40, 384, 32), (64, 128, 2048, 128),
+                                         (70, 100, 1024, 64), (33, 64, 512, 32)])
 def test_lut_gemm_in_bounds(build_dir, M, N, K, group):
+    """Ragged M and N, every group size; for M > 16 the split-K path twice (its
+    arrival counters must be left at zero) and the no-workspace path."""
     exe = _build(build_dir, "lut_gemm.hip", "drv_lut.cpp", "emu_lut")
     out = _run(exe, M, N, K, group)
-    assert "status 0" in out, out
+    assert out.count("status 0 counters left 0") == 2, out
+    if M > 16 and " ws=0 " not in out:
+        assert "short workspace status 0" in out, out
 
 
 @pytest.mark.parametrize("M,N,K,tail", [(16, 512, 512, 0), (1, 40, 96, 0), (130, 72, 640, 64), (33, 40, 2048, 32),

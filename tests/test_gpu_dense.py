@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import oracle
+import oracle.native as on
 import synth
 from parity import assert_rows_close, banner, to_np, vq_ref_block_scales
 
@@ -123,7 +124,11 @@ def test_block_hadamard_gemm_parity_and_error():
     a = gbw.mx_quantize(x, gbw.FMT_E8M0_B32, rotate=True)
     wq = gbw.mx_quantize(w, gbw.FMT_E8M0_B32, rotate=True)
     y = to_np(gbw.mx_gemm(a, gbw.weight_from_act(wq))).astype(np.float64)
-    ref = oracle.mx_gemm(to_np(a.codes), to_np(a.scales), to_np(wq.codes), to_np(wq.scales))
+    ac, as_ = on.quantize_e8m0_b32(oracle.fwht32_fp32(x.float().cpu().numpy()))
+    wc, ws = on.quantize_e8m0_b32(oracle.fwht32_fp32(w.cpu().numpy()))
+    assert np.array_equal(to_np(a.codes), ac) and np.array_equal(to_np(wq.codes), wc)
+    assert np.array_equal(to_np(a.scales), as_) and np.array_equal(to_np(wq.scales), ws)
+    ref = on.mx_gemm(ac, as_, wc, ws)
     assert_rows_close(y, ref, what="rotated mx_gemm")
     y_plain = to_np(gbw.mx_gemm(gbw.mx_quantize(x, gbw.FMT_E8M0_B32),
                                 gbw.weight_from_act(gbw.mx_quantize(w, gbw.FMT_E8M0_B32)))).astype(np.float64)
@@ -286,11 +291,19 @@ def test_dequantize_vq_b16_bitexact(scale_fmt, scales, qblock, N, K):
 # ---------------------------------------------------------------------------
 
 def _dense_case(M, N, K, seed):
+    """GPU operands quantized by the library, the reference from the oracle's
+    own quantization of the same synthetic inputs (the codes agree bit for
+    bit)."""
     d = synth.dense_linear(M, N, K, seed=seed, device=DEV)
     a = gbw.mx_quantize(d["x"], gbw.FMT_E8M0_B32)
     wq = gbw.mx_quantize(d["w"], gbw.FMT_E8M0_B32)
     w = gbw.weight_from_act(wq)
-    ref = oracle.mx_gemm(to_np(a.codes), to_np(a.scales), to_np(wq.codes), to_np(wq.scales))
+    ac, as_ = on.quantize_e8m0_b32(d["x"].float().cpu().numpy())
+    wc, ws = on.quantize_e8m0_b32(d["w"].cpu().numpy())
+    assert np.array_equal(to_np(a.codes), ac) and np.array_equal(to_np(a.scales), as_)
+    assert np.array_equal(to_np(wq.codes), wc) and np.array_equal(to_np(wq.scales), ws)
+    ref = on.mx_gemm(ac, as_, wc, ws)
+    assert on.last_inexact == 0
     return a, w, ref
 
 
@@ -316,6 +329,27 @@ def test_mx_gemm_ragged(M, N, K):
     y = gbw.mx_gemm(a, w)
     assert torch.equal(y, gbw.mx_gemm(a, w))
     assert_rows_close(to_np(gbw.mx_gemm(a, w, ws=False)), ref, what="serial")
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 256, 1024), (9, 70, 96), (64, 512, 2048), (128, 2560, 9728),
+                                   (40, 100, 640)])
+def test_mx_gemm_wide_scale_codes(M, N, K):
+    """Random E2M1 codes with E8M0 scale codes over 1 .. 253: a low
+    activation scale against a high weight scale in every block (each product
+    of two scales within 2^+-7, so every sum is exact and finite).  Covers
+    the 16-row and 32-row kernels and the serial path."""
+    banner(f"mx_gemm wide scale codes {M}x{N}x{K}")
+    ac = synth.random_codes(M, K, 8, "wide.a")
+    wc = synth.random_codes(N, K, 8, "wide.w")
+    asc, wsc = synth.paired_scale_codes(M, N, K, 8, "wide.s")
+    ref = on.mx_gemm(ac.numpy(), asc.numpy(), wc.numpy(), wsc.numpy())
+    assert on.last_inexact == 0
+    A = _gpu_act(ac.numpy(), asc.numpy())
+    W = _gpu_w(wc.numpy(), wsc.numpy())
+    assert_rows_close(to_np(gbw.mx_gemm(A, W)), ref, what="wide-scale mx_gemm")
+    assert_rows_close(to_np(gbw.mx_gemm(A, W, ws=False)), ref, what="wide-scale mx_gemm serial")
+    print(f"[stats] scale codes a {int(asc.min())}..{int(asc.max())} w {int(wsc.min())}..{int(wsc.max())}",
+          flush=True)
 
 
 def test_mx_gemm_integer_special_case_bitexact():
@@ -353,8 +387,28 @@ def _tail_case(M, N, K, tail, seed=0):
 def test_mx_residual_bitexact():
     banner("mx_residual 256x2048 tail 256")
     p, a, wq, r, rq = _tail_case(8, 256, 2048, 256)
-    ref = oracle.residual_weight(to_np(p["w"]), to_np(wq.codes), to_np(wq.scales), 256)
+    wn = to_np(p["w"])
+    wc, ws = on.quantize_e8m0_b32(wn)
+    assert np.array_equal(to_np(wq.codes), wc) and np.array_equal(to_np(wq.scales), ws)
+    ref = oracle.residual_weight(wn, wc, ws, 256)
     assert np.array_equal(to_np(r), ref)
+
+
+def test_residual_tail_gemm_wide_scale_codes():
+    """The tail-residual GEMM on random codes whose E8M0 scales span 1 .. 253
+    (low activation scales against high weight and residual scales)."""
+    banner("residual_tail_gemm wide scale codes 128x512x2048 tail 256")
+    M, N, K, t = 128, 512, 2048, 256
+    ac = synth.random_codes(M, K, 9, "wt.a")
+    wc = synth.random_codes(N, K, 9, "wt.w")
+    rc = synth.random_codes(N, t, 9, "wt.r")
+    asc, wsc = synth.paired_scale_codes(M, N, K, 9, "wt.s")
+    rsc = wsc[:, -t // 32:].contiguous()        # the residual blocks carry the weight's tail scales
+    ref = on.residual_tail_gemm(ac.numpy(), asc.numpy(), wc.numpy(), wsc.numpy(), rc.numpy(), rsc.numpy(), t)
+    assert on.last_inexact == 0
+    A = _gpu_act(ac.numpy(), asc.numpy())
+    y = gbw.residual_tail_gemm(A, _gpu_w(wc.numpy(), wsc.numpy()), _gpu_w(rc.numpy(), rsc.numpy()), t)
+    assert_rows_close(to_np(y), ref, what="wide-scale residual_tail_gemm")
 
 
 @pytest.mark.parametrize("M,N,K,tail", [(8, 256, 2048, 256), (13, 100, 1024, 96), (128, 2560, 9728, 256),
@@ -365,9 +419,15 @@ def test_residual_tail_gemm(M, N, K, tail):
     t = tail
     w = gbw.weight_from_act(wq)
     rw = gbw.weight_from_act(rq) if t else None
-    ref = oracle.residual_tail_gemm(to_np(a.codes), to_np(a.scales), to_np(wq.codes), to_np(wq.scales),
-                                    to_np(rq.codes)[:, :t // 2] if t else to_np(rq.codes)[:, :0],
-                                    to_np(rq.scales)[:, :t // 32] if t else to_np(rq.scales)[:, :0], t)
+    # the oracle's own chain from the synthetic inputs: Q(X), Q(W), R = W_tail - deq(Q(W))_tail, Q(R)
+    ac, as_ = on.quantize_e8m0_b32(p["x"].float().cpu().numpy())
+    wn = p["w"].cpu().numpy()
+    wc, ws = on.quantize_e8m0_b32(wn)
+    rc, rs = on.quantize_e8m0_b32(oracle.residual_weight(wn, wc, ws, max(tail, 96)))
+    for g, o in ((a.codes, ac), (a.scales, as_), (wq.codes, wc), (wq.scales, ws), (rq.codes, rc), (rq.scales, rs)):
+        assert np.array_equal(to_np(g), o)
+    ref = on.residual_tail_gemm(ac, as_, wc, ws, rc[:, :t // 2], rs[:, :t // 32], t)
+    assert on.last_inexact == 0
     y = to_np(gbw.residual_tail_gemm(a, w, rw, t))
     assert_rows_close(y, ref, what="residual_tail_gemm")
     yd = to_np(gbw.residual_tail_gemm(a, w, rw, t, ws=False))

@@ -1,7 +1,10 @@
 """GPU parity: the codebook (LUT) GEMM against the oracle.
 
 Outputs must satisfy max_n |y - y_ref| <= 1e-3 * ||y_ref row||_2; the
-integer-valued case (centroids j - 8, integer x) must be bit-exact.
+integer-valued case (centroids j - 8, integer x) must be bit-exact.  x covers
+the whole bf16 range (values up to 1e30 and below 2^-24) and every
+workspace path of the split-K kernel (a reused zeroed workspace, one that is
+too short, none).
 """
 
 import numpy as np
@@ -9,6 +12,7 @@ import pytest
 import torch
 
 import oracle
+import oracle.native as on
 import synth
 from parity import assert_rows_close, banner, to_np, u16
 
@@ -29,7 +33,7 @@ def setup_module():
 
 
 def _ref(d, group):
-    return oracle.lut_gemm(u16(d["x"]), to_np(d["idx"]), to_np(d["centroids"]), group)
+    return on.lut_gemm(u16(d["x"]), to_np(d["idx"]), to_np(d["centroids"]), group)
 
 
 @pytest.mark.parametrize("M,N,K,group", [(1, 64, 256, 128), (3, 100, 512, 64), (8, 256, 1024, 128),
@@ -67,6 +71,58 @@ def test_lut_gemm_full_size(M):
     y = gbw.lut_gemm(d["x"], d["idx"], d["centroids"], 128)
     ref = _ref(d, 128)
     assert_rows_close(to_np(y), ref, what=f"lut_gemm full M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 8, 16, 40, 64, 100])
+def test_lut_gemm_whole_bf16_range(M):
+    """x rows and 128-chunks at very different magnitudes: whole rows near
+    1e30, rows below 2^-24, chunks that mix 1e30 with 2^-30 and ordinary
+    N(0,1) values; the oracle is finite everywhere, and so must the GPU be."""
+    banner(f"lut_gemm bf16 range M={M} N=192 K=1024")
+    N, K, group = 192, 1024, 128
+    w = synth.clustered_weight(N, K, group=group, seed=60 + M, device="cpu", iters=4)
+    x = synth.normal((M, K), 1.0, 61 + M, "lut.range", "cpu")
+    row_gain = torch.tensor([1e30, 2.0 ** -30, 1.0, 3e-38, 2.0 ** -100, 6e4, 7e4, 1e-8][:M] +
+                            [1.0] * max(0, M - 8)).reshape(-1, 1)
+    x = x * row_gain
+    if M > 2:                                  # a row whose chunks mix huge and tiny values
+        x[2, :128] *= 1e30
+        x[2, 128:256] *= 2.0 ** -30
+        x[2, 300] = 1e30
+    if M > 9:
+        x[9:, 512:640] *= 2.0 ** -40           # one tiny chunk in every other row
+    xb = x.to(torch.bfloat16)
+    assert torch.isfinite(xb.float()).all()
+    d = dict(x=xb, idx=w["idx"], centroids=w["centroids"])
+    ref = _ref(d, group)
+    y = gbw.lut_gemm(xb.to(DEV), w["idx"].to(DEV), w["centroids"].to(DEV), group)
+    assert torch.isfinite(y).all()
+    assert_rows_close(to_np(y), ref, what="lut_gemm bf16 range")
+
+
+@pytest.mark.parametrize("M", [24, 64])
+def test_lut_gemm_workspace_paths(M):
+    """The split-K kernel with one zeroed workspace reused over several calls
+    (its arrival counters must be left at zero: every call gives the same
+    bits), with a workspace one byte too short and with none (both the
+    one-workgroup-per-tile path)."""
+    banner(f"lut_gemm workspace paths M={M} N=512 K=4096")
+    N, K, group = 512, 4096, 128
+    w = synth.clustered_weight(N, K, group=group, seed=70, device="cpu", iters=4)
+    x = synth.normal((M, K), 1.0, 71, "lut.ws", "cpu").to(torch.bfloat16)
+    ref = _ref(dict(x=x, idx=w["idx"], centroids=w["centroids"]), group)
+    xd, idx, cent = x.to(DEV), w["idx"].to(DEV), w["centroids"].to(DEV)
+    need = gbw.workspace_size(gbw.OP_LUT_GEMM, M, N, K)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    ys = [gbw.lut_gemm(xd, idx, cent, group, ws=ws) for _ in range(4)]
+    assert_rows_close(to_np(ys[0]), ref, what="split-K")
+    assert all(torch.equal(ys[0], yy) for yy in ys[1:])
+    short = torch.zeros(need - 1, dtype=torch.uint8, device=DEV)
+    y_short = gbw.lut_gemm(xd, idx, cent, group, ws=short)
+    y_none = gbw.lut_gemm(xd, idx, cent, group, ws=False)
+    assert_rows_close(to_np(y_short), ref, what="short workspace")
+    assert torch.equal(y_short, y_none)
 
 
 def test_lut_gemm_rejects_bad_shapes():
