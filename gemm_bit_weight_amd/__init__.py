@@ -55,7 +55,8 @@ OP_MOE_ROUTE = 3
 OP_MOE_GEMM = 4
 
 EXPORTED = ["gbw_status_string", "gbw_last_error", "gbw_workspace_size", "mx_quantize", "mx_dequantize",
-            "mx_residual", "mx_gemm", "residual_tail_gemm", "lut_gemm", "moe_route", "moe_grouped_gemm"]
+            "mx_residual", "mx_gemm", "residual_tail_gemm", "lut_gemm", "moe_route", "moe_route_noalloc",
+            "moe_grouped_gemm"]
 
 _c = ctypes
 _vp = _c.c_void_p
@@ -99,6 +100,8 @@ _lib.lut_gemm.restype = _c.c_int
 _lib.lut_gemm.argtypes = [_i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _c.c_size_t, _vp]
 _lib.moe_route.restype = _c.c_int
 _lib.moe_route.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _c.c_size_t, _vp]
+_lib.moe_route_noalloc.restype = _c.c_int
+_lib.moe_route_noalloc.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.moe_grouped_gemm.restype = _c.c_int
 _lib.moe_grouped_gemm.argtypes = [_i32, _i64, _i32, _vp, _vp, _vp, _vp, _c.POINTER(_Act), _c.POINTER(_Weight),
                                   _c.POINTER(_MoeOut), _i32, _vp, _c.c_size_t, _vp]
@@ -323,6 +326,24 @@ def moe_route(logits, topk, out=None, ws=None, stream=None):
     _check(_lib.moe_route(_ptr(logits), T, E, topk, _ptr(out["topk_ids"]), _ptr(out["topk_w"]),
                           _ptr(out["expert_offsets"]), _ptr(out["pair_token"]), _ptr(out["pair_pos"]), _ptr(ws),
                           ws.numel() if ws is not None else 0, _stream(stream)))
+    return out
+
+
+def moe_route_noalloc(logits, topk, out=None, stream=None):
+    """moe_route with its scratch in the library's fixed per-GPU array (no
+    workspace; ceil(T / 64) * E <= 131072).  Calls that overlap in time on
+    one GPU share that array and race."""
+    T, E = logits.shape
+    dev = logits.device
+    if out is None:
+        out = dict(topk_ids=torch.empty((T, topk), dtype=torch.int32, device=dev),
+                   topk_w=torch.empty((T, topk), dtype=torch.float32, device=dev),
+                   expert_offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                   pair_token=torch.empty(T * topk, dtype=torch.int32, device=dev),
+                   pair_pos=torch.empty((T, topk), dtype=torch.int32, device=dev))
+    _check(_lib.moe_route_noalloc(_ptr(logits), T, E, topk, _ptr(out["topk_ids"]), _ptr(out["topk_w"]),
+                                  _ptr(out["expert_offsets"]), _ptr(out["pair_token"]), _ptr(out["pair_pos"]),
+                                  _stream(stream)))
     return out
 
 

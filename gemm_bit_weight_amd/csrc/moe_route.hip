@@ -22,6 +22,8 @@
 //     expert + the number of earlier tokens of the chunk in that expert's
 //     mask (a popcount).
 // With at most kScanLds counts, 2 and 3 are one kernel, k_route_scan_scatter.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace gbw {
@@ -401,27 +403,32 @@ static int launch_route(const float* logits, int64_t T, int E, int32_t* ids, flo
 
 using namespace gbw;
 
-extern "C" int moe_route(const float* logits, int64_t T, int32_t E, int32_t topk, int32_t* topk_ids, float* topk_w,
-                         int32_t* expert_offsets, int32_t* pair_token, int32_t* pair_pos, void* ws, size_t ws_bytes,
-                         void* stream) {
-  if (T < 0 || E <= 0 || E > kMaxExperts) return fail(GBW_E_ARG, "moe_route: need 0 < E <= %d", kMaxExperts);
-  if (topk < 1 || topk > E || topk > kMaxTopk) return fail(GBW_E_ARG, "moe_route: need 1 <= topk <= min(E, 16)");
-  if (!expert_offsets) return fail(GBW_E_ARG, "moe_route: null expert_offsets");
+namespace gbw {
+
+// Validation and launches shared by moe_route and moe_route_noalloc; `ws`
+// holds ws_moe_route(T, E) bytes (counts + bases), every byte written by the
+// kernels before it is read.
+static int route_checked(const char* who, const float* logits, int64_t T, int32_t E, int32_t topk,
+                         int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* pair_token,
+                         int32_t* pair_pos) {
+  if (T < 0 || E <= 0 || E > kMaxExperts) return fail(GBW_E_ARG, "%s: need 0 < E <= %d", who, kMaxExperts);
+  if (topk < 1 || topk > E || topk > kMaxTopk) return fail(GBW_E_ARG, "%s: need 1 <= topk <= min(E, 16)", who);
+  if (!expert_offsets) return fail(GBW_E_ARG, "%s: null expert_offsets", who);
   if (T > 0 && (!logits || !topk_ids || !topk_w || !pair_token || !pair_pos))
-    return fail(GBW_E_ARG, "moe_route: null pointer");
-  if ((int64_t)T * topk > INT32_MAX) return fail(GBW_E_SHAPE, "moe_route: too many pairs for int32 indices");
-  if (T > 0 && (!ws || ws_bytes < ws_moe_route(T, E)))
-    return fail(GBW_E_WORKSPACE, "moe_route: needs %zu bytes of workspace", ws_moe_route(T, E));
-  int st = check_device();
-  if (st) return st;
-  hipStream_t s = as_stream(stream);
+    return fail(GBW_E_ARG, "%s: null pointer", who);
+  if ((int64_t)T * topk > INT32_MAX) return fail(GBW_E_SHAPE, "%s: too many pairs for int32 indices", who);
+  return GBW_OK;
+}
+
+static int route_launch(const float* logits, int64_t T, int32_t E, int32_t topk, int32_t* topk_ids, float* topk_w,
+                        int32_t* expert_offsets, int32_t* pair_token, int32_t* pair_pos, int32_t* w32,
+                        hipStream_t s) {
   if (T == 0) {
     // no tokens: every expert offset is zero
     hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(kMaxExperts), 0, s, (const int32_t*)nullptr, (int64_t)0, E,
                        (int32_t*)nullptr, expert_offsets);
     return check_launch("moe_route(empty)");
   }
-  int32_t* w32 = reinterpret_cast<int32_t*>(ws);
   switch (topk) {
 #define GBW_ROUTE_CASE(K) \
   case K:                 \
@@ -446,4 +453,66 @@ extern "C" int moe_route(const float* logits, int64_t T, int32_t E, int32_t topk
     default:
       return fail(GBW_E_UNSUPPORTED, "moe_route: topk out of range");
   }
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free routing: the counts and bases live in this file-scope
+// device array (one copy per GPU, alive until the process ends) instead of
+// a caller workspace.  Host code never passes `scratch` itself to a kernel:
+// its device address on the current GPU is looked up once per device and
+// kept in g_scratch[dev].
+// ---------------------------------------------------------------------------
+constexpr size_t kRouteScratchBytes = (size_t)1 << 20;  // counts + bases of C * E <= 131072 (chunks of 64 tokens)
+static __device__ __align__(256) int32_t scratch[kRouteScratchBytes / sizeof(int32_t)];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::once_flag g_scratch_once[kScratchDevices];
+int32_t* g_scratch[kScratchDevices];
+hipError_t g_scratch_err[kScratchDevices];
+}  // namespace
+
+static int32_t* route_scratch(int dev) {
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch[dev] = g_scratch_err[dev] == hipSuccess ? static_cast<int32_t*>(ptr) : nullptr;
+  });
+  return g_scratch[dev];
+}
+
+}  // namespace gbw
+
+extern "C" int moe_route(const float* logits, int64_t T, int32_t E, int32_t topk, int32_t* topk_ids, float* topk_w,
+                         int32_t* expert_offsets, int32_t* pair_token, int32_t* pair_pos, void* ws, size_t ws_bytes,
+                         void* stream) {
+  int st = route_checked("moe_route", logits, T, E, topk, topk_ids, topk_w, expert_offsets, pair_token, pair_pos);
+  if (st) return st;
+  if (T > 0 && (!ws || ws_bytes < ws_moe_route(T, E)))
+    return fail(GBW_E_WORKSPACE, "moe_route: needs %zu bytes of workspace", ws_moe_route(T, E));
+  if ((st = check_device())) return st;
+  return route_launch(logits, T, E, topk, topk_ids, topk_w, expert_offsets, pair_token, pair_pos,
+                      reinterpret_cast<int32_t*>(ws), as_stream(stream));
+}
+
+extern "C" int moe_route_noalloc(const float* logits, int64_t T, int32_t E, int32_t topk, int32_t* topk_ids,
+                                 float* topk_w, int32_t* expert_offsets, int32_t* pair_token, int32_t* pair_pos,
+                                 void* stream) {
+  int st = route_checked("moe_route_noalloc", logits, T, E, topk, topk_ids, topk_w, expert_offsets, pair_token,
+                         pair_pos);
+  if (st) return st;
+  if (ws_moe_route(T, E) > kRouteScratchBytes)
+    return fail(GBW_E_SHAPE, "moe_route_noalloc: %lld tokens x %d experts need %zu bytes of scratch, more than the "
+                "fixed %zu (ceil(T / 64) * E must be <= %zu)", (long long)T, E, ws_moe_route(T, E),
+                kRouteScratchBytes, kRouteScratchBytes / 8);
+  if ((st = check_device())) return st;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices)
+    return fail(GBW_E_UNSUPPORTED, "moe_route_noalloc: no usable HIP device");
+  int32_t* w32 = route_scratch(dev);
+  if (!w32)
+    return fail(GBW_E_LAUNCH, "moe_route_noalloc: scratch address lookup failed on device %d: %s", dev,
+                hipGetErrorString(g_scratch_err[dev]));
+  return route_launch(logits, T, E, topk, topk_ids, topk_w, expert_offsets, pair_token, pair_pos, w32,
+                      as_stream(stream));
 }

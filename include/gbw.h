@@ -253,6 +253,21 @@ int moe_route(const float* logits, int64_t T, int32_t E, int32_t topk, int32_t* 
               float* topk_w, int32_t* expert_offsets, int32_t* pair_token, int32_t* pair_pos,
               void* ws, size_t ws_bytes, void* stream);
 
+/* moe_route_noalloc: moe_route for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, outputs and results (bit for bit) as
+ * moe_route, without the workspace: the per-chunk counts and bases go to a
+ * fixed 1 MiB array the library holds on each GPU it runs on until the
+ * process ends.  Limit: ceil(T / 64) * E <= 131072 (e.g. 65536 tokens with
+ * 128 experts); larger problems fail with GBW_E_SHAPE before anything is
+ * launched.  The call allocates nothing.  Every call on one GPU shares that
+ * array, and each call writes all of it that it reads: calls that overlap
+ * in time on one GPU (different streams, no ordering between them) race and
+ * may return wrong pair lists; calls ordered on one stream are safe. */
+int moe_route_noalloc(const float* logits, int64_t T, int32_t E, int32_t topk, int32_t* topk_ids,
+                      float* topk_w, int32_t* expert_offsets, int32_t* pair_token, int32_t* pair_pos,
+                      void* stream);
+
 /* moe_grouped_gemm: one stage of the routed expert FFN (gated MLP of PRQuant
  * §4 Eq. (1), applied per expert as in CodeQuant Fig. 1-2):
  *  GBW_MOE_GATEUP_SWIGLU: for each pair p=(t,e): g,u = deq(a[t]) deq(w_e)^T

@@ -58,5 +58,19 @@ int main(int argc, char** argv) {
     }
   printf("route T=%lld E=%d K=%d status %d mismatched ids %ld mismatched pairs %ld off[E]=%d\n", (long long)T, E, K,
          st, bad, badp, off[E]);
+  // the allocation-free entry point (scratch in the library's fixed array):
+  // the same outputs, in bounds of that array
+  int32_t* ids2 = (int32_t*)malloc(T * K * 4); float* w2 = (float*)malloc(T * K * 4);
+  int32_t* off2 = (int32_t*)malloc((E + 1) * 4); int32_t* pt2 = (int32_t*)malloc(T * K * 4);
+  int32_t* pp2 = (int32_t*)malloc(T * K * 4);
+  const int st2 = moe_route_noalloc(l, T, E, K, ids2, w2, off2, pt2, pp2, nullptr);
+  long diff = 0;
+  if (st2 == 0) {
+    diff += memcmp(ids, ids2, T * K * 4) != 0;
+    diff += memcmp(off, off2, (E + 1) * 4) != 0;
+    diff += memcmp(pt, pt2, T * K * 4) != 0;
+    diff += memcmp(pp, pp2, T * K * 4) != 0;
+  }
+  printf("noalloc status %d differing outputs %ld\n", st2, diff);
   return 0;
 }

@@ -40,6 +40,12 @@ inline void __syncthreads() { emu_bar->arrive_and_wait(); }
 
 typedef void* hipStream_t;
 typedef int hipError_t;
+#define hipSuccess 0
+#define __align__(n) __attribute__((aligned(n)))
+#define HIP_SYMBOL(x) (&(x))
+inline hipError_t hipGetDevice(int* d) { *d = 0; return hipSuccess; }
+inline hipError_t hipGetSymbolAddress(void** p, const void* sym) { *p = const_cast<void*>(sym); return hipSuccess; }
+inline const char* hipGetErrorString(hipError_t) { return "emulated"; }
 struct uint2 { unsigned x, y; };
 
 template <class A, class B> inline auto min(A a, B b) { return a < b ? a : b; }

@@ -90,6 +90,8 @@ def test_moe_route_in_bounds_and_exact(build_dir, T, E, K, mode):
     exe = _build(build_dir, "moe_route.hip", "drv_route.cpp", "emu_route")
     out = _run(exe, T, E, K, *([mode] if mode else []))
     assert "status 0 mismatched ids 0 mismatched pairs 0" in out, out
+    # the allocation-free entry point gives the same outputs (every case here fits its scratch)
+    assert "noalloc status 0 differing outputs 0" in out, out
 
 
 @pytest.mark.parametrize("M,N,K,group", [(1, 40, 384, 32), (5, 256, 1024, 128), (17, 40, 384, 32), (64, 128, 2048, 128),
