@@ -271,7 +271,7 @@ def tail_decode(gbw, synth, torch):
         rq = gbw.mx_quantize(gbw.mx_residual(w, wq.codes, wq.scales, tail), gbw.FMT_E8M0_B32)
         reps.append((gbw.weight_from_act(wq), gbw.weight_from_act(rq)))
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(1, gbw.workspace_size(gbw.OP_MX_GEMM, M, N, K + tail)), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(1, gbw.workspace_size(gbw.OP_MX_GEMM, M, N, K + tail)), dtype=torch.uint8, device="cuda")
 
     def fn():
         for w, r in reps:
@@ -285,14 +285,21 @@ def tail_decode(gbw, synth, torch):
 
 def moe_mxfp4_prquant(gbw, synth, torch, steps=5, tail=128):
     """MXFP4 experts at the E4M3-B16 workload's shape (T=4096, H=2048, I=768,
-    128 experts, top-8), plain and with PRQuant's tail residual on the
-    down-projections (gate/up appends the tail copy of h; the down stage runs
-    over I + tail against [W_down | R]).  Overhead of the residual in %."""
+    128 experts, top-8): plain, with PRQuant's tail residual on the
+    down-projections through the online tail copy (gate/up appends the copy
+    of h's last `tail` columns), and through the offline copy (gate/up
+    weights with their last `tail` rows duplicated, so the FFN itself emits
+    I + tail columns); the down stage then runs over I + tail against
+    [W_down | R].  Overheads in % of the plain step."""
     T, H, I, E, K = 4096, 2048, 768, 128, 8
     d = synth.moe_problem(T, H, I, E, seed=0, device="cuda")
     q = gbw.mx_quantize(d["w_gate_up"].reshape(E * 2 * I, H), gbw.FMT_E8M0_B32)
-    Wgu = gbw.Weight(gbw.FMT_E8M0_B32, 2 * I, H, q.codes.view(E, 2 * I, H // 2), q.scales.view(E, 2 * I, H // 32),
-                     n_experts=E)
+    gc, gs = q.codes.view(E, 2 * I, H // 2), q.scales.view(E, 2 * I, H // 32)
+    Wgu = gbw.Weight(gbw.FMT_E8M0_B32, 2 * I, H, gc, gs, n_experts=E)
+
+    def dup(t):  # gate rows + copies of the last `tail`, then up rows + copies
+        return torch.cat([t[:, :I], t[:, I - tail:I], t[:, I:], t[:, 2 * I - tail:]], dim=1).contiguous()
+    Woff = gbw.Weight(gbw.FMT_E8M0_B32, 2 * (I + tail), H, dup(gc), dup(gs), n_experts=E)
     wd = d["w_down"]
     qc = torch.empty((E, H, (I + tail) // 2), dtype=torch.uint8, device="cuda")
     qs = torch.empty((E, H, (I + tail) // 32), dtype=torch.uint8, device="cuda")
@@ -301,22 +308,25 @@ def moe_mxfp4_prquant(gbw, synth, torch, steps=5, tail=128):
         rq = gbw.mx_quantize(gbw.mx_residual(wd[e].contiguous(), wq.codes, wq.scales, tail), gbw.FMT_E8M0_B32)
         qc[e] = torch.cat([wq.codes, rq.codes], dim=1)
         qs[e] = torch.cat([wq.scales, rq.scales], dim=1)
-    Wd = {0: gbw.Weight(gbw.FMT_E8M0_B32, H, I, qc[:, :, :I // 2].contiguous(), qs[:, :, :I // 32].contiguous(),
-                        n_experts=E),
-          tail: gbw.Weight(gbw.FMT_E8M0_B32, H, I + tail, qc, qs, n_experts=E)}
+    Wd0 = gbw.Weight(gbw.FMT_E8M0_B32, H, I, qc[:, :, :I // 2].contiguous(), qs[:, :, :I // 32].contiguous(),
+                     n_experts=E)
+    Wda = gbw.Weight(gbw.FMT_E8M0_B32, H, I + tail, qc, qs, n_experts=E)
     del d["w_gate_up"], d["w_down"]
     P = T * K
     y = torch.empty((T, H), dtype=torch.float32, device="cuda")
     res = {"T": T, "hidden": H, "intermediate": I, "experts": E, "topk": K, "tail": tail}
-    for tl in (0, tail):
-        hc = torch.empty((P, (I + tl) // 2), dtype=torch.uint8, device="cuda")
-        hs = torch.empty((P, (I + tl) // 32), dtype=torch.uint8, device="cuda")
+    # (name, gate/up weight, h columns, h_tail of the gate/up call, down weight)
+    variants = (("tail0", Wgu, I, 0, Wd0), ("tail%d" % tail, Wgu, I + tail, tail, Wda),
+                ("offline%d" % tail, Woff, I + tail, 0, Wda))
+    for name, wg, hw, ht, wdn in variants:
+        hc = torch.empty((P, hw // 2), dtype=torch.uint8, device="cuda")
+        hs = torch.empty((P, hw // 32), dtype=torch.uint8, device="cuda")
 
-        def step(tl=tl, hc=hc, hs=hs):
+        def step(wg=wg, ht=ht, wdn=wdn, hc=hc, hs=hs):
             route = gbw.moe_route(d["logits"], K)
             xq = gbw.mx_quantize(d["x"], gbw.FMT_E8M0_B32)
-            gbw.moe_grouped_gemm(gbw.MOE_GATEUP_SWIGLU, route, xq, Wgu, h_codes=hc, h_scales=hs, h_tail=tl)
-            gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, gbw.Act(gbw.FMT_E8M0_B32, hc, hs), Wd[tl], y=y)
+            gbw.moe_grouped_gemm(gbw.MOE_GATEUP_SWIGLU, route, xq, wg, h_codes=hc, h_scales=hs, h_tail=ht)
+            gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, gbw.Act(gbw.FMT_E8M0_B32, hc, hs), wdn, y=y)
         step()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -325,9 +335,12 @@ def moe_mxfp4_prquant(gbw, synth, torch, steps=5, tail=128):
             step()
         e1.record()
         torch.cuda.synchronize()
-        res["ms_per_step_tail%d" % tl] = e0.elapsed_time(e1) / steps
-    res["overhead_pct"] = 100.0 * (res["ms_per_step_tail%d" % tail] / res["ms_per_step_tail0"] - 1.0)
+        res["ms_per_step_" + name] = e0.elapsed_time(e1) / steps
+    base = res["ms_per_step_tail0"]
+    res["overhead_pct"] = 100.0 * (res["ms_per_step_tail%d" % tail] / base - 1.0)
+    res["overhead_pct_offline"] = 100.0 * (res["ms_per_step_offline%d" % tail] / base - 1.0)
     res["added_down_flop_pct"] = 100.0 * tail / I
+    res["added_gate_up_flop_pct_offline"] = 100.0 * tail / I
     return res
 
 
@@ -355,7 +368,7 @@ def dense_small(gbw, synth, torch):
     a = gbw.mx_quantize(d["x"], gbw.FMT_E8M0_B32)
     w = gbw.weight_from_act(gbw.mx_quantize(d["w"], gbw.FMT_E8M0_B32))
     y = torch.empty((16, 512), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(1, gbw.workspace_size(gbw.OP_MX_GEMM, 16, 512, 512)), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(1, gbw.workspace_size(gbw.OP_MX_GEMM, 16, 512, 512)), dtype=torch.uint8, device="cuda")
 
     def fn():
         for _ in range(50):

@@ -257,8 +257,10 @@ def weight_from_act(a: Act) -> Weight:
 
 
 def _ws(ws, nbytes, device):
+    """A GEMM workspace: zeroed when made here, as split-K GEMMs need their
+    arrival counters (its first 64 KiB) zero; calls leave them zero."""
     if ws is None and nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
     return ws, (ws.numel() if ws is not None else 0)
 
 

@@ -176,6 +176,64 @@ __device__ __forceinline__ v4i load16(const void* p) { return *reinterpret_cast<
 
 __host__ __device__ constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Split-K GEMM workspaces (mx_gemm, residual_tail_gemm, lut_gemm) start with
+// this many bytes of per-tile arrival counters (one uint32 per output tile,
+// at most kWsCounterBytes / 4 tiles); the partial tiles follow.  The counters
+// are zero before a workspace's first use and every call leaves them zero,
+// so one zeroed workspace serves any sequence of these GEMMs.
+constexpr size_t kWsCounterBytes = 65536;
+constexpr int64_t kWsMaxTiles = (int64_t)(kWsCounterBytes / 4);
+
+// Partial tiles that the workgroups of one split-K launch hand to each other
+// are written and read with relaxed agent-scope atomics: those are coherent
+// across every CU of the GPU (they bypass the per-CU and per-XCD caches)
+// without the whole-L2 write-back and invalidate that an agent-scope fence
+// costs.  Ordering comes from the hardware: a thread waits until its stores
+// have completed (vmcnt counts stores on this chip) before the workgroup
+// counts its arrival, and the last arrival's loads are issued only after
+// the counter has told it so.
+__device__ __forceinline__ void store_shared_f32(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_shared_f32(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The same accesses 16 bytes at a time: buffer loads and stores with the
+// cache policy the compiler gives agent-scope atomics (sc1), through a raw
+// buffer resource over `nbytes` at `base` (word 3 0x00020000: the raw
+// 32-bit format of this chip family; out-of-range accesses read 0 and write
+// nothing).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t shared_tile_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, 0x00020000);
+}
+constexpr int kCpolAgentCoherent = 16;  // sc1
+__device__ __forceinline__ void store_shared_v4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, v4f v) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, (int)byte_off, 0, kCpolAgentCoherent);
+}
+__device__ __forceinline__ v4f load_shared_v4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kCpolAgentCoherent));
+}
+// every memory operation this thread issued has completed
+__device__ __forceinline__ void wait_all_memory() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  __asm__ volatile("" ::: "memory");
+}
+// Arrival of this workgroup at its tile's counter, after every thread's
+// partial-tile stores: true in the last of `splits` workgroups, which then
+// resets the counter (with an atomic store) for the next call.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, int splits, int* s_flag) {
+  wait_all_memory();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *s_flag = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(splits - 1);
+  __syncthreads();
+  const bool last = *s_flag != 0;
+  if (last && threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return last;
+}
+
 }  // namespace gbw
 
 // ---------------------------------------------------------------------------

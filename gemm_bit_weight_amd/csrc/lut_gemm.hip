@@ -108,7 +108,7 @@ struct LutArgs {
   const uint8_t* idx;    // [N][K/2]
   const uint16_t* cent;  // [N][K/group][16] fp16
   float* y;              // [M][N]
-  float* part;           // [splits][M][N] fp32 partial tiles (splits > 1)
+  float* part;           // [tiles][splits][32 MT x 64] fp32 partial tiles (splits > 1)
   uint32_t* counters;    // one arrival counter per output tile (splits > 1), zero between calls
   int32_t chunks_per_split;  // 128-element chunks of K per workgroup
   int32_t splits;
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(512) void k_lut_gemm(const LutArgs p) {
   constexpr int XR = 32 * MT;          // x rows per tile
   constexpr int XROW = 128 * 2 + 16;   // LDS bytes per x row of a chunk slot
   constexpr int XSB = 4 * XR * XROW;   // the four slots
-  constexpr int REDB = 8 * MT * 16 * 64 * 4;  // per-wave partial sums
+  constexpr int REDB = 8 * MT * 16 * 64 * 4 + XR * 64 * 4;  // per-wave partial sums, then the tile
   __shared__ __attribute__((aligned(16))) uint8_t smem[XSB > REDB ? XSB : REDB];
   __shared__ __attribute__((aligned(16))) float invs[4][XR];
   __shared__ int s_last;
@@ -256,122 +256,159 @@ __global__ __launch_bounds__(512) void k_lut_gemm(const LutArgs p) {
 #pragma unroll
   for (int i = 0; i < MT; ++i) acc[i] = v16f{};
 
-  for (int rd = 0; rd < rounds; ++rd) {
-    const int cl = 4 * rd + kg;  // chunk of the range for this K group
-    const bool has = cl < nc;    // the same for both waves of the group
-    const int c = cs0 + (has ? cl : nc - 1);
-    // weights of this wave's chunk: the lane's 64 indices, its table(s)
-    const uint8_t* ir = p.idx + n * (p.K / 2) + (int64_t)c * 64 + 32 * h;
-    const v4i iq0 = load16(ir), iq1 = load16(ir + 16);
-    const int64_t g0 = ((int64_t)c * 128 + 64 * h) / p.group;  // table of elements 64h .. 64h + 31
-    const int64_t g1 = ((int64_t)c * 128 + 64 * h + 32) / p.group;
-    const uint16_t* t0 = p.cent + (n * G + g0) * 16;
-    const uint16_t* t1 = p.cent + (n * G + g1) * 16;
-    const v4i ta0 = load16(t0), tb0 = load16(t0 + 8);
-    const v4i ta1 = load16(t1), tb1 = load16(t1 + 8);  // the same table unless group == 32
-    // x: XR rows x 16 pieces of this K group's chunk over its 128 lanes
-    constexpr int XP = XR * 16 / 128;  // pieces per lane
-    v4i xv[XP];
+  constexpr int XP = XR * 16 / 128;  // x pieces (8 elements) per lane per chunk
+  // Rounds go two at a time: every load of both (the lane's indices and
+  // tables, its share of the chunk's x rows) is issued before the first is
+  // used, so a workgroup has its whole K range in flight at once.
+  for (int rb = 0; rb < rounds; rb += 2) {
+    v4i iq[2][2], ta[2][2], tb[2][2], xv[2][XP];
+    bool has[2];
 #pragma unroll
-    for (int t = 0; t < XP; ++t) {
-      const int u = nb * 64 + lane + 128 * t;
-      const int64_t m = m0 + (u >> 4);
-      xv[t] = m < p.M ? load16(p.x + m * p.K + (int64_t)c * 128 + 8 * (u & 15)) : v4i{0, 0, 0, 0};
-    }
+    for (int r = 0; r < 2; ++r) {
+      const int cl = 4 * (rb + r) + kg;  // chunk of the range for this K group
+      has[r] = cl < nc;                  // the same for both waves of the group
+      const int c = cs0 + (has[r] ? cl : nc - 1);
+      const uint8_t* ir = p.idx + n * (p.K / 2) + (int64_t)c * 64 + 32 * h;
+      iq[r][0] = load16(ir);
+      iq[r][1] = load16(ir + 16);
+      const int64_t g0 = ((int64_t)c * 128 + 64 * h) / p.group;  // table of elements 64h .. 64h + 31
+      const int64_t g1 = ((int64_t)c * 128 + 64 * h + 32) / p.group;
+      const uint16_t* t0 = p.cent + (n * G + g0) * 16;
+      const uint16_t* t1 = p.cent + (n * G + g1) * 16;
+      ta[r][0] = load16(t0);
+      tb[r][0] = load16(t0 + 8);
+      ta[r][1] = load16(t1);  // the same table unless group == 32
+      tb[r][1] = load16(t1 + 8);
 #pragma unroll
-    for (int t = 0; t < XP; ++t) {
-      const int u = nb * 64 + lane + 128 * t;
-      const int r = u >> 4, j = u & 15;
-      const int s = chunk_prescale(row16_max_u32(bf16x8_absmax_bits(xv[t])));
-      *reinterpret_cast<v4i*>(xs + r * XROW + 16 * j) = x8_to_f16(xv[t], pow2f(s));
-      if (j == 0) invs[kg][r] = pow2f(-s);
-    }
-    __syncthreads();
-    if (has) {
-      uint32_t L0[4], H0[4], L1[4], H1[4];
-      split_table(ta0, tb0, L0, H0);
-      split_table(ta1, tb1, L1, H1);
-      const uint32_t wd[8] = {(uint32_t)iq0[0], (uint32_t)iq0[1], (uint32_t)iq0[2], (uint32_t)iq0[3],
-                              (uint32_t)iq1[0], (uint32_t)iq1[1], (uint32_t)iq1[2], (uint32_t)iq1[3]};
-      v8h bf[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        uint32_t o[4];
-        if (s < 4)
-          decode8(wd[s], L0, H0, o);
-        else
-          decode8(wd[s], L1, H1, o);
-        bf[s] = __builtin_bit_cast(v8h, v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]});
+      for (int t = 0; t < XP; ++t) {
+        const int u = nb * 64 + lane + 128 * t;
+        const int64_t m = m0 + (u >> 4);
+        xv[r][t] = m < p.M ? load16(p.x + m * p.K + (int64_t)c * 128 + 8 * (u & 15)) : v4i{0, 0, 0, 0};
       }
+    }
 #pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        v16f part = v16f{};
+    for (int r = 0; r < 2; ++r) {
+      if (rb + r >= rounds) break;  // uniform over the workgroup
+      // x: XR rows x 16 pieces of this K group's chunk over its 128 lanes
+#pragma unroll
+      for (int t = 0; t < XP; ++t) {
+        const int u = nb * 64 + lane + 128 * t;
+        const int row = u >> 4, j = u & 15;
+        const int s = chunk_prescale(row16_max_u32(bf16x8_absmax_bits(xv[r][t])));
+        *reinterpret_cast<v4i*>(xs + row * XROW + 16 * j) = x8_to_f16(xv[r][t], pow2f(s));
+        if (j == 0) invs[kg][row] = pow2f(-s);
+      }
+      __syncthreads();
+      if (has[r]) {
+        uint32_t L0[4], H0[4], L1[4], H1[4];
+        split_table(ta[r][0], tb[r][0], L0, H0);
+        split_table(ta[r][1], tb[r][1], L1, H1);
+        const uint32_t wd[8] = {(uint32_t)iq[r][0][0], (uint32_t)iq[r][0][1], (uint32_t)iq[r][0][2],
+                                (uint32_t)iq[r][0][3], (uint32_t)iq[r][1][0], (uint32_t)iq[r][1][1],
+                                (uint32_t)iq[r][1][2], (uint32_t)iq[r][1][3]};
+        v8h bf[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-          const v8h af = *reinterpret_cast<const v8h*>(xs + (32 * i + l32) * XROW + (64 * h + 8 * s) * 2);
-          part = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[s], part, 0, 0, 0);
+          uint32_t o[4];
+          if (s < 4)
+            decode8(wd[s], L0, H0, o);
+          else
+            decode8(wd[s], L1, H1, o);
+          bf[s] = __builtin_bit_cast(v8h, v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]});
         }
-        // part[r]: x row 32i + 8(r/4) + 4h + r%4
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const v4f inv = *reinterpret_cast<const v4f*>(&invs[kg][32 * i + 8 * q + 4 * h]);
+        for (int i = 0; i < MT; ++i) {
+          v16f part = v16f{};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][4 * q + r] += part[4 * q + r] * inv[r];
+          for (int s = 0; s < 8; ++s) {
+            const v8h af = *reinterpret_cast<const v8h*>(xs + (32 * i + l32) * XROW + (64 * h + 8 * s) * 2);
+            part = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[s], part, 0, 0, 0);
+          }
+          // part[r]: x row 32i + 8(r/4) + 4h + r%4
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const v4f inv = *reinterpret_cast<const v4f*>(&invs[kg][32 * i + 8 * q + 4 * h]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][4 * q + e] += part[4 * q + e] * inv[e];
+          }
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
 
-  // the four K groups' sums, in group order
-  float* red = reinterpret_cast<float*>(smem);  // [wave][MT][16][64]
+  // the four K groups' sums, in group order, into a row-major tile in LDS
+  float* red = reinterpret_cast<float*>(smem);                // [wave][MT][16][64]
+  float* tile = red + 8 * MT * 16 * 64;                       // [XR][64]: row m, column n
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) red[((wave * MT + i) * 16 + r) * 64 + lane] = acc[i][r];
   __syncthreads();
   constexpr int OUTS = 2 * MT * 16 * 64;  // outputs of the tile (2 column blocks)
-  constexpr int PER = OUTS / 512;
-  float v[PER];
-  int64_t om[PER], on[PER];
 #pragma unroll
-  for (int t = 0; t < PER; ++t) {
+  for (int t = 0; t < OUTS / 512; ++t) {
     const int o = (int)threadIdx.x + 512 * t;
     const int ob = o / (MT * 1024), rem = o % (MT * 1024);  // column block, then (i, r, lane)
     const int i = rem / 1024, r = (rem / 64) % 16, l = rem % 64;
     float sum = 0.f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) sum += red[(((2 * g + ob) * MT + i) * 16 + r) * 64 + l];
-    v[t] = sum;
-    om[t] = m0 + 32 * i + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-    on[t] = ntile0 + 32 * ob + (l & 31);
+    tile[(32 * i + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3)) * 64 + 32 * ob + (l & 31)] = sum;
   }
+  __syncthreads();
+
+  // 16-byte pieces: XR rows x 16
+  constexpr int PC = XR * 16 / 512;  // pieces per thread
+  const bool vec = (p.N & 3) == 0 && !(reinterpret_cast<uintptr_t>(p.y) & 15u);
+  auto store_y = [&](int pc, v4f v) __attribute__((always_inline)) {
+    const int64_t m = m0 + (pc >> 4), nn = ntile0 + 4 * (pc & 15);
+    if (m >= p.M || nn >= p.N) return;
+    float* dst = p.y + m * p.N + nn;
+    if (vec && nn + 4 <= p.N) {
+      *reinterpret_cast<v4f*>(dst) = v;
+    } else {
+      for (int e = 0; e < 4 && nn + e < p.N; ++e) dst[e] = v[e];
+    }
+  };
   if (p.splits == 1) {
 #pragma unroll
-    for (int t = 0; t < PER; ++t)
-      if (om[t] < p.M && on[t] < p.N) p.y[om[t] * p.N + on[t]] = v[t];
+    for (int u = 0; u < PC; ++u) {
+      const int pc = (int)threadIdx.x + 512 * u;
+      store_y(pc, *reinterpret_cast<const v4f*>(tile + 4 * pc));
+    }
     return;
   }
-  const int64_t MN = p.M * p.N;
+  // this tile's S slots of XR x 64 fp32, one per split, contiguous; the last
+  // workgroup to arrive sums them in split order
+  const int64_t tile_id = (int64_t)blockIdx.z * gridDim.x + blockIdx.x;
+  constexpr uint32_t SLOT = XR * 64 * 4;  // bytes
+  const __amdgpu_buffer_rsrc_t rs = shared_tile_rsrc(p.part + tile_id * p.splits * (XR * 64), SLOT * p.splits);
 #pragma unroll
-  for (int t = 0; t < PER; ++t)
-    if (om[t] < p.M && on[t] < p.N) p.part[(int64_t)blockIdx.y * MN + om[t] * p.N + on[t]] = v[t];
-  __threadfence();  // this thread's partial tile is visible device-wide before the arrival below
-  __syncthreads();
-  uint32_t* const cnt = p.counters + (int64_t)blockIdx.z * gridDim.x + blockIdx.x;
-  if (threadIdx.x == 0) s_last = atomicAdd(cnt, 1u) == (uint32_t)(p.splits - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();  // the other splits' tiles, published before their arrivals, are visible now
-#pragma unroll
-  for (int t = 0; t < PER; ++t) {
-    if (om[t] >= p.M || on[t] >= p.N) continue;
-    const int64_t off = om[t] * p.N + on[t];
-    float sum = 0.f;
-    for (int sp = 0; sp < p.splits; ++sp) sum += sp == (int)blockIdx.y ? v[t] : p.part[(int64_t)sp * MN + off];
-    p.y[off] = sum;
+  for (int u = 0; u < PC; ++u) {
+    const int pc = (int)threadIdx.x + 512 * u;
+    store_shared_v4(rs, SLOT * blockIdx.y + 16 * pc, *reinterpret_cast<const v4f*>(tile + 4 * pc));
   }
-  if (threadIdx.x == 0) *cnt = 0u;  // ready for the next call
+  if (!arrive_last(p.counters + tile_id, p.splits, &s_last)) return;
+  constexpr int SMX = 8;  // splits whose loads are in flight together
+#pragma unroll
+  for (int u = 0; u < PC; ++u) {
+    const int pc = (int)threadIdx.x + 512 * u;
+    const v4f own = *reinterpret_cast<const v4f*>(tile + 4 * pc);
+    v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int sp0 = 0; sp0 < p.splits; sp0 += SMX) {
+      v4f ld[SMX];
+#pragma unroll
+      for (int q = 0; q < SMX; ++q) {
+        const int sp = sp0 + q;
+        ld[q] = sp < p.splits && sp != (int)blockIdx.y ? load_shared_v4(rs, SLOT * sp + 16 * pc) : own;
+      }
+#pragma unroll
+      for (int q = 0; q < SMX; ++q)
+        if (sp0 + q < p.splits) sum += ld[q];
+    }
+    store_y(pc, sum);
+  }
 }
 
 constexpr int kGemvNW = 16, kGemvCB = 2;
@@ -388,14 +425,12 @@ static int lut_splits(int64_t M, int64_t N, int64_t K) {
   return (int)cdiv(chunks, per);  // no empty split
 }
 
-static size_t lut_counter_bytes(int64_t M, int64_t N) {
-  return (size_t)cdiv(cdiv(N, 64) * cdiv(M, 64) * 4, 256) * 256;
-}
-
 size_t ws_lut_gemm(int64_t M, int64_t N, int64_t K) {
   if (M <= 16 || N <= 0 || K <= 0 || K % 128) return 0;  // M <= 16: one kernel, no partials
+  if (cdiv(N, 64) * cdiv(M, 64) > kWsMaxTiles) return 0;  // too many tiles for the counters: no split
   const int splits = lut_splits(M, N, K);
-  return splits > 1 ? lut_counter_bytes(M, N) + (size_t)splits * M * N * sizeof(float) : 0;
+  const int64_t xr = M <= 32 ? 32 : 64;  // x rows per tile
+  return splits > 1 ? kWsCounterBytes + (size_t)(cdiv(N, 64) * cdiv(M, xr)) * splits * xr * 64 * sizeof(float) : 0;
 }
 
 }  // namespace gbw
@@ -437,12 +472,13 @@ extern "C" int lut_gemm(int64_t M, int64_t N, int64_t K, int32_t group, const ui
   int splits = lut_splits(M, N, K);
   // too little workspace for the partial tiles: one workgroup per tile over
   // all of K (no workspace; slower, same results up to the summation order)
-  if (splits > 1 && (!ws || ws_bytes < ws_lut_gemm(M, N, K) || ((uintptr_t)ws & 15u))) splits = 1;
+  if (splits > 1 && (!ws || ws_lut_gemm(M, N, K) == 0 || ws_bytes < ws_lut_gemm(M, N, K) || ((uintptr_t)ws & 15u)))
+    splits = 1;
   p.chunks_per_split = (int)cdiv(chunks, splits);
   p.splits = splits;
   if (splits > 1) {
     p.counters = reinterpret_cast<uint32_t*>(ws);
-    p.part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + lut_counter_bytes(M, N));
+    p.part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + kWsCounterBytes);
   }
   const dim3 grid((unsigned)cdiv(N, 64), (unsigned)splits, (unsigned)cdiv(M, M <= 32 ? 32 : 64));
   if (M <= 32)

@@ -23,8 +23,11 @@
 //    for all rows of the M tile (up to 128).
 // Decode-shaped problems (M <= 128, N in the thousands) stream the weights
 // from HBM once; the K range is split across workgroups when the (N, M) tiles
-// alone cannot fill 256 CUs, each split writes its own fp32 partial slab and
-// k_splitk_reduce sums the slabs in split order (bitwise repeatable).
+// alone cannot fill 256 CUs.  k_mx_gemm32 reduces the splits inside the
+// kernel (the last workgroup of a tile to arrive adds the split tiles in
+// split order); k_mx_gemm writes one fp32 partial slab per split and
+// k_splitk_reduce sums them in split order.  Either way the result is
+// bitwise repeatable.
 #include "common.hpp"
 
 namespace gbw {
@@ -48,7 +51,9 @@ struct MxGemmArgs {
   float* y;
   int64_t ldy;
   int32_t atomic;  // 1: K is split over workgroups, partials go to `part`
-  float* part;     // [splits][M][N] fp32 workspace
+  float* part;     // 16-row kernel: [splits][M][N] fp32; 32-row kernel: [tiles][splits][rows x 64] fp32
+  uint32_t* counters;  // 32-row kernel with splits: one arrival counter per output tile, zero between calls
+  int32_t splits;
 };
 
 // Fields of the segment that K step s belongs to.  Selected with uniform
@@ -223,48 +228,62 @@ __global__ __launch_bounds__(64 * NW) void k_mx_gemm(const MxGemmArgs p) {
 // alike, with that block's own scale.
 //
 // A workgroup (4 waves) owns 64 output columns, all 32*TM rows of its M tile
-// and a range of at most SMAX K steps: waves 0/1 take columns 0-31/32-63 over
-// the first half of the steps, waves 2/3 the same columns over the second
-// half (their sums meet in LDS at the end, in a fixed order).  The weight
-// slice is read once from HBM straight into registers; the activation range
-// goes HBM/L2 -> LDS by direct-to-LDS loads (no registers), issued before the
-// weight loads so the barrier only waits for them, and the MFMAs consume the
-// weight steps in arrival order.
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
-
-// s_waitcnt operand that waits until at most n vector memory operations of
-// this wave are outstanding (vmcnt in bits 3:0 and 15:14; expcnt, lgkmcnt
-// left at their maxima, i.e. not waited for)
-constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-
+// and a range of at most 2*HALF K steps: waves 0/1 take columns 0-31/32-63
+// over the first half of the steps, waves 2/3 the same columns over the
+// second half.  Each wave issues, step by step, its share of the step's
+// activation blocks and scales and its own weight codes and scales, all to
+// registers, so every byte of the range is in flight at once and arrives in
+// step order.  Step t waits only for its own registers, writes its share of
+// the step's activation to LDS (the two waves of a half share it), meets the
+// other waves at a barrier and runs its MFMAs while later steps are still
+// arriving.  (Direct-to-LDS loads would save the registers, but the compiler
+// then waits for every one of them before the first LDS read.)  The two
+// halves' sums meet in LDS in a fixed order.
+//
+// With the K range split over S workgroups, each writes its 64-column tile
+// to its own slot of the workspace; the last of the tile's S workgroups to
+// arrive (an atomic counter per tile) adds the S slots in split order -- a
+// fixed order whatever the arrival order, so results are bitwise repeatable
+// -- writes y and resets the counter.  No second kernel runs.
 // 16-byte slot of logical block `blk` in LDS row `rr` (0..15) of a 1 KB
 // activation block: rows are 64 bytes, so 8 (or 16) consecutive rows read by
 // one ds_read_b128 pass land in distinct banks
 __device__ __forceinline__ int a_slot(int rr, int blk) { return blk ^ (((rr >> 2) & 3) ^ (rr & 2)); }
 
-template <int TM, int SMAX>
+template <int TM>
+struct Mx32Cfg {
+  static constexpr int ROWS = 32 * TM;
+  static constexpr int RB = ROWS / 16;               // 1 KB activation blocks per step
+  static constexpr int RBW = RB / 2;                 // of them loaded by each wave of a half
+  static constexpr int SR = ROWS > 64 ? ROWS : 64;   // scale dwords per step slot (a 4-byte direct load fills 64)
+  static constexpr int LPS = RBW + 1 + 3;            // loads per wave per step: activation, its scales, weight x 3
+  static constexpr int HALF = 56 / LPS;              // K steps per wave at most (registers: (RBW + 2) x 4 + 2 a step)
+  static constexpr int LDS = 2 * HALF * RB * 1024 + 2 * HALF * SR * 4;
+};
+
+template <int TM>
 __global__ __launch_bounds__(256) void k_mx_gemm32(const MxGemmArgs p) {
-  constexpr int ROWS = 32 * TM;
-  constexpr int RB = ROWS / 16;              // 1 KB activation blocks (16 rows x 64 bytes) per step
-  constexpr int SR = ROWS > 64 ? ROWS : 64;  // scale dwords per step (a 4-byte direct load fills 64)
-  constexpr int HALF = SMAX / 2;             // K steps per wave at most
-  static_assert(SMAX % 2 == 0 && TM >= 1 && TM <= 4, "tile");
-  static_assert(3 * HALF <= 63, "weight loads must fit the vmcnt counter");
-  __shared__ __attribute__((aligned(16))) uint8_t sa[SMAX * RB * 1024];
-  __shared__ __attribute__((aligned(16))) uint32_t ssc[SMAX * SR];
+  using C = Mx32Cfg<TM>;
+  constexpr int ROWS = C::ROWS, RB = C::RB, RBW = C::RBW, SR = C::SR, LPS = C::LPS, HALF = C::HALF;
+  static_assert(TM == 1 || TM == 2 || TM == 4, "tile");
+  static_assert(2 * TM * 16 * 64 * 4 + ROWS * 64 * 4 <= 2 * HALF * RB * 1024, "epilogue staging fits");
+  __shared__ __attribute__((aligned(16))) uint8_t sa[2 * HALF * RB * 1024];  // [half][step][RB KB]
+  __shared__ __attribute__((aligned(16))) uint32_t ssc[2 * HALF * SR];
+  __shared__ int s_last;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int cg = wave & 1, kh = wave >> 1;
   const int c = lane & 31, j = lane >> 5;
   const int64_t m0 = (int64_t)blockIdx.z * ROWS;
-  const int64_t n0 = (int64_t)blockIdx.x * 64 + cg * 32;
+  const int64_t ntile0 = (int64_t)blockIdx.x * 64;
+  const int64_t n0 = ntile0 + cg * 32;
   const int s0 = blockIdx.y * p.steps_per_split;
-  const int ns = min(p.total_steps - s0, p.steps_per_split);  // >= 1
+  const int ns = min(p.total_steps - s0, p.steps_per_split);  // 1 .. 2 HALF
   const int h0 = (ns + 1) >> 1;
   const int tb = kh ? h0 : 0;         // this wave's first step within the range
   const int cnt = kh ? ns - h0 : h0;  // and its step count (0 when ns = 1, kh = 1)
+  const int last = tb + cnt - 1 > 0 ? tb + cnt - 1 : 0;
   const int steps0 = p.seg[0].steps;
   // first A column of range step t (segment 1 starts at its own A column)
   auto a_col = [&](int t) __attribute__((always_inline)) {
@@ -272,29 +291,6 @@ __global__ __launch_bounds__(256) void k_mx_gemm32(const MxGemmArgs p) {
     return s >= steps0 ? p.seg[1].a_k0 + (int64_t)(s - steps0) * 128 : (int64_t)s * 128;
   };
 
-  // --- activation range -> LDS (direct loads; rows past M re-read row M-1) --
-  {
-    const int rr = lane >> 2;
-    const int blk = (lane & 3) ^ (((rr >> 2) & 3) ^ (rr & 2));  // inverse of a_slot for this lane's slot
-    for (int b = wave; b < ns * RB; b += 4) {
-      const int t = b / RB, rb = b - t * RB;
-      int64_t m = m0 + rb * 16 + rr;
-      m = m < p.M ? m : p.M - 1;
-      __builtin_amdgcn_global_load_lds((glb_void*)(p.a_codes + m * p.lda + (a_col(t) + 32 * blk) / 2),
-                                       (lds_void*)(sa + b * 1024), 16, 0, 0);
-    }
-    for (int b = wave; b < ns * (SR / 64); b += 4) {
-      const int t = b / (SR / 64), hb = b - t * (SR / 64);
-      int64_t m = m0 + hb * 64 + lane;
-      m = m < p.M ? m : p.M - 1;
-      __builtin_amdgcn_global_load_lds((glb_void*)(p.a_scales + m * p.ldas + a_col(t) / 32),
-                                       (lds_void*)(ssc + t * SR + hb * 64), 4, 0, 0);
-    }
-  }
-  __asm__ volatile("" ::: "memory");
-
-  // --- this wave's weight steps -> registers (3 loads per step, all in flight)
-  // Steps past the wave's count re-read its last step (never used).
   int64_t n = n0 + c;
   n = n < p.N ? n : p.N - 1;
   const bool two = p.seg[1].steps > 0;
@@ -302,12 +298,34 @@ __global__ __launch_bounds__(256) void k_mx_gemm32(const MxGemmArgs p) {
   const uint8_t* ws0 = p.seg[0].w_scales + n * p.seg[0].ldws;
   const uint8_t* wc1 = two ? p.seg[1].w_codes + n * p.seg[1].ldw : wc0;
   const uint8_t* ws1 = two ? p.seg[1].w_scales + n * p.seg[1].ldws : ws0;
-  const int last = tb + cnt - 1 > 0 ? tb + cnt - 1 : 0;
+  const int rr = lane >> 2;                                        // row of a 1 KB block this lane fills
+  const int ablk = (lane & 3) ^ (((rr >> 2) & 3) ^ (rr & 2));      // inverse of a_slot for this lane's slot
+  const int srow = ROWS > 64 ? cg * 64 : 0;                        // scale rows of this wave's direct load
+
+  // --- issue: per step, this wave's activation blocks, scales and weights ---
+  // (steps past the wave's count re-read its last step; nothing uses them).
+  // Every load of the range is in flight before any is waited for, in step
+  // order; each goes to registers, so step t waits only for its own loads.
+  v4i av[HALF][RBW];
+  uint32_t asv[HALF];
   v4i bq[HALF][2];
   uint32_t bs[HALF];
 #pragma unroll
   for (int t = 0; t < HALF; ++t) {
-    const int s = s0 + min(tb + t, last);
+    const int st = min(tb + t, last);
+    const int64_t ac = a_col(st);
+#pragma unroll
+    for (int u = 0; u < RBW; ++u) {
+      int64_t m = m0 + (cg + 2 * u) * 16 + rr;
+      m = m < p.M ? m : p.M - 1;
+      av[t][u] = load16(p.a_codes + m * p.lda + (ac + 32 * ablk) / 2);
+    }
+    {
+      int64_t m = m0 + srow + lane;
+      m = m < p.M ? m : p.M - 1;
+      asv[t] = *reinterpret_cast<const uint32_t*>(p.a_scales + m * p.ldas + ac / 32);
+    }
+    const int s = s0 + st;
     const bool sb = s >= steps0;
     const int64_t kb = (int64_t)(sb ? s - steps0 : s) * 64;  // byte offset of the step in the code row
     const uint8_t* wc = (sb ? wc1 : wc0) + kb + 16 * j;
@@ -315,32 +333,34 @@ __global__ __launch_bounds__(256) void k_mx_gemm32(const MxGemmArgs p) {
     bq[t][1] = load16(wc + 32);  // block 2 + j
     bs[t] = *reinterpret_cast<const uint32_t*>((sb ? ws1 : ws0) + kb / 16);  // the step's 4 scales
   }
-  __asm__ volatile("" ::: "memory");
-  // the direct loads were issued before the 3*HALF weight loads: once at most
-  // that many are outstanding, this wave's LDS data has landed
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * HALF));
-  // a bare barrier between two compiler memory barriers (no memory access
-  // moves across it): __syncthreads()' fences would also wait for the weight
-  // loads still in flight
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
 
   v16f acc[TM];
 #pragma unroll
   for (int i = 0; i < TM; ++i) acc[i] = v16f{};
 #pragma unroll
   for (int t = 0; t < HALF; ++t) {
+    // the step's activation blocks and scales -> this half's LDS slot (each
+    // wave writes its share; the wait is for those registers only), then a
+    // bare barrier: __syncthreads() would also wait for every later step's
+    // loads still in flight
+    const int slot = kh * HALF + t;
+#pragma unroll
+    for (int u = 0; u < RBW; ++u)
+      *reinterpret_cast<v4i*>(sa + (slot * RB + cg + 2 * u) * 1024 + lane * 16) = av[t][u];
+    ssc[slot * SR + srow + lane] = asv[t];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
     if (t < cnt) {
-      const int tt = tb + t;
       const int bsc0 = (int)((bs[t] >> (8 * j)) & 0xFFu), bsc1 = (int)((bs[t] >> (8 * (2 + j))) & 0xFFu);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const int R = 32 * i + c, rr = R & 15;
-        const uint8_t* row = sa + (tt * RB + (R >> 4)) * 1024 + rr * 64;
-        const v4i a0 = *reinterpret_cast<const v4i*>(row + 16 * a_slot(rr, j));
-        const v4i a1 = *reinterpret_cast<const v4i*>(row + 16 * a_slot(rr, 2 + j));
-        const uint32_t asw = ssc[tt * SR + R];
+        const int R = 32 * i + c, r16 = R & 15;
+        const uint8_t* row = sa + (slot * RB + (R >> 4)) * 1024 + r16 * 64;
+        const v4i a0 = *reinterpret_cast<const v4i*>(row + 16 * a_slot(r16, j));
+        const v4i a1 = *reinterpret_cast<const v4i*>(row + 16 * a_slot(r16, 2 + j));
+        const uint32_t asw = ssc[slot * SR + R];
         const int asc0 = (int)((asw >> (8 * j)) & 0xFFu), asc1 = (int)((asw >> (8 * (2 + j))) & 0xFFu);
         acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(a0), widen(bq[t][0]), acc[i], 4, 4, 0, asc0,
                                                                   0, bsc0);
@@ -350,9 +370,10 @@ __global__ __launch_bounds__(256) void k_mx_gemm32(const MxGemmArgs p) {
     }
   }
 
-  // --- second-half sums join the first half's through LDS ----------------
+  // --- the halves' sums meet in LDS; the tile is staged row-major --------
   __syncthreads();  // every wave is done reading the activation range
-  float* red = reinterpret_cast<float*>(sa);  // [2 column groups][TM * 16][64 lanes]
+  float* red = reinterpret_cast<float*>(sa);                 // [2 column groups][TM * 16][64 lanes]
+  float* tile = red + 2 * TM * 16 * 64;                      // [ROWS][64] fp32
   if (kh) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -360,18 +381,79 @@ __global__ __launch_bounds__(256) void k_mx_gemm32(const MxGemmArgs p) {
       for (int v = 0; v < 16; ++v) red[((cg * TM + i) * 16 + v) * 64 + lane] = acc[i][v];
   }
   __syncthreads();
-  if (kh) return;
-  const int64_t nn = n0 + c;
-  if (nn >= p.N) return;
-  float* out = p.atomic ? p.part + (int64_t)blockIdx.y * p.M * p.N : p.y;
-  const int64_t ld = p.atomic ? p.N : p.ldy;
+  if (!kh) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t m = m0 + 32 * i + 8 * (v >> 2) + 4 * j + (v & 3);
-      if (m < p.M) out[m * ld + nn] = acc[i][v] + red[((cg * TM + i) * 16 + v) * 64 + lane];
+      for (int v = 0; v < 16; ++v) {
+        const int r = 32 * i + 8 * (v >> 2) + 4 * j + (v & 3);
+        tile[r * 64 + cg * 32 + c] = acc[i][v] + red[((cg * TM + i) * 16 + v) * 64 + lane];
+      }
+  }
+  __syncthreads();
+
+  // --- stores: 16-byte pieces, 16 per tile row ----------------------------
+  constexpr int PIECES = ROWS * 16 / 256;  // per thread
+  const bool vec = (p.N & 3) == 0 && (p.ldy & 3) == 0 && !(reinterpret_cast<uintptr_t>(p.y) & 15u);
+  auto store_y = [&](int r, int q, v4f v) __attribute__((always_inline)) {
+    const int64_t m = m0 + r, nn = ntile0 + 4 * q;
+    if (m >= p.M || nn >= p.N) return;
+    float* dst = p.y + m * p.ldy + nn;
+    if (vec && nn + 4 <= p.N) {
+      *reinterpret_cast<v4f*>(dst) = v;
+    } else {
+      for (int e = 0; e < 4 && nn + e < p.N; ++e) dst[e] = v[e];
     }
+  };
+  if (!p.atomic) {
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const int pc = (int)threadIdx.x + 256 * u, r = pc >> 4, q = pc & 15;
+      store_y(r, q, *reinterpret_cast<const v4f*>(tile + r * 64 + 4 * q));
+    }
+    return;
+  }
+  const int64_t tile_id = (int64_t)blockIdx.z * gridDim.x + blockIdx.x;
+  // this tile's S slots of ROWS x 64 fp32, one per split, contiguous
+  constexpr uint32_t SLOT = ROWS * 64 * 4;  // bytes
+  const __amdgpu_buffer_rsrc_t rs = shared_tile_rsrc(p.part + tile_id * p.splits * (ROWS * 64), SLOT * p.splits);
+#pragma unroll
+  for (int u = 0; u < PIECES; ++u) {
+    const int pc = (int)threadIdx.x + 256 * u;
+    store_shared_v4(rs, SLOT * blockIdx.y + 16 * pc, *reinterpret_cast<const v4f*>(tile + 4 * pc));
+  }
+  if (!arrive_last(p.counters + tile_id, p.splits, &s_last)) return;
+  // the last arrival: every other split's slot, all loads in flight per
+  // batch of PB pieces, then the sums in split order
+  constexpr int PB = PIECES < 4 ? PIECES : 4;
+  constexpr int SMX = 8;  // splits per pass of the load batch (more passes beyond)
+#pragma unroll
+  for (int u0 = 0; u0 < PIECES; u0 += PB) {
+    v4f sum[PB];
+#pragma unroll
+    for (int b = 0; b < PB; ++b) sum[b] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int sp0 = 0; sp0 < p.splits; sp0 += SMX) {
+      v4f ld[SMX][PB];
+#pragma unroll
+      for (int q = 0; q < SMX; ++q)
+#pragma unroll
+        for (int b = 0; b < PB; ++b) {
+          const int sp = sp0 + q, pc = (int)threadIdx.x + 256 * (u0 + b);
+          ld[q][b] = sp < p.splits && sp != (int)blockIdx.y ? load_shared_v4(rs, SLOT * sp + 16 * pc)
+                                                              : *reinterpret_cast<const v4f*>(tile + 4 * pc);
+        }
+#pragma unroll
+      for (int q = 0; q < SMX; ++q)
+#pragma unroll
+        for (int b = 0; b < PB; ++b)
+          if (sp0 + q < p.splits) sum[b] += ld[q][b];
+    }
+#pragma unroll
+    for (int b = 0; b < PB; ++b) {
+      const int pc = (int)threadIdx.x + 256 * (u0 + b);
+      store_y(pc >> 4, pc & 15, sum[b]);
+    }
+  }
 }
 
 // Split count: enough K splits that the grid fills the CUs, but never more
@@ -394,6 +476,7 @@ static int launch_mx(MxGemmArgs& p, int splits, hipStream_t st) {
   const int64_t n_tiles = cdiv(p.N, 16 * TN * NW);
   const int64_t m_tiles = cdiv(p.M, 16 * TM);
   p.steps_per_split = (int)cdiv(p.total_steps, splits);
+  splits = (int)cdiv(p.total_steps, p.steps_per_split);  // no empty split
   p.atomic = splits > 1;
   hipLaunchKernelGGL((k_mx_gemm<TM, TN, NW, SMAX>), dim3((unsigned)n_tiles, (unsigned)splits, (unsigned)m_tiles),
                      dim3(64 * NW), 0, st, p);
@@ -487,6 +570,12 @@ template <int TM, int SMAX>
 static int dispatch_tm(MxGemmArgs& p, size_t ws_bytes, hipStream_t st) {
   int splits = pick_splits<TM, 1, 4, SMAX>(p.M, p.N, p.total_steps);
   const size_t slab = (size_t)p.M * p.N * sizeof(float);
+  // the partial slabs follow the workspace's counter region (never touched here)
+  if (p.part) {
+    p.part = ws_bytes > kWsCounterBytes ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(p.part) + kWsCounterBytes)
+                                        : nullptr;
+    ws_bytes = ws_bytes > kWsCounterBytes ? ws_bytes - kWsCounterBytes : 0;
+  }
   if (splits > 1 && (!p.part || ws_bytes < (size_t)splits * slab)) {
     // not enough workspace for the partials: the serial-K kernel needs none
     const int fit = p.part ? (int)(ws_bytes / slab) : 0;
@@ -508,51 +597,58 @@ static int ws_splits(int64_t M, int64_t N, int steps) {
   return pick_splits<4, 1, 4, SMAX>(M, N, steps);
 }
 
-// 32x32x64 path: K steps per workgroup at most, and its split count
-constexpr int kMx32Smax = 16;
-
+// 32x32x64 path: splits of the K steps so that the (column, row) tiles fill
+// the CUs once (one resident round), each range within 2 HALF steps
 template <int TM>
 static int pick_splits32(int64_t M, int64_t N, int total_steps) {
+  using C = Mx32Cfg<TM>;
   const int64_t tiles = cdiv(N, 64) * cdiv(M, 32 * TM);
-  constexpr int lds = kMx32Smax * 2 * TM * 1024 + kMx32Smax * (32 * TM > 64 ? 32 * TM : 64) * 4;
-  const int per_cu = lds > 80 * 1024 ? 1 : 2;
+  const int per_cu = 1;  // one resident workgroup per CU (LDS and, for two row tiles, registers)
   const int64_t slots = (int64_t)per_cu * device_cu_count();
-  int splits = (int)cdiv(total_steps, kMx32Smax);
+  int splits = (int)cdiv(total_steps, 2 * C::HALF);
   while ((int64_t)(splits + 1) * tiles <= slots && splits < total_steps) ++splits;
   const int steps = (int)cdiv(total_steps, splits);
   return (int)cdiv(total_steps, steps);
 }
 
-static int ws_splits32(int64_t M, int64_t N, int steps) {
-  if (M <= 32) return pick_splits32<1>(M, N, steps);
-  if (M <= 64) return pick_splits32<2>(M, N, steps);
-  return pick_splits32<4>(M, N, steps);
+template <int TM>
+static size_t ws_bytes32(int64_t M, int64_t N, int splits) {
+  const int64_t tiles = cdiv(N, 64) * cdiv(M, 32 * TM);
+  if (tiles > kWsMaxTiles) return 0;  // too many tiles for the counters: no split
+  return splits > 1 ? kWsCounterBytes + (size_t)tiles * splits * (32 * TM) * 64 * sizeof(float) : 0;
+}
+
+static size_t ws32(int64_t M, int64_t N, int steps) {
+  if (M <= 32) return ws_bytes32<1>(M, N, pick_splits32<1>(M, N, steps));
+  if (M <= 64) return ws_bytes32<2>(M, N, pick_splits32<2>(M, N, steps));
+  return ws_bytes32<4>(M, N, pick_splits32<4>(M, N, steps));
 }
 
 size_t ws_mx_gemm(int64_t M, int64_t N, int64_t Ktot) {
   if (M <= 0 || N <= 0 || Ktot <= 0) return 0;
   const int steps = (int)cdiv(Ktot, 128) + 1;  // + 1: the tail segment may start a step of its own
-  // the largest split count any kernel choice can make for these steps
+  // the largest workspace any kernel choice can ask for at these extents
   int splits = ws_splits<8>(M, N, steps);
   const int s16 = ws_splits<16>(M, N, steps);
   splits = splits > s16 ? splits : s16;
+  size_t b = splits > 1 ? kWsCounterBytes + (size_t)splits * M * N * sizeof(float) : 0;
   if (M > 16) {
-    const int s32 = ws_splits32(M, N, steps);
-    splits = splits > s32 ? splits : s32;
+    for (int st = steps - 1; st <= steps; ++st) {
+      const size_t b32 = ws32(M, N, st);
+      b = b > b32 ? b : b32;
+    }
   }
-  return splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
+  return b;
 }
 
 template <int TM>
 static int dispatch32(MxGemmArgs& p, size_t ws_bytes, hipStream_t st) {
+  using C = Mx32Cfg<TM>;
   int splits = pick_splits32<TM>(p.M, p.N, p.total_steps);
-  const size_t slab = (size_t)p.M * p.N * sizeof(float);
-  if (splits > 1 && (!p.part || ws_bytes < (size_t)splits * slab)) {
-    const int fit = p.part ? (int)(ws_bytes / slab) : 0;
-    const int need = (int)cdiv(p.total_steps, kMx32Smax);
-    if (fit >= need && fit >= 2)
-      splits = fit;
-    else if (need == 1)
+  const size_t need = ws_bytes32<TM>(p.M, p.N, splits);
+  if (splits > 1 && (!p.part || need == 0 || ws_bytes < need || (reinterpret_cast<uintptr_t>(p.part) & 15u))) {
+    // not enough workspace for the split tiles: the serial-K kernel needs none
+    if (cdiv(p.total_steps, 2 * C::HALF) == 1)
       splits = 1;
     else
       return launch_serial<4>(p, st);
@@ -560,12 +656,16 @@ static int dispatch32(MxGemmArgs& p, size_t ws_bytes, hipStream_t st) {
   const int64_t n_tiles = cdiv(p.N, 64), m_tiles = cdiv(p.M, 32 * TM);
   p.steps_per_split = (int)cdiv(p.total_steps, splits);
   splits = (int)cdiv(p.total_steps, p.steps_per_split);
+  p.splits = splits;
   p.atomic = splits > 1;
-  hipLaunchKernelGGL((k_mx_gemm32<TM, kMx32Smax>), dim3((unsigned)n_tiles, (unsigned)splits, (unsigned)m_tiles),
-                     dim3(256), 0, st, p);
-  int s = check_launch("mx_gemm");
-  if (s || splits == 1) return s;
-  return launch_splitk_reduce(p.part, splits, p.M * p.N, p.y, st);
+  if (splits > 1) {
+    uint8_t* ws = reinterpret_cast<uint8_t*>(p.part);
+    p.counters = reinterpret_cast<uint32_t*>(ws);
+    p.part = reinterpret_cast<float*>(ws + kWsCounterBytes);
+  }
+  hipLaunchKernelGGL((k_mx_gemm32<TM>), dim3((unsigned)n_tiles, (unsigned)splits, (unsigned)m_tiles), dim3(256), 0,
+                     st, p);
+  return check_launch("mx_gemm");
 }
 
 static bool aligned4(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 3u) == 0; }

@@ -32,11 +32,18 @@ int main(int argc, char** argv) {
   gbw_weight w{}; w.fmt = GBW_FMT_E8M0_B32; w.n_experts = 1; w.N = N; w.K = K; w.codes = mk(N * K / 2); w.scales = mk(N * K / 32);
   gbw_weight r{}; r.fmt = GBW_FMT_E8M0_B32; r.n_experts = 1; r.N = N; r.K = tail; r.codes = mk(N * tail / 2 + (tail ? 0 : 16)); r.scales = mk(N * tail / 32 + 1);
   float* y = (float*)malloc(M * N * 4);
+  // no workspace, then one zeroed workspace for two calls in a row: the
+  // arrival counters at its front (64 KiB) must be back at zero after each
   for (int wsmode = 0; wsmode < 2; ++wsmode) {
     size_t wsb = wsmode ? gbw::ws_mx_gemm(M, N, K + tail) : 0;
-    void* ws = wsb ? malloc(wsb) : nullptr;
-    int st = tail ? residual_tail_gemm(M, &a, &w, &r, tail, y, 0, ws, wsb, nullptr) : mx_gemm(M, &a, &w, y, 0, ws, wsb, nullptr);
-    printf("mx M=%lld N=%lld K=%lld tail=%lld ws=%zu status %d\n", (long long)M, (long long)N, (long long)K, (long long)tail, wsb, st);
+    uint8_t* ws = wsb ? (uint8_t*)calloc(wsb, 1) : nullptr;
+    for (int rep = 0; rep < (wsmode ? 2 : 1); ++rep) {
+      int st = tail ? residual_tail_gemm(M, &a, &w, &r, tail, y, 0, ws, wsb, nullptr) : mx_gemm(M, &a, &w, y, 0, ws, wsb, nullptr);
+      size_t left = 0;
+      for (size_t i = 0; wsb && i < 65536 / 4; ++i) left += ((uint32_t*)ws)[i] != 0;
+      printf("mx M=%lld N=%lld K=%lld tail=%lld ws=%zu status %d counters left %zu\n", (long long)M, (long long)N,
+             (long long)K, (long long)tail, wsb, st, left);
+    }
     free(ws);
   }
   return 0;

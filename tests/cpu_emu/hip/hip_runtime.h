@@ -61,6 +61,33 @@ inline unsigned long long atomicOr(unsigned long long* p, unsigned long long v) 
 template <class T> inline T __shfl_xor(T v, int) { return v; }
 inline unsigned atomicAdd(unsigned* p, unsigned v) { std::lock_guard<std::mutex> g(emu_atomic_mu); auto o = *p; *p += v; return o; }
 inline void __threadfence() { std::atomic_thread_fence(std::memory_order_seq_cst); }
+#define __HIP_MEMORY_SCOPE_AGENT 3
+template <class T, class V> inline void emu_atomic_store(T* p, V v) { T t = (T)v; __atomic_store(p, &t, __ATOMIC_SEQ_CST); }
+template <class T> inline T emu_atomic_load(T* p) { T t; __atomic_load(p, &t, __ATOMIC_SEQ_CST); return t; }
+#define __hip_atomic_store(p, v, order, scope) emu_atomic_store((p), (v))
+#define __hip_atomic_load(p, order, scope) emu_atomic_load((p))
+#define __hip_atomic_fetch_add(p, v, order, scope) __atomic_fetch_add((p), (v), __ATOMIC_SEQ_CST)
+// raw buffer resources: a base and a byte count; accesses past the count read
+// zero and write nothing, as on the hardware (within the count, ASan checks
+// the access against the real allocation)
+struct emu_rsrc { char* base; uint32_t n; };
+typedef emu_rsrc __amdgpu_buffer_rsrc_t;
+#define __builtin_amdgcn_make_buffer_rsrc(p, stride, num, flags) emu_rsrc{(char*)(p), (uint32_t)(num)}
+typedef unsigned int emu_v4u __attribute__((ext_vector_type(4)));
+inline void emu_buf_store(emu_v4u v, emu_rsrc r, int off) {
+  if ((uint32_t)off + 16 > r.n) return;
+  std::lock_guard<std::mutex> g(emu_atomic_mu);
+  memcpy(r.base + off, &v, 16);
+}
+inline emu_v4u emu_buf_load(emu_rsrc r, int off) {
+  emu_v4u v = {0, 0, 0, 0};
+  if ((uint32_t)off + 16 > r.n) return v;
+  std::lock_guard<std::mutex> g(emu_atomic_mu);
+  memcpy(&v, r.base + off, 16);
+  return v;
+}
+#define __builtin_amdgcn_raw_buffer_store_b128(v, r, off, soff, aux) emu_buf_store((v), (r), (off) + (soff))
+#define __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, aux) emu_buf_load((r), (off) + (soff))
 
 #define __builtin_amdgcn_readfirstlane(x) (x)
 // DPP: the 64 lanes of a wave exchange through a per-wave array (all lanes

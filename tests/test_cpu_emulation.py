@@ -112,4 +112,4 @@ def test_lut_gemm_in_bounds(build_dir, M, N, K, group):
 def test_mx_gemm_in_bounds(build_dir, M, N, K, tail):
     exe = _build(build_dir, "mx_gemm.hip", "drv_mx.cpp", "emu_mx")
     out = _run(exe, M, N, K, tail)
-    assert out.count("status 0") == 2, out
+    assert out.count("status 0 counters left 0") == 3, out

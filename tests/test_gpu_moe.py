@@ -694,3 +694,80 @@ def test_moe_prquant_down_residual(T, H, I, E, k, tail):
     e_plain = np.linalg.norm(to_np(y_plain) - exact) / np.linalg.norm(exact)
     print(f"[stats] down-weight error with residual {e_res:.4f}, plain {e_plain:.4f}", flush=True)
     assert e_res < e_plain
+
+
+def _offline_copy_weight(codes, scales, I, tail):
+    """PRQuant offline copy: the gate and up weights with their last `tail`
+    rows (output channels) duplicated, [E][2(I + tail)][...]: gate rows
+    [0, I + tail), then up rows.  Rows are quantized along K on their own, so
+    duplicating quantized rows is quantizing the duplicated weight."""
+    g, u = codes[:, :I], codes[:, I:]
+    gs, us = scales[:, :I], scales[:, I:]
+    c = torch.cat([g, g[:, I - tail:], u, u[:, I - tail:]], dim=1).contiguous()
+    sc = torch.cat([gs, gs[:, I - tail:], us, us[:, I - tail:]], dim=1).contiguous()
+    return c, sc
+
+
+@pytest.mark.parametrize("T,H,I,E,k,tail", [(300, 512, 256, 8, 2, 128), (64, 1024, 384, 16, 8, 128),
+                                            (200, 256, 768, 6, 4, 128)])
+def test_moe_prquant_offline_copy(T, H, I, E, k, tail):
+    """PRQuant's offline copy (§4 "Activation tail construction"): gate/up
+    run over I + tail intermediate columns whose last `tail` are copies of
+    columns I - tail .. I - 1, so the FFN itself emits [h, h_tail] and no tail
+    copy runs.  Its h codes equal the online copy's bit for bit (the tail
+    starts on a 32-block boundary), and the down stage over I + tail matches
+    the oracle's residual formula."""
+    banner(f"moe prquant offline copy T={T} H={H} I={I} E={E} k={k} tail={tail}")
+    d = synth.moe_problem(T, H, I, E, seed=7, device=DEV)
+    route, ref_route = _check_route(d["logits"], k)
+    P = T * k
+    q = gbw.mx_quantize(d["w_gate_up"].reshape(E * 2 * I, H), gbw.FMT_E8M0_B32)
+    gc, gs = q.codes.view(E, 2 * I, H // 2), q.scales.view(E, 2 * I, H // 32)
+    Wgu = gbw.Weight(gbw.FMT_E8M0_B32, 2 * I, H, gc, gs, n_experts=E)
+    oc, os_ = _offline_copy_weight(gc, gs, I, tail)
+    Woff = gbw.Weight(gbw.FMT_E8M0_B32, 2 * (I + tail), H, oc, os_, n_experts=E)
+    xq = gbw.mx_quantize(d["x"], gbw.FMT_E8M0_B32)
+    W2 = (I + tail) // 2
+    on_c = torch.empty((P, W2), dtype=torch.uint8, device=DEV)
+    on_s = torch.empty((P, (I + tail) // 32), dtype=torch.uint8, device=DEV)
+    gbw.moe_grouped_gemm(gbw.MOE_GATEUP_SWIGLU, route, xq, Wgu, h_codes=on_c, h_scales=on_s, h_tail=tail)
+    off_c = torch.empty_like(on_c)
+    off_s = torch.empty_like(on_s)
+    gbw.moe_grouped_gemm(gbw.MOE_GATEUP_SWIGLU, route, xq, Woff, h_codes=off_c, h_scales=off_s)
+    torch.cuda.synchronize()
+    assert torch.equal(off_c, on_c) and torch.equal(off_s, on_s), "offline copy h differs from the online copy"
+    Waug, _ = _prquant_weights(d["w_down"], tail)
+    y = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, gbw.Act(gbw.FMT_E8M0_B32, off_c, off_s), Waug, y=y)
+    # the oracle's own chain: Q(x), gate/up, SwiGLU, Q(h), residual down
+    ac, as_ = on.quantize_e8m0_b32(d["x"].float().cpu().numpy())
+    gq = [on.quantize_e8m0_b32(d["w_gate_up"][e].cpu().numpy()) for e in range(E)]
+    g, u = on.moe_gateup(ac, as_, "e8m0_b32", ref_route, [c for c, _ in gq], [s_ for _, s_ in gq])
+    h_ref = on.swiglu_bf16(g, u)
+    qc, qs = on.quantize_e8m0_b32(oracle.bf16_bits_to_f32(h_ref))
+    wd = d["w_down"].cpu().numpy()
+    wc, ws, rc, rs = [], [], [], []
+    for e in range(E):
+        c, s_ = on.quantize_e8m0_b32(wd[e])
+        r_c, r_s = on.quantize_e8m0_b32(oracle.residual_weight(wd[e], c, s_, tail))
+        wc.append(c); ws.append(s_); rc.append(r_c); rs.append(r_s)
+    y_ref = on.moe_down_combine_residual(qc, qs, ref_route, np.array(wc), np.array(ws), np.array(rc), np.array(rs),
+                                         tail)
+    assert on.last_inexact == 0
+    # the down stage on the oracle's h with its tail columns: every token within 1e-3
+    hqa = gbw.Act(gbw.FMT_E8M0_B32, torch.from_numpy(np.concatenate([qc, qc[:, (I - tail) // 2:]], 1)).to(DEV),
+                  torch.from_numpy(np.concatenate([qs, qs[:, (I - tail) // 32:]], 1)).to(DEV))
+    yo = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hqa, Waug, y=yo)
+    assert_rows_close(to_np(yo), y_ref, what="offline-copy down on the oracle's h")
+    # pipeline: tokens whose h requantized identically within 1e-3
+    gcn, gsn = to_np(off_c)[:, :I // 2], to_np(off_s)[:, :I // 32]
+    same = (gcn == qc).all(axis=1) & (gsn == qs).all(axis=1)
+    pp = ref_route["pair_pos"]
+    clean = same[pp].all(axis=1)
+    yv = to_np(y).astype(np.float64)
+    nrm = np.linalg.norm(y_ref, axis=1)
+    err = np.abs(yv - y_ref).max(axis=1)
+    assert np.all(err[clean] <= 1e-3 * nrm[clean]), "clean tokens outside 1e-3"
+    print(f"[stats] offline copy: tokens with identically requantized h {clean.mean():.1%}", flush=True)
+    assert clean.mean() > 0.5
