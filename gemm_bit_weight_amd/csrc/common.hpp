@@ -174,6 +174,18 @@ __device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
 
 __device__ __forceinline__ v4i load16(const void* p) { return *reinterpret_cast<const v4i*>(p); }
 
+// Direct global -> LDS load of 16 bytes per lane (lane l's bytes land at
+// lds + 16 l; `lds` must be the same in every lane of the wave).  Measured on
+// this chip: a load instruction whose 64 lanes read one contiguous 1 KiB
+// streams far faster than one whose lanes spread over many rows (every
+// distinct row costs its own address translation in flight), so weight tiles
+// are copied into LDS this way, a kilobyte of one row at a time.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds, 16, 0, 0);
+}
+
 __host__ __device__ constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Split-K GEMM workspaces (mx_gemm, residual_tail_gemm, lut_gemm) start with

@@ -117,83 +117,93 @@ struct LutArgs {
 // ---------------------------------------------------------------------------
 // M <= 16: one workgroup per 16 output rows n over the whole of K
 // ---------------------------------------------------------------------------
-// Wave w takes the 128-element chunks w, w + NW, ...; a lane (r16 = n, q)
-// holds elements [32q, 32q + 32) of a chunk and feeds them to four
-// v_mfma_f32_16x16x32_f16 steps.  Every weight load of a batch of CB chunks is
-// issued before the first is used, so a CU has all its weight bytes in flight
-// at once.  The x rows of the wave's chunks (M x 128 each) are converted once,
-// by the wave that uses them, into its own LDS slice (16 lanes per row, the
-// chunk's prescale from a 16-lane maximum); rows >= M of that slice are never
-// written and feed only output rows that are never stored.  The NW per-wave
-// 16 x 16 partial products are summed in LDS in wave order (a fixed order:
-// repeatable).
-template <int NW, int CB>
+// The 16 rows' indices and tables are contiguous in HBM ([N][K/2] and
+// [N][K/group][16]); a segment of up to KSEG elements of all 16 rows is
+// copied into LDS by direct loads, each instruction one contiguous kilobyte
+// of one row (LDS rows padded by 16 bytes, so the 16 rows a fragment read
+// touches fall in different banks).  Then wave w takes the 128-element
+// chunks w, w + NW, ... of the segment: it converts the chunk's x rows
+// (16 lanes per row, the chunk's prescale from a 16-lane maximum) into its
+// own LDS slot -- rows >= M are never written and feed only outputs that are
+// never stored -- and a lane (r16 = n, q) decodes elements [32q, 32q + 32)
+// of row n and feeds them to four v_mfma_f32_16x16x32_f16 steps.  The NW
+// per-wave 16 x 16 partial products are summed in LDS in wave order (a fixed
+// order: repeatable).
+template <int NW>
 __global__ __launch_bounds__(64 * NW) void k_lut_gemv(const LutArgs p) {
-  constexpr int XROW = 128 * 2 + 16;  // LDS bytes per x row in a chunk slot (16-byte pad)
-  __shared__ __attribute__((aligned(16))) uint8_t xs[NW][CB][16 * XROW];
-  __shared__ __attribute__((aligned(16))) float invs[NW][CB][16];
+  constexpr int XROW = 128 * 2 + 16;         // LDS bytes per x row of a chunk slot (16-byte pad)
+  constexpr int WLDS = 64 * 1024;            // weight segment: 16 rows of indices + tables
+  __shared__ __attribute__((aligned(16))) uint8_t sw[WLDS + 2 * 16 * 16];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[NW][16 * XROW];
+  __shared__ __attribute__((aligned(16))) float invs[NW][16];
   __shared__ float red[NW][256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int64_t n = n0 + r16 < p.N ? n0 + r16 : p.N - 1;
-  const int chunks = (int)(p.K / 128);
-  const int64_t G = p.K / p.group;
   const int M = (int)p.M;
   const int xrounds = (M * 16 + 63) / 64;  // rounds of 64 pieces (16 lanes per row)
-  const uint8_t* wr = p.idx + n * (p.K / 2);
-  const uint16_t* cr = p.cent + n * G * 16;
+  const int64_t G = p.K / p.group;
+  const int kseg = p.group == 32 ? 2048 : 4096;   // elements per segment: 16 rows fit WLDS
+  const int tpc = 128 / p.group;                  // tables per 128-element chunk
+  const int64_t tb_row = (int64_t)G * 32;         // table bytes per row in HBM
 
   v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int cb0 = wave; cb0 < chunks; cb0 += NW * CB) {
-    v4i iq[CB], ca[CB], cc[CB];
-#pragma unroll
-    for (int b = 0; b < CB; ++b) {
-      const int c0 = cb0 + NW * b;
-      const int c = c0 < chunks ? c0 : chunks - 1;  // clamped: redundant loads hit L2
-      const int64_t k = (int64_t)c * 128 + 32 * q;  // this lane's first element
-      iq[b] = load16(wr + k / 2);
-      const uint16_t* t = cr + (k / p.group) * 16;
-      ca[b] = load16(t);
-      cc[b] = load16(t + 8);
+  for (int64_t k0 = 0; k0 < p.K; k0 += kseg) {
+    const int seg = (int)(p.K - k0 < kseg ? p.K - k0 : kseg);
+    const int ib = seg / 2, tbb = seg / p.group * 32;  // index and table bytes per row of the segment
+    const int irow = ib + 16, trow = tbb + 16;          // LDS row strides
+    uint8_t* const si = sw;
+    uint8_t* const st = sw + 16 * irow;
+    // copy: 16 rows x ib index bytes, then 16 rows x tbb table bytes, 1 KiB per instruction
+    const int ipc = (ib + 1023) / 1024, tpcs = (tbb + 1023) / 1024;  // pieces per row
+    for (int pc = wave; pc < 16 * (ipc + tpcs); pc += NW) {
+      const bool isidx = pc < 16 * ipc;
+      const int rel = isidx ? pc : pc - 16 * ipc;
+      const int r = rel / (isidx ? ipc : tpcs), part = rel % (isidx ? ipc : tpcs);
+      const int len = isidx ? ib : tbb;
+      const int o = part * 1024 + lane * 16;
+      int64_t n = n0 + r;
+      n = n < p.N ? n : p.N - 1;
+      if (o < len) {
+        const uint8_t* src = isidx ? p.idx + n * (p.K / 2) + k0 / 2 + o
+                                   : reinterpret_cast<const uint8_t*>(p.cent) + n * tb_row + (k0 / p.group) * 32 + o;
+        load_lds16(src, (isidx ? si + r * irow : st + r * trow) + part * 1024);
+      }
     }
-    // x: M rows x 128 of each chunk, 16 pieces of 8 per row -> prescaled fp16
-    // in the order 0,2,4,6,1,3,5,7 into this wave's slot
-#pragma unroll
-    for (int b = 0; b < CB; ++b) {
-      const int c0 = cb0 + NW * b;
-      const int c = c0 < chunks ? c0 : chunks - 1;
+    __syncthreads();
+    const int nch = seg / 128;
+    for (int c = wave; c < nch; c += NW) {
+      // x rows of the chunk -> prescaled fp16 in decode order, this wave's slot
       for (int t = 0; t < xrounds; ++t) {
         const int u = lane + 64 * t;
         const int m = u >> 4, j = u & 15;
         const bool ok = m < M;  // the same for all 16 lanes of a DPP row
-        const v4i v = ok ? load16(p.x + (int64_t)m * p.K + (int64_t)c * 128 + 8 * j) : v4i{0, 0, 0, 0};
-        const int s = chunk_prescale(row16_max_u32(bf16x8_absmax_bits(v)));
+        const v4i v = ok ? load16(p.x + (int64_t)m * p.K + k0 + (int64_t)c * 128 + 8 * j) : v4i{0, 0, 0, 0};
+        const int sx = chunk_prescale(row16_max_u32(bf16x8_absmax_bits(v)));
         if (ok) {
-          *reinterpret_cast<v4i*>(&xs[wave][b][m * XROW + 16 * j]) = x8_to_f16(v, pow2f(s));
-          if (j == 0) invs[wave][b][m] = pow2f(-s);
+          *reinterpret_cast<v4i*>(&xs[wave][m * XROW + 16 * j]) = x8_to_f16(v, pow2f(sx));
+          if (j == 0) invs[wave][m] = pow2f(-sx);
         }
       }
-    }
-#pragma unroll
-    for (int b = 0; b < CB; ++b) {
-      if (cb0 + NW * b >= chunks) break;
+      const v4i iq = *reinterpret_cast<const v4i*>(si + r16 * irow + c * 64 + 16 * q);
+      const uint8_t* tr = st + r16 * trow + (c * tpc + (32 * q) / p.group) * 32;
       uint32_t L[4], H[4];
-      split_table(ca[b], cc[b], L, H);
+      split_table(*reinterpret_cast<const v4i*>(tr), *reinterpret_cast<const v4i*>(tr + 16), L, H);
       v4f part = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         uint32_t o[4];
-        decode8((uint32_t)iq[b][s], L, H, o);
+        decode8((uint32_t)iq[s], L, H, o);
         const v8h bfrag = __builtin_bit_cast(v8h, v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]});
-        const v8h afrag = *reinterpret_cast<const v8h*>(&xs[wave][b][r16 * XROW + (32 * q + 8 * s) * 2]);
+        const v8h afrag = *reinterpret_cast<const v8h*>(&xs[wave][r16 * XROW + (32 * q + 8 * s) * 2]);
         part = __builtin_amdgcn_mfma_f32_16x16x32_f16(afrag, bfrag, part, 0, 0, 0);
       }
       // part[r]: x row 4q + r; undo that row's prescale for this chunk
-      const v4f inv = *reinterpret_cast<const v4f*>(&invs[wave][b][4 * q]);
+      const v4f inv = *reinterpret_cast<const v4f*>(&invs[wave][4 * q]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] += part[r] * inv[r];
     }
+    __syncthreads();  // the segment's LDS copy is free again
   }
   // acc[r]: x row 4q + r, output row n0 + r16
 #pragma unroll
@@ -411,7 +421,7 @@ __global__ __launch_bounds__(512) void k_lut_gemm(const LutArgs p) {
   }
 }
 
-constexpr int kGemvNW = 16, kGemvCB = 2;
+constexpr int kGemvNW = 16;
 
 // K splits for the M > 16 kernel: about one workgroup per CU over all tiles,
 // each K group with at least one chunk when K allows it
@@ -465,7 +475,7 @@ extern "C" int lut_gemm(int64_t M, int64_t N, int64_t K, int32_t group, const ui
   p.y = y;
   hipStream_t s = as_stream(stream);
   if (M <= 16) {
-    hipLaunchKernelGGL((k_lut_gemv<kGemvNW, kGemvCB>), dim3((unsigned)cdiv(N, 16)), dim3(64 * kGemvNW), 0, s, p);
+    hipLaunchKernelGGL((k_lut_gemv<kGemvNW>), dim3((unsigned)cdiv(N, 16)), dim3(64 * kGemvNW), 0, s, p);
     return check_launch("lut_gemm");
   }
   const int chunks = (int)(K / 128);

@@ -95,7 +95,7 @@ def test_moe_route_in_bounds_and_exact(build_dir, T, E, K, mode):
 
 
 @pytest.mark.parametrize("M,N,K,group", [(1, 40, 384, 32), (5, 256, 1024, 128), (17, 40, 384, 32), (64, 128, 2048, 128),
-                                         (70, 100, 1024, 64), (33, 64, 512, 32)])
+                                         (70, 100, 1024, 64), (33, 64, 512, 32), (3, 20, 4608, 64), (16, 33, 2176, 32)])
 def test_lut_gemm_in_bounds(build_dir, M, N, K, group):
     """Ragged M and N, every group size; for M > 16 the split-K path twice (its
     arrival counters must be left at zero) and the no-workspace path."""

@@ -38,7 +38,8 @@ def _ref(d, group):
 
 @pytest.mark.parametrize("M,N,K,group", [(1, 64, 256, 128), (3, 100, 512, 64), (8, 256, 1024, 128),
                                          (17, 130, 384, 32), (64, 512, 2048, 128), (70, 96, 640, 128),
-                                         (128, 64, 256, 64)])
+                                         (128, 64, 256, 64), (3, 100, 4608, 64), (16, 50, 2176, 32),
+                                         (11, 70, 8320, 128)])
 def test_lut_gemm_small(M, N, K, group):
     banner(f"lut_gemm {M}x{N}x{K} group {group}")
     w = synth.clustered_weight(N, K, group=group, seed=M + N, device="cpu", iters=4)
