@@ -240,12 +240,20 @@ def lut_decode(gbw, synth, torch, M):
     w_bytes = N * K // 2 + N * (K // 128) * 16 * 2
     R = max(2, int(2 * 256e6 // w_bytes) + 1)
     base = synth.lut_problem(M, N=N, K=K, group=128, seed=0, device="cuda", iters=10)
-    reps = [(base["idx"], base["centroids"])]
-    for r in range(1, R):  # replicas: same statistics, distinct memory
+    # replicas (same statistics, distinct memory) carved from one allocation,
+    # so their placement does not depend on the caching allocator's history
+    ib, cb = N * K // 2, N * (K // 128) * 16 * 2
+    pool = torch.empty(R * (ib + cb), dtype=torch.uint8, device="cuda")
+    reps = []
+    for r in range(R):
         g = torch.Generator(device="cuda")
         g.manual_seed(r)
-        perm = torch.randperm(N, generator=g, device="cuda")
-        reps.append((base["idx"][perm].contiguous(), base["centroids"][perm].contiguous()))
+        perm = torch.randperm(N, generator=g, device="cuda") if r else torch.arange(N, device="cuda")
+        idx = pool[r * (ib + cb):r * (ib + cb) + ib].view(N, K // 2)
+        cent = pool[r * (ib + cb) + ib:(r + 1) * (ib + cb)].view(torch.float16).view(N, K // 128, 16)
+        idx.copy_(base["idx"][perm])
+        cent.copy_(base["centroids"][perm])
+        reps.append((idx, cent))
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
     # zeroed once: the split-K arrival counters at its front start at zero and every call leaves them so
     ws = torch.zeros(max(1, gbw.workspace_size(gbw.OP_LUT_GEMM, M, N, K)), dtype=torch.uint8, device="cuda")

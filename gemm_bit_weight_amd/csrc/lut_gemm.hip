@@ -121,15 +121,16 @@ struct LutArgs {
 // [N][K/group][16]); a segment of up to KSEG elements of all 16 rows is
 // copied into LDS by direct loads, each instruction one contiguous kilobyte
 // of one row (LDS rows padded by 16 bytes, so the 16 rows a fragment read
-// touches fall in different banks).  Then wave w takes the 128-element
-// chunks w, w + NW, ... of the segment: it converts the chunk's x rows
+// touches fall in different banks).  Each wave has at most two 128-element
+// chunks of a segment, w and w + NW; their x rows are loaded into registers
+// before the copy is waited for.  Then wave w converts each chunk's x rows
 // (16 lanes per row, the chunk's prescale from a 16-lane maximum) into its
 // own LDS slot -- rows >= M are never written and feed only outputs that are
 // never stored -- and a lane (r16 = n, q) decodes elements [32q, 32q + 32)
 // of row n and feeds them to four v_mfma_f32_16x16x32_f16 steps.  The NW
 // per-wave 16 x 16 partial products are summed in LDS in wave order (a fixed
 // order: repeatable).
-template <int NW>
+template <int NW, int XRND>
 __global__ __launch_bounds__(64 * NW) void k_lut_gemv(const LutArgs p) {
   constexpr int XROW = 128 * 2 + 16;         // LDS bytes per x row of a chunk slot (16-byte pad)
   constexpr int WLDS = 64 * 1024;            // weight segment: 16 rows of indices + tables
@@ -140,10 +141,10 @@ __global__ __launch_bounds__(64 * NW) void k_lut_gemv(const LutArgs p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int M = (int)p.M;
-  const int xrounds = (M * 16 + 63) / 64;  // rounds of 64 pieces (16 lanes per row)
+  const int M = (int)p.M;  // XRND = ceil(M / 4): rounds of 64 x pieces (16 lanes per row)
   const int64_t G = p.K / p.group;
   const int kseg = p.group == 32 ? 2048 : 4096;   // elements per segment: 16 rows fit WLDS
+  static_assert(NW == 16, "a segment of 4096 elements is two chunks per wave");
   const int tpc = 128 / p.group;                  // tables per 128-element chunk
   const int64_t tb_row = (int64_t)G * 32;         // table bytes per row in HBM
 
@@ -154,6 +155,19 @@ __global__ __launch_bounds__(64 * NW) void k_lut_gemv(const LutArgs p) {
     const int irow = ib + 16, trow = tbb + 16;          // LDS row strides
     uint8_t* const si = sw;
     uint8_t* const st = sw + 16 * irow;
+    const int nch = seg / 128;  // <= 2 NW: a wave has at most two chunks of a segment
+    // x of the wave's chunks wave and wave + NW, loaded before the weights
+    // are waited for (rows >= M load row M - 1 and are never stored)
+    v4i xv[2][XRND];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = wave + NW * i < nch ? wave + NW * i : nch - 1;
+#pragma unroll
+      for (int t = 0; t < XRND; ++t) {
+        const int m = min((lane + 64 * t) >> 4, M - 1);
+        xv[i][t] = load16(p.x + (int64_t)m * p.K + k0 + (int64_t)c * 128 + 8 * (lane & 15));
+      }
+    }
     // copy: 16 rows x ib index bytes, then 16 rows x tbb table bytes, 1 KiB per instruction
     const int ipc = (ib + 1023) / 1024, tpcs = (tbb + 1023) / 1024;  // pieces per row
     for (int pc = wave; pc < 16 * (ipc + tpcs); pc += NW) {
@@ -171,17 +185,18 @@ __global__ __launch_bounds__(64 * NW) void k_lut_gemv(const LutArgs p) {
       }
     }
     __syncthreads();
-    const int nch = seg / 128;
-    for (int c = wave; c < nch; c += NW) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = wave + NW * i;
+      if (c >= nch) break;  // uniform over the wave
       // x rows of the chunk -> prescaled fp16 in decode order, this wave's slot
-      for (int t = 0; t < xrounds; ++t) {
+#pragma unroll
+      for (int t = 0; t < XRND; ++t) {
         const int u = lane + 64 * t;
         const int m = u >> 4, j = u & 15;
-        const bool ok = m < M;  // the same for all 16 lanes of a DPP row
-        const v4i v = ok ? load16(p.x + (int64_t)m * p.K + k0 + (int64_t)c * 128 + 8 * j) : v4i{0, 0, 0, 0};
-        const int sx = chunk_prescale(row16_max_u32(bf16x8_absmax_bits(v)));
-        if (ok) {
-          *reinterpret_cast<v4i*>(&xs[wave][m * XROW + 16 * j]) = x8_to_f16(v, pow2f(sx));
+        const int sx = chunk_prescale(row16_max_u32(bf16x8_absmax_bits(xv[i][t])));
+        if (m < M) {  // the same for all 16 lanes of a DPP row
+          *reinterpret_cast<v4i*>(&xs[wave][m * XROW + 16 * j]) = x8_to_f16(xv[i][t], pow2f(sx));
           if (j == 0) invs[wave][m] = pow2f(-sx);
         }
       }
@@ -475,7 +490,13 @@ extern "C" int lut_gemm(int64_t M, int64_t N, int64_t K, int32_t group, const ui
   p.y = y;
   hipStream_t s = as_stream(stream);
   if (M <= 16) {
-    hipLaunchKernelGGL((k_lut_gemv<kGemvNW>), dim3((unsigned)cdiv(N, 16)), dim3(64 * kGemvNW), 0, s, p);
+    const dim3 grid((unsigned)cdiv(N, 16)), block(64 * kGemvNW);
+    switch ((M + 3) / 4) {
+      case 1: hipLaunchKernelGGL((k_lut_gemv<kGemvNW, 1>), grid, block, 0, s, p); break;
+      case 2: hipLaunchKernelGGL((k_lut_gemv<kGemvNW, 2>), grid, block, 0, s, p); break;
+      case 3: hipLaunchKernelGGL((k_lut_gemv<kGemvNW, 3>), grid, block, 0, s, p); break;
+      default: hipLaunchKernelGGL((k_lut_gemv<kGemvNW, 4>), grid, block, 0, s, p); break;
+    }
     return check_launch("lut_gemm");
   }
   const int chunks = (int)(K / 128);
