@@ -235,6 +235,57 @@ def _graph_time(torch, fn, calls, reps=10):
     return e0.elapsed_time(e1) * 1e3 / (reps * calls)  # us per call
 
 
+_FLOOR = None
+
+
+def _floor_lib():
+    """The streaming-read measurement aid built beside the library (a plain
+    read of a buffer, and an empty kernel); None if it was not built."""
+    global _FLOOR
+    if _FLOOR is None:
+        import ctypes
+        path = os.path.join(ROOT, "gemm_bit_weight_amd", "libgbw_floor.so")
+        if not os.path.exists(path):
+            return None
+        lib = ctypes.CDLL(path)
+        lib.gbw_floor_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        lib.gbw_floor_empty.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        _FLOOR = lib
+    return _FLOOR
+
+
+def read_floor(torch, regions):
+    """Microseconds per call of a plain streaming read of each (address,
+    bytes) region in turn, one kernel per region, timed like the kernels
+    (one graph, cold caches): what merely reading the same bytes costs."""
+    lib = _floor_lib()
+    if lib is None:
+        return None
+    import ctypes
+    out = torch.zeros(1024, dtype=torch.int32, device="cuda")
+
+    def fn():
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for addr, nbytes in regions:
+            assert lib.gbw_floor_stream_read(ctypes.c_void_p(addr), nbytes, ctypes.c_void_p(out.data_ptr()), st) == 0
+    return _graph_time(torch, fn, len(regions))
+
+
+def empty_kernel_floor(torch, calls=64):
+    """Microseconds per launch of an empty one-wave kernel in a graph."""
+    lib = _floor_lib()
+    if lib is None:
+        return None
+    import ctypes
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def fn():
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for _ in range(calls):
+            assert lib.gbw_floor_empty(ctypes.c_void_p(out.data_ptr()), st) == 0
+    return _graph_time(torch, fn, calls)
+
+
 def lut_decode(gbw, synth, torch, M):
     N = K = 4096
     w_bytes = N * K // 2 + N * (K // 128) * 16 * 2
@@ -262,22 +313,37 @@ def lut_decode(gbw, synth, torch, M):
         for idx, cent in reps:
             gbw.lut_gemm(base["x"], idx, cent, 128, out=y, ws=ws)
     us = _graph_time(torch, fn, len(reps))
+    floor = read_floor(torch, [(pool.data_ptr() + r * (ib + cb), ib + cb) for r in range(R)])
     return {"M": M, "us_per_call": us, "weight_bytes": w_bytes, "GB_s": w_bytes / us / 1e3,
-            "frac_hbm": w_bytes / us / 1e3 / HBM_PEAK_GBS, "replicas": len(reps)}
+            "frac_hbm": w_bytes / us / 1e3 / HBM_PEAK_GBS, "replicas": len(reps),
+            "read_floor_us": floor, "frac_of_read_floor": floor / us if floor else None}
 
 
 def tail_decode(gbw, synth, torch):
     M, N, K, tail = 128, 2560, 9728, 256
     p = synth.tail_residual_problem(M, N, K, tail=tail, seed=0, device="cuda")
     a = gbw.mx_quantize(p["x"], gbw.FMT_E8M0_B32)
-    w_bytes = N * K // 2 + N * K // 32 + N * tail // 2 + N * tail // 32
+    parts = (N * K // 2, N * K // 32, N * tail // 2, N * tail // 32)  # W codes, scales; R codes, scales
+    w_bytes = sum(parts)
     R = int(2 * 256e6 // w_bytes) + 1
+    # replicas carved from one allocation (placement independent of the
+    # caching allocator's history), each one contiguous region
+    stride = (w_bytes + 4095) // 4096 * 4096
+    pool = torch.empty(R * stride, dtype=torch.uint8, device="cuda")
     reps = []
     for r in range(R):
         w = p["w"] if r == 0 else synth.normal((N, K), 0.02, r, "bench.tail.w", "cuda")
         wq = gbw.mx_quantize(w, gbw.FMT_E8M0_B32)
         rq = gbw.mx_quantize(gbw.mx_residual(w, wq.codes, wq.scales, tail), gbw.FMT_E8M0_B32)
-        reps.append((gbw.weight_from_act(wq), gbw.weight_from_act(rq)))
+        views, o = [], r * stride
+        for t, nb in zip((wq.codes, wq.scales, rq.codes, rq.scales), parts):
+            v = pool[o:o + nb].view(t.shape)
+            v.copy_(t)
+            views.append(v)
+            o += nb
+        reps.append((gbw.weight_from_act(gbw.Act(gbw.FMT_E8M0_B32, views[0], views[1])),
+                     gbw.weight_from_act(gbw.Act(gbw.FMT_E8M0_B32, views[2], views[3]))))
+        del w, wq, rq
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
     ws = torch.zeros(max(1, gbw.workspace_size(gbw.OP_MX_GEMM, M, N, K + tail)), dtype=torch.uint8, device="cuda")
 
@@ -285,10 +351,12 @@ def tail_decode(gbw, synth, torch):
         for w, r in reps:
             gbw.residual_tail_gemm(a, w, r, tail, out=y, ws=ws)
     us = _graph_time(torch, fn, len(reps))
+    floor = read_floor(torch, [(pool.data_ptr() + r * stride, w_bytes) for r in range(R)])
     flops = 2.0 * M * N * (K + tail)
     return {"M": M, "N": N, "K": K, "tail": tail, "us_per_call": us, "weight_bytes": w_bytes,
             "GB_s": w_bytes / us / 1e3, "frac_hbm": w_bytes / us / 1e3 / HBM_PEAK_GBS,
-            "TFLOP_s": flops / us / 1e6, "replicas": R}
+            "TFLOP_s": flops / us / 1e6, "replicas": R,
+            "read_floor_us": floor, "frac_of_read_floor": floor / us if floor else None}
 
 
 def moe_mxfp4_prquant(gbw, synth, torch, steps=5, tail=128):
@@ -534,7 +602,10 @@ def main():
     if not args.headline_only:
         log("decode: LUT GEMM M=1/8/64, tail-residual MXFP4 GEMM")
         out["decode"] = {"lut_gemm": [lut_decode(gbw, synth, torch, M) for M in (1, 8, 64)],
-                         "residual_tail_gemm": tail_decode(gbw, synth, torch)}
+                         "residual_tail_gemm": tail_decode(gbw, synth, torch),
+                         "empty_kernel_us": empty_kernel_floor(torch),
+                         "read_floor_note": "read_floor_us: a plain streaming read of the same weight bytes, "
+                                            "one kernel per call, timed the same way"}
         torch.cuda.empty_cache()
         log("extra: E4M3-B16 MoE, 16x512x512 linear")
         out["extra"] = {"moe_e4m3_b16": moe_e4m3(gbw, synth, torch),

@@ -321,7 +321,8 @@ def test_mx_gemm_single_linear_16x512x512():
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (5, 20, 96), (17, 300, 160), (33, 64, 544), (100, 129, 1056),
                                    (128, 2560, 9728), (200, 70, 256), (17, 64, 128), (40, 130, 640),
-                                   (96, 64, 4096), (129, 100, 1280)])
+                                   (96, 64, 4096), (129, 100, 1280), (70, 4100, 1024), (65, 4098, 256),
+                                   (17, 8192, 384)])
 def test_mx_gemm_ragged(M, N, K):
     banner(f"mx_gemm {M}x{N}x{K}")
     a, w, ref = _dense_case(M, N, K, 7)
@@ -332,7 +333,7 @@ def test_mx_gemm_ragged(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 256, 1024), (9, 70, 96), (64, 512, 2048), (128, 2560, 9728),
-                                   (40, 100, 640)])
+                                   (40, 100, 640), (70, 4100, 1024)])
 def test_mx_gemm_wide_scale_codes(M, N, K):
     """Random E2M1 codes with E8M0 scale codes over 1 .. 253: a low
     activation scale against a high weight scale in every block (each product
@@ -412,7 +413,8 @@ def test_residual_tail_gemm_wide_scale_codes():
 
 
 @pytest.mark.parametrize("M,N,K,tail", [(8, 256, 2048, 256), (13, 100, 1024, 96), (128, 2560, 9728, 256),
-                                        (64, 64, 512, 0), (33, 200, 1024, 128), (70, 96, 2048, 256)])
+                                        (64, 64, 512, 0), (33, 200, 1024, 128), (70, 96, 2048, 256),
+                                        (100, 2600, 2048, 256)])
 def test_residual_tail_gemm(M, N, K, tail):
     banner(f"residual_tail_gemm {M}x{N}x{K} tail {tail}")
     p, a, wq, r, rq = _tail_case(M, N, K, max(tail, 96))
