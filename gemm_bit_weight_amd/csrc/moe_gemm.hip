@@ -620,10 +620,6 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
       lstore(s + 1);
       if (VQ) vq_expand(s + 1);
       gload(s + 2);
-      // keep the loads of stage s+2 ahead of the MFMAs: left to itself the
-      // scheduler sinks the index and table loads below them, leaving only
-      // half an iteration to cover their latency (down: 4 % faster)
-      __builtin_amdgcn_sched_barrier(0);
       mma(s & 1, nb);
       __syncthreads();
     }
