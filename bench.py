@@ -41,7 +41,7 @@ F16_PEAK_TFLOPS = 2500.0       # dense MFMA, fp16 / bf16
 # WRITE_SIZE of k_moe_fp4<VQ,256>, scaled by a 1 GiB copy (factors 2.0 and 1.0);
 # profiles/k_moe_fp4_vq_prefill_T8192_H4096_I1536_E128_top8.md.  Must be
 # measured again (or set to None) whenever that kernel changes.
-GATEUP_HBM_BYTES = 431005.2 * 2 * 1024 + 62916.5 * 1024   # FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (calibrated KiB per launch)
+GATEUP_HBM_BYTES = 435966.9 * 2 * 1024 + 61115.0 * 1024   # FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (calibrated KiB per launch)
 
 
 def log(msg):
@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true")
+    ap.add_argument("--part", choices=("decode", "e4m3"), default=None,
+                    help="profiling aid: run only the decode GEMMs or only the E4M3-B16 MoE and print their "
+                         "measurements (not the benchmark line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES between two device buffers 3 times (scale for the HBM byte counters)")
     return ap.parse_args()
@@ -559,6 +562,13 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_calibration:
         copy_calibration(torch, args.copy_calibration)
+        return
+    if args.part == "decode":
+        print(json.dumps({"lut_gemm": [lut_decode(gbw, synth, torch, M) for M in (1, 8, 64)],
+                          "residual_tail_gemm": tail_decode(gbw, synth, torch)}), flush=True)
+        return
+    if args.part == "e4m3":
+        print(json.dumps({"moe_e4m3_b16": moe_e4m3(gbw, synth, torch, steps=args.steps)}), flush=True)
         return
 
     log("headline: VQ->MX MoE prefill T=8192 H=4096 I=1536 E=128 top-8")
