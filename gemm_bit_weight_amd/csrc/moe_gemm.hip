@@ -941,11 +941,26 @@ __global__ __launch_bounds__(kE4Threads) void k_moe_e4m3(const MoeArgs p) {
         }
     }
   };
+  // Waves 0-3 decode and store stage s+1 before the MFMAs of stage s, waves
+  // 4-7 after them.  Wave w runs on SIMD w % 4, so each SIMD holds one wave
+  // of each order, and one's decode overlaps the other's MFMAs instead of the
+  // two decoding together between barriers (3 % faster; the FP4 kernel has
+  // no registers to spare for the two orders).  The order inside a wave is
+  // free: the MFMAs read buffer s & 1, the stores write buffer (s+1) & 1.
+  // (The condition is left a vector compare: made scalar, it changes the
+  // register allocation of the two orders and the kernel spills.)
+  const bool mfma_first = wave >= 4;
   auto kloop = [&](auto nb) __attribute__((always_inline)) {
     for (int s = 0; s < steps; ++s) {
-      lstore(s + 1);
-      gload(s + 2);
-      mma(s & 1, nb);
+      if (mfma_first) {
+        mma(s & 1, nb);
+        lstore(s + 1);
+        gload(s + 2);
+      } else {
+        lstore(s + 1);
+        gload(s + 2);
+        mma(s & 1, nb);
+      }
       __syncthreads();
     }
   };
