@@ -216,7 +216,11 @@ def cpu_baseline(synth, torch, np, res):
 # decode-shaped GEMMs (weights streamed from HBM)
 # ---------------------------------------------------------------------------
 
-def _graph_time(torch, fn, calls, reps=10):
+def _graph_time(torch, fn, calls, reps=5, min_calls=200):
+    """Microseconds per call of ``fn`` (``calls`` launches) captured in one
+    HIP graph: two warm-up replays, then ``reps`` repetitions of enough
+    back-to-back replays for at least ``min_calls`` calls, each timed with
+    events; the median repetition."""
     fn()
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
@@ -229,13 +233,17 @@ def _graph_time(torch, fn, calls, reps=10):
     for _ in range(2):
         g.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
+    per = -(-min_calls // calls)  # replays per repetition
+    times = []
     for _ in range(reps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / (reps * calls)  # us per call
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(per):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / (per * calls))
+    return sorted(times)[reps // 2]
 
 
 _FLOOR = None
@@ -317,9 +325,10 @@ def lut_decode(gbw, synth, torch, M):
             gbw.lut_gemm(base["x"], idx, cent, 128, out=y, ws=ws)
     us = _graph_time(torch, fn, len(reps))
     floor = read_floor(torch, [(pool.data_ptr() + r * (ib + cb), ib + cb) for r in range(R)])
+    all_bytes = w_bytes + M * K * 2 + M * N * 4  # weights + bf16 x + fp32 y
     return {"M": M, "us_per_call": us, "weight_bytes": w_bytes, "GB_s": w_bytes / us / 1e3,
-            "frac_hbm": w_bytes / us / 1e3 / HBM_PEAK_GBS, "replicas": len(reps),
-            "read_floor_us": floor, "frac_of_read_floor": floor / us if floor else None}
+            "frac_hbm": w_bytes / us / 1e3 / HBM_PEAK_GBS, "frac_hbm_all_bytes": all_bytes / us / 1e3 / HBM_PEAK_GBS,
+            "replicas": len(reps), "read_floor_us": floor, "frac_of_read_floor": floor / us if floor else None}
 
 
 def tail_decode(gbw, synth, torch):
@@ -356,9 +365,11 @@ def tail_decode(gbw, synth, torch):
     us = _graph_time(torch, fn, len(reps))
     floor = read_floor(torch, [(pool.data_ptr() + r * stride, w_bytes) for r in range(R)])
     flops = 2.0 * M * N * (K + tail)
+    all_bytes = w_bytes + M * (K + tail) // 2 + M * (K + tail) // 32 + M * N * 4  # weights + codes/scales + y
     return {"M": M, "N": N, "K": K, "tail": tail, "us_per_call": us, "weight_bytes": w_bytes,
             "GB_s": w_bytes / us / 1e3, "frac_hbm": w_bytes / us / 1e3 / HBM_PEAK_GBS,
-            "TFLOP_s": flops / us / 1e6, "replicas": R,
+            "frac_hbm_all_bytes": all_bytes / us / 1e3 / HBM_PEAK_GBS,
+            "TFLOP_s": flops / us / 1e6, "frac_mxfp4_mfma": flops / us / 1e6 / MXFP4_PEAK_TFLOPS, "replicas": R,
             "read_floor_us": floor, "frac_of_read_floor": floor / us if floor else None}
 
 

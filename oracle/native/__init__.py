@@ -40,6 +40,7 @@ _lib.gbwo_quantize_b16.argtypes = [_int, _i64, _i64, _vp, _dbl, _vp, _vp]
 _lib.gbwo_swiglu_bf16.argtypes = [_i64, _vp, _vp, _vp]
 _lib.gbwo_combine.argtypes = [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.gbwo_route.argtypes = [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.gbwo_e2m1_rne.argtypes = [_i64, _vp, _vp]
 
 _FMT = {"e8m0_b32": 0, "e4m3_b16": 1, "e5m3_b16": 2}
 TENSOR_SCALED = ("e4m3_b16", "e5m3_b16")

@@ -221,6 +221,13 @@ extern "C" {
 
 int gbwo_threads(void) { return n_threads(); }
 
+// The E2M1 magnitude code (0..7) of each |v[i]|: round to the nearest of
+// {0, 0.5, 1, 1.5, 2, 3, 4, 6}, ties to the even code, saturating at 6 -- the
+// rounding step every quantizer above applies to a scaled value.
+void gbwo_e2m1_rne(int64_t n, const double* v, uint8_t* codes) {
+  for (int64_t i = 0; i < n; ++i) codes[i] = (uint8_t)e2m1_rne(std::fabs(v[i]));
+}
+
 // Decode [rows][K] packed codes + block scales (fmt 0 E8M0-B32, 1 E4M3-B16,
 // 2 E5M3-B16) to doubles, times `tensor_scale` (1 for E8M0-B32).
 void gbwo_dequantize(int64_t rows, int64_t K, int fmt, const uint8_t* codes, const uint8_t* scales,

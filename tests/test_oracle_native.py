@@ -6,8 +6,10 @@ The C++ side is the reference the GPU parity tests and the CPU baseline use
 for the contractions; numpy stays as the cross-check.
 """
 
+import ctypes
 import json
 import os
+import subprocess
 from fractions import Fraction
 
 import numpy as np
@@ -268,3 +270,17 @@ def test_route_special_values():
     with np.errstate(invalid="ignore"):
         r = on.moe_route(row, 8)
     assert r["topk_ids"][0].tolist() == [5, 3, 6, 1, 2, 4, 0, 7]
+
+
+def test_e2m1_rounding_exhaustive_over_fp32(tmp_path):
+    """Every non-negative finite fp32 value: the oracle's E2M1 rounding
+    against an interval statement of round-to-nearest-even with saturation,
+    written independently in C (tests/pins/e2m1_all.c)."""
+    src = os.path.join(os.path.dirname(__file__), "pins", "e2m1_all.c")
+    so = str(tmp_path / "e2m1_all.so")
+    subprocess.run(["gcc", "-O2", "-fPIC", "-shared", "-ffp-contract=off", src, "-o", so], check=True)
+    lib = ctypes.CDLL(so)
+    lib.check_all.restype = ctypes.c_int64
+    lib.check_all.argtypes = [ctypes.c_void_p]
+    fn = ctypes.cast(on._lib.gbwo_e2m1_rne, ctypes.c_void_p)
+    assert lib.check_all(fn) == 0
