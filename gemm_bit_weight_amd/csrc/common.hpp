@@ -175,11 +175,9 @@ __device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
 __device__ __forceinline__ v4i load16(const void* p) { return *reinterpret_cast<const v4i*>(p); }
 
 // Direct global -> LDS load of 16 bytes per lane (lane l's bytes land at
-// lds + 16 l; `lds` must be the same in every lane of the wave).  Measured on
-// this chip: a load instruction whose 64 lanes read one contiguous 1 KiB
-// streams far faster than one whose lanes spread over many rows (every
-// distinct row costs its own address translation in flight), so weight tiles
-// are copied into LDS this way, a kilobyte of one row at a time.
+// lds + 16 l; `lds` must be the same in every lane of the wave): a weight
+// segment is copied into LDS one contiguous kilobyte of a row per
+// instruction, with no registers in between.
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 __device__ __forceinline__ void load_lds16(const void* g, void* lds) {
