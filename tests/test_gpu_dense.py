@@ -353,6 +353,39 @@ def test_mx_gemm_wide_scale_codes(M, N, K):
           flush=True)
 
 
+def test_dense_empty_extents():
+    """M = 0 or N = 0: every GEMM entry point returns without touching its
+    output; a zero-row quantization returns an empty result."""
+    banner("dense empty extents")
+    K = 256
+    codes = np.zeros((4, K // 2), np.uint8)
+    scales = np.full((4, K // 32), 127, np.uint8)
+    A0 = gbw.Act(gbw.FMT_E8M0_B32, torch.empty((0, K // 2), dtype=torch.uint8, device=DEV),
+                 torch.empty((0, K // 32), dtype=torch.uint8, device=DEV))
+    W = _gpu_w(codes, scales)
+    y = torch.full((0, 4), 7.0, device=DEV)
+    assert gbw.mx_gemm(A0, W, out=y).shape == (0, 4)
+    R = _gpu_w(np.ascontiguousarray(codes[:, :64]), np.ascontiguousarray(scales[:, :4]))
+    assert gbw.residual_tail_gemm(A0, W, R, 128, out=y).shape == (0, 4)
+    A = _gpu_act(codes, scales)
+    W0 = gbw.Weight(gbw.FMT_E8M0_B32, 0, K, torch.empty((0, K // 2), dtype=torch.uint8, device=DEV),
+                    torch.empty((0, K // 32), dtype=torch.uint8, device=DEV))
+    y4 = torch.full((4, 0), 7.0, device=DEV)
+    assert gbw.mx_gemm(A, W0, out=y4).shape == (4, 0)
+    q = gbw.mx_quantize(torch.empty((0, K), dtype=torch.bfloat16, device=DEV), gbw.FMT_E8M0_B32)
+    assert q.codes.shape == (0, K // 2) and q.scales.shape == (0, K // 32)
+    torch.cuda.synchronize()
+
+
+def test_mx_gemm_long_k():
+    """K = 32768 (256 steps of 128; the 16-row kernel's longest K ranges) at
+    M = 16, N = 1024."""
+    banner("mx_gemm 16x1024x32768")
+    a, w, ref = _dense_case(16, 1024, 32768, 11)
+    assert_rows_close(to_np(gbw.mx_gemm(a, w)), ref, what="mx_gemm long K")
+    assert_rows_close(to_np(gbw.mx_gemm(a, w, ws=False)), ref, what="mx_gemm long K serial")
+
+
 def test_mx_gemm_integer_special_case_bitexact():
     """All scales 127: Y = int64 GEMM / 4 exactly (|Y| < 2^22)."""
     banner("mx_gemm integer case")

@@ -126,6 +126,20 @@ def test_lut_gemm_workspace_paths(M):
     assert torch.equal(y_short, y_none)
 
 
+def test_lut_gemm_empty_extents():
+    """M = 0 or N = 0 returns without touching the output."""
+    banner("lut_gemm empty extents")
+    K, group = 256, 128
+    x0 = torch.empty((0, K), dtype=torch.bfloat16, device=DEV)
+    idx = torch.zeros((8, K // 2), dtype=torch.uint8, device=DEV)
+    cent = torch.zeros((8, K // group, 16), dtype=torch.float16, device=DEV)
+    assert gbw.lut_gemm(x0, idx, cent, group).shape == (0, 8)
+    x = torch.ones((3, K), dtype=torch.bfloat16, device=DEV)
+    y = gbw.lut_gemm(x, idx[:0], cent[:0], group)
+    assert y.shape == (3, 0)
+    torch.cuda.synchronize()
+
+
 def test_lut_gemm_rejects_bad_shapes():
     x = torch.zeros((4, 200), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(gbw.GbwError):
