@@ -196,11 +196,17 @@ int mx_residual(const float* w, int64_t N, int64_t K, int64_t tail, const uint8_
  * §4 Eq. (1) (with the permutation and scaling already folded into the
  * operands), on the E8M0-B32-FP4 format of MXCode: MX-Native Codebook
  * Quantization, Table 1; deq() decodes each element as e2m1 * 2^(scale-127).
- * K must be a multiple of 32.  y is overwritten.  When the grid needs the reduction over K split across
- * workgroups, the split partials go to the workspace
- * (gbw_workspace_size(GBW_OP_MX_GEMM, M, N, K [+ tail], 0) bytes) and are
- * summed in split order by a second kernel; with a smaller or NULL workspace
- * a slower serial-K kernel is used.  Results are bitwise repeatable.
+ * K must be a multiple of 32.  y is overwritten.  When the grid needs the
+ * reduction over K split across workgroups, the split partials go to the
+ * workspace (gbw_workspace_size(GBW_OP_MX_GEMM, M, N, K [+ tail], 0) bytes)
+ * and are summed in split order: with 17 or more rows and K segments that
+ * are multiples of 128, inside the same kernel (the last workgroup of an
+ * output tile to arrive adds the tile's partials; the arrival counters are
+ * the workspace's first 64 KiB, which must be zero before the first call and
+ * are left zero by every call, so calls that share a workspace must not
+ * overlap in time), otherwise by a second kernel.  With a smaller or NULL
+ * workspace a slower serial-K kernel is used.  Results are bitwise
+ * repeatable.
  */
 int mx_gemm(int64_t M, const gbw_act* a, const gbw_weight* w, float* y, int32_t flags,
             void* ws, size_t ws_bytes, void* stream);
