@@ -144,7 +144,7 @@ def moe_vq_prefill(gbw, synth, torch, steps, warmup, scales="prescale"):
                 flops_dn=flops_dn, weight_bytes=weight_bytes, data=d, route=route, T=T, H=H, I=I, E=E, K=K)
 
 
-CPU_SAMPLE_EXPERTS = 8    # about 10-30 s of oracle work on the host cores
+CPU_SAMPLE_EXPERTS = 24   # about 10-30 s of oracle work on 16 host threads (5 s per 8 experts)
 
 
 def moe_vq_scale_layouts(gbw, synth, torch, steps=5, warmup=2):
