@@ -386,6 +386,28 @@ def test_mx_gemm_long_k():
     assert_rows_close(to_np(gbw.mx_gemm(a, w, ws=False)), ref, what="mx_gemm long K serial")
 
 
+def test_split_k_workspace_shared_across_shapes():
+    """One zeroed workspace, sized for the largest call, serves a sequence of
+    split-K GEMMs of different shapes (both split-K kernels, with and without
+    the tail segment): every call leaves the arrival counters at zero, so each
+    result is bitwise the one a fresh workspace gives."""
+    banner("split-K workspace shared across shapes")
+    shapes = [(128, 2560, 2048, 256), (40, 1024, 4096, 0), (16, 512, 4096, 0), (70, 640, 1024, 128),
+              (128, 2560, 2048, 256)]
+    cases = []
+    for i, (M, N, K, tail) in enumerate(shapes):
+        p, a, wq, r, rq = _tail_case(M, N, K, max(tail, 96), seed=20 + i)
+        cases.append((a, gbw.weight_from_act(wq), gbw.weight_from_act(rq) if tail else None, tail, K))
+    need = max(gbw.workspace_size(gbw.OP_MX_GEMM, a.rows, w.N, K + t) for a, w, rw, t, K in cases)
+    shared = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for a, w, rw, t, K in cases:
+        y_shared = gbw.residual_tail_gemm(a, w, rw, t, ws=shared)
+        y_fresh = gbw.residual_tail_gemm(a, w, rw, t)
+        assert torch.equal(y_shared, y_fresh)
+    torch.cuda.synchronize()
+    assert int(shared[:65536].count_nonzero()) == 0  # the counters are back at zero
+
+
 def test_mx_gemm_integer_special_case_bitexact():
     """All scales 127: Y = int64 GEMM / 4 exactly (|Y| < 2^22)."""
     banner("mx_gemm integer case")
