@@ -562,7 +562,7 @@ def moe_vq_b16(gbw, synth, torch, steps=5):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import numpy as np
