@@ -496,3 +496,44 @@ def test_residual_tail_gemm(M, N, K, tail):
         waug = gbw.weight_from_act(gbw.mx_quantize(wcat, gbw.FMT_E8M0_B32))
         yaug = to_np(gbw.mx_gemm(at, waug))
         assert_rows_close(yaug, ref, what="augmented")
+
+
+def test_split_k_gemms_in_a_replayed_graph():
+    """The split-K GEMMs captured in one HIP graph (their arrival counters are
+    never cleared by a memset node: every call leaves them zero) and
+    replayed several times, with eager work and synchronizations between the
+    replays: every replay gives the eager result bit for bit."""
+    banner("split-K GEMMs in a replayed graph")
+    p, a, wq, r, rq = _tail_case(128, 2560, 2048, 256, seed=31)
+    w, rw = gbw.weight_from_act(wq), gbw.weight_from_act(rq)
+    lut = synth.lut_problem(64, N=1024, K=4096, group=128, seed=32, device=DEV, iters=4)
+    ws_mx = torch.zeros(gbw.workspace_size(gbw.OP_MX_GEMM, 128, 2560, 2048 + 256), dtype=torch.uint8, device=DEV)
+    ws_lut = torch.zeros(gbw.workspace_size(gbw.OP_LUT_GEMM, 64, 1024, 4096), dtype=torch.uint8, device=DEV)
+    y_mx = torch.empty((128, 2560), dtype=torch.float32, device=DEV)
+    y_lut = torch.empty((64, 1024), dtype=torch.float32, device=DEV)
+
+    def calls():
+        gbw.residual_tail_gemm(a, w, rw, 256, out=y_mx, ws=ws_mx)
+        gbw.lut_gemm(lut["x"], lut["idx"], lut["centroids"], 128, out=y_lut, ws=ws_lut)
+
+    calls()
+    torch.cuda.synchronize()
+    eager_mx, eager_lut = y_mx.clone(), y_lut.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            calls()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        y_mx.fill_(float("nan"))
+        y_lut.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_mx, eager_mx), f"replay {rep}: residual_tail_gemm"
+        assert torch.equal(y_lut, eager_lut), f"replay {rep}: lut_gemm"
+        calls()  # eager work between replays, on the same workspaces
+        torch.cuda.synchronize()
+        assert torch.equal(y_mx, eager_mx) and torch.equal(y_lut, eager_lut)
+    assert int(ws_mx[:65536].count_nonzero()) == 0 and int(ws_lut[:65536].count_nonzero()) == 0
