@@ -941,15 +941,17 @@ __global__ __launch_bounds__(kE4Threads) void k_moe_e4m3(const MoeArgs p) {
         }
     }
   };
-  // Waves 0-3 decode and store stage s+1 before the MFMAs of stage s, waves
-  // 4-7 after them.  Wave w runs on SIMD w % 4, so each SIMD holds one wave
-  // of each order, and one's decode overlaps the other's MFMAs instead of the
-  // two decoding together between barriers (3 % faster; the FP4 kernel has
-  // no registers to spare for the two orders).  The order inside a wave is
-  // free: the MFMAs read buffer s & 1, the stores write buffer (s+1) & 1.
-  // (The condition is left a vector compare: made scalar, it changes the
-  // register allocation of the two orders and the kernel spills.)
-  const bool mfma_first = wave >= 4;
+  // Packed codes: waves 0-3 decode and store stage s+1 before the MFMAs of
+  // stage s, waves 4-7 after them.  Wave w runs on SIMD w % 4, so each SIMD
+  // holds one wave of each order, and one's decode overlaps the other's MFMAs
+  // instead of the two decoding together between barriers (3 % faster; with
+  // VQ weights, whose B rows also expand indices, 6-9 % slower, so those
+  // keep one order; the FP4 kernel has no registers to spare for the two
+  // orders).  The order inside a wave is free: the MFMAs read buffer s & 1,
+  // the stores write buffer (s+1) & 1.  (The condition is left a vector
+  // compare: made scalar, it changes the register allocation of the two
+  // orders and the kernel spills.)
+  const bool mfma_first = !VQ && wave >= 4;
   auto kloop = [&](auto nb) __attribute__((always_inline)) {
     for (int s = 0; s < steps; ++s) {
       if (mfma_first) {
