@@ -423,10 +423,11 @@ __global__ __launch_bounds__(256) void k_mx_gemm32(const MxGemmArgs p) {
     store_shared_v4(rs, SLOT * blockIdx.y + 16 * pc, *reinterpret_cast<const v4f*>(tile + 4 * pc));
   }
   if (!arrive_last(p.counters + tile_id, p.splits, &s_last)) return;
-  // the last arrival: every other split's slot, all loads in flight per
-  // batch of PB pieces, then the sums in split order
-  constexpr int PB = PIECES < 4 ? PIECES : 4;
-  constexpr int SMX = 8;  // splits per pass of the load batch (more passes beyond)
+  // the last arrival: every piece of up to SMX other splits' slots in flight
+  // at once (one memory round trip; 48 registers of 16 bytes), then the sums
+  // in split order
+  constexpr int PB = PIECES;
+  constexpr int SMX = 48 / PB;  // splits per pass of the load batch (more passes beyond)
 #pragma unroll
   for (int u0 = 0; u0 < PIECES; u0 += PB) {
     v4f sum[PB];
