@@ -55,9 +55,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true")
-    ap.add_argument("--part", choices=("decode", "e4m3"), default=None,
-                    help="profiling aid: run only the decode GEMMs or only the E4M3-B16 MoE and print their "
-                         "measurements (not the benchmark line)")
+    ap.add_argument("--part", choices=("decode", "e4m3", "mfma"), default=None,
+                    help="profiling aid: run only the decode GEMMs, only the E4M3-B16 MoE or only the MFMA rate "
+                         "probe and print their measurements (not the benchmark line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES between two device buffers 3 times (scale for the HBM byte counters)")
     return ap.parse_args()
@@ -295,6 +295,41 @@ def empty_kernel_floor(torch, calls=64):
         for _ in range(calls):
             assert lib.gbw_floor_empty(ctypes.c_void_p(out.data_ptr()), st) == 0
     return _graph_time(torch, fn, calls)
+
+
+def mfma_rate_probe(torch, iters=4096):
+    """TFLOP/s that each MFMA shape sustains with nothing else running (the
+    measurement aid's register-only MFMA loop, two waves per SIMD), next to
+    the published dense peak of its type: the matrix cores' rate under load,
+    clock behaviour included."""
+    lib = _floor_lib()
+    if lib is None:
+        return None
+    import ctypes
+    lib.gbw_floor_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    blocks = 2 * torch.cuda.get_device_properties(0).multi_processor_count  # 4-wave workgroups
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    shapes = (("fp4_32x32x64", 0, 32 * 32 * 64, MXFP4_PEAK_TFLOPS), ("fp4_16x16x128", 1, 16 * 16 * 128, MXFP4_PEAK_TFLOPS),
+              ("fp16_32x32x16", 2, 32 * 32 * 16, F16_PEAK_TFLOPS), ("fp16_16x16x32", 3, 16 * 16 * 32, F16_PEAK_TFLOPS))
+    res = {}
+    for name, kind, mnk, peak in shapes:
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+        def launch():
+            assert lib.gbw_floor_mfma_rate(kind, blocks, iters, ctypes.c_void_p(out.data_ptr()), st) == 0
+        launch()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            launch()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 3
+        flops = blocks * 4 * iters * 8 * 2 * mnk
+        tf = flops / ms / 1e9
+        res[name] = {"TFLOP_s": tf, "frac_of_peak": tf / peak, "peak_TFLOP_s": peak, "ms_per_launch": ms}
+    return res
 
 
 def lut_decode(gbw, synth, torch, M):
@@ -581,6 +616,9 @@ def main():
     if args.part == "e4m3":
         print(json.dumps({"moe_e4m3_b16": moe_e4m3(gbw, synth, torch, steps=args.steps)}), flush=True)
         return
+    if args.part == "mfma":
+        print(json.dumps({"mfma_rate_probe": mfma_rate_probe(torch)}), flush=True)
+        return
 
     log("headline: VQ->MX MoE prefill T=8192 H=4096 I=1536 E=128 top-8")
     res = moe_vq_prefill(gbw, synth, torch, args.steps, args.warmup)
@@ -613,6 +651,15 @@ def main():
         "stages_ms": {"gate_up": res["gu_ms"], "down_combine": res["dn_ms"],
                       "route_quant_other": res["ms_step"] - res["gu_ms"] - res["dn_ms"]},
     }
+    # what the FP4 matrix cores sustain on this device with nothing else
+    # running (clock under load included), beside the published peak
+    probe = mfma_rate_probe(torch)
+    if probe:
+        ceil = probe["fp4_32x32x64"]["TFLOP_s"]
+        out["roofline"]["mfma_only_ceiling"] = ceil
+        out["roofline"]["frac_of_mfma_only_ceiling"] = gu_tflops / ceil
+        out["roofline"]["mfma_only_ceiling_note"] = ("v_mfma_scale_f32_32x32x64_f8f6f4 in a register-only loop, "
+                                                     "two waves per SIMD on every CU")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, bounded sample)")
         out["cpu_baseline"] = cpu_baseline(synth, torch, np, res)
@@ -635,7 +682,8 @@ def main():
                         "quantize_e8m0_8192x4096": quantize_rate(gbw, synth, torch),
                         "moe_mxfp4_prquant_down": moe_mxfp4_prquant(gbw, synth, torch),
                         "moe_vq_scale_layouts": moe_vq_scale_layouts(gbw, synth, torch),
-                        "moe_vq_e4m3_b16": moe_vq_b16(gbw, synth, torch)}
+                        "moe_vq_e4m3_b16": moe_vq_b16(gbw, synth, torch),
+                        "mfma_rate_probe": probe}
     print(json.dumps(out), flush=True)
 
 

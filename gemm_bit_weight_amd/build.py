@@ -24,7 +24,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgbw.so")
 # measurement aid for the benchmark (a plain streaming read), its own library
-FLOOR_SRC = os.path.join(HERE, "floor", "stream_read.hip")
+FLOOR_SRCS = [os.path.join(HERE, "floor", f) for f in ("stream_read.hip", "mfma_rate.hip")]
 FLOOR_LIB = os.path.join(HERE, "libgbw_floor.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -70,9 +70,9 @@ def build(jobs=None, verbose=False):
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
     tmp = FLOOR_LIB + ".tmp"
-    r = subprocess.run([HIPCC, *FLAGS, "-shared", FLOOR_SRC, "-o", tmp], capture_output=True, text=True)
+    r = subprocess.run([HIPCC, *FLAGS, "-shared", *FLOOR_SRCS, "-o", tmp], capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {FLOOR_SRC}:\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"hipcc failed on {FLOOR_SRCS}:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, FLOOR_LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources, and {FLOOR_LIB}")
