@@ -615,14 +615,26 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
                                                                        0, asc[i], 0, bsc[j]);
     }
   };
+  // the last two stages are peeled: no loads past the last stage, no store
+  // or expansion of a stage that does not exist
   auto kloop = [&](auto nb) __attribute__((always_inline)) {
-    for (int s = 0; s < steps; ++s) {
+    int s = 0;
+    for (; s < steps - 2; ++s) {
       lstore(s + 1);
       if (VQ) vq_expand(s + 1);
       gload(s + 2);
       mma(s & 1, nb);
       __syncthreads();
     }
+    if (s == steps - 2) {
+      lstore(s + 1);
+      if (VQ) vq_expand(s + 1);
+      mma(s & 1, nb);
+      __syncthreads();
+      ++s;
+    }
+    mma(s & 1, nb);
+    __syncthreads();
   };
   if (nband == 2)
     kloop(IntC<2>{});
@@ -952,8 +964,10 @@ __global__ __launch_bounds__(kE4Threads) void k_moe_e4m3(const MoeArgs p) {
   // compare: made scalar, it changes the register allocation of the two
   // orders and the kernel spills.)
   const bool mfma_first = !VQ && wave >= 4;
+  // (the last two stages peeled, as in the FP4 kernel)
   auto kloop = [&](auto nb) __attribute__((always_inline)) {
-    for (int s = 0; s < steps; ++s) {
+    int s = 0;
+    for (; s < steps - 2; ++s) {
       if (mfma_first) {
         mma(s & 1, nb);
         lstore(s + 1);
@@ -965,6 +979,19 @@ __global__ __launch_bounds__(kE4Threads) void k_moe_e4m3(const MoeArgs p) {
       }
       __syncthreads();
     }
+    if (s == steps - 2) {
+      if (mfma_first) {
+        mma(s & 1, nb);
+        lstore(s + 1);
+      } else {
+        lstore(s + 1);
+        mma(s & 1, nb);
+      }
+      __syncthreads();
+      ++s;
+    }
+    mma(s & 1, nb);
+    __syncthreads();
   };
   if (nband == 2)
     kloop(IntC<2>{});
