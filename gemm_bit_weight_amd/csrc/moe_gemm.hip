@@ -461,8 +461,9 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
   //   2. issue the global loads of stage s+2 (and the tables of stage s+3);
   //   3. the MFMAs of stage s from buffer s&1;
   //   4. barrier.
-  // Indices past the last stage are clamped, so the loop body has no branches
-  // (the redundant work at the end hits L2 and a spare buffer).
+  // The last two iterations are peeled (no loads of stage s+2 in the second
+  // to last, only the MFMAs in the last); the tables, which run one stage
+  // further ahead, clamp their stage index to the last stage instead.
   v4i pa[NA], pb[2];
   uint32_t ps0 = 0, ps1 = 0;
   // with p.scales16 (256-wide tiles only: the 128-wide kernel has no
