@@ -107,6 +107,9 @@ def moe_vq_prefill(gbw, synth, torch, steps, warmup, scales="prescale"):
     hs = torch.empty((P, I // 32), dtype=torch.uint8, device=dev)
     hq = gbw.Act(gbw.FMT_E8M0_B32, hc, hs)
     y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    # the down stage's workspace (slot buffer), allocated and zeroed once as
+    # a caller would; every call overwrites every slot
+    wsd = torch.zeros(gbw.workspace_size(gbw.OP_MOE_GEMM, P, H, 0), dtype=torch.uint8, device=dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def step(marks=None):
@@ -117,7 +120,7 @@ def moe_vq_prefill(gbw, synth, torch, steps, warmup, scales="prescale"):
         gbw.moe_grouped_gemm(gbw.MOE_GATEUP_SWIGLU, route, xq, Wgu, h_codes=hc, h_scales=hs)
         if marks is not None:
             marks[1].record()
-        gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, Wd, y=y)
+        gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, Wd, y=y, ws=wsd)
         if marks is not None:
             marks[2].record()
 
@@ -439,6 +442,7 @@ def moe_mxfp4_prquant(gbw, synth, torch, steps=5, tail=128):
     del d["w_gate_up"], d["w_down"]
     P = T * K
     y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    wsd = torch.zeros(gbw.workspace_size(gbw.OP_MOE_GEMM, P, H, 0), dtype=torch.uint8, device="cuda")
     res = {"T": T, "hidden": H, "intermediate": I, "experts": E, "topk": K, "tail": tail}
     # (name, gate/up weight, h columns, h_tail of the gate/up call, down weight)
     variants = (("tail0", Wgu, I, 0, Wd0), ("tail%d" % tail, Wgu, I + tail, tail, Wda),
@@ -451,7 +455,7 @@ def moe_mxfp4_prquant(gbw, synth, torch, steps=5, tail=128):
             route = gbw.moe_route(d["logits"], K)
             xq = gbw.mx_quantize(d["x"], gbw.FMT_E8M0_B32)
             gbw.moe_grouped_gemm(gbw.MOE_GATEUP_SWIGLU, route, xq, wg, h_codes=hc, h_scales=hs, h_tail=ht)
-            gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, gbw.Act(gbw.FMT_E8M0_B32, hc, hs), wdn, y=y)
+            gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, gbw.Act(gbw.FMT_E8M0_B32, hc, hs), wdn, y=y, ws=wsd)
         step()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -527,13 +531,14 @@ def moe_e4m3(gbw, synth, torch, steps=5, fmt=None):
     P = T * K
     hb = torch.empty((P, I), dtype=torch.bfloat16, device=dev)
     y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    wsd = torch.zeros(gbw.workspace_size(gbw.OP_MOE_GEMM, P, H, 0), dtype=torch.uint8, device=dev)
 
     def step():
         route = gbw.moe_route(d["logits"], K)
         xq = gbw.mx_quantize(d["x"], fmt)
         gbw.moe_grouped_gemm(gbw.MOE_GATEUP_SWIGLU, route, xq, Wgu, h_bf16=hb)
         hq = gbw.mx_quantize(hb, fmt)
-        gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, Wd, y=y)
+        gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, Wd, y=y, ws=wsd)
     step()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -567,13 +572,14 @@ def moe_vq_b16(gbw, synth, torch, steps=5):
         P = T * K
         hb = torch.empty((P, I), dtype=torch.bfloat16, device="cuda")
         y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        wsd = torch.zeros(gbw.workspace_size(gbw.OP_MOE_GEMM, P, H, 0), dtype=torch.uint8, device="cuda")
 
         def step():
             route = gbw.moe_route(d["logits"], K)
             xq = gbw.mx_quantize(d["x"], gbw.FMT_E4M3_B16)
             gbw.moe_grouped_gemm(gbw.MOE_GATEUP_SWIGLU, route, xq, Wgu, h_bf16=hb)
             hq = gbw.mx_quantize(hb, gbw.FMT_E4M3_B16)
-            gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, Wd, y=y)
+            gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, Wd, y=y, ws=wsd)
         step()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
