@@ -358,7 +358,10 @@ def moe_grouped_gemm(stage, route, a: Act, w: Weight, h_bf16=None, h_codes=None,
             are appended again, PRQuant's online tail copy).
     DOWN:   overwrites y [T][H] through a bf16 (flags=FP32_COMBINE: fp32)
             slot buffer in the workspace and a fixed-order combine; ws=False
-            adds into y with fp32 atomics instead (no workspace).
+            adds into y with fp32 atomics instead (no workspace).  With
+            ws=None each call allocates and zero-fills a workspace (P x H
+            x 2 bytes); repeated calls should pass one made once with
+            torch.zeros(workspace_size(OP_MOE_GEMM, P, H, fp32_combine)).
     """
     T, topk = route["topk_ids"].shape
     P = T * topk
