@@ -331,6 +331,15 @@ def _run_and_check(pb, tokens=None, experts=None, h_amax=None, exact=True):
     gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, pb.Wd, y=y2)
     torch.cuda.synchronize()
     assert torch.equal(y, y2), "slot combine differs between runs"
+    # one workspace shared by several calls, as a serving loop passes it:
+    # the bits of a fresh workspace each time
+    wsd = torch.zeros(gbw.workspace_size(gbw.OP_MOE_GEMM, route["topk_ids"].numel(), H, 0), dtype=torch.uint8,
+                      device=DEV)
+    for _ in range(3):
+        y3 = torch.empty_like(y)
+        gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, hq, pb.Wd, y=y3, ws=wsd)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y3), "a reused workspace changes the result"
 
     # ---- oracle pipeline, from the synthetic inputs only ----
     xn = pb.x.float().cpu().numpy()
