@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "quantized GEMM TFLOP/s (prefill) + weight GB/s (decode) at 1 GPU"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MXFP4_PEAK_TFLOPS = 10100.0    # dense MFMA, fp4 / fp6
+HOT_CALLS = 16                 # calls per graph for the cache-resident decode figures
 F16_PEAK_TFLOPS = 2500.0       # dense MFMA, fp16 / bf16
 # HBM bytes per gate/up launch of the headline workload: rocprofv3 FETCH_SIZE and
 # WRITE_SIZE of k_moe_fp4<VQ,256>, scaled by a 1 GiB copy (factors 2.0 and 1.0);
@@ -215,6 +216,58 @@ def cpu_baseline(synth, torch, np, res):
                       f"with compensated double sums, {secs:.1f} s"}
 
 
+def cpu_oracle_1core(synth, torch, np):
+    """The C++ oracle on one host thread for the dense and decode-shaped
+    configurations (inputs generated first, not timed): the 16x512x512
+    MXFP4 linear, the LUT GEMM at M = 1, 8 and 64 (K = N = 4096), and the
+    tail-residual GEMM (M = 128, N = 2560, K = 9728 + 256).  The larger
+    ones run on a leading slice of their rows and are scaled to the whole
+    call; every entry states its sample.  Milliseconds per call."""
+    import oracle
+    import oracle.native as on
+    out = {}
+
+    def timed(fn):  # the timed call alone runs on one thread; the set-up uses them all
+        prev = os.environ.get("GBWO_THREADS")
+        os.environ["GBWO_THREADS"] = "1"
+        try:
+            t0 = time.perf_counter()
+            fn()
+            return (time.perf_counter() - t0) * 1e3
+        finally:
+            if prev is None:
+                os.environ.pop("GBWO_THREADS", None)
+            else:
+                os.environ["GBWO_THREADS"] = prev
+
+    if True:  # (one block, so the inputs of one configuration are freed before the next)
+        d = synth.dense_linear(16, 512, 512, seed=0, device="cpu")
+        ac, as_ = on.quantize_e8m0_b32(d["x"].float().numpy())
+        wc, ws = on.quantize_e8m0_b32(d["w"].numpy())
+        out["mx_gemm_16x512x512"] = {"ms_per_call": timed(lambda: on.mx_gemm(ac, as_, wc, ws)),
+                                     "sample": "whole call (activation quantized beforehand)"}
+        lut = []
+        for M, rows in ((1, 1), (8, 8), (64, 8)):
+            w = synth.lut_problem(M, N=4096, K=4096, group=128, seed=0, device="cuda", iters=10)
+            xb = w["x"][:rows].cpu().view(torch.int16).numpy().view(np.uint16)
+            idx, cent = w["idx"].cpu().numpy(), w["centroids"].cpu().numpy()
+            ms = timed(lambda: on.lut_gemm(xb, idx, cent, 128)) * M / rows
+            lut.append({"M": M, "ms_per_call": ms,
+                        "sample": "whole call" if rows == M else f"{rows} of {M} rows, scaled by {M // rows}"})
+        out["lut_gemm"] = lut
+        M, N, K, tail, rows = 128, 2560, 9728, 256, 8
+        p = synth.tail_residual_problem(M, N, K, tail=tail, seed=0, device="cpu")
+        ac, as_ = on.quantize_e8m0_b32(p["x"][:rows].float().numpy())
+        wn = p["w"].numpy()
+        wc, ws = on.quantize_e8m0_b32(wn)
+        rc, rs = on.quantize_e8m0_b32(oracle.residual_weight(wn, wc, ws, tail))
+        ms = timed(lambda: on.residual_tail_gemm(ac, as_, wc, ws, rc, rs, tail)) * M / rows
+        out["residual_tail_gemm"] = {"ms_per_call": ms, "sample": f"{rows} of {M} rows, scaled by {M // rows}"}
+    out["threads"] = 1
+    out["cpu_model"] = _cpu_model()
+    return out
+
+
 # ---------------------------------------------------------------------------
 # decode-shaped GEMMs (weights streamed from HBM)
 # ---------------------------------------------------------------------------
@@ -363,10 +416,16 @@ def lut_decode(gbw, synth, torch, M):
             gbw.lut_gemm(base["x"], idx, cent, 128, out=y, ws=ws)
     us = _graph_time(torch, fn, len(reps))
     floor = read_floor(torch, [(pool.data_ptr() + r * (ib + cb), ib + cb) for r in range(R)])
+
+    def fn_hot():  # one replica, re-read by every call: its weights stay in the on-chip caches
+        for _ in range(HOT_CALLS):
+            gbw.lut_gemm(base["x"], reps[0][0], reps[0][1], 128, out=y, ws=ws)
+    hot = _graph_time(torch, fn_hot, HOT_CALLS)
     all_bytes = w_bytes + M * K * 2 + M * N * 4  # weights + bf16 x + fp32 y
     return {"M": M, "us_per_call": us, "weight_bytes": w_bytes, "GB_s": w_bytes / us / 1e3,
             "frac_hbm": w_bytes / us / 1e3 / HBM_PEAK_GBS, "frac_hbm_all_bytes": all_bytes / us / 1e3 / HBM_PEAK_GBS,
-            "replicas": len(reps), "read_floor_us": floor, "frac_of_read_floor": floor / us if floor else None}
+            "replicas": len(reps), "read_floor_us": floor, "frac_of_read_floor": floor / us if floor else None,
+            "hot_us_per_call": hot}
 
 
 def tail_decode(gbw, synth, torch):
@@ -402,13 +461,18 @@ def tail_decode(gbw, synth, torch):
             gbw.residual_tail_gemm(a, w, r, tail, out=y, ws=ws)
     us = _graph_time(torch, fn, len(reps))
     floor = read_floor(torch, [(pool.data_ptr() + r * stride, w_bytes) for r in range(R)])
+
+    def fn_hot():  # one replica, re-read by every call: its weights stay in the on-chip caches
+        for _ in range(HOT_CALLS):
+            gbw.residual_tail_gemm(a, reps[0][0], reps[0][1], tail, out=y, ws=ws)
+    hot = _graph_time(torch, fn_hot, HOT_CALLS)
     flops = 2.0 * M * N * (K + tail)
     all_bytes = w_bytes + M * (K + tail) // 2 + M * (K + tail) // 32 + M * N * 4  # weights + codes/scales + y
     return {"M": M, "N": N, "K": K, "tail": tail, "us_per_call": us, "weight_bytes": w_bytes,
             "GB_s": w_bytes / us / 1e3, "frac_hbm": w_bytes / us / 1e3 / HBM_PEAK_GBS,
             "frac_hbm_all_bytes": all_bytes / us / 1e3 / HBM_PEAK_GBS,
             "TFLOP_s": flops / us / 1e6, "frac_mxfp4_mfma": flops / us / 1e6 / MXFP4_PEAK_TFLOPS, "replicas": R,
-            "read_floor_us": floor, "frac_of_read_floor": floor / us if floor else None}
+            "read_floor_us": floor, "frac_of_read_floor": floor / us if floor else None, "hot_us_per_call": hot}
 
 
 def moe_mxfp4_prquant(gbw, synth, torch, steps=5, tail=128):
@@ -679,7 +743,12 @@ def main():
                          "residual_tail_gemm": tail_decode(gbw, synth, torch),
                          "empty_kernel_us": empty_kernel_floor(torch),
                          "read_floor_note": "read_floor_us: a plain streaming read of the same weight bytes, "
-                                            "one kernel per call, timed the same way"}
+                                            "one kernel per call, timed the same way",
+                         "hot_note": "hot_us_per_call: one weight replica re-read by every call, so the weights "
+                                     "come from the on-chip caches (a cache-resident figure, not an HBM one)"}
+        if not args.no_cpu_baseline:
+            log("oracle on one host thread: dense and decode-shaped configurations")
+            out["decode"]["cpu_oracle_1core"] = cpu_oracle_1core(synth, torch, np)
         torch.cuda.empty_cache()
         log("extra: E4M3-B16 MoE, 16x512x512 linear")
         out["extra"] = {"moe_e4m3_b16": moe_e4m3(gbw, synth, torch),
