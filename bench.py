@@ -56,9 +56,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true")
-    ap.add_argument("--part", choices=("decode", "e4m3", "mfma"), default=None,
+    ap.add_argument("--part", choices=("decode", "e4m3", "mfma", "tiletrace"), default=None,
                     help="profiling aid: run only the decode GEMMs, only the E4M3-B16 MoE or only the MFMA rate "
-                         "probe and print their measurements (not the benchmark line)")
+                         "probe and print their measurements (not the benchmark line); tiletrace: the per-tile "
+                         "timeline of one headline gate/up and one down launch, with GBW_LIBRARY naming "
+                         "libgbw_tiletrace.so (python gemm_bit_weight_amd/build.py --tile-trace)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES between two device buffers 3 times (scale for the HBM byte counters)")
     return ap.parse_args()
@@ -146,6 +148,75 @@ def moe_vq_prefill(gbw, synth, torch, steps, warmup, scales="prescale"):
                        + tuple(w.scale_codebook for w in (Wgu, Wd) if w.scale_codebook is not None))
     return dict(ms_step=ms_step, gu_ms=gu_ms, dn_ms=dn_ms, flops=flops_gu + flops_dn, flops_gu=flops_gu,
                 flops_dn=flops_dn, weight_bytes=weight_bytes, data=d, route=route, T=T, H=H, I=I, E=E, K=K)
+
+
+def tile_timeline(gbw, synth, torch, np):
+    """Per-tile timeline of one gate/up and one down launch of the headline
+    MoE step, from the wall-clock stamps of the tile-trace build (100 MHz):
+    median lookup / prologue / K-loop / epilogue times of full tiles and of
+    tiles holding 1-32 pairs, the CUs' finish times, the gaps between a CU's
+    tiles and how many tiles are in their epilogue at once."""
+    import ctypes
+    lib = gbw._lib
+    if not hasattr(lib, "gbw_tile_trace"):
+        raise SystemExit("--part tiletrace needs GBW_LIBRARY=<repo>/gemm_bit_weight_amd/libgbw_tiletrace.so "
+                         "(built by: python gemm_bit_weight_amd/build.py --tile-trace)")
+    lib.gbw_tile_trace.restype = ctypes.c_int
+    lib.gbw_tile_trace.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    res = moe_vq_prefill(gbw, synth, torch, steps=2, warmup=2)
+    route, d, T, H, I, E, K = res["route"], res["data"], res["T"], res["H"], res["I"], res["E"], res["K"]
+    fmt = getattr(gbw, VQ_SCALE_FMT["prescale"])
+    W = lambda v, N, Kd: gbw.Weight(fmt, N, Kd, v["idx"], v["scales"], v["codebook"], n_experts=E)  # noqa: E731
+    Wgu, Wd = W(d["gate_up"], 2 * I, H), W(d["down"], H, I)
+    P = T * K
+    xq = gbw.mx_quantize(d["x"], gbw.FMT_E8M0_B32)
+    hc = torch.empty((P, I // 2), dtype=torch.uint8, device="cuda")
+    hs = torch.empty((P, I // 32), dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    wsd = torch.zeros(gbw.workspace_size(gbw.OP_MOE_GEMM, P, H, 0), dtype=torch.uint8, device="cuda")
+    stages = {"gate_up": lambda: gbw.moe_grouped_gemm(gbw.MOE_GATEUP_SWIGLU, route, xq, Wgu, h_codes=hc, h_scales=hs),
+              "down": lambda: gbw.moe_grouped_gemm(gbw.MOE_DOWN_COMBINE, route, gbw.Act(gbw.FMT_E8M0_B32, hc, hs),
+                                                   Wd, y=y, ws=wsd)}
+    for fn in stages.values():
+        fn()
+    torch.cuda.synchronize()
+    buf = np.zeros(16384 * 8, dtype=np.uint64)
+    us = lambda t: t * 10 / 1000  # noqa: E731  (100 MHz ticks -> us)
+    out = {}
+    for name, fn in stages.items():
+        assert lib.gbw_tile_trace(None, 0, 1) == 0
+        torch.cuda.synchronize()
+        fn()
+        torch.cuda.synchronize()
+        assert lib.gbw_tile_trace(buf.ctypes.data, buf.nbytes, 0) == 0
+        a = buf.reshape(16384, 8).astype(np.int64)
+        v = a[a[:, 1] > 0]
+        t0, t1, t2, t3, t4, cu = (v[:, i] for i in range(6))
+        rows = v[:, 6] & 0xFFFF
+        base = t0.min()
+
+        def phases(m):
+            med = lambda x: float(us(np.median(x[m])))  # noqa: E731
+            return {"tiles": int(m.sum()), "lookup_us": med(t1 - t0), "prologue_us": med(t2 - t1),
+                    "kloop_us": med(t3 - t2), "epilogue_us": med(t4 - t3), "tile_us": med(t4 - t0)}
+        ends, gaps = [], []
+        for c in np.unique(cu):
+            m = cu == c
+            o = np.argsort(t0[m])
+            ends.append(t4[m].max())
+            gaps.extend((t0[m][o][1:] - t4[m][o][:-1]).tolist())
+        ends = us(np.array(ends) - base)
+        e3, e4 = us(t3 - base), us(t4 - base)
+        span = float(us(t4.max() - base))
+        inepi = np.array([((e3 <= g) & (e4 > g)).sum() for g in np.arange(0.0, span, 1.0)])
+        out[name] = {"span_us": span, "full_tiles": phases(rows == 256), "tiles_1_32_pairs": phases(rows <= 32),
+                     "cu_finish_us": {"min": float(ends.min()), "median": float(np.median(ends)),
+                                      "max": float(ends.max())},
+                     "gap_between_tiles_us": {"median": float(us(np.median(gaps))),
+                                              "per_cu_total": float(us(np.sum(gaps)) / len(ends))},
+                     "tiles_in_epilogue": {"median": float(np.median(inepi)), "p90": float(np.percentile(inepi, 90)),
+                                           "max": int(inepi.max())}}
+    return out
 
 
 CPU_SAMPLE_EXPERTS = 24   # about 10-30 s of oracle work on 16 host threads (5 s per 8 experts)
@@ -685,6 +756,9 @@ def main():
         return
     if args.part == "e4m3":
         print(json.dumps({"moe_e4m3_b16": moe_e4m3(gbw, synth, torch, steps=args.steps)}), flush=True)
+        return
+    if args.part == "tiletrace":
+        print(json.dumps(tile_timeline(gbw, synth, torch, np)), flush=True)
         return
     if args.part == "mfma":
         print(json.dumps({"mfma_rate_probe": mfma_rate_probe(torch)}), flush=True)

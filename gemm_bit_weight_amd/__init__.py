@@ -4,8 +4,10 @@ Argument marshalling only.  Every step of the hot path runs in the HIP
 kernels behind the C ABI declared in include/gbw.h; torch supplies device
 memory (tensors) and the current stream.  The names match the C entry points.
 
-The library is loaded from this directory; importing this package when it has
-not been built raises ImportError -- there is no fallback implementation.
+The library is loaded from this directory (GBW_LIBRARY may name another build
+of the same sources, such as the tile-trace measurement build); importing this
+package when it has not been built raises ImportError -- there is no fallback
+implementation.
 """
 
 import ctypes
@@ -16,7 +18,7 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgbw.so")
+LIB_PATH = os.environ.get("GBW_LIBRARY") or os.path.join(_HERE, "libgbw.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run gemm_bit_weight_amd.build.build() "

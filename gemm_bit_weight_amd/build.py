@@ -23,6 +23,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgbw.so")
+# measurement aid: the same sources with the MoE tile timeline compiled in
+TRACE_LIB = os.path.join(HERE, "libgbw_tiletrace.so")
 # measurement aid for the benchmark (a plain streaming read), its own library
 FLOOR_SRCS = [os.path.join(HERE, "floor", f) for f in ("stream_read.hip", "mfma_rate.hip")]
 FLOOR_LIB = os.path.join(HERE, "libgbw_floor.so")
@@ -48,9 +50,9 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+def _compile(src, build_dir=BUILD, extra=()):
+    obj = os.path.join(build_dir, os.path.basename(src)[:-4] + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
@@ -79,6 +81,29 @@ def build(jobs=None, verbose=False):
     return LIB
 
 
+def build_tile_trace(verbose=False):
+    """The library with the per-tile wall-clock stamps of the FP4 MoE kernel
+    compiled in (-DGBW_TILE_TRACE), as libgbw_tiletrace.so; loaded only when
+    GBW_LIBRARY names it (bench.py --part tiletrace)."""
+    bdir = BUILD + "_trace"
+    os.makedirs(bdir, exist_ok=True)
+    srcs = sources()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, bdir, ("-DGBW_TILE_TRACE",)), srcs))
+    tmp = TRACE_LIB + ".tmp"
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, TRACE_LIB)
+    if verbose:
+        print(f"built {TRACE_LIB}")
+    return TRACE_LIB
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--tile-trace" in sys.argv[1:]:
+        build_tile_trace(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)

@@ -43,6 +43,26 @@
 
 namespace gbw {
 
+// Measurement aid, compiled in only with -DGBW_TILE_TRACE (a separate
+// library; the normal build has none of it): thread 0 of each FP4 MoE
+// workgroup stamps the wall clock (100 MHz) at tile entry, after the tile
+// lookup, after the prologue, after the K loop and after the epilogue, and
+// records its CU id and tile (rows, expert, m tile, n tile).  Slots per
+// workgroup: 0 entry, 1 lookup done, 2 K loop start, 3 K loop end, 4 tile
+// end, 5 CU id, 6 rows | e << 16 | mt << 32 | nt << 40.
+#ifdef GBW_TILE_TRACE
+constexpr int kTraceBlocks = 16384;
+__device__ unsigned long long g_tile_trace[kTraceBlocks * 8];
+#define GBW_TRACE(slot, val)                                                    \
+  do {                                                                          \
+    if (threadIdx.x == 0 && blockIdx.x < kTraceBlocks) g_tile_trace[blockIdx.x * 8 + (slot)] = (val); \
+  } while (0)
+#else
+#define GBW_TRACE(slot, val) \
+  do {                       \
+  } while (0)
+#endif
+
 constexpr int kMoeBM = 256;       // pairs (A rows) per tile
 constexpr int kMoeThreads = 256;  // threads that run the tile-list scan (every kernel has at least this many)
 constexpr int kRowB = 80;         // LDS bytes per FP4 operand row per stage (64 of data + 16 of padding)
@@ -321,8 +341,16 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
   uint8_t* const sA0 = sOp;              // A buffer b at sA0 + b * kABuf
   uint8_t* const sB0 = sOp + 2 * kABuf;  // B buffer b at sB0 + b * kBBuf
 
+#ifdef GBW_TILE_TRACE
+  const unsigned long long t_entry = wall_clock64();
+#endif
   TileInfo ti;
   if (!find_tile(p, ti, scan)) return;
+  GBW_TRACE(0, t_entry);
+  GBW_TRACE(1, wall_clock64());
+  GBW_TRACE(5, __smid());
+  GBW_TRACE(6, (unsigned long long)ti.rows | ((unsigned long long)ti.e << 16) | ((unsigned long long)ti.mt << 32) |
+                   ((unsigned long long)ti.nt << 40));
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
@@ -637,12 +665,14 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
     mma(s & 1, nb);
     __syncthreads();
   };
+  GBW_TRACE(2, wall_clock64());
   if (nband == 2)
     kloop(IntC<2>{});
   else if (nband == 1)
     kloop(IntC<1>{});
   else
     kloop(IntC<0>{});
+  GBW_TRACE(3, wall_clock64());
 
   // ---------------------------------------------------------------------
   // epilogues; acc[i][j][r] is row 64*wm + 32*i + 8*(r/4) + 4*g2 + r%4 of
@@ -652,6 +682,10 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
   if (!gate) {
     static_assert(fp4_threads(BN) / 64 * 8192 <= 2 * kABuf + 2 * kBBuf, "down staging fits the operand buffers");
     down_epilogue<BN>(p, ti, acc, wm, wn, lane, 1.0f, sA0, s_tok, s_w);
+#ifdef GBW_TILE_TRACE
+    __syncthreads();
+    GBW_TRACE(4, wall_clock64());
+#endif
     return;
   }
 
@@ -675,6 +709,10 @@ __global__ __launch_bounds__(fp4_threads(BN), 2) void k_moe_fp4(const MoeArgs p)
     }
   __syncthreads();
   h_tile_store<BN>(p, ti, sHb, tid);
+#ifdef GBW_TILE_TRACE
+  __syncthreads();
+  GBW_TRACE(4, wall_clock64());
+#endif
 }
 
 template <int WF>
@@ -1257,3 +1295,14 @@ extern "C" int moe_grouped_gemm(int32_t stage, int64_t T, int32_t topk, const in
   }
   return st;
 }
+
+#ifdef GBW_TILE_TRACE
+// Copy the tile trace to host memory (bytes <= 16384 * 8 * 8), or with
+// clear != 0 zero it.  Synchronous; only in the trace build.
+extern "C" int gbw_tile_trace(void* host, size_t bytes, int clear) {
+  static unsigned long long zero[gbw::kTraceBlocks * 8];
+  if (clear) return (int)hipMemcpyToSymbol(HIP_SYMBOL(gbw::g_tile_trace), zero, sizeof(zero));
+  if (bytes > sizeof(zero)) return (int)hipErrorInvalidValue;
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(gbw::g_tile_trace), bytes);
+}
+#endif
