@@ -258,7 +258,10 @@ __device__ __forceinline__ void down_epilogue(const MoeArgs& p, const TileInfo& 
         const int m = 64 * wm + 32 * i + 16 * h + mr;
         if (m < ti.rows) {
           uint8_t* dst = reinterpret_cast<uint8_t*>(p.slots) + ((int64_t)(ti.row0 + m) * p.N + col0) * esz + pc * 16;
-          *reinterpret_cast<v4i*>(dst) = *reinterpret_cast<const v4i*>(st + mr * 128 * esz + pc * 16);
+          // streaming store: a slot row is read once, by the combine, after
+          // this launch; it should not displace weight tiles from L2
+          __builtin_nontemporal_store(*reinterpret_cast<const v4i*>(st + mr * 128 * esz + pc * 16),
+                                      reinterpret_cast<v4i*>(dst));
         }
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -1115,15 +1118,16 @@ __global__ void k_moe_combine(const void* __restrict__ slots, const float* __res
     const float w = topk_w[t * topk + j];
     const int64_t base = (int64_t)pair_pos[t * topk + j] * H + n;
     if (F32) {
-      const v4f a = *reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(slots) + base);
-      const v4f b = *reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(slots) + base + 4);
+      const v4f a = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(slots) + base));
+      const v4f b =
+          __builtin_nontemporal_load(reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(slots) + base + 4));
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         acc[q] += w * a[q];
         acc[4 + q] += w * b[q];
       }
     } else {
-      const v4i v = load16(reinterpret_cast<const uint16_t*>(slots) + base);
+      const v4i v = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(reinterpret_cast<const uint16_t*>(slots) + base));
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         acc[2 * q] += w * bf16_to_f32((uint32_t)v[q] & 0xFFFFu);
@@ -1131,8 +1135,8 @@ __global__ void k_moe_combine(const void* __restrict__ slots, const float* __res
       }
     }
   }
-  *reinterpret_cast<v4f*>(y + i) = v4f{acc[0], acc[1], acc[2], acc[3]};
-  *reinterpret_cast<v4f*>(y + i + 4) = v4f{acc[4], acc[5], acc[6], acc[7]};
+  __builtin_nontemporal_store(v4f{acc[0], acc[1], acc[2], acc[3]}, reinterpret_cast<v4f*>(y + i));
+  __builtin_nontemporal_store(v4f{acc[4], acc[5], acc[6], acc[7]}, reinterpret_cast<v4f*>(y + i + 4));
 }
 
 }  // namespace gbw
