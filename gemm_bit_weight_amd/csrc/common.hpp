@@ -180,8 +180,11 @@ __device__ __forceinline__ v4i load16(const void* p) { return *reinterpret_cast<
 // instruction, with no registers in between.
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
+// `stream`: the non-temporal cache policy (bit 1 of the instruction's cache
+// policy field), for data read once per call such as a decode GEMV's weights.
+template <bool stream = false>
 __device__ __forceinline__ void load_lds16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds, 16, 0, stream ? 2 : 0);
 }
 
 __host__ __device__ constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

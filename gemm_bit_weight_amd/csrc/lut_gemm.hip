@@ -181,7 +181,9 @@ __global__ __launch_bounds__(64 * NW) void k_lut_gemv(const LutArgs p) {
       if (o < len) {
         const uint8_t* src = isidx ? p.idx + n * (p.K / 2) + k0 / 2 + o
                                    : reinterpret_cast<const uint8_t*>(p.cent) + n * tb_row + (k0 / p.group) * 32 + o;
-        load_lds16(src, (isidx ? si + r * irow : st + r * trow) + part * 1024);
+        // streaming: each weight byte is read once per call (measured: 7.8 -> 7.5 us
+        // at M = 1 and 8.6 -> 8.2 us at M = 8 with the weights in HBM)
+        load_lds16<true>(src, (isidx ? si + r * irow : st + r * trow) + part * 1024);
       }
     }
     __syncthreads();
