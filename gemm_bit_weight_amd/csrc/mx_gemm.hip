@@ -459,9 +459,13 @@ __global__ __launch_bounds__(256) void k_mx_gemm32(const MxGemmArgs p) {
 
 // Split count: enough K splits that the grid fills the CUs, but never more
 // workgroups than can be resident at once (a second partial round of
-// workgroups would double the latency of this one-pass kernel).
+// workgroups would double the latency of this one-pass kernel).  A K range
+// that one workgroup loads in a single batch (at most SMAX steps) is not
+// split: there the partial slabs and the second kernel that sums them cost
+// more than the extra workgroups gain.
 template <int TM, int TN, int NW, int SMAX>
 static int pick_splits(int64_t M, int64_t N, int total_steps) {
+  if (total_steps <= SMAX) return 1;
   const int64_t tiles = cdiv(N, 16 * TN * NW) * cdiv(M, 16 * TM);
   constexpr int lds = 16 * TM * (SMAX * 64 + 16) + 16 * TM * SMAX * 4;
   const int per_cu = lds > 80 * 1024 ? 1 : 2;
